@@ -1,0 +1,103 @@
+"""Pins for the oracle's number-format conversions.
+
+The oracle writes bf16 and fp16 rounding from the format definitions; these
+tests hold them to independent library routines (torch's CPU fp32->bf16 cast,
+numpy's fp32->fp16 cast), exhaustively over all 16-bit inputs for widening and
+over every low half-word of many high half-words for narrowing, which covers
+every tie, every carry into the exponent and the overflow to infinity.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _torch_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_widen_exhaustive():
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_to_f32(h)
+    ref = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_bf16_round_matches_torch_on_every_low_half():
+    g = np.random.default_rng(7)
+    highs = np.concatenate([
+        g.integers(0, 1 << 16, size=200, dtype=np.uint32),
+        np.array([0x0000, 0x8000, 0x0001, 0x007F, 0x0080, 0x3F80, 0x3F81,
+                  0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0, 0x4000, 0xC000], np.uint32)])
+    low = np.arange(1 << 16, dtype=np.uint32)
+    bits = ((highs[:, None] << 16) | low[None, :]).reshape(-1)
+    x = bits.view(np.float32)
+    mine = oracle.f32_to_bf16(x)
+    ref = _torch_bf16_bits(x)
+    nan = np.isnan(x)
+    # NaN payloads are not graded: both sides must give a NaN
+    assert np.all((mine[nan] & 0x7F80) == 0x7F80) and np.all((mine[nan] & 0x7F) != 0)
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("value,expect", [
+    (1.0, 0x3F80),
+    (1.0 + 2.0 ** -8, 0x3F80),            # exact tie, kept part even -> down
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),        # exact tie, kept part odd -> up
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),
+    (-2.5, 0xC020),
+    (3.3895313892515355e38, 0x7F7F),      # max finite bf16 is exact
+    (float.fromhex("0x1.ffp127"), 0x7F80),      # tie above max, kept part odd -> inf
+    (float.fromhex("0x1.ff8p127"), 0x7F80),     # above the tie -> inf
+    (float.fromhex("0x1.fefffep127"), 0x7F7F),   # just below the tie to inf
+    (0.0, 0x0000),
+    (-0.0, 0x8000),
+    (float.fromhex("0x1p-133"), 0x0001),  # bf16 subnormal kept
+])
+def test_bf16_round_closed_forms(value, expect):
+    assert int(oracle.f32_to_bf16(np.array([value], np.float32))[0]) == expect
+
+
+def test_f16_widen_exhaustive():
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.f16_to_f32(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_round_matches_numpy():
+    g = np.random.default_rng(11)
+    # exponents around the binary16 range, every low half-word of a few values
+    highs = np.concatenate([
+        g.integers(0x3000, 0x4800, size=60, dtype=np.uint32),   # |x| ~ 2^-31 .. 2^17
+        g.integers(0xB000, 0xC800, size=60, dtype=np.uint32),
+        np.array([0x3380, 0x3800, 0x3880, 0x477F, 0x4780, 0x0000, 0x7F80, 0x7FC0,
+                  0x33FF, 0x3400, 0x387F], np.uint32)])
+    low = np.arange(1 << 16, dtype=np.uint32)
+    bits = ((highs[:, None] << 16) | low[None, :]).reshape(-1)
+    x = bits.view(np.float32)
+    mine = oracle.f32_to_f16(x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    assert np.all((mine[nan] & 0x7C00) == 0x7C00) and np.all((mine[nan] & 0x3FF) != 0)
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("value,expect", [
+    (65504.0, 0x7BFF),
+    (65519.99, 0x7BFF),
+    (65520.0, 0x7C00),          # tie at the top rounds to even -> overflow
+    (2.0 ** -24, 0x0001),
+    (2.0 ** -25, 0x0000),       # tie to even at the smallest subnormal
+    (3 * 2.0 ** -25, 0x0002),
+    (2.0 ** -14 - 2.0 ** -25, 0x0400),   # rounds up into the smallest normal
+    (-1.5, 0xBE00),
+])
+def test_f16_round_closed_forms(value, expect):
+    assert int(oracle.f32_to_f16(np.array([value], np.float32))[0]) == expect
