@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Benchmark of the collectives hot path on one MI355X.
+
+One step is one pass of every hot-path row over one batch of synthetic,
+HBM-resident input, R = 8 virtual ranks, bf16 unless noted:
+
+  ar_160k      AllReduce, R=4, 160 KiB per rank (the four-segment A-D example)
+  ar_decode    AllReduce, [64, 7168] per rank (TP decode)
+  ar_64m       AllReduce, 64 MiB per rank
+  rs_sp        ReduceScatter [8192, 4096] -> 1024-token shards
+  ag_sp        AllGather of those shards back to [8192, 4096]
+  gather       Gather fp32 logits [256, 19008] x 8 -> [256, 152064] on rank 0
+  bcast        Broadcast int32 [256] from rank 7
+  moe_layout   expert histogram / scans / stable slots, 4096 x top-8, 256 experts
+  moe_permute  dispatch permute into per-destination send buffers
+  a2av_dispatch  All-to-All-v of the dispatched rows (hidden 7168)
+  moe_expert   the test expert y = x * (1 + e/256) on received rows
+  a2av_combine   All-to-All-v back (counts transposed)
+  moe_combine  gate-weighted top-8 sum back to each token
+
+value = algorithmic bytes of the whole step / step time (GB/s).  Algorithmic
+bytes are the minimum each row must read plus write (e.g. AllReduce 2*R*S,
+All-to-All-v 2 * rows * row_bytes).  Per-row times come from HIP events on the
+stream the kernels run on; the dominant kernel (a2av_dispatch) is reported
+against the 8 TB/s HBM roofline.  A separate AllReduce sweep at 16/32/64 MiB
+per rank rotates four buffer sets so the 256 MB Infinity Cache cannot serve it.
+
+The CPU baseline times the oracle (single-threaded C) on a bounded sample of
+the same step (MoE leg at 512 of the 4096 tokens per rank).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "AllReduce/A2A-v algorithmic GB/s at R=8 bf16; % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+R = 8
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--only", default="", help="comma list of rows to run (profiling)")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ inputs
+
+def make_inputs(torch, synth, coll):
+    import numpy as np
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    W = {}
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    W["ar160_in"] = [dev_bf16(synth.gaussian(81920, 1.0, 1000 + r, "bf16")) for r in range(4)]
+    W["ar160_out"] = [torch.empty_like(t) for t in W["ar160_in"]]
+    W["ard_in"] = [dev_bf16(synth.gaussian((64, 7168), 0.02, 2000 + r, "bf16")) for r in range(R)]
+    W["ard_out"] = [torch.empty_like(t) for t in W["ard_in"]]
+    n64 = (64 << 20) // 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(26)
+    W["ar64_in"] = [(torch.randn(n64, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+                    for _ in range(R)]
+    W["ar64_out"] = [torch.empty_like(t) for t in W["ar64_in"]]
+    W["sp_in"] = [dev_bf16(synth.gaussian((8192, 4096), 1.0, 3000 + r, "bf16")) for r in range(R)]
+    W["sp_shard"] = [torch.empty((1024, 4096), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    W["sp_full"] = [torch.empty_like(t) for t in W["sp_in"]]
+    W["lg_in"] = [torch.from_numpy(synth.gaussian((256, 19008), 2.0, 4000 + r, "fp32")).cuda()
+                  for r in range(R)]
+    W["lg_out"] = torch.empty((256, R * 19008), dtype=torch.float32, device="cuda")
+    W["bc_src"] = torch.from_numpy(synth.uniform_int32(256, 0, 152064, 4107)).cuda()
+    W["bc_out"] = [torch.empty_like(W["bc_src"]) for _ in range(R)]
+    W["bc_out"][7] = W["bc_src"]
+
+    E, T, K, H = 256, 4096, 8, 7168
+    W["moe"] = (E, T, K, H)
+    ids, ws = [], []
+    for s in range(R):
+        i, w = synth.zipf_routing(T, E, K, seed=5100 + s)
+        ids.append(torch.from_numpy(i).cuda())
+        ws.append(torch.from_numpy(w).cuda())
+    W["moe_ids"], W["moe_w"] = ids, ws
+    W["moe_x"] = [dev_bf16(synth.gaussian((T, H), 1.0, 5000 + s, "bf16")) for s in range(R)]
+    W["sc"] = torch.empty(R * R, dtype=torch.int64, device="cuda")
+    W["sd"] = torch.empty_like(W["sc"])
+    W["rd"] = torch.empty_like(W["sc"])
+    W["sc_t"] = torch.empty_like(W["sc"])
+    W["ec"] = torch.empty(R * E, dtype=torch.int32, device="cuda")
+    W["pos"] = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(R)]
+    W["ws"] = torch.empty(coll.moe_workspace_bytes(R, T, K, E), dtype=torch.uint8, device="cuda")
+    W["send"] = [torch.empty((T * K, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    W["back"] = [torch.empty((T * K, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    W["out"] = [torch.empty((T, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    # the routing is fixed, so the receive sizes are known once (outside timing)
+    coll.moe_layout(ids, E, W["sc"], W["sd"], W["rd"], W["ec"], W["pos"], W["ws"])
+    torch.cuda.synchronize()
+    sc = W["sc"].view(R, R).cpu()
+    W["sc_t"].copy_(W["sc"].view(R, R).t().contiguous().view(-1))
+    W["recv"] = [torch.empty((int(sc[:, d].sum()), H), dtype=torch.bfloat16, device="cuda")
+                 for d in range(R)]
+    W["moe_rows"] = int(sc.sum())
+    W["dest_share"] = [round(float(sc[:, d].sum()) / float(sc.sum()), 4) for d in range(R)]
+    torch.cuda.synchronize()
+    return W
+
+
+def row_bytes(W):
+    """Algorithmic HBM bytes of every row (minimum read + write)."""
+    E, T, K, H = W["moe"]
+    rows = W["moe_rows"]
+    b = {}
+    b["ar_160k"] = 2 * 4 * 81920 * 2
+    b["ar_decode"] = 2 * R * 64 * 7168 * 2
+    b["ar_64m"] = 2 * R * (64 << 20)
+    S = 8192 * 4096 * 2
+    b["rs_sp"] = (R + 1) * S
+    b["ag_sp"] = S + R * S
+    b["gather"] = 2 * R * 256 * 19008 * 4
+    b["bcast"] = 256 * 4 * R                          # 1 read + 7 writes (root keeps its own)
+    b["moe_layout"] = 2 * R * T * K * 4
+    b["moe_permute"] = R * T * H * 2 + rows * H * 2 + R * T * K * 4
+    b["a2av_dispatch"] = 2 * rows * H * 2
+    b["moe_expert"] = 2 * rows * H * 2
+    b["a2av_combine"] = 2 * rows * H * 2
+    b["moe_combine"] = rows * H * 2 + R * T * H * 2 + R * T * K * 8
+    return b
+
+
+def step_rows(W, coll, torch):
+    """(name, callable) for every row of one step, in order."""
+    E, T, K, H = W["moe"]
+    return [
+        ("ar_160k", lambda: coll.allreduce(W["ar160_in"], W["ar160_out"])),
+        ("ar_decode", lambda: coll.allreduce(W["ard_in"], W["ard_out"])),
+        ("ar_64m", lambda: coll.allreduce(W["ar64_in"], W["ar64_out"])),
+        ("rs_sp", lambda: coll.reduce_scatter(W["sp_in"], W["sp_shard"])),
+        ("ag_sp", lambda: coll.all_gather(W["sp_shard"], W["sp_full"])),
+        ("gather", lambda: coll.gather(W["lg_in"], W["lg_out"], 0)),
+        ("bcast", lambda: coll.broadcast(W["bc_src"], W["bc_out"], 7)),
+        ("moe_layout", lambda: coll.moe_layout(W["moe_ids"], E, W["sc"], W["sd"], W["rd"],
+                                               W["ec"], W["pos"], W["ws"])),
+        ("moe_permute", lambda: coll.moe_permute(W["moe_x"], W["pos"], W["send"])),
+        ("a2av_dispatch", lambda: coll.all_to_all_v(W["send"], W["sc"], W["sd"], W["recv"],
+                                                    W["rd"], H)),
+        ("moe_expert", lambda: coll.moe_expert_scale(W["recv"], W["ec"], W["rd"], E, H)),
+        ("a2av_combine", lambda: coll.all_to_all_v(W["recv"], W["sc_t"], W["rd"], W["back"],
+                                                   W["sd"], H)),
+        ("moe_combine", lambda: coll.moe_combine(W["back"], W["pos"], W["moe_w"], W["out"])),
+    ]
+
+
+def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=20):
+    """AllReduce R=8 bf16 at large sizes, rotating `sets` buffer sets so the
+    working set (>= 1 GiB) exceeds the Infinity Cache."""
+    res = {}
+    for mib in sizes_mib:
+        n = (mib << 20) // 2
+        bufs = [([torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(0, 0.02)
+                  for _ in range(R)],
+                 [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(R)])
+                for _ in range(sets)]
+        for i in range(sets):
+            coll.allreduce(*bufs[i])
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record()
+            coll.allreduce(*bufs[i % sets])
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        med = ts[len(ts) // 2]
+        gbs = 2 * R * (mib << 20) / (med * 1e-3) / 1e9
+        res[f"{mib}MiB"] = {"median_us": round(med * 1e3, 2), "GBps": round(gbs, 1),
+                            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------- CPU baseline
+
+def cpu_baseline():
+    """The oracle as it stands, single-threaded, on a bounded sample of the
+    step: every row at its bench size except the MoE leg (512 of 4096 tokens
+    per rank) and the 64 MiB AllReduce (16 MiB per rank)."""
+    import numpy as np
+
+    import oracle
+    from collective_communication_amd import synth
+
+    oracle.lib()
+    t_total = 0.0
+    bytes_total = 0
+
+    def timed(fn, nbytes):
+        nonlocal t_total, bytes_total
+        t0 = time.perf_counter()
+        fn()
+        t_total += time.perf_counter() - t0
+        bytes_total += nbytes
+
+    xs = [synth.gaussian(81920, 1.0, 1000 + r, "bf16") for r in range(4)]
+    timed(lambda: oracle.allreduce(xs, "bf16"), 2 * 4 * 81920 * 2)
+    xs = [synth.gaussian(64 * 7168, 0.02, 2000 + r, "bf16") for r in range(R)]
+    timed(lambda: oracle.allreduce(xs, "bf16"), 2 * R * 64 * 7168 * 2)
+    n = (16 << 20) // 2
+    xs = [synth.gaussian(n, 0.02, 7000 + r, "bf16") for r in range(R)]
+    timed(lambda: oracle.allreduce(xs, "bf16"), 2 * R * n * 2)
+    xs = [synth.gaussian(8192 * 4096, 1.0, 3000 + r, "bf16") for r in range(R)]
+    S = 8192 * 4096 * 2
+    holder = {}
+    timed(lambda: holder.setdefault("rs", oracle.reduce_scatter(xs, "bf16")), (R + 1) * S)
+    timed(lambda: oracle.all_gather(holder["rs"]), S + R * S)
+    del xs, holder
+    lg = [synth.gaussian((256, 19008), 2.0, 4000 + r, "fp32") for r in range(R)]
+    timed(lambda: oracle.gather(lg, 0), 2 * R * 256 * 19008 * 4)
+    ids = synth.uniform_int32(256, 0, 152064, 4107)
+    timed(lambda: oracle.broadcast(ids, R, 7), 256 * 4 * R)
+    E, T, K, H = 256, 512, 8, 7168
+    tid, tw = [], []
+    for s in range(R):
+        i, w = synth.zipf_routing(4096, E, K, seed=5100 + s)
+        tid.append(np.ascontiguousarray(i[:T]))
+        tw.append(np.ascontiguousarray(w[:T]))
+    tx = [synth.gaussian((T, H), 1.0, 5000 + s, "bf16") for s in range(R)]
+    rows = R * T * K
+    moe_bytes = (2 * R * T * K * 4 + (R * T * H * 2 + rows * H * 2) + 3 * 2 * rows * H * 2
+                 + rows * H * 2 + R * T * H * 2)
+    timed(lambda: oracle.moe_pipeline(tx, tid, tw, E), moe_bytes)
+    return {"value": round(bytes_total / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "seconds": round(t_total, 2),
+            "sample": "every step row at bench size except AllReduce 16 MiB/rank instead of "
+                      "64 MiB and the MoE leg at 512 of 4096 tokens per rank; single-threaded C "
+                      "oracle (gcc -O2), algorithmic bytes / wall time"}
+
+
+# ------------------------------------------------------------------ roofline
+
+def counter_traffic(kernel_src: str):
+    """HBM traffic per launch of the dominant kernel from the committed
+    rocprofv3 --pmc summary, or None when missing or when the kernel source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "a2av_dispatch_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic bytes per launch:\s*([0-9]+)", text)
+    if not m_sha or not m_b:
+        return None
+    with open(kernel_src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != m_sha.group(1):
+            return None
+    return int(m_b.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the R ranks are virtual "
+                                   "ranks in one GPU's HBM; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from collective_communication_amd import coll, synth
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    coll.lib()
+    W = make_inputs(torch, synth, coll)
+    rows = step_rows(W, coll, torch)
+    if args.only:
+        keep = set(args.only.split(","))
+        rows = [r for r in rows if r[0] in keep]
+    nbytes = row_bytes(W)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for _, fn in rows:
+            fn()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    names = [n for n, _ in rows]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)]
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        e = evs[k]
+        e[0].record()
+        for j, (_, fn) in enumerate(rows):
+            fn()
+            e[j + 1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    per_row = {n: sum(evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(args.steps)) / args.steps
+               for j, n in enumerate(names)}
+    step_bytes = sum(nbytes[n] for n in names)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    rows_out = {}
+    for n in names:
+        ms = per_row[n]
+        gbs = nbytes[n] / (ms * 1e-3) / 1e9
+        rows_out[n] = {"us": round(ms * 1e3, 2), "bytes": nbytes[n], "GBps": round(gbs, 1),
+                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    dom = "a2av_dispatch"
+    roof = None
+    if dom in per_row:
+        ach = nbytes[dom] / (per_row[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "a2av_kernel<16> (All-to-All-v dispatch)",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(os.path.join(ROOT, "collective_communication_amd",
+                                                        "csrc", "a2av.hip")),
+                "bytes_per_launch": nbytes[dom],
+                "avg_launch_us": round(per_row[dom] * 1e3, 2)}
+
+    sweep = None
+    if not args.no_sweep and not args.only:
+        print("[bench] allreduce sweep", file=sys.stderr, flush=True)
+        sweep = ar_sweep(torch, coll)
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.only:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hot path over R=8 virtual ranks in one GPU: AllReduce "
+                               "(160 KiB x4, [64,7168] x8, 64 MiB x8), SP ReduceScatter+"
+                               "AllGather [8192,4096] x8, Gather fp32 [256,19008] x8 + "
+                               "Broadcast int32[256], MoE dispatch/combine 4096 tok x 7168 "
+                               "top-8 of 256 experts via All-to-All-v",
+                   "ranks": R, "step_bytes": step_bytes,
+                   "moe_rows": W["moe_rows"], "moe_dest_share": W["dest_share"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "rows": rows_out,
+        "allreduce_sweep": sweep,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

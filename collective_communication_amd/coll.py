@@ -1,0 +1,281 @@
+"""ctypes binding of libcoll.so -- argument marshalling only.
+
+Every function takes lists of CUDA (HIP) tensors, one per virtual rank,
+checks shapes and dtypes on the host, passes raw device pointers and the
+current stream to the C ABI in ``include/coll.h``, and raises ``CollError`` on
+a negative status.  All computation happens in the library's HIP kernels;
+there is no fallback: if ``libcoll.so`` has not been built this module raises
+on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcoll.so")
+
+COLL_BF16, COLL_FP16, COLL_FP32, COLL_INT32 = 0, 1, 2, 3
+OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
+MAX_RANKS = 16
+
+_REDUCE_DTYPES = {torch.bfloat16: COLL_BF16, torch.float16: COLL_FP16,
+                  torch.float32: COLL_FP32, torch.int32: COLL_INT32}
+
+# exported symbol -> (restype, argtypes)
+_vp, _sz, _i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+SIGNATURES = {
+    "coll_status_string": (ctypes.c_char_p, [_i]),
+    "coll_version": (_i, []),
+    "coll_allreduce": (_i, [_i, _vp, _vp, _sz, _i, _i, _vp]),
+    "coll_reduce_scatter": (_i, [_i, _vp, _vp, _sz, _i, _i, _vp]),
+    "coll_all_gather": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
+    "coll_gather": (_i, [_i, _vp, _vp, _i, _sz, _sz, _i, _vp]),
+    "coll_broadcast": (_i, [_i, _vp, _vp, _i, _sz, _i, _vp]),
+    "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp]),
+    "coll_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "coll_moe_layout": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
+    "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _vp]),
+    "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
+}
+
+
+class CollError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().coll_status_string(status).decode()} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcoll.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m collective_communication_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise CollError(status, what)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, what: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{what}: tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _table(ts: Sequence[torch.Tensor], what: str):
+    return (ctypes.c_void_p * len(ts))(*[_dev(t, what) for t in ts])
+
+
+def _ranks(ts, what) -> int:
+    R = len(ts)
+    if not 1 <= R <= MAX_RANKS:
+        raise ValueError(f"{what}: {R} ranks (1..{MAX_RANKS} supported)")
+    return R
+
+
+def _copy_dtype(t: torch.Tensor) -> tuple[int, int]:
+    """(coll dtype code, elements-per-tensor-element) for pure copies."""
+    es = t.element_size()
+    if es == 2:
+        return COLL_BF16, 1
+    if es == 4:
+        return COLL_FP32, 1
+    if es == 8:
+        return COLL_FP32, 2
+    raise ValueError(f"element size {es} not supported by the copy primitives")
+
+
+def _reduce_dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _REDUCE_DTYPES:
+        raise ValueError(f"reductions support bf16/fp16/fp32/int32, got {t.dtype}")
+    return _REDUCE_DTYPES[t.dtype]
+
+
+def _same(ts, dtype, numel, what):
+    for t in ts:
+        if t.dtype != dtype or t.numel() != numel:
+            raise ValueError(f"{what}: every rank needs {numel} elements of {dtype}")
+
+
+# --------------------------------------------------------------------- API
+
+def allreduce(sends, recvs, op: str = "sum", stream=None) -> None:
+    """AllReduce: every recvs[r] gets the reduction of all sends (recvs may be sends)."""
+    R = _ranks(sends, "allreduce")
+    n = sends[0].numel()
+    _same(sends, sends[0].dtype, n, "allreduce send")
+    _same(recvs, sends[0].dtype, n, "allreduce recv")
+    if len(recvs) != R:
+        raise ValueError("allreduce: one recv per rank")
+    _check(lib().coll_allreduce(R, _table(sends, "send"), _table(recvs, "recv"), n,
+                                _reduce_dtype(sends[0]), OPS[op], _stream(stream)), "allreduce")
+
+
+def reduce_scatter(sends, recvs, op: str = "sum", stream=None) -> None:
+    """ReduceScatter: recvs[r] = chunk r of the reduction (sends hold R chunks)."""
+    R = _ranks(sends, "reduce_scatter")
+    n = recvs[0].numel()
+    _same(sends, sends[0].dtype, R * n, "reduce_scatter send")
+    _same(recvs, sends[0].dtype, n, "reduce_scatter recv")
+    _check(lib().coll_reduce_scatter(R, _table(sends, "send"), _table(recvs, "recv"), n,
+                                     _reduce_dtype(sends[0]), OPS[op], _stream(stream)),
+           "reduce_scatter")
+
+
+def all_gather(sends, recvs, stream=None) -> None:
+    """AllGather: recvs[r] = concatenation of sends in rank order."""
+    R = _ranks(sends, "all_gather")
+    n = sends[0].numel()
+    _same(sends, sends[0].dtype, n, "all_gather send")
+    _same(recvs, sends[0].dtype, R * n, "all_gather recv")
+    dt, mult = _copy_dtype(sends[0])
+    _check(lib().coll_all_gather(R, _table(sends, "send"), _table(recvs, "recv"), n * mult, dt,
+                                 _stream(stream)), "all_gather")
+
+
+def gather(sends, recv_root, root: int = 0, stream=None) -> None:
+    """Gather: sends[q] of shape [outer, inner] concatenated along the last
+    axis into recv_root [outer, R*inner]; only the root's buffer is written."""
+    R = _ranks(sends, "gather")
+    s0 = sends[0]
+    outer = s0.shape[0] if s0.dim() == 2 else 1
+    inner = s0.shape[-1] if s0.dim() >= 1 else 1
+    _same(sends, s0.dtype, outer * inner, "gather send")
+    if recv_root.dtype != s0.dtype or recv_root.numel() != outer * R * inner:
+        raise ValueError("gather: root buffer must be [outer, R*inner] of the send dtype")
+    dt, mult = _copy_dtype(s0)
+    _check(lib().coll_gather(R, _table(sends, "send"), _dev(recv_root, "recv"), root, outer,
+                             inner * mult, dt, _stream(stream)), "gather")
+
+
+def broadcast(send_root, recvs, root: int, stream=None) -> None:
+    """Broadcast: every recvs[r] = send_root (recvs[root] may be send_root)."""
+    R = _ranks(recvs, "broadcast")
+    n = send_root.numel()
+    _same(recvs, send_root.dtype, n, "broadcast recv")
+    dt, mult = _copy_dtype(send_root)
+    _check(lib().coll_broadcast(R, _dev(send_root, "send"), _table(recvs, "recv"), root,
+                                n * mult, dt, _stream(stream)), "broadcast")
+
+
+def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
+                 stream=None) -> None:
+    """All-to-All-v with device int64 [R*R] counts (s-major), sdispls (s-major)
+    and rdispls (d-major), in rows of ``row_elems`` elements."""
+    R = _ranks(sends, "all_to_all_v")
+    for t, name in ((sendcounts, "sendcounts"), (sdispls, "sdispls"), (rdispls, "rdispls")):
+        if t.dtype != torch.int64 or t.numel() != R * R:
+            raise ValueError(f"all_to_all_v: {name} must be int64 [R*R] on the device")
+    if len(recvs) != R:
+        raise ValueError("all_to_all_v: one recv per rank")
+    dt, mult = _copy_dtype(sends[0])
+    for t in list(sends) + list(recvs):
+        if t.dtype != sends[0].dtype:
+            raise ValueError("all_to_all_v: one dtype for every buffer")
+    _check(lib().coll_all_to_all_v(R, _table(sends, "send"), _dev(sendcounts, "counts"),
+                                   _dev(sdispls, "sdispls"), _table(recvs, "recv"),
+                                   _dev(rdispls, "rdispls"), row_elems * mult, dt,
+                                   _stream(stream)), "all_to_all_v")
+
+
+def moe_workspace_bytes(R: int, tokens: int, topk: int, n_experts: int) -> int:
+    return int(lib().coll_moe_workspace_bytes(R, tokens, topk, n_experts))
+
+
+def moe_layout(topk_ids, n_experts: int, sendcounts, sdispls, rdispls, expert_counts, pos,
+               workspace, stream=None) -> None:
+    """MoE layout from int32 [T, K] ids per rank into device count tables and
+    int32 [T, K] send-slot positions."""
+    R = _ranks(topk_ids, "moe_layout")
+    T, K = topk_ids[0].shape
+    for t in topk_ids:
+        if t.dtype != torch.int32 or tuple(t.shape) != (T, K):
+            raise ValueError("moe_layout: ids must be int32 [T, K] on every rank")
+    for t in pos:
+        if t.dtype != torch.int32 or t.numel() != T * K:
+            raise ValueError("moe_layout: pos must be int32 [T, K] on every rank")
+    for t in (sendcounts, sdispls, rdispls):
+        if t.dtype != torch.int64 or t.numel() != R * R:
+            raise ValueError("moe_layout: count tables are int64 [R*R]")
+    if expert_counts.dtype != torch.int32 or expert_counts.numel() != R * n_experts:
+        raise ValueError("moe_layout: expert_counts is int32 [R*E]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().coll_moe_layout(R, _table(topk_ids, "ids"), T, K, n_experts,
+                                 _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
+                                 _dev(rdispls, "rd"), _dev(expert_counts, "ec"),
+                                 _table(pos, "pos"), _dev(workspace, "ws"), ws_bytes,
+                                 _stream(stream)), "moe_layout")
+
+
+def moe_permute(xs, pos, sends, stream=None) -> None:
+    """sends[s][pos[s][t,k]] = xs[s][t] (x [T, H], sends [T*K, H])."""
+    R = _ranks(xs, "moe_permute")
+    T, H = xs[0].shape
+    K = pos[0].shape[1]
+    for x in xs:
+        if tuple(x.shape) != (T, H) or x.dtype != xs[0].dtype:
+            raise ValueError("moe_permute: x must be [T, H] of one dtype")
+    for s in sends:
+        if s.numel() != T * K * H or s.dtype != xs[0].dtype:
+            raise ValueError("moe_permute: send buffers must be [T*K, H]")
+    dt, mult = _copy_dtype(xs[0])
+    _check(lib().coll_moe_permute(R, _table(xs, "x"), _table(pos, "pos"), T, K, H * mult, dt,
+                                  _table(sends, "send"), _stream(stream)), "moe_permute")
+
+
+def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
+                     stream=None) -> None:
+    """Test expert y = rne(x * (1 + e/256)) in place on received bf16 rows."""
+    R = _ranks(recvs, "moe_expert_scale")
+    for r in recvs:
+        if r.dtype != torch.bfloat16:
+            raise ValueError("moe_expert_scale: bf16 rows only")
+    _check(lib().coll_moe_expert_scale(R, _table(recvs, "recv"), _dev(expert_counts, "ec"),
+                                       _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
+                                       _stream(stream)), "moe_expert_scale")
+
+
+def moe_combine(backs, pos, weights, outs, stream=None) -> None:
+    """outs[s][t] = rne(sum_k w[s][t,k] * backs[s][pos[s][t,k]]), k ascending."""
+    R = _ranks(backs, "moe_combine")
+    T, K = pos[0].shape
+    H = outs[0].shape[-1]
+    for b in backs:
+        if b.dtype != torch.bfloat16 or b.numel() != T * K * H:
+            raise ValueError("moe_combine: back buffers are bf16 [T*K, H]")
+    for w in weights:
+        if w.dtype != torch.float32 or w.numel() != T * K:
+            raise ValueError("moe_combine: weights are fp32 [T, K]")
+    for o in outs:
+        if o.dtype != torch.bfloat16 or o.numel() != T * H:
+            raise ValueError("moe_combine: outputs are bf16 [T, H]")
+    _check(lib().coll_moe_combine(R, _table(backs, "back"), _table(pos, "pos"),
+                                  _table(weights, "w"), T, K, H, COLL_BF16, _table(outs, "out"),
+                                  _stream(stream)), "moe_combine")

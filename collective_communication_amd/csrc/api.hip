@@ -1,0 +1,248 @@
+// api.hip -- the extern "C" boundary of libcoll.so (declared in include/coll.h).
+//
+// Every entry point validates its arguments on the host, copies the caller's
+// host pointer arrays into by-value kernel arguments, and enqueues the
+// kernels on the caller's stream.  Nothing is allocated and nothing is
+// synchronised; no C++ exception can escape (the code below throws none and
+// every HIP call reports through its return code).
+#include <stdlib.h>
+#include <string.h>
+
+#include "coll_internal.h"
+
+namespace coll {
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct DevInfo {
+  int ready;
+  int num_cus;
+};
+DevInfo g_dev[kMaxDevices];   // per-device compute-unit count (filled once)
+
+long env_long(const char *name, long dflt) {
+  const char *v = getenv(name);
+  if (!v || !*v) return dflt;
+  char *end = nullptr;
+  long x = strtol(v, &end, 10);
+  return (end && *end == '\0') ? x : dflt;
+}
+
+}  // namespace
+
+Launch launch_ctx(void *stream) {
+  Launch L;
+  L.stream = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  if (!g_dev[dev].ready) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    g_dev[dev].num_cus = cus;
+    g_dev[dev].ready = 1;
+  }
+  L.num_cus = g_dev[dev].num_cus;
+  long w = env_long("COLL_WGS_PER_CU", 8);
+  L.wgs_per_cu = (int)(w < 1 ? 1 : (w > 64 ? 64 : w));
+  long nt = env_long("COLL_NT_MIN_BYTES", 1L << 62);
+  L.nt_bytes = nt < 0 ? 0 : (size_t)nt;
+  L.a2a_nt = env_long("COLL_A2A_NT", 0) ? 1 : 0;
+  return L;
+}
+
+}  // namespace coll
+
+using namespace coll;
+
+namespace {
+
+bool ranks_ok(int R) { return R >= 1 && R <= COLL_MAX_RANKS; }
+bool dtype_ok(int dt) { return dt >= COLL_BF16 && dt <= COLL_INT32; }
+bool op_ok(int op) { return op >= COLL_SUM && op <= COLL_MIN; }
+
+// count * elem * factor must stay far from size_t overflow (2^56 bytes)
+bool bytes_ok(size_t count, size_t elem, size_t factor) {
+  const size_t lim = (size_t)1 << 56;
+  return count < lim / (elem * (factor ? factor : 1));
+}
+
+// Copy R host pointers; false if the array or any entry is NULL.
+bool fill_in(int R, const void *const *src, const void **dst) {
+  if (!src) return false;
+  for (int r = 0; r < R; r++) {
+    if (!src[r]) return false;
+    dst[r] = src[r];
+  }
+  return true;
+}
+bool fill_out(int R, void *const *src, void **dst) {
+  if (!src) return false;
+  for (int r = 0; r < R; r++) {
+    if (!src[r]) return false;
+    dst[r] = src[r];
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *coll_status_string(int status) {
+  switch (status) {
+    case COLL_OK: return "COLL_OK";
+    case COLL_ERR_INVALID_ARG: return "COLL_ERR_INVALID_ARG: invalid argument";
+    case COLL_ERR_UNSUPPORTED: return "COLL_ERR_UNSUPPORTED: unsupported dtype, op or size";
+    case COLL_ERR_HIP: return "COLL_ERR_HIP: HIP launch or runtime error";
+    default: return "unknown coll status";
+  }
+}
+
+int coll_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+int coll_allreduce(int R, const void *const *sendbufs, void *const *recvbufs, size_t count,
+                   coll_dtype_t dtype, coll_op_t op, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (!op_ok(op)) return COLL_ERR_UNSUPPORTED;
+  if (count == 0) return COLL_OK;
+  if (!bytes_ok(count, dtype_size(dtype), 2 * (size_t)R)) return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, sendbufs, p.in) || !fill_out(R, recvbufs, p.out)) return COLL_ERR_INVALID_ARG;
+  return launch_allreduce(launch_ctx(stream), R, p, count, dtype, op);
+}
+
+int coll_reduce_scatter(int R, const void *const *sendbufs, void *const *recvbufs,
+                        size_t recvcount, coll_dtype_t dtype, coll_op_t op, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (!op_ok(op)) return COLL_ERR_UNSUPPORTED;
+  if (recvcount == 0) return COLL_OK;
+  if (!bytes_ok(recvcount, dtype_size(dtype), (size_t)R * (R + 1))) return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, sendbufs, p.in) || !fill_out(R, recvbufs, p.out)) return COLL_ERR_INVALID_ARG;
+  return launch_reduce_scatter(launch_ctx(stream), R, p, recvcount, dtype, op);
+}
+
+int coll_all_gather(int R, const void *const *sendbufs, void *const *recvbufs, size_t sendcount,
+                    coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (sendcount == 0) return COLL_OK;
+  if (!bytes_ok(sendcount, dtype_size(dtype), (size_t)R * (R + 1))) return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, sendbufs, p.in) || !fill_out(R, recvbufs, p.out)) return COLL_ERR_INVALID_ARG;
+  return launch_all_gather(launch_ctx(stream), R, p, sendcount * dtype_size(dtype));
+}
+
+int coll_gather(int R, const void *const *sendbufs, void *recvbuf_root, int root, size_t outer,
+                size_t inner, coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || root < 0 || root >= R) return COLL_ERR_INVALID_ARG;
+  if (outer == 0 || inner == 0) return COLL_OK;
+  if (!recvbuf_root || !bytes_ok(outer, inner * dtype_size(dtype), 2 * (size_t)R))
+    return COLL_ERR_INVALID_ARG;
+  if (inner > ((size_t)1 << 40) / outer) return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, sendbufs, p.in)) return COLL_ERR_INVALID_ARG;
+  return launch_gather(launch_ctx(stream), R, p, recvbuf_root, outer, inner * dtype_size(dtype));
+}
+
+int coll_broadcast(int R, const void *sendbuf_root, void *const *recvbufs, int root, size_t count,
+                   coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || root < 0 || root >= R) return COLL_ERR_INVALID_ARG;
+  if (count == 0) return COLL_OK;
+  if (!sendbuf_root || !recvbufs || !bytes_ok(count, dtype_size(dtype), (size_t)R + 1))
+    return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  for (int r = 0; r < R; r++) {
+    if (!recvbufs[r] && r != root) return COLL_ERR_INVALID_ARG;
+    p.out[r] = recvbufs[r];
+  }
+  return launch_broadcast(launch_ctx(stream), R, sendbuf_root, p, count * dtype_size(dtype));
+}
+
+int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcounts,
+                      const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
+                      size_t row_elems, coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (row_elems == 0) return COLL_OK;
+  if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
+    return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, sendbufs, p.in) || !fill_out(R, recvbufs, p.out)) return COLL_ERR_INVALID_ARG;
+  return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls,
+                     row_elems * dtype_size(dtype));
+}
+
+size_t coll_moe_workspace_bytes(int R, int tokens, int topk, int n_experts) {
+  if (!ranks_ok(R) || tokens < 0 || topk < 1 || n_experts < 1 || n_experts > kMoeMaxExperts ||
+      n_experts % R != 0 || (int64_t)tokens * topk >= ((int64_t)1 << 31))
+    return 0;
+  return moe_workspace_bytes(R, tokens, topk, n_experts);
+}
+
+int coll_moe_layout(int R, const int32_t *const *topk_ids, int tokens, int topk, int n_experts,
+                    int64_t *sendcounts, int64_t *sdispls, int64_t *rdispls,
+                    int32_t *expert_counts, int32_t *const *pos, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  size_t need = coll_moe_workspace_bytes(R, tokens, topk, n_experts);
+  if (need == 0) return COLL_ERR_INVALID_ARG;
+  if (!sendcounts || !sdispls || !rdispls || !expert_counts || !workspace ||
+      workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return COLL_ERR_INVALID_ARG;
+  PtrTable ids{};
+  MutPtrTable ps{};
+  if (tokens > 0) {
+    if (!fill_in(R, reinterpret_cast<const void *const *>(topk_ids), ids.p) ||
+        !fill_out(R, reinterpret_cast<void *const *>(pos), ps.p))
+      return COLL_ERR_INVALID_ARG;
+  }
+  return launch_moe_layout(launch_ctx(stream), R, ids, tokens, topk, n_experts, sendcounts,
+                           sdispls, rdispls, expert_counts, ps, workspace);
+}
+
+int coll_moe_permute(int R, const void *const *x, const int32_t *const *pos, int tokens, int topk,
+                     size_t hidden, coll_dtype_t dtype, void *const *sendbufs, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || tokens < 0 || topk < 1) return COLL_ERR_INVALID_ARG;
+  if (tokens == 0 || hidden == 0) return COLL_OK;
+  if ((int64_t)tokens * topk >= ((int64_t)1 << 31) || !bytes_ok(hidden, dtype_size(dtype), 1))
+    return COLL_ERR_INVALID_ARG;
+  PtrTable xs{}, ps{};
+  MutPtrTable ss{};
+  if (!fill_in(R, x, xs.p) || !fill_in(R, reinterpret_cast<const void *const *>(pos), ps.p) ||
+      !fill_out(R, sendbufs, ss.p))
+    return COLL_ERR_INVALID_ARG;
+  return launch_moe_permute(launch_ctx(stream), R, xs, ps, tokens, topk,
+                            hidden * dtype_size(dtype), ss);
+}
+
+int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_counts,
+                          const int64_t *rdispls, int n_experts, size_t hidden,
+                          coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0)
+    return COLL_ERR_INVALID_ARG;
+  if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
+  if (hidden == 0) return COLL_OK;
+  if (!expert_counts || !rdispls || hidden >= ((size_t)1 << 31)) return COLL_ERR_INVALID_ARG;
+  MutPtrTable rs{};
+  if (!fill_out(R, recvbufs, rs.p)) return COLL_ERR_INVALID_ARG;
+  return launch_moe_expert_scale(launch_ctx(stream), R, rs, expert_counts, rdispls, n_experts,
+                                 hidden);
+}
+
+int coll_moe_combine(int R, const void *const *back, const int32_t *const *pos,
+                     const float *const *topk_w, int tokens, int topk, size_t hidden,
+                     coll_dtype_t dtype, void *const *out, void *stream) {
+  if (!ranks_ok(R) || tokens < 0 || topk < 1) return COLL_ERR_INVALID_ARG;
+  if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
+  if (tokens == 0 || hidden == 0) return COLL_OK;
+  if ((int64_t)tokens * topk >= ((int64_t)1 << 31) || hidden >= ((size_t)1 << 31))
+    return COLL_ERR_INVALID_ARG;
+  PtrTable bs{}, ps{}, ws{};
+  MutPtrTable os{};
+  if (!fill_in(R, back, bs.p) || !fill_in(R, reinterpret_cast<const void *const *>(pos), ps.p) ||
+      !fill_in(R, reinterpret_cast<const void *const *>(topk_w), ws.p) || !fill_out(R, out, os.p))
+    return COLL_ERR_INVALID_ARG;
+  return launch_moe_combine(launch_ctx(stream), R, bs, ps, ws, tokens, topk, hidden, os);
+}
+
+}  // extern "C"

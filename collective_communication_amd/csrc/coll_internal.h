@@ -1,0 +1,317 @@
+// coll_internal.h -- shared device helpers of libcoll (gfx950 only).
+//
+// Data model: R virtual ranks are R device pointers per buffer role, passed by
+// value in the kernel arguments (RankPtrs).  On one GPU a "rank boundary" is
+// only a pointer, so every primitive is a streaming HBM kernel: 16-byte
+// (dwordx4) coalesced loads and stores, fp32 accumulation of narrow types in a
+// fixed ascending rank order, and a grid-stride loop sized to the compute
+// units for large messages or a single pass for small ones.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "coll.h"
+
+namespace coll {
+
+constexpr int kBlock = 256;   // threads per workgroup: 4 wave64s
+
+struct RankPtrs {
+  const void *in[COLL_MAX_RANKS];
+  void *out[COLL_MAX_RANKS];
+};
+
+// One pointer per rank for a single buffer role (MoE helpers).
+struct PtrTable {
+  const void *p[COLL_MAX_RANKS];
+};
+struct MutPtrTable {
+  void *p[COLL_MAX_RANKS];
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ vector memory
+
+template <class U>
+__device__ __forceinline__ U ld(const void *base, size_t i) {
+  return reinterpret_cast<const U *>(base)[i];
+}
+
+template <class U>
+__device__ __forceinline__ void st(void *base, size_t i, U v, bool nt) {
+  U *p = reinterpret_cast<U *>(base) + i;
+  if (nt)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
+// ------------------------------------------------ element formats (exact widening)
+
+// bf16 pair in one dword -> two fp32 (exact: bf16 is the top half of fp32)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// two fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+// two fp32 -> fp16 pair, round to nearest even (v_cvt_f16_f32 in RNE mode)
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+}
+
+// ------------------------------------------------------- reduction operators
+
+// MAX / MIN: NaN if either operand is NaN; -0 orders below +0.
+__device__ __forceinline__ float op_max(float a, float b) {
+  if (a != a || b != b) return __builtin_bit_cast(float, 0x7FC00000u);
+  if (a == b) return __builtin_signbit(a) ? b : a;
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float op_min(float a, float b) {
+  if (a != a || b != b) return __builtin_bit_cast(float, 0x7FC00000u);
+  if (a == b) return __builtin_signbit(a) ? a : b;
+  return a < b ? a : b;
+}
+
+template <int OP>
+__device__ __forceinline__ float fold(float acc, float x) {
+  if constexpr (OP == COLL_SUM) return acc + x;
+  else if constexpr (OP == COLL_PROD) return acc * x;
+  else if constexpr (OP == COLL_MAX) return op_max(acc, x);
+  else return op_min(acc, x);
+}
+
+template <int OP>
+__device__ __forceinline__ int32_t fold_i(int32_t acc, int32_t x) {
+  if constexpr (OP == COLL_SUM) return (int32_t)((uint32_t)acc + (uint32_t)x);
+  else if constexpr (OP == COLL_PROD) return (int32_t)((uint32_t)acc * (uint32_t)x);
+  else if constexpr (OP == COLL_MAX) return acc > x ? acc : x;
+  else return acc < x ? acc : x;
+}
+
+// Per-dtype view of a 16-byte vector as fp32 lanes (int32 stays integer).
+//   kLanes: elements per 16 bytes; Acc: accumulator vector.
+template <int DT> struct Fmt;
+
+template <> struct Fmt<COLL_BF16> {
+  static constexpr int kLanes = 8;
+  static constexpr int kSize = 2;
+  struct Acc { float v[8]; };
+  __device__ static Acc widen(u32x4 w) {
+    Acc a;
+#pragma unroll
+    for (int j = 0; j < 4; j++) { a.v[2 * j] = bf16_lo(w[j]); a.v[2 * j + 1] = bf16_hi(w[j]); }
+    return a;
+  }
+  template <int OP> __device__ static void fold_in(Acc &a, u32x4 w) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      a.v[2 * j] = fold<OP>(a.v[2 * j], bf16_lo(w[j]));
+      a.v[2 * j + 1] = fold<OP>(a.v[2 * j + 1], bf16_hi(w[j]));
+    }
+  }
+  __device__ static u32x4 narrow(const Acc &a) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; j++) w[j] = pack_bf16(a.v[2 * j], a.v[2 * j + 1]);
+    return w;
+  }
+  // scalar element path (tails, unaligned buffers)
+  typedef uint16_t Elem;
+  __device__ static float widen1(Elem e) { return bf16_lo(e); }
+  __device__ static Elem narrow1(float f) { return (Elem)(pack_bf16(f, 0.0f) & 0xFFFFu); }
+};
+
+template <> struct Fmt<COLL_FP16> {
+  static constexpr int kLanes = 8;
+  static constexpr int kSize = 2;
+  struct Acc { float v[8]; };
+  __device__ static Acc widen(u32x4 w) {
+    Acc a;
+#pragma unroll
+    for (int j = 0; j < 4; j++) { a.v[2 * j] = f16_lo(w[j]); a.v[2 * j + 1] = f16_hi(w[j]); }
+    return a;
+  }
+  template <int OP> __device__ static void fold_in(Acc &a, u32x4 w) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      a.v[2 * j] = fold<OP>(a.v[2 * j], f16_lo(w[j]));
+      a.v[2 * j + 1] = fold<OP>(a.v[2 * j + 1], f16_hi(w[j]));
+    }
+  }
+  __device__ static u32x4 narrow(const Acc &a) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; j++) w[j] = pack_f16(a.v[2 * j], a.v[2 * j + 1]);
+    return w;
+  }
+  typedef uint16_t Elem;
+  __device__ static float widen1(Elem e) { return f16_lo(e); }
+  __device__ static Elem narrow1(float f) { return (Elem)(pack_f16(f, 0.0f) & 0xFFFFu); }
+};
+
+template <> struct Fmt<COLL_FP32> {
+  static constexpr int kLanes = 4;
+  static constexpr int kSize = 4;
+  struct Acc { float v[4]; };
+  // (a vector element is copied to a scalar before __builtin_bit_cast: applied
+  // to an ext_vector subscript directly, clang reinterprets element 0)
+  __device__ static Acc widen(u32x4 w) {
+    Acc a;
+#pragma unroll
+    for (int j = 0; j < 4; j++) { const uint32_t x = w[j]; a.v[j] = __builtin_bit_cast(float, x); }
+    return a;
+  }
+  template <int OP> __device__ static void fold_in(Acc &a, u32x4 w) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t x = w[j];
+      a.v[j] = fold<OP>(a.v[j], __builtin_bit_cast(float, x));
+    }
+  }
+  __device__ static u32x4 narrow(const Acc &a) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; j++) w[j] = __builtin_bit_cast(uint32_t, a.v[j]);
+    return w;
+  }
+  typedef float Elem;
+  __device__ static float widen1(Elem e) { return e; }
+  __device__ static Elem narrow1(float f) { return f; }
+};
+
+template <> struct Fmt<COLL_INT32> {
+  static constexpr int kLanes = 4;
+  static constexpr int kSize = 4;
+  struct Acc { int32_t v[4]; };
+  __device__ static Acc widen(u32x4 w) {
+    Acc a;
+#pragma unroll
+    for (int j = 0; j < 4; j++) a.v[j] = (int32_t)w[j];
+    return a;
+  }
+  template <int OP> __device__ static void fold_in(Acc &a, u32x4 w) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) a.v[j] = fold_i<OP>(a.v[j], (int32_t)w[j]);
+  }
+  __device__ static u32x4 narrow(const Acc &a) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; j++) w[j] = (uint32_t)a.v[j];
+    return w;
+  }
+  typedef int32_t Elem;
+};
+
+// ------------------------------------------------------------ fast division
+// Division of n < 2^31 by a runtime constant d >= 1 with one mul-high, add and
+// shift (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994): q = (umulhi(n, m) + n) >> s with s = ceil(log2 d)
+// and m = floor(2^32 (2^s - d) / d) + 1.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) s++;
+  f.s = s;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ----------------------------------------------------------- launch helpers
+
+struct Launch {
+  hipStream_t stream;
+  int num_cus;       // compute units of the current device
+  int wgs_per_cu;    // resident workgroups per CU for grid-stride kernels
+  size_t nt_bytes;   // bytes moved at or above which stores are non-temporal
+  int a2a_nt;        // non-temporal stores in All-to-All-v (size unknown on the host)
+};
+
+// Device properties and tuning knobs (environment: COLL_WGS_PER_CU,
+// COLL_NT_MIN_BYTES, COLL_A2A_NT), read once per device.
+Launch launch_ctx(void *stream);
+
+// Blocks for a grid-stride loop over `work` items of kBlock*per_thread each:
+// a single pass when that fits the resident grid, else the resident grid.
+inline unsigned grid_for(const Launch &L, size_t work, int per_thread = 1) {
+  size_t per_block = (size_t)kBlock * per_thread;
+  size_t need = (work + per_block - 1) / per_block;
+  size_t cap = (size_t)L.num_cus * L.wgs_per_cu;
+  if (need < 1) need = 1;
+  return (unsigned)(need < cap ? need : cap);
+}
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest power-of-two unit (<= 16 bytes) dividing every pointer and `bytes`.
+inline int copy_unit(uintptr_t bits_or) {
+  if ((bits_or & 15u) == 0) return 16;
+  if ((bits_or & 7u) == 0) return 8;
+  if ((bits_or & 3u) == 0) return 4;
+  if ((bits_or & 1u) == 0) return 2;
+  return 1;
+}
+
+inline size_t dtype_size(int dt) {
+  switch (dt) {
+    case COLL_BF16: case COLL_FP16: return 2;
+    case COLL_FP32: case COLL_INT32: return 4;
+    default: return 0;
+  }
+}
+
+inline int hip_status() {
+  return hipGetLastError() == hipSuccess ? COLL_OK : COLL_ERR_HIP;
+}
+
+// ------------------------------------------------------- internal launchers
+int launch_allreduce(const Launch &L, int R, const RankPtrs &p, size_t count, int dt, int op);
+int launch_reduce_scatter(const Launch &L, int R, const RankPtrs &p, size_t recvcount, int dt, int op);
+int launch_all_gather(const Launch &L, int R, const RankPtrs &p, size_t bytes_per_rank);
+int launch_gather(const Launch &L, int R, const RankPtrs &p, void *out, size_t outer,
+                  size_t inner_bytes);
+int launch_broadcast(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes);
+int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
+                const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes);
+
+constexpr int kMoeMaxExperts = 1024;
+size_t moe_workspace_bytes(int R, int T, int K, int E);
+int launch_moe_layout(const Launch &L, int R, const PtrTable &ids, int T, int K, int E,
+                      int64_t *sendcounts, int64_t *sdispls, int64_t *rdispls,
+                      int32_t *expert_counts, const MutPtrTable &pos, void *ws);
+int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable &pos, int T,
+                       int K, size_t row_bytes, const MutPtrTable &send);
+int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
+                            const int32_t *expert_counts, const int64_t *rdispls, int E,
+                            size_t hidden);
+int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTable &pos,
+                       const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
+
+}  // namespace coll

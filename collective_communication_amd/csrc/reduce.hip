@@ -1,0 +1,249 @@
+// reduce.hip -- AllReduce and ReduceScatter kernels.
+//
+// AllReduce follows the owner-per-segment dataflow of the IPC AllReduce blog
+// ("From NCCL Ring LL to PCIe IPC AllReduce", section "Pro5000 ?"): each
+// segment is gathered from all R ranks by its owner, summed once, and the sum
+// is sent back to all R ranks.  On one GPU the owner of a 16-byte tile is the
+// lane that holds it: it issues the R loads back to back (R * 16 B in flight
+// per lane), folds them in ascending rank order in fp32, narrows once (RNE)
+// and issues R stores of the same register tile.  ReduceScatter is the first
+// half of that (tutorial section 5): one store, to the owner only.
+//
+// Every output element has exactly one writer, which reads all of its inputs
+// before writing, so AllReduce in place (recv[r] == send[r]) and the
+// documented in-place ReduceScatter are race free.
+#include "coll_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace coll {
+namespace {
+
+// ---------------------------------------------------------------- AllReduce
+
+// R known at compile time: all R loads are independent and issued together.
+template <int R, int DT, int OP>
+__global__ __launch_bounds__(kBlock) void ar_vec(RankPtrs p, size_t nvec, int nt) {
+  using F = Fmt<DT>;
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec; i += stride) {
+    u32x4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) v[r] = ld<u32x4>(p.in[r], i);
+    typename F::Acc a = F::widen(v[0]);
+#pragma unroll
+    for (int r = 1; r < R; r++) F::template fold_in<OP>(a, v[r]);
+    u32x4 o = F::narrow(a);
+#pragma unroll
+    for (int r = 0; r < R; r++) st<u32x4>(p.out[r], i, o, nt);
+  }
+}
+
+// Runtime R (ops other than SUM): loads predicated on r < R.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void ar_vec_rt(RankPtrs p, int R, size_t nvec, int nt) {
+  using F = Fmt<DT>;
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec; i += stride) {
+    u32x4 v[COLL_MAX_RANKS];
+#pragma unroll
+    for (int r = 0; r < COLL_MAX_RANKS; r++)
+      if (r < R) v[r] = ld<u32x4>(p.in[r], i);
+    typename F::Acc a = F::widen(v[0]);
+#pragma unroll
+    for (int r = 1; r < COLL_MAX_RANKS; r++)
+      if (r < R) F::template fold_in<OP>(a, v[r]);
+    u32x4 o = F::narrow(a);
+#pragma unroll
+    for (int r = 0; r < COLL_MAX_RANKS; r++)
+      if (r < R) st<u32x4>(p.out[r], i, o, nt);
+  }
+}
+
+// One element per thread, any alignment: tails and unaligned buffers.
+template <int DT, int OP>
+__device__ __forceinline__ typename Fmt<DT>::Elem reduce_one(const RankPtrs &p, int R, size_t i) {
+  using F = Fmt<DT>;
+  using E = typename F::Elem;
+  if constexpr (DT == COLL_INT32) {
+    int32_t acc = reinterpret_cast<const int32_t *>(p.in[0])[i];
+    for (int r = 1; r < R; r++) acc = fold_i<OP>(acc, reinterpret_cast<const int32_t *>(p.in[r])[i]);
+    return acc;
+  } else {
+    float acc = F::widen1(reinterpret_cast<const E *>(p.in[0])[i]);
+    for (int r = 1; r < R; r++) acc = fold<OP>(acc, F::widen1(reinterpret_cast<const E *>(p.in[r])[i]));
+    return F::narrow1(acc);
+  }
+}
+
+// Elements [first, first + n) of every rank.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void ar_scalar(RankPtrs p, int R, size_t first, size_t n) {
+  using E = typename Fmt<DT>::Elem;
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t j = (size_t)blockIdx.x * kBlock + threadIdx.x; j < n; j += stride) {
+    size_t i = first + j;
+    E v = reduce_one<DT, OP>(p, R, i);
+    for (int r = 0; r < R; r++) reinterpret_cast<E *>(p.out[r])[i] = v;
+  }
+}
+
+// ------------------------------------------------------------ ReduceScatter
+
+// blockIdx.y = owner rank r: out[r][i] = fold over q of in[q][r*seg + i].
+template <int R, int DT, int OP>
+__global__ __launch_bounds__(kBlock) void rs_vec(RankPtrs p, size_t nvec_seg, int nt) {
+  using F = Fmt<DT>;
+  const int r = blockIdx.y;
+  const size_t base = (size_t)r * nvec_seg;
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec_seg; i += stride) {
+    u32x4 v[R];
+#pragma unroll
+    for (int q = 0; q < R; q++) v[q] = ld<u32x4>(p.in[q], base + i);
+    typename F::Acc a = F::widen(v[0]);
+#pragma unroll
+    for (int q = 1; q < R; q++) F::template fold_in<OP>(a, v[q]);
+    st<u32x4>(p.out[r], i, F::narrow(a), nt);
+  }
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void rs_vec_rt(RankPtrs p, int R, size_t nvec_seg, int nt) {
+  using F = Fmt<DT>;
+  const int r = blockIdx.y;
+  const size_t base = (size_t)r * nvec_seg;
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec_seg; i += stride) {
+    u32x4 v[COLL_MAX_RANKS];
+#pragma unroll
+    for (int q = 0; q < COLL_MAX_RANKS; q++)
+      if (q < R) v[q] = ld<u32x4>(p.in[q], base + i);
+    typename F::Acc a = F::widen(v[0]);
+#pragma unroll
+    for (int q = 1; q < COLL_MAX_RANKS; q++)
+      if (q < R) F::template fold_in<OP>(a, v[q]);
+    st<u32x4>(p.out[r], i, F::narrow(a), nt);
+  }
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void rs_scalar(RankPtrs p, int R, size_t seg) {
+  const int r = blockIdx.y;
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < seg; i += stride)
+    reinterpret_cast<typename Fmt<DT>::Elem *>(p.out[r])[i] = reduce_one<DT, OP>(p, R, (size_t)r * seg + i);
+}
+
+// ------------------------------------------------------------ dispatchers
+
+template <int DT, int OP>
+int ar_dispatch(const Launch &L, int R, const RankPtrs &p, size_t count) {
+  constexpr int VL = Fmt<DT>::kLanes;
+  bool aligned = true;
+  for (int r = 0; r < R; r++) aligned = aligned && aligned16(p.in[r]) && aligned16(p.out[r]);
+  size_t nvec = aligned ? count / VL : 0;
+  size_t tail0 = nvec * VL;
+  int nt = (2 * (size_t)R * count * Fmt<DT>::kSize >= L.nt_bytes) ? 1 : 0;
+  if (nvec) {
+    dim3 grid(grid_for(L, nvec));
+    if constexpr (OP == COLL_SUM) {
+      switch (R) {
+#define COLL_AR_CASE(RR) \
+  case RR: hipLaunchKernelGGL((ar_vec<RR, DT, OP>), grid, dim3(kBlock), 0, L.stream, p, nvec, nt); break;
+        COLL_AR_CASE(1) COLL_AR_CASE(2) COLL_AR_CASE(3) COLL_AR_CASE(4)
+        COLL_AR_CASE(5) COLL_AR_CASE(6) COLL_AR_CASE(7) COLL_AR_CASE(8)
+        COLL_AR_CASE(16)
+#undef COLL_AR_CASE
+        default:
+          hipLaunchKernelGGL((ar_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
+      }
+    } else {
+      hipLaunchKernelGGL((ar_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
+    }
+  }
+  if (count > tail0) {
+    size_t n = count - tail0;
+    hipLaunchKernelGGL((ar_scalar<DT, OP>), dim3(grid_for(L, n)), dim3(kBlock), 0, L.stream,
+                       p, R, tail0, n);
+  }
+  return hip_status();
+}
+
+template <int DT, int OP>
+int rs_dispatch(const Launch &L, int R, const RankPtrs &p, size_t seg) {
+  constexpr int VL = Fmt<DT>::kLanes;
+  bool aligned = (seg % VL) == 0;
+  for (int r = 0; r < R; r++) aligned = aligned && aligned16(p.in[r]) && aligned16(p.out[r]);
+  int nt = ((size_t)(R + 1) * R * seg * Fmt<DT>::kSize >= L.nt_bytes) ? 1 : 0;
+  if (aligned) {
+    size_t nvec = seg / VL;
+    unsigned gx = grid_for(L, nvec * R);
+    gx = (gx + R - 1) / R;
+    dim3 grid(gx, R);
+    if constexpr (OP == COLL_SUM) {
+      switch (R) {
+#define COLL_RS_CASE(RR) \
+  case RR: hipLaunchKernelGGL((rs_vec<RR, DT, OP>), grid, dim3(kBlock), 0, L.stream, p, nvec, nt); break;
+        COLL_RS_CASE(1) COLL_RS_CASE(2) COLL_RS_CASE(3) COLL_RS_CASE(4)
+        COLL_RS_CASE(5) COLL_RS_CASE(6) COLL_RS_CASE(7) COLL_RS_CASE(8)
+        COLL_RS_CASE(16)
+#undef COLL_RS_CASE
+        default:
+          hipLaunchKernelGGL((rs_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
+      }
+    } else {
+      hipLaunchKernelGGL((rs_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
+    }
+  } else {
+    unsigned gx = (grid_for(L, seg * R) + R - 1) / R;
+    hipLaunchKernelGGL((rs_scalar<DT, OP>), dim3(gx, R), dim3(kBlock), 0, L.stream, p, R, seg);
+  }
+  return hip_status();
+}
+
+template <int DT>
+int ar_by_op(const Launch &L, int R, const RankPtrs &p, size_t count, int op) {
+  switch (op) {
+    case COLL_SUM: return ar_dispatch<DT, COLL_SUM>(L, R, p, count);
+    case COLL_PROD: return ar_dispatch<DT, COLL_PROD>(L, R, p, count);
+    case COLL_MAX: return ar_dispatch<DT, COLL_MAX>(L, R, p, count);
+    case COLL_MIN: return ar_dispatch<DT, COLL_MIN>(L, R, p, count);
+  }
+  return COLL_ERR_UNSUPPORTED;
+}
+
+template <int DT>
+int rs_by_op(const Launch &L, int R, const RankPtrs &p, size_t seg, int op) {
+  switch (op) {
+    case COLL_SUM: return rs_dispatch<DT, COLL_SUM>(L, R, p, seg);
+    case COLL_PROD: return rs_dispatch<DT, COLL_PROD>(L, R, p, seg);
+    case COLL_MAX: return rs_dispatch<DT, COLL_MAX>(L, R, p, seg);
+    case COLL_MIN: return rs_dispatch<DT, COLL_MIN>(L, R, p, seg);
+  }
+  return COLL_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int launch_allreduce(const Launch &L, int R, const RankPtrs &p, size_t count, int dt, int op) {
+  switch (dt) {
+    case COLL_BF16: return ar_by_op<COLL_BF16>(L, R, p, count, op);
+    case COLL_FP16: return ar_by_op<COLL_FP16>(L, R, p, count, op);
+    case COLL_FP32: return ar_by_op<COLL_FP32>(L, R, p, count, op);
+    case COLL_INT32: return ar_by_op<COLL_INT32>(L, R, p, count, op);
+  }
+  return COLL_ERR_UNSUPPORTED;
+}
+
+int launch_reduce_scatter(const Launch &L, int R, const RankPtrs &p, size_t seg, int dt, int op) {
+  switch (dt) {
+    case COLL_BF16: return rs_by_op<COLL_BF16>(L, R, p, seg, op);
+    case COLL_FP16: return rs_by_op<COLL_FP16>(L, R, p, seg, op);
+    case COLL_FP32: return rs_by_op<COLL_FP32>(L, R, p, seg, op);
+    case COLL_INT32: return rs_by_op<COLL_INT32>(L, R, p, seg, op);
+  }
+  return COLL_ERR_UNSUPPORTED;
+}
+
+}  // namespace coll

@@ -1,0 +1,205 @@
+/*
+ * coll.h -- C ABI of libcoll.so: collectives over R "virtual ranks" whose
+ * buffers all live in one MI355X's HBM, computed by hand-written gfx950 HIP
+ * kernels.
+ *
+ * A rank here is only a set of device pointers: rank r owns sendbufs[r] and
+ * recvbufs[r].  Every call takes the pointer arrays in HOST memory, copies
+ * them into the kernel arguments before returning, and keeps no reference to
+ * them afterwards.  Device buffers and device count arrays must stay valid
+ * until the work queued on `stream` has finished.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - nranks R is in [1, COLL_MAX_RANKS]; anything else -> COLL_ERR_INVALID_ARG.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    calls are asynchronous: they enqueue kernels and return without a host
+ *    synchronisation.
+ *  - A count of 0 returns COLL_OK and launches nothing.
+ *  - Host-detectable errors (bad R, root, dtype/op, NULL pointer where data is
+ *    needed, a size that overflows) return a negative status and launch
+ *    nothing.  A launch failure returns COLL_ERR_HIP.  No C++ exception ever
+ *    crosses this boundary.
+ *  - The library allocates nothing and holds no state beyond a per-device
+ *    cache of the compute-unit count; calls on different streams are
+ *    independent.  The MoE layout takes caller-provided workspace.
+ *  - Reductions of bf16 / fp16 widen every element exactly to fp32, fold the
+ *    ranks in ascending order 0, 1, ..., R-1 with the accumulator seeded by
+ *    rank 0's value (no FMA, no reassociation), and round once to the output
+ *    type, round-to-nearest-even.  fp32 folds in the same order; int32 wraps.
+ *    The result is therefore bit-identical on every rank and across calls.
+ *  - Element counts are in elements of `dtype`; A2A-v counts are in rows.
+ *
+ * Sources: "Collective primitives tutorial" (gsyq.cn news 307221), sections
+ * 1-8; "From NCCL Ring LL to PCIe IPC AllReduce" (hjcheng0602 blog), section
+ * "Pro5000 ?" for the owner-per-segment AllReduce layout; sglang PR 27492
+ * digest (all_to_all_single: output mutated, world size 1 is a copy); sglang
+ * PR 33307 digest (broadcast from the owner; no host sync on the path).
+ */
+#ifndef COLL_H
+#define COLL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    COLL_OK = 0,
+    COLL_ERR_INVALID_ARG = -1,
+    COLL_ERR_UNSUPPORTED = -2,
+    COLL_ERR_HIP = -3
+} coll_status_t;
+
+typedef enum { COLL_BF16 = 0, COLL_FP16 = 1, COLL_FP32 = 2, COLL_INT32 = 3 } coll_dtype_t;
+
+/* Reduction operators of the tutorial's section 3 (Reduce). */
+typedef enum { COLL_SUM = 0, COLL_PROD = 1, COLL_MAX = 2, COLL_MIN = 3 } coll_op_t;
+
+#define COLL_MAX_RANKS 16
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *coll_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int coll_version(void);
+
+/*
+ * AllReduce -- tutorial section 6 (every rank ends with the same full
+ * reduction), computed in the owner-per-segment layout of the IPC AllReduce
+ * blog ("Pro5000 ?"): the element range is split into tiles; each tile is read
+ * once from all R ranks, reduced once, and the result stored to all R outputs
+ * (ReduceScatter to the tile's owner fused with AllGather from it).
+ *
+ *   sendbufs[r], recvbufs[r]: R device pointers, `count` elements each.
+ *   recvbufs[r] == sendbufs[r] (in place) is allowed; any other overlap is not.
+ *   All ops for all dtypes; MAX/MIN propagate NaN and order -0 below +0.
+ */
+int coll_allreduce(int nranks, const void *const *sendbufs, void *const *recvbufs,
+                   size_t count, coll_dtype_t dtype, coll_op_t op, void *stream);
+
+/*
+ * ReduceScatter -- tutorial section 5: reduce, then rank r keeps chunk r.
+ *   sendbufs[r]: nranks * recvcount elements; recvbufs[r]: recvcount elements.
+ *   recvbufs[r][i] = reduction over q of sendbufs[q][r * recvcount + i].
+ *   In place allowed when recvbufs[r] == sendbufs[r] + r * recvcount elements.
+ */
+int coll_reduce_scatter(int nranks, const void *const *sendbufs, void *const *recvbufs,
+                        size_t recvcount, coll_dtype_t dtype, coll_op_t op, void *stream);
+
+/*
+ * AllGather -- tutorial section 7: concatenation in rank order on every rank.
+ *   sendbufs[q]: sendcount elements; recvbufs[r]: nranks * sendcount elements.
+ *   recvbufs[r][q * sendcount + i] = sendbufs[q][i].  A pure copy: any dtype.
+ *   In place allowed when sendbufs[r] == recvbufs[r] + r * sendcount elements.
+ */
+int coll_all_gather(int nranks, const void *const *sendbufs, void *const *recvbufs,
+                    size_t sendcount, coll_dtype_t dtype, void *stream);
+
+/*
+ * Gather -- tutorial section 2 (2.2.1: vocab-sharded logits collected on dst 0):
+ * each rank's row-major [outer, inner] block is concatenated along the LAST
+ * axis onto the root, giving [outer, nranks * inner]:
+ *   recvbuf_root[o * nranks * inner + q * inner + i] = sendbufs[q][o * inner + i].
+ * Only the root's buffer is written (the other ranks receive nothing, as the
+ * tutorial's non-dst ranks get None).  recvbuf_root must not overlap any send
+ * buffer.  A dim-0 concatenation is outer = 1.
+ */
+int coll_gather(int nranks, const void *const *sendbufs, void *recvbuf_root, int root,
+                size_t outer, size_t inner, coll_dtype_t dtype, void *stream);
+
+/*
+ * Broadcast -- tutorial section 1: every rank ends with root's `count`
+ * elements, bit for bit.  recvbufs[r] may equal sendbuf_root for r == root
+ * (the owner keeps its own tensor, as in the sglang PR 33307 digest); that
+ * buffer is then not written.  recvbufs[r] may be NULL for r == root only.
+ */
+int coll_broadcast(int nranks, const void *sendbuf_root, void *const *recvbufs, int root,
+                   size_t count, coll_dtype_t dtype, void *stream);
+
+/*
+ * All-to-All-v -- tutorial sections 8.1-8.2: rank s sends a distinct, variable
+ * length block to every rank d; d's receive buffer holds the blocks ordered by
+ * source.  Units are rows of `row_elems` elements of `dtype`.
+ *   sendcounts[s * R + d]: rows s sends to d            (DEVICE int64, R*R)
+ *   sdispls   [s * R + d]: first such row in sendbufs[s] (DEVICE int64, R*R)
+ *   rdispls   [d * R + s]: where they land in recvbufs[d] (DEVICE int64, R*R)
+ *   recvbufs[d][(rdispls[d*R+s] + j) * row_elems + c]
+ *        = sendbufs[s][(sdispls[s*R+d] + j) * row_elems + c],  j < sendcounts[s*R+d].
+ * Counts live on the device so a layout kernel can feed this call with no
+ * host synchronisation; consequently they are not validated on the host: the
+ * caller guarantees every block lies inside its buffers and receive blocks do
+ * not overlap.  Send and receive buffers must not overlap.
+ * The reverse exchange (MoE combine) is the same call with the count matrix
+ * transposed and the two displacement tables swapped.
+ */
+int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *sendcounts,
+                      const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
+                      size_t row_elems, coll_dtype_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * MoE dispatch / combine over expert parallelism -- tutorial section 8.4.
+ * Experts are placed on ranks in contiguous blocks: rank d owns experts
+ * [d*E/R, (d+1)*E/R); E must be a multiple of R.  Each (token t, slot k) pair
+ * is one dispatched row; rows bound for a rank are ordered stably by
+ * (expert, t, k), so within a source's send buffer the rows are sorted by
+ * expert.  topk_ids are int32 in [0, E) (out-of-range ids are the caller's
+ * error: they are not checked on the device).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace coll_moe_layout needs (0 on invalid sizes). */
+size_t coll_moe_workspace_bytes(int nranks, int tokens, int topk, int n_experts);
+
+/*
+ * Layout: from R device arrays topk_ids[s] (int32 [tokens, topk]) compute
+ *   sendcounts[s*R+d], sdispls[s*R+d], rdispls[d*R+s]  (DEVICE int64, R*R each),
+ *   expert_counts[s*E+e]  rows of expert e from source s (DEVICE int32, R*E),
+ *   pos[s][t*topk+k]      slot of (t,k) in source s's send buffer (DEVICE int32).
+ * Uses `workspace` (coll_moe_workspace_bytes, 256-byte aligned, device).
+ * Supports n_experts <= 1024 and tokens * topk < 2^31.
+ */
+int coll_moe_layout(int nranks, const int32_t *const *topk_ids, int tokens, int topk,
+                    int n_experts, int64_t *sendcounts, int64_t *sdispls, int64_t *rdispls,
+                    int32_t *expert_counts, int32_t *const *pos, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * Dispatch permute (an indexed write; the tutorial's 4.3.2 warns it is not the
+ * Scatter collective): sendbufs[s][pos[s][t*topk+k]] = x[s][t] for every k.
+ * x[s]: [tokens, hidden]; sendbufs[s]: [tokens*topk, hidden].  Any dtype.
+ */
+int coll_moe_permute(int nranks, const void *const *x, const int32_t *const *pos,
+                     int tokens, int topk, size_t hidden, coll_dtype_t dtype,
+                     void *const *sendbufs, void *stream);
+
+/*
+ * Test expert used to exercise the round trip: each received bf16 row of
+ * expert e becomes y = rne(x * (1 + e/256)) in place (the fp32 product is
+ * exact, so y is unique).  Row order in recvbufs[d] is: for s ascending,
+ * starting at rdispls[d*R+s], the rows of d's experts in ascending expert
+ * order, expert_counts[s*E+e] rows each.
+ */
+int coll_moe_expert_scale(int nranks, void *const *recvbufs, const int32_t *expert_counts,
+                          const int64_t *rdispls, int n_experts, size_t hidden,
+                          coll_dtype_t dtype, void *stream);
+
+/*
+ * Combine (results return to the token's owner and are gate-weighted):
+ *   out[s][t] = rne( sum_{k=0..topk-1} w[s][t*topk+k] * widen(back[s][pos[s][t*topk+k]]) )
+ * with k ascending, the accumulator seeded by the k = 0 product, multiply and
+ * add rounded separately (no FMA) and one final rounding: bit-identical to
+ * the fold written out.  back[s]: [tokens*topk, hidden] bf16 in s's send-slot
+ * order (the output of the reverse All-to-All-v); w[s]: fp32 [tokens, topk];
+ * out[s]: bf16 [tokens, hidden], must not overlap back[s].
+ */
+int coll_moe_combine(int nranks, const void *const *back, const int32_t *const *pos,
+                     const float *const *topk_w, int tokens, int topk, size_t hidden,
+                     coll_dtype_t dtype, void *const *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLL_H */

@@ -1,0 +1,113 @@
+"""CPU checks of the C-ABI boundary: the library loads, exports every entry
+point include/coll.h declares, and rejects bad arguments on the host before
+touching the GPU (so these calls are safe without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from collective_communication_amd import coll
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "coll.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coll_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(coll.LIB_PATH):
+        from collective_communication_amd import build
+        build.build()
+    return coll.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    syms = declared_symbols()
+    assert len(syms) >= 13
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(coll.SIGNATURES)
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, 5):
+        assert L.coll_status_string(st)
+
+
+NULL = None
+
+
+@pytest.mark.parametrize("R", [0, -1, 17, 1000])
+def test_rank_count_rejected(L, R):
+    assert L.coll_allreduce(R, NULL, NULL, 8, 0, 0, NULL) == -1
+    assert L.coll_reduce_scatter(R, NULL, NULL, 8, 0, 0, NULL) == -1
+    assert L.coll_all_gather(R, NULL, NULL, 8, 0, NULL) == -1
+    assert L.coll_gather(R, NULL, NULL, 0, 1, 8, 0, NULL) == -1
+    assert L.coll_broadcast(R, NULL, NULL, 0, 8, 0, NULL) == -1
+    assert L.coll_all_to_all_v(R, NULL, NULL, NULL, NULL, NULL, 8, 0, NULL) == -1
+
+
+def test_zero_count_is_a_no_op(L):
+    assert L.coll_allreduce(4, NULL, NULL, 0, 0, 0, NULL) == 0
+    assert L.coll_reduce_scatter(4, NULL, NULL, 0, 0, 0, NULL) == 0
+    assert L.coll_all_gather(4, NULL, NULL, 0, 0, NULL) == 0
+    assert L.coll_gather(4, NULL, NULL, 0, 0, 8, 0, NULL) == 0
+    assert L.coll_broadcast(4, NULL, NULL, 0, 0, 0, NULL) == 0
+    assert L.coll_moe_permute(4, NULL, NULL, 0, 8, 16, 0, NULL, NULL) == 0
+
+
+def test_null_pointers_rejected(L):
+    assert L.coll_allreduce(2, NULL, NULL, 8, 0, 0, NULL) == -1
+    two = (ctypes.c_void_p * 2)(0x1000, 0)          # second rank NULL
+    ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.coll_allreduce(2, two, ok, 8, 0, 0, NULL) == -1
+    assert L.coll_allreduce(2, ok, two, 8, 0, 0, NULL) == -1
+    assert L.coll_broadcast(2, NULL, ok, 0, 8, 0, NULL) == -1
+    assert L.coll_gather(2, ok, NULL, 0, 1, 8, 0, NULL) == -1
+
+
+def test_root_range(L):
+    ok = (ctypes.c_void_p * 4)(0x1000, 0x2000, 0x3000, 0x4000)
+    for root in (-1, 4, 99):
+        assert L.coll_broadcast(4, 0x1000, ok, root, 8, 0, NULL) == -1
+        assert L.coll_gather(4, ok, 0x1000, root, 1, 8, 0, NULL) == -1
+
+
+def test_dtype_and_op_rejected(L):
+    assert L.coll_allreduce(2, NULL, NULL, 8, 7, 0, NULL) == -1
+    assert L.coll_allreduce(2, NULL, NULL, 8, 0, 9, NULL) == -2
+    assert L.coll_reduce_scatter(2, NULL, NULL, 8, 0, -1, NULL) == -2
+    assert L.coll_moe_expert_scale(2, NULL, NULL, NULL, 4, 8, 2, NULL) == -2   # fp32
+    assert L.coll_moe_combine(2, NULL, NULL, NULL, 4, 2, 8, 1, NULL, NULL) == -2
+
+
+def test_size_overflow_rejected(L):
+    ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.coll_allreduce(2, ok, ok, 1 << 62, 0, 0, NULL) == -1
+
+
+def test_moe_workspace_and_layout_validation(L):
+    assert L.coll_moe_workspace_bytes(8, 4096, 8, 256) > 8 * 256 * 4
+    assert L.coll_moe_workspace_bytes(8, 4096, 8, 250) == 0      # E % R != 0
+    assert L.coll_moe_workspace_bytes(8, 4096, 8, 2048) == 0     # E > 1024
+    assert L.coll_moe_workspace_bytes(8, 1 << 28, 8, 256) == 0   # T*K >= 2^31
+    assert L.coll_moe_workspace_bytes(3, 10, 0, 3) == 0
+    # workspace too small -> rejected before any launch
+    t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.coll_moe_layout(2, t, 10, 2, 4, 0x100, 0x200, 0x300, 0x400, t, 0x1000, 16, NULL) == -1
+    # misaligned workspace
+    need = L.coll_moe_workspace_bytes(2, 10, 2, 4)
+    assert L.coll_moe_layout(2, t, 10, 2, 4, 0x100, 0x200, 0x300, 0x400, t, 0x1008, need, NULL) == -1
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(coll, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(coll, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        coll.lib()
