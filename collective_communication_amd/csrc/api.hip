@@ -167,8 +167,12 @@ int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcou
   if (row_elems == 0) return COLL_OK;
   if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
     return COLL_ERR_INVALID_ARG;
+  if (!sendbufs || !recvbufs) return COLL_ERR_INVALID_ARG;
   RankPtrs p{};
-  if (!fill_in(R, sendbufs, p.in) || !fill_out(R, recvbufs, p.out)) return COLL_ERR_INVALID_ARG;
+  for (int r = 0; r < R; r++) {       // NULL is allowed: a rank that moves no rows
+    p.in[r] = sendbufs[r];
+    p.out[r] = recvbufs[r];
+  }
   return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls,
                      row_elems * dtype_size(dtype));
 }

@@ -131,7 +131,9 @@ int coll_broadcast(int nranks, const void *sendbuf_root, void *const *recvbufs, 
  * Counts live on the device so a layout kernel can feed this call with no
  * host synchronisation; consequently they are not validated on the host: the
  * caller guarantees every block lies inside its buffers and receive blocks do
- * not overlap.  Send and receive buffers must not overlap.
+ * not overlap.  Send and receive buffers must not overlap.  A rank that sends
+ * (or receives) no rows may pass NULL for its buffer; the arrays themselves
+ * must not be NULL.
  * The reverse exchange (MoE combine) is the same call with the count matrix
  * transposed and the two displacement tables swapped.
  */

@@ -111,3 +111,12 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(coll, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         coll.lib()
+
+
+def test_a2av_null_arrays_rejected_but_null_entries_allowed_on_host(L):
+    # the pointer arrays themselves are required
+    assert L.coll_all_to_all_v(2, NULL, 0x10, 0x20, NULL, 0x30, 8, 0, NULL) == -1
+    # device count tables are required
+    ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.coll_all_to_all_v(2, ok, NULL, 0x20, ok, 0x30, 8, 0, NULL) == -1
+    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, NULL, 8, 0, NULL) == -1
