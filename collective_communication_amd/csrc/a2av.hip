@@ -18,13 +18,6 @@
 namespace coll {
 namespace {
 
-template <int B> struct AUnit;
-template <> struct AUnit<16> { typedef u32x4 T; };
-template <> struct AUnit<8> { typedef u32x2 T; };
-template <> struct AUnit<4> { typedef uint32_t T; };
-template <> struct AUnit<2> { typedef uint16_t T; };
-template <> struct AUnit<1> { typedef uint8_t T; };
-
 constexpr int kMaxBlocks = COLL_MAX_RANKS * COLL_MAX_RANKS;   // 256
 
 // Inclusive prefix sum across one wave64 (Hillis-Steele over lanes).
@@ -38,12 +31,23 @@ __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
   return x;
 }
 
-template <int B>
+// Global-address-space views of an integer address (so the compiler emits
+// global_load / global_store rather than flat accesses).
+template <class U>
+__device__ __forceinline__ const __attribute__((address_space(1))) U *gconst(uint64_t a) {
+  return (const __attribute__((address_space(1))) U *)a;
+}
+template <class U>
+__device__ __forceinline__ __attribute__((address_space(1))) U *gmut(uint64_t a) {
+  return (__attribute__((address_space(1))) U *)a;
+}
+
+template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const int64_t *counts,
                                                       const int64_t *sdispls,
-                                                      const int64_t *rdispls, uint64_t row_units,
-                                                      int nt) {
-  using U = typename AUnit<B>::T;
+                                                      const int64_t *rdispls, uint64_t row_units) {
+  using U = typename UnitT<B>::T;
+  constexpr int UN = kCopyU;
   __shared__ uint64_t s_end[kMaxBlocks];   // inclusive end of block b in the global unit space
   __shared__ uint64_t s_src[kMaxBlocks];   // src unit address minus block start (in units)
   __shared__ uint64_t s_dst[kMaxBlocks];
@@ -56,23 +60,23 @@ __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const i
     uint64_t local = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      int b = lane * 4 + j;
+      const int b = lane * 4 + j;
       len[j] = 0;
       if (b < nb) {
-        int64_t c = counts[b];
+        const int64_t c = counts[b];
         len[j] = c > 0 ? (uint64_t)c * row_units : 0;
       }
       local += len[j];
     }
-    uint64_t incl = wave_incl_scan(local);
+    const uint64_t incl = wave_incl_scan(local);
     uint64_t start = incl - local;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      int b = lane * 4 + j;
+      const int b = lane * 4 + j;
       if (b < nb) {
-        int s = b / R, d = b - s * R;
-        uint64_t so = (uint64_t)sdispls[b] * row_units;
-        uint64_t ro = (uint64_t)rdispls[d * R + s] * row_units;
+        const int s = b / R, d = b - s * R;
+        const uint64_t so = (uint64_t)sdispls[b] * row_units;
+        const uint64_t ro = (uint64_t)rdispls[d * R + s] * row_units;
         s_src[b] = reinterpret_cast<uintptr_t>(p.in[s]) / B + so - start;
         s_dst[b] = reinterpret_cast<uintptr_t>(p.out[d]) / B + ro - start;
         start += len[j];
@@ -85,23 +89,39 @@ __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const i
   const uint64_t total = s_end[nb - 1];
   int top = 1;
   while (top * 2 <= nb) top *= 2;            // largest power of two <= nb
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  const uint64_t tile = (uint64_t)kBlock * UN;
   int b = 0;
-  for (uint64_t v = (uint64_t)blockIdx.x * kBlock + threadIdx.x; v < total; v += stride) {
-    if (v >= s_end[b] || (b > 0 && v < s_end[b - 1])) {
-      // b = number of blocks that end at or before v
-      int lo = 0;
-      for (int step = top; step > 0; step >>= 1) {
-        int c = lo + step;
-        if (c <= nb && s_end[c - 1] <= v) lo = c;
+  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
+       base += (uint64_t)gridDim.x * tile) {
+    U v[UN];
+    uint64_t dst[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t x = base + (uint64_t)u * kBlock;
+      if (x < total) {
+        if (x >= s_end[b] || (b > 0 && x < s_end[b - 1])) {
+          int lo = 0;                           // blocks ending at or before x
+          for (int step = top; step > 0; step >>= 1) {
+            const int c = lo + step;
+            if (c <= nb && s_end[c - 1] <= x) lo = c;
+          }
+          b = lo;
+        }
+        const auto *src = gconst<U>((s_src[b] + x) * B);
+        dst[u] = (s_dst[b] + x) * B;
+        if constexpr (NT) v[u] = __builtin_nontemporal_load(src);
+        else v[u] = *src;
       }
-      b = lo;
     }
-    const U *src = reinterpret_cast<const U *>((s_src[b] + v) * B);
-    U *dst = reinterpret_cast<U *>((s_dst[b] + v) * B);
-    U x = *src;
-    if (nt) __builtin_nontemporal_store(x, dst);
-    else *dst = x;
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t x = base + (uint64_t)u * kBlock;
+      if (x < total) {
+        auto *d = gmut<U>(dst[u]);
+        if constexpr (NT) __builtin_nontemporal_store(v[u], d);
+        else *d = v[u];
+      }
+    }
   }
 }
 
@@ -111,19 +131,13 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
                 const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes) {
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
-  int unit = copy_unit(bits);
-  uint64_t row_units = row_bytes / unit;
+  const int unit = copy_unit(bits);
+  const uint64_t row_units = row_bytes / unit;
   // The total is only known on the device: launch the resident grid and let
-  // the grid-stride loop cover whatever the counts say.
-  dim3 grid((unsigned)L.num_cus * L.wgs_per_cu);
-  int nt = L.a2a_nt;
-  switch (unit) {
-    case 16: hipLaunchKernelGGL(a2av_kernel<16>, grid, dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, row_units, nt); break;
-    case 8: hipLaunchKernelGGL(a2av_kernel<8>, grid, dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, row_units, nt); break;
-    case 4: hipLaunchKernelGGL(a2av_kernel<4>, grid, dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, row_units, nt); break;
-    case 2: hipLaunchKernelGGL(a2av_kernel<2>, grid, dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, row_units, nt); break;
-    default: hipLaunchKernelGGL(a2av_kernel<1>, grid, dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, row_units, nt); break;
-  }
+  // the tile-stride loop cover whatever the counts say.
+  dim3 grid(grid_resident(L));
+  COLL_UNIT_SWITCH(a2av_kernel, unit, L.a2a_nt, grid, L.stream, p, R, counts, sdispls, rdispls,
+                   row_units);
   return hip_status();
 }
 

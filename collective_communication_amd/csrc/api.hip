@@ -46,9 +46,9 @@ Launch launch_ctx(void *stream) {
   L.num_cus = g_dev[dev].num_cus;
   long w = env_long("COLL_WGS_PER_CU", 8);
   L.wgs_per_cu = (int)(w < 1 ? 1 : (w > 64 ? 64 : w));
-  long nt = env_long("COLL_NT_MIN_BYTES", 1L << 62);
+  long nt = env_long("COLL_NT_MIN_BYTES", 32L << 20);
   L.nt_bytes = nt < 0 ? 0 : (size_t)nt;
-  L.a2a_nt = env_long("COLL_A2A_NT", 0) ? 1 : 0;
+  L.a2a_nt = env_long("COLL_A2A_NT", 1) ? 1 : 0;
   return L;
 }
 

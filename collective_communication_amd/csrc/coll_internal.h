@@ -39,19 +39,31 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------ vector memory
 
-template <class U>
+// Streaming loads and stores.  NT = non-temporal (the "nt" cache policy):
+// data moved once is not kept in the caches, which on MI355X lifts a plain
+// copy from ~5.5 to ~6.2 TB/s when BOTH sides are non-temporal.
+template <class U, bool NT = false>
 __device__ __forceinline__ U ld(const void *base, size_t i) {
-  return reinterpret_cast<const U *>(base)[i];
+  const U *p = reinterpret_cast<const U *>(base) + i;
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
 
-template <class U>
-__device__ __forceinline__ void st(void *base, size_t i, U v, bool nt) {
+template <class U, bool NT = false>
+__device__ __forceinline__ void st(void *base, size_t i, U v) {
   U *p = reinterpret_cast<U *>(base) + i;
-  if (nt)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
+
+// Work decomposition shared by the streaming kernels: a workgroup owns a tile
+// of kBlock * U consecutive units (lane l takes units l, l + kBlock, ...,
+// so every load and store instruction of a wave covers 64 consecutive units),
+// issues all of the tile's loads before any store, and the grid has one
+// workgroup per tile (a single pass: the dispatcher balances the load).
+// Measured on MI355X for a plain 1 GiB copy: 16 KiB tiles (U = 4 x 16 B),
+// non-temporal both ways, reach ~6.2-6.4 TB/s.
+constexpr int kCopyU = 4;
 
 // ------------------------------------------------ element formats (exact widening)
 
@@ -244,28 +256,86 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
 
+// The same for 64-bit numerators n < 2^63: m = floor(2^64 (2^s - d) / d) + 1.
+struct FastDiv64 {
+  uint64_t d, m;
+  uint32_t s;
+};
+
+inline FastDiv64 make_fastdiv64(uint64_t d) {
+  FastDiv64 f;
+  f.d = d;
+  uint32_t s = 0;
+  while (s < 64 && (((unsigned __int128)1) << s) < d) s++;
+  f.s = s;
+  const unsigned __int128 one = 1;
+  f.m = (uint64_t)(((one << 64) * ((one << s) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint64_t fdiv64(uint64_t n, const FastDiv64 &f) {
+  return (__umul64hi(n, f.m) + n) >> f.s;
+}
+
+// ----------------------------------------------------------- copy units
+// Widest power-of-two unit (<= 16 bytes) a copy can use, as a type.
+template <int B> struct UnitT;
+template <> struct UnitT<16> { typedef u32x4 T; };
+template <> struct UnitT<8> { typedef u32x2 T; };
+template <> struct UnitT<4> { typedef uint32_t T; };
+template <> struct UnitT<2> { typedef uint16_t T; };
+template <> struct UnitT<1> { typedef uint8_t T; };
+
+// Launch KERNEL<unit, nt> for a unit size and cache policy chosen at run time.
+#define COLL_UNIT_SWITCH(KERNEL, UNIT, NT, GRID, STREAM, ...)                                    \
+  do {                                                                                         \
+    if (NT) {                                                                                  \
+      switch (UNIT) {                                                                          \
+        case 16: hipLaunchKernelGGL((KERNEL<16, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break; \
+        case 8: hipLaunchKernelGGL((KERNEL<8, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
+        case 4: hipLaunchKernelGGL((KERNEL<4, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
+        case 2: hipLaunchKernelGGL((KERNEL<2, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
+        default: hipLaunchKernelGGL((KERNEL<1, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;  \
+      }                                                                                        \
+    } else {                                                                                   \
+      switch (UNIT) {                                                                          \
+        case 16: hipLaunchKernelGGL((KERNEL<16, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break; \
+        case 8: hipLaunchKernelGGL((KERNEL<8, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
+        case 4: hipLaunchKernelGGL((KERNEL<4, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
+        case 2: hipLaunchKernelGGL((KERNEL<2, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
+        default: hipLaunchKernelGGL((KERNEL<1, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;  \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
+
 // ----------------------------------------------------------- launch helpers
 
 struct Launch {
   hipStream_t stream;
   int num_cus;       // compute units of the current device
-  int wgs_per_cu;    // resident workgroups per CU for grid-stride kernels
-  size_t nt_bytes;   // bytes moved at or above which stores are non-temporal
-  int a2a_nt;        // non-temporal stores in All-to-All-v (size unknown on the host)
+  int wgs_per_cu;    // workgroups per CU for persistent (device-sized) kernels
+  size_t nt_bytes;   // bytes moved at or above which loads/stores are non-temporal
+  int a2a_nt;        // non-temporal loads/stores in All-to-All-v (size unknown on the host)
 };
 
 // Device properties and tuning knobs (environment: COLL_WGS_PER_CU,
 // COLL_NT_MIN_BYTES, COLL_A2A_NT), read once per device.
 Launch launch_ctx(void *stream);
 
-// Blocks for a grid-stride loop over `work` items of kBlock*per_thread each:
-// a single pass when that fits the resident grid, else the resident grid.
+// One workgroup per tile of kBlock * per_thread units (single pass), capped
+// at 2^31 - 1 workgroups; kernels still loop in case the cap binds.
 inline unsigned grid_for(const Launch &L, size_t work, int per_thread = 1) {
+  (void)L;
   size_t per_block = (size_t)kBlock * per_thread;
   size_t need = (work + per_block - 1) / per_block;
-  size_t cap = (size_t)L.num_cus * L.wgs_per_cu;
   if (need < 1) need = 1;
-  return (unsigned)(need < cap ? need : cap);
+  if (need > 0x7FFFFFFFu) need = 0x7FFFFFFFu;
+  return (unsigned)need;
+}
+
+// Resident grid for kernels whose amount of work is only known on the device.
+inline unsigned grid_resident(const Launch &L) {
+  return (unsigned)L.num_cus * (unsigned)L.wgs_per_cu;
 }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }

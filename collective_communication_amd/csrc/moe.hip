@@ -180,109 +180,129 @@ __global__ __launch_bounds__(kBlock) void moe_pos(PtrTable ids, MutPtrTable pos,
 
 // ------------------------------------------------------------------ permute
 
-template <int B> struct MUnit;
-template <> struct MUnit<16> { typedef u32x4 T; };
-template <> struct MUnit<8> { typedef u32x2 T; };
-template <> struct MUnit<4> { typedef uint32_t T; };
-template <> struct MUnit<2> { typedef uint16_t T; };
-template <> struct MUnit<1> { typedef uint8_t T; };
-
-template <int B>
+// blockIdx.y = source s; flattened over (token, unit) of x[s].  A tile's units
+// are loaded once, then each is stored to its K slots.
+template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void moe_permute_kernel(PtrTable x, PtrTable pos,
-                                                             MutPtrTable send, uint32_t total,
-                                                             FastDiv upr, int K, uint32_t TK) {
-  using U = typename MUnit<B>::T;
+                                                             MutPtrTable send, uint64_t total,
+                                                             FastDiv64 upr, int K, uint32_t TK) {
+  using U = typename UnitT<B>::T;
+  constexpr int UN = kCopyU;
   const int s = blockIdx.y;
-  const U *src = reinterpret_cast<const U *>(x.p[s]);
+  const void *src = x.p[s];
   const int32_t *ps = reinterpret_cast<const int32_t *>(pos.p[s]);
-  U *dst = reinterpret_cast<U *>(send.p[s]);
-  const uint32_t stride = gridDim.x * kBlock;
-  for (uint32_t j = blockIdx.x * kBlock + threadIdx.x; j < total; j += stride) {
-    const uint32_t t = fdiv(j, upr);
-    const uint32_t v = j - t * upr.d;
-    const U val = src[j];
-    const int32_t *pk = ps + (size_t)t * K;
-    for (int k = 0; k < K; k++) {
-      const int32_t slot = pk[k];
-      if ((uint32_t)slot < TK) dst[(size_t)slot * upr.d + v] = val;   // never write outside
+  void *dst = send.p[s];
+  const uint64_t tile = (uint64_t)kBlock * UN;
+  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
+       base += (uint64_t)gridDim.x * tile) {
+    U val[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t j = base + (uint64_t)u * kBlock;
+      if (j < total) val[u] = ld<U, NT>(src, j);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t j = base + (uint64_t)u * kBlock;
+      if (j < total) {
+        const uint64_t t = fdiv64(j, upr);
+        const uint64_t v = j - t * upr.d;
+        const int32_t *pk = ps + t * K;
+        for (int k = 0; k < K; k++) {
+          const int32_t slot = pk[k];
+          if ((uint32_t)slot < TK) st<U, NT>(dst, (uint64_t)slot * upr.d + v, val[u]);   // never write outside
+        }
+      }
     }
   }
 }
 
 // ------------------------------------------------------------- test expert
 
+// Receive-order entry table shared by every destination: entry
+// j = d*E + s*per + el covers the rows of expert d*per + el sent by s to d.
+// s_end[j] = inclusive prefix of the row counts over all entries, so one
+// global row index addresses every received row of every rank, and the work
+// is balanced over ranks however skewed the routing is.
+
 // G = bf16 elements per unit (8: 16-byte vectors; 1: scalar fallback)
-template <int G>
+template <int G, bool NT>
 __global__ __launch_bounds__(kBlock) void moe_expert_scale_kernel(MutPtrTable recv, int R, int E,
                                                                   const int32_t *expert_counts,
                                                                   const int64_t *rdispls,
-                                                                  uint32_t upr) {
-  __shared__ uint32_t s_end[kMaxExperts];     // inclusive end (rows) of entry j
-  __shared__ int64_t s_base[kMaxExperts];     // receive row = s_base[j] + global row
-  const int d = blockIdx.y;
+                                                                  FastDiv64 upr) {
+  HIP_DYNAMIC_SHARED(uint32_t, s_end);          // R * E entries (launch-time size)
+  __shared__ uint32_t wsum[kBlock / 64];
   const int per = E / R;
-  // Wave 0: entries j = s*per + el in receive order (source, then expert)
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int chunk = (E + 63) / 64;           // entries per lane (<= 16)
-    int local = 0;
-    for (int c = 0; c < chunk; c++) {
-      int j = lane * chunk + c;
-      if (j < E) {
-        int s = j / per, el = j - s * per;
-        local += expert_counts[(size_t)s * E + d * per + el];
-      }
-    }
-    int incl = wave_incl_scan_i32(local);
-    int start = incl - local;
-    for (int c = 0; c < chunk; c++) {
-      int j = lane * chunk + c;
-      if (j < E) {
-        int s = j / per, el = j - s * per;
-        start += expert_counts[(size_t)s * E + d * per + el];
-        s_end[j] = start;
-      }
+  const int N = R * E;
+  // block-wide scan: thread t owns a contiguous chunk of entries
+  const int chunk = (N + kBlock - 1) / kBlock;
+  const int j0 = threadIdx.x * chunk;
+  uint32_t local = 0;
+  for (int c = 0; c < chunk; c++) {
+    const int j = j0 + c;
+    if (j < N) {
+      const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
+      local += (uint32_t)expert_counts[(size_t)s * E + d * per + el];
     }
   }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t incl = (uint32_t)wave_incl_scan_i32((int)local);
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  // s_base needs the global start of each source's first entry
-  for (int j = threadIdx.x; j < E; j += kBlock) {
-    int s = j / per;
-    int first = s * per;
-    uint32_t gstart = first == 0 ? 0u : s_end[first - 1];
-    s_base[j] = rdispls[d * R + s] - (int64_t)gstart;
+  uint32_t before = 0;
+  for (int q = 0; q < w; q++) before += wsum[q];
+  uint32_t run = before + incl - local;
+  for (int c = 0; c < chunk; c++) {
+    const int j = j0 + c;
+    if (j < N) {
+      const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
+      run += (uint32_t)expert_counts[(size_t)s * E + d * per + el];
+      s_end[j] = run;
+    }
   }
   __syncthreads();
 
-  const uint32_t nrows = s_end[E - 1];
+  const uint64_t nrows = s_end[N - 1];
+  const uint64_t total = nrows * upr.d;
   int top = 1;
-  while (top * 2 <= E) top *= 2;
-  const int lane = threadIdx.x & 63;
-  const uint32_t nwaves = gridDim.x * (kBlock / 64);
-  uint16_t *y = reinterpret_cast<uint16_t *>(recv.p[d]);
-  for (uint32_t g = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6); g < nrows; g += nwaves) {
-    int lo = 0;
-    for (int step = top; step > 0; step >>= 1) {
-      int c = lo + step;
-      if (c <= E && s_end[c - 1] <= g) lo = c;
-    }
-    const int e = d * per + (lo - (lo / per) * per);
-    const float scale = 1.0f + (float)e / 256.0f;
-    const size_t row = (size_t)(s_base[lo] + g);
-    if constexpr (G == 8) {
-      u32x4 *p = reinterpret_cast<u32x4 *>(y + row * upr * 8);
-      for (uint32_t u = lane; u < upr; u += 64) {
-        u32x4 v = p[u];
+  while (top * 2 <= N) top *= 2;
+  int jc = 0;                                   // cached entry
+  constexpr int UN = 2;
+  const uint64_t tile = (uint64_t)kBlock * UN;
+  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
+       base += (uint64_t)gridDim.x * tile) {
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t x = base + (uint64_t)u * kBlock;
+      if (x >= total) continue;
+      const uint64_t g = fdiv64(x, upr);        // global row
+      const uint64_t unit = x - g * upr.d;
+      if (g >= s_end[jc] || (jc > 0 && g < s_end[jc - 1])) {
+        int lo = 0;
+        for (int step = top; step > 0; step >>= 1) {
+          const int c = lo + step;
+          if (c <= N && s_end[c - 1] <= g) lo = c;
+        }
+        jc = lo;
+      }
+      const int d = jc / E, rem = jc - d * E, s = rem / per, el = rem - s * per;
+      const int e = d * per + el;
+      const int first = d * E + s * per;        // first entry of (d, s)
+      const uint64_t gstart = first == 0 ? 0 : s_end[first - 1];
+      const uint64_t row = (uint64_t)rdispls[d * R + s] + (g - gstart);
+      const float scale = 1.0f + (float)e / 256.0f;
+      void *y = recv.p[d];
+      if constexpr (G == 8) {
+        const u32x4 v = ld<u32x4, NT>(y, row * upr.d + unit);
         u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-          o[q] = pack_bf16(bf16_lo(v[q]) * scale, bf16_hi(v[q]) * scale);
-        p[u] = o;
+        for (int q = 0; q < 4; q++) o[q] = pack_bf16(bf16_lo(v[q]) * scale, bf16_hi(v[q]) * scale);
+        st<u32x4, NT>(y, row * upr.d + unit, o);
+      } else {
+        uint16_t *p = reinterpret_cast<uint16_t *>(y) + row * upr.d + unit;
+        *p = (uint16_t)(pack_bf16(bf16_lo(*p) * scale, 0.0f) & 0xFFFFu);
       }
-    } else {
-      uint16_t *p = y + row * upr;
-      for (uint32_t u = lane; u < upr; u += 64)
-        p[u] = (uint16_t)(pack_bf16(bf16_lo(p[u]) * scale, 0.0f) & 0xFFFFu);
     }
   }
 }
@@ -295,12 +315,15 @@ __device__ __forceinline__ uint32_t slot_of(int32_t p, uint32_t TK) {
   return (uint32_t)p < TK ? (uint32_t)p : 0u;
 }
 
-template <int G>
+// One wave per token (blockIdx.y = source s); lanes stride over the row's
+// 16-byte units, two units per lane per step, each gathering its K rows.
+template <int G, bool NT>
 __global__ __launch_bounds__(kBlock) void moe_combine_kernel(PtrTable back, PtrTable pos,
                                                              PtrTable wts, MutPtrTable out,
                                                              int T, int K, uint32_t upr) {
+  constexpr int kChunk = 8;                    // gathered rows in flight per unit
+  constexpr int UN = 2;
   const uint32_t TK = (uint32_t)T * (uint32_t)K;
-  constexpr int kChunk = 8;                    // gathered rows in flight per lane
   const int s = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const uint16_t *bk = reinterpret_cast<const uint16_t *>(back.p[s]);
@@ -312,37 +335,55 @@ __global__ __launch_bounds__(kBlock) void moe_combine_kernel(PtrTable back, PtrT
     const int tu = __builtin_amdgcn_readfirstlane(t);
     const int32_t *pk = ps + (size_t)tu * K;
     const float *wk = ws + (size_t)tu * K;
-    for (uint32_t u = lane; u < upr; u += 64) {
-      if constexpr (G == 8) {
-        float acc[8];
+    if constexpr (G == 8) {
+      for (uint32_t u0 = lane; u0 < upr; u0 += 64 * UN) {
+        float acc[UN][8];
         for (int k0 = 0; k0 < K; k0 += kChunk) {
-          u32x4 v[kChunk];
+          u32x4 v[UN][kChunk];
 #pragma unroll
-          for (int c = 0; c < kChunk; c++)
-            if (k0 + c < K)
-              v[c] = reinterpret_cast<const u32x4 *>(bk + (size_t)slot_of(pk[k0 + c], TK) * upr * 8)[u];
+          for (int c = 0; c < kChunk; c++) {
+            if (k0 + c < K) {
+              const uint16_t *row = bk + (size_t)slot_of(pk[k0 + c], TK) * upr * 8;
+#pragma unroll
+              for (int uu = 0; uu < UN; uu++) {
+                const uint32_t u = u0 + uu * 64;
+                if (u < upr) v[uu][c] = ld<u32x4, NT>(row, u);
+              }
+            }
+          }
 #pragma unroll
           for (int c = 0; c < kChunk; c++) {
             if (k0 + c < K) {
               const float wgt = wk[k0 + c];
 #pragma unroll
-              for (int q = 0; q < 4; q++) {
-                float lo = wgt * bf16_lo(v[c][q]);
-                float hi = wgt * bf16_hi(v[c][q]);
-                if (k0 + c == 0) { acc[2 * q] = lo; acc[2 * q + 1] = hi; }
-                else { acc[2 * q] = acc[2 * q] + lo; acc[2 * q + 1] = acc[2 * q + 1] + hi; }
+              for (int uu = 0; uu < UN; uu++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                  const float lo = wgt * bf16_lo(v[uu][c][q]);
+                  const float hi = wgt * bf16_hi(v[uu][c][q]);
+                  if (k0 + c == 0) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
+                  else { acc[uu][2 * q] = acc[uu][2 * q] + lo; acc[uu][2 * q + 1] = acc[uu][2 * q + 1] + hi; }
+                }
               }
             }
           }
         }
-        u32x4 r;
 #pragma unroll
-        for (int q = 0; q < 4; q++) r[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
-        reinterpret_cast<u32x4 *>(o + (size_t)tu * upr * 8)[u] = r;
-      } else {
+        for (int uu = 0; uu < UN; uu++) {
+          const uint32_t u = u0 + uu * 64;
+          if (u < upr) {
+            u32x4 r;
+#pragma unroll
+            for (int q = 0; q < 4; q++) r[q] = pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]);
+            st<u32x4, NT>(o + (size_t)tu * upr * 8, u, r);
+          }
+        }
+      }
+    } else {
+      for (uint32_t u = lane; u < upr; u += 64) {
         float acc = 0.0f;
         for (int k = 0; k < K; k++) {
-          float prod = wk[k] * bf16_lo(bk[(size_t)slot_of(pk[k], TK) * upr + u]);
+          const float prod = wk[k] * bf16_lo(bk[(size_t)slot_of(pk[k], TK) * upr + u]);
           acc = (k == 0) ? prod : acc + prod;
         }
         o[(size_t)tu * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
@@ -379,21 +420,14 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)x.p[r] | (uintptr_t)send.p[r];
   const int unit = copy_unit(bits);
-  const size_t upr = row_bytes / unit;
-  const size_t total = (size_t)T * upr;
-  if (total >= (1ull << 31)) return COLL_ERR_UNSUPPORTED;
+  const uint64_t upr = row_bytes / unit;
+  const uint64_t total = (uint64_t)T * upr;
   if (total == 0) return COLL_OK;
-  FastDiv f = make_fastdiv((uint32_t)upr);
-  unsigned gx = (grid_for(L, total * R) + R - 1) / R;
-  dim3 grid(gx, R);
-  uint32_t t32 = (uint32_t)total;
-  switch (unit) {
-    case 16: hipLaunchKernelGGL(moe_permute_kernel<16>, grid, dim3(kBlock), 0, L.stream, x, pos, send, t32, f, K, (uint32_t)(T * K)); break;
-    case 8: hipLaunchKernelGGL(moe_permute_kernel<8>, grid, dim3(kBlock), 0, L.stream, x, pos, send, t32, f, K, (uint32_t)(T * K)); break;
-    case 4: hipLaunchKernelGGL(moe_permute_kernel<4>, grid, dim3(kBlock), 0, L.stream, x, pos, send, t32, f, K, (uint32_t)(T * K)); break;
-    case 2: hipLaunchKernelGGL(moe_permute_kernel<2>, grid, dim3(kBlock), 0, L.stream, x, pos, send, t32, f, K, (uint32_t)(T * K)); break;
-    default: hipLaunchKernelGGL(moe_permute_kernel<1>, grid, dim3(kBlock), 0, L.stream, x, pos, send, t32, f, K, (uint32_t)(T * K)); break;
-  }
+  const FastDiv64 f = make_fastdiv64(upr);
+  const bool nt = (uint64_t)R * total * unit * (1 + K) >= L.nt_bytes;
+  dim3 grid(grid_for(L, total, kCopyU), R);
+  COLL_UNIT_SWITCH(moe_permute_kernel, unit, nt, grid, L.stream, x, pos, send, total, f, K,
+                   (uint32_t)(T * K));
   return hip_status();
 }
 
@@ -402,13 +436,22 @@ int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             size_t hidden) {
   bool vec = (hidden % 8) == 0;
   for (int r = 0; r < R; r++) vec = vec && aligned16(recv.p[r]);
-  dim3 grid((unsigned)((L.num_cus * L.wgs_per_cu + R - 1) / R), R);
-  if (vec)
-    hipLaunchKernelGGL(moe_expert_scale_kernel<8>, grid, dim3(kBlock), 0, L.stream, recv, R, E,
-                       expert_counts, rdispls, (uint32_t)(hidden / 8));
-  else
-    hipLaunchKernelGGL(moe_expert_scale_kernel<1>, grid, dim3(kBlock), 0, L.stream, recv, R, E,
-                       expert_counts, rdispls, (uint32_t)hidden);
+  dim3 grid(grid_resident(L));
+  const bool nt = L.a2a_nt != 0;
+  const size_t lds = (size_t)R * E * sizeof(uint32_t);   // <= 64 KiB (R <= 16, E <= 1024)
+  if (vec) {
+    const FastDiv64 f = make_fastdiv64(hidden / 8);
+    if (nt)
+      hipLaunchKernelGGL((moe_expert_scale_kernel<8, true>), grid, dim3(kBlock), lds, L.stream,
+                         recv, R, E, expert_counts, rdispls, f);
+    else
+      hipLaunchKernelGGL((moe_expert_scale_kernel<8, false>), grid, dim3(kBlock), lds, L.stream,
+                         recv, R, E, expert_counts, rdispls, f);
+  } else {
+    const FastDiv64 f = make_fastdiv64(hidden);
+    hipLaunchKernelGGL((moe_expert_scale_kernel<1, false>), grid, dim3(kBlock), lds, L.stream,
+                       recv, R, E, expert_counts, rdispls, f);
+  }
   return hip_status();
 }
 
@@ -416,17 +459,21 @@ int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTa
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out) {
   bool vec = (hidden % 8) == 0;
   for (int r = 0; r < R; r++) vec = vec && aligned16(back.p[r]) && aligned16(out.p[r]);
-  unsigned gx = (unsigned)((T + 3) / 4);       // one wave per token
-  unsigned cap = (unsigned)((L.num_cus * L.wgs_per_cu + R - 1) / R);
-  if (gx > cap) gx = cap;
+  const unsigned gx = (unsigned)((T + 3) / 4);         // one wave per token
   if (gx == 0) return COLL_OK;
   dim3 grid(gx, R);
-  if (vec)
-    hipLaunchKernelGGL(moe_combine_kernel<8>, grid, dim3(kBlock), 0, L.stream, back, pos, w, out,
-                       T, K, (uint32_t)(hidden / 8));
-  else
-    hipLaunchKernelGGL(moe_combine_kernel<1>, grid, dim3(kBlock), 0, L.stream, back, pos, w, out,
-                       T, K, (uint32_t)hidden);
+  const bool nt = (uint64_t)R * T * (K + 1) * hidden * 2 >= L.nt_bytes;
+  if (vec) {
+    if (nt)
+      hipLaunchKernelGGL((moe_combine_kernel<8, true>), grid, dim3(kBlock), 0, L.stream, back, pos,
+                         w, out, T, K, (uint32_t)(hidden / 8));
+    else
+      hipLaunchKernelGGL((moe_combine_kernel<8, false>), grid, dim3(kBlock), 0, L.stream, back,
+                         pos, w, out, T, K, (uint32_t)(hidden / 8));
+  } else {
+    hipLaunchKernelGGL((moe_combine_kernel<1, false>), grid, dim3(kBlock), 0, L.stream, back, pos,
+                       w, out, T, K, (uint32_t)hidden);
+  }
   return hip_status();
 }
 

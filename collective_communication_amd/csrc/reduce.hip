@@ -21,42 +21,61 @@ namespace {
 
 // ---------------------------------------------------------------- AllReduce
 
-// R known at compile time: all R loads are independent and issued together.
-template <int R, int DT, int OP>
-__global__ __launch_bounds__(kBlock) void ar_vec(RankPtrs p, size_t nvec, int nt) {
+// 16-byte units per lane per tile for an R-way reduction: U * R independent
+// loads in flight per lane without exhausting the VGPR budget.
+template <int R>
+constexpr int red_u() { return R <= 2 ? 4 : (R <= 8 ? 2 : 1); }
+
+// R known at compile time: all U * R loads of a tile issue back to back.
+template <int R, int DT, int OP, bool NT>
+__global__ __launch_bounds__(kBlock) void ar_vec(RankPtrs p, size_t nvec) {
   using F = Fmt<DT>;
-  const size_t stride = (size_t)gridDim.x * kBlock;
-  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec; i += stride) {
-    u32x4 v[R];
+  constexpr int U = red_u<R>();
+  const size_t tile = (size_t)kBlock * U;
+  for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nvec;
+       base += (size_t)gridDim.x * tile) {
+    u32x4 v[U][R];
 #pragma unroll
-    for (int r = 0; r < R; r++) v[r] = ld<u32x4>(p.in[r], i);
-    typename F::Acc a = F::widen(v[0]);
+    for (int u = 0; u < U; u++) {
+      const size_t i = base + (size_t)u * kBlock;
+      if (i < nvec) {
 #pragma unroll
-    for (int r = 1; r < R; r++) F::template fold_in<OP>(a, v[r]);
-    u32x4 o = F::narrow(a);
+        for (int r = 0; r < R; r++) v[u][r] = ld<u32x4, NT>(p.in[r], i);
+      }
+    }
 #pragma unroll
-    for (int r = 0; r < R; r++) st<u32x4>(p.out[r], i, o, nt);
+    for (int u = 0; u < U; u++) {
+      const size_t i = base + (size_t)u * kBlock;
+      if (i < nvec) {
+        typename F::Acc a = F::widen(v[u][0]);
+#pragma unroll
+        for (int r = 1; r < R; r++) F::template fold_in<OP>(a, v[u][r]);
+        const u32x4 o = F::narrow(a);
+#pragma unroll
+        for (int r = 0; r < R; r++) st<u32x4, NT>(p.out[r], i, o);
+      }
+    }
   }
 }
 
-// Runtime R (ops other than SUM): loads predicated on r < R.
-template <int DT, int OP>
-__global__ __launch_bounds__(kBlock) void ar_vec_rt(RankPtrs p, int R, size_t nvec, int nt) {
+// Runtime R (ops other than SUM, unusual R): loads predicated on r < R.
+template <int DT, int OP, bool NT>
+__global__ __launch_bounds__(kBlock) void ar_vec_rt(RankPtrs p, int R, size_t nvec) {
   using F = Fmt<DT>;
   const size_t stride = (size_t)gridDim.x * kBlock;
   for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec; i += stride) {
     u32x4 v[COLL_MAX_RANKS];
 #pragma unroll
     for (int r = 0; r < COLL_MAX_RANKS; r++)
-      if (r < R) v[r] = ld<u32x4>(p.in[r], i);
+      if (r < R) v[r] = ld<u32x4, NT>(p.in[r], i);
     typename F::Acc a = F::widen(v[0]);
 #pragma unroll
     for (int r = 1; r < COLL_MAX_RANKS; r++)
       if (r < R) F::template fold_in<OP>(a, v[r]);
-    u32x4 o = F::narrow(a);
+    const u32x4 o = F::narrow(a);
 #pragma unroll
     for (int r = 0; r < COLL_MAX_RANKS; r++)
-      if (r < R) st<u32x4>(p.out[r], i, o, nt);
+      if (r < R) st<u32x4, NT>(p.out[r], i, o);
   }
 }
 
@@ -82,8 +101,8 @@ __global__ __launch_bounds__(kBlock) void ar_scalar(RankPtrs p, int R, size_t fi
   using E = typename Fmt<DT>::Elem;
   const size_t stride = (size_t)gridDim.x * kBlock;
   for (size_t j = (size_t)blockIdx.x * kBlock + threadIdx.x; j < n; j += stride) {
-    size_t i = first + j;
-    E v = reduce_one<DT, OP>(p, R, i);
+    const size_t i = first + j;
+    const E v = reduce_one<DT, OP>(p, R, i);
     for (int r = 0; r < R; r++) reinterpret_cast<E *>(p.out[r])[i] = v;
   }
 }
@@ -91,39 +110,53 @@ __global__ __launch_bounds__(kBlock) void ar_scalar(RankPtrs p, int R, size_t fi
 // ------------------------------------------------------------ ReduceScatter
 
 // blockIdx.y = owner rank r: out[r][i] = fold over q of in[q][r*seg + i].
-template <int R, int DT, int OP>
-__global__ __launch_bounds__(kBlock) void rs_vec(RankPtrs p, size_t nvec_seg, int nt) {
+template <int R, int DT, int OP, bool NT>
+__global__ __launch_bounds__(kBlock) void rs_vec(RankPtrs p, size_t nvec_seg) {
   using F = Fmt<DT>;
+  constexpr int U = red_u<R>();
   const int r = blockIdx.y;
-  const size_t base = (size_t)r * nvec_seg;
-  const size_t stride = (size_t)gridDim.x * kBlock;
-  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec_seg; i += stride) {
-    u32x4 v[R];
+  const size_t off = (size_t)r * nvec_seg;
+  const size_t tile = (size_t)kBlock * U;
+  for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nvec_seg;
+       base += (size_t)gridDim.x * tile) {
+    u32x4 v[U][R];
 #pragma unroll
-    for (int q = 0; q < R; q++) v[q] = ld<u32x4>(p.in[q], base + i);
-    typename F::Acc a = F::widen(v[0]);
+    for (int u = 0; u < U; u++) {
+      const size_t i = base + (size_t)u * kBlock;
+      if (i < nvec_seg) {
 #pragma unroll
-    for (int q = 1; q < R; q++) F::template fold_in<OP>(a, v[q]);
-    st<u32x4>(p.out[r], i, F::narrow(a), nt);
+        for (int q = 0; q < R; q++) v[u][q] = ld<u32x4, NT>(p.in[q], off + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const size_t i = base + (size_t)u * kBlock;
+      if (i < nvec_seg) {
+        typename F::Acc a = F::widen(v[u][0]);
+#pragma unroll
+        for (int q = 1; q < R; q++) F::template fold_in<OP>(a, v[u][q]);
+        st<u32x4, NT>(p.out[r], i, F::narrow(a));
+      }
+    }
   }
 }
 
-template <int DT, int OP>
-__global__ __launch_bounds__(kBlock) void rs_vec_rt(RankPtrs p, int R, size_t nvec_seg, int nt) {
+template <int DT, int OP, bool NT>
+__global__ __launch_bounds__(kBlock) void rs_vec_rt(RankPtrs p, int R, size_t nvec_seg) {
   using F = Fmt<DT>;
   const int r = blockIdx.y;
-  const size_t base = (size_t)r * nvec_seg;
+  const size_t off = (size_t)r * nvec_seg;
   const size_t stride = (size_t)gridDim.x * kBlock;
   for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nvec_seg; i += stride) {
     u32x4 v[COLL_MAX_RANKS];
 #pragma unroll
     for (int q = 0; q < COLL_MAX_RANKS; q++)
-      if (q < R) v[q] = ld<u32x4>(p.in[q], base + i);
+      if (q < R) v[q] = ld<u32x4, NT>(p.in[q], off + i);
     typename F::Acc a = F::widen(v[0]);
 #pragma unroll
     for (int q = 1; q < COLL_MAX_RANKS; q++)
       if (q < R) F::template fold_in<OP>(a, v[q]);
-    st<u32x4>(p.out[r], i, F::narrow(a), nt);
+    st<u32x4, NT>(p.out[r], i, F::narrow(a));
   }
 }
 
@@ -137,37 +170,76 @@ __global__ __launch_bounds__(kBlock) void rs_scalar(RankPtrs p, int R, size_t se
 
 // ------------------------------------------------------------ dispatchers
 
+template <int R, int DT, int OP, bool NT>
+void launch_ar_r(const Launch &L, const RankPtrs &p, size_t nvec) {
+  dim3 grid(grid_for(L, nvec, red_u<R>()));
+  hipLaunchKernelGGL((ar_vec<R, DT, OP, NT>), grid, dim3(kBlock), 0, L.stream, p, nvec);
+}
+
+template <int DT, int OP, bool NT>
+void ar_vec_dispatch(const Launch &L, int R, const RankPtrs &p, size_t nvec) {
+  if constexpr (OP == COLL_SUM) {
+    switch (R) {
+      case 1: return launch_ar_r<1, DT, OP, NT>(L, p, nvec);
+      case 2: return launch_ar_r<2, DT, OP, NT>(L, p, nvec);
+      case 3: return launch_ar_r<3, DT, OP, NT>(L, p, nvec);
+      case 4: return launch_ar_r<4, DT, OP, NT>(L, p, nvec);
+      case 5: return launch_ar_r<5, DT, OP, NT>(L, p, nvec);
+      case 6: return launch_ar_r<6, DT, OP, NT>(L, p, nvec);
+      case 7: return launch_ar_r<7, DT, OP, NT>(L, p, nvec);
+      case 8: return launch_ar_r<8, DT, OP, NT>(L, p, nvec);
+      case 16: return launch_ar_r<16, DT, OP, NT>(L, p, nvec);
+      default: break;
+    }
+  }
+  hipLaunchKernelGGL((ar_vec_rt<DT, OP, NT>), dim3(grid_for(L, nvec)), dim3(kBlock), 0, L.stream,
+                     p, R, nvec);
+}
+
 template <int DT, int OP>
 int ar_dispatch(const Launch &L, int R, const RankPtrs &p, size_t count) {
   constexpr int VL = Fmt<DT>::kLanes;
   bool aligned = true;
   for (int r = 0; r < R; r++) aligned = aligned && aligned16(p.in[r]) && aligned16(p.out[r]);
-  size_t nvec = aligned ? count / VL : 0;
-  size_t tail0 = nvec * VL;
-  int nt = (2 * (size_t)R * count * Fmt<DT>::kSize >= L.nt_bytes) ? 1 : 0;
+  const size_t nvec = aligned ? count / VL : 0;
+  const size_t tail0 = nvec * VL;
+  const bool nt = 2 * (size_t)R * count * Fmt<DT>::kSize >= L.nt_bytes;
   if (nvec) {
-    dim3 grid(grid_for(L, nvec));
-    if constexpr (OP == COLL_SUM) {
-      switch (R) {
-#define COLL_AR_CASE(RR) \
-  case RR: hipLaunchKernelGGL((ar_vec<RR, DT, OP>), grid, dim3(kBlock), 0, L.stream, p, nvec, nt); break;
-        COLL_AR_CASE(1) COLL_AR_CASE(2) COLL_AR_CASE(3) COLL_AR_CASE(4)
-        COLL_AR_CASE(5) COLL_AR_CASE(6) COLL_AR_CASE(7) COLL_AR_CASE(8)
-        COLL_AR_CASE(16)
-#undef COLL_AR_CASE
-        default:
-          hipLaunchKernelGGL((ar_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
-      }
-    } else {
-      hipLaunchKernelGGL((ar_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
-    }
+    if (nt) ar_vec_dispatch<DT, OP, true>(L, R, p, nvec);
+    else ar_vec_dispatch<DT, OP, false>(L, R, p, nvec);
   }
   if (count > tail0) {
-    size_t n = count - tail0;
+    const size_t n = count - tail0;
     hipLaunchKernelGGL((ar_scalar<DT, OP>), dim3(grid_for(L, n)), dim3(kBlock), 0, L.stream,
                        p, R, tail0, n);
   }
   return hip_status();
+}
+
+template <int R, int DT, int OP, bool NT>
+void launch_rs_r(const Launch &L, const RankPtrs &p, size_t nvec) {
+  dim3 grid(grid_for(L, nvec, red_u<R>()), R);
+  hipLaunchKernelGGL((rs_vec<R, DT, OP, NT>), grid, dim3(kBlock), 0, L.stream, p, nvec);
+}
+
+template <int DT, int OP, bool NT>
+void rs_vec_dispatch(const Launch &L, int R, const RankPtrs &p, size_t nvec) {
+  if constexpr (OP == COLL_SUM) {
+    switch (R) {
+      case 1: return launch_rs_r<1, DT, OP, NT>(L, p, nvec);
+      case 2: return launch_rs_r<2, DT, OP, NT>(L, p, nvec);
+      case 3: return launch_rs_r<3, DT, OP, NT>(L, p, nvec);
+      case 4: return launch_rs_r<4, DT, OP, NT>(L, p, nvec);
+      case 5: return launch_rs_r<5, DT, OP, NT>(L, p, nvec);
+      case 6: return launch_rs_r<6, DT, OP, NT>(L, p, nvec);
+      case 7: return launch_rs_r<7, DT, OP, NT>(L, p, nvec);
+      case 8: return launch_rs_r<8, DT, OP, NT>(L, p, nvec);
+      case 16: return launch_rs_r<16, DT, OP, NT>(L, p, nvec);
+      default: break;
+    }
+  }
+  hipLaunchKernelGGL((rs_vec_rt<DT, OP, NT>), dim3(grid_for(L, nvec), R), dim3(kBlock), 0,
+                     L.stream, p, R, nvec);
 }
 
 template <int DT, int OP>
@@ -175,29 +247,14 @@ int rs_dispatch(const Launch &L, int R, const RankPtrs &p, size_t seg) {
   constexpr int VL = Fmt<DT>::kLanes;
   bool aligned = (seg % VL) == 0;
   for (int r = 0; r < R; r++) aligned = aligned && aligned16(p.in[r]) && aligned16(p.out[r]);
-  int nt = ((size_t)(R + 1) * R * seg * Fmt<DT>::kSize >= L.nt_bytes) ? 1 : 0;
+  const bool nt = (size_t)(R + 1) * R * seg * Fmt<DT>::kSize >= L.nt_bytes;
   if (aligned) {
-    size_t nvec = seg / VL;
-    unsigned gx = grid_for(L, nvec * R);
-    gx = (gx + R - 1) / R;
-    dim3 grid(gx, R);
-    if constexpr (OP == COLL_SUM) {
-      switch (R) {
-#define COLL_RS_CASE(RR) \
-  case RR: hipLaunchKernelGGL((rs_vec<RR, DT, OP>), grid, dim3(kBlock), 0, L.stream, p, nvec, nt); break;
-        COLL_RS_CASE(1) COLL_RS_CASE(2) COLL_RS_CASE(3) COLL_RS_CASE(4)
-        COLL_RS_CASE(5) COLL_RS_CASE(6) COLL_RS_CASE(7) COLL_RS_CASE(8)
-        COLL_RS_CASE(16)
-#undef COLL_RS_CASE
-        default:
-          hipLaunchKernelGGL((rs_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
-      }
-    } else {
-      hipLaunchKernelGGL((rs_vec_rt<DT, OP>), grid, dim3(kBlock), 0, L.stream, p, R, nvec, nt);
-    }
+    const size_t nvec = seg / VL;
+    if (nt) rs_vec_dispatch<DT, OP, true>(L, R, p, nvec);
+    else rs_vec_dispatch<DT, OP, false>(L, R, p, nvec);
   } else {
-    unsigned gx = (grid_for(L, seg * R) + R - 1) / R;
-    hipLaunchKernelGGL((rs_scalar<DT, OP>), dim3(gx, R), dim3(kBlock), 0, L.stream, p, R, seg);
+    hipLaunchKernelGGL((rs_scalar<DT, OP>), dim3(grid_for(L, seg), R), dim3(kBlock), 0,
+                       L.stream, p, R, seg);
   }
   return hip_status();
 }
