@@ -113,6 +113,10 @@ def make_inputs(torch, synth, coll):
     W["sc_t"].copy_(W["sc"].view(R, R).t().contiguous().view(-1))
     W["recv"] = [torch.empty((int(sc[:, d].sum()), H), dtype=torch.bfloat16, device="cuda")
                  for d in range(R)]
+    # plain-copy reference (1 GiB through the library's copy kernel), only for
+    # calibrating the HBM counters; not part of the step
+    W["copy_src"] = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
+    W["copy_dst"] = [torch.empty_like(W["copy_src"])]
     W["moe_rows"] = int(sc.sum())
     W["dest_share"] = [round(float(sc[:, d].sum()) / float(sc.sum()), 4) for d in range(R)]
     torch.cuda.synchronize()
@@ -138,6 +142,7 @@ def row_bytes(W):
     b["moe_expert"] = 2 * rows * H * 2
     b["a2av_combine"] = 2 * rows * H * 2
     b["moe_combine"] = rows * H * 2 + R * T * H * 2 + R * T * K * 8
+    b["copy_ref"] = 2 << 30
     return b
 
 
@@ -162,6 +167,12 @@ def step_rows(W, coll, torch):
                                                    W["sd"], H)),
         ("moe_combine", lambda: coll.moe_combine(W["back"], W["pos"], W["moe_w"], W["out"])),
     ]
+
+
+# rows run only when named with --only
+EXTRA_ROWS = {
+    "copy_ref": lambda W, coll: coll.broadcast(W["copy_src"], W["copy_dst"], 0),
+}
 
 
 def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=20):
@@ -292,6 +303,7 @@ def main():
     if args.only:
         keep = set(args.only.split(","))
         rows = [r for r in rows if r[0] in keep]
+        rows += [(n, (lambda f=f: f(W, coll))) for n, f in EXTRA_ROWS.items() if n in keep]
     nbytes = row_bytes(W)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
