@@ -39,31 +39,38 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, extra=(), bdir: str = BUILD_DIR) -> str:
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libcoll.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile every HIP source and link libcoll.so; returns its path.
+
+    ``defines`` (e.g. ``["COLL_A2A_U=8"]``) and ``out`` build a variant of the
+    library with other tuning constants elsewhere (used for tuning sweeps)."""
+    bdir = build_dir or BUILD_DIR
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    extra = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, extra, bdir), srcs))
+    target = out or LIB
+    tmp = target + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, target)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {target}")
+    return target
 
 
 if __name__ == "__main__":

@@ -35,11 +35,11 @@ SIGNATURES = {
     "coll_all_gather": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_gather": (_i, [_i, _vp, _vp, _i, _sz, _sz, _i, _vp]),
     "coll_broadcast": (_i, [_i, _vp, _vp, _i, _sz, _i, _vp]),
-    "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp]),
+    "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp]),
     "coll_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "coll_moe_layout": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
-    "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _vp]),
+    "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp]),
     "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
 }
 
@@ -199,9 +199,11 @@ def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
     for t in list(sends) + list(recvs):
         if t.dtype != sends[0].dtype:
             raise ValueError("all_to_all_v: one dtype for every buffer")
+    # receive capacity in rows: an upper bound of the rows moved (sizes the launch)
+    capacity = sum(t.numel() // row_elems for t in recvs)
     _check(lib().coll_all_to_all_v(R, _table(sends, "send"), _dev(sendcounts, "counts"),
                                    _dev(sdispls, "sdispls"), _table(recvs, "recv"),
-                                   _dev(rdispls, "rdispls"), row_elems * mult, dt,
+                                   _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity,
                                    _stream(stream)), "all_to_all_v")
 
 
@@ -257,9 +259,10 @@ def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
     for r in recvs:
         if r.dtype != torch.bfloat16:
             raise ValueError("moe_expert_scale: bf16 rows only")
+    capacity = sum(t.numel() // hidden for t in recvs)
     _check(lib().coll_moe_expert_scale(R, _table(recvs, "recv"), _dev(expert_counts, "ec"),
                                        _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
-                                       _stream(stream)), "moe_expert_scale")
+                                       capacity, _stream(stream)), "moe_expert_scale")
 
 
 def moe_combine(backs, pos, weights, outs, stream=None) -> None:

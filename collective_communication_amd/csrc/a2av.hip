@@ -19,6 +19,10 @@ namespace coll {
 namespace {
 
 constexpr int kMaxBlocks = COLL_MAX_RANKS * COLL_MAX_RANKS;   // 256
+#ifndef COLL_A2A_U
+#define COLL_A2A_U 4
+#endif
+constexpr int kA2aU = COLL_A2A_U;             // units per lane per tile
 
 // Inclusive prefix sum across one wave64 (Hillis-Steele over lanes).
 __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const i
                                                       const int64_t *sdispls,
                                                       const int64_t *rdispls, uint64_t row_units) {
   using U = typename UnitT<B>::T;
-  constexpr int UN = kCopyU;
+  constexpr int UN = kA2aU;
   __shared__ uint64_t s_end[kMaxBlocks];   // inclusive end of block b in the global unit space
   __shared__ uint64_t s_src[kMaxBlocks];   // src unit address minus block start (in units)
   __shared__ uint64_t s_dst[kMaxBlocks];
@@ -90,7 +94,9 @@ __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const i
   int top = 1;
   while (top * 2 <= nb) top *= 2;            // largest power of two <= nb
   const uint64_t tile = (uint64_t)kBlock * UN;
-  int b = 0;
+  // the current block's bounds and address bases live in registers; LDS is
+  // read only when a unit falls outside them
+  uint64_t blo = 1, bhi = 0, sbase = 0, dbase = 0;
   for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
        base += (uint64_t)gridDim.x * tile) {
     U v[UN];
@@ -99,16 +105,19 @@ __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const i
     for (int u = 0; u < UN; u++) {
       const uint64_t x = base + (uint64_t)u * kBlock;
       if (x < total) {
-        if (x >= s_end[b] || (b > 0 && x < s_end[b - 1])) {
+        if (x < blo || x >= bhi) {
           int lo = 0;                           // blocks ending at or before x
           for (int step = top; step > 0; step >>= 1) {
             const int c = lo + step;
             if (c <= nb && s_end[c - 1] <= x) lo = c;
           }
-          b = lo;
+          blo = lo > 0 ? s_end[lo - 1] : 0;
+          bhi = s_end[lo];
+          sbase = s_src[lo];
+          dbase = s_dst[lo];
         }
-        const auto *src = gconst<U>((s_src[b] + x) * B);
-        dst[u] = (s_dst[b] + x) * B;
+        const auto *src = gconst<U>((sbase + x) * B);
+        dst[u] = (dbase + x) * B;
         if constexpr (NT) v[u] = __builtin_nontemporal_load(src);
         else v[u] = *src;
       }
@@ -128,14 +137,19 @@ __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const i
 }  // namespace
 
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes) {
+                const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
+                size_t rows_capacity) {
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
   const int unit = copy_unit(bits);
   const uint64_t row_units = row_bytes / unit;
-  // The total is only known on the device: launch the resident grid and let
-  // the tile-stride loop cover whatever the counts say.
-  dim3 grid(grid_resident(L));
+  // The total is only known on the device.  With a capacity bound: one
+  // workgroup per tile of the bound (surplus workgroups exit at once);
+  // without one: the resident grid loops over the tiles.
+  unsigned g = grid_resident(L);
+  if (rows_capacity > 0) g = grid_for(L, (uint64_t)rows_capacity * row_units, kA2aU);
+  if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
+  dim3 grid(g);
   COLL_UNIT_SWITCH(a2av_kernel, unit, L.a2a_nt, grid, L.stream, p, R, counts, sdispls, rdispls,
                    row_units);
   return hip_status();

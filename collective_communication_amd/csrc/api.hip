@@ -49,6 +49,8 @@ Launch launch_ctx(void *stream) {
   long nt = env_long("COLL_NT_MIN_BYTES", 32L << 20);
   L.nt_bytes = nt < 0 ? 0 : (size_t)nt;
   L.a2a_nt = env_long("COLL_A2A_NT", 1) ? 1 : 0;
+  const long g = env_long("COLL_A2A_GRID", 0);
+  L.a2a_grid = (g > 0 && g < 0x7FFFFFFFL) ? g : 0;
   return L;
 }
 
@@ -162,7 +164,8 @@ int coll_broadcast(int R, const void *sendbuf_root, void *const *recvbufs, int r
 
 int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcounts,
                       const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
-                      size_t row_elems, coll_dtype_t dtype, void *stream) {
+                      size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
+                      void *stream) {
   if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
   if (row_elems == 0) return COLL_OK;
   if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
@@ -173,8 +176,10 @@ int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcou
     p.in[r] = sendbufs[r];
     p.out[r] = recvbufs[r];
   }
+  if (recv_rows_capacity > ((size_t)1 << 48) / (row_elems * dtype_size(dtype)))
+    return COLL_ERR_INVALID_ARG;
   return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls,
-                     row_elems * dtype_size(dtype));
+                     row_elems * dtype_size(dtype), recv_rows_capacity);
 }
 
 size_t coll_moe_workspace_bytes(int R, int tokens, int topk, int n_experts) {
@@ -221,7 +226,7 @@ int coll_moe_permute(int R, const void *const *x, const int32_t *const *pos, int
 
 int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
-                          coll_dtype_t dtype, void *stream) {
+                          coll_dtype_t dtype, size_t recv_rows_capacity, void *stream) {
   if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0)
     return COLL_ERR_INVALID_ARG;
   if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
@@ -229,8 +234,9 @@ int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_co
   if (!expert_counts || !rdispls || hidden >= ((size_t)1 << 31)) return COLL_ERR_INVALID_ARG;
   MutPtrTable rs{};
   if (!fill_out(R, recvbufs, rs.p)) return COLL_ERR_INVALID_ARG;
+  if (recv_rows_capacity > ((size_t)1 << 48) / hidden) return COLL_ERR_INVALID_ARG;
   return launch_moe_expert_scale(launch_ctx(stream), R, rs, expert_counts, rdispls, n_experts,
-                                 hidden);
+                                 hidden, recv_rows_capacity);
 }
 
 int coll_moe_combine(int R, const void *const *back, const int32_t *const *pos,

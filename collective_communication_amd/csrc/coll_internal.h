@@ -63,7 +63,10 @@ __device__ __forceinline__ void st(void *base, size_t i, U v) {
 // workgroup per tile (a single pass: the dispatcher balances the load).
 // Measured on MI355X for a plain 1 GiB copy: 16 KiB tiles (U = 4 x 16 B),
 // non-temporal both ways, reach ~6.2-6.4 TB/s.
-constexpr int kCopyU = 4;
+#ifndef COLL_COPY_U
+#define COLL_COPY_U 4
+#endif
+constexpr int kCopyU = COLL_COPY_U;
 
 // ------------------------------------------------ element formats (exact widening)
 
@@ -316,10 +319,11 @@ struct Launch {
   int wgs_per_cu;    // workgroups per CU for persistent (device-sized) kernels
   size_t nt_bytes;   // bytes moved at or above which loads/stores are non-temporal
   int a2a_nt;        // non-temporal loads/stores in All-to-All-v (size unknown on the host)
+  long a2a_grid;     // 0: resident grid; > 0: this many workgroups (tuning)
 };
 
 // Device properties and tuning knobs (environment: COLL_WGS_PER_CU,
-// COLL_NT_MIN_BYTES, COLL_A2A_NT), read once per device.
+// COLL_NT_MIN_BYTES, COLL_A2A_NT, COLL_A2A_GRID).
 Launch launch_ctx(void *stream);
 
 // One workgroup per tile of kBlock * per_thread units (single pass), capped
@@ -369,7 +373,8 @@ int launch_gather(const Launch &L, int R, const RankPtrs &p, void *out, size_t o
                   size_t inner_bytes);
 int launch_broadcast(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes);
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes);
+                const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
+                size_t rows_capacity);
 
 constexpr int kMoeMaxExperts = 1024;
 size_t moe_workspace_bytes(int R, int T, int K, int E);
@@ -380,7 +385,7 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
                        int K, size_t row_bytes, const MutPtrTable &send);
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
-                            size_t hidden);
+                            size_t hidden, size_t rows_capacity);
 int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTable &pos,
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
 

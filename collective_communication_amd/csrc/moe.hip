@@ -31,6 +31,18 @@
 namespace coll {
 
 constexpr int kMoeTile = 1024;        // ids per layout tile (kBlock * 4)
+#ifndef COLL_PERMUTE_U
+#define COLL_PERMUTE_U 4
+#endif
+#ifndef COLL_EXPERT_U
+#define COLL_EXPERT_U 8
+#endif
+#ifndef COLL_COMBINE_U
+#define COLL_COMBINE_U 1
+#endif
+constexpr int kPermuteU = COLL_PERMUTE_U;     // 16-byte units per lane, permute
+constexpr int kExpertU = COLL_EXPERT_U;       // ... test expert
+constexpr int kCombineU = COLL_COMBINE_U;     // ... combine (each gathers K rows)
 constexpr int kMaxExperts = kMoeMaxExperts;
 
 size_t moe_workspace_bytes(int R, int T, int K, int E) {
@@ -180,38 +192,61 @@ __global__ __launch_bounds__(kBlock) void moe_pos(PtrTable ids, MutPtrTable pos,
 
 // ------------------------------------------------------------------ permute
 
-// blockIdx.y = source s; flattened over (token, unit) of x[s].  A tile's units
-// are loaded once, then each is stored to its K slots.
+// Work item of the token-row kernels: one wave per (source s, token t,
+// segment of a row).  Everything that identifies the item is wave-uniform
+// and lives in scalar registers, so the token's K slots (and weights) are
+// scalar loads and the vector memory pipe carries only row data: a wave
+// issues all of its row loads, then all of its stores, and exits (no wave
+// ever waits on its own stores, which the in-order vmcnt counter would force
+// if it went on to a next item).
+struct RowItem {
+  int t;            // token
+  int seg;          // segment index within the row
+  bool valid;
+};
+
+__device__ __forceinline__ RowItem row_item(int T, int nseg) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int id = (int)blockIdx.x * (kBlock / 64) + wave;     // < T * nseg + 3
+  RowItem it;
+  it.t = id / nseg;
+  it.seg = id - it.t * nseg;
+  it.valid = it.t < T;
+  return it;
+}
+
+// send[s][pos[s][t,k]] = x[s][t] for every k.  Segment = 64 lanes x UN units.
 template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void moe_permute_kernel(PtrTable x, PtrTable pos,
-                                                             MutPtrTable send, uint64_t total,
-                                                             FastDiv64 upr, int K, uint32_t TK) {
+                                                             MutPtrTable send, int T, int K,
+                                                             uint32_t upr, int nseg) {
   using U = typename UnitT<B>::T;
-  constexpr int UN = kCopyU;
+  constexpr int UN = kPermuteU;
+  const RowItem it = row_item(T, nseg);
+  if (!it.valid) return;
   const int s = blockIdx.y;
-  const void *src = x.p[s];
-  const int32_t *ps = reinterpret_cast<const int32_t *>(pos.p[s]);
-  void *dst = send.p[s];
-  const uint64_t tile = (uint64_t)kBlock * UN;
-  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
-       base += (uint64_t)gridDim.x * tile) {
-    U val[UN];
+  const uint32_t TK = (uint32_t)T * (uint32_t)K;
+  const int lane = threadIdx.x & 63;
+  const U *src = reinterpret_cast<const U *>(x.p[s]) + (size_t)it.t * upr;
+  const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
+  U *dst = reinterpret_cast<U *>(send.p[s]);
+  const uint32_t u0 = (uint32_t)it.seg * (64 * UN) + lane;
+  U v[UN];
+#pragma unroll
+  for (int u = 0; u < UN; u++) {
+    const uint32_t x_u = u0 + u * 64;
+    if (x_u < upr) v[u] = NT ? __builtin_nontemporal_load(src + x_u) : src[x_u];
+  }
+  for (int k = 0; k < K; k++) {
+    const int32_t slot = __builtin_amdgcn_readfirstlane(pk[k]);
+    if ((uint32_t)slot >= TK) continue;                      // never write outside
+    U *row = dst + (size_t)slot * upr;
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t j = base + (uint64_t)u * kBlock;
-      if (j < total) val[u] = ld<U, NT>(src, j);
-    }
-#pragma unroll
-    for (int u = 0; u < UN; u++) {
-      const uint64_t j = base + (uint64_t)u * kBlock;
-      if (j < total) {
-        const uint64_t t = fdiv64(j, upr);
-        const uint64_t v = j - t * upr.d;
-        const int32_t *pk = ps + t * K;
-        for (int k = 0; k < K; k++) {
-          const int32_t slot = pk[k];
-          if ((uint32_t)slot < TK) st<U, NT>(dst, (uint64_t)slot * upr.d + v, val[u]);   // never write outside
-        }
+      const uint32_t x_u = u0 + u * 64;
+      if (x_u < upr) {
+        if constexpr (NT) __builtin_nontemporal_store(v[u], row + x_u);
+        else row[x_u] = v[u];
       }
     }
   }
@@ -267,41 +302,63 @@ __global__ __launch_bounds__(kBlock) void moe_expert_scale_kernel(MutPtrTable re
   const uint64_t total = nrows * upr.d;
   int top = 1;
   while (top * 2 <= N) top *= 2;
-  int jc = 0;                                   // cached entry
-  constexpr int UN = 2;
+  // the current entry, decoded once: global rows [glo, ghi) of rank d at
+  // receive row rbase + g, scaled by `scale`
+  uint64_t glo = 1, ghi = 0;
+  int64_t rbase = 0;
+  float scale = 1.0f;
+  void *y = nullptr;
+  constexpr int UN = kExpertU;
   const uint64_t tile = (uint64_t)kBlock * UN;
   for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
        base += (uint64_t)gridDim.x * tile) {
+    u32x4 v[UN];
+    uint64_t at[UN];
+    float sc[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
       const uint64_t x = base + (uint64_t)u * kBlock;
       if (x >= total) continue;
       const uint64_t g = fdiv64(x, upr);        // global row
-      const uint64_t unit = x - g * upr.d;
-      if (g >= s_end[jc] || (jc > 0 && g < s_end[jc - 1])) {
+      if (g < glo || g >= ghi) {
         int lo = 0;
         for (int step = top; step > 0; step >>= 1) {
           const int c = lo + step;
           if (c <= N && s_end[c - 1] <= g) lo = c;
         }
-        jc = lo;
+        const int d = lo / E, rem = lo - d * E, s = rem / per, el = rem - s * per;
+        const int first = d * E + s * per;     // first entry of (d, s)
+        const uint64_t gstart = first == 0 ? 0 : s_end[first - 1];
+        glo = lo > 0 ? s_end[lo - 1] : 0;
+        ghi = s_end[lo];
+        rbase = rdispls[d * R + s] - (int64_t)gstart;
+        scale = 1.0f + (float)(d * per + el) / 256.0f;
+        y = recv.p[d];
       }
-      const int d = jc / E, rem = jc - d * E, s = rem / per, el = rem - s * per;
-      const int e = d * per + el;
-      const int first = d * E + s * per;        // first entry of (d, s)
-      const uint64_t gstart = first == 0 ? 0 : s_end[first - 1];
-      const uint64_t row = (uint64_t)rdispls[d * R + s] + (g - gstart);
-      const float scale = 1.0f + (float)e / 256.0f;
-      void *y = recv.p[d];
+      const uint64_t unit = x - g * upr.d;
+      at[u] = (uint64_t)(rbase + (int64_t)g) * upr.d + unit;
+      sc[u] = scale;
       if constexpr (G == 8) {
-        const u32x4 v = ld<u32x4, NT>(y, row * upr.d + unit);
+        v[u] = ld<u32x4, NT>(y, at[u]);
+        at[u] = reinterpret_cast<uint64_t>(reinterpret_cast<u32x4 *>(y) + at[u]);
+      } else {
+        at[u] = reinterpret_cast<uint64_t>(reinterpret_cast<uint16_t *>(y) + at[u]);
+        v[u][0] = *reinterpret_cast<const uint16_t *>(at[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t x = base + (uint64_t)u * kBlock;
+      if (x >= total) continue;
+      if constexpr (G == 8) {
         u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; q++) o[q] = pack_bf16(bf16_lo(v[q]) * scale, bf16_hi(v[q]) * scale);
-        st<u32x4, NT>(y, row * upr.d + unit, o);
+        for (int q = 0; q < 4; q++)
+          o[q] = pack_bf16(bf16_lo(v[u][q]) * sc[u], bf16_hi(v[u][q]) * sc[u]);
+        st<u32x4, NT>(reinterpret_cast<void *>(at[u]), 0, o);
       } else {
-        uint16_t *p = reinterpret_cast<uint16_t *>(y) + row * upr.d + unit;
-        *p = (uint16_t)(pack_bf16(bf16_lo(*p) * scale, 0.0f) & 0xFFFFu);
+        *reinterpret_cast<uint16_t *>(at[u]) =
+            (uint16_t)(pack_bf16(bf16_lo(v[u][0]) * sc[u], 0.0f) & 0xFFFFu);
       }
     }
   }
@@ -315,79 +372,88 @@ __device__ __forceinline__ uint32_t slot_of(int32_t p, uint32_t TK) {
   return (uint32_t)p < TK ? (uint32_t)p : 0u;
 }
 
-// One wave per token (blockIdx.y = source s); lanes stride over the row's
-// 16-byte units, two units per lane per step, each gathering its K rows.
+// One wave per (token, segment of 64 x UN units); its K slots and weights
+// are scalar loads, all K x UN gathered loads issue before the fold.
 template <int G, bool NT>
 __global__ __launch_bounds__(kBlock) void moe_combine_kernel(PtrTable back, PtrTable pos,
                                                              PtrTable wts, MutPtrTable out,
-                                                             int T, int K, uint32_t upr) {
+                                                             int T, int K, uint32_t upr,
+                                                             int nseg) {
   constexpr int kChunk = 8;                    // gathered rows in flight per unit
-  constexpr int UN = 2;
+  constexpr int UN = (G == 8) ? kCombineU : 1;
+  const RowItem it = row_item(T, nseg);
+  if (!it.valid) return;
   const uint32_t TK = (uint32_t)T * (uint32_t)K;
   const int s = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const uint16_t *bk = reinterpret_cast<const uint16_t *>(back.p[s]);
-  const int32_t *ps = reinterpret_cast<const int32_t *>(pos.p[s]);
-  const float *ws = reinterpret_cast<const float *>(wts.p[s]);
+  const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
+  const float *wk = reinterpret_cast<const float *>(wts.p[s]) + (size_t)it.t * K;
   uint16_t *o = reinterpret_cast<uint16_t *>(out.p[s]);
-  const int nwaves = gridDim.x * (kBlock / 64);
-  for (int t = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6); t < T; t += nwaves) {
-    const int tu = __builtin_amdgcn_readfirstlane(t);
-    const int32_t *pk = ps + (size_t)tu * K;
-    const float *wk = ws + (size_t)tu * K;
-    if constexpr (G == 8) {
-      for (uint32_t u0 = lane; u0 < upr; u0 += 64 * UN) {
-        float acc[UN][8];
-        for (int k0 = 0; k0 < K; k0 += kChunk) {
-          u32x4 v[UN][kChunk];
+  const uint32_t u0 = (uint32_t)it.seg * (64 * UN) + lane;
+  if constexpr (G == 8) {
+    float acc[UN][8];
+    for (int k0 = 0; k0 < K; k0 += kChunk) {
+      uint32_t slot[kChunk];
+      float wgt[kChunk];
 #pragma unroll
-          for (int c = 0; c < kChunk; c++) {
-            if (k0 + c < K) {
-              const uint16_t *row = bk + (size_t)slot_of(pk[k0 + c], TK) * upr * 8;
-#pragma unroll
-              for (int uu = 0; uu < UN; uu++) {
-                const uint32_t u = u0 + uu * 64;
-                if (u < upr) v[uu][c] = ld<u32x4, NT>(row, u);
-              }
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < kChunk; c++) {
-            if (k0 + c < K) {
-              const float wgt = wk[k0 + c];
-#pragma unroll
-              for (int uu = 0; uu < UN; uu++) {
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                  const float lo = wgt * bf16_lo(v[uu][c][q]);
-                  const float hi = wgt * bf16_hi(v[uu][c][q]);
-                  if (k0 + c == 0) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
-                  else { acc[uu][2 * q] = acc[uu][2 * q] + lo; acc[uu][2 * q + 1] = acc[uu][2 * q + 1] + hi; }
-                }
-              }
-            }
-          }
+      for (int c = 0; c < kChunk; c++) {
+        slot[c] = 0;
+        wgt[c] = 0.0f;
+        if (k0 + c < K) {
+          slot[c] = slot_of(__builtin_amdgcn_readfirstlane(pk[k0 + c]), TK);
+          wgt[c] = __builtin_bit_cast(
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wk[k0 + c])));
         }
+      }
+      u32x4 v[UN][kChunk];
 #pragma unroll
-        for (int uu = 0; uu < UN; uu++) {
-          const uint32_t u = u0 + uu * 64;
-          if (u < upr) {
-            u32x4 r;
+      for (int c = 0; c < kChunk; c++) {
+        if (k0 + c < K) {
+          const uint16_t *row = bk + (size_t)slot[c] * upr * 8;
 #pragma unroll
-            for (int q = 0; q < 4; q++) r[q] = pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]);
-            st<u32x4, NT>(o + (size_t)tu * upr * 8, u, r);
+          for (int uu = 0; uu < UN; uu++) {
+            const uint32_t u = u0 + uu * 64;
+            if (u < upr) v[uu][c] = ld<u32x4, NT>(row, u);
           }
         }
       }
-    } else {
-      for (uint32_t u = lane; u < upr; u += 64) {
-        float acc = 0.0f;
-        for (int k = 0; k < K; k++) {
-          const float prod = wk[k] * bf16_lo(bk[(size_t)slot_of(pk[k], TK) * upr + u]);
-          acc = (k == 0) ? prod : acc + prod;
+#pragma unroll
+      for (int c = 0; c < kChunk; c++) {
+        if (k0 + c < K) {
+#pragma unroll
+          for (int uu = 0; uu < UN; uu++) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const float lo = wgt[c] * bf16_lo(v[uu][c][q]);
+              const float hi = wgt[c] * bf16_hi(v[uu][c][q]);
+              if (k0 + c == 0) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
+              else { acc[uu][2 * q] = acc[uu][2 * q] + lo; acc[uu][2 * q + 1] = acc[uu][2 * q + 1] + hi; }
+            }
+          }
         }
-        o[(size_t)tu * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
       }
+    }
+#pragma unroll
+    for (int uu = 0; uu < UN; uu++) {
+      const uint32_t u = u0 + uu * 64;
+      if (u < upr) {
+        u32x4 r;
+#pragma unroll
+        for (int q = 0; q < 4; q++) r[q] = pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]);
+        st<u32x4, NT>(o + (size_t)it.t * upr * 8, u, r);
+      }
+    }
+  } else {
+    const uint32_t u = u0;
+    if (u < upr) {
+      float acc = 0.0f;
+      for (int k = 0; k < K; k++) {
+        const uint32_t slot = slot_of(__builtin_amdgcn_readfirstlane(pk[k]), TK);
+        const float prod = wk[k] * bf16_lo(bk[(size_t)slot * upr + u]);
+        acc = (k == 0) ? prod : acc + prod;
+      }
+      o[(size_t)it.t * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
     }
   }
 }
@@ -421,19 +487,22 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
   for (int r = 0; r < R; r++) bits |= (uintptr_t)x.p[r] | (uintptr_t)send.p[r];
   const int unit = copy_unit(bits);
   const uint64_t upr = row_bytes / unit;
-  const uint64_t total = (uint64_t)T * upr;
-  if (total == 0) return COLL_OK;
-  const FastDiv64 f = make_fastdiv64(upr);
-  const bool nt = (uint64_t)R * total * unit * (1 + K) >= L.nt_bytes;
-  dim3 grid(grid_for(L, total, kCopyU), R);
-  COLL_UNIT_SWITCH(moe_permute_kernel, unit, nt, grid, L.stream, x, pos, send, total, f, K,
-                   (uint32_t)(T * K));
+  if (T == 0 || upr == 0) return COLL_OK;
+  if (upr >= (1ull << 31)) return COLL_ERR_UNSUPPORTED;
+  const int nseg = (int)((upr + 64 * kPermuteU - 1) / (64 * kPermuteU));
+  const uint64_t items = (uint64_t)T * nseg;
+  if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
+  const bool nt = (uint64_t)R * T * upr * unit * (1 + K) >= L.nt_bytes;
+  dim3 grid((unsigned)((items + 3) / 4), R);
+  COLL_UNIT_SWITCH(moe_permute_kernel, unit, nt, grid, L.stream, x, pos, send, T, K,
+                   (uint32_t)upr, nseg);
   return hip_status();
 }
 
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
-                            size_t hidden) {
+                            size_t hidden, size_t rows_capacity) {
+  (void)rows_capacity;           // the resident grid: each workgroup builds the R*E table once
   bool vec = (hidden % 8) == 0;
   for (int r = 0; r < R; r++) vec = vec && aligned16(recv.p[r]);
   dim3 grid(grid_resident(L));
@@ -459,20 +528,24 @@ int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTa
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out) {
   bool vec = (hidden % 8) == 0;
   for (int r = 0; r < R; r++) vec = vec && aligned16(back.p[r]) && aligned16(out.p[r]);
-  const unsigned gx = (unsigned)((T + 3) / 4);         // one wave per token
-  if (gx == 0) return COLL_OK;
-  dim3 grid(gx, R);
+  if (T == 0) return COLL_OK;
+  const uint64_t upr = vec ? hidden / 8 : hidden;
+  const int per_seg = vec ? 64 * kCombineU : 64;
+  const int nseg = (int)((upr + per_seg - 1) / per_seg);
+  const uint64_t items = (uint64_t)T * nseg;
+  if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)((items + 3) / 4), R);
   const bool nt = (uint64_t)R * T * (K + 1) * hidden * 2 >= L.nt_bytes;
   if (vec) {
     if (nt)
       hipLaunchKernelGGL((moe_combine_kernel<8, true>), grid, dim3(kBlock), 0, L.stream, back, pos,
-                         w, out, T, K, (uint32_t)(hidden / 8));
+                         w, out, T, K, (uint32_t)upr, nseg);
     else
       hipLaunchKernelGGL((moe_combine_kernel<8, false>), grid, dim3(kBlock), 0, L.stream, back,
-                         pos, w, out, T, K, (uint32_t)(hidden / 8));
+                         pos, w, out, T, K, (uint32_t)upr, nseg);
   } else {
     hipLaunchKernelGGL((moe_combine_kernel<1, false>), grid, dim3(kBlock), 0, L.stream, back, pos,
-                       w, out, T, K, (uint32_t)hidden);
+                       w, out, T, K, (uint32_t)upr, nseg);
   }
   return hip_status();
 }

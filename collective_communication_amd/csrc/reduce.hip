@@ -23,8 +23,11 @@ namespace {
 
 // 16-byte units per lane per tile for an R-way reduction: U * R independent
 // loads in flight per lane without exhausting the VGPR budget.
+#ifndef COLL_RED_U_MID
+#define COLL_RED_U_MID 2        // units per lane for 3 <= R <= 8
+#endif
 template <int R>
-constexpr int red_u() { return R <= 2 ? 4 : (R <= 8 ? 2 : 1); }
+constexpr int red_u() { return R <= 2 ? 4 : (R <= 8 ? COLL_RED_U_MID : 1); }
 
 // R known at compile time: all U * R loads of a tile issue back to back.
 template <int R, int DT, int OP, bool NT>

@@ -136,10 +136,16 @@ int coll_broadcast(int nranks, const void *sendbuf_root, void *const *recvbufs, 
  * must not be NULL.
  * The reverse exchange (MoE combine) is the same call with the count matrix
  * transposed and the two displacement tables swapped.
+ *   recv_rows_capacity: the rows of all receive buffers together, an upper
+ *   bound of the rows moved that the host knows without reading the counts.
+ *   It sizes the launch (one workgroup per 16 KiB tile, the fastest form on
+ *   MI355X); 0 means unknown, and a resident grid then loops over the tiles.
+ *   It is never used to address memory.
  */
 int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *sendcounts,
                       const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
-                      size_t row_elems, coll_dtype_t dtype, void *stream);
+                      size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
+                      void *stream);
 
 /* ---------------------------------------------------------------------------
  * MoE dispatch / combine over expert parallelism -- tutorial section 8.4.
@@ -181,11 +187,12 @@ int coll_moe_permute(int nranks, const void *const *x, const int32_t *const *pos
  * expert e becomes y = rne(x * (1 + e/256)) in place (the fp32 product is
  * exact, so y is unique).  Row order in recvbufs[d] is: for s ascending,
  * starting at rdispls[d*R+s], the rows of d's experts in ascending expert
- * order, expert_counts[s*E+e] rows each.
+ * order, expert_counts[s*E+e] rows each.  recv_rows_capacity has the meaning
+ * it has for coll_all_to_all_v (launch sizing only; 0 = unknown).
  */
 int coll_moe_expert_scale(int nranks, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
-                          coll_dtype_t dtype, void *stream);
+                          coll_dtype_t dtype, size_t recv_rows_capacity, void *stream);
 
 /*
  * Combine (results return to the token's owner and are gate-weighted):

@@ -50,7 +50,7 @@ def test_rank_count_rejected(L, R):
     assert L.coll_all_gather(R, NULL, NULL, 8, 0, NULL) == -1
     assert L.coll_gather(R, NULL, NULL, 0, 1, 8, 0, NULL) == -1
     assert L.coll_broadcast(R, NULL, NULL, 0, 8, 0, NULL) == -1
-    assert L.coll_all_to_all_v(R, NULL, NULL, NULL, NULL, NULL, 8, 0, NULL) == -1
+    assert L.coll_all_to_all_v(R, NULL, NULL, NULL, NULL, NULL, 8, 0, 0, NULL) == -1
 
 
 def test_zero_count_is_a_no_op(L):
@@ -83,7 +83,7 @@ def test_dtype_and_op_rejected(L):
     assert L.coll_allreduce(2, NULL, NULL, 8, 7, 0, NULL) == -1
     assert L.coll_allreduce(2, NULL, NULL, 8, 0, 9, NULL) == -2
     assert L.coll_reduce_scatter(2, NULL, NULL, 8, 0, -1, NULL) == -2
-    assert L.coll_moe_expert_scale(2, NULL, NULL, NULL, 4, 8, 2, NULL) == -2   # fp32
+    assert L.coll_moe_expert_scale(2, NULL, NULL, NULL, 4, 8, 2, 0, NULL) == -2   # fp32
     assert L.coll_moe_combine(2, NULL, NULL, NULL, 4, 2, 8, 1, NULL, NULL) == -2
 
 
@@ -115,8 +115,10 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def test_a2av_null_arrays_rejected_but_null_entries_allowed_on_host(L):
     # the pointer arrays themselves are required
-    assert L.coll_all_to_all_v(2, NULL, 0x10, 0x20, NULL, 0x30, 8, 0, NULL) == -1
+    assert L.coll_all_to_all_v(2, NULL, 0x10, 0x20, NULL, 0x30, 8, 0, 0, NULL) == -1
     # device count tables are required
     ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
-    assert L.coll_all_to_all_v(2, ok, NULL, 0x20, ok, 0x30, 8, 0, NULL) == -1
-    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, NULL, 8, 0, NULL) == -1
+    assert L.coll_all_to_all_v(2, ok, NULL, 0x20, ok, 0x30, 8, 0, 0, NULL) == -1
+    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, NULL, 8, 0, 0, NULL) == -1
+    # an absurd capacity is rejected (it would overflow the launch size)
+    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, 0x30, 8, 0, 1 << 62, NULL) == -1
