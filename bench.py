@@ -175,6 +175,45 @@ EXTRA_ROWS = {
 }
 
 
+def bcast_vs_padded_ag(torch, coll, n_toks=(256, 1024, 4096, 16384), H=7168, owner=3,
+                       iters=20):
+    """The single-image vision-embedding A/B of the sglang PR 33307 digest on
+    one GPU: path A pads every rank to max_len rows (= n_tok here, the best
+    case for A), AllGathers and keeps the owner's slice; path B broadcasts the
+    owner's rows.  Both results are checked bitwise; times are medians."""
+    res = {}
+    for n in n_toks:
+        emb = torch.empty((n, H), dtype=torch.bfloat16, device="cuda").normal_()
+        padded = [torch.zeros_like(emb) for _ in range(R)]
+        padded[owner].copy_(emb)
+        gathered = [torch.empty((R * n, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        outs = [torch.empty_like(emb) for _ in range(R)]
+        outs[owner] = emb
+
+        def med(fn):
+            fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(iters)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) for a, b in ev)
+            return ts[len(ts) // 2]
+
+        ta = med(lambda: coll.all_gather(padded, gathered))
+        tb = med(lambda: coll.broadcast(emb, outs, owner))
+        same = all(torch.equal(gathered[r].view(R, n, H)[owner].view(torch.int16),
+                               outs[r].view(torch.int16)) for r in range(R))
+        res[str(n)] = {"allgather_us": round(ta * 1e3, 2), "broadcast_us": round(tb * 1e3, 2),
+                       "speedup": round(ta / tb, 2), "bitwise_equal": bool(same)}
+        del emb, padded, gathered, outs
+        torch.cuda.empty_cache()
+    return res
+
+
 def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=20):
     """AllReduce R=8 bf16 at large sizes, rotating `sets` buffer sets so the
     working set (>= 1 GiB) exceeds the Infinity Cache."""
@@ -359,6 +398,11 @@ def main():
         print("[bench] allreduce sweep", file=sys.stderr, flush=True)
         sweep = ar_sweep(torch, coll)
 
+    ab = None
+    if not args.no_sweep and not args.only:
+        print("[bench] broadcast vs padded allgather", file=sys.stderr, flush=True)
+        ab = bcast_vs_padded_ag(torch, coll)
+
     cpu = None
     if not args.no_cpu_baseline and not args.only:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -380,6 +424,7 @@ def main():
         "cpu_baseline": cpu,
         "rows": rows_out,
         "allreduce_sweep": sweep,
+        "broadcast_vs_padded_allgather": ab,
     }
     print(json.dumps(out))
 

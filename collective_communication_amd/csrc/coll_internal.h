@@ -337,6 +337,14 @@ inline unsigned grid_for(const Launch &L, size_t work, int per_thread = 1) {
   return (unsigned)need;
 }
 
+// One workgroup per tile of `tile_units` units (single pass), capped likewise.
+inline unsigned grid_tiles(size_t work, size_t tile_units) {
+  size_t need = (work + tile_units - 1) / tile_units;
+  if (need < 1) need = 1;
+  if (need > 0x7FFFFFFFu) need = 0x7FFFFFFFu;
+  return (unsigned)need;
+}
+
 // Resident grid for kernels whose amount of work is only known on the device.
 inline unsigned grid_resident(const Launch &L) {
   return (unsigned)L.num_cus * (unsigned)L.wgs_per_cu;

@@ -21,26 +21,42 @@ namespace {
 
 // ---------------------------------------------------------------- AllReduce
 
-// 16-byte units per lane per tile for an R-way reduction: U * R independent
-// loads in flight per lane without exhausting the VGPR budget.
-#ifndef COLL_RED_U_MID
-#define COLL_RED_U_MID 2        // units per lane for 3 <= R <= 8
+// Tile shape of the R-way reductions (measured on MI355X, R = 8, 16-64 MiB
+// per rank): AllReduce does best with 128-lane workgroups and one 16-byte
+// unit per lane per rank (8 loads in flight per lane, many small tiles);
+// ReduceScatter, whose writes are 1/R of its reads, with 256 lanes x 2 units.
+#ifndef COLL_AR_BLOCK
+#define COLL_AR_BLOCK 128
 #endif
+#ifndef COLL_AR_U_MID
+#define COLL_AR_U_MID 1          // units per lane for 3 <= R <= 8
+#endif
+#ifndef COLL_RS_BLOCK
+#define COLL_RS_BLOCK 256
+#endif
+#ifndef COLL_RS_U_MID
+#define COLL_RS_U_MID 2
+#endif
+constexpr int kArBlock = COLL_AR_BLOCK;
+constexpr int kRsBlock = COLL_RS_BLOCK;
+
 template <int R>
-constexpr int red_u() { return R <= 2 ? 4 : (R <= 8 ? COLL_RED_U_MID : 1); }
+constexpr int ar_u() { return R <= 2 ? 4 : (R <= 8 ? COLL_AR_U_MID : 1); }
+template <int R>
+constexpr int rs_u() { return R <= 2 ? 4 : (R <= 8 ? COLL_RS_U_MID : 1); }
 
 // R known at compile time: all U * R loads of a tile issue back to back.
 template <int R, int DT, int OP, bool NT>
-__global__ __launch_bounds__(kBlock) void ar_vec(RankPtrs p, size_t nvec) {
+__global__ __launch_bounds__(kArBlock) void ar_vec(RankPtrs p, size_t nvec) {
   using F = Fmt<DT>;
-  constexpr int U = red_u<R>();
-  const size_t tile = (size_t)kBlock * U;
+  constexpr int U = ar_u<R>();
+  const size_t tile = (size_t)kArBlock * U;
   for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nvec;
        base += (size_t)gridDim.x * tile) {
     u32x4 v[U][R];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const size_t i = base + (size_t)u * kBlock;
+      const size_t i = base + (size_t)u * kArBlock;
       if (i < nvec) {
 #pragma unroll
         for (int r = 0; r < R; r++) v[u][r] = ld<u32x4, NT>(p.in[r], i);
@@ -48,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void ar_vec(RankPtrs p, size_t nvec) {
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const size_t i = base + (size_t)u * kBlock;
+      const size_t i = base + (size_t)u * kArBlock;
       if (i < nvec) {
         typename F::Acc a = F::widen(v[u][0]);
 #pragma unroll
@@ -114,18 +130,18 @@ __global__ __launch_bounds__(kBlock) void ar_scalar(RankPtrs p, int R, size_t fi
 
 // blockIdx.y = owner rank r: out[r][i] = fold over q of in[q][r*seg + i].
 template <int R, int DT, int OP, bool NT>
-__global__ __launch_bounds__(kBlock) void rs_vec(RankPtrs p, size_t nvec_seg) {
+__global__ __launch_bounds__(kRsBlock) void rs_vec(RankPtrs p, size_t nvec_seg) {
   using F = Fmt<DT>;
-  constexpr int U = red_u<R>();
+  constexpr int U = rs_u<R>();
   const int r = blockIdx.y;
   const size_t off = (size_t)r * nvec_seg;
-  const size_t tile = (size_t)kBlock * U;
+  const size_t tile = (size_t)kRsBlock * U;
   for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nvec_seg;
        base += (size_t)gridDim.x * tile) {
     u32x4 v[U][R];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const size_t i = base + (size_t)u * kBlock;
+      const size_t i = base + (size_t)u * kRsBlock;
       if (i < nvec_seg) {
 #pragma unroll
         for (int q = 0; q < R; q++) v[u][q] = ld<u32x4, NT>(p.in[q], off + i);
@@ -133,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void rs_vec(RankPtrs p, size_t nvec_seg) {
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const size_t i = base + (size_t)u * kBlock;
+      const size_t i = base + (size_t)u * kRsBlock;
       if (i < nvec_seg) {
         typename F::Acc a = F::widen(v[u][0]);
 #pragma unroll
@@ -175,8 +191,8 @@ __global__ __launch_bounds__(kBlock) void rs_scalar(RankPtrs p, int R, size_t se
 
 template <int R, int DT, int OP, bool NT>
 void launch_ar_r(const Launch &L, const RankPtrs &p, size_t nvec) {
-  dim3 grid(grid_for(L, nvec, red_u<R>()));
-  hipLaunchKernelGGL((ar_vec<R, DT, OP, NT>), grid, dim3(kBlock), 0, L.stream, p, nvec);
+  dim3 grid(grid_tiles(nvec, (size_t)ar_u<R>() * kArBlock));
+  hipLaunchKernelGGL((ar_vec<R, DT, OP, NT>), grid, dim3(kArBlock), 0, L.stream, p, nvec);
 }
 
 template <int DT, int OP, bool NT>
@@ -221,8 +237,8 @@ int ar_dispatch(const Launch &L, int R, const RankPtrs &p, size_t count) {
 
 template <int R, int DT, int OP, bool NT>
 void launch_rs_r(const Launch &L, const RankPtrs &p, size_t nvec) {
-  dim3 grid(grid_for(L, nvec, red_u<R>()), R);
-  hipLaunchKernelGGL((rs_vec<R, DT, OP, NT>), grid, dim3(kBlock), 0, L.stream, p, nvec);
+  dim3 grid(grid_tiles(nvec, (size_t)rs_u<R>() * kRsBlock), R);
+  hipLaunchKernelGGL((rs_vec<R, DT, OP, NT>), grid, dim3(kRsBlock), 0, L.stream, p, nvec);
 }
 
 template <int DT, int OP, bool NT>

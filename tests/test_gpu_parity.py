@@ -493,3 +493,27 @@ def moe_gpu_outputs_only(xs, ids, ws, E):
     torch.cuda.synchronize()
     return dict(sc=sc_h, rd=host(rd).reshape(R, R), pos=[host(p) for p in pos],
                 outs=[host(o) for o in outs])
+
+
+# ------------------------------------------- broadcast vs pad-to-max AllGather
+
+@pytest.mark.parametrize("n_tok,max_len", [(37, 37), (1000, 1024), (4096, 4096)])
+def test_single_image_broadcast_equals_padded_allgather(n_tok, max_len):
+    """sglang PR 33307 digest: the owner's embedding broadcast is bitwise equal
+    to the owner's slice of the pad-to-max AllGather (the old path)."""
+    R, owner, H = 8, 3, 7168
+    say("bcast vs padded AG", n_tok, max_len)
+    emb = dev(synth.gaussian((n_tok, H), 1.0, 33307, "bf16"))
+    padded = [torch.zeros((max_len, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    padded[owner][:n_tok].copy_(emb)
+    gathered = [poison_like(torch.empty((R * max_len, H), dtype=torch.bfloat16, device="cuda"))
+                for _ in range(R)]
+    coll.all_gather(padded, gathered)
+    outs = [poison_like(emb) for _ in range(R)]
+    outs[owner] = emb
+    coll.broadcast(emb, outs, owner)
+    torch.cuda.synchronize()
+    for r in range(R):
+        via_ag = gathered[r].view(R, max_len, H)[owner, :n_tok]
+        assert torch.equal(via_ag.view(torch.int16), outs[r].view(torch.int16)), f"rank {r}"
+        assert torch.equal(outs[r].view(torch.int16), emb.view(torch.int16))
