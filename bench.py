@@ -214,6 +214,41 @@ def bcast_vs_padded_ag(torch, coll, n_toks=(256, 1024, 4096, 16384), H=7168, own
     return res
 
 
+def next_rows(torch, coll, iters=20):
+    """Rows beyond the step: Reduce to a root and Scatter from it (R=8, 64 MiB
+    per rank), with their algorithmic bytes ((R+1)*S and 2*R*S)."""
+    res = {}
+    n = (64 << 20) // 2
+    xs = [torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_() for _ in range(R)]
+    out = torch.empty_like(xs[0])
+    root_buf = torch.empty(R * n, dtype=torch.bfloat16, device="cuda").normal_()
+    chunks = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return ts[len(ts) // 2] * 1e-3
+
+    for name, fn, nbytes in (
+            ("reduce_64m", lambda: coll.reduce(xs, out, 0), (R + 1) * n * 2),
+            ("scatter_64m", lambda: coll.scatter(root_buf, chunks, 0), 2 * R * n * 2)):
+        t = med(fn)
+        gbs = nbytes / t / 1e9
+        res[name] = {"us": round(t * 1e6, 2), "bytes": nbytes, "GBps": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del xs, out, root_buf, chunks
+    torch.cuda.empty_cache()
+    return res
+
+
 def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=20):
     """AllReduce R=8 bf16 at large sizes, rotating `sets` buffer sets so the
     working set (>= 1 GiB) exceeds the Infinity Cache."""
@@ -398,10 +433,12 @@ def main():
         print("[bench] allreduce sweep", file=sys.stderr, flush=True)
         sweep = ar_sweep(torch, coll)
 
-    ab = None
+    ab = extra = None
     if not args.no_sweep and not args.only:
         print("[bench] broadcast vs padded allgather", file=sys.stderr, flush=True)
         ab = bcast_vs_padded_ag(torch, coll)
+        print("[bench] reduce / scatter", file=sys.stderr, flush=True)
+        extra = next_rows(torch, coll)
 
     cpu = None
     if not args.no_cpu_baseline and not args.only:
@@ -425,6 +462,7 @@ def main():
         "rows": rows_out,
         "allreduce_sweep": sweep,
         "broadcast_vs_padded_allgather": ab,
+        "next_rows": extra,
     }
     print(json.dumps(out))
 

@@ -32,6 +32,8 @@ SIGNATURES = {
     "coll_version": (_i, []),
     "coll_allreduce": (_i, [_i, _vp, _vp, _sz, _i, _i, _vp]),
     "coll_reduce_scatter": (_i, [_i, _vp, _vp, _sz, _i, _i, _vp]),
+    "coll_reduce": (_i, [_i, _vp, _vp, _i, _sz, _i, _i, _vp]),
+    "coll_scatter": (_i, [_i, _vp, _vp, _i, _sz, _i, _vp]),
     "coll_all_gather": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_gather": (_i, [_i, _vp, _vp, _i, _sz, _sz, _i, _vp]),
     "coll_broadcast": (_i, [_i, _vp, _vp, _i, _sz, _i, _vp]),
@@ -147,6 +149,28 @@ def reduce_scatter(sends, recvs, op: str = "sum", stream=None) -> None:
     _check(lib().coll_reduce_scatter(R, _table(sends, "send"), _table(recvs, "recv"), n,
                                      _reduce_dtype(sends[0]), OPS[op], _stream(stream)),
            "reduce_scatter")
+
+
+def reduce(sends, recv_root, root: int, op: str = "sum", stream=None) -> None:
+    """Reduce: recv_root = reduction of all sends (recv_root may be sends[root])."""
+    R = _ranks(sends, "reduce")
+    n = sends[0].numel()
+    _same(sends, sends[0].dtype, n, "reduce send")
+    _same([recv_root], sends[0].dtype, n, "reduce recv")
+    _check(lib().coll_reduce(R, _table(sends, "send"), _dev(recv_root, "recv"), root, n,
+                             _reduce_dtype(sends[0]), OPS[op], _stream(stream)), "reduce")
+
+
+def scatter(send_root, recvs, root: int, stream=None) -> None:
+    """Scatter: recvs[r] = chunk r of send_root (R equal chunks)."""
+    R = _ranks(recvs, "scatter")
+    n = recvs[0].numel()
+    _same(recvs, send_root.dtype, n, "scatter recv")
+    if send_root.numel() != R * n:
+        raise ValueError("scatter: the root buffer must hold R chunks")
+    dt, mult = _copy_dtype(send_root)
+    _check(lib().coll_scatter(R, _dev(send_root, "send"), _table(recvs, "recv"), root,
+                              n * mult, dt, _stream(stream)), "scatter")
 
 
 def all_gather(sends, recvs, stream=None) -> None:

@@ -123,7 +123,34 @@ int coll_reduce_scatter(int R, const void *const *sendbufs, void *const *recvbuf
   if (!bytes_ok(recvcount, dtype_size(dtype), (size_t)R * (R + 1))) return COLL_ERR_INVALID_ARG;
   RankPtrs p{};
   if (!fill_in(R, sendbufs, p.in) || !fill_out(R, recvbufs, p.out)) return COLL_ERR_INVALID_ARG;
-  return launch_reduce_scatter(launch_ctx(stream), R, p, recvcount, dtype, op);
+  return launch_reduce_scatter(launch_ctx(stream), R, p, recvcount, dtype, op, R);
+}
+
+int coll_reduce(int R, const void *const *sendbufs, void *recvbuf_root, int root, size_t count,
+                coll_dtype_t dtype, coll_op_t op, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || root < 0 || root >= R) return COLL_ERR_INVALID_ARG;
+  if (!op_ok(op)) return COLL_ERR_UNSUPPORTED;
+  if (count == 0) return COLL_OK;
+  if (!recvbuf_root || !bytes_ok(count, dtype_size(dtype), (size_t)R + 1))
+    return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, sendbufs, p.in)) return COLL_ERR_INVALID_ARG;
+  p.out[0] = recvbuf_root;
+  return launch_reduce_scatter(launch_ctx(stream), R, p, count, dtype, op, 1);
+}
+
+int coll_scatter(int R, const void *sendbuf_root, void *const *recvbufs, int root,
+                 size_t recvcount, coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || root < 0 || root >= R) return COLL_ERR_INVALID_ARG;
+  if (recvcount == 0) return COLL_OK;
+  if (!sendbuf_root || !recvbufs || !bytes_ok(recvcount, dtype_size(dtype), 2 * (size_t)R))
+    return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  for (int r = 0; r < R; r++) {
+    if (!recvbufs[r] && r != root) return COLL_ERR_INVALID_ARG;
+    p.out[r] = recvbufs[r];
+  }
+  return launch_scatter(launch_ctx(stream), R, sendbuf_root, p, recvcount * dtype_size(dtype));
 }
 
 int coll_all_gather(int R, const void *const *sendbufs, void *const *recvbufs, size_t sendcount,

@@ -375,11 +375,13 @@ inline int hip_status() {
 
 // ------------------------------------------------------- internal launchers
 int launch_allreduce(const Launch &L, int R, const RankPtrs &p, size_t count, int dt, int op);
-int launch_reduce_scatter(const Launch &L, int R, const RankPtrs &p, size_t recvcount, int dt, int op);
+int launch_reduce_scatter(const Launch &L, int R, const RankPtrs &p, size_t recvcount, int dt, int op,
+                          int nout);
 int launch_all_gather(const Launch &L, int R, const RankPtrs &p, size_t bytes_per_rank);
 int launch_gather(const Launch &L, int R, const RankPtrs &p, void *out, size_t outer,
                   size_t inner_bytes);
 int launch_broadcast(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes);
+int launch_scatter(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes);
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
                 const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
                 size_t rows_capacity);

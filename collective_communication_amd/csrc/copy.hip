@@ -101,7 +101,47 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(const void *src, RankPtrs
   }
 }
 
+// ----------------------------------------------------------------- Scatter
+// blockIdx.y = destination rank r: out[r][i] = root[r*n + i] (tutorial 4).
+// A rank whose buffer is its own chunk of the root buffer is skipped.
+template <int B, bool NT>
+__global__ __launch_bounds__(kBlock) void scatter_kernel(const void *src, RankPtrs p,
+                                                         size_t nunits) {
+  using U = typename UnitT<B>::T;
+  constexpr int UN = kCopyU;
+  const int r = blockIdx.y;
+  const U *s = reinterpret_cast<const U *>(src) + (size_t)r * nunits;
+  void *dst = p.out[r];
+  if (dst == nullptr || dst == (const void *)s) return;
+  const size_t tile = (size_t)kBlock * UN;
+  for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nunits;
+       base += (size_t)gridDim.x * tile) {
+    U v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const size_t i = base + (size_t)u * kBlock;
+      if (i < nunits) v[u] = ld<U, NT>(s, i);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const size_t i = base + (size_t)u * kBlock;
+      if (i < nunits) st<U, NT>(dst, i, v[u]);
+    }
+  }
+}
+
 }  // namespace
+
+int launch_scatter(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes) {
+  uintptr_t bits = bytes | (uintptr_t)src;
+  for (int r = 0; r < R; r++) bits |= (uintptr_t)p.out[r];
+  const int unit = copy_unit(bits);
+  const size_t nunits = bytes / unit;
+  const bool nt = 2 * (size_t)R * bytes >= L.nt_bytes;
+  dim3 grid(grid_for(L, nunits, kCopyU), R);
+  COLL_UNIT_SWITCH(scatter_kernel, unit, nt, grid, L.stream, src, p, nunits);
+  return hip_status();
+}
 
 int launch_all_gather(const Launch &L, int R, const RankPtrs &p, size_t bytes) {
   uintptr_t bits = bytes;

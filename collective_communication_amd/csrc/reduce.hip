@@ -236,43 +236,46 @@ int ar_dispatch(const Launch &L, int R, const RankPtrs &p, size_t count) {
 }
 
 template <int R, int DT, int OP, bool NT>
-void launch_rs_r(const Launch &L, const RankPtrs &p, size_t nvec) {
-  dim3 grid(grid_tiles(nvec, (size_t)rs_u<R>() * kRsBlock), R);
+void launch_rs_r(const Launch &L, const RankPtrs &p, size_t nvec, int nout) {
+  dim3 grid(grid_tiles(nvec, (size_t)rs_u<R>() * kRsBlock), nout);
   hipLaunchKernelGGL((rs_vec<R, DT, OP, NT>), grid, dim3(kRsBlock), 0, L.stream, p, nvec);
 }
 
 template <int DT, int OP, bool NT>
-void rs_vec_dispatch(const Launch &L, int R, const RankPtrs &p, size_t nvec) {
+void rs_vec_dispatch(const Launch &L, int R, const RankPtrs &p, size_t nvec, int nout) {
   if constexpr (OP == COLL_SUM) {
     switch (R) {
-      case 1: return launch_rs_r<1, DT, OP, NT>(L, p, nvec);
-      case 2: return launch_rs_r<2, DT, OP, NT>(L, p, nvec);
-      case 3: return launch_rs_r<3, DT, OP, NT>(L, p, nvec);
-      case 4: return launch_rs_r<4, DT, OP, NT>(L, p, nvec);
-      case 5: return launch_rs_r<5, DT, OP, NT>(L, p, nvec);
-      case 6: return launch_rs_r<6, DT, OP, NT>(L, p, nvec);
-      case 7: return launch_rs_r<7, DT, OP, NT>(L, p, nvec);
-      case 8: return launch_rs_r<8, DT, OP, NT>(L, p, nvec);
-      case 16: return launch_rs_r<16, DT, OP, NT>(L, p, nvec);
+      case 1: return launch_rs_r<1, DT, OP, NT>(L, p, nvec, nout);
+      case 2: return launch_rs_r<2, DT, OP, NT>(L, p, nvec, nout);
+      case 3: return launch_rs_r<3, DT, OP, NT>(L, p, nvec, nout);
+      case 4: return launch_rs_r<4, DT, OP, NT>(L, p, nvec, nout);
+      case 5: return launch_rs_r<5, DT, OP, NT>(L, p, nvec, nout);
+      case 6: return launch_rs_r<6, DT, OP, NT>(L, p, nvec, nout);
+      case 7: return launch_rs_r<7, DT, OP, NT>(L, p, nvec, nout);
+      case 8: return launch_rs_r<8, DT, OP, NT>(L, p, nvec, nout);
+      case 16: return launch_rs_r<16, DT, OP, NT>(L, p, nvec, nout);
       default: break;
     }
   }
-  hipLaunchKernelGGL((rs_vec_rt<DT, OP, NT>), dim3(grid_for(L, nvec), R), dim3(kBlock), 0,
+  hipLaunchKernelGGL((rs_vec_rt<DT, OP, NT>), dim3(grid_for(L, nvec), nout), dim3(kBlock), 0,
                      L.stream, p, R, nvec);
 }
 
+// nout = R: ReduceScatter (owner r = blockIdx.y writes chunk r);
+// nout = 1: Reduce (one output, out[0], of the whole range: seg = count).
 template <int DT, int OP>
-int rs_dispatch(const Launch &L, int R, const RankPtrs &p, size_t seg) {
+int rs_dispatch(const Launch &L, int R, const RankPtrs &p, size_t seg, int nout) {
   constexpr int VL = Fmt<DT>::kLanes;
   bool aligned = (seg % VL) == 0;
-  for (int r = 0; r < R; r++) aligned = aligned && aligned16(p.in[r]) && aligned16(p.out[r]);
-  const bool nt = (size_t)(R + 1) * R * seg * Fmt<DT>::kSize >= L.nt_bytes;
+  for (int r = 0; r < R; r++) aligned = aligned && aligned16(p.in[r]);
+  for (int r = 0; r < nout; r++) aligned = aligned && aligned16(p.out[r]);
+  const bool nt = (size_t)(R + 1) * nout * seg * Fmt<DT>::kSize >= L.nt_bytes;
   if (aligned) {
     const size_t nvec = seg / VL;
-    if (nt) rs_vec_dispatch<DT, OP, true>(L, R, p, nvec);
-    else rs_vec_dispatch<DT, OP, false>(L, R, p, nvec);
+    if (nt) rs_vec_dispatch<DT, OP, true>(L, R, p, nvec, nout);
+    else rs_vec_dispatch<DT, OP, false>(L, R, p, nvec, nout);
   } else {
-    hipLaunchKernelGGL((rs_scalar<DT, OP>), dim3(grid_for(L, seg), R), dim3(kBlock), 0,
+    hipLaunchKernelGGL((rs_scalar<DT, OP>), dim3(grid_for(L, seg), nout), dim3(kBlock), 0,
                        L.stream, p, R, seg);
   }
   return hip_status();
@@ -290,12 +293,12 @@ int ar_by_op(const Launch &L, int R, const RankPtrs &p, size_t count, int op) {
 }
 
 template <int DT>
-int rs_by_op(const Launch &L, int R, const RankPtrs &p, size_t seg, int op) {
+int rs_by_op(const Launch &L, int R, const RankPtrs &p, size_t seg, int op, int nout) {
   switch (op) {
-    case COLL_SUM: return rs_dispatch<DT, COLL_SUM>(L, R, p, seg);
-    case COLL_PROD: return rs_dispatch<DT, COLL_PROD>(L, R, p, seg);
-    case COLL_MAX: return rs_dispatch<DT, COLL_MAX>(L, R, p, seg);
-    case COLL_MIN: return rs_dispatch<DT, COLL_MIN>(L, R, p, seg);
+    case COLL_SUM: return rs_dispatch<DT, COLL_SUM>(L, R, p, seg, nout);
+    case COLL_PROD: return rs_dispatch<DT, COLL_PROD>(L, R, p, seg, nout);
+    case COLL_MAX: return rs_dispatch<DT, COLL_MAX>(L, R, p, seg, nout);
+    case COLL_MIN: return rs_dispatch<DT, COLL_MIN>(L, R, p, seg, nout);
   }
   return COLL_ERR_UNSUPPORTED;
 }
@@ -312,12 +315,13 @@ int launch_allreduce(const Launch &L, int R, const RankPtrs &p, size_t count, in
   return COLL_ERR_UNSUPPORTED;
 }
 
-int launch_reduce_scatter(const Launch &L, int R, const RankPtrs &p, size_t seg, int dt, int op) {
+int launch_reduce_scatter(const Launch &L, int R, const RankPtrs &p, size_t seg, int dt, int op,
+                          int nout) {
   switch (dt) {
-    case COLL_BF16: return rs_by_op<COLL_BF16>(L, R, p, seg, op);
-    case COLL_FP16: return rs_by_op<COLL_FP16>(L, R, p, seg, op);
-    case COLL_FP32: return rs_by_op<COLL_FP32>(L, R, p, seg, op);
-    case COLL_INT32: return rs_by_op<COLL_INT32>(L, R, p, seg, op);
+    case COLL_BF16: return rs_by_op<COLL_BF16>(L, R, p, seg, op, nout);
+    case COLL_FP16: return rs_by_op<COLL_FP16>(L, R, p, seg, op, nout);
+    case COLL_FP32: return rs_by_op<COLL_FP32>(L, R, p, seg, op, nout);
+    case COLL_INT32: return rs_by_op<COLL_INT32>(L, R, p, seg, op, nout);
   }
   return COLL_ERR_UNSUPPORTED;
 }

@@ -111,6 +111,26 @@ int coll_gather(int nranks, const void *const *sendbufs, void *recvbuf_root, int
                 size_t outer, size_t inner, coll_dtype_t dtype, void *stream);
 
 /*
+ * Reduce -- tutorial section 3: the full reduction lands on `root` only.
+ *   sendbufs[r]: `count` elements each; recvbuf_root: `count` elements.
+ *   recvbuf_root[i] = reduction over r (ascending) of sendbufs[r][i], with the
+ *   same arithmetic as coll_allreduce (so it equals AllReduce's output on the
+ *   root bit for bit).  recvbuf_root may be sendbufs[root]; no other overlap.
+ */
+int coll_reduce(int nranks, const void *const *sendbufs, void *recvbuf_root, int root,
+                size_t count, coll_dtype_t dtype, coll_op_t op, void *stream);
+
+/*
+ * Scatter -- tutorial section 4: the root's buffer is cut into nranks equal
+ * chunks of recvcount elements and chunk r goes to rank r.
+ *   recvbufs[r][i] = sendbuf_root[r * recvcount + i].  A pure copy: any dtype.
+ *   recvbufs[root] may be NULL or sendbuf_root + root * recvcount (then not
+ *   written); no other overlap.
+ */
+int coll_scatter(int nranks, const void *sendbuf_root, void *const *recvbufs, int root,
+                 size_t recvcount, coll_dtype_t dtype, void *stream);
+
+/*
  * Broadcast -- tutorial section 1: every rank ends with root's `count`
  * elements, bit for bit.  recvbufs[r] may equal sendbuf_root for r == root
  * (the owner keeps its own tensor, as in the sglang PR 33307 digest); that

@@ -122,3 +122,16 @@ def test_a2av_null_arrays_rejected_but_null_entries_allowed_on_host(L):
     assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, NULL, 8, 0, 0, NULL) == -1
     # an absurd capacity is rejected (it would overflow the launch size)
     assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, 0x30, 8, 0, 1 << 62, NULL) == -1
+
+
+def test_reduce_and_scatter_validation(L):
+    ok = (ctypes.c_void_p * 4)(0x1000, 0x2000, 0x3000, 0x4000)
+    assert L.coll_reduce(4, ok, 0x5000, 4, 8, 0, 0, NULL) == -1      # root out of range
+    assert L.coll_reduce(4, ok, NULL, 0, 8, 0, 0, NULL) == -1        # no root buffer
+    assert L.coll_reduce(4, ok, 0x5000, 0, 8, 0, 7, NULL) == -2      # bad op
+    assert L.coll_reduce(4, ok, 0x5000, 0, 0, 0, 0, NULL) == 0       # empty
+    assert L.coll_scatter(4, 0x1000, ok, -1, 8, 0, NULL) == -1
+    assert L.coll_scatter(4, NULL, ok, 0, 8, 0, NULL) == -1
+    holes = (ctypes.c_void_p * 4)(0x1000, 0, 0x3000, 0x4000)
+    assert L.coll_scatter(4, 0x9000, holes, 0, 8, 0, NULL) == -1     # NULL only at the root
+    assert L.coll_scatter(4, 0x9000, ok, 0, 0, 0, NULL) == 0

@@ -517,3 +517,64 @@ def test_single_image_broadcast_equals_padded_allgather(n_tok, max_len):
         via_ag = gathered[r].view(R, max_len, H)[owner, :n_tok]
         assert torch.equal(via_ag.view(torch.int16), outs[r].view(torch.int16)), f"rank {r}"
         assert torch.equal(outs[r].view(torch.int16), emb.view(torch.int16))
+
+
+# ------------------------------------------------------------ Reduce / Scatter
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", ["sum", "max"])
+@pytest.mark.parametrize("R,n,root", [(1, 5, 0), (3, 4100, 2), (8, 65536, 5), (16, 1001, 15)])
+def test_reduce_to_root(dtype, op, R, n, root):
+    say("reduce", dtype, op, R, n, root)
+    xs = [gen(dtype, n, 1300 + r) for r in range(R)]
+    want = oracle.reduce(xs, root, dtype, op)
+    sends = [to_dev(x, dtype) for x in xs]
+    out = poison_like(sends[0])
+    coll.reduce(sends, out, root, op)
+    torch.cuda.synchronize()
+    assert float_equal_nan_ok(np_of(out, dtype), want, dtype)
+    # equal to AllReduce's output on the root
+    ar = run_allreduce(xs, dtype, op)
+    assert float_equal_nan_ok(np_of(out, dtype), ar[root], dtype)
+
+
+def test_reduce_in_place_on_root_buffer():
+    R, n, root = 8, 8192, 6
+    say("reduce in place")
+    xs = [synth.gaussian(n, 1.0, 1400 + r, "bf16") for r in range(R)]
+    want = oracle.reduce(xs, root, "bf16")
+    sends = [dev(x) for x in xs]
+    coll.reduce(sends, sends[root], root)
+    torch.cuda.synchronize()
+    assert bits_equal(host(sends[root]), want)
+
+
+@pytest.mark.parametrize("R,n,dtype,root", [(8, 1 << 20, "bf16", 0), (3, 7, "bf16", 1),
+                                            (16, 4097, "int32", 9), (1, 100, "fp32", 0)])
+def test_scatter_and_gather_of_scatter(R, n, dtype, root):
+    say("scatter", R, n, dtype, root)
+    x = gen(dtype, R * n, 1500)
+    want = oracle.scatter(x, R, root)
+    src = to_dev(x, dtype)
+    outs = [poison_like(torch.empty(n, dtype=src.dtype, device="cuda")) for _ in range(R)]
+    coll.scatter(src, outs, root)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert bits_equal(host(outs[r]), want[r]), f"rank {r}"
+    back = poison_like(src)
+    coll.gather([o.view(1, n) for o in outs], back.view(1, R * n), root)
+    torch.cuda.synchronize()
+    assert bits_equal(host(back), x)                  # Gather after Scatter = identity
+
+
+def test_scatter_root_keeps_its_chunk_in_place():
+    R, n, root = 4, 1000, 2
+    say("scatter in place")
+    x = synth.gaussian(R * n, 1.0, 1600, "bf16")
+    src = dev(x)
+    outs = [poison_like(torch.empty(n, dtype=torch.bfloat16, device="cuda")) for _ in range(R)]
+    outs[root] = src[root * n:(root + 1) * n]
+    coll.scatter(src, outs, root)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert bits_equal(host(outs[r]), x[r * n:(r + 1) * n])
