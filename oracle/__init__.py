@@ -73,11 +73,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_moe_permute.argtypes = [i32, vp, vp, i32, i32, sz, vp]
         L.oracle_moe_expert_scale.argtypes = [i32, vp, vp, i64p, i32, sz]
         L.oracle_moe_combine.argtypes = [i32, vp, vp, vp, i32, i32, sz, vp]
+        L.oracle_all_to_all.argtypes = [i32, vp, vp, sz, sz]
+        L.oracle_ulysses.argtypes = [i32, vp, vp, sz, sz, sz, sz, i32]
         for name in ("oracle_allreduce", "oracle_reduce", "oracle_reduce_scatter",
                      "oracle_all_gather", "oracle_gather", "oracle_scatter",
                      "oracle_broadcast", "oracle_all_to_all_v", "oracle_moe_layout",
                      "oracle_moe_permute", "oracle_moe_expert_scale",
-                     "oracle_moe_combine"):
+                     "oracle_moe_combine", "oracle_all_to_all", "oracle_ulysses"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -334,3 +336,25 @@ def moe_pipeline(xs, ids, w, E: int):
     backs = all_to_all_v(ys, sc.T.copy(), rd, sd, send_rows_back, H)
     outs = moe_combine(backs, lay["pos"], w, H)
     return dict(layout=lay, sends=sends, recvs=recvs, ys=ys, backs=backs, outs=outs)
+
+
+def all_to_all(xs):
+    """all_to_all_single with equal splits: out[d][s*n+i] = in[s][d*n+i]."""
+    xs = [np.ascontiguousarray(x).reshape(-1) for x in xs]
+    R = len(xs)
+    assert xs[0].size % R == 0
+    n = xs[0].size // R
+    outs = [np.empty_like(xs[0]) for _ in range(R)]
+    _check(lib().oracle_all_to_all(R, _ptrs(xs), _ptrs(outs), n, xs[0].itemsize), "all_to_all")
+    return outs
+
+
+def ulysses(xs, SL: int, H: int, D: int, to_heads: bool):
+    """Sequence <-> heads re-shard: to_heads maps x_s [SL, H, D] to
+    y_d [R*SL, H/R, D]; otherwise the inverse."""
+    xs = [np.ascontiguousarray(x).reshape(-1) for x in xs]
+    R = len(xs)
+    outs = [np.empty_like(xs[0]) for _ in range(R)]
+    _check(lib().oracle_ulysses(R, _ptrs(xs), _ptrs(outs), SL, H, D, xs[0].itemsize,
+                                1 if to_heads else 0), "ulysses")
+    return outs

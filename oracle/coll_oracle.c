@@ -485,3 +485,49 @@ void oracle_f16_to_f32_n(size_t n, const uint16_t *in, float *out)
 {
     for (size_t i = 0; i < n; i++) out[i] = oracle_f16_to_f32(in[i]);
 }
+
+/* ------------------------------------------------------------------ */
+/* Uniform all-to-all and the sequence <-> heads re-shard              */
+/* ------------------------------------------------------------------ */
+
+/* all_to_all_single with equal splits (sglang PR 27492 digest; tutorial
+ * 8.1): rank s's buffer is R chunks of n elements, chunk d for rank d;
+ * rank d receives them ordered by source: out[d][s*n + i] = in[s][d*n + i]. */
+int oracle_all_to_all(int R, const void *const *in, void *const *out, size_t n,
+                      size_t elem_size)
+{
+    if (R < 1 || R > 64 || elem_size == 0) return O_EINVAL;
+    size_t b = n * elem_size;
+    for (int s = 0; s < R; s++)
+        for (int d = 0; d < R; d++)
+            memcpy((char *)out[d] + (size_t)s * b, (const char *)in[s] + (size_t)d * b, b);
+    return O_OK;
+}
+
+/* Sequence-parallel re-shard used for all-to-all sequence parallelism at the
+ * model level (sglang PR 27492 digest's motivation): rank s holds its
+ * sequence chunk of all heads, x_s[t][h][c] with t < SL, h < H, c < D; after
+ * the exchange rank d holds the whole sequence for its head group,
+ * y_d[s*SL + t][h'][c] = x_s[t][d*(H/R) + h'][c].  to_heads = 0 is the
+ * inverse map (y -> x). */
+int oracle_ulysses(int R, const void *const *in, void *const *out, size_t SL, size_t H,
+                   size_t D, size_t elem_size, int to_heads)
+{
+    if (R < 1 || R > 64 || elem_size == 0 || H % (size_t)R != 0) return O_EINVAL;
+    size_t HR = H / (size_t)R;
+    for (int s = 0; s < R; s++)
+        for (size_t t = 0; t < SL; t++)
+            for (int d = 0; d < R; d++)
+                for (size_t hh = 0; hh < HR; hh++)
+                    for (size_t c = 0; c < D; c++) {
+                        size_t xi = (t * H + (size_t)d * HR + hh) * D + c;        /* in x_s */
+                        size_t yi = (((size_t)s * SL + t) * HR + hh) * D + c;     /* in y_d */
+                        if (to_heads)
+                            memcpy((char *)out[d] + yi * elem_size,
+                                   (const char *)in[s] + xi * elem_size, elem_size);
+                        else
+                            memcpy((char *)out[s] + xi * elem_size,
+                                   (const char *)in[d] + yi * elem_size, elem_size);
+                    }
+    return O_OK;
+}

@@ -446,3 +446,48 @@ def test_moe_combine_closed_form_bound():
         # a dropped expert term is far outside the bound for most elements
         drop = (ws[s][:, 1:].astype(np.float64) * (1 + ids[s][:, 1:] / 256.0)).sum(axis=1)[:, None]
         assert np.mean(np.abs(x * drop - exact) > bound) > 0.9
+
+
+# ---------------------------------------- uniform all-to-all, Ulysses re-shard
+
+@pytest.mark.parametrize("R", [1, 2, 3, 8])
+def test_uniform_all_to_all_is_block_transpose(R):
+    n = 7
+    xs = [synth.random_bits(R * n, 2, 80 + s) for s in range(R)]
+    outs = oracle.all_to_all(xs)
+    blocks = np.stack(xs).reshape(R, R, n).transpose(1, 0, 2)
+    for d in range(R):
+        assert np.array_equal(outs[d], blocks[d].reshape(-1))
+    # it is All-to-All-v with equal counts
+    counts = np.full((R, R), n, np.int64)
+    sd, rd = oracle.packed_displs(counts)
+    v = oracle.all_to_all_v(xs, counts, sd, rd, counts.sum(axis=0), 1)
+    for d in range(R):
+        assert np.array_equal(outs[d], v[d])
+
+
+def test_uniform_all_to_all_single_rank_is_copy():
+    x = synth.random_bits(33, 4, 3)
+    assert np.array_equal(oracle.all_to_all([x])[0], x)
+
+
+@pytest.mark.parametrize("R,SL,H,D", [(1, 3, 4, 2), (2, 4, 4, 3), (4, 5, 8, 16), (8, 3, 32, 8)])
+def test_ulysses_matches_concat_and_head_slice(R, SL, H, D):
+    """to_heads: rank d's result is the full sequence (ranks' chunks in rank
+    order) of heads [d*H/R, (d+1)*H/R) -- numpy concatenate + slice."""
+    xs = [synth.random_bits((SL, H, D), 2, 200 + s) for s in range(R)]
+    ys = oracle.ulysses(xs, SL, H, D, to_heads=True)
+    full = np.concatenate(xs, axis=0)                # [R*SL, H, D]
+    HR = H // R
+    for d in range(R):
+        assert np.array_equal(ys[d].reshape(R * SL, HR, D), full[:, d * HR:(d + 1) * HR, :])
+    back = oracle.ulysses(ys, SL, H, D, to_heads=False)
+    for s in range(R):
+        assert np.array_equal(back[s], xs[s].reshape(-1))
+
+
+def test_ulysses_with_one_sequence_row_is_the_uniform_all_to_all():
+    R, H, D = 4, 8, 5
+    xs = [synth.random_bits((1, H, D), 4, 300 + s) for s in range(R)]
+    assert all(np.array_equal(a, b) for a, b in
+               zip(oracle.ulysses(xs, 1, H, D, True), oracle.all_to_all(xs)))
