@@ -215,8 +215,10 @@ def bcast_vs_padded_ag(torch, coll, n_toks=(256, 1024, 4096, 16384), H=7168, own
 
 
 def next_rows(torch, coll, iters=20):
-    """Rows beyond the step: Reduce to a root and Scatter from it (R=8, 64 MiB
-    per rank), with their algorithmic bytes ((R+1)*S and 2*R*S)."""
+    """Rows beyond the step, with their algorithmic bytes: Reduce to a root and
+    Scatter from it (R=8, 64 MiB per rank: (R+1)*S and 2*R*S), the uniform
+    all-to-all (2*R*S) and the sequence <-> heads re-shard of all-to-all
+    sequence parallelism (2 * bytes of all ranks)."""
     res = {}
     n = (64 << 20) // 2
     xs = [torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_() for _ in range(R)]
@@ -237,14 +239,27 @@ def next_rows(torch, coll, iters=20):
         ts = sorted(a.elapsed_time(b) for a, b in ev)
         return ts[len(ts) // 2] * 1e-3
 
+    a2a_out = [torch.empty_like(x) for x in xs]
+    # all-to-all sequence parallelism: 32768-token sequence over 8 ranks,
+    # 32 heads x 128, bf16 (32 MiB per rank each way)
+    SL, H, D = 4096, 32, 128
+    seq = [torch.empty((SL, H, D), dtype=torch.bfloat16, device="cuda").normal_()
+           for _ in range(R)]
+    heads = [torch.empty_like(t) for t in seq]
+    seq_back = [torch.empty_like(t) for t in seq]
+    rb = R * SL * H * D * 2
     for name, fn, nbytes in (
             ("reduce_64m", lambda: coll.reduce(xs, out, 0), (R + 1) * n * 2),
-            ("scatter_64m", lambda: coll.scatter(root_buf, chunks, 0), 2 * R * n * 2)):
+            ("scatter_64m", lambda: coll.scatter(root_buf, chunks, 0), 2 * R * n * 2),
+            ("all_to_all_64m", lambda: coll.all_to_all(xs, a2a_out), 2 * R * n * 2),
+            ("seq_to_heads_32k", lambda: coll.seq_heads_reshard(seq, heads, H, D, True), 2 * rb),
+            ("heads_to_seq_32k", lambda: coll.seq_heads_reshard(heads, seq_back, H, D, False),
+             2 * rb)):
         t = med(fn)
         gbs = nbytes / t / 1e9
         res[name] = {"us": round(t * 1e6, 2), "bytes": nbytes, "GBps": round(gbs, 1),
                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    del xs, out, root_buf, chunks
+    del xs, out, root_buf, chunks, a2a_out, seq, heads, seq_back
     torch.cuda.empty_cache()
     return res
 

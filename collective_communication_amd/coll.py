@@ -38,6 +38,8 @@ SIGNATURES = {
     "coll_gather": (_i, [_i, _vp, _vp, _i, _sz, _sz, _i, _vp]),
     "coll_broadcast": (_i, [_i, _vp, _vp, _i, _sz, _i, _vp]),
     "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp]),
+    "coll_all_to_all": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
+    "coll_seq_heads_reshard": (_i, [_i, _vp, _vp, _sz, _sz, _sz, _i, _i, _vp]),
     "coll_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "coll_moe_layout": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
@@ -229,6 +231,36 @@ def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
                                    _dev(sdispls, "sdispls"), _table(recvs, "recv"),
                                    _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity,
                                    _stream(stream)), "all_to_all_v")
+
+
+def all_to_all(sends, recvs, stream=None) -> None:
+    """all_to_all_single with equal splits: recvs[d][s*n+i] = sends[s][d*n+i]."""
+    R = _ranks(sends, "all_to_all")
+    total = sends[0].numel()
+    if total % R:
+        raise ValueError("all_to_all: the send buffer must split into R equal chunks")
+    _same(sends, sends[0].dtype, total, "all_to_all send")
+    _same(recvs, sends[0].dtype, total, "all_to_all recv")
+    dt, mult = _copy_dtype(sends[0])
+    _check(lib().coll_all_to_all(R, _table(sends, "send"), _table(recvs, "recv"),
+                                 total // R * mult, dt, _stream(stream)), "all_to_all")
+
+
+def seq_heads_reshard(ins, outs, heads: int, head_dim: int, to_heads: bool,
+                      stream=None) -> None:
+    """[SL, H, D] per rank <-> [R*SL, H/R, D] per rank (to_heads selects the
+    direction)."""
+    R = _ranks(ins, "seq_heads_reshard")
+    per = ins[0].numel()
+    if heads % R or per % (heads * head_dim):
+        raise ValueError("seq_heads_reshard: heads must divide by R and rows must be whole")
+    SL = per // (heads * head_dim)          # both layouts hold SL*H*D elements per rank
+    _same(ins, ins[0].dtype, per, "seq_heads_reshard in")
+    _same(outs, ins[0].dtype, per, "seq_heads_reshard out")
+    dt, mult = _copy_dtype(ins[0])
+    _check(lib().coll_seq_heads_reshard(R, _table(ins, "in"), _table(outs, "out"), SL, heads,
+                                        head_dim * mult, dt, 1 if to_heads else 0,
+                                        _stream(stream)), "seq_heads_reshard")
 
 
 def moe_workspace_bytes(R: int, tokens: int, topk: int, n_experts: int) -> int:

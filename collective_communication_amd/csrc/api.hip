@@ -209,6 +209,33 @@ int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcou
                      row_elems * dtype_size(dtype), recv_rows_capacity);
 }
 
+int coll_all_to_all(int R, const void *const *sendbufs, void *const *recvbufs,
+                    size_t count_per_peer, coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (count_per_peer == 0) return COLL_OK;
+  if (!bytes_ok(count_per_peer, dtype_size(dtype), 2 * (size_t)R * R)) return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, sendbufs, p.in) || !fill_out(R, recvbufs, p.out)) return COLL_ERR_INVALID_ARG;
+  // one sequence row whose R chunks are the per-peer blocks
+  return launch_reshard(launch_ctx(stream), R, p, 1, count_per_peer * dtype_size(dtype), true);
+}
+
+int coll_seq_heads_reshard(int R, const void *const *in, void *const *out, size_t seq_local,
+                           size_t heads, size_t head_dim, coll_dtype_t dtype, int to_heads,
+                           void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || heads == 0 || heads % (size_t)R != 0)
+    return COLL_ERR_INVALID_ARG;
+  if (seq_local == 0 || head_dim == 0) return COLL_OK;
+  const size_t chunk = heads / (size_t)R * head_dim;
+  if (!bytes_ok(chunk, dtype_size(dtype), 1) ||
+      !bytes_ok(seq_local, chunk * dtype_size(dtype), 2 * (size_t)R * R))
+    return COLL_ERR_INVALID_ARG;
+  RankPtrs p{};
+  if (!fill_in(R, in, p.in) || !fill_out(R, out, p.out)) return COLL_ERR_INVALID_ARG;
+  return launch_reshard(launch_ctx(stream), R, p, seq_local, chunk * dtype_size(dtype),
+                        to_heads != 0);
+}
+
 size_t coll_moe_workspace_bytes(int R, int tokens, int topk, int n_experts) {
   if (!ranks_ok(R) || tokens < 0 || topk < 1 || n_experts < 1 || n_experts > kMoeMaxExperts ||
       n_experts % R != 0 || (int64_t)tokens * topk >= ((int64_t)1 << 31))

@@ -382,6 +382,8 @@ int launch_gather(const Launch &L, int R, const RankPtrs &p, void *out, size_t o
                   size_t inner_bytes);
 int launch_broadcast(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes);
 int launch_scatter(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes);
+int launch_reshard(const Launch &L, int R, const RankPtrs &p, size_t seq_local,
+                   size_t chunk_bytes, bool to_heads);
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
                 const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
                 size_t rows_capacity);

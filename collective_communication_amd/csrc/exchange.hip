@@ -1,0 +1,103 @@
+// exchange.hip -- the uniform all-to-all and the sequence <-> heads re-shard.
+//
+// all_to_all_single with equal splits (sglang PR 27492 digest; tutorial
+// section 8.1): rank s's buffer is R chunks, chunk d for rank d; rank d
+// receives them ordered by source.  The all-to-all sequence parallelism that
+// motivates it re-shards attention inputs between "my sequence chunk, all
+// heads" [SL, H, D] and "the whole sequence, my head group" [R*SL, H/R, D].
+// Frameworks do that as a transpose into contiguous per-destination chunks
+// followed by all_to_all_single; here one kernel gathers the strided chunks
+// directly, so no packed copy exists.
+//
+// Both maps move rows of C = (H/R)*D elements between a source and a
+// destination rank:
+//   to_heads:  y_d[(s*SL + t)] <- x_s[t] chunk d    (row q = s*SL + t of y_d)
+//   to_seq:    x_s[t] chunk d  <- y_d[(s*SL + t)]   (row q = t*R + d of x_s)
+// The uniform all-to-all is to_heads with SL = 1.  blockIdx.y is the
+// destination rank; its output is streamed in 16-byte units, one workgroup
+// per tile, each unit finding its source row with two fast divisions.
+#include "coll_internal.h"
+
+namespace coll {
+namespace {
+
+template <int B, bool NT, bool TO_HEADS>
+__device__ __forceinline__ void reshard_body(const RankPtrs &p, int R, uint64_t SL,
+                                             uint64_t total, const FastDiv64 &cu,
+                                             const FastDiv64 &div2) {
+  using U = typename UnitT<B>::T;
+  constexpr int UN = kCopyU;
+  const int y = blockIdx.y;                       // destination rank
+  void *dst = p.out[y];
+  const uint64_t tile = (uint64_t)kBlock * UN;
+  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
+       base += (uint64_t)gridDim.x * tile) {
+    U v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t x = base + (uint64_t)u * kBlock;
+      if (x < total) {
+        const uint64_t q = fdiv64(x, cu);          // destination row
+        const uint64_t j = x - q * cu.d;            // unit within the row
+        const uint64_t a = fdiv64(q, div2);
+        const uint64_t b = q - a * div2.d;
+        const void *src;
+        uint64_t at;
+        if constexpr (TO_HEADS) {                   // a = source s, b = t
+          src = p.in[a];
+          at = (b * (uint64_t)R + (uint64_t)y) * cu.d + j;
+        } else {                                    // a = t, b = source d
+          src = p.in[b];
+          at = ((uint64_t)y * SL + a) * cu.d + j;
+        }
+        v[u] = ld<U, NT>(src, at);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t x = base + (uint64_t)u * kBlock;
+      if (x < total) st<U, NT>(dst, x, v[u]);
+    }
+  }
+}
+
+template <int B, bool NT>
+__global__ __launch_bounds__(kBlock) void to_heads_kernel(RankPtrs p, int R, uint64_t SL,
+                                                          uint64_t total, FastDiv64 cu,
+                                                          FastDiv64 sl) {
+  reshard_body<B, NT, true>(p, R, SL, total, cu, sl);
+}
+template <int B, bool NT>
+__global__ __launch_bounds__(kBlock) void to_seq_kernel(RankPtrs p, int R, uint64_t SL,
+                                                        uint64_t total, FastDiv64 cu,
+                                                        FastDiv64 rr) {
+  reshard_body<B, NT, false>(p, R, SL, total, cu, rr);
+}
+
+}  // namespace
+
+// chunk_bytes = (H/R)*D*elem; seq_local rows per rank.
+int launch_reshard(const Launch &L, int R, const RankPtrs &p, size_t seq_local,
+                   size_t chunk_bytes, bool to_heads) {
+  uintptr_t bits = chunk_bytes;
+  for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
+  const int unit = copy_unit(bits);
+  const uint64_t cu = chunk_bytes / unit;                 // units per row
+  const uint64_t total = (uint64_t)R * seq_local * cu;    // units per destination
+  if (total == 0) return COLL_OK;
+  const FastDiv64 fcu = make_fastdiv64(cu);
+  const bool nt = 2 * (uint64_t)R * total * unit >= L.nt_bytes;
+  dim3 grid(grid_for(L, total, kCopyU), R);
+  if (to_heads) {
+    const FastDiv64 fsl = make_fastdiv64(seq_local);
+    COLL_UNIT_SWITCH(to_heads_kernel, unit, nt, grid, L.stream, p, R, (uint64_t)seq_local,
+                     total, fcu, fsl);
+  } else {
+    const FastDiv64 fr = make_fastdiv64((uint64_t)R);
+    COLL_UNIT_SWITCH(to_seq_kernel, unit, nt, grid, L.stream, p, R, (uint64_t)seq_local, total,
+                     fcu, fr);
+  }
+  return hip_status();
+}
+
+}  // namespace coll

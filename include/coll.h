@@ -167,6 +167,31 @@ int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *se
                       size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
                       void *stream);
 
+/*
+ * Uniform all-to-all -- all_to_all_single with equal splits (sglang PR 27492
+ * digest; tutorial section 8.1's figure): sendbufs[s] holds nranks chunks of
+ * count_per_peer elements, chunk d for rank d; rank d receives them ordered
+ * by source: recvbufs[d][s * count_per_peer + i] = sendbufs[s][d * count_per_peer + i].
+ * With one rank it is a copy.  Send and receive buffers must not overlap.
+ */
+int coll_all_to_all(int nranks, const void *const *sendbufs, void *const *recvbufs,
+                    size_t count_per_peer, coll_dtype_t dtype, void *stream);
+
+/*
+ * Sequence <-> heads re-shard of all-to-all sequence parallelism (the use the
+ * sglang PR 27492 digest gives for all_to_all_single): with SL = seq_local,
+ * H = heads (a multiple of nranks), HR = H / nranks, D = head_dim,
+ *   to_heads = 1:  in[s] is [SL, H, D] (rank s's sequence chunk, all heads);
+ *                  out[d] is [nranks*SL, HR, D] (the whole sequence, head group d):
+ *                  out[d][s*SL + t][h][c] = in[s][t][d*HR + h][c]
+ *   to_heads = 0:  the inverse map (in is [nranks*SL, HR, D] per rank).
+ * The strided head groups are gathered in the exchange itself (no packed
+ * copy).  Inputs and outputs must not overlap.
+ */
+int coll_seq_heads_reshard(int nranks, const void *const *in, void *const *out,
+                           size_t seq_local, size_t heads, size_t head_dim, coll_dtype_t dtype,
+                           int to_heads, void *stream);
+
 /* ---------------------------------------------------------------------------
  * MoE dispatch / combine over expert parallelism -- tutorial section 8.4.
  * Experts are placed on ranks in contiguous blocks: rank d owns experts

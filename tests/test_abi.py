@@ -135,3 +135,13 @@ def test_reduce_and_scatter_validation(L):
     holes = (ctypes.c_void_p * 4)(0x1000, 0, 0x3000, 0x4000)
     assert L.coll_scatter(4, 0x9000, holes, 0, 8, 0, NULL) == -1     # NULL only at the root
     assert L.coll_scatter(4, 0x9000, ok, 0, 0, 0, NULL) == 0
+
+
+def test_all_to_all_and_reshard_validation(L):
+    ok = (ctypes.c_void_p * 4)(0x1000, 0x2000, 0x3000, 0x4000)
+    assert L.coll_all_to_all(0, ok, ok, 8, 0, NULL) == -1
+    assert L.coll_all_to_all(4, ok, ok, 0, 0, NULL) == 0
+    assert L.coll_all_to_all(4, NULL, ok, 8, 0, NULL) == -1
+    assert L.coll_seq_heads_reshard(4, ok, ok, 16, 6, 128, 0, 1, NULL) == -1   # 6 % 4 != 0
+    assert L.coll_seq_heads_reshard(4, ok, ok, 0, 8, 128, 0, 1, NULL) == 0
+    assert L.coll_seq_heads_reshard(4, ok, NULL, 16, 8, 128, 0, 1, NULL) == -1

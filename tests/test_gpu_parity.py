@@ -578,3 +578,37 @@ def test_scatter_root_keeps_its_chunk_in_place():
     torch.cuda.synchronize()
     for r in range(R):
         assert bits_equal(host(outs[r]), x[r * n:(r + 1) * n])
+
+
+# ------------------------------------- uniform all-to-all / Ulysses re-shard
+
+@pytest.mark.parametrize("R,n,dtype", [(1, 100, "bf16"), (2, 8, "bf16"), (3, 5, "fp32"),
+                                       (8, 1 << 17, "bf16"), (16, 33, "int32")])
+def test_uniform_all_to_all(R, n, dtype):
+    say("all_to_all", R, n, dtype)
+    xs = [gen(dtype, R * n, 1700 + s) for s in range(R)]
+    want = oracle.all_to_all(xs)
+    sends = [to_dev(x, dtype) for x in xs]
+    recvs = [poison_like(s) for s in sends]
+    coll.all_to_all(sends, recvs)
+    torch.cuda.synchronize()
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), f"dest {d}"
+
+
+@pytest.mark.parametrize("R,SL,H,D", [(1, 3, 4, 8), (2, 5, 4, 3), (4, 17, 8, 16),
+                                      (8, 512, 32, 128), (8, 3, 16, 5)])
+def test_seq_heads_reshard_round_trip(R, SL, H, D):
+    say("reshard", R, SL, H, D)
+    xs = [synth.gaussian((SL, H, D), 1.0, 1800 + s, "bf16") for s in range(R)]
+    want = oracle.ulysses(xs, SL, H, D, to_heads=True)
+    ins = [dev(x) for x in xs]
+    mid = [poison_like(t) for t in ins]
+    coll.seq_heads_reshard(ins, mid, H, D, to_heads=True)
+    back = [poison_like(t) for t in ins]
+    coll.seq_heads_reshard(mid, back, H, D, to_heads=False)
+    torch.cuda.synchronize()
+    for d in range(R):
+        assert bits_equal(host(mid[d]).reshape(-1), want[d]), f"to_heads dest {d}"
+    for s in range(R):
+        assert bits_equal(host(back[s]), xs[s]), f"round trip rank {s}"
