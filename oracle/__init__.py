@@ -75,11 +75,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_moe_combine.argtypes = [i32, vp, vp, vp, i32, i32, sz, vp]
         L.oracle_all_to_all.argtypes = [i32, vp, vp, sz, sz]
         L.oracle_ulysses.argtypes = [i32, vp, vp, sz, sz, sz, sz, i32]
+        L.oracle_lse_merge.argtypes = [i32, vp, vp, vp, vp, sz, sz, i32]
         for name in ("oracle_allreduce", "oracle_reduce", "oracle_reduce_scatter",
                      "oracle_all_gather", "oracle_gather", "oracle_scatter",
                      "oracle_broadcast", "oracle_all_to_all_v", "oracle_moe_layout",
                      "oracle_moe_permute", "oracle_moe_expert_scale",
-                     "oracle_moe_combine", "oracle_all_to_all", "oracle_ulysses"):
+                     "oracle_moe_combine", "oracle_all_to_all", "oracle_ulysses",
+                     "oracle_lse_merge"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -358,3 +360,20 @@ def ulysses(xs, SL: int, H: int, D: int, to_heads: bool):
     _check(lib().oracle_ulysses(R, _ptrs(xs), _ptrs(outs), SL, H, D, xs[0].itemsize,
                                 1 if to_heads else 0), "ulysses")
     return outs
+
+
+def lse_merge(o_parts, lse_parts, dtype: str):
+    """Context-parallel merge (primitives tutorial 5.4.2 / 7.4.3): partial
+    attention outputs o_r [rows, D] with their log-sum-exps l_r [rows] (fp32)
+    -> the corrected sum o and L = log sum exp l_r, in fp64, rounded once.
+    Returns (o, L) (every rank receives the same)."""
+    o_parts = [_bits(o, dtype) for o in o_parts]
+    lse_parts = [np.ascontiguousarray(l, np.float32) for l in lse_parts]
+    R = len(o_parts)
+    rows = lse_parts[0].size
+    D = o_parts[0].size // rows
+    outs = [np.empty_like(o_parts[0]) for _ in range(R)]
+    ls = [np.empty(rows, np.float32) for _ in range(R)]
+    _check(lib().oracle_lse_merge(R, _ptrs(o_parts), _ptrs(lse_parts), _ptrs(outs), _ptrs(ls),
+                                  rows, D, DTYPES[dtype]), "lse_merge")
+    return outs[0], ls[0]

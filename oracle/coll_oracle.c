@@ -531,3 +531,46 @@ int oracle_ulysses(int R, const void *const *in, void *const *out, size_t SL, si
                     }
     return O_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Context-parallel merge of partial attention (tutorial 5.4.2, 7.4.3) */
+/* ------------------------------------------------------------------ */
+
+/* Each rank holds, per (token, head) row, a partial attention output o_r
+ * normalised over its own key chunk and that chunk's log-sum-exp l_r.  The
+ * pages: the partial outputs cannot be summed as they are; the LSEs are
+ * gathered first and the corrected contributions are then summed.  Written
+ * out in fp64:
+ *     m = max_r l_r,  e_r = exp(l_r - m),  s = sum_r e_r (r ascending),
+ *     L = m + log(s),  o = sum_r (e_r / s) * o_r (r ascending),
+ * rounded once to the output type; every rank receives (o, L).  A row whose
+ * chunks are all empty (every l_r = -inf) gives o = 0, L = -inf.
+ * dt is the dtype of o (bf16 or fp32); lse are fp32. */
+int oracle_lse_merge(int R, const void *const *o_parts, const float *const *lse_parts,
+                     void *const *o_out, float *const *lse_out, size_t rows, size_t D, int dt)
+{
+    if (R < 1 || R > 64 || (dt != O_BF16 && dt != O_FP32)) return O_EINVAL;
+    for (size_t i = 0; i < rows; i++) {
+        double m = -INFINITY;
+        for (int r = 0; r < R; r++)
+            if ((double)lse_parts[r][i] > m) m = (double)lse_parts[r][i];
+        double e[64], s = 0.0, L;
+        if (m == -INFINITY) {
+            for (int r = 0; r < R; r++) e[r] = 0.0;
+            L = -INFINITY;
+        } else {
+            for (int r = 0; r < R; r++) { e[r] = exp((double)lse_parts[r][i] - m); s += e[r]; }
+            L = m + log(s);
+        }
+        for (size_t c = 0; c < D; c++) {
+            double acc = 0.0;
+            if (m != -INFINITY)
+                for (int r = 0; r < R; r++)
+                    acc += (e[r] / s) * (double)load_fp(o_parts[r], i * D + c, dt);
+            for (int r = 0; r < R; r++) store_fp(o_out[r], i * D + c, dt, (float)acc);
+        }
+        for (int r = 0; r < R; r++)
+            if (lse_out && lse_out[r]) lse_out[r][i] = (float)L;
+    }
+    return O_OK;
+}

@@ -491,3 +491,60 @@ def test_ulysses_with_one_sequence_row_is_the_uniform_all_to_all():
     xs = [synth.random_bits((1, H, D), 4, 300 + s) for s in range(R)]
     assert all(np.array_equal(a, b) for a, b in
                zip(oracle.ulysses(xs, 1, H, D, True), oracle.all_to_all(xs)))
+
+
+# -------------------------------------------- context-parallel LSE merge
+
+def _partial_attention(q, k, v):
+    """fp64 softmax attention of queries q [T, D] over keys k [N, D]: returns
+    (o [T, D], lse [T]).  An empty key set gives o = 0, lse = -inf."""
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1])), np.full(q.shape[0], -np.inf)
+    s = q @ k.T
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    z = p.sum(axis=1, keepdims=True)
+    return (p @ v) / z, (m + np.log(z))[:, 0]
+
+
+@pytest.mark.parametrize("R,N", [(1, 40), (2, 64), (4, 100), (8, 333)])
+def test_lse_merge_reproduces_full_attention(R, N):
+    """Attention over all keys = the merge of attention over R key chunks
+    (independent full-softmax formulation, numpy fp64)."""
+    g = np.random.default_rng(R * 31 + N)
+    T, D = 24, 16
+    q, k, v = g.normal(size=(T, D)), g.normal(size=(N, D)), g.normal(size=(N, D))
+    full_o, full_l = _partial_attention(q, k, v)
+    cuts = np.linspace(0, N, R + 1).astype(int)
+    parts = [_partial_attention(q, k[a:b], v[a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
+    o, l = oracle.lse_merge([p[0].astype(np.float32) for p in parts],
+                            [p[1].astype(np.float32) for p in parts], "fp32")
+    assert np.allclose(o.reshape(T, D), full_o, rtol=1e-5, atol=1e-6)
+    assert np.allclose(l, full_l, rtol=1e-6, atol=1e-5)
+
+
+def test_lse_merge_with_empty_chunks_and_all_empty_rows():
+    g = np.random.default_rng(5)
+    T, D, N = 6, 8, 10
+    q, k, v = g.normal(size=(T, D)), g.normal(size=(N, D)), g.normal(size=(N, D))
+    full_o, full_l = _partial_attention(q, k, v)
+    parts = [_partial_attention(q, k[:0], v[:0]), _partial_attention(q, k, v),
+             _partial_attention(q, k[:0], v[:0])]
+    o, l = oracle.lse_merge([p[0].astype(np.float32) for p in parts],
+                            [p[1].astype(np.float32) for p in parts], "fp32")
+    assert np.allclose(o.reshape(T, D), full_o, rtol=1e-5, atol=1e-6)
+    empty = [_partial_attention(q, k[:0], v[:0])] * 2
+    o, l = oracle.lse_merge([p[0].astype(np.float32) for p in empty],
+                            [p[1].astype(np.float32) for p in empty], "fp32")
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+def test_lse_merge_single_rank_is_identity_and_equal_lse_is_mean():
+    x = synth.gaussian((50, 8), 1.0, 9, "bf16")
+    l = np.linspace(-3, 3, 50).astype(np.float32)
+    o, lo = oracle.lse_merge([x], [l], "bf16")
+    assert np.array_equal(o, x) and np.array_equal(lo, l)
+    # equal LSEs on 4 ranks with identical parts: weights 1/4 each -> the part
+    o, lo = oracle.lse_merge([x] * 4, [l] * 4, "bf16")
+    assert np.array_equal(o, x)
+    assert np.allclose(lo, l + np.log(4.0), atol=1e-6)
