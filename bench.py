@@ -217,8 +217,9 @@ def bcast_vs_padded_ag(torch, coll, n_toks=(256, 1024, 4096, 16384), H=7168, own
 def next_rows(torch, coll, iters=20):
     """Rows beyond the step, with their algorithmic bytes: Reduce to a root and
     Scatter from it (R=8, 64 MiB per rank: (R+1)*S and 2*R*S), the uniform
-    all-to-all (2*R*S) and the sequence <-> heads re-shard of all-to-all
-    sequence parallelism (2 * bytes of all ranks)."""
+    all-to-all (2*R*S), the sequence <-> heads re-shard of all-to-all
+    sequence parallelism (2 * bytes of all ranks) and the context-parallel
+    LSE merge (R partials + R lse read, R outputs + R lse written)."""
     res = {}
     n = (64 << 20) // 2
     xs = [torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_() for _ in range(R)]
@@ -248,18 +249,27 @@ def next_rows(torch, coll, iters=20):
     heads = [torch.empty_like(t) for t in seq]
     seq_back = [torch.empty_like(t) for t in seq]
     rb = R * SL * H * D * 2
+    # context-parallel attention merge: 8192 tokens x 32 heads, head_dim 128
+    rows = 8192 * 32
+    op_ = [torch.empty((rows, 128), dtype=torch.bfloat16, device="cuda").normal_()
+           for _ in range(R)]
+    lp_ = [torch.empty(rows, dtype=torch.float32, device="cuda").normal_(0, 3) for _ in range(R)]
+    oo_ = [torch.empty_like(t) for t in op_]
+    lo_ = [torch.empty_like(t) for t in lp_]
+    mb = 2 * R * rows * 128 * 2 + 2 * R * rows * 4
     for name, fn, nbytes in (
             ("reduce_64m", lambda: coll.reduce(xs, out, 0), (R + 1) * n * 2),
             ("scatter_64m", lambda: coll.scatter(root_buf, chunks, 0), 2 * R * n * 2),
             ("all_to_all_64m", lambda: coll.all_to_all(xs, a2a_out), 2 * R * n * 2),
             ("seq_to_heads_32k", lambda: coll.seq_heads_reshard(seq, heads, H, D, True), 2 * rb),
             ("heads_to_seq_32k", lambda: coll.seq_heads_reshard(heads, seq_back, H, D, False),
-             2 * rb)):
+             2 * rb),
+            ("lse_merge_8k_x32h", lambda: coll.lse_merge(op_, lp_, oo_, lo_), mb)):
         t = med(fn)
         gbs = nbytes / t / 1e9
         res[name] = {"us": round(t * 1e6, 2), "bytes": nbytes, "GBps": round(gbs, 1),
                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    del xs, out, root_buf, chunks, a2a_out, seq, heads, seq_back
+    del xs, out, root_buf, chunks, a2a_out, seq, heads, seq_back, op_, lp_, oo_, lo_
     torch.cuda.empty_cache()
     return res
 

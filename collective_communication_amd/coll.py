@@ -40,6 +40,7 @@ SIGNATURES = {
     "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp]),
     "coll_all_to_all": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_seq_heads_reshard": (_i, [_i, _vp, _vp, _sz, _sz, _sz, _i, _i, _vp]),
+    "coll_lse_merge": (_i, [_i, _vp, _vp, _vp, _vp, _sz, _sz, _i, _vp]),
     "coll_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "coll_moe_layout": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
@@ -261,6 +262,27 @@ def seq_heads_reshard(ins, outs, heads: int, head_dim: int, to_heads: bool,
     _check(lib().coll_seq_heads_reshard(R, _table(ins, "in"), _table(outs, "out"), SL, heads,
                                         head_dim * mult, dt, 1 if to_heads else 0,
                                         _stream(stream)), "seq_heads_reshard")
+
+
+def lse_merge(o_parts, lse_parts, o_out, lse_out=None, stream=None) -> None:
+    """Context-parallel merge: o_parts[r] [rows, D] (bf16/fp32) with fp32
+    lse_parts[r] [rows] -> o_out[r] (and lse_out[r]) on every rank."""
+    R = _ranks(o_parts, "lse_merge")
+    rows = lse_parts[0].numel()
+    D = o_parts[0].numel() // max(rows, 1)
+    dt = {torch.bfloat16: COLL_BF16, torch.float32: COLL_FP32}.get(o_parts[0].dtype)
+    if dt is None:
+        raise ValueError("lse_merge: bf16 or fp32 outputs")
+    _same(o_parts, o_parts[0].dtype, rows * D, "lse_merge o")
+    _same(o_out, o_parts[0].dtype, rows * D, "lse_merge out")
+    _same(lse_parts, torch.float32, rows, "lse_merge lse")
+    lo = None
+    if lse_out is not None:
+        _same(lse_out, torch.float32, rows, "lse_merge lse_out")
+        lo = _table(lse_out, "lse_out")
+    _check(lib().coll_lse_merge(R, _table(o_parts, "o"), _table(lse_parts, "lse"),
+                                _table(o_out, "out"), lo, rows, D, dt, _stream(stream)),
+           "lse_merge")
 
 
 def moe_workspace_bytes(R: int, tokens: int, topk: int, n_experts: int) -> int:

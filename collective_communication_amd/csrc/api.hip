@@ -236,6 +236,24 @@ int coll_seq_heads_reshard(int R, const void *const *in, void *const *out, size_
                         to_heads != 0);
 }
 
+int coll_lse_merge(int R, const void *const *o_parts, const float *const *lse_parts,
+                   void *const *o_out, float *const *lse_out, size_t rows, size_t head_dim,
+                   coll_dtype_t dtype, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (dtype != COLL_BF16 && dtype != COLL_FP32) return COLL_ERR_UNSUPPORTED;
+  if (rows == 0 || head_dim == 0) return COLL_OK;
+  if (!bytes_ok(rows, head_dim * dtype_size(dtype), 2 * (size_t)R)) return COLL_ERR_INVALID_ARG;
+  RankPtrs o{};
+  PtrTable li{};
+  MutPtrTable lo{};
+  if (!fill_in(R, o_parts, o.in) || !fill_out(R, o_out, o.out) ||
+      !fill_in(R, reinterpret_cast<const void *const *>(lse_parts), li.p))
+    return COLL_ERR_INVALID_ARG;
+  if (lse_out)
+    for (int r = 0; r < R; r++) lo.p[r] = lse_out[r];      // NULL entries: not written
+  return launch_lse_merge(launch_ctx(stream), R, o, li, lo, rows, head_dim, dtype);
+}
+
 size_t coll_moe_workspace_bytes(int R, int tokens, int topk, int n_experts) {
   if (!ranks_ok(R) || tokens < 0 || topk < 1 || n_experts < 1 || n_experts > kMoeMaxExperts ||
       n_experts % R != 0 || (int64_t)tokens * topk >= ((int64_t)1 << 31))

@@ -384,6 +384,8 @@ int launch_broadcast(const Launch &L, int R, const void *src, const RankPtrs &p,
 int launch_scatter(const Launch &L, int R, const void *src, const RankPtrs &p, size_t bytes);
 int launch_reshard(const Launch &L, int R, const RankPtrs &p, size_t seq_local,
                    size_t chunk_bytes, bool to_heads);
+int launch_lse_merge(const Launch &L, int R, const RankPtrs &o, const PtrTable &lse_in,
+                     const MutPtrTable &lse_out, size_t rows, size_t D, int dt);
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
                 const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
                 size_t rows_capacity);

@@ -192,6 +192,25 @@ int coll_seq_heads_reshard(int nranks, const void *const *in, void *const *out,
                            size_t seq_local, size_t heads, size_t head_dim, coll_dtype_t dtype,
                            int to_heads, void *stream);
 
+/*
+ * Context-parallel merge of partial attention -- tutorial sections 5.4.2 and
+ * 7.4.3 (the partial outputs cannot be summed as they are: the log-sum-exps
+ * are gathered and the corrected contributions summed).  Per row i (a
+ * (token, head) pair) with o_parts[r] row i and lse_parts[r][i]:
+ *   m = max_r lse, e_r = exp(lse_r - m), s = sum_r e_r, L = m + log(s),
+ *   o_out[r][i] = sum_r (e_r / s) * o_parts[r][i]   (fp32, ranks ascending),
+ *   lse_out[r][i] = L,   for every rank r (AllReduce of the corrected terms).
+ * A row whose lse are all -inf gives 0 and -inf.  o_parts/o_out: [rows,
+ * head_dim] of bf16 or fp32; lse: fp32 [rows].  o_out[r] may be o_parts[r]
+ * (in place); lse_out (or an entry of it) may be NULL to skip it.  exp/log
+ * are the device library's fp32 functions: o differs from the exact (fp64)
+ * merge rounded once by at most 2 ulps of the output type plus a few fp32
+ * ulps of sum_r w_r |o_r| (cancellation); L by a few fp32 ulps.
+ */
+int coll_lse_merge(int nranks, const void *const *o_parts, const float *const *lse_parts,
+                   void *const *o_out, float *const *lse_out, size_t rows, size_t head_dim,
+                   coll_dtype_t dtype, void *stream);
+
 /* ---------------------------------------------------------------------------
  * MoE dispatch / combine over expert parallelism -- tutorial section 8.4.
  * Experts are placed on ranks in contiguous blocks: rank d owns experts

@@ -145,3 +145,11 @@ def test_all_to_all_and_reshard_validation(L):
     assert L.coll_seq_heads_reshard(4, ok, ok, 16, 6, 128, 0, 1, NULL) == -1   # 6 % 4 != 0
     assert L.coll_seq_heads_reshard(4, ok, ok, 0, 8, 128, 0, 1, NULL) == 0
     assert L.coll_seq_heads_reshard(4, ok, NULL, 16, 8, 128, 0, 1, NULL) == -1
+
+
+def test_lse_merge_validation(L):
+    ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.coll_lse_merge(2, ok, ok, ok, NULL, 16, 128, 1, NULL) == -2     # fp16 unsupported
+    assert L.coll_lse_merge(2, ok, ok, ok, NULL, 0, 128, 0, NULL) == 0
+    assert L.coll_lse_merge(2, NULL, ok, ok, NULL, 16, 128, 0, NULL) == -1
+    assert L.coll_lse_merge(0, ok, ok, ok, NULL, 16, 128, 0, NULL) == -1

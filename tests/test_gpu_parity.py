@@ -612,3 +612,79 @@ def test_seq_heads_reshard_round_trip(R, SL, H, D):
         assert bits_equal(host(mid[d]).reshape(-1), want[d]), f"to_heads dest {d}"
     for s in range(R):
         assert bits_equal(host(back[s]), xs[s]), f"round trip rank {s}"
+
+
+# ------------------------------------------------- context-parallel LSE merge
+
+def _merge_close(got, want, o, lse, dtype):
+    """Tolerance derived from the arithmetic: the GPU forms the weights with
+    fp32 exp/log and folds R fp32 products, the oracle works in fp64; each
+    rounds once to the output type.  So
+        |got - want| <= 2 ulp_out(|want|) + 16 * 2^-24 * sum_r w_r |o_r|
+    (two final roundings, plus a few fp32 ulps of every term, which matters
+    where the weighted partials cancel).  w_r is recomputed here in fp64 only
+    to size the bound."""
+    def f64(a):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).double().numpy()
+        return a.astype(np.float64)
+    rows = lse[0].size
+    g, w = f64(got).reshape(rows, -1), f64(want).reshape(rows, -1)
+    L = np.stack([l.astype(np.float64) for l in lse])            # [R, rows]
+    m = L.max(axis=0)
+    e = np.where(np.isfinite(m), np.exp(L - np.where(np.isfinite(m), m, 0)), 0.0)
+    wts = e / np.maximum(e.sum(axis=0), 1e-300)
+    mag = sum(wts[r][:, None] * np.abs(f64(o[r]).reshape(rows, -1)) for r in range(len(o)))
+    frac = 7 if dtype == "bf16" else 23
+    a = np.abs(w)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(a, 1e-30))) - frac)
+    bound = 2 * ulp + 16 * 2.0 ** -24 * mag + 1e-30
+    return bool(np.all(np.abs(g - w) <= bound))
+
+
+@pytest.mark.parametrize("R,rows,D,dtype", [(1, 100, 128, "bf16"), (2, 37, 64, "fp32"),
+                                            (8, 4096, 128, "bf16"), (4, 10, 5, "bf16"),
+                                            (16, 300, 16, "fp32")])
+def test_lse_merge(R, rows, D, dtype):
+    say("lse_merge", R, rows, D, dtype)
+    o = [synth.gaussian((rows, D), 1.0, 1900 + r, dtype) for r in range(R)]
+    g = np.random.default_rng(R + rows)
+    lse = [(g.normal(size=rows) * 3).astype(np.float32) for _ in range(R)]
+    if R > 2:
+        lse[1][::7] = -np.inf                    # empty chunks on some rows
+    want_o, want_l = oracle.lse_merge(o, lse, dtype)
+    o_d = [to_dev(x, dtype) for x in o]
+    l_d = [torch.from_numpy(x).cuda() for x in lse]
+    outs = [poison_like(t) for t in o_d]
+    louts = [torch.empty(rows, dtype=torch.float32, device="cuda") for _ in range(R)]
+    coll.lse_merge(o_d, l_d, outs, louts)
+    torch.cuda.synchronize()
+    for r in range(R):
+        got = host(outs[r]).reshape(-1)
+        assert _merge_close(got, want_o.reshape(-1), o, lse, dtype), f"rank {r}"
+        gl = host(louts[r])
+        assert np.allclose(gl, want_l, rtol=2e-6, atol=2e-6), f"lse rank {r}"
+
+
+def test_lse_merge_single_rank_is_exact_identity_and_in_place():
+    rows, D = 512, 128
+    say("lse_merge identity")
+    x = synth.gaussian((rows, D), 1.0, 1950, "bf16")
+    l = np.linspace(-5, 5, rows).astype(np.float32)
+    xd = dev(x)
+    coll.lse_merge([xd], [torch.from_numpy(l).cuda()], [xd])     # in place
+    torch.cuda.synchronize()
+    assert bits_equal(host(xd), x)
+
+
+def test_lse_merge_all_empty_rows():
+    R, rows, D = 4, 64, 32
+    say("lse_merge empty rows")
+    o = [dev(synth.gaussian((rows, D), 1.0, 1960 + r, "bf16")) for r in range(R)]
+    l = [torch.full((rows,), -float("inf"), device="cuda") for _ in range(R)]
+    outs = [poison_like(t) for t in o]
+    lo = [torch.zeros(rows, device="cuda") for _ in range(R)]
+    coll.lse_merge(o, l, outs, lo)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert torch.all(outs[r].float() == 0) and torch.all(torch.isneginf(lo[r]))
