@@ -18,6 +18,7 @@ states the readings taken where the pages are silent.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -47,44 +48,76 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def _load(path: str) -> ctypes.CDLL:
+    L = ctypes.CDLL(path)
+    vp, sz, i32, i64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p
+    L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    for name in ("oracle_f32_to_bf16_n", "oracle_bf16_to_f32_n",
+                 "oracle_f32_to_f16_n", "oracle_f16_to_f32_n"):
+        getattr(L, name).argtypes = [sz, vp, vp]
+        getattr(L, name).restype = None
+    L.oracle_allreduce.argtypes = [i32, vp, vp, sz, i32, i32]
+    L.oracle_reduce.argtypes = [i32, vp, vp, i32, sz, i32, i32]
+    L.oracle_reduce_scatter.argtypes = [i32, vp, vp, sz, i32, i32]
+    L.oracle_all_gather.argtypes = [i32, vp, vp, sz, sz]
+    L.oracle_gather.argtypes = [i32, vp, vp, i32, sz, sz, sz]
+    L.oracle_scatter.argtypes = [i32, vp, vp, i32, sz, sz]
+    L.oracle_broadcast.argtypes = [i32, vp, vp, i32, sz, sz]
+    L.oracle_all_to_all_v.argtypes = [i32, vp, i64p, i64p, vp, i64p, sz, i64p, i64p]
+    L.oracle_moe_layout.argtypes = [i32, vp, i32, i32, i32, i64p, i64p, i64p, vp, vp]
+    L.oracle_moe_permute.argtypes = [i32, vp, vp, i32, i32, sz, vp]
+    L.oracle_moe_expert_scale.argtypes = [i32, vp, vp, i64p, i32, sz]
+    L.oracle_moe_combine.argtypes = [i32, vp, vp, vp, i32, i32, sz, vp]
+    L.oracle_all_to_all.argtypes = [i32, vp, vp, sz, sz]
+    L.oracle_ulysses.argtypes = [i32, vp, vp, sz, sz, sz, sz, i32]
+    L.oracle_lse_merge.argtypes = [i32, vp, vp, vp, vp, sz, sz, i32]
+    for name in ("oracle_allreduce", "oracle_reduce", "oracle_reduce_scatter",
+                 "oracle_all_gather", "oracle_gather", "oracle_scatter",
+                 "oracle_broadcast", "oracle_all_to_all_v", "oracle_moe_layout",
+                 "oracle_moe_permute", "oracle_moe_expert_scale",
+                 "oracle_moe_combine", "oracle_all_to_all", "oracle_ulysses",
+                 "oracle_lse_merge"):
+        getattr(L, name).restype = ctypes.c_int
+    return L
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH) or (
                 os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
-        vp, sz, i32, i64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p
-        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
-        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
-        for name in ("oracle_f32_to_bf16_n", "oracle_bf16_to_f32_n",
-                     "oracle_f32_to_f16_n", "oracle_f16_to_f32_n"):
-            getattr(L, name).argtypes = [sz, vp, vp]
-            getattr(L, name).restype = None
-        L.oracle_allreduce.argtypes = [i32, vp, vp, sz, i32, i32]
-        L.oracle_reduce.argtypes = [i32, vp, vp, i32, sz, i32, i32]
-        L.oracle_reduce_scatter.argtypes = [i32, vp, vp, sz, i32, i32]
-        L.oracle_all_gather.argtypes = [i32, vp, vp, sz, sz]
-        L.oracle_gather.argtypes = [i32, vp, vp, i32, sz, sz, sz]
-        L.oracle_scatter.argtypes = [i32, vp, vp, i32, sz, sz]
-        L.oracle_broadcast.argtypes = [i32, vp, vp, i32, sz, sz]
-        L.oracle_all_to_all_v.argtypes = [i32, vp, i64p, i64p, vp, i64p, sz, i64p, i64p]
-        L.oracle_moe_layout.argtypes = [i32, vp, i32, i32, i32, i64p, i64p, i64p, vp, vp]
-        L.oracle_moe_permute.argtypes = [i32, vp, vp, i32, i32, sz, vp]
-        L.oracle_moe_expert_scale.argtypes = [i32, vp, vp, i64p, i32, sz]
-        L.oracle_moe_combine.argtypes = [i32, vp, vp, vp, i32, i32, sz, vp]
-        L.oracle_all_to_all.argtypes = [i32, vp, vp, sz, sz]
-        L.oracle_ulysses.argtypes = [i32, vp, vp, sz, sz, sz, sz, i32]
-        L.oracle_lse_merge.argtypes = [i32, vp, vp, vp, vp, sz, sz, i32]
-        for name in ("oracle_allreduce", "oracle_reduce", "oracle_reduce_scatter",
-                     "oracle_all_gather", "oracle_gather", "oracle_scatter",
-                     "oracle_broadcast", "oracle_all_to_all_v", "oracle_moe_layout",
-                     "oracle_moe_permute", "oracle_moe_expert_scale",
-                     "oracle_moe_combine", "oracle_all_to_all", "oracle_ulysses",
-                     "oracle_lse_merge"):
-            getattr(L, name).restype = ctypes.c_int
-        _lib = L
+        _lib = _load(_LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Run the oracle's functions against another build of ``coll_oracle.c``
+    (the pin tests use it to show that planted mistakes are caught)."""
+    global _lib
+    saved = _lib
+    _lib = _load(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def compile_variant(source_text: str, out_path: str) -> str:
+    """Compile a (modified) copy of the oracle source with the same flags."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(source_text)
+    subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-w", "-o", out_path, src, "-lm"])
+    return out_path
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
 
 
 class OracleError(RuntimeError):
