@@ -25,8 +25,8 @@ stream the kernels run on; the dominant kernel (a2av_dispatch) is reported
 against the 8 TB/s HBM roofline.  A separate AllReduce sweep at 16/32/64 MiB
 per rank rotates four buffer sets so the 256 MB Infinity Cache cannot serve it.
 
-The CPU baseline times the oracle (single-threaded C) on a bounded sample of
-the same step (MoE leg at 2048 of the 4096 tokens per rank).
+The CPU baseline times the oracle (single-threaded C) on one pass of the same
+step at its bench sizes.
 """
 from __future__ import annotations
 
@@ -307,9 +307,8 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=20):
 # --------------------------------------------------------------- CPU baseline
 
 def cpu_baseline():
-    """The oracle as it stands, single-threaded, on a bounded sample of the
-    step: every row at its bench size except the MoE leg, which runs 2048 of
-    the 4096 tokens per rank (about 10-20 s of CPU work)."""
+    """The oracle as it stands, single-threaded, on one pass of the whole step
+    at its bench sizes (about 10-20 s of CPU work)."""
     import numpy as np
 
     import oracle
@@ -343,7 +342,7 @@ def cpu_baseline():
     timed(lambda: oracle.gather(lg, 0), 2 * R * 256 * 19008 * 4)
     ids = synth.uniform_int32(256, 0, 152064, 4107)
     timed(lambda: oracle.broadcast(ids, R, 7), 256 * 4 * R)
-    E, T, K, H = 256, 2048, 8, 7168
+    E, T, K, H = 256, 4096, 8, 7168
     tid, tw = [], []
     for s in range(R):
         i, w = synth.zipf_routing(4096, E, K, seed=5100 + s)
@@ -357,8 +356,8 @@ def cpu_baseline():
     return {"value": round(bytes_total / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "seconds": round(t_total, 2),
-            "sample": "every step row at its bench size except the MoE leg at 2048 of 4096 "
-                      "tokens per rank; single-threaded C oracle (gcc -O2), algorithmic bytes "
+            "sample": "one pass of every step row at its bench size (MoE leg: all 4096 "
+                      "tokens per rank); single-threaded C oracle (gcc -O2), algorithmic bytes "
                       "of the sample / its wall time"}
 
 
