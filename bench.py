@@ -67,25 +67,32 @@ def make_inputs(torch, synth, coll):
 
     W = {}
     print("[bench] generating inputs", file=sys.stderr, flush=True)
-    W["ar160_in"] = [dev_bf16(synth.gaussian(81920, 1.0, 1000 + r, "bf16")) for r in range(4)]
-    W["ar160_out"] = [torch.empty_like(t) for t in W["ar160_in"]]
-    W["ard_in"] = [dev_bf16(synth.gaussian((64, 7168), 0.02, 2000 + r, "bf16")) for r in range(R)]
-    W["ard_out"] = [torch.empty_like(t) for t in W["ard_in"]]
+    bf = torch.bfloat16
+    # every group of rank buffers lives in a rank arena: the buffers one call
+    # touches together start on their own 2 MiB pages at distinct 4 KiB colours
+    W["ar160_in"], W["ar160_out"] = coll.rank_arena([(4, 81920, bf), (4, 81920, bf)])
+    for r, t in enumerate(W["ar160_in"]):
+        t.copy_(dev_bf16(synth.gaussian(81920, 1.0, 1000 + r, "bf16")))
+    W["ard_in"], W["ard_out"] = coll.rank_arena([(R, (64, 7168), bf), (R, (64, 7168), bf)])
+    for r, t in enumerate(W["ard_in"]):
+        t.copy_(dev_bf16(synth.gaussian((64, 7168), 0.02, 2000 + r, "bf16")))
     n64 = (64 << 20) // 2
     g = torch.Generator(device="cuda")
     g.manual_seed(26)
-    W["ar64_in"] = [(torch.randn(n64, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-                    for _ in range(R)]
-    W["ar64_out"] = [torch.empty_like(t) for t in W["ar64_in"]]
-    W["sp_in"] = [dev_bf16(synth.gaussian((8192, 4096), 1.0, 3000 + r, "bf16")) for r in range(R)]
-    W["sp_shard"] = [torch.empty((1024, 4096), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
-    W["sp_full"] = [torch.empty_like(t) for t in W["sp_in"]]
-    W["lg_in"] = [torch.from_numpy(synth.gaussian((256, 19008), 2.0, 4000 + r, "fp32")).cuda()
-                  for r in range(R)]
-    W["lg_out"] = torch.empty((256, R * 19008), dtype=torch.float32, device="cuda")
-    W["bc_src"] = torch.from_numpy(synth.uniform_int32(256, 0, 152064, 4107)).cuda()
-    W["bc_out"] = [torch.empty_like(W["bc_src"]) for _ in range(R)]
-    W["bc_out"][7] = W["bc_src"]
+    W["ar64_in"], W["ar64_out"] = coll.rank_arena([(R, n64, bf), (R, n64, bf)])
+    for t in W["ar64_in"]:
+        t.copy_(torch.randn(n64, generator=g, device="cuda") * 0.02)
+    W["sp_in"], W["sp_shard"], W["sp_full"] = coll.rank_arena(
+        [(R, (8192, 4096), bf), (R, (1024, 4096), bf), (R, (8192, 4096), bf)])
+    for r, t in enumerate(W["sp_in"]):
+        t.copy_(dev_bf16(synth.gaussian((8192, 4096), 1.0, 3000 + r, "bf16")))
+    W["lg_in"], (W["lg_out"],) = coll.rank_arena(
+        [(R, (256, 19008), torch.float32), (1, (256, R * 19008), torch.float32)])
+    for r, t in enumerate(W["lg_in"]):
+        t.copy_(torch.from_numpy(synth.gaussian((256, 19008), 2.0, 4000 + r, "fp32")))
+    (W["bc_out"],) = coll.rank_arena([(R, 256, torch.int32)])
+    W["bc_src"] = W["bc_out"][7]                 # the root keeps its own buffer
+    W["bc_src"].copy_(torch.from_numpy(synth.uniform_int32(256, 0, 152064, 4107)))
 
     E, T, K, H = 256, 4096, 8, 7168
     W["moe"] = (E, T, K, H)
@@ -95,7 +102,6 @@ def make_inputs(torch, synth, coll):
         ids.append(torch.from_numpy(i).cuda())
         ws.append(torch.from_numpy(w).cuda())
     W["moe_ids"], W["moe_w"] = ids, ws
-    W["moe_x"] = [dev_bf16(synth.gaussian((T, H), 1.0, 5000 + s, "bf16")) for s in range(R)]
     W["sc"] = torch.empty(R * R, dtype=torch.int64, device="cuda")
     W["sd"] = torch.empty_like(W["sc"])
     W["rd"] = torch.empty_like(W["sc"])
@@ -103,16 +109,17 @@ def make_inputs(torch, synth, coll):
     W["ec"] = torch.empty(R * E, dtype=torch.int32, device="cuda")
     W["pos"] = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(R)]
     W["ws"] = torch.empty(coll.moe_workspace_bytes(R, T, K, E), dtype=torch.uint8, device="cuda")
-    W["send"] = [torch.empty((T * K, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
-    W["back"] = [torch.empty((T * K, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
-    W["out"] = [torch.empty((T, H), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
     # the routing is fixed, so the receive sizes are known once (outside timing)
     coll.moe_layout(ids, E, W["sc"], W["sd"], W["rd"], W["ec"], W["pos"], W["ws"])
     torch.cuda.synchronize()
     sc = W["sc"].view(R, R).cpu()
     W["sc_t"].copy_(W["sc"].view(R, R).t().contiguous().view(-1))
-    W["recv"] = [torch.empty((int(sc[:, d].sum()), H), dtype=torch.bfloat16, device="cuda")
-                 for d in range(R)]
+    W["moe_x"], W["send"], W["recv"], W["back"], W["out"] = coll.rank_arena(
+        [(R, (T, H), bf), (R, (T * K, H), bf),
+         [((int(sc[:, d].sum()), H), bf) for d in range(R)],
+         (R, (T * K, H), bf), (R, (T, H), bf)])
+    for s, t in enumerate(W["moe_x"]):
+        t.copy_(dev_bf16(synth.gaussian((T, H), 1.0, 5000 + s, "bf16")))
     # plain-copy reference (1 GiB through the library's copy kernel), only for
     # calibrating the HBM counters; not part of the step
     W["copy_src"] = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
@@ -221,11 +228,13 @@ def next_rows(torch, coll, iters=20):
     sequence parallelism (2 * bytes of all ranks) and the context-parallel
     LSE merge (R partials + R lse read, R outputs + R lse written)."""
     res = {}
+    bf = torch.bfloat16
     n = (64 << 20) // 2
-    xs = [torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_() for _ in range(R)]
-    out = torch.empty_like(xs[0])
-    root_buf = torch.empty(R * n, dtype=torch.bfloat16, device="cuda").normal_()
-    chunks = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    xs, (out,), a2a_out = coll.rank_arena([(R, n, bf), (1, n, bf), (R, n, bf)])
+    for t in xs:
+        t.normal_()
+    (root_buf,), chunks = coll.rank_arena([(1, R * n, bf), (R, n, bf)])
+    root_buf.normal_()
 
     def med(fn):
         fn()
@@ -240,22 +249,21 @@ def next_rows(torch, coll, iters=20):
         ts = sorted(a.elapsed_time(b) for a, b in ev)
         return ts[len(ts) // 2] * 1e-3
 
-    a2a_out = [torch.empty_like(x) for x in xs]
     # all-to-all sequence parallelism: 32768-token sequence over 8 ranks,
     # 32 heads x 128, bf16 (32 MiB per rank each way)
     SL, H, D = 4096, 32, 128
-    seq = [torch.empty((SL, H, D), dtype=torch.bfloat16, device="cuda").normal_()
-           for _ in range(R)]
-    heads = [torch.empty_like(t) for t in seq]
-    seq_back = [torch.empty_like(t) for t in seq]
+    seq, heads, seq_back = coll.rank_arena([(R, (SL, H, D), bf)] * 3)
+    for t in seq:
+        t.normal_()
     rb = R * SL * H * D * 2
     # context-parallel attention merge: 8192 tokens x 32 heads, head_dim 128
     rows = 8192 * 32
-    op_ = [torch.empty((rows, 128), dtype=torch.bfloat16, device="cuda").normal_()
-           for _ in range(R)]
-    lp_ = [torch.empty(rows, dtype=torch.float32, device="cuda").normal_(0, 3) for _ in range(R)]
-    oo_ = [torch.empty_like(t) for t in op_]
-    lo_ = [torch.empty_like(t) for t in lp_]
+    op_, lp_, oo_, lo_ = coll.rank_arena([(R, (rows, 128), bf), (R, rows, torch.float32),
+                                          (R, (rows, 128), bf), (R, rows, torch.float32)])
+    for t in op_:
+        t.normal_()
+    for t in lp_:
+        t.normal_(0, 3)
     mb = 2 * R * rows * 128 * 2 + 2 * R * rows * 4
     for name, fn, nbytes in (
             ("reduce_64m", lambda: coll.reduce(xs, out, 0), (R + 1) * n * 2),
@@ -274,31 +282,76 @@ def next_rows(torch, coll, iters=20):
     return res
 
 
-def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=20):
-    """AllReduce R=8 bf16 at large sizes, rotating `sets` buffer sets so the
-    working set (>= 1 GiB) exceeds the Infinity Cache."""
+def _launch_times(torch, fn, sets, iters):
+    """(median of per-launch event pairs, mean over one event pair around
+    `iters` back-to-back launches), seconds; launch i uses buffer set i % sets."""
+    for i in range(sets):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        fn(i % sets)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        fn(i % sets)
+    b.record()
+    torch.cuda.synchronize()
+    return ts[len(ts) // 2] * 1e-3, a.elapsed_time(b) / iters * 1e-3
+
+
+def _ar_sets(torch, coll, n, sets, arena):
+    out = []
+    for _ in range(sets):
+        if arena:
+            ins, outs = coll.rank_arena([(R, n, torch.bfloat16), (R, n, torch.bfloat16)])
+            for t in ins:
+                t.normal_(0, 0.02)
+        else:
+            ins = [torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(0, 0.02)
+                   for _ in range(R)]
+            outs = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        out.append((ins, outs))
+    return out
+
+
+def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
+    """AllReduce R=8 bf16 at large sizes, rank buffers in rank arenas,
+    rotating `sets` buffer sets so the working set (>= 1 GiB) exceeds the
+    Infinity Cache.  Reports the median of per-launch event timings and the
+    mean launch time of a back-to-back batch (no events between launches)."""
     res = {}
     for mib in sizes_mib:
-        n = (mib << 20) // 2
-        bufs = [([torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(0, 0.02)
-                  for _ in range(R)],
-                 [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(R)])
-                for _ in range(sets)]
-        for i in range(sets):
-            coll.allreduce(*bufs[i])
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(iters)]
-        for i in range(iters):
-            ev[i][0].record()
-            coll.allreduce(*bufs[i % sets])
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        ts = sorted(a.elapsed_time(b) for a, b in ev)
-        med = ts[len(ts) // 2]
-        gbs = 2 * R * (mib << 20) / (med * 1e-3) / 1e9
-        res[f"{mib}MiB"] = {"median_us": round(med * 1e3, 2), "GBps": round(gbs, 1),
-                            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        bufs = _ar_sets(torch, coll, (mib << 20) // 2, sets, True)
+        med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters)
+        nbytes = 2 * R * (mib << 20)
+        res[f"{mib}MiB"] = {"median_us": round(med * 1e6, 2),
+                            "GBps": round(nbytes / med / 1e9, 1),
+                            "frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4),
+                            "batch_us": round(batch * 1e6, 2),
+                            "batch_GBps": round(nbytes / batch / 1e9, 1),
+                            "batch_frac": round(nbytes / batch / 1e9 / HBM_PEAK_GBS, 4)}
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
+def layout_ab(torch, coll, mib=16, sets=4, iters=24):
+    """AllReduce R=8 bf16 at `mib` MiB per rank with the 16 buffers of a call
+    allocated one by one by torch (each its own large allocation, so they tend
+    to share their offset modulo 64 KiB) vs placed in a rank arena."""
+    res = {}
+    nbytes = 2 * R * (mib << 20)
+    for name, arena in (("torch_alloc", False), ("rank_arena", True)):
+        bufs = _ar_sets(torch, coll, (mib << 20) // 2, sets, arena)
+        med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters)
+        res[name] = {"median_us": round(med * 1e6, 2), "GBps": round(nbytes / med / 1e9, 1),
+                     "batch_GBps": round(nbytes / batch / 1e9, 1)}
         del bufs
         torch.cuda.empty_cache()
     return res
@@ -452,10 +505,12 @@ def main():
                 "bytes_per_launch": nbytes[dom],
                 "avg_launch_us": round(per_row[dom] * 1e3, 2)}
 
-    sweep = None
+    sweep = lab = None
     if not args.no_sweep and not args.only:
         print("[bench] allreduce sweep", file=sys.stderr, flush=True)
         sweep = ar_sweep(torch, coll)
+        print("[bench] allocation layout A/B", file=sys.stderr, flush=True)
+        lab = layout_ab(torch, coll)
 
     ab = extra = None
     if not args.no_sweep and not args.only:
@@ -480,11 +535,13 @@ def main():
                                "Broadcast int32[256], MoE dispatch/combine 4096 tok x 7168 "
                                "top-8 of 256 experts via All-to-All-v",
                    "ranks": R, "step_bytes": step_bytes,
+                   "buffers": "rank arenas (coll_arena_layout: own 2 MiB page + 4 KiB colour per buffer)",
                    "moe_rows": W["moe_rows"], "moe_dest_share": W["dest_share"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "rows": rows_out,
         "allreduce_sweep": sweep,
+        "allreduce_16mib_layout_ab": lab,
         "broadcast_vs_padded_allgather": ab,
         "next_rows": extra,
     }

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libcoll.so")
 COLL_BF16, COLL_FP16, COLL_FP32, COLL_INT32 = 0, 1, 2, 3
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 MAX_RANKS = 16
+ARENA_ALIGN = 2 << 20           # COLL_ARENA_ALIGN of include/coll.h
 
 _REDUCE_DTYPES = {torch.bfloat16: COLL_BF16, torch.float16: COLL_FP16,
                   torch.float32: COLL_FP32, torch.int32: COLL_INT32}
@@ -30,6 +31,7 @@ _vp, _sz, _i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 SIGNATURES = {
     "coll_status_string": (ctypes.c_char_p, [_i]),
     "coll_version": (_i, []),
+    "coll_arena_layout": (_i, [_i, _vp, _vp, _vp]),
     "coll_allreduce": (_i, [_i, _vp, _vp, _sz, _i, _i, _vp]),
     "coll_reduce_scatter": (_i, [_i, _vp, _vp, _sz, _i, _i, _vp]),
     "coll_reduce": (_i, [_i, _vp, _vp, _i, _sz, _i, _i, _vp]),
@@ -127,6 +129,51 @@ def _same(ts, dtype, numel, what):
     for t in ts:
         if t.dtype != dtype or t.numel() != numel:
             raise ValueError(f"{what}: every rank needs {numel} elements of {dtype}")
+
+
+# ------------------------------------------------------------- rank arena
+
+def arena_layout(sizes: Sequence[int]) -> tuple[list[int], int]:
+    """Offsets (from an ARENA_ALIGN-aligned base) and total size that
+    ``coll_arena_layout`` gives buffers of ``sizes`` bytes, in order."""
+    n = len(sizes)
+    b = (ctypes.c_size_t * max(n, 1))(*[int(x) for x in sizes])
+    o = (ctypes.c_size_t * max(n, 1))()
+    tot = ctypes.c_size_t()
+    _check(lib().coll_arena_layout(n, b, o, ctypes.byref(tot)), "arena_layout")
+    return [int(o[k]) for k in range(n)], int(tot.value)
+
+
+def rank_arena(groups, device="cuda"):
+    """Allocate groups of rank buffers in one device allocation, placed by
+    ``coll_arena_layout`` (each buffer on its own 2 MiB boundary plus a 4 KiB
+    colour that differs from its neighbours'), so that the R same-offset
+    streams of a collective spread over the HBM channels.
+
+    Each group is either ``(count, shape, dtype)`` (``count`` buffers alike)
+    or a list of ``(shape, dtype)`` (one per buffer).  Returns one list of
+    uninitialised tensors per group, in order; they are views of one
+    allocation, which lives as long as any of them."""
+    specs, counts = [], []
+    for g in groups:
+        items = g if isinstance(g, list) else [(g[1], g[2])] * int(g[0])
+        counts.append(len(items))
+        for shape, dtype in items:
+            shape = (shape,) if isinstance(shape, int) else tuple(int(d) for d in shape)
+            numel = 1
+            for d in shape:
+                numel *= d
+            specs.append((shape, dtype, numel * torch.empty(0, dtype=dtype).element_size()))
+    offs, total = arena_layout([nb for _, _, nb in specs])
+    raw = torch.empty(total + ARENA_ALIGN, dtype=torch.uint8, device=device)
+    base = (-raw.data_ptr()) % ARENA_ALIGN
+    views = [raw[base + o: base + o + nb].view(dtype).view(shape)
+             for (shape, dtype, nb), o in zip(specs, offs)]
+    out, k = [], 0
+    for c in counts:
+        out.append(views[k:k + c])
+        k += c
+    return out
 
 
 # --------------------------------------------------------------------- API

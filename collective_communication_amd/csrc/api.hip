@@ -104,6 +104,23 @@ const char *coll_status_string(int status) {
 
 int coll_version(void) { return 1 * 10000 + 0 * 100 + 0; }
 
+int coll_arena_layout(int n, const size_t *bytes, size_t *offsets, size_t *total) {
+  if (n < 0 || !total || (n > 0 && (!bytes || !offsets))) return COLL_ERR_INVALID_ARG;
+  const size_t page = COLL_ARENA_ALIGN;
+  const size_t lim = (size_t)1 << 56;
+  size_t end = 0;
+  for (int k = 0; k < n; k++) {
+    if (bytes[k] >= lim) return COLL_ERR_INVALID_ARG;
+    const size_t start = (end + page - 1) / page * page +
+                         (size_t)(k % COLL_ARENA_COLORS) * COLL_ARENA_COLOR_BYTES;
+    offsets[k] = start;
+    end = start + bytes[k];
+    if (end >= lim) return COLL_ERR_INVALID_ARG;
+  }
+  *total = end;
+  return COLL_OK;
+}
+
 int coll_allreduce(int R, const void *const *sendbufs, void *const *recvbufs, size_t count,
                    coll_dtype_t dtype, coll_op_t op, void *stream) {
   if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;

@@ -22,11 +22,12 @@ namespace {
 // ---------------------------------------------------------------- AllReduce
 
 // Tile shape of the R-way reductions (measured on MI355X, R = 8, 16-64 MiB
-// per rank): AllReduce does best with 128-lane workgroups and one 16-byte
-// unit per lane per rank (8 loads in flight per lane, many small tiles);
-// ReduceScatter, whose writes are 1/R of its reads, with 256 lanes x 2 units.
+// per rank, rank buffers placed at distinct 4 KiB colours): AllReduce does
+// best with one-wave workgroups and one 16-byte unit per lane per rank (8
+// loads in flight per lane, many small tiles); ReduceScatter, whose writes are
+// 1/R of its reads, with 256 lanes x 2 units.
 #ifndef COLL_AR_BLOCK
-#define COLL_AR_BLOCK 128
+#define COLL_AR_BLOCK 64
 #endif
 #ifndef COLL_AR_U_MID
 #define COLL_AR_U_MID 1          // units per lane for 3 <= R <= 8

@@ -67,6 +67,41 @@ const char *coll_status_string(int status);
 int coll_version(void);
 
 /*
+ * Placement of virtual-rank buffers in one device allocation (a "rank
+ * arena").  Not an operation of the pages: a layout rule for this one-GPU
+ * setting, where the R ranks' buffers share one HBM.  A collective touches
+ * all R buffers of a role at the same element offset at the same time; when
+ * those buffers start at the same address modulo the interleave of the HBM
+ * channels, the R concurrent streams fall on the same channels and the
+ * pattern loses up to a fifth of its bandwidth (measured on MI355X, AllReduce
+ * of 8 inputs + 8 outputs of 16 MiB: separately allocated buffers vs this
+ * placement).  The channel hash takes address bits both below and above
+ * 2 MiB, so the rule varies both.
+ *
+ * Buffer k (k = 0..n-1, in the caller's order) starts at the first multiple
+ * of COLL_ARENA_ALIGN (2 MiB) at or after the end of buffer k-1, plus
+ * (k mod COLL_ARENA_COLORS) * COLL_ARENA_COLOR_BYTES.  Consecutive buffers
+ * thus start at distinct 4 KiB colours within their 2 MiB page, and a 2 MiB
+ * boundary lies between any two of them; each wastes less than 2 MiB +
+ * 124 KiB.  Order the buffers of one call consecutively (e.g. the R inputs,
+ * then the R outputs).
+ *
+ *   bytes[k]:   size of buffer k (0 allowed); host array of n entries.
+ *   offsets[k]: (out) byte offset of buffer k from a base aligned to
+ *               COLL_ARENA_ALIGN; host array of n entries.
+ *   total:      (out) bytes from that base to the end of the last buffer.
+ * The caller allocates total + COLL_ARENA_ALIGN - 1 bytes (or an aligned
+ * block of `total`), aligns the base up to COLL_ARENA_ALIGN and places buffer
+ * k at base + offsets[k].  Host-only: no HIP call, no allocation.
+ * Errors: n < 0, a NULL array with n > 0, NULL total, or a size overflow ->
+ * COLL_ERR_INVALID_ARG with the outputs unspecified.  n = 0 gives total 0.
+ */
+#define COLL_ARENA_COLOR_BYTES 4096u
+#define COLL_ARENA_COLORS 32u
+#define COLL_ARENA_ALIGN (2u << 20)
+int coll_arena_layout(int n, const size_t *bytes, size_t *offsets, size_t *total);
+
+/*
  * AllReduce -- tutorial section 6 (every rank ends with the same full
  * reduction), computed in the owner-per-segment layout of the IPC AllReduce
  * blog ("Pro5000 ?"): the element range is split into tiles; each tile is read

@@ -153,3 +153,97 @@ def test_lse_merge_validation(L):
     assert L.coll_lse_merge(2, ok, ok, ok, NULL, 0, 128, 0, NULL) == 0
     assert L.coll_lse_merge(2, NULL, ok, ok, NULL, 16, 128, 0, NULL) == -1
     assert L.coll_lse_merge(0, ok, ok, ok, NULL, 16, 128, 0, NULL) == -1
+
+
+# ------------------------------------------------------------- rank arena
+
+def _header_define(name):
+    with open(os.path.join(ROOT, "include", "coll.h")) as f:
+        text = f.read()
+    return re.search(rf"#define {name} (.+)", text).group(1)
+
+
+def test_arena_constants_match_header():
+    unit = int(_header_define("COLL_ARENA_COLOR_BYTES").rstrip("u"))
+    colors = int(_header_define("COLL_ARENA_COLORS").rstrip("u"))
+    assert unit == 4096 and colors == 32
+    assert _header_define("COLL_ARENA_ALIGN") == "(2u << 20)"
+    assert coll.ARENA_ALIGN == 2 << 20
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_arena_layout_colours_and_no_overlap(L, seed):
+    import numpy as np
+    g = np.random.default_rng(seed)
+    n = int(g.integers(1, 80))
+    pick = g.integers(0, 4, size=n)
+    sizes = [int(x) for x in np.where(pick == 0, 0, np.where(
+        pick == 1, g.integers(1, 5000, size=n),
+        np.where(pick == 2, g.integers(1, 64, size=n) << 20, g.integers(1, 1 << 30, size=n))))]
+    offs, total = coll.arena_layout(sizes)
+    end = 0
+    page = coll.ARENA_ALIGN
+    for k, (o, b) in enumerate(zip(offs, sizes)):
+        assert o % page == (k % 32) * 4096          # its page plus its colour
+        assert o - o % page >= end                   # a 2 MiB boundary after the previous end
+        assert o - end < page + 32 * 4096            # wastes less than 2 MiB + 128 KiB
+        end = o + b
+    assert total == end
+    # any 32 consecutive buffers start at distinct colours
+    for k in range(max(0, n - 31)):
+        assert len({(o // 4096) % 32 for o in offs[k:k + 32]}) == min(32, n - k)
+
+
+def test_arena_layout_edge_cases(L):
+    assert coll.arena_layout([]) == ([], 0)
+    M = 1 << 20
+    assert coll.arena_layout([0, 0, 0]) == ([0, 4096, 2 * M + 8192], 2 * M + 8192)
+    assert coll.arena_layout([2 * M, 5, 1]) == ([0, 2 * M + 4096, 4 * M + 8192], 4 * M + 8193)
+    offs, total = coll.arena_layout([16 * M] * 3)
+    assert offs == [0, 16 * M + 4096, 34 * M + 8192] and total == 50 * M + 8192
+    tot = ctypes.c_size_t()
+    sz = (ctypes.c_size_t * 2)(8, 8)
+    out = (ctypes.c_size_t * 2)()
+    assert L.coll_arena_layout(-1, sz, out, ctypes.byref(tot)) == -1
+    assert L.coll_arena_layout(2, NULL, out, ctypes.byref(tot)) == -1
+    assert L.coll_arena_layout(2, sz, NULL, ctypes.byref(tot)) == -1
+    assert L.coll_arena_layout(2, sz, out, NULL) == -1
+    huge = (ctypes.c_size_t * 2)(1 << 54, 1 << 54)
+    assert L.coll_arena_layout(2, huge, out, ctypes.byref(tot)) == 0
+    assert tot.value == (1 << 55) + 4096
+    huge = (ctypes.c_size_t * 3)(1 << 55, 1 << 55, 1 << 55)
+    out3 = (ctypes.c_size_t * 3)()
+    assert L.coll_arena_layout(3, huge, out3, ctypes.byref(tot)) == -1   # past 2^56
+    assert L.coll_arena_layout(1, (ctypes.c_size_t * 1)(1 << 56), out, ctypes.byref(tot)) == -1
+
+
+def test_rank_arena_views_on_host(L):
+    import torch
+    ins, outs, one = coll.rank_arena([(8, (64, 7168), torch.bfloat16),
+                                      (8, 64 * 7168, torch.bfloat16),
+                                      (1, (3,), torch.int32)], device="cpu")
+    ts = ins + outs + one
+    assert [tuple(t.shape) for t in ins] == [(64, 7168)] * 8
+    assert [tuple(t.shape) for t in outs] == [(64 * 7168,)] * 8
+    assert one[0].dtype == torch.int32 and one[0].numel() == 3
+    base = ts[0].data_ptr()
+    assert base % coll.ARENA_ALIGN == 0
+    spans = sorted((t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()) for t in ts)
+    for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert [(t.data_ptr() // 4096) % 32 for t in ts] == list(range(17))
+    for k, t in enumerate(ts):                       # writes land in their own views
+        t.view(-1)[:1].fill_(k + 1)
+    assert [int(t.view(-1)[0]) for t in ts][:16] == [k + 1 for k in range(16)]
+
+
+def test_rank_arena_per_buffer_shapes_on_host(L):
+    import torch
+    (a,), recv = coll.rank_arena([(1, 5, torch.float32),
+                                  [((3, 7), torch.bfloat16), ((0, 7), torch.bfloat16),
+                                   ((11,), torch.int64)]], device="cpu")
+    assert tuple(a.shape) == (5,)
+    assert [tuple(t.shape) for t in recv] == [(3, 7), (0, 7), (11,)]
+    assert [t.dtype for t in recv] == [torch.bfloat16, torch.bfloat16, torch.int64]
+    # (torch reports data_ptr() 0 for the empty view)
+    assert [(t.data_ptr() // 4096) % 32 for t in [a] + recv if t.numel()] == [0, 1, 3]
