@@ -282,6 +282,58 @@ def next_rows(torch, coll, iters=20):
     return res
 
 
+def moe_fused(torch, coll, W, per_row_us, iters=10):
+    """The fused MoE path on the step's inputs: layout, dispatch straight into
+    the receive buffers (permute + All-to-All-v in one pass), combine reading
+    them back with the test expert applied as rows are read (expert + reverse
+    All-to-All-v + combine in one pass).  Its outputs must equal the unfused
+    step's bit for bit.  Bytes: x read + rows written (+ pos) for the
+    dispatch; rows read + outputs written (+ w, pos, ids) for the combine."""
+    E, T, K, H = W["moe"]
+    bf = torch.bfloat16
+    recv2, out2 = coll.rank_arena([[(tuple(t.shape), bf) for t in W["recv"]], (R, (T, H), bf)])
+    rows = W["moe_rows"]
+    b_disp = R * T * H * 2 + rows * H * 2 + R * T * K * 4
+    b_comb = rows * H * 2 + R * T * H * 2 + R * T * K * 12
+    lay = lambda: coll.moe_layout(W["moe_ids"], E, W["sc"], W["sd"], W["rd"], W["ec"],
+                                  W["pos"], W["ws"])
+    disp = lambda: coll.moe_dispatch(W["moe_x"], W["pos"], W["sc"], W["sd"], W["rd"], recv2)
+    comb = lambda: coll.moe_combine_recv(recv2, W["pos"], W["sc"], W["sd"], W["rd"],
+                                         W["moe_w"], out2, topk_ids=W["moe_ids"])
+    lay(), disp(), comb()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+               for a, b in zip(out2, W["out"]))
+    t = {}
+    for name, fn in (("layout", lay), ("dispatch", disp), ("combine", comb)):
+        med, _ = _launch_times(torch, lambda i, f=fn: f(), 1, iters)
+        t[name] = med
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        lay(), disp(), comb()
+    b.record()
+    torch.cuda.synchronize()
+    pipe = a.elapsed_time(b) / iters * 1e-3
+    unfused = sum(per_row_us[n] for n in ("moe_layout", "moe_permute", "a2av_dispatch",
+                                          "moe_expert", "a2av_combine", "moe_combine")) * 1e-6
+    del recv2, out2
+    torch.cuda.empty_cache()
+    gb = lambda n, sec: round(n / sec / 1e9, 1)
+    return {"dispatch": {"us": round(t["dispatch"] * 1e6, 2), "bytes": b_disp,
+                         "GBps": gb(b_disp, t["dispatch"]),
+                         "frac": round(b_disp / t["dispatch"] / 1e9 / HBM_PEAK_GBS, 4)},
+            "combine": {"us": round(t["combine"] * 1e6, 2), "bytes": b_comb,
+                        "GBps": gb(b_comb, t["combine"]),
+                        "frac": round(b_comb / t["combine"] / 1e9 / HBM_PEAK_GBS, 4)},
+            "layout_us": round(t["layout"] * 1e6, 2),
+            "pipeline_us": round(pipe * 1e6, 2),
+            "pipeline_GBps": gb(b_disp + b_comb, pipe),
+            "unfused_pipeline_us": round(unfused * 1e6, 2),
+            "speedup_vs_unfused": round(unfused / pipe, 2),
+            "outputs_bitwise_equal_unfused": bool(same)}
+
+
 def _launch_times(torch, fn, sets, iters):
     """(median of per-launch event pairs, mean over one event pair around
     `iters` back-to-back launches), seconds; launch i uses buffer set i % sets."""
@@ -303,6 +355,51 @@ def _launch_times(torch, fn, sets, iters):
     b.record()
     torch.cuda.synchronize()
     return ts[len(ts) // 2] * 1e-3, a.elapsed_time(b) / iters * 1e-3
+
+
+def _graph_time(torch, fn, sets, n=24, reps=4):
+    """Mean time of one launch when `n` launches (launch i on buffer set
+    i % sets) are captured in one HIP graph and replayed: the GPU-side cost
+    without the host's per-call marshalling in between."""
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i % sets)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / (n * reps) * 1e-3
+    del g
+    return t
+
+
+def latency_rows_graph(torch, coll, W, per_row_us):
+    """The latency-bound rows of the step (and a small fused MoE pipeline)
+    timed by HIP-graph replay, beside their eager per-launch times."""
+    E, T, K, H = W["moe"]
+    rows = {
+        "ar_160k": lambda i: coll.allreduce(W["ar160_in"], W["ar160_out"]),
+        "ar_decode": lambda i: coll.allreduce(W["ard_in"], W["ard_out"]),
+        "bcast": lambda i: coll.broadcast(W["bc_src"], W["bc_out"], 7),
+        "moe_layout": lambda i: coll.moe_layout(W["moe_ids"], E, W["sc"], W["sd"], W["rd"],
+                                                W["ec"], W["pos"], W["ws"]),
+    }
+    res = {}
+    for name, fn in rows.items():
+        t = _graph_time(torch, fn, 1)
+        res[name] = {"graph_us": round(t * 1e6, 2), "eager_us": per_row_us[name]}
+    return res
 
 
 def _ar_sets(torch, coll, n, sets, arena):
@@ -329,8 +426,12 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
     for mib in sizes_mib:
         bufs = _ar_sets(torch, coll, (mib << 20) // 2, sets, True)
         med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters)
+        gt = _graph_time(torch, lambda i: coll.allreduce(*bufs[i]), sets)
         nbytes = 2 * R * (mib << 20)
-        res[f"{mib}MiB"] = {"median_us": round(med * 1e6, 2),
+        res[f"{mib}MiB"] = {"graph_us": round(gt * 1e6, 2),
+                            "graph_GBps": round(nbytes / gt / 1e9, 1),
+                            "graph_frac": round(nbytes / gt / 1e9 / HBM_PEAK_GBS, 4),
+                            "median_us": round(med * 1e6, 2),
                             "GBps": round(nbytes / med / 1e9, 1),
                             "frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4),
                             "batch_us": round(batch * 1e6, 2),
@@ -338,6 +439,78 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
                             "batch_frac": round(nbytes / batch / 1e9 / HBM_PEAK_GBS, 4)}
         del bufs
         torch.cuda.empty_cache()
+    return res
+
+
+def a2a_sweep(torch, coll, synth, iters=20):
+    """All-to-All-v at R=8 (bf16): (i) uniform 1-D, S = 8 KiB .. 64 MiB per
+    rank in rows of one element, equal counts; (ii) MoE-shaped, T tokens per
+    rank x top-8 of 256 experts (Zipf 1.2 routing), rows of 7168.  Buffers in
+    rank arenas; sets rotate so that a size's working set exceeds the 256 MB
+    Infinity Cache where it can.  Algorithmic bytes 2 * (rows moved) * row
+    bytes.  Reports the median per-launch time and a batch mean."""
+    import numpy as np
+    bf = torch.bfloat16
+    res = {"uniform_row1": {}, "moe_rows7168": {}}
+    for lg in range(13, 27):
+        S = 1 << lg
+        n = S // 2
+        c = np.full((R, R), n // R, np.int64)
+        sd = np.tile(np.arange(R, dtype=np.int64) * (n // R), (R, 1))
+        dc = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+        tabs = (dc(c), dc(sd), dc(sd))          # packed: rdispls[d][s] = s * n/R
+        sets = 4 if S >= (8 << 20) else 1
+        bufs = []
+        for _ in range(sets):
+            snd, rcv = coll.rank_arena([(R, n, bf), (R, n, bf)])
+            for t in snd:
+                t.normal_()
+            bufs.append((snd, rcv))
+        fn = lambda i: coll.all_to_all_v(bufs[i][0], tabs[0], tabs[1], bufs[i][1], tabs[2], 1)
+        med, batch = _launch_times(torch, fn, sets, iters)
+        gt = _graph_time(torch, fn, sets)
+        nb = 2 * R * S
+        res["uniform_row1"][f"{S >> 10}KiB"] = {
+            "graph_us": round(gt * 1e6, 2), "graph_GBps": round(nb / gt / 1e9, 1),
+            "graph_frac": round(nb / gt / 1e9 / HBM_PEAK_GBS, 4),
+            "median_us": round(med * 1e6, 2), "GBps": round(nb / med / 1e9, 1),
+            "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
+            "batch_GBps": round(nb / batch / 1e9, 1)}
+        del bufs
+    E, K, H = 256, 8, 7168
+    for T in (16, 64, 256, 1024, 4096):
+        ids = [torch.from_numpy(synth.zipf_routing(T, E, K, seed=5100 + s)[0]).cuda()
+               for s in range(R)]
+        sc = torch.empty(R * R, dtype=torch.int64, device="cuda")
+        sdd, rdd = torch.empty_like(sc), torch.empty_like(sc)
+        ec = torch.empty(R * E, dtype=torch.int32, device="cuda")
+        pos = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(R)]
+        ws = torch.empty(coll.moe_workspace_bytes(R, T, K, E), dtype=torch.uint8, device="cuda")
+        coll.moe_layout(ids, E, sc, sdd, rdd, ec, pos, ws)
+        torch.cuda.synchronize()
+        cnt = sc.view(R, R).cpu()
+        rows = int(cnt.sum())
+        sets = 1 if T >= 4096 else (2 if T >= 256 else 4)
+        bufs = []
+        for _ in range(sets):
+            snd, rcv = coll.rank_arena([(R, (T * K, H), bf),
+                                        [((int(cnt[:, d].sum()), H), bf) for d in range(R)]])
+            for t in snd:
+                t.normal_()
+            bufs.append((snd, rcv))
+        fn = lambda i: coll.all_to_all_v(bufs[i][0], sc, sdd, bufs[i][1], rdd, H)
+        med, batch = _launch_times(torch, fn, sets, iters)
+        gt = _graph_time(torch, fn, sets, n=8 if T >= 4096 else 24, reps=2)
+        nb = 2 * rows * H * 2
+        res["moe_rows7168"][f"T{T}"] = {
+            "per_rank_MiB": round(T * K * H * 2 / 2**20, 2), "rows": rows,
+            "graph_us": round(gt * 1e6, 2), "graph_GBps": round(nb / gt / 1e9, 1),
+            "graph_frac": round(nb / gt / 1e9 / HBM_PEAK_GBS, 4),
+            "median_us": round(med * 1e6, 2), "GBps": round(nb / med / 1e9, 1),
+            "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
+            "batch_GBps": round(nb / batch / 1e9, 1)}
+        del bufs, ids, pos, ws
+    torch.cuda.empty_cache()
     return res
 
 
@@ -505,12 +678,21 @@ def main():
                 "bytes_per_launch": nbytes[dom],
                 "avg_launch_us": round(per_row[dom] * 1e3, 2)}
 
-    sweep = lab = None
+    sweep = lab = a2s = None
     if not args.no_sweep and not args.only:
         print("[bench] allreduce sweep", file=sys.stderr, flush=True)
         sweep = ar_sweep(torch, coll)
         print("[bench] allocation layout A/B", file=sys.stderr, flush=True)
         lab = layout_ab(torch, coll)
+        print("[bench] all-to-all-v sweep", file=sys.stderr, flush=True)
+        a2s = a2a_sweep(torch, coll, synth)
+
+    fused = lat = None
+    if not args.only:
+        print("[bench] fused MoE path", file=sys.stderr, flush=True)
+        fused = moe_fused(torch, coll, W, {n: rows_out[n]["us"] for n in names})
+        print("[bench] latency rows by graph replay", file=sys.stderr, flush=True)
+        lat = latency_rows_graph(torch, coll, W, {n: rows_out[n]["us"] for n in names})
 
     ab = extra = None
     if not args.no_sweep and not args.only:
@@ -542,8 +724,11 @@ def main():
         "rows": rows_out,
         "allreduce_sweep": sweep,
         "allreduce_16mib_layout_ab": lab,
+        "all_to_all_v_sweep": a2s,
         "broadcast_vs_padded_allgather": ab,
         "next_rows": extra,
+        "moe_fused": fused,
+        "latency_rows_graph": lat,
     }
     print(json.dumps(out))
 

@@ -48,6 +48,9 @@ SIGNATURES = {
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp]),
     "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
+    "coll_moe_dispatch": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
+    "coll_moe_combine_recv": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp,
+                                   _vp]),
 }
 
 
@@ -407,3 +410,62 @@ def moe_combine(backs, pos, weights, outs, stream=None) -> None:
     _check(lib().coll_moe_combine(R, _table(backs, "back"), _table(pos, "pos"),
                                   _table(weights, "w"), T, K, H, COLL_BF16, _table(outs, "out"),
                                   _stream(stream)), "moe_combine")
+
+
+def _layout_tables(R, tables, what):
+    for t, name in zip(tables, ("sendcounts", "sdispls", "rdispls")):
+        if t.dtype != torch.int64 or t.numel() != R * R:
+            raise ValueError(f"{what}: {name} must be int64 [R*R] on the device")
+
+
+def moe_dispatch(xs, pos, sendcounts, sdispls, rdispls, recvs, stream=None) -> None:
+    """Fused permute + All-to-All-v: every (t, k) row of xs[s] goes straight
+    to its receive row in recvs[d] (the layout of moe_layout)."""
+    R = _ranks(xs, "moe_dispatch")
+    T, H = xs[0].shape
+    K = pos[0].shape[1]
+    _layout_tables(R, (sendcounts, sdispls, rdispls), "moe_dispatch")
+    if len(recvs) != R:
+        raise ValueError("moe_dispatch: one receive buffer per rank")
+    for x in xs:
+        if tuple(x.shape) != (T, H) or x.dtype != xs[0].dtype:
+            raise ValueError("moe_dispatch: x must be [T, H] of one dtype")
+    for r in recvs:
+        if r.dtype != xs[0].dtype or r.numel() % max(H, 1) != 0:
+            raise ValueError("moe_dispatch: receive buffers are [rows, H] of x's dtype")
+    dt, mult = _copy_dtype(xs[0])
+    _check(lib().coll_moe_dispatch(R, _table(xs, "x"), _table(pos, "pos"),
+                                   _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
+                                   _dev(rdispls, "rd"), T, K, H * mult, dt,
+                                   _table(recvs, "recv"), _stream(stream)), "moe_dispatch")
+
+
+def moe_combine_recv(recvs, pos, sendcounts, sdispls, rdispls, weights, outs, topk_ids=None,
+                     stream=None) -> None:
+    """Fused reverse exchange + combine: outs[s][t] = rne(sum_k w * row_k), row_k
+    read from the receive buffers where moe_dispatch put it; with topk_ids the
+    test expert rne(x * (1 + e/256)) is applied to each row as it is read."""
+    R = _ranks(recvs, "moe_combine_recv")
+    T, K = pos[0].shape
+    H = outs[0].shape[-1]
+    _layout_tables(R, (sendcounts, sdispls, rdispls), "moe_combine_recv")
+    for r in recvs:
+        if r.dtype != torch.bfloat16 or r.numel() % max(H, 1) != 0:
+            raise ValueError("moe_combine_recv: receive buffers are bf16 [rows, H]")
+    for w in weights:
+        if w.dtype != torch.float32 or w.numel() != T * K:
+            raise ValueError("moe_combine_recv: weights are fp32 [T, K]")
+    for o in outs:
+        if o.dtype != torch.bfloat16 or o.numel() != T * H:
+            raise ValueError("moe_combine_recv: outputs are bf16 [T, H]")
+    ids = None
+    if topk_ids is not None:
+        for t in topk_ids:
+            if t.dtype != torch.int32 or t.numel() != T * K:
+                raise ValueError("moe_combine_recv: topk_ids are int32 [T, K]")
+        ids = _table(topk_ids, "ids")
+    _check(lib().coll_moe_combine_recv(R, _table(recvs, "recv"), _table(pos, "pos"),
+                                       _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
+                                       _dev(rdispls, "rd"), _table(weights, "w"), ids, T, K, H,
+                                       COLL_BF16, _table(outs, "out"), _stream(stream)),
+           "moe_combine_recv")

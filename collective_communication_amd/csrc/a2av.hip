@@ -134,6 +134,141 @@ __global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const i
   }
 }
 
+// Rows whose size or buffers do not allow 16-byte units on every row (the
+// host only knows the row size): the index space is 16-byte chunks of each
+// block, every block padded to whole chunks, so a chunk never spans two
+// blocks.  A chunk whose source and destination are 16-byte aligned and that
+// lies wholly inside its block moves as one 16-byte vector; any other chunk
+// (a block's tail, or a block whose two ends are misaligned) moves in the
+// widest unit that divides both addresses and its length.  With rows of one
+// bf16 and equal counts every block is aligned, so this runs at vector speed.
+// n (<= 16) bytes in units of T: all loads, then all stores.
+template <class T>
+__device__ __forceinline__ void copy_pieces(uint64_t src, uint64_t dst, uint32_t n) {
+  constexpr int M = 16 / (int)sizeof(T);
+  T t[M];
+#pragma unroll
+  for (int i = 0; i < M; i++)
+    if ((uint32_t)(i * sizeof(T)) < n) t[i] = gconst<T>(src)[i];
+#pragma unroll
+  for (int i = 0; i < M; i++)
+    if ((uint32_t)(i * sizeof(T)) < n) gmut<T>(dst)[i] = t[i];
+}
+
+__device__ __forceinline__ void copy_chunk_narrow(uint64_t src, uint64_t dst, uint32_t n) {
+  const uint32_t a = (uint32_t)(src | dst) | n;
+  if ((a & 7) == 0) copy_pieces<uint64_t>(src, dst, n);
+  else if ((a & 3) == 0) copy_pieces<uint32_t>(src, dst, n);
+  else if ((a & 1) == 0) copy_pieces<uint16_t>(src, dst, n);
+  else copy_pieces<uint8_t>(src, dst, n);
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
+                                                            const int64_t *counts,
+                                                            const int64_t *sdispls,
+                                                            const int64_t *rdispls,
+                                                            uint64_t row_bytes) {
+  constexpr int UN = kA2aU;
+  __shared__ uint64_t s_end[kMaxBlocks];   // inclusive end of block b, in chunks
+  __shared__ uint64_t s_src[kMaxBlocks];   // source byte address of the block's chunk 0
+  __shared__ uint64_t s_dst[kMaxBlocks];
+  __shared__ uint64_t s_len[kMaxBlocks];   // block length in bytes
+
+  const int nb = R * R;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint64_t len[4], nch[4];
+    uint64_t local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int b = lane * 4 + j;
+      len[j] = 0;
+      if (b < nb) {
+        const int64_t c = counts[b];
+        len[j] = c > 0 ? (uint64_t)c * row_bytes : 0;
+      }
+      nch[j] = (len[j] + 15) / 16;
+      local += nch[j];
+    }
+    const uint64_t incl = wave_incl_scan(local);
+    uint64_t start = incl - local;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int b = lane * 4 + j;
+      if (b < nb) {
+        const int s = b / R, d = b - s * R;
+        s_src[b] = reinterpret_cast<uintptr_t>(p.in[s]) + (uint64_t)sdispls[b] * row_bytes;
+        s_dst[b] = reinterpret_cast<uintptr_t>(p.out[d]) + (uint64_t)rdispls[d * R + s] * row_bytes;
+        s_len[b] = len[j];
+        start += nch[j];
+        s_end[b] = start;
+      }
+    }
+  }
+  __syncthreads();
+
+  const uint64_t total = s_end[nb - 1];
+  int top = 1;
+  while (top * 2 <= nb) top *= 2;
+  const uint64_t tile = (uint64_t)kBlock * UN;
+  uint64_t blo = 1, bhi = 0, sbase = 0, dbase = 0, blen = 0;
+  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
+       base += (uint64_t)gridDim.x * tile) {
+    uint64_t sa[UN], da[UN];
+    uint32_t n[UN];                 // bytes of the chunk; 0 = no chunk
+    bool vec[UN];
+    // 1. locate every chunk (LDS only)
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t x = base + (uint64_t)u * kBlock;
+      n[u] = 0;
+      vec[u] = false;
+      sa[u] = da[u] = 0;
+      if (x < total) {
+        if (x < blo || x >= bhi) {
+          int lo = 0;
+          for (int step = top; step > 0; step >>= 1) {
+            const int c = lo + step;
+            if (c <= nb && s_end[c - 1] <= x) lo = c;
+          }
+          blo = lo > 0 ? s_end[lo - 1] : 0;
+          bhi = s_end[lo];
+          sbase = s_src[lo];
+          dbase = s_dst[lo];
+          blen = s_len[lo];
+        }
+        const uint64_t off = (x - blo) * 16;
+        const uint64_t rem = blen - off;                 // > 0: x lies inside the block
+        n[u] = rem < 16 ? (uint32_t)rem : 16u;
+        sa[u] = sbase + off;
+        da[u] = dbase + off;
+        vec[u] = n[u] == 16 && ((sa[u] | da[u]) & 15) == 0;
+      }
+    }
+    // 2. all 16-byte loads, 3. all 16-byte stores
+    u32x4 v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      if (vec[u]) {
+        if constexpr (NT) v[u] = __builtin_nontemporal_load(gconst<u32x4>(sa[u]));
+        else v[u] = *gconst<u32x4>(sa[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      if (vec[u]) {
+        if constexpr (NT) __builtin_nontemporal_store(v[u], gmut<u32x4>(da[u]));
+        else *gmut<u32x4>(da[u]) = v[u];
+      }
+    }
+    // 4. the rest (block tails, misaligned blocks) in narrower units
+#pragma unroll
+    for (int u = 0; u < UN; u++)
+      if (n[u] && !vec[u]) copy_chunk_narrow(sa[u], da[u], n[u]);
+  }
+}
+
 }  // namespace
 
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
@@ -147,11 +282,23 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
   // workgroup per tile of the bound (surplus workgroups exit at once);
   // without one: the resident grid loops over the tiles.
   unsigned g = grid_resident(L);
-  if (rows_capacity > 0) g = grid_for(L, (uint64_t)rows_capacity * row_units, kA2aU);
-  if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
-  dim3 grid(g);
-  COLL_UNIT_SWITCH(a2av_kernel, unit, L.a2a_nt, grid, L.stream, p, R, counts, sdispls, rdispls,
-                   row_units);
+  if (unit == 16) {
+    if (rows_capacity > 0) g = grid_for(L, (uint64_t)rows_capacity * row_units, kA2aU);
+    if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
+    COLL_UNIT_SWITCH(a2av_kernel, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts, sdispls,
+                     rdispls, row_units);
+  } else {
+    // chunks: at most capacity bytes / 16 plus one partial chunk per block
+    if (rows_capacity > 0)
+      g = grid_for(L, ((uint64_t)rows_capacity * row_bytes + 15) / 16 + (uint64_t)R * R, kA2aU);
+    if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
+    if (L.a2a_nt)
+      hipLaunchKernelGGL((a2av_chunk_kernel<true>), dim3(g), dim3(kBlock), 0, L.stream, p, R,
+                         counts, sdispls, rdispls, (uint64_t)row_bytes);
+    else
+      hipLaunchKernelGGL((a2av_chunk_kernel<false>), dim3(g), dim3(kBlock), 0, L.stream, p, R,
+                         counts, sdispls, rdispls, (uint64_t)row_bytes);
+  }
   return hip_status();
 }
 

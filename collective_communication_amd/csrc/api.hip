@@ -344,4 +344,54 @@ int coll_moe_combine(int R, const void *const *back, const int32_t *const *pos,
   return launch_moe_combine(launch_ctx(stream), R, bs, ps, ws, tokens, topk, hidden, os);
 }
 
+// Receive pointers of the fused MoE calls: NULL only for ranks that receive
+// no rows (as in coll_all_to_all_v).
+static bool fill_recv(int R, const void *const *src, const void **dst) {
+  if (!src) return false;
+  for (int r = 0; r < R; r++) dst[r] = src[r];
+  return true;
+}
+
+int coll_moe_dispatch(int R, const void *const *x, const int32_t *const *pos,
+                      const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
+                      int tokens, int topk, size_t hidden, coll_dtype_t dtype,
+                      void *const *recvbufs, void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || tokens < 0 || topk < 1) return COLL_ERR_INVALID_ARG;
+  if (tokens == 0 || hidden == 0) return COLL_OK;
+  if ((int64_t)tokens * topk >= ((int64_t)1 << 31) || !bytes_ok(hidden, dtype_size(dtype), 1))
+    return COLL_ERR_INVALID_ARG;
+  if (!sendcounts || !sdispls || !rdispls) return COLL_ERR_INVALID_ARG;
+  PtrTable xs{}, ps{}, rs{};
+  if (!fill_in(R, x, xs.p) || !fill_in(R, reinterpret_cast<const void *const *>(pos), ps.p) ||
+      !fill_recv(R, reinterpret_cast<const void *const *>(recvbufs), rs.p))
+    return COLL_ERR_INVALID_ARG;
+  MutPtrTable out{};
+  for (int r = 0; r < R; r++) out.p[r] = const_cast<void *>(rs.p[r]);
+  return launch_moe_dispatch(launch_ctx(stream), R, xs, ps, sendcounts, sdispls, rdispls, tokens,
+                             topk, hidden * dtype_size(dtype), out);
+}
+
+int coll_moe_combine_recv(int R, const void *const *recvbufs, const int32_t *const *pos,
+                          const int64_t *sendcounts, const int64_t *sdispls,
+                          const int64_t *rdispls, const float *const *topk_w,
+                          const int32_t *const *topk_ids, int tokens, int topk, size_t hidden,
+                          coll_dtype_t dtype, void *const *out, void *stream) {
+  if (!ranks_ok(R) || tokens < 0 || topk < 1) return COLL_ERR_INVALID_ARG;
+  if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
+  if (tokens == 0 || hidden == 0) return COLL_OK;
+  if ((int64_t)tokens * topk >= ((int64_t)1 << 31) || hidden >= ((size_t)1 << 31))
+    return COLL_ERR_INVALID_ARG;
+  if (!sendcounts || !sdispls || !rdispls) return COLL_ERR_INVALID_ARG;
+  PtrTable rs{}, ps{}, ws{}, is{};
+  MutPtrTable os{};
+  if (!fill_recv(R, recvbufs, rs.p) ||
+      !fill_in(R, reinterpret_cast<const void *const *>(pos), ps.p) ||
+      !fill_in(R, reinterpret_cast<const void *const *>(topk_w), ws.p) || !fill_out(R, out, os.p))
+    return COLL_ERR_INVALID_ARG;
+  if (topk_ids && !fill_in(R, reinterpret_cast<const void *const *>(topk_ids), is.p))
+    return COLL_ERR_INVALID_ARG;
+  return launch_moe_combine_recv(launch_ctx(stream), R, rs, ps, sendcounts, sdispls, rdispls, ws,
+                                 topk_ids ? &is : nullptr, tokens, topk, hidden, os);
+}
+
 }  // extern "C"

@@ -402,5 +402,12 @@ int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             size_t hidden, size_t rows_capacity);
 int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTable &pos,
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
+int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,
+                        const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
+                        int T, int K, size_t row_bytes, const MutPtrTable &recv);
+int launch_moe_combine_recv(const Launch &L, int R, const PtrTable &recv, const PtrTable &pos,
+                            const int64_t *sendcounts, const int64_t *sdispls,
+                            const int64_t *rdispls, const PtrTable &w, const PtrTable *ids, int T,
+                            int K, size_t hidden, const MutPtrTable &out);
 
 }  // namespace coll

@@ -458,6 +458,201 @@ __global__ __launch_bounds__(kBlock) void moe_combine_kernel(PtrTable back, PtrT
   }
 }
 
+// ------------------------------------------------- fused dispatch / combine
+
+// The send blocks of source s (its row of the layout), staged in LDS once per
+// workgroup: send slots [lo[d], hi[d]) go to rank d, whose receive rows start
+// at rd[d].  A slot's destination is found by a wave-uniform scan over d.
+struct SrcBlocks {
+  int64_t lo[COLL_MAX_RANKS];
+  int64_t hi[COLL_MAX_RANKS];
+  int64_t rd[COLL_MAX_RANKS];
+};
+
+__device__ __forceinline__ void load_src_blocks(SrcBlocks &b, int R, int s,
+                                                const int64_t *sendcounts,
+                                                const int64_t *sdispls,
+                                                const int64_t *rdispls) {
+  if ((int)threadIdx.x < R) {
+    const int d = threadIdx.x;
+    const int64_t a = sdispls[s * R + d];
+    b.lo[d] = a;
+    b.hi[d] = a + sendcounts[s * R + d];
+    b.rd[d] = rdispls[d * R + s];
+  }
+  __syncthreads();
+}
+
+// Receive row of send slot `slot` of the staged source; d = -1 when no block
+// holds it (only a corrupt layout does that).
+__device__ __forceinline__ int64_t recv_row_of(const SrcBlocks &b, int R, int64_t slot, int &d) {
+  for (int q = 0; q < R; q++) {
+    if (slot >= b.lo[q] && slot < b.hi[q]) {
+      d = q;
+      return b.rd[q] + (slot - b.lo[q]);
+    }
+  }
+  d = -1;
+  return 0;
+}
+
+// recv[d][rdispls[d][s] + pos - sdispls[s][d]] = x[s][t] for every k: the
+// permute and the exchange in one pass (each token row read once, written K
+// times straight into its destination's receive buffer).
+template <int B, bool NT>
+__global__ __launch_bounds__(kBlock) void moe_dispatch_kernel(PtrTable x, PtrTable pos,
+                                                              MutPtrTable recv,
+                                                              const int64_t *sendcounts,
+                                                              const int64_t *sdispls,
+                                                              const int64_t *rdispls, int R,
+                                                              int T, int K, uint32_t upr,
+                                                              int nseg) {
+  using U = typename UnitT<B>::T;
+  constexpr int UN = kPermuteU;
+  __shared__ SrcBlocks blk;
+  const int s = blockIdx.y;
+  load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls);
+  const RowItem it = row_item(T, nseg);
+  if (!it.valid) return;
+  const int lane = threadIdx.x & 63;
+  const U *src = reinterpret_cast<const U *>(x.p[s]) + (size_t)it.t * upr;
+  const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
+  const uint32_t u0 = (uint32_t)it.seg * (64 * UN) + lane;
+  U v[UN];
+#pragma unroll
+  for (int u = 0; u < UN; u++) {
+    const uint32_t x_u = u0 + u * 64;
+    if (x_u < upr) v[u] = NT ? __builtin_nontemporal_load(src + x_u) : src[x_u];
+  }
+  for (int k = 0; k < K; k++) {
+    const int32_t slot = __builtin_amdgcn_readfirstlane(pk[k]);
+    int d;
+    const int64_t row = recv_row_of(blk, R, slot, d);
+    if (d < 0) continue;                                     // never write outside
+    U *base = reinterpret_cast<U *>(recv.p[__builtin_amdgcn_readfirstlane(d)]);
+    if (!base) continue;                                     // a rank that receives nothing
+    U *dst = base + (size_t)row * upr;
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint32_t x_u = u0 + u * 64;
+      if (x_u < upr) {
+        if constexpr (NT) __builtin_nontemporal_store(v[u], dst + x_u);
+        else dst[x_u] = v[u];
+      }
+    }
+  }
+}
+
+// out[s][t] = rne(fold_k w[t,k] * widen(y_k)), y_k the receive row of (s,t,k)
+// (the reverse exchange is a read of the destination's buffer).  EXPERT: y_k
+// = rne(widen(row) * (1 + e/256)) with e = ids[s][t,k], the test expert applied
+// as the row is read.  A slot that no block holds contributes +0.
+template <int G, bool NT, bool EXPERT>
+__global__ __launch_bounds__(kBlock) void moe_combine_recv_kernel(
+    PtrTable recv, PtrTable pos, PtrTable wts, PtrTable ids, MutPtrTable out,
+    const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls, int R, int T, int K,
+    uint32_t upr, int nseg) {
+  constexpr int kChunk = 8;
+  constexpr int UN = (G == 8) ? kCombineU : 1;
+  __shared__ SrcBlocks blk;
+  const int s = blockIdx.y;
+  load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls);
+  const RowItem it = row_item(T, nseg);
+  if (!it.valid) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
+  const float *wk = reinterpret_cast<const float *>(wts.p[s]) + (size_t)it.t * K;
+  const int32_t *ek = EXPERT ? reinterpret_cast<const int32_t *>(ids.p[s]) + (size_t)it.t * K
+                             : nullptr;
+  uint16_t *o = reinterpret_cast<uint16_t *>(out.p[s]);
+  const uint32_t u0 = (uint32_t)it.seg * (64 * UN) + lane;
+  if constexpr (G == 8) {
+    float acc[UN][8];
+    for (int k0 = 0; k0 < K; k0 += kChunk) {
+      const uint16_t *rowp[kChunk];
+      float wgt[kChunk], sc[kChunk];
+      bool live[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; c++) {
+        rowp[c] = nullptr;
+        wgt[c] = 0.0f;
+        sc[c] = 1.0f;
+        live[c] = false;
+        if (k0 + c < K) {
+          int d;
+          const int64_t row = recv_row_of(blk, R, __builtin_amdgcn_readfirstlane(pk[k0 + c]), d);
+          live[c] = d >= 0 && recv.p[__builtin_amdgcn_readfirstlane(d >= 0 ? d : 0)] != nullptr;
+          if (live[c])
+            rowp[c] = reinterpret_cast<const uint16_t *>(
+                          recv.p[__builtin_amdgcn_readfirstlane(d)]) + (size_t)row * upr * 8;
+          wgt[c] = __builtin_bit_cast(
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wk[k0 + c])));
+          if constexpr (EXPERT) sc[c] = 1.0f + (float)__builtin_amdgcn_readfirstlane(ek[k0 + c]) / 256.0f;
+        }
+      }
+      u32x4 v[UN][kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; c++) {
+#pragma unroll
+        for (int uu = 0; uu < UN; uu++) {
+          const uint32_t u = u0 + uu * 64;
+          v[uu][c] = u32x4{0u, 0u, 0u, 0u};
+          if (live[c] && u < upr) v[uu][c] = ld<u32x4, NT>(rowp[c], u);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kChunk; c++) {
+        if (k0 + c < K) {
+#pragma unroll
+          for (int uu = 0; uu < UN; uu++) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              uint32_t y = v[uu][c][q];
+              if constexpr (EXPERT) y = pack_bf16(bf16_lo(y) * sc[c], bf16_hi(y) * sc[c]);
+              const float lo = wgt[c] * bf16_lo(y);
+              const float hi = wgt[c] * bf16_hi(y);
+              if (k0 + c == 0) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
+              else { acc[uu][2 * q] = acc[uu][2 * q] + lo; acc[uu][2 * q + 1] = acc[uu][2 * q + 1] + hi; }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < UN; uu++) {
+      const uint32_t u = u0 + uu * 64;
+      if (u < upr) {
+        u32x4 r;
+#pragma unroll
+        for (int q = 0; q < 4; q++) r[q] = pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]);
+        st<u32x4, NT>(o + (size_t)it.t * upr * 8, u, r);
+      }
+    }
+  } else {
+    const uint32_t u = u0;
+    if (u < upr) {
+      float acc = 0.0f;
+      for (int k = 0; k < K; k++) {
+        int d;
+        const int64_t row = recv_row_of(blk, R, __builtin_amdgcn_readfirstlane(pk[k]), d);
+        uint32_t y = 0u;
+        if (d >= 0) {
+          const uint16_t *rp = reinterpret_cast<const uint16_t *>(
+              recv.p[__builtin_amdgcn_readfirstlane(d)]);
+          if (rp) y = rp[(size_t)row * upr + u];
+        }
+        if constexpr (EXPERT) {
+          const float sc = 1.0f + (float)__builtin_amdgcn_readfirstlane(ek[k]) / 256.0f;
+          y = pack_bf16(bf16_lo(y) * sc, 0.0f) & 0xFFFFu;
+        }
+        const float prod = wk[k] * bf16_lo(y);
+        acc = (k == 0) ? prod : acc + prod;
+      }
+      o[(size_t)it.t * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
+    }
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -547,6 +742,54 @@ int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTa
     hipLaunchKernelGGL((moe_combine_kernel<1, false>), grid, dim3(kBlock), 0, L.stream, back, pos,
                        w, out, T, K, (uint32_t)upr, nseg);
   }
+  return hip_status();
+}
+
+int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,
+                        const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
+                        int T, int K, size_t row_bytes, const MutPtrTable &recv) {
+  uintptr_t bits = row_bytes;
+  for (int r = 0; r < R; r++) bits |= (uintptr_t)x.p[r] | (uintptr_t)recv.p[r];
+  const int unit = copy_unit(bits);
+  const uint64_t upr = row_bytes / unit;
+  if (T == 0 || upr == 0) return COLL_OK;
+  if (upr >= (1ull << 31)) return COLL_ERR_UNSUPPORTED;
+  const int nseg = (int)((upr + 64 * kPermuteU - 1) / (64 * kPermuteU));
+  const uint64_t items = (uint64_t)T * nseg;
+  if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
+  const bool nt = (uint64_t)R * T * upr * unit * (1 + K) >= L.nt_bytes;
+  dim3 grid((unsigned)((items + 3) / 4), R);
+  COLL_UNIT_SWITCH(moe_dispatch_kernel, unit, nt, grid, L.stream, x, pos, recv, sendcounts,
+                   sdispls, rdispls, R, T, K, (uint32_t)upr, nseg);
+  return hip_status();
+}
+
+int launch_moe_combine_recv(const Launch &L, int R, const PtrTable &recv, const PtrTable &pos,
+                            const int64_t *sendcounts, const int64_t *sdispls,
+                            const int64_t *rdispls, const PtrTable &w, const PtrTable *ids, int T,
+                            int K, size_t hidden, const MutPtrTable &out) {
+  bool vec = (hidden % 8) == 0;
+  for (int r = 0; r < R; r++) vec = vec && aligned16(recv.p[r]) && aligned16(out.p[r]);
+  if (T == 0) return COLL_OK;
+  const uint64_t upr = vec ? hidden / 8 : hidden;
+  const int per_seg = vec ? 64 * kCombineU : 64;
+  const int nseg = (int)((upr + per_seg - 1) / per_seg);
+  const uint64_t items = (uint64_t)T * nseg;
+  if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)((items + 3) / 4), R);
+  const bool nt = (uint64_t)R * T * (K + 1) * hidden * 2 >= L.nt_bytes;
+  const PtrTable none{};
+  const PtrTable &idt = ids ? *ids : none;
+#define COLL_COMBINE_RECV(G, NTV, EX)                                                              \
+  hipLaunchKernelGGL((moe_combine_recv_kernel<G, NTV, EX>), grid, dim3(kBlock), 0, L.stream, recv, \
+                     pos, w, idt, out, sendcounts, sdispls, rdispls, R, T, K, (uint32_t)upr, nseg)
+  if (vec && nt && ids) COLL_COMBINE_RECV(8, true, true);
+  else if (vec && nt) COLL_COMBINE_RECV(8, true, false);
+  else if (vec && ids) COLL_COMBINE_RECV(8, false, true);
+  else if (vec) COLL_COMBINE_RECV(8, false, false);
+  else if (ids) COLL_COMBINE_RECV(1, false, true);
+  else COLL_COMBINE_RECV(1, false, false);
+#undef COLL_COMBINE_RECV
   return hip_status();
 }
 

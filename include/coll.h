@@ -306,6 +306,49 @@ int coll_moe_combine(int nranks, const void *const *back, const int32_t *const *
                      const float *const *topk_w, int tokens, int topk, size_t hidden,
                      coll_dtype_t dtype, void *const *out, void *stream);
 
+/*
+ * Fused dispatch -- the tutorial's 8.4 dispatch (tokens go to the rank that
+ * owns their expert) as one pass: on one GPU the exchange is a store into the
+ * destination's buffer, so the permute writes each (t, k) row straight to its
+ * receive row instead of a send buffer:
+ *   recv[d][rdispls[d*R+s] + p - sdispls[s*R+d]] = x[s][t],  p = pos[s][t*topk+k],
+ * where d is the rank whose send block [sdispls[s*R+d], sdispls[s*R+d] +
+ * sendcounts[s*R+d]) holds p.  recvbufs end up exactly as after
+ * coll_moe_permute followed by coll_all_to_all_v with the same layout.
+ *   x[s]: [tokens, hidden]; pos, counts, displacements: the outputs of
+ *   coll_moe_layout (device arrays); recvbufs[d]: the receive buffers, NULL
+ *   allowed for a rank that receives no rows.  Any dtype (a copy).
+ * A slot that no block holds is not written (a corrupt layout); the caller
+ * guarantees that every receive buffer holds the rows the layout sends it.
+ */
+int coll_moe_dispatch(int nranks, const void *const *x, const int32_t *const *pos,
+                      const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
+                      int tokens, int topk, size_t hidden, coll_dtype_t dtype,
+                      void *const *recvbufs, void *stream);
+
+/*
+ * Fused combine -- the tutorial's 8.4 combine (results return to the token's
+ * owner and are gate-weighted) as one pass: the reverse exchange is a read of
+ * the destination's buffer, so each (t, k) row is read where
+ * coll_moe_dispatch put it:
+ *   out[s][t] = rne( sum_{k ascending} w[s][t*topk+k] * widen(y_k) ),
+ *   y_k = recvbufs[d][rdispls[d*R+s] + p - sdispls[s*R+d]]  (p, d as above),
+ * with the fold, rounding and no-FMA rule of coll_moe_combine: bit-identical
+ * to coll_all_to_all_v with transposed counts followed by coll_moe_combine.
+ * topk_ids != NULL (the routing, [tokens, topk] int32 per rank): the test
+ * expert of coll_moe_expert_scale is applied to each row as it is read,
+ * y_k = rne(widen(row) * (1 + e/256)) with e = topk_ids[s][t*topk+k], so the
+ * expert op, the reverse exchange and the combine are one read of recvbufs
+ * (which is not modified).  topk_ids == NULL: the rows are used as they are.
+ *   bf16 only; out[s]: [tokens, hidden], must not overlap any recvbufs.
+ * A slot that no block holds contributes +0 (a corrupt layout).
+ */
+int coll_moe_combine_recv(int nranks, const void *const *recvbufs, const int32_t *const *pos,
+                          const int64_t *sendcounts, const int64_t *sdispls,
+                          const int64_t *rdispls, const float *const *topk_w,
+                          const int32_t *const *topk_ids, int tokens, int topk, size_t hidden,
+                          coll_dtype_t dtype, void *const *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

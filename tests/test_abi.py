@@ -247,3 +247,35 @@ def test_rank_arena_per_buffer_shapes_on_host(L):
     assert [t.dtype for t in recv] == [torch.bfloat16, torch.bfloat16, torch.int64]
     # (torch reports data_ptr() 0 for the empty view)
     assert [(t.data_ptr() // 4096) % 32 for t in [a] + recv if t.numel()] == [0, 1, 3]
+
+
+def test_fused_moe_entry_points_validate_on_host(L):
+    ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    tab = 0x3000                                       # a (never dereferenced) device table
+    # bad rank count, topk, tokens
+    assert L.coll_moe_dispatch(0, ok, ok, tab, tab, tab, 4, 2, 8, 0, ok, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 0, 8, 0, ok, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, -1, 2, 8, 0, ok, NULL) == -1
+    # zero tokens / zero hidden: no-op
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 0, 2, 8, 0, ok, NULL) == 0
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 2, 0, 0, ok, NULL) == 0
+    # missing layout tables or buffers
+    assert L.coll_moe_dispatch(2, ok, ok, NULL, tab, tab, 4, 2, 8, 0, ok, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, NULL, 4, 2, 8, 0, ok, NULL) == -1
+    assert L.coll_moe_dispatch(2, NULL, ok, tab, tab, tab, 4, 2, 8, 0, ok, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 2, 8, 0, NULL, NULL) == -1
+    # T*K must stay below 2^31
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 1 << 28, 8, 8, 0, ok, NULL) == -1
+
+    def cr(R=2, recv=ok, pos=ok, sc=tab, w=ok, ids=NULL, T=4, K=2, H=8, dt=0, out=ok):
+        return L.coll_moe_combine_recv(R, recv, pos, sc, tab, tab, w, ids, T, K, H, dt, out, NULL)
+    assert cr(R=17) == -1
+    assert cr(K=0) == -1
+    assert cr(dt=2) == -2                              # bf16 only
+    assert cr(T=0) == 0 and cr(H=0) == 0
+    assert cr(sc=NULL) == -1
+    assert cr(w=NULL) == -1
+    assert cr(out=NULL) == -1
+    assert cr(pos=NULL) == -1
+    half = (ctypes.c_void_p * 2)(0x1000, 0)
+    assert cr(ids=half) == -1                          # ids given: every rank needs them

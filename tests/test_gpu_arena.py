@@ -105,3 +105,49 @@ def test_all_to_all_v_on_rank_arena():
     for d in range(R):
         assert bits_equal(host(recvs[d]).reshape(-1), want[d].reshape(-1)), d
     assert outside_unchanged(before, host(full), recvs)
+
+
+@pytest.mark.parametrize("S", [8 << 10, 1 << 20, 16 << 20])
+def test_all_to_all_v_one_element_rows_uniform(S):
+    """Rows of one bf16, equal counts (the uniform All-to-All-v of the size
+    sweep): every block is 16-byte aligned, so the chunked path moves whole
+    16-byte vectors; the result is the block transpose."""
+    R = 8
+    n = S // 2
+    say("a2av one-element rows", S)
+    xs = [synth.random_bits(n, 2, 94000 + s) for s in range(R)]
+    c = np.full((R, R), n // R, np.int64)
+    sd, rd = oracle.packed_displs(c)
+    sends, recvs = coll.rank_arena([(R, n, torch.bfloat16), (R, n, torch.bfloat16)])
+    for t, x in zip(sends, xs):
+        t.copy_(dev(x))
+    for t in recvs:
+        t.view(torch.int16).fill_(0x7FAB)
+    dc = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+    coll.all_to_all_v(sends, dc(c), dc(sd), recvs, dc(rd), 1)
+    torch.cuda.synchronize()
+    want = oracle.all_to_all(xs)
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_all_to_all_v_one_element_rows_misaligned_blocks(seed):
+    """Odd counts put most blocks off 16-byte boundaries at one end or both:
+    such blocks move in narrower units; the result is still exact."""
+    R = 8
+    say("a2av misaligned one-element rows", seed)
+    g = np.random.default_rng(seed)
+    c = (g.integers(0, 3000, size=(R, R)) | 1).astype(np.int64)
+    sd, rd = oracle.packed_displs(c)
+    srows, rrows = c.sum(axis=1), c.sum(axis=0)
+    xs = [synth.random_bits(int(srows[s]), 2, 95000 + s) for s in range(R)]
+    sends = [dev(x) for x in xs]
+    recvs = [torch.full((int(rrows[d]),), 0x7FAB, dtype=torch.int16, device="cuda")
+             .view(torch.bfloat16) for d in range(R)]
+    dc = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+    coll.all_to_all_v(sends, dc(c), dc(sd), recvs, dc(rd), 1)
+    torch.cuda.synchronize()
+    want = oracle.all_to_all_v(xs, c, sd, rd, rrows, 1)
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
