@@ -150,6 +150,8 @@ def row_bytes(W):
     b["a2av_combine"] = 2 * rows * H * 2
     b["moe_combine"] = rows * H * 2 + R * T * H * 2 + R * T * K * 8
     b["copy_ref"] = 2 << 30
+    b["moe_dispatch_fused"] = R * T * H * 2 + rows * H * 2 + R * T * K * 4
+    b["moe_combine_fused"] = rows * H * 2 + R * T * H * 2 + R * T * K * 12
     return b
 
 
@@ -179,6 +181,12 @@ def step_rows(W, coll, torch):
 # rows run only when named with --only
 EXTRA_ROWS = {
     "copy_ref": lambda W, coll: coll.broadcast(W["copy_src"], W["copy_dst"], 0),
+    # the fused MoE kernels on the step's layout (into the step's buffers)
+    "moe_dispatch_fused": lambda W, coll: coll.moe_dispatch(W["moe_x"], W["pos"], W["sc"],
+                                                            W["sd"], W["rd"], W["recv"]),
+    "moe_combine_fused": lambda W, coll: coll.moe_combine_recv(
+        W["recv"], W["pos"], W["sc"], W["sd"], W["rd"], W["moe_w"], W["out"],
+        topk_ids=W["moe_ids"]),
 }
 
 
@@ -691,8 +699,9 @@ def main():
     if not args.only:
         print("[bench] fused MoE path", file=sys.stderr, flush=True)
         fused = moe_fused(torch, coll, W, {n: rows_out[n]["us"] for n in names})
-        print("[bench] latency rows by graph replay", file=sys.stderr, flush=True)
-        lat = latency_rows_graph(torch, coll, W, {n: rows_out[n]["us"] for n in names})
+        if not args.no_sweep:
+            print("[bench] latency rows by graph replay", file=sys.stderr, flush=True)
+            lat = latency_rows_graph(torch, coll, W, {n: rows_out[n]["us"] for n in names})
 
     ab = extra = None
     if not args.no_sweep and not args.only:
