@@ -392,6 +392,15 @@ def _graph_time(torch, fn, sets, n=24, reps=4):
     return t
 
 
+def copy_ceiling(torch, coll, W):
+    """Practical HBM ceiling on this machine: a plain 1 GiB -> 1 GiB copy through
+    the library's copy kernel (2 GiB moved), graph-timed."""
+    t = _graph_time(torch, lambda i: coll.broadcast(W["copy_src"], W["copy_dst"], 0), 1,
+                    n=8, reps=2)
+    gbs = (2 << 30) / t / 1e9
+    return {"us": round(t * 1e6, 2), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def latency_rows_graph(torch, coll, W, per_row_us):
     """The latency-bound rows of the step (and a small fused MoE pipeline)
     timed by HIP-graph replay, beside their eager per-launch times."""
@@ -436,9 +445,12 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
         med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters)
         gt = _graph_time(torch, lambda i: coll.allreduce(*bufs[i]), sets)
         nbytes = 2 * R * (mib << 20)
+        algbw = (mib << 20) / gt / 1e9           # nccl-tests style: S / t
         res[f"{mib}MiB"] = {"graph_us": round(gt * 1e6, 2),
                             "graph_GBps": round(nbytes / gt / 1e9, 1),
                             "graph_frac": round(nbytes / gt / 1e9 / HBM_PEAK_GBS, 4),
+                            "algbw_GBps": round(algbw, 1),
+                            "busbw_GBps": round(algbw * 2 * (R - 1) / R, 1),
                             "median_us": round(med * 1e6, 2),
                             "GBps": round(nbytes / med / 1e9, 1),
                             "frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4),
@@ -540,9 +552,10 @@ def layout_ab(torch, coll, mib=16, sets=4, iters=24):
 
 # --------------------------------------------------------------- CPU baseline
 
-def cpu_baseline():
-    """The oracle as it stands, single-threaded, on one pass of the whole step
-    at its bench sizes (about 10-20 s of CPU work)."""
+def cpu_baseline(min_seconds=10.0, max_passes=3):
+    """The oracle as it stands, single-threaded, on whole passes of the step at
+    its bench sizes, repeated until at least `min_seconds` of CPU work (at
+    most `max_passes` passes; inputs generated once)."""
     import numpy as np
 
     import oracle
@@ -559,40 +572,43 @@ def cpu_baseline():
         t_total += time.perf_counter() - t0
         bytes_total += nbytes
 
-    xs = [synth.gaussian(81920, 1.0, 1000 + r, "bf16") for r in range(4)]
-    timed(lambda: oracle.allreduce(xs, "bf16"), 2 * 4 * 81920 * 2)
-    xs = [synth.gaussian(64 * 7168, 0.02, 2000 + r, "bf16") for r in range(R)]
-    timed(lambda: oracle.allreduce(xs, "bf16"), 2 * R * 64 * 7168 * 2)
+    ar160 = [synth.gaussian(81920, 1.0, 1000 + r, "bf16") for r in range(4)]
+    ard = [synth.gaussian(64 * 7168, 0.02, 2000 + r, "bf16") for r in range(R)]
     n = (64 << 20) // 2
-    xs = [synth.gaussian(n, 0.02, 7000 + r, "bf16") for r in range(R)]
-    timed(lambda: oracle.allreduce(xs, "bf16"), 2 * R * n * 2)
-    xs = [synth.gaussian(8192 * 4096, 1.0, 3000 + r, "bf16") for r in range(R)]
+    ar64 = [synth.gaussian(n, 0.02, 7000 + r, "bf16") for r in range(R)]
+    sp = [synth.gaussian(8192 * 4096, 1.0, 3000 + r, "bf16") for r in range(R)]
     S = 8192 * 4096 * 2
-    holder = {}
-    timed(lambda: holder.setdefault("rs", oracle.reduce_scatter(xs, "bf16")), (R + 1) * S)
-    timed(lambda: oracle.all_gather(holder["rs"]), S + R * S)
-    del xs, holder
     lg = [synth.gaussian((256, 19008), 2.0, 4000 + r, "fp32") for r in range(R)]
-    timed(lambda: oracle.gather(lg, 0), 2 * R * 256 * 19008 * 4)
     ids = synth.uniform_int32(256, 0, 152064, 4107)
-    timed(lambda: oracle.broadcast(ids, R, 7), 256 * 4 * R)
     E, T, K, H = 256, 4096, 8, 7168
     tid, tw = [], []
     for s in range(R):
-        i, w = synth.zipf_routing(4096, E, K, seed=5100 + s)
-        tid.append(np.ascontiguousarray(i[:T]))
-        tw.append(np.ascontiguousarray(w[:T]))
+        i, w = synth.zipf_routing(T, E, K, seed=5100 + s)
+        tid.append(i)
+        tw.append(w)
     tx = [synth.gaussian((T, H), 1.0, 5000 + s, "bf16") for s in range(R)]
     rows = R * T * K
     moe_bytes = (2 * R * T * K * 4 + (R * T * H * 2 + rows * H * 2 + R * T * K * 4)
                  + 3 * 2 * rows * H * 2 + rows * H * 2 + R * T * H * 2 + R * T * K * 8)
-    timed(lambda: oracle.moe_pipeline(tx, tid, tw, E), moe_bytes)
+    passes = 0
+    while passes < max_passes and (passes == 0 or t_total < min_seconds):
+        timed(lambda: oracle.allreduce(ar160, "bf16"), 2 * 4 * 81920 * 2)
+        timed(lambda: oracle.allreduce(ard, "bf16"), 2 * R * 64 * 7168 * 2)
+        timed(lambda: oracle.allreduce(ar64, "bf16"), 2 * R * n * 2)
+        holder = {}
+        timed(lambda: holder.setdefault("rs", oracle.reduce_scatter(sp, "bf16")), (R + 1) * S)
+        timed(lambda: oracle.all_gather(holder["rs"]), S + R * S)
+        del holder
+        timed(lambda: oracle.gather(lg, 0), 2 * R * 256 * 19008 * 4)
+        timed(lambda: oracle.broadcast(ids, R, 7), 256 * 4 * R)
+        timed(lambda: oracle.moe_pipeline(tx, tid, tw, E), moe_bytes)
+        passes += 1
     return {"value": round(bytes_total / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "seconds": round(t_total, 2),
-            "sample": "one pass of every step row at its bench size (MoE leg: all 4096 "
-                      "tokens per rank); single-threaded C oracle (gcc -O2), algorithmic bytes "
-                      "of the sample / its wall time"}
+            "seconds": round(t_total, 2), "passes": passes,
+            "sample": f"{passes} pass(es) of every step row at its bench size (MoE leg: all "
+                      "4096 tokens per rank); single-threaded C oracle (gcc -O2), algorithmic "
+                      "bytes of the sample / its wall time"}
 
 
 # ------------------------------------------------------------------ roofline
@@ -695,13 +711,14 @@ def main():
         print("[bench] all-to-all-v sweep", file=sys.stderr, flush=True)
         a2s = a2a_sweep(torch, coll, synth)
 
-    fused = lat = None
+    fused = lat = ceil_ = None
     if not args.only:
         print("[bench] fused MoE path", file=sys.stderr, flush=True)
         fused = moe_fused(torch, coll, W, {n: rows_out[n]["us"] for n in names})
         if not args.no_sweep:
             print("[bench] latency rows by graph replay", file=sys.stderr, flush=True)
             lat = latency_rows_graph(torch, coll, W, {n: rows_out[n]["us"] for n in names})
+            ceil_ = copy_ceiling(torch, coll, W)
 
     ab = extra = None
     if not args.no_sweep and not args.only:
@@ -738,6 +755,7 @@ def main():
         "next_rows": extra,
         "moe_fused": fused,
         "latency_rows_graph": lat,
+        "copy_ceiling_1gib": ceil_,
     }
     print(json.dumps(out))
 
