@@ -51,6 +51,8 @@ Launch launch_ctx(void *stream) {
   L.a2a_nt = env_long("COLL_A2A_NT", 1) ? 1 : 0;
   const long g = env_long("COLL_A2A_GRID", 0);
   L.a2a_grid = (g > 0 && g < 0x7FFFFFFFL) ? g : 0;
+  const long ga = env_long("COLL_AR_GRID", 0);
+  L.ar_grid = (ga > 0 && ga < 0x7FFFFFFFL) ? ga : 0;
   return L;
 }
 

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kBlock) void rs_scalar(RankPtrs p, int R, size_t se
 
 template <int R, int DT, int OP, bool NT>
 void launch_ar_r(const Launch &L, const RankPtrs &p, size_t nvec) {
-  dim3 grid(grid_tiles(nvec, (size_t)ar_u<R>() * kArBlock));
+  dim3 grid(L.ar_grid > 0 ? (unsigned)L.ar_grid : grid_tiles(nvec, (size_t)ar_u<R>() * kArBlock));
   hipLaunchKernelGGL((ar_vec<R, DT, OP, NT>), grid, dim3(kArBlock), 0, L.stream, p, nvec);
 }
 
