@@ -44,7 +44,9 @@ Launch launch_ctx(void *stream) {
     g_dev[dev].ready = 1;
   }
   L.num_cus = g_dev[dev].num_cus;
-  long w = env_long("COLL_WGS_PER_CU", 8);
+  // persistent grids: 4 workgroups of 256 lanes per CU measured best for the
+  // test expert (MI355X, 3.5 GiB in place: 4 -> 5655 GB/s, 8 -> 5575, 2 -> 4460)
+  long w = env_long("COLL_WGS_PER_CU", 4);
   L.wgs_per_cu = (int)(w < 1 ? 1 : (w > 64 ? 64 : w));
   long nt = env_long("COLL_NT_MIN_BYTES", 32L << 20);
   L.nt_bytes = nt < 0 ? 0 : (size_t)nt;
