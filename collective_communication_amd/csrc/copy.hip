@@ -75,6 +75,36 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(RankPtrs p, void *out, u
   }
 }
 
+// The same with 64-bit indices, for outputs of 2^31 units (32 GiB with
+// 16-byte units) and more.
+template <int B, bool NT>
+__global__ __launch_bounds__(kBlock) void gather_kernel64(RankPtrs p, void *out, uint64_t total,
+                                                          FastDiv64 per_row, FastDiv64 upr) {
+  using U = typename UnitT<B>::T;
+  constexpr int UN = kCopyU;
+  const uint64_t tile = (uint64_t)kBlock * UN;
+  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
+       base += (uint64_t)gridDim.x * tile) {
+    U v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t j = base + (uint64_t)u * kBlock;
+      if (j < total) {
+        const uint64_t o = fdiv64(j, per_row);
+        const uint64_t rem = j - o * per_row.d;
+        const uint64_t q = fdiv64(rem, upr);
+        const uint64_t i = rem - q * upr.d;
+        v[u] = ld<U, NT>(p.in[q], o * upr.d + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      const uint64_t j = base + (uint64_t)u * kBlock;
+      if (j < total) st<U, NT>(out, j, v[u]);
+    }
+  }
+}
+
 // --------------------------------------------------------------- Broadcast
 template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void bcast_kernel(const void *src, RankPtrs p, int R,
@@ -161,13 +191,19 @@ int launch_gather(const Launch &L, int R, const RankPtrs &p, void *out, size_t o
   const int unit = copy_unit(bits);
   const size_t upr = inner_bytes / unit;            // units per rank per row
   const size_t total = outer * R * upr;
-  if (total >= (1ull << 31)) return COLL_ERR_UNSUPPORTED;   // 32-bit index space
-  const FastDiv f_row = make_fastdiv((uint32_t)(R * upr));
-  const FastDiv f_upr = make_fastdiv((uint32_t)upr);
   const bool nt = 2 * total * (size_t)unit >= L.nt_bytes;
   dim3 grid(grid_for(L, total, kCopyU));
-  const uint32_t t = (uint32_t)total;
-  COLL_UNIT_SWITCH(gather_kernel, unit, nt, grid, L.stream, p, out, t, f_row, f_upr);
+  if (total < (1ull << 31)) {                        // 32-bit index space
+    const FastDiv f_row = make_fastdiv((uint32_t)(R * upr));
+    const FastDiv f_upr = make_fastdiv((uint32_t)upr);
+    const uint32_t t = (uint32_t)total;
+    COLL_UNIT_SWITCH(gather_kernel, unit, nt, grid, L.stream, p, out, t, f_row, f_upr);
+  } else {
+    const FastDiv64 f_row = make_fastdiv64((uint64_t)R * upr);
+    const FastDiv64 f_upr = make_fastdiv64(upr);
+    COLL_UNIT_SWITCH(gather_kernel64, unit, nt, grid, L.stream, p, out, (uint64_t)total, f_row,
+                     f_upr);
+  }
   return hip_status();
 }
 
