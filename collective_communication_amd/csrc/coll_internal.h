@@ -61,10 +61,13 @@ __device__ __forceinline__ void st(void *base, size_t i, U v) {
 // so every load and store instruction of a wave covers 64 consecutive units),
 // issues all of the tile's loads before any store, and the grid has one
 // workgroup per tile (a single pass: the dispatcher balances the load).
-// Measured on MI355X for a plain 1 GiB copy: 16 KiB tiles (U = 4 x 16 B),
-// non-temporal both ways, reach ~6.2-6.4 TB/s.
+// Units per lane of the copy-family kernels (Gather, Broadcast, Scatter, the
+// uniform all-to-all and re-shard).  Measured on MI355X, graph replay, rank
+// buffers in an arena: one 16-byte unit per lane (4 KiB tiles) beat four
+// (16 KiB tiles) everywhere: plain 1 GiB copy 6.26 -> 6.53 TB/s, all-to-all
+// 8 x 64 MiB 6.23 -> 6.45, sequence -> heads re-shard 5.26 -> 5.87.
 #ifndef COLL_COPY_U
-#define COLL_COPY_U 4
+#define COLL_COPY_U 1
 #endif
 constexpr int kCopyU = COLL_COPY_U;
 
@@ -290,26 +293,28 @@ template <> struct UnitT<2> { typedef uint16_t T; };
 template <> struct UnitT<1> { typedef uint8_t T; };
 
 // Launch KERNEL<unit, nt> for a unit size and cache policy chosen at run time.
-#define COLL_UNIT_SWITCH(KERNEL, UNIT, NT, GRID, STREAM, ...)                                    \
+#define COLL_UNIT_SWITCH_BLOCK(KERNEL, UNIT, NT, GRID, BLOCK, STREAM, ...)                      \
   do {                                                                                         \
     if (NT) {                                                                                  \
       switch (UNIT) {                                                                          \
-        case 16: hipLaunchKernelGGL((KERNEL<16, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break; \
-        case 8: hipLaunchKernelGGL((KERNEL<8, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
-        case 4: hipLaunchKernelGGL((KERNEL<4, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
-        case 2: hipLaunchKernelGGL((KERNEL<2, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
-        default: hipLaunchKernelGGL((KERNEL<1, true>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;  \
+        case 16: hipLaunchKernelGGL((KERNEL<16, true>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break; \
+        case 8: hipLaunchKernelGGL((KERNEL<8, true>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;   \
+        case 4: hipLaunchKernelGGL((KERNEL<4, true>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;   \
+        case 2: hipLaunchKernelGGL((KERNEL<2, true>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;   \
+        default: hipLaunchKernelGGL((KERNEL<1, true>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;  \
       }                                                                                        \
     } else {                                                                                   \
       switch (UNIT) {                                                                          \
-        case 16: hipLaunchKernelGGL((KERNEL<16, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break; \
-        case 8: hipLaunchKernelGGL((KERNEL<8, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
-        case 4: hipLaunchKernelGGL((KERNEL<4, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
-        case 2: hipLaunchKernelGGL((KERNEL<2, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;   \
-        default: hipLaunchKernelGGL((KERNEL<1, false>), GRID, dim3(kBlock), 0, STREAM, __VA_ARGS__); break;  \
+        case 16: hipLaunchKernelGGL((KERNEL<16, false>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break; \
+        case 8: hipLaunchKernelGGL((KERNEL<8, false>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;   \
+        case 4: hipLaunchKernelGGL((KERNEL<4, false>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;   \
+        case 2: hipLaunchKernelGGL((KERNEL<2, false>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;   \
+        default: hipLaunchKernelGGL((KERNEL<1, false>), GRID, dim3(BLOCK), 0, STREAM, __VA_ARGS__); break;  \
       }                                                                                        \
     }                                                                                          \
   } while (0)
+#define COLL_UNIT_SWITCH(KERNEL, UNIT, NT, GRID, STREAM, ...) \
+  COLL_UNIT_SWITCH_BLOCK(KERNEL, UNIT, NT, GRID, kBlock, STREAM, __VA_ARGS__)
 
 // ----------------------------------------------------------- launch helpers
 
