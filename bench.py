@@ -342,9 +342,14 @@ def moe_fused(torch, coll, W, per_row_us, iters=10):
             "outputs_bitwise_equal_unfused": bool(same)}
 
 
-def _launch_times(torch, fn, sets, iters):
+def _pct(ts, q):
+    return ts[min(len(ts) - 1, int(q * len(ts)))]
+
+
+def _launch_times(torch, fn, sets, iters, pcts=None):
     """(median of per-launch event pairs, mean over one event pair around
-    `iters` back-to-back launches), seconds; launch i uses buffer set i % sets."""
+    `iters` back-to-back launches), seconds; launch i uses buffer set i % sets.
+    If `pcts` is a dict, the p10 / p90 of the per-launch times go into it."""
     for i in range(sets):
         fn(i)
     torch.cuda.synchronize()
@@ -356,6 +361,9 @@ def _launch_times(torch, fn, sets, iters):
         ev[i][1].record()
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in ev)
+    if pcts is not None:
+        pcts["p10_us"] = round(_pct(ts, 0.1) * 1e3, 2)
+        pcts["p90_us"] = round(_pct(ts, 0.9) * 1e3, 2)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(iters):
@@ -434,7 +442,7 @@ def _ar_sets(torch, coll, n, sets, arena):
     return out
 
 
-def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
+def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=50):
     """AllReduce R=8 bf16 at large sizes, rank buffers in rank arenas,
     rotating `sets` buffer sets so the working set (>= 1 GiB) exceeds the
     Infinity Cache.  Reports the median of per-launch event timings and the
@@ -442,7 +450,8 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
     res = {}
     for mib in sizes_mib:
         bufs = _ar_sets(torch, coll, (mib << 20) // 2, sets, True)
-        med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters)
+        pc = {}
+        med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters, pc)
         gt = _graph_time(torch, lambda i: coll.allreduce(*bufs[i]), sets)
         nbytes = 2 * R * (mib << 20)
         algbw = (mib << 20) / gt / 1e9           # nccl-tests style: S / t
@@ -451,7 +460,7 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
                             "graph_frac": round(nbytes / gt / 1e9 / HBM_PEAK_GBS, 4),
                             "algbw_GBps": round(algbw, 1),
                             "busbw_GBps": round(algbw * 2 * (R - 1) / R, 1),
-                            "median_us": round(med * 1e6, 2),
+                            "median_us": round(med * 1e6, 2), **pc,
                             "GBps": round(nbytes / med / 1e9, 1),
                             "frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4),
                             "batch_us": round(batch * 1e6, 2),
@@ -462,7 +471,7 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=24):
     return res
 
 
-def a2a_sweep(torch, coll, synth, iters=20):
+def a2a_sweep(torch, coll, synth):
     """All-to-All-v at R=8 (bf16): (i) uniform 1-D, S = 8 KiB .. 64 MiB per
     rank in rows of one element, equal counts; (ii) MoE-shaped, T tokens per
     rank x top-8 of 256 experts (Zipf 1.2 routing), rows of 7168.  Buffers in
@@ -487,13 +496,14 @@ def a2a_sweep(torch, coll, synth, iters=20):
                 t.normal_()
             bufs.append((snd, rcv))
         fn = lambda i: coll.all_to_all_v(bufs[i][0], tabs[0], tabs[1], bufs[i][1], tabs[2], 1)
-        med, batch = _launch_times(torch, fn, sets, iters)
+        pc = {}
+        med, batch = _launch_times(torch, fn, sets, 1000 if S < (1 << 20) else 50, pc)
         gt = _graph_time(torch, fn, sets)
         nb = 2 * R * S
         res["uniform_row1"][f"{S >> 10}KiB"] = {
             "graph_us": round(gt * 1e6, 2), "graph_GBps": round(nb / gt / 1e9, 1),
             "graph_frac": round(nb / gt / 1e9 / HBM_PEAK_GBS, 4),
-            "median_us": round(med * 1e6, 2), "GBps": round(nb / med / 1e9, 1),
+            "median_us": round(med * 1e6, 2), **pc, "GBps": round(nb / med / 1e9, 1),
             "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
             "batch_GBps": round(nb / batch / 1e9, 1)}
         del bufs
@@ -519,14 +529,15 @@ def a2a_sweep(torch, coll, synth, iters=20):
                 t.normal_()
             bufs.append((snd, rcv))
         fn = lambda i: coll.all_to_all_v(bufs[i][0], sc, sdd, bufs[i][1], rdd, H)
-        med, batch = _launch_times(torch, fn, sets, iters)
+        pc = {}
+        med, batch = _launch_times(torch, fn, sets, 50, pc)
         gt = _graph_time(torch, fn, sets, n=8 if T >= 4096 else 24, reps=2)
         nb = 2 * rows * H * 2
         res["moe_rows7168"][f"T{T}"] = {
             "per_rank_MiB": round(T * K * H * 2 / 2**20, 2), "rows": rows,
             "graph_us": round(gt * 1e6, 2), "graph_GBps": round(nb / gt / 1e9, 1),
             "graph_frac": round(nb / gt / 1e9 / HBM_PEAK_GBS, 4),
-            "median_us": round(med * 1e6, 2), "GBps": round(nb / med / 1e9, 1),
+            "median_us": round(med * 1e6, 2), **pc, "GBps": round(nb / med / 1e9, 1),
             "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
             "batch_GBps": round(nb / batch / 1e9, 1)}
         del bufs, ids, pos, ws
@@ -603,8 +614,16 @@ def cpu_baseline(min_seconds=10.0, max_passes=3):
         timed(lambda: oracle.broadcast(ids, R, 7), 256 * 4 * R)
         timed(lambda: oracle.moe_pipeline(tx, tid, tw, E), moe_bytes)
         passes += 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
     return {"value": round(bytes_total / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
+            "host_cpus_visible": len(os.sched_getaffinity(0)), "host_cpu_model": model,
             "seconds": round(t_total, 2), "passes": passes,
             "sample": f"{passes} pass(es) of every step row at its bench size (MoE leg: all "
                       "4096 tokens per rank); single-threaded C oracle (gcc -O2), algorithmic "
