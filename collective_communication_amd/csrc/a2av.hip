@@ -64,13 +64,19 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     uint64_t len[4];
+    int64_t sdv[4], rdv[4];
     uint64_t local = 0;
+    // all three tables are loaded before the scan: one round trip to L2
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int b = lane * 4 + j;
       len[j] = 0;
+      sdv[j] = rdv[j] = 0;
       if (b < nb) {
+        const int s = b / R, d = b - s * R;
         const int64_t c = counts[b];
+        sdv[j] = sdispls[b];
+        rdv[j] = rdispls[d * R + s];
         len[j] = c > 0 ? (uint64_t)c * row_units : 0;
       }
       local += len[j];
@@ -82,8 +88,8 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
       const int b = lane * 4 + j;
       if (b < nb) {
         const int s = b / R, d = b - s * R;
-        const uint64_t so = (uint64_t)sdispls[b] * row_units;
-        const uint64_t ro = (uint64_t)rdispls[d * R + s] * row_units;
+        const uint64_t so = (uint64_t)sdv[j] * row_units;
+        const uint64_t ro = (uint64_t)rdv[j] * row_units;
         s_src[b] = reinterpret_cast<uintptr_t>(p.in[s]) / B + so - start;
         s_dst[b] = reinterpret_cast<uintptr_t>(p.out[d]) / B + ro - start;
         start += len[j];
@@ -102,11 +108,14 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
   uint64_t blo = 1, bhi = 0, sbase = 0, dbase = 0;
   for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
        base += (uint64_t)gridDim.x * tile) {
-    U v[UN];
-    uint64_t dst[UN];
+    // 1. locate every unit of the tile (LDS only), 2. all loads, 3. all
+    // stores: with the lookups kept out from between the loads, the loads
+    // issue back to back (measured ~5% faster at the MoE shape)
+    uint64_t sa[UN], da[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
       const uint64_t x = base + (uint64_t)u * kBlock;
+      sa[u] = da[u] = 0;
       if (x < total) {
         if (x < blo || x >= bhi) {
           int lo = 0;                           // blocks ending at or before x
@@ -119,19 +128,23 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
           sbase = s_src[lo];
           dbase = s_dst[lo];
         }
-        const auto *src = gconst<U>((sbase + x) * B);
-        dst[u] = (dbase + x) * B;
-        if constexpr (NT) v[u] = __builtin_nontemporal_load(src);
-        else v[u] = *src;
+        sa[u] = (sbase + x) * B;
+        da[u] = (dbase + x) * B;
+      }
+    }
+    U v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+      if (base + (uint64_t)u * kBlock < total) {
+        if constexpr (NT) v[u] = __builtin_nontemporal_load(gconst<U>(sa[u]));
+        else v[u] = *gconst<U>(sa[u]);
       }
     }
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t x = base + (uint64_t)u * kBlock;
-      if (x < total) {
-        auto *d = gmut<U>(dst[u]);
-        if constexpr (NT) __builtin_nontemporal_store(v[u], d);
-        else *d = v[u];
+      if (base + (uint64_t)u * kBlock < total) {
+        if constexpr (NT) __builtin_nontemporal_store(v[u], gmut<U>(da[u]));
+        else *gmut<U>(da[u]) = v[u];
       }
     }
   }
@@ -199,14 +212,19 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     uint64_t len[4], nch[4];
+    int64_t sdv[4], rdv[4];
     uint64_t local = 0;
     bool misaligned = false;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int b = lane * 4 + j;
       len[j] = 0;
+      sdv[j] = rdv[j] = 0;
       if (b < nb) {
+        const int s = b / R, d = b - s * R;
         const int64_t c = counts[b];
+        sdv[j] = sdispls[b];
+        rdv[j] = rdispls[d * R + s];
         len[j] = c > 0 ? (uint64_t)c * row_bytes : 0;
       }
       nch[j] = (len[j] + 15) / 16;
@@ -219,8 +237,8 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
       const int b = lane * 4 + j;
       if (b < nb) {
         const int s = b / R, d = b - s * R;
-        s_src[b] = reinterpret_cast<uintptr_t>(p.in[s]) + (uint64_t)sdispls[b] * row_bytes;
-        s_dst[b] = reinterpret_cast<uintptr_t>(p.out[d]) + (uint64_t)rdispls[d * R + s] * row_bytes;
+        s_src[b] = reinterpret_cast<uintptr_t>(p.in[s]) + (uint64_t)sdv[j] * row_bytes;
+        s_dst[b] = reinterpret_cast<uintptr_t>(p.out[d]) + (uint64_t)rdv[j] * row_bytes;
         s_len[b] = len[j];
         start += nch[j];
         s_end[b] = start;
