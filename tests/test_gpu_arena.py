@@ -151,3 +151,48 @@ def test_all_to_all_v_one_element_rows_misaligned_blocks(seed):
     want = oracle.all_to_all_v(xs, c, sd, rd, rrows, 1)
     for d in range(R):
         assert bits_equal(host(recvs[d]), want[d]), d
+
+
+def test_all_to_all_v_one_element_rows_one_pass_grid():
+    """64 MiB per rank (512 MiB received in all): above the resident-grid
+    bound, so the chunked path runs on its one-pass grid; compared in full."""
+    R, S = 8, 64 << 20
+    n = S // 2
+    say("a2av one-element rows, one-pass grid", S)
+    xs = [synth.random_bits(n, 2, 96000 + s) for s in range(R)]
+    c = np.full((R, R), n // R, np.int64)
+    sd, rd = oracle.packed_displs(c)
+    sends, recvs = coll.rank_arena([(R, n, torch.bfloat16), (R, n, torch.bfloat16)])
+    for t, x in zip(sends, xs):
+        t.copy_(dev(x))
+    for t in recvs:
+        t.view(torch.int16).fill_(0x7FAB)
+    dc = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+    coll.all_to_all_v(sends, dc(c), dc(sd), recvs, dc(rd), 1)
+    torch.cuda.synchronize()
+    want = oracle.all_to_all(xs)
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
+
+
+def test_all_to_all_v_misaligned_blocks_one_pass_grid():
+    """Odd counts of one-element rows, about 290 MB received in all: the
+    chunked path's general loop (aligned middles, narrow ends) on its one-pass
+    grid."""
+    R = 8
+    say("a2av misaligned blocks, one-pass grid")
+    g = np.random.default_rng(11)
+    c = (g.integers(2_000_000, 2_500_000, size=(R, R)) | 1).astype(np.int64)
+    sd, rd = oracle.packed_displs(c)
+    srows, rrows = c.sum(axis=1), c.sum(axis=0)
+    assert int(rrows.sum()) * 2 > (256 << 20)
+    xs = [synth.random_bits(int(srows[s]), 2, 96500 + s) for s in range(R)]
+    sends = [dev(x) for x in xs]
+    recvs = [torch.full((int(rrows[d]),), 0x7FAB, dtype=torch.int16, device="cuda")
+             .view(torch.bfloat16) for d in range(R)]
+    dc = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+    coll.all_to_all_v(sends, dc(c), dc(sd), recvs, dc(rd), 1)
+    torch.cuda.synchronize()
+    want = oracle.all_to_all_v(xs, c, sd, rd, rrows, 1)
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
