@@ -730,6 +730,35 @@ def main():
         print("[bench] all-to-all-v sweep", file=sys.stderr, flush=True)
         a2s = a2a_sweep(torch, coll, synth)
 
+    # the same step captured once in a HIP graph and replayed K times: the
+    # GPU-side step time without per-row events or host launch gaps
+    step_graph = None
+    if not args.only:
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            for _, fn in rows:
+                fn()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _, fn in rows:
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        gms = a.elapsed_time(b) / args.steps
+        step_graph = {"ms_per_step": round(gms, 4),
+                      "GBps": round(step_bytes / (gms * 1e-3) / 1e9, 1),
+                      "frac": round(step_bytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del g
+
     fused = lat = ceil_ = None
     if not args.only:
         print("[bench] fused MoE path", file=sys.stderr, flush=True)
@@ -765,6 +794,7 @@ def main():
                    "buffers": "rank arenas (coll_arena_layout: own 2 MiB page + 4 KiB colour per buffer)",
                    "moe_rows": W["moe_rows"], "moe_dest_share": W["dest_share"]},
         "roofline": roof,
+        "step_graph_replay": step_graph,
         "cpu_baseline": cpu,
         "rows": rows_out,
         "allreduce_sweep": sweep,
