@@ -44,17 +44,34 @@ Launch launch_ctx(void *stream) {
     g_dev[dev].ready = 1;
   }
   L.num_cus = g_dev[dev].num_cus;
-  // persistent grids: 4 workgroups of 256 lanes per CU measured best for the
-  // test expert (MI355X, 3.5 GiB in place: 4 -> 5655 GB/s, 8 -> 5575, 2 -> 4460)
-  long w = env_long("COLL_WGS_PER_CU", 4);
-  L.wgs_per_cu = (int)(w < 1 ? 1 : (w > 64 ? 64 : w));
-  long nt = env_long("COLL_NT_MIN_BYTES", 32L << 20);
-  L.nt_bytes = nt < 0 ? 0 : (size_t)nt;
-  L.a2a_nt = env_long("COLL_A2A_NT", 1) ? 1 : 0;
-  const long g = env_long("COLL_A2A_GRID", 0);
-  L.a2a_grid = (g > 0 && g < 0x7FFFFFFFL) ? g : 0;
-  const long ga = env_long("COLL_AR_GRID", 0);
-  L.ar_grid = (ga > 0 && ga < 0x7FFFFFFFL) ? ga : 0;
+  // Tuning knobs, read from the environment once per process.
+  struct Knobs {
+    int wgs_per_cu;
+    size_t nt_bytes;
+    int a2a_nt;
+    long a2a_grid, ar_grid;
+  };
+  static const Knobs k = [] {
+    Knobs v;
+    // persistent grids: 4 workgroups of 256 lanes per CU measured best for
+    // the test expert (MI355X, 3.5 GiB in place: 4 -> 5655 GB/s, 8 -> 5575,
+    // 2 -> 4460)
+    const long w = env_long("COLL_WGS_PER_CU", 4);
+    v.wgs_per_cu = (int)(w < 1 ? 1 : (w > 64 ? 64 : w));
+    const long nt = env_long("COLL_NT_MIN_BYTES", 32L << 20);
+    v.nt_bytes = nt < 0 ? 0 : (size_t)nt;
+    v.a2a_nt = env_long("COLL_A2A_NT", 1) ? 1 : 0;
+    const long g = env_long("COLL_A2A_GRID", 0);
+    v.a2a_grid = (g > 0 && g < 0x7FFFFFFFL) ? g : 0;
+    const long ga = env_long("COLL_AR_GRID", 0);
+    v.ar_grid = (ga > 0 && ga < 0x7FFFFFFFL) ? ga : 0;
+    return v;
+  }();
+  L.wgs_per_cu = k.wgs_per_cu;
+  L.nt_bytes = k.nt_bytes;
+  L.a2a_nt = k.a2a_nt;
+  L.a2a_grid = k.a2a_grid;
+  L.ar_grid = k.ar_grid;
   return L;
 }
 

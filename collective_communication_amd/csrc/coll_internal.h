@@ -328,7 +328,8 @@ struct Launch {
   long ar_grid;      // > 0: AllReduce launches this many workgroups (tuning)
 };
 
-// Device properties and tuning knobs (environment: COLL_WGS_PER_CU,
+// Device properties and tuning knobs (environment, read once per process:
+// COLL_WGS_PER_CU,
 // COLL_NT_MIN_BYTES, COLL_A2A_NT, COLL_A2A_GRID, COLL_AR_GRID).
 Launch launch_ctx(void *stream);
 

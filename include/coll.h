@@ -21,7 +21,8 @@
  *    nothing.  A launch failure returns COLL_ERR_HIP.  No C++ exception ever
  *    crosses this boundary.
  *  - The library allocates nothing and holds no state beyond a per-device
- *    cache of the compute-unit count; calls on different streams are
+ *    cache of the compute-unit count and its tuning knobs (COLL_* environment
+ *    variables, read once per process); calls on different streams are
  *    independent.  The MoE layout takes caller-provided workspace.
  *  - Reductions of bf16 / fp16 widen every element exactly to fp32, fold the
  *    ranks in ascending order 0, 1, ..., R-1 with the accumulator seeded by
@@ -193,9 +194,10 @@ int coll_broadcast(int nranks, const void *sendbuf_root, void *const *recvbufs, 
  * transposed and the two displacement tables swapped.
  *   recv_rows_capacity: the rows of all receive buffers together, an upper
  *   bound of the rows moved that the host knows without reading the counts.
- *   It sizes the launch (one workgroup per 16 KiB tile, the fastest form on
- *   MI355X); 0 means unknown, and a resident grid then loops over the tiles.
- *   It is never used to address memory.
+ *   It only shapes the launch, never the result or the memory addressed.
+ *   Above 256 MiB of capacity there is one workgroup per tile of the bound.
+ *   Up to 256 MiB, or with 0 (unknown), a resident grid loops over the tiles
+ *   (the faster forms on MI355X at those sizes).
  */
 int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *sendcounts,
                       const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
@@ -286,8 +288,9 @@ int coll_moe_permute(int nranks, const void *const *x, const int32_t *const *pos
  * expert e becomes y = rne(x * (1 + e/256)) in place (the fp32 product is
  * exact, so y is unique).  Row order in recvbufs[d] is: for s ascending,
  * starting at rdispls[d*R+s], the rows of d's experts in ascending expert
- * order, expert_counts[s*E+e] rows each.  recv_rows_capacity has the meaning
- * it has for coll_all_to_all_v (launch sizing only; 0 = unknown).
+ * order, expert_counts[s*E+e] rows each.  recv_rows_capacity: as for
+ * coll_all_to_all_v, an upper bound of the rows; it is not used by the
+ * current kernel, which always runs a resident grid.
  */
 int coll_moe_expert_scale(int nranks, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
