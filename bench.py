@@ -22,11 +22,12 @@ value = algorithmic bytes of the whole step / step time (GB/s).  Algorithmic
 bytes are the minimum each row must read plus write (e.g. AllReduce 2*R*S,
 All-to-All-v 2 * rows * row_bytes).  Per-row times come from HIP events on the
 stream the kernels run on; the dominant kernel (a2av_dispatch) is reported
-against the 8 TB/s HBM roofline.  A separate AllReduce sweep at 16/32/64 MiB
-per rank rotates four buffer sets so the 256 MB Infinity Cache cannot serve it.
+against the 8 TB/s HBM roofline.  Separate sweeps: AllReduce at 8 KiB .. 64 MiB
+per rank and All-to-All-v (uniform and MoE-shaped), rotating four buffer sets
+from 8 MiB up so the 256 MB Infinity Cache cannot serve the large sizes.
 
-The CPU baseline times the oracle (single-threaded C) on one pass of the same
-step at its bench sizes.
+The CPU baseline times the oracle (single-threaded C) on whole passes of the
+same step at its bench sizes.
 """
 from __future__ import annotations
 
@@ -410,8 +411,9 @@ def copy_ceiling(torch, coll, W):
 
 
 def latency_rows_graph(torch, coll, W, per_row_us):
-    """The latency-bound rows of the step (and a small fused MoE pipeline)
-    timed by HIP-graph replay, beside their eager per-launch times."""
+    """The latency-bound rows of the step timed by HIP-graph replay, beside
+    their eager per-launch times as prepared calls (the step's rows) and as
+    plain binding calls (argument checks and marshalling on every call)."""
     E, T, K, H = W["moe"]
     rows = {
         "ar_160k": lambda i: coll.allreduce(W["ar160_in"], W["ar160_out"]),
@@ -423,7 +425,9 @@ def latency_rows_graph(torch, coll, W, per_row_us):
     res = {}
     for name, fn in rows.items():
         t = _graph_time(torch, fn, 1)
-        res[name] = {"graph_us": round(t * 1e6, 2), "eager_us": per_row_us[name]}
+        plain, _ = _launch_times(torch, fn, 1, 200)
+        res[name] = {"graph_us": round(t * 1e6, 2), "eager_prepared_us": per_row_us[name],
+                     "eager_plain_us": round(plain * 1e6, 2)}
     return res
 
 
@@ -442,20 +446,26 @@ def _ar_sets(torch, coll, n, sets, arena):
     return out
 
 
-def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=50):
-    """AllReduce R=8 bf16 at large sizes, rank buffers in rank arenas,
-    rotating `sets` buffer sets so the working set (>= 1 GiB) exceeds the
-    Infinity Cache.  Reports the median of per-launch event timings and the
-    mean launch time of a back-to-back batch (no events between launches)."""
+def ar_sweep(torch, coll, log2_sizes=range(13, 27)):
+    """AllReduce R=8 bf16 1-D, S = 8 KiB .. 64 MiB per rank (powers of two),
+    N(0, 0.02^2), rank buffers in rank arenas.  From 8 MiB up, 4 buffer sets
+    rotate so the working set (>= 1 GiB at 16 MiB) exceeds the Infinity Cache.
+    Reports graph-replay time, the median (p10/p90) of per-launch event
+    timings over 50 launches (1000 below 1 MiB) and a back-to-back batch."""
     res = {}
-    for mib in sizes_mib:
-        bufs = _ar_sets(torch, coll, (mib << 20) // 2, sets, True)
+    for lg in log2_sizes:
+        S = 1 << lg
+        sets = 4 if S >= (8 << 20) else 1
+        iters = 1000 if S < (1 << 20) else 50
+        bufs = _ar_sets(torch, coll, S // 2, sets, True)
+        plans = [coll.prepare(coll.allreduce, *b) for b in bufs]
         pc = {}
-        med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters, pc)
-        gt = _graph_time(torch, lambda i: coll.allreduce(*bufs[i]), sets)
-        nbytes = 2 * R * (mib << 20)
-        algbw = (mib << 20) / gt / 1e9           # nccl-tests style: S / t
-        res[f"{mib}MiB"] = {"graph_us": round(gt * 1e6, 2),
+        med, batch = _launch_times(torch, lambda i: plans[i](), sets, iters, pc)
+        gt = _graph_time(torch, lambda i: plans[i](), sets)
+        nbytes = 2 * R * S
+        algbw = S / gt / 1e9                     # nccl-tests style: S / t
+        key = f"{S >> 20}MiB" if S >= (1 << 20) else f"{S >> 10}KiB"
+        res[key] = {"graph_us": round(gt * 1e6, 2),
                             "graph_GBps": round(nbytes / gt / 1e9, 1),
                             "graph_frac": round(nbytes / gt / 1e9 / HBM_PEAK_GBS, 4),
                             "algbw_GBps": round(algbw, 1),
@@ -466,7 +476,7 @@ def ar_sweep(torch, coll, sizes_mib=(16, 32, 64), sets=4, iters=50):
                             "batch_us": round(batch * 1e6, 2),
                             "batch_GBps": round(nbytes / batch / 1e9, 1),
                             "batch_frac": round(nbytes / batch / 1e9 / HBM_PEAK_GBS, 4)}
-        del bufs
+        del bufs, plans
         torch.cuda.empty_cache()
     return res
 
@@ -495,7 +505,9 @@ def a2a_sweep(torch, coll, synth):
             for t in snd:
                 t.normal_()
             bufs.append((snd, rcv))
-        fn = lambda i: coll.all_to_all_v(bufs[i][0], tabs[0], tabs[1], bufs[i][1], tabs[2], 1)
+        plans = [coll.prepare(coll.all_to_all_v, b[0], tabs[0], tabs[1], b[1], tabs[2], 1)
+                 for b in bufs]
+        fn = lambda i: plans[i]()
         pc = {}
         med, batch = _launch_times(torch, fn, sets, 1000 if S < (1 << 20) else 50, pc)
         gt = _graph_time(torch, fn, sets)
@@ -506,7 +518,7 @@ def a2a_sweep(torch, coll, synth):
             "median_us": round(med * 1e6, 2), **pc, "GBps": round(nb / med / 1e9, 1),
             "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
             "batch_GBps": round(nb / batch / 1e9, 1)}
-        del bufs
+        del bufs, plans
     E, K, H = 256, 8, 7168
     for T in (16, 64, 256, 1024, 4096):
         ids = [torch.from_numpy(synth.zipf_routing(T, E, K, seed=5100 + s)[0]).cuda()
@@ -528,7 +540,8 @@ def a2a_sweep(torch, coll, synth):
             for t in snd:
                 t.normal_()
             bufs.append((snd, rcv))
-        fn = lambda i: coll.all_to_all_v(bufs[i][0], sc, sdd, bufs[i][1], rdd, H)
+        plans = [coll.prepare(coll.all_to_all_v, b[0], sc, sdd, b[1], rdd, H) for b in bufs]
+        fn = lambda i: plans[i]()
         pc = {}
         med, batch = _launch_times(torch, fn, sets, 50, pc)
         gt = _graph_time(torch, fn, sets, n=8 if T >= 4096 else 24, reps=2)
@@ -540,7 +553,7 @@ def a2a_sweep(torch, coll, synth):
             "median_us": round(med * 1e6, 2), **pc, "GBps": round(nb / med / 1e9, 1),
             "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
             "batch_GBps": round(nb / batch / 1e9, 1)}
-        del bufs, ids, pos, ws
+        del bufs, plans, ids, pos, ws
     torch.cuda.empty_cache()
     return res
 
@@ -553,10 +566,11 @@ def layout_ab(torch, coll, mib=16, sets=4, iters=24):
     nbytes = 2 * R * (mib << 20)
     for name, arena in (("torch_alloc", False), ("rank_arena", True)):
         bufs = _ar_sets(torch, coll, (mib << 20) // 2, sets, arena)
-        med, batch = _launch_times(torch, lambda i: coll.allreduce(*bufs[i]), sets, iters)
+        plans = [coll.prepare(coll.allreduce, *b) for b in bufs]
+        med, batch = _launch_times(torch, lambda i: plans[i](), sets, iters)
         res[name] = {"median_us": round(med * 1e6, 2), "GBps": round(nbytes / med / 1e9, 1),
                      "batch_GBps": round(nbytes / batch / 1e9, 1)}
-        del bufs
+        del bufs, plans
         torch.cuda.empty_cache()
     return res
 
@@ -671,6 +685,9 @@ def main():
         keep = set(args.only.split(","))
         rows = [r for r in rows if r[0] in keep]
         rows += [(n, (lambda f=f: f(W, coll))) for n, f in EXTRA_ROWS.items() if n in keep]
+    # every row is a prepared call: argument checks and marshalling happen
+    # once, each launch only re-issues the C entry point
+    rows = [(n, coll.prepare(fn)) for n, fn in rows]
     nbytes = row_bytes(W)
 
     print("[bench] warmup", file=sys.stderr, flush=True)

@@ -6,11 +6,16 @@ current stream to the C ABI in ``include/coll.h``, and raises ``CollError`` on
 a negative status.  All computation happens in the library's HIP kernels;
 there is no fallback: if ``libcoll.so`` has not been built this module raises
 on first use.
+
+``prepare(fn, *args)`` runs those checks once and returns a ``Plan`` that only
+re-issues the C call (on the current stream), for loops that repeat a
+collective on persistent buffers.
 """
 from __future__ import annotations
 
 import ctypes
 import os
+import threading
 from typing import Sequence
 
 import torch
@@ -179,9 +184,60 @@ def rank_arena(groups, device="cuda"):
     return out
 
 
+# ----------------------------------------------------------- prepared calls
+
+_PLANNING = threading.local()
+
+
+class Plan:
+    """A library call validated and marshalled once: calling it re-issues the
+    same entry point with the same buffers on a stream (default: the current
+    one).  The plan holds references to every argument it was made from
+    (tensors included), so its device pointers stay valid for its lifetime;
+    the caller must not resize or re-point those tensors."""
+
+    __slots__ = ("_fn", "_args", "_what", "_keep")
+
+    def __init__(self, fn, args, what):
+        self._fn, self._args, self._what = fn, args, what
+        self._keep = None
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)), self._what)
+
+
+def _issue(name: str, what: str, stream, *args):
+    """Call entry point `name` with the marshalled `args` and the stream, or,
+    inside prepare(), return them as a Plan (which keeps the ctypes pointer
+    tables alive)."""
+    fn = getattr(lib(), name)
+    if getattr(_PLANNING, "on", False):
+        return Plan(fn, args, what)
+    _check(fn(*args, _stream(stream)), what)
+    return None
+
+
+def prepare(call, *args, **kwargs) -> Plan:
+    """Validate and marshal `call(*args, **kwargs)` (any collective of this
+    module) once and return a Plan that only re-issues the C call.  For loops
+    that repeat one collective on persistent buffers, where the per-call
+    argument checks would otherwise dominate small messages."""
+    _PLANNING.on = True
+    try:
+        plan = call(*args, **kwargs)
+    finally:
+        _PLANNING.on = False
+    if not isinstance(plan, Plan):
+        raise TypeError(f"{getattr(call, '__name__', call)} cannot be prepared")
+    # the plan owns what its pointers came from: a device tensor made inline
+    # for the call (e.g. a count table) must not be freed and reused
+    plan._keep = (call, args, kwargs)
+    return plan
+
+
 # --------------------------------------------------------------------- API
 
-def allreduce(sends, recvs, op: str = "sum", stream=None) -> None:
+def allreduce(sends, recvs, op: str = "sum", stream=None):
     """AllReduce: every recvs[r] gets the reduction of all sends (recvs may be sends)."""
     R = _ranks(sends, "allreduce")
     n = sends[0].numel()
@@ -189,32 +245,31 @@ def allreduce(sends, recvs, op: str = "sum", stream=None) -> None:
     _same(recvs, sends[0].dtype, n, "allreduce recv")
     if len(recvs) != R:
         raise ValueError("allreduce: one recv per rank")
-    _check(lib().coll_allreduce(R, _table(sends, "send"), _table(recvs, "recv"), n,
-                                _reduce_dtype(sends[0]), OPS[op], _stream(stream)), "allreduce")
+    return _issue("coll_allreduce", "allreduce", stream, R, _table(sends, "send"),
+                  _table(recvs, "recv"), n, _reduce_dtype(sends[0]), OPS[op])
 
 
-def reduce_scatter(sends, recvs, op: str = "sum", stream=None) -> None:
+def reduce_scatter(sends, recvs, op: str = "sum", stream=None):
     """ReduceScatter: recvs[r] = chunk r of the reduction (sends hold R chunks)."""
     R = _ranks(sends, "reduce_scatter")
     n = recvs[0].numel()
     _same(sends, sends[0].dtype, R * n, "reduce_scatter send")
     _same(recvs, sends[0].dtype, n, "reduce_scatter recv")
-    _check(lib().coll_reduce_scatter(R, _table(sends, "send"), _table(recvs, "recv"), n,
-                                     _reduce_dtype(sends[0]), OPS[op], _stream(stream)),
-           "reduce_scatter")
+    return _issue("coll_reduce_scatter", "reduce_scatter", stream, R, _table(sends, "send"),
+                  _table(recvs, "recv"), n, _reduce_dtype(sends[0]), OPS[op])
 
 
-def reduce(sends, recv_root, root: int, op: str = "sum", stream=None) -> None:
+def reduce(sends, recv_root, root: int, op: str = "sum", stream=None):
     """Reduce: recv_root = reduction of all sends (recv_root may be sends[root])."""
     R = _ranks(sends, "reduce")
     n = sends[0].numel()
     _same(sends, sends[0].dtype, n, "reduce send")
     _same([recv_root], sends[0].dtype, n, "reduce recv")
-    _check(lib().coll_reduce(R, _table(sends, "send"), _dev(recv_root, "recv"), root, n,
-                             _reduce_dtype(sends[0]), OPS[op], _stream(stream)), "reduce")
+    return _issue("coll_reduce", "reduce", stream, R, _table(sends, "send"),
+                  _dev(recv_root, "recv"), root, n, _reduce_dtype(sends[0]), OPS[op])
 
 
-def scatter(send_root, recvs, root: int, stream=None) -> None:
+def scatter(send_root, recvs, root: int, stream=None):
     """Scatter: recvs[r] = chunk r of send_root (R equal chunks)."""
     R = _ranks(recvs, "scatter")
     n = recvs[0].numel()
@@ -222,22 +277,22 @@ def scatter(send_root, recvs, root: int, stream=None) -> None:
     if send_root.numel() != R * n:
         raise ValueError("scatter: the root buffer must hold R chunks")
     dt, mult = _copy_dtype(send_root)
-    _check(lib().coll_scatter(R, _dev(send_root, "send"), _table(recvs, "recv"), root,
-                              n * mult, dt, _stream(stream)), "scatter")
+    return _issue("coll_scatter", "scatter", stream, R, _dev(send_root, "send"),
+                  _table(recvs, "recv"), root, n * mult, dt)
 
 
-def all_gather(sends, recvs, stream=None) -> None:
+def all_gather(sends, recvs, stream=None):
     """AllGather: recvs[r] = concatenation of sends in rank order."""
     R = _ranks(sends, "all_gather")
     n = sends[0].numel()
     _same(sends, sends[0].dtype, n, "all_gather send")
     _same(recvs, sends[0].dtype, R * n, "all_gather recv")
     dt, mult = _copy_dtype(sends[0])
-    _check(lib().coll_all_gather(R, _table(sends, "send"), _table(recvs, "recv"), n * mult, dt,
-                                 _stream(stream)), "all_gather")
+    return _issue("coll_all_gather", "all_gather", stream, R, _table(sends, "send"),
+                  _table(recvs, "recv"), n * mult, dt)
 
 
-def gather(sends, recv_root, root: int = 0, stream=None) -> None:
+def gather(sends, recv_root, root: int = 0, stream=None):
     """Gather: sends[q] of shape [outer, inner] concatenated along the last
     axis into recv_root [outer, R*inner]; only the root's buffer is written."""
     R = _ranks(sends, "gather")
@@ -248,22 +303,22 @@ def gather(sends, recv_root, root: int = 0, stream=None) -> None:
     if recv_root.dtype != s0.dtype or recv_root.numel() != outer * R * inner:
         raise ValueError("gather: root buffer must be [outer, R*inner] of the send dtype")
     dt, mult = _copy_dtype(s0)
-    _check(lib().coll_gather(R, _table(sends, "send"), _dev(recv_root, "recv"), root, outer,
-                             inner * mult, dt, _stream(stream)), "gather")
+    return _issue("coll_gather", "gather", stream, R, _table(sends, "send"),
+                  _dev(recv_root, "recv"), root, outer, inner * mult, dt)
 
 
-def broadcast(send_root, recvs, root: int, stream=None) -> None:
+def broadcast(send_root, recvs, root: int, stream=None):
     """Broadcast: every recvs[r] = send_root (recvs[root] may be send_root)."""
     R = _ranks(recvs, "broadcast")
     n = send_root.numel()
     _same(recvs, send_root.dtype, n, "broadcast recv")
     dt, mult = _copy_dtype(send_root)
-    _check(lib().coll_broadcast(R, _dev(send_root, "send"), _table(recvs, "recv"), root,
-                                n * mult, dt, _stream(stream)), "broadcast")
+    return _issue("coll_broadcast", "broadcast", stream, R, _dev(send_root, "send"),
+                  _table(recvs, "recv"), root, n * mult, dt)
 
 
 def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
-                 stream=None) -> None:
+                 stream=None):
     """All-to-All-v with device int64 [R*R] counts (s-major), sdispls (s-major)
     and rdispls (d-major), in rows of ``row_elems`` elements."""
     R = _ranks(sends, "all_to_all_v")
@@ -278,13 +333,12 @@ def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
             raise ValueError("all_to_all_v: one dtype for every buffer")
     # receive capacity in rows: an upper bound of the rows moved (sizes the launch)
     capacity = sum(t.numel() // row_elems for t in recvs)
-    _check(lib().coll_all_to_all_v(R, _table(sends, "send"), _dev(sendcounts, "counts"),
-                                   _dev(sdispls, "sdispls"), _table(recvs, "recv"),
-                                   _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity,
-                                   _stream(stream)), "all_to_all_v")
+    return _issue("coll_all_to_all_v", "all_to_all_v", stream, R, _table(sends, "send"),
+                  _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"), _table(recvs, "recv"),
+                  _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity)
 
 
-def all_to_all(sends, recvs, stream=None) -> None:
+def all_to_all(sends, recvs, stream=None):
     """all_to_all_single with equal splits: recvs[d][s*n+i] = sends[s][d*n+i]."""
     R = _ranks(sends, "all_to_all")
     total = sends[0].numel()
@@ -293,12 +347,12 @@ def all_to_all(sends, recvs, stream=None) -> None:
     _same(sends, sends[0].dtype, total, "all_to_all send")
     _same(recvs, sends[0].dtype, total, "all_to_all recv")
     dt, mult = _copy_dtype(sends[0])
-    _check(lib().coll_all_to_all(R, _table(sends, "send"), _table(recvs, "recv"),
-                                 total // R * mult, dt, _stream(stream)), "all_to_all")
+    return _issue("coll_all_to_all", "all_to_all", stream, R, _table(sends, "send"),
+                  _table(recvs, "recv"), total // R * mult, dt)
 
 
 def seq_heads_reshard(ins, outs, heads: int, head_dim: int, to_heads: bool,
-                      stream=None) -> None:
+                      stream=None):
     """[SL, H, D] per rank <-> [R*SL, H/R, D] per rank (to_heads selects the
     direction)."""
     R = _ranks(ins, "seq_heads_reshard")
@@ -309,12 +363,11 @@ def seq_heads_reshard(ins, outs, heads: int, head_dim: int, to_heads: bool,
     _same(ins, ins[0].dtype, per, "seq_heads_reshard in")
     _same(outs, ins[0].dtype, per, "seq_heads_reshard out")
     dt, mult = _copy_dtype(ins[0])
-    _check(lib().coll_seq_heads_reshard(R, _table(ins, "in"), _table(outs, "out"), SL, heads,
-                                        head_dim * mult, dt, 1 if to_heads else 0,
-                                        _stream(stream)), "seq_heads_reshard")
+    return _issue("coll_seq_heads_reshard", "seq_heads_reshard", stream, R, _table(ins, "in"),
+                  _table(outs, "out"), SL, heads, head_dim * mult, dt, 1 if to_heads else 0)
 
 
-def lse_merge(o_parts, lse_parts, o_out, lse_out=None, stream=None) -> None:
+def lse_merge(o_parts, lse_parts, o_out, lse_out=None, stream=None):
     """Context-parallel merge: o_parts[r] [rows, D] (bf16/fp32) with fp32
     lse_parts[r] [rows] -> o_out[r] (and lse_out[r]) on every rank."""
     R = _ranks(o_parts, "lse_merge")
@@ -330,9 +383,8 @@ def lse_merge(o_parts, lse_parts, o_out, lse_out=None, stream=None) -> None:
     if lse_out is not None:
         _same(lse_out, torch.float32, rows, "lse_merge lse_out")
         lo = _table(lse_out, "lse_out")
-    _check(lib().coll_lse_merge(R, _table(o_parts, "o"), _table(lse_parts, "lse"),
-                                _table(o_out, "out"), lo, rows, D, dt, _stream(stream)),
-           "lse_merge")
+    return _issue("coll_lse_merge", "lse_merge", stream, R, _table(o_parts, "o"),
+                  _table(lse_parts, "lse"), _table(o_out, "out"), lo, rows, D, dt)
 
 
 def moe_workspace_bytes(R: int, tokens: int, topk: int, n_experts: int) -> int:
@@ -340,7 +392,7 @@ def moe_workspace_bytes(R: int, tokens: int, topk: int, n_experts: int) -> int:
 
 
 def moe_layout(topk_ids, n_experts: int, sendcounts, sdispls, rdispls, expert_counts, pos,
-               workspace, stream=None) -> None:
+               workspace, stream=None):
     """MoE layout from int32 [T, K] ids per rank into device count tables and
     int32 [T, K] send-slot positions."""
     R = _ranks(topk_ids, "moe_layout")
@@ -357,14 +409,12 @@ def moe_layout(topk_ids, n_experts: int, sendcounts, sdispls, rdispls, expert_co
     if expert_counts.dtype != torch.int32 or expert_counts.numel() != R * n_experts:
         raise ValueError("moe_layout: expert_counts is int32 [R*E]")
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().coll_moe_layout(R, _table(topk_ids, "ids"), T, K, n_experts,
-                                 _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
-                                 _dev(rdispls, "rd"), _dev(expert_counts, "ec"),
-                                 _table(pos, "pos"), _dev(workspace, "ws"), ws_bytes,
-                                 _stream(stream)), "moe_layout")
+    return _issue("coll_moe_layout", "moe_layout", stream, R, _table(topk_ids, "ids"), T, K,
+                  n_experts, _dev(sendcounts, "sc"), _dev(sdispls, "sd"), _dev(rdispls, "rd"),
+                  _dev(expert_counts, "ec"), _table(pos, "pos"), _dev(workspace, "ws"), ws_bytes)
 
 
-def moe_permute(xs, pos, sends, stream=None) -> None:
+def moe_permute(xs, pos, sends, stream=None):
     """sends[s][pos[s][t,k]] = xs[s][t] (x [T, H], sends [T*K, H])."""
     R = _ranks(xs, "moe_permute")
     T, H = xs[0].shape
@@ -376,24 +426,24 @@ def moe_permute(xs, pos, sends, stream=None) -> None:
         if s.numel() != T * K * H or s.dtype != xs[0].dtype:
             raise ValueError("moe_permute: send buffers must be [T*K, H]")
     dt, mult = _copy_dtype(xs[0])
-    _check(lib().coll_moe_permute(R, _table(xs, "x"), _table(pos, "pos"), T, K, H * mult, dt,
-                                  _table(sends, "send"), _stream(stream)), "moe_permute")
+    return _issue("coll_moe_permute", "moe_permute", stream, R, _table(xs, "x"),
+                  _table(pos, "pos"), T, K, H * mult, dt, _table(sends, "send"))
 
 
 def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
-                     stream=None) -> None:
+                     stream=None):
     """Test expert y = rne(x * (1 + e/256)) in place on received bf16 rows."""
     R = _ranks(recvs, "moe_expert_scale")
     for r in recvs:
         if r.dtype != torch.bfloat16:
             raise ValueError("moe_expert_scale: bf16 rows only")
     capacity = sum(t.numel() // hidden for t in recvs)
-    _check(lib().coll_moe_expert_scale(R, _table(recvs, "recv"), _dev(expert_counts, "ec"),
-                                       _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
-                                       capacity, _stream(stream)), "moe_expert_scale")
+    return _issue("coll_moe_expert_scale", "moe_expert_scale", stream, R, _table(recvs, "recv"),
+                  _dev(expert_counts, "ec"), _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
+                  capacity)
 
 
-def moe_combine(backs, pos, weights, outs, stream=None) -> None:
+def moe_combine(backs, pos, weights, outs, stream=None):
     """outs[s][t] = rne(sum_k w[s][t,k] * backs[s][pos[s][t,k]]), k ascending."""
     R = _ranks(backs, "moe_combine")
     T, K = pos[0].shape
@@ -407,9 +457,9 @@ def moe_combine(backs, pos, weights, outs, stream=None) -> None:
     for o in outs:
         if o.dtype != torch.bfloat16 or o.numel() != T * H:
             raise ValueError("moe_combine: outputs are bf16 [T, H]")
-    _check(lib().coll_moe_combine(R, _table(backs, "back"), _table(pos, "pos"),
-                                  _table(weights, "w"), T, K, H, COLL_BF16, _table(outs, "out"),
-                                  _stream(stream)), "moe_combine")
+    return _issue("coll_moe_combine", "moe_combine", stream, R, _table(backs, "back"),
+                  _table(pos, "pos"), _table(weights, "w"), T, K, H, COLL_BF16,
+                  _table(outs, "out"))
 
 
 def _layout_tables(R, tables, what):
@@ -418,7 +468,7 @@ def _layout_tables(R, tables, what):
             raise ValueError(f"{what}: {name} must be int64 [R*R] on the device")
 
 
-def moe_dispatch(xs, pos, sendcounts, sdispls, rdispls, recvs, stream=None) -> None:
+def moe_dispatch(xs, pos, sendcounts, sdispls, rdispls, recvs, stream=None):
     """Fused permute + All-to-All-v: every (t, k) row of xs[s] goes straight
     to its receive row in recvs[d] (the layout of moe_layout)."""
     R = _ranks(xs, "moe_dispatch")
@@ -434,14 +484,13 @@ def moe_dispatch(xs, pos, sendcounts, sdispls, rdispls, recvs, stream=None) -> N
         if r.dtype != xs[0].dtype or r.numel() % max(H, 1) != 0:
             raise ValueError("moe_dispatch: receive buffers are [rows, H] of x's dtype")
     dt, mult = _copy_dtype(xs[0])
-    _check(lib().coll_moe_dispatch(R, _table(xs, "x"), _table(pos, "pos"),
-                                   _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
-                                   _dev(rdispls, "rd"), T, K, H * mult, dt,
-                                   _table(recvs, "recv"), _stream(stream)), "moe_dispatch")
+    return _issue("coll_moe_dispatch", "moe_dispatch", stream, R, _table(xs, "x"),
+                  _table(pos, "pos"), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
+                  _dev(rdispls, "rd"), T, K, H * mult, dt, _table(recvs, "recv"))
 
 
 def moe_combine_recv(recvs, pos, sendcounts, sdispls, rdispls, weights, outs, topk_ids=None,
-                     stream=None) -> None:
+                     stream=None):
     """Fused reverse exchange + combine: outs[s][t] = rne(sum_k w * row_k), row_k
     read from the receive buffers where moe_dispatch put it; with topk_ids the
     test expert rne(x * (1 + e/256)) is applied to each row as it is read."""
@@ -464,8 +513,7 @@ def moe_combine_recv(recvs, pos, sendcounts, sdispls, rdispls, weights, outs, to
             if t.dtype != torch.int32 or t.numel() != T * K:
                 raise ValueError("moe_combine_recv: topk_ids are int32 [T, K]")
         ids = _table(topk_ids, "ids")
-    _check(lib().coll_moe_combine_recv(R, _table(recvs, "recv"), _table(pos, "pos"),
-                                       _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
-                                       _dev(rdispls, "rd"), _table(weights, "w"), ids, T, K, H,
-                                       COLL_BF16, _table(outs, "out"), _stream(stream)),
-           "moe_combine_recv")
+    return _issue("coll_moe_combine_recv", "moe_combine_recv", stream, R, _table(recvs, "recv"),
+                  _table(pos, "pos"), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
+                  _dev(rdispls, "rd"), _table(weights, "w"), ids, T, K, H, COLL_BF16,
+                  _table(outs, "out"))

@@ -279,3 +279,31 @@ def test_fused_moe_entry_points_validate_on_host(L):
     assert cr(pos=NULL) == -1
     half = (ctypes.c_void_p * 2)(0x1000, 0)
     assert cr(ids=half) == -1                          # ids given: every rank needs them
+
+
+def test_prepare_rejects_a_non_collective():
+    with pytest.raises(TypeError):
+        coll.prepare(lambda: 3)
+
+
+def test_plan_keeps_the_arguments_it_was_made_from():
+    """A prepared call owns its arguments: tensors created inline for the call
+    (whose raw pointers the plan re-issues) stay alive with the plan."""
+    import gc
+    import weakref
+    import torch
+
+    fake = coll.Plan(lambda *a: 0, (), "fake")
+    t = torch.empty(4)
+    ref = weakref.ref(t)
+
+    def call(x):
+        return fake
+
+    plan = coll.prepare(call, t)
+    del t
+    gc.collect()
+    assert ref() is not None and plan is fake
+    del plan, fake
+    gc.collect()
+    assert ref() is None
