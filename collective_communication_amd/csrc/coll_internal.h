@@ -323,14 +323,16 @@ struct Launch {
   int num_cus;       // compute units of the current device
   int wgs_per_cu;    // workgroups per CU for persistent (device-sized) kernels
   size_t nt_bytes;   // bytes moved at or above which loads/stores are non-temporal
+  size_t nt_store_bytes;  // ReduceScatter / Reduce: bytes written at or above which
+                          // their stores are non-temporal too
   int a2a_nt;        // non-temporal loads/stores in All-to-All-v (size unknown on the host)
   long a2a_grid;     // > 0: All-to-All-v launches this many workgroups (tuning)
   long ar_grid;      // > 0: AllReduce launches this many workgroups (tuning)
 };
 
 // Device properties and tuning knobs (environment, read once per process:
-// COLL_WGS_PER_CU,
-// COLL_NT_MIN_BYTES, COLL_A2A_NT, COLL_A2A_GRID, COLL_AR_GRID).
+// COLL_WGS_PER_CU, COLL_NT_MIN_BYTES, COLL_NT_STORE_MIN_BYTES, COLL_A2A_NT,
+// COLL_A2A_GRID, COLL_AR_GRID).
 Launch launch_ctx(void *stream);
 
 // One workgroup per tile of kBlock * per_thread units (single pass), capped

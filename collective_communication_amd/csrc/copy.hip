@@ -19,7 +19,13 @@ namespace {
 // to every rank's slot q; a rank whose slot q IS the source (the in-place form
 // send[q] == recv[q] + q*n) is skipped, so in place costs R-1 stores.
 // AllGather tile: one wave, one 16-byte unit per lane (1 load, R stores);
-// measured 3-4% above 256 lanes x 4 units at R = 8, 8 MiB shards (MI355X)
+// measured 3-4% above 256 lanes x 4 units at R = 8, 8 MiB shards (MI355X).
+// The shard loads are always temporal (cacheable): each shard is read once
+// and often was just written by the producer (a ReduceScatter), so it may
+// still be in the Infinity Cache.  On MI355X at R = 8 they beat non-temporal
+// loads both there (120 -> 114 us with 8 MiB shards) and cold (64 MiB shards,
+// non-temporal stores: 890 vs 915 us); the R-fold stores stay non-temporal
+// for large calls.
 #ifndef COLL_AG_BLOCK
 #define COLL_AG_BLOCK 64
 #endif
@@ -42,7 +48,7 @@ __global__ __launch_bounds__(kAgBlock) void ag_kernel(RankPtrs p, int R, size_t 
 #pragma unroll
     for (int u = 0; u < UN; u++) {
       const size_t i = base + (size_t)u * kAgBlock;
-      if (i < nunits) v[u] = ld<U, NT>(src, i);
+      if (i < nunits) v[u] = ld<U, false>(src, i);
     }
     for (int r = 0; r < R; r++) {
       U *dst = reinterpret_cast<U *>(p.out[r]) + (size_t)q * nunits;
