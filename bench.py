@@ -110,6 +110,7 @@ def make_inputs(torch, synth, coll):
     W["ec"] = torch.empty(R * E, dtype=torch.int32, device="cuda")
     W["pos"] = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(R)]
     W["ws"] = torch.empty(coll.moe_workspace_bytes(R, T, K, E), dtype=torch.uint8, device="cuda")
+    W["ews"] = torch.empty(coll.moe_expert_workspace_bytes(R, E), dtype=torch.uint8, device="cuda")
     # the routing is fixed, so the receive sizes are known once (outside timing)
     coll.moe_layout(ids, E, W["sc"], W["sd"], W["rd"], W["ec"], W["pos"], W["ws"])
     torch.cuda.synchronize()
@@ -172,7 +173,7 @@ def step_rows(W, coll, torch):
         ("moe_permute", lambda: coll.moe_permute(W["moe_x"], W["pos"], W["send"])),
         ("a2av_dispatch", lambda: coll.all_to_all_v(W["send"], W["sc"], W["sd"], W["recv"],
                                                     W["rd"], H)),
-        ("moe_expert", lambda: coll.moe_expert_scale(W["recv"], W["ec"], W["rd"], E, H)),
+        ("moe_expert", lambda: coll.moe_expert_scale(W["recv"], W["ec"], W["rd"], E, H, W["ews"])),
         ("a2av_combine", lambda: coll.all_to_all_v(W["recv"], W["sc_t"], W["rd"], W["back"],
                                                    W["sd"], H)),
         ("moe_combine", lambda: coll.moe_combine(W["back"], W["pos"], W["moe_w"], W["out"])),

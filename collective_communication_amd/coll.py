@@ -51,7 +51,8 @@ SIGNATURES = {
     "coll_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "coll_moe_layout": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
-    "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp]),
+    "coll_moe_expert_workspace_bytes": (_sz, [_i, _i]),
+    "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _sz, _vp]),
     "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_dispatch": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_combine_recv": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp,
@@ -430,17 +431,24 @@ def moe_permute(xs, pos, sends, stream=None):
                   _table(pos, "pos"), T, K, H * mult, dt, _table(sends, "send"))
 
 
-def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
+def moe_expert_workspace_bytes(R: int, n_experts: int) -> int:
+    return int(lib().coll_moe_expert_workspace_bytes(R, n_experts))
+
+
+def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int, workspace,
                      stream=None):
-    """Test expert y = rne(x * (1 + e/256)) in place on received bf16 rows."""
+    """Test expert y = rne(x * (1 + e/256)) in place on received bf16 rows.
+    ``workspace``: a device tensor of at least moe_expert_workspace_bytes(R, E)
+    bytes (the layout's workspace may be reused once the layout is done)."""
     R = _ranks(recvs, "moe_expert_scale")
     for r in recvs:
         if r.dtype != torch.bfloat16:
             raise ValueError("moe_expert_scale: bf16 rows only")
-    capacity = sum(t.numel() // hidden for t in recvs)
+    capacity = sum(t.numel() // hidden for t in recvs) if hidden > 0 else 0
+    ws_bytes = workspace.numel() * workspace.element_size()
     return _issue("coll_moe_expert_scale", "moe_expert_scale", stream, R, _table(recvs, "recv"),
                   _dev(expert_counts, "ec"), _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
-                  capacity)
+                  capacity, _dev(workspace, "ws"), ws_bytes)
 
 
 def moe_combine(backs, pos, weights, outs, stream=None):

@@ -341,19 +341,28 @@ int coll_moe_permute(int R, const void *const *x, const int32_t *const *pos, int
                             hidden * dtype_size(dtype), ss);
 }
 
+size_t coll_moe_expert_workspace_bytes(int R, int n_experts) {
+  if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0) return 0;
+  return moe_expert_workspace_bytes(R, n_experts);
+}
+
 int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
-                          coll_dtype_t dtype, size_t recv_rows_capacity, void *stream) {
+                          coll_dtype_t dtype, size_t recv_rows_capacity, void *workspace,
+                          size_t workspace_bytes, void *stream) {
   if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0)
     return COLL_ERR_INVALID_ARG;
   if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
   if (hidden == 0) return COLL_OK;
   if (!expert_counts || !rdispls || hidden >= ((size_t)1 << 31)) return COLL_ERR_INVALID_ARG;
+  if (!workspace || ((uintptr_t)workspace & 255) != 0 ||
+      workspace_bytes < moe_expert_workspace_bytes(R, n_experts))
+    return COLL_ERR_INVALID_ARG;
   MutPtrTable rs{};
   if (!fill_out(R, recvbufs, rs.p)) return COLL_ERR_INVALID_ARG;
   if (recv_rows_capacity > ((size_t)1 << 48) / hidden) return COLL_ERR_INVALID_ARG;
   return launch_moe_expert_scale(launch_ctx(stream), R, rs, expert_counts, rdispls, n_experts,
-                                 hidden, recv_rows_capacity);
+                                 hidden, recv_rows_capacity, workspace);
 }
 
 int coll_moe_combine(int R, const void *const *back, const int32_t *const *pos,

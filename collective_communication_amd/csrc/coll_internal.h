@@ -401,6 +401,7 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
 
 constexpr int kMoeMaxExperts = 1024;
 size_t moe_workspace_bytes(int R, int T, int K, int E);
+size_t moe_expert_workspace_bytes(int R, int E);
 int launch_moe_layout(const Launch &L, int R, const PtrTable &ids, int T, int K, int E,
                       int64_t *sendcounts, int64_t *sdispls, int64_t *rdispls,
                       int32_t *expert_counts, const MutPtrTable &pos, void *ws);
@@ -408,7 +409,7 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
                        int K, size_t row_bytes, const MutPtrTable &send);
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
-                            size_t hidden, size_t rows_capacity);
+                            size_t hidden, size_t rows_capacity, void *ws);
 int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTable &pos,
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
 int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,

@@ -21,7 +21,8 @@
 //   moe_permute   send[s][pos[t,k]] = x[s][t]: each token row is read once and
 //                 written topk times, 16-byte units.
 //   moe_expert_scale  the harness's test expert y = rne(x * (1 + e/256)), in
-//                 place, one wave per received row.
+//                 place: a one-workgroup table of row prefixes, then one
+//                 workgroup per tile of received units.
 //   moe_combine   one wave per token: topk rows gathered by pos, fp32
 //                 fold k = 0..K-1 of separately rounded products, one RNE.
 #include "coll_internal.h"
@@ -38,6 +39,9 @@ constexpr int kMoeTile = 1024;        // ids per layout tile (kBlock * 4)
 #ifndef COLL_PERMUTE_U
 #define COLL_PERMUTE_U 1
 #endif
+// test expert, one-pass tiles of 256 lanes x U units; MI355X, the 3.5 GiB
+// in-place MoE shape: U = 2 -> 1655 us, 4 -> 1338, 8 -> 1284, 16 -> 1288 (the
+// resident grid it replaced: 1345)
 #ifndef COLL_EXPERT_U
 #define COLL_EXPERT_U 8
 #endif
@@ -48,6 +52,10 @@ constexpr int kPermuteU = COLL_PERMUTE_U;     // 16-byte units per lane, permute
 constexpr int kExpertU = COLL_EXPERT_U;       // ... test expert
 constexpr int kCombineU = COLL_COMBINE_U;     // ... combine (each gathers K rows)
 constexpr int kMaxExperts = kMoeMaxExperts;
+
+size_t moe_expert_workspace_bytes(int R, int E) {
+  return ((size_t)R * E * 2 * sizeof(int64_t) + 255) & ~(size_t)255;
+}
 
 size_t moe_workspace_bytes(int R, int T, int K, int E) {
   size_t tk = (size_t)T * K;
@@ -268,111 +276,155 @@ __global__ __launch_bounds__(kBlock) void moe_permute_kernel(PtrTable x, PtrTabl
 
 // ------------------------------------------------------------- test expert
 
-// Receive-order entry table shared by every destination: entry
-// j = d*E + s*per + el covers the rows of expert d*per + el sent by s to d.
-// s_end[j] = inclusive prefix of the row counts over all entries, so one
-// global row index addresses every received row of every rank, and the work
-// is balanced over ranks however skewed the routing is.
-
-// G = bf16 elements per unit (8: 16-byte vectors; 1: scalar fallback)
-template <int G, bool NT>
-__global__ __launch_bounds__(kBlock) void moe_expert_scale_kernel(MutPtrTable recv, int R, int E,
-                                                                  const int32_t *expert_counts,
-                                                                  const int64_t *rdispls,
-                                                                  FastDiv64 upr) {
-  HIP_DYNAMIC_SHARED(uint32_t, s_end);          // R * E entries (launch-time size)
-  __shared__ uint32_t wsum[kBlock / 64];
+// Receive-order entries: entry j = d*E + s*per + el (per = E/R) covers the
+// rows of expert d*per + el sent by s to d, expert_counts[s*E + d*per + el]
+// of them.  Numbering every received row of every rank in entry order (global
+// row g) balances the work over ranks however skewed the routing is.
+//
+// moe_expert_table: one 1024-thread workgroup writes two int64 tables:
+//   s_end[j] = rows in entries 0..j (inclusive prefix), so g is in entry j
+//              iff s_end[j-1] <= g < s_end[j];
+//   rb[j]    = rdispls[d*R+s] - (rows in entries before (d, s)'s first),
+//              so the receive row of g in recv[d] is rb[j] + g.
+__global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_counts,
+                                                         const int64_t *rdispls, int R, int E,
+                                                         int64_t *s_end, int64_t *rb) {
+  __shared__ int64_t wsum[16];
+  __shared__ int64_t first_end[COLL_MAX_RANKS * COLL_MAX_RANKS];   // rows before (d, s)
   const int per = E / R;
   const int N = R * E;
-  // block-wide scan: thread t owns a contiguous chunk of entries
-  const int chunk = (N + kBlock - 1) / kBlock;
-  const int j0 = threadIdx.x * chunk;
-  uint32_t local = 0;
-  for (int c = 0; c < chunk; c++) {
-    const int j = j0 + c;
-    if (j < N) {
-      const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
-      local += (uint32_t)expert_counts[(size_t)s * E + d * per + el];
-    }
-  }
+  const int chunk = (N + 1023) / 1024;           // <= 16 (R <= 16, E <= 1024)
+  const int j0 = (int)threadIdx.x * chunk;
+  auto count_of = [&](int j) -> int64_t {
+    const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
+    return (int64_t)expert_counts[(size_t)s * E + d * per + el];
+  };
+  int64_t local = 0;
+  for (int c = 0; c < chunk; c++)
+    if (j0 + c < N) local += count_of(j0 + c);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t incl = (uint32_t)wave_incl_scan_i32((int)local);
+  int64_t incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  uint32_t before = 0;
-  for (int q = 0; q < w; q++) before += wsum[q];
-  uint32_t run = before + incl - local;
+  int64_t run = incl - local;
+  for (int q = 0; q < w; q++) run += wsum[q];
   for (int c = 0; c < chunk; c++) {
     const int j = j0 + c;
-    if (j < N) {
-      const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
-      run += (uint32_t)expert_counts[(size_t)s * E + d * per + el];
-      s_end[j] = run;
-    }
+    if (j >= N) break;
+    const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
+    if (el == 0) first_end[d * R + s] = run;
+    run += count_of(j);
+    s_end[j] = run;
   }
   __syncthreads();
+  for (int c = 0; c < chunk; c++) {
+    const int j = j0 + c;
+    if (j >= N) break;
+    const int d = j / E, s = (j - d * E) / per;
+    rb[j] = rdispls[d * R + s] - first_end[d * R + s];
+  }
+}
 
-  const uint64_t nrows = s_end[N - 1];
-  const uint64_t total = nrows * upr.d;
-  int top = 1;
-  while (top * 2 <= N) top *= 2;
-  // the current entry, decoded once: global rows [glo, ghi) of rank d at
-  // receive row rbase + g, scaled by `scale`
-  uint64_t glo = 1, ghi = 0;
-  int64_t rbase = 0;
-  float scale = 1.0f;
-  void *y = nullptr;
+// moe_expert_scale_kernel: one workgroup per tile of kBlock * UN units (G bf16
+// elements each: 8 = 16-byte vectors, 1 = scalar fallback), looping when the
+// grid is smaller than the work.  Each wave finds the entries of the tile's
+// first and last rows with two 64-way searches over s_end, interleaved, one
+// ballot per level (log64(N) levels).  The last level also loads each probed
+// entry's bounds and receive base, so the winner's come from a lane shuffle:
+// two dependent L2 round trips before the data loads, the row total loading
+// beside the first.  A unit whose row is past the first entry bisects between
+// the two.  Every unit of the tile is located, then all loads issue, then the
+// scaled values are stored.
+template <int G, bool NT>
+__global__ __launch_bounds__(kBlock) void moe_expert_scale_kernel(MutPtrTable recv, int R, int E,
+                                                                  const int64_t *s_end,
+                                                                  const int64_t *rb, int top,
+                                                                  FastDiv64 upr) {
+  using U = typename std::conditional<G == 8, u32x4, uint16_t>::type;
   constexpr int UN = kExpertU;
+  const int per = E / R;
+  const int N = R * E;
+  const int lane = threadIdx.x & 63;
+  const int64_t nrows = s_end[N - 1];
   const uint64_t tile = (uint64_t)kBlock * UN;
-  for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
-       base += (uint64_t)gridDim.x * tile) {
-    u32x4 v[UN];
-    uint64_t at[UN];
+  for (uint64_t t0 = (uint64_t)blockIdx.x * tile;; t0 += (uint64_t)gridDim.x * tile) {
+    // lo(g) = number of entries with s_end <= g = the entry holding row g;
+    // rows past the total search to N and are never used
+    const int64_t g_first = (int64_t)fdiv64(t0, upr);
+    const int64_t g_last = (int64_t)fdiv64(t0 + tile - 1, upr);
+    int lo_f = 0, lo_l = 0;
+    for (int stride = top; stride > 1; stride >>= 6) {
+      const int jf = lo_f + (lane + 1) * stride - 1;
+      const int jl = lo_l + (lane + 1) * stride - 1;
+      const bool inf = jf < N && s_end[jf] <= g_first;
+      const bool inl = jl < N && s_end[jl] <= g_last;
+      lo_f += (int)__popcll(__ballot(inf)) * stride;
+      lo_l += (int)__popcll(__ballot(inl)) * stride;
+    }
+    const int jf = lo_f + lane, jl = lo_l + lane;
+    const int64_t end_f = jf < N ? s_end[jf] : INT64_MAX;
+    const int64_t beg_f = jf < N ? (jf > 0 ? s_end[jf - 1] : 0) : 0;
+    const int64_t rb_f = jf < N ? rb[jf] : 0;
+    const bool inl = jl < N && s_end[jl] <= g_last;
+    const int cf = (int)__popcll(__ballot(end_f <= g_first));
+    lo_l += (int)__popcll(__ballot(inl));
+    if (t0 >= (uint64_t)nrows * upr.d) break;
+    lo_f += cf;                                   // < N: g_first is a real row
+    if (lo_l > N - 1) lo_l = N - 1;
+    // the lane's current entry, decoded once: rows [glo, ghi), receive row
+    // rbase + g of rank d, scaled by `scale`
+    int cur = lo_f;
+    int64_t glo = __shfl(beg_f, cf, 64), ghi = __shfl(end_f, cf, 64), rbase = __shfl(rb_f, cf, 64);
+    int d = cur / E;
+    float scale = 1.0f + (float)(d * per + (cur - d * E) % per) / 256.0f;
+    const uint64_t total = (uint64_t)nrows * upr.d;
+    U *at[UN];
     float sc[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t x = base + (uint64_t)u * kBlock;
+      const uint64_t x = t0 + threadIdx.x + (uint64_t)u * kBlock;
+      at[u] = nullptr;
       if (x >= total) continue;
-      const uint64_t g = fdiv64(x, upr);        // global row
+      const int64_t g = (int64_t)fdiv64(x, upr);
       if (g < glo || g >= ghi) {
-        int lo = 0;
-        for (int step = top; step > 0; step >>= 1) {
-          const int c = lo + step;
-          if (c <= N && s_end[c - 1] <= g) lo = c;
+        int a = lo_f, b = lo_l;                   // the entry is in [a, b]
+        while (a < b) {
+          const int m = (a + b) >> 1;
+          if (s_end[m] <= g) a = m + 1;
+          else b = m;
         }
-        const int d = lo / E, rem = lo - d * E, s = rem / per, el = rem - s * per;
-        const int first = d * E + s * per;     // first entry of (d, s)
-        const uint64_t gstart = first == 0 ? 0 : s_end[first - 1];
-        glo = lo > 0 ? s_end[lo - 1] : 0;
-        ghi = s_end[lo];
-        rbase = rdispls[d * R + s] - (int64_t)gstart;
-        scale = 1.0f + (float)(d * per + el) / 256.0f;
-        y = recv.p[d];
+        cur = a;
+        glo = cur > 0 ? s_end[cur - 1] : 0;
+        ghi = s_end[cur];
+        rbase = rb[cur];
+        d = cur / E;
+        scale = 1.0f + (float)(d * per + (cur - d * E) % per) / 256.0f;
       }
-      const uint64_t unit = x - g * upr.d;
-      at[u] = (uint64_t)(rbase + (int64_t)g) * upr.d + unit;
+      // receive unit = (rbase + g) * upr + (x - g * upr) = rbase * upr + x
+      at[u] = reinterpret_cast<U *>(recv.p[d]) + (int64_t)x + rbase * (int64_t)upr.d;
       sc[u] = scale;
-      if constexpr (G == 8) {
-        v[u] = ld<u32x4, NT>(y, at[u]);
-        at[u] = reinterpret_cast<uint64_t>(reinterpret_cast<u32x4 *>(y) + at[u]);
-      } else {
-        at[u] = reinterpret_cast<uint64_t>(reinterpret_cast<uint16_t *>(y) + at[u]);
-        v[u][0] = *reinterpret_cast<const uint16_t *>(at[u]);
-      }
     }
+    U v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++)
+      if (at[u]) v[u] = NT ? __builtin_nontemporal_load(at[u]) : *at[u];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t x = base + (uint64_t)u * kBlock;
-      if (x >= total) continue;
+      if (!at[u]) continue;
       if constexpr (G == 8) {
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; q++)
           o[q] = pack_bf16(bf16_lo(v[u][q]) * sc[u], bf16_hi(v[u][q]) * sc[u]);
-        st<u32x4, NT>(reinterpret_cast<void *>(at[u]), 0, o);
+        if constexpr (NT) __builtin_nontemporal_store(o, at[u]);
+        else *at[u] = o;
       } else {
-        *reinterpret_cast<uint16_t *>(at[u]) =
-            (uint16_t)(pack_bf16(bf16_lo(v[u][0]) * sc[u], 0.0f) & 0xFFFFu);
+        *at[u] = (uint16_t)(pack_bf16(bf16_lo((uint32_t)v[u]) * sc[u], 0.0f) & 0xFFFFu);
       }
     }
   }
@@ -710,25 +762,36 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
 
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
-                            size_t hidden, size_t rows_capacity) {
-  (void)rows_capacity;           // the resident grid: each workgroup builds the R*E table once
+                            size_t hidden, size_t rows_capacity, void *ws) {
+  const int N = R * E;
+  int64_t *s_end = reinterpret_cast<int64_t *>(ws);
+  int64_t *rb = s_end + N;
+  hipLaunchKernelGGL(moe_expert_table, dim3(1), dim3(1024), 0, L.stream, expert_counts, rdispls,
+                     R, E, s_end, rb);
+  int top = 1;
+  while (top * 64 < N) top *= 64;
   bool vec = (hidden % 8) == 0;
   for (int r = 0; r < R; r++) vec = vec && aligned16(recv.p[r]);
-  dim3 grid(grid_resident(L));
+  const size_t upr = vec ? hidden / 8 : hidden;
+  // one workgroup per tile of the capacity; with no capacity, a resident grid
+  // (the kernel loops over tiles either way)
+  const size_t tile = (size_t)kBlock * kExpertU;
+  const size_t cap_units = rows_capacity * upr;
+  size_t g = rows_capacity ? (cap_units + tile - 1) / tile : grid_resident(L);
+  if (g < 1) g = 1;
+  if (g > 0x7FFFFFFFu) g = 0x7FFFFFFFu;
+  const FastDiv64 f = make_fastdiv64(upr);
   const bool nt = L.a2a_nt != 0;
-  const size_t lds = (size_t)R * E * sizeof(uint32_t);   // <= 64 KiB (R <= 16, E <= 1024)
   if (vec) {
-    const FastDiv64 f = make_fastdiv64(hidden / 8);
     if (nt)
-      hipLaunchKernelGGL((moe_expert_scale_kernel<8, true>), grid, dim3(kBlock), lds, L.stream,
-                         recv, R, E, expert_counts, rdispls, f);
+      hipLaunchKernelGGL((moe_expert_scale_kernel<8, true>), dim3((unsigned)g), dim3(kBlock), 0,
+                         L.stream, recv, R, E, s_end, rb, top, f);
     else
-      hipLaunchKernelGGL((moe_expert_scale_kernel<8, false>), grid, dim3(kBlock), lds, L.stream,
-                         recv, R, E, expert_counts, rdispls, f);
+      hipLaunchKernelGGL((moe_expert_scale_kernel<8, false>), dim3((unsigned)g), dim3(kBlock), 0,
+                         L.stream, recv, R, E, s_end, rb, top, f);
   } else {
-    const FastDiv64 f = make_fastdiv64(hidden);
-    hipLaunchKernelGGL((moe_expert_scale_kernel<1, false>), grid, dim3(kBlock), lds, L.stream,
-                       recv, R, E, expert_counts, rdispls, f);
+    hipLaunchKernelGGL((moe_expert_scale_kernel<1, false>), dim3((unsigned)g), dim3(kBlock), 0,
+                       L.stream, recv, R, E, s_end, rb, top, f);
   }
   return hip_status();
 }

@@ -283,18 +283,35 @@ int coll_moe_permute(int nranks, const void *const *x, const int32_t *const *pos
                      int tokens, int topk, size_t hidden, coll_dtype_t dtype,
                      void *const *sendbufs, void *stream);
 
+/* Bytes of device workspace coll_moe_expert_scale needs (0 on invalid sizes):
+ * two int64 tables of nranks * n_experts entries, rounded up to 256 bytes. */
+size_t coll_moe_expert_workspace_bytes(int nranks, int n_experts);
+
 /*
  * Test expert used to exercise the round trip: each received bf16 row of
  * expert e becomes y = rne(x * (1 + e/256)) in place (the fp32 product is
  * exact, so y is unique).  Row order in recvbufs[d] is: for s ascending,
  * starting at rdispls[d*R+s], the rows of d's experts in ascending expert
- * order, expert_counts[s*E+e] rows each.  recv_rows_capacity: as for
- * coll_all_to_all_v, an upper bound of the rows; it is not used by the
- * current kernel, which always runs a resident grid.
+ * order, expert_counts[s*E+e] rows each (expert_counts and rdispls: DEVICE
+ * arrays, the outputs of coll_moe_layout).
+ * workspace: DEVICE, 256-byte aligned, at least
+ * coll_moe_expert_workspace_bytes(nranks, n_experts) bytes; it is
+ * overwritten (a row-prefix table built on the device), so calls that may
+ * run concurrently need workspaces of their own.  The layout's workspace may
+ * be reused once coll_moe_layout has completed on the same stream.
+ * recv_rows_capacity: as for coll_all_to_all_v, an upper bound of the rows
+ * received by all ranks together; it only sizes the launch (one workgroup per
+ * tile of the bound, 0 = unknown: a resident grid) and never addresses
+ * memory, so a wrong bound costs time, not correctness.
+ * Errors: COLL_ERR_INVALID_ARG for a NULL or misaligned workspace, a smaller
+ * workspace_bytes, n_experts outside [1, 1024] or not a multiple of nranks,
+ * NULL tables or receive buffers; COLL_ERR_UNSUPPORTED for a dtype other
+ * than bf16.
  */
 int coll_moe_expert_scale(int nranks, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
-                          coll_dtype_t dtype, size_t recv_rows_capacity, void *stream);
+                          coll_dtype_t dtype, size_t recv_rows_capacity, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * Combine (results return to the token's owner and are gate-weighted):

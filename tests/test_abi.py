@@ -83,7 +83,7 @@ def test_dtype_and_op_rejected(L):
     assert L.coll_allreduce(2, NULL, NULL, 8, 7, 0, NULL) == -1
     assert L.coll_allreduce(2, NULL, NULL, 8, 0, 9, NULL) == -2
     assert L.coll_reduce_scatter(2, NULL, NULL, 8, 0, -1, NULL) == -2
-    assert L.coll_moe_expert_scale(2, NULL, NULL, NULL, 4, 8, 2, 0, NULL) == -2   # fp32
+    assert L.coll_moe_expert_scale(2, NULL, NULL, NULL, 4, 8, 2, 0, NULL, 0, NULL) == -2   # fp32
     assert L.coll_moe_combine(2, NULL, NULL, NULL, 4, 2, 8, 1, NULL, NULL) == -2
 
 
@@ -104,6 +104,28 @@ def test_moe_workspace_and_layout_validation(L):
     # misaligned workspace
     need = L.coll_moe_workspace_bytes(2, 10, 2, 4)
     assert L.coll_moe_layout(2, t, 10, 2, 4, 0x100, 0x200, 0x300, 0x400, t, 0x1008, need, NULL) == -1
+
+
+def test_moe_expert_workspace_validation(L):
+    # two int64 tables of R*E entries, rounded up to 256 bytes
+    assert L.coll_moe_expert_workspace_bytes(8, 256) == 8 * 256 * 16
+    assert L.coll_moe_expert_workspace_bytes(2, 4) == 256
+    assert L.coll_moe_expert_workspace_bytes(16, 1024) == 16 * 1024 * 16
+    assert L.coll_moe_expert_workspace_bytes(8, 250) == 0       # E % R != 0
+    assert L.coll_moe_expert_workspace_bytes(8, 2048) == 0      # E > 1024
+    assert L.coll_moe_expert_workspace_bytes(17, 17) == 0       # R > 16
+    t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    need = L.coll_moe_expert_workspace_bytes(2, 4)
+    # NULL, misaligned or too small workspace -> rejected before any launch
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, NULL, need, NULL) == -1
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, 0x1008, need, NULL) == -1
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, 0x1000, need - 1, NULL) == -1
+    # NULL receive buffer / tables
+    z = (ctypes.c_void_p * 2)(0x1000, None)
+    assert L.coll_moe_expert_scale(2, z, 0x100, 0x200, 4, 8, 0, 16, 0x1000, need, NULL) == -1
+    assert L.coll_moe_expert_scale(2, t, NULL, 0x200, 4, 8, 0, 16, 0x1000, need, NULL) == -1
+    # hidden 0: nothing to do, nothing launched
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 0, 0, 16, NULL, 0, NULL) == 0
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

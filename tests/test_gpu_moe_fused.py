@@ -96,7 +96,8 @@ def test_fused_moe_matches_unfused_oracle(R, E, T, K, H):
     # without topk_ids the combine uses the rows as they are: run the test
     # expert in place first and the outputs must not change
     recvs, pos, sc, sd, rd, ec, w_d, x_d = got["dev"]
-    coll.moe_expert_scale(recvs, ec, rd, E, H)
+    ews = torch.empty(coll.moe_expert_workspace_bytes(R, E), dtype=torch.uint8, device="cuda")
+    coll.moe_expert_scale(recvs, ec, rd, E, H, ews)
     outs = [poison_like(x) for x in x_d]
     coll.moe_combine_recv(recvs, pos, sc, sd, rd, w_d, outs)
     torch.cuda.synchronize()

@@ -370,7 +370,8 @@ def moe_gpu(xs, ids, ws, E):
     coll.all_to_all_v(sends, sc, sd, recvs, rd, H)
     torch.cuda.synchronize()
     recvs_h = [host(r).copy() for r in recvs]
-    coll.moe_expert_scale(recvs, ec, rd, E, H)
+    ews = torch.empty(coll.moe_expert_workspace_bytes(R, E), dtype=torch.uint8, device="cuda")
+    coll.moe_expert_scale(recvs, ec, rd, E, H, ews)
     torch.cuda.synchronize()
     ys_h = [host(r).copy() for r in recvs]
     sc_t = sc.view(R, R).t().contiguous().view(-1)
@@ -485,7 +486,7 @@ def moe_gpu_outputs_only(xs, ids, ws, E):
     recvs = [torch.empty((max(int(n), 1), H), dtype=torch.bfloat16, device="cuda")
              for n in sc_h.sum(axis=0)]
     coll.all_to_all_v(sends, sc, sd, recvs, rd, H)
-    coll.moe_expert_scale(recvs, ec, rd, E, H)
+    coll.moe_expert_scale(recvs, ec, rd, E, H, work)       # the layout's workspace, reused
     sc_t = sc.view(R, R).t().contiguous().view(-1)
     coll.all_to_all_v(recvs, sc_t, rd, sends, sd, H)        # back into the send buffers
     outs = [poison_like(x) for x in x_d]
