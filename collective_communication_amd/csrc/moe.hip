@@ -45,12 +45,21 @@ constexpr int kMoeTile = 1024;        // ids per layout tile (kBlock * 4)
 #ifndef COLL_EXPERT_U
 #define COLL_EXPERT_U 8
 #endif
+// combine / fused combine: 16-byte units per lane of a wave (a wave reduces
+// 64 * U units of one token from its K rows); MI355X, 4096 x 7168 x top-8:
+// combine 1 -> 740 us, 2 -> 764, 4 -> 764; fused combine (which also stages
+// its source's send blocks per workgroup and applies the expert) 1 -> 828,
+// 2 -> 766, 4 -> 764, 7 -> 1008, 8 -> 1072
 #ifndef COLL_COMBINE_U
 #define COLL_COMBINE_U 1
+#endif
+#ifndef COLL_COMBINE_RECV_U
+#define COLL_COMBINE_RECV_U 2
 #endif
 constexpr int kPermuteU = COLL_PERMUTE_U;     // 16-byte units per lane, permute
 constexpr int kExpertU = COLL_EXPERT_U;       // ... test expert
 constexpr int kCombineU = COLL_COMBINE_U;     // ... combine (each gathers K rows)
+constexpr int kCombineRecvU = COLL_COMBINE_RECV_U;   // ... fused combine
 constexpr int kMaxExperts = kMoeMaxExperts;
 
 size_t moe_expert_workspace_bytes(int R, int E) {
@@ -619,7 +628,7 @@ __global__ __launch_bounds__(kBlock) void moe_combine_recv_kernel(
     const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls, int R, int T, int K,
     uint32_t upr, int nseg) {
   constexpr int kChunk = 8;
-  constexpr int UN = (G == 8) ? kCombineU : 1;
+  constexpr int UN = (G == 8) ? kCombineRecvU : 1;
   __shared__ SrcBlocks blk;
   const int s = blockIdx.y;
   load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls);
@@ -849,7 +858,7 @@ int launch_moe_combine_recv(const Launch &L, int R, const PtrTable &recv, const 
   for (int r = 0; r < R; r++) vec = vec && aligned16(recv.p[r]) && aligned16(out.p[r]);
   if (T == 0) return COLL_OK;
   const uint64_t upr = vec ? hidden / 8 : hidden;
-  const int per_seg = vec ? 64 * kCombineU : 64;
+  const int per_seg = vec ? 64 * kCombineRecvU : 64;
   const int nseg = (int)((upr + per_seg - 1) / per_seg);
   const uint64_t items = (uint64_t)T * nseg;
   if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
