@@ -70,6 +70,28 @@ def test_allreduce_past_2g_elements():
     del ins, outs
 
 
+@pytest.mark.parametrize("n", [1 << 23, 1 << 24])
+def test_reduce_scatter_store_policy_sides(n):
+    """R = 8 ReduceScatter writing 128 MiB in all (sums stored cacheable) and
+    256 MiB (stored non-temporally): each output element is the rank-order
+    fold of its R inputs, checked on samples against the oracle."""
+    R = 8
+    say("reduce_scatter store policy", n)
+    blocks = [synth.gaussian(PERIOD, 1.0, 98000 + r, "bf16") for r in range(R)]
+    ins = [torch.empty(R * n, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    for t, b in zip(ins, blocks):
+        tiled(t, b)
+    outs = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    coll.reduce_scatter(ins, outs)
+    torch.cuda.synchronize()
+    idx = sample_idx(n, 5, boundary=n // 2)
+    for r in range(R):
+        src = (r * n + idx) % PERIOD
+        want = oracle.allreduce([np.ascontiguousarray(b[src]) for b in blocks], "bf16")[0]
+        assert bits_equal(gather_host(outs[r], idx), want), r
+    del ins, outs
+
+
 def test_all_gather_outputs_past_4gib():
     R, n = 4, (1 << 29) + 40                       # shards of 1 GiB + 80 B; outputs 4 GiB +
     say("max-size all_gather", n)
