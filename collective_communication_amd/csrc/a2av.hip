@@ -64,21 +64,25 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     uint64_t len[4];
-    int64_t sdv[4], rdv[4];
+    int64_t cnt[4], sdv[4], rdv[4];
     uint64_t local = 0;
-    // all three tables are loaded before the scan: one round trip to L2
+    // all three tables are loaded before the scan: one round trip to L2.  The
+    // loads are unconditional (a lane past the last block reads block 0 and
+    // discards it): a load under `if (b < nb)` made the compiler wait for it
+    // inside the branch, one round trip per block of the lane.
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int b = lane * 4 + j;
-      len[j] = 0;
-      sdv[j] = rdv[j] = 0;
-      if (b < nb) {
-        const int s = b / R, d = b - s * R;
-        const int64_t c = counts[b];
-        sdv[j] = sdispls[b];
-        rdv[j] = rdispls[d * R + s];
-        len[j] = c > 0 ? (uint64_t)c * row_units : 0;
-      }
+      const int bb = b < nb ? b : 0;
+      const int s = bb / R, d = bb - s * R;
+      cnt[j] = counts[bb];
+      sdv[j] = sdispls[bb];
+      rdv[j] = rdispls[d * R + s];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int b = lane * 4 + j;
+      len[j] = (b < nb && cnt[j] > 0) ? (uint64_t)cnt[j] * row_units : 0;
       local += len[j];
     }
     const uint64_t incl = wave_incl_scan(local);
@@ -212,21 +216,23 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     uint64_t len[4], nch[4];
-    int64_t sdv[4], rdv[4];
+    int64_t cnt[4], sdv[4], rdv[4];
     uint64_t local = 0;
     bool misaligned = false;
+    // unconditional loads (clamped index), then the bounds: one round trip
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int b = lane * 4 + j;
-      len[j] = 0;
-      sdv[j] = rdv[j] = 0;
-      if (b < nb) {
-        const int s = b / R, d = b - s * R;
-        const int64_t c = counts[b];
-        sdv[j] = sdispls[b];
-        rdv[j] = rdispls[d * R + s];
-        len[j] = c > 0 ? (uint64_t)c * row_bytes : 0;
-      }
+      const int bb = b < nb ? b : 0;
+      const int s = bb / R, d = bb - s * R;
+      cnt[j] = counts[bb];
+      sdv[j] = sdispls[bb];
+      rdv[j] = rdispls[d * R + s];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int b = lane * 4 + j;
+      len[j] = (b < nb && cnt[j] > 0) ? (uint64_t)cnt[j] * row_bytes : 0;
       nch[j] = (len[j] + 15) / 16;
       local += nch[j];
     }

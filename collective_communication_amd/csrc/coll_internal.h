@@ -316,6 +316,18 @@ template <> struct UnitT<1> { typedef uint8_t T; };
 #define COLL_UNIT_SWITCH(KERNEL, UNIT, NT, GRID, STREAM, ...) \
   COLL_UNIT_SWITCH_BLOCK(KERNEL, UNIT, NT, GRID, kBlock, STREAM, __VA_ARGS__)
 
+// Scheduling fences that emit no instruction.  COLL_OPAQUE(x): x is taken to
+// be rewritten in a vector register here, so the optimizer can neither see
+// its value (a load through it stays a vector load) nor hoist what depends on
+// it above this point.  COLL_KEEP(x): x must be available here, so its load
+// is issued and completed before this point.
+#ifndef COLL_OPAQUE
+#define COLL_OPAQUE(x) asm volatile("" : "+v"(x))
+#endif
+#ifndef COLL_KEEP
+#define COLL_KEEP(x) asm volatile("" ::"v"(x))
+#endif
+
 // ----------------------------------------------------------- launch helpers
 
 struct Launch {

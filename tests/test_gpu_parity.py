@@ -395,6 +395,8 @@ def moe_gpu(xs, ids, ws, E):
     (2, 8, 50, 2, 5),         # 10-byte rows: scalar element paths
     (3, 12, 1500, 4, 16),
     (16, 1024, 200, 8, 8),
+    (2, 16, 40, 10, 16),      # top-10: a second, partial chunk of slots
+    (2, 16, 40, 10, 5),
 ])
 def test_moe_pipeline(R, E, T, K, H):
     say("moe", R, E, T, K, H)
