@@ -99,13 +99,18 @@ __global__ __launch_bounds__(kBlock) void moe_hist(PtrTable ids, int TK, int E, 
   for (int e = threadIdx.x; e < E; e += kBlock) h[e] = 0;
   __syncthreads();
   const int32_t *id = reinterpret_cast<const int32_t *>(ids.p[s]);
+  // the tile's ids are loaded together (clamped index; TK > tile * kMoeTile)
+  int v[kMoeTile / kBlock];
 #pragma unroll
   for (int j = 0; j < kMoeTile / kBlock; j++) {
-    int i = tile * kMoeTile + j * kBlock + threadIdx.x;
-    if (i < TK) {
-      const int e = id[i];
-      if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);   // out-of-range ids are dropped
-    }
+    const int i = tile * kMoeTile + j * kBlock + threadIdx.x;
+    v[j] = id[i < TK ? i : TK - 1];
+  }
+#pragma unroll
+  for (int j = 0; j < kMoeTile / kBlock; j++) {
+    const int i = tile * kMoeTile + j * kBlock + threadIdx.x;
+    const int e = v[j];
+    if (i < TK && (unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);   // out-of-range ids dropped
   }
   __syncthreads();
   int32_t *out = hist + ((size_t)s * ntiles + tile) * E;
@@ -172,13 +177,17 @@ __global__ __launch_bounds__(kBlock) void moe_pos(PtrTable ids, MutPtrTable pos,
   __shared__ int base[kMaxExperts];
   __shared__ int run[kMaxExperts];
   __shared__ int wcnt[kBlock / 64][kMaxExperts];
+  __shared__ int64_t sc[COLL_MAX_RANKS * COLL_MAX_RANKS];
   const int s = blockIdx.y, tile = blockIdx.x;
   if (s == 0 && tile == 0) {
-    // receive displacements: rdispls[d][s'] = sum_{s'' < s'} sendcounts[s''][d]
-    for (int t = threadIdx.x; t < R * R; t += kBlock) {
-      int d = t / R, s2 = t - d * R;
+    // receive displacements: rdispls[d][s'] = sum_{s'' < s'} sendcounts[s''][d],
+    // from the counts staged in LDS (one load per thread, R * R <= kBlock)
+    if ((int)threadIdx.x < R * R) sc[threadIdx.x] = sendcounts[threadIdx.x];
+    __syncthreads();
+    if ((int)threadIdx.x < R * R) {
+      const int t = threadIdx.x, d = t / R, s2 = t - d * R;
       int64_t acc = 0;
-      for (int q = 0; q < s2; q++) acc += sendcounts[q * R + d];
+      for (int q = 0; q < s2; q++) acc += sc[q * R + d];
       rdispls[d * R + s2] = acc;
     }
   }
@@ -192,13 +201,21 @@ __global__ __launch_bounds__(kBlock) void moe_pos(PtrTable ids, MutPtrTable pos,
   int32_t *out = reinterpret_cast<int32_t *>(pos.p[s]);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // every round's id is loaded up front (clamped index; TK > tile * kMoeTile)
+  int ids_r[kMoeTile / kBlock];
+#pragma unroll
+  for (int round = 0; round < kMoeTile / kBlock; round++) {
+    const int i = tile * kMoeTile + round * kBlock + threadIdx.x;
+    ids_r[round] = id[i < TK ? i : TK - 1];
+  }
+#pragma unroll
   for (int round = 0; round < kMoeTile / kBlock; round++) {
     for (int x = threadIdx.x; x < E; x += kBlock)
 #pragma unroll
       for (int q = 0; q < kBlock / 64; q++) wcnt[q][x] = 0;
     __syncthreads();
     const int i = tile * kMoeTile + round * kBlock + threadIdx.x;
-    const int raw = i < TK ? id[i] : -1;
+    const int raw = i < TK ? ids_r[round] : -1;
     const bool valid = (unsigned)raw < (unsigned)E;   // out-of-range ids get no slot
     const int e = valid ? raw : 0;
     uint64_t mask = __ballot(valid);
