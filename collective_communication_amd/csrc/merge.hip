@@ -21,13 +21,14 @@ __device__ __forceinline__ void row_weights(const PtrTable &lse, int R, uint64_t
                                             float *w, float *L) {
   float l[COLL_MAX_RANKS];
   float m = -__builtin_inff();
+  // all R loads first, then the max: a use inside the load's own `if` made
+  // the compiler wait for each load in turn
 #pragma unroll
-  for (int r = 0; r < COLL_MAX_RANKS; r++) {
-    if (r < R) {
-      l[r] = reinterpret_cast<const float *>(lse.p[r])[row];
-      m = l[r] > m ? l[r] : m;
-    }
-  }
+  for (int r = 0; r < COLL_MAX_RANKS; r++)
+    if (r < R) l[r] = reinterpret_cast<const float *>(lse.p[r])[row];
+#pragma unroll
+  for (int r = 0; r < COLL_MAX_RANKS; r++)
+    if (r < R) m = l[r] > m ? l[r] : m;
   if (m == -__builtin_inff()) {
 #pragma unroll
     for (int r = 0; r < COLL_MAX_RANKS; r++) w[r] = 0.0f;
