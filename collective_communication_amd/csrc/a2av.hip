@@ -27,6 +27,12 @@ constexpr int kA2aU = COLL_A2A_U;             // units per lane per tile (one-pa
 #define COLL_A2A_RES_U 2
 #endif
 constexpr int kA2aResU = COLL_A2A_RES_U;      // ... resident grid
+#ifndef COLL_A2A_BLOCK
+#define COLL_A2A_BLOCK 256
+#endif
+// lanes per workgroup, one-pass grid (MI355X, the MoE exchange: 256 -> 1247 us,
+// 128 -> 1275, 64 -> 1320: the workgroup shares one block-table build)
+constexpr int kA2aBlock = COLL_A2A_BLOCK;
 
 // Inclusive prefix sum across one wave64 (Hillis-Steele over lanes).
 __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
@@ -50,7 +56,7 @@ __device__ __forceinline__ __attribute__((address_space(1))) U *gmut(uint64_t a)
   return (__attribute__((address_space(1))) U *)a;
 }
 
-template <int B, bool NT, int UN>
+template <int B, bool NT, int UN, int BS>
 __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_t *counts,
                                           const int64_t *sdispls, const int64_t *rdispls,
                                           uint64_t row_units) {
@@ -106,7 +112,7 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
   const uint64_t total = s_end[nb - 1];
   int top = 1;
   while (top * 2 <= nb) top *= 2;            // largest power of two <= nb
-  const uint64_t tile = (uint64_t)kBlock * UN;
+  const uint64_t tile = (uint64_t)BS * UN;
   // the current block's bounds and address bases live in registers; LDS is
   // read only when a unit falls outside them
   uint64_t blo = 1, bhi = 0, sbase = 0, dbase = 0;
@@ -118,7 +124,7 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
     uint64_t sa[UN], da[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t x = base + (uint64_t)u * kBlock;
+      const uint64_t x = base + (uint64_t)u * BS;
       sa[u] = da[u] = 0;
       if (x < total) {
         if (x < blo || x >= bhi) {
@@ -139,14 +145,14 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
     U v[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      if (base + (uint64_t)u * kBlock < total) {
+      if (base + (uint64_t)u * BS < total) {
         if constexpr (NT) v[u] = __builtin_nontemporal_load(gconst<U>(sa[u]));
         else v[u] = *gconst<U>(sa[u]);
       }
     }
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      if (base + (uint64_t)u * kBlock < total) {
+      if (base + (uint64_t)u * BS < total) {
         if constexpr (NT) __builtin_nontemporal_store(v[u], gmut<U>(da[u]));
         else *gmut<U>(da[u]) = v[u];
       }
@@ -156,10 +162,10 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
 
 // One-pass grid (large exchanges): kA2aU units per lane per tile.
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void a2av_kernel(RankPtrs p, int R, const int64_t *counts,
+__global__ __launch_bounds__(kA2aBlock) void a2av_kernel(RankPtrs p, int R, const int64_t *counts,
                                                       const int64_t *sdispls,
                                                       const int64_t *rdispls, uint64_t row_units) {
-  a2av_body<B, NT, kA2aU>(p, R, counts, sdispls, rdispls, row_units);
+  a2av_body<B, NT, kA2aU, kA2aBlock>(p, R, counts, sdispls, rdispls, row_units);
 }
 // Resident grid (up to 256 MiB): kA2aResU units per lane per tile.
 template <int B, bool NT>
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void a2av_res_kernel(RankPtrs p, int R,
                                                           const int64_t *sdispls,
                                                           const int64_t *rdispls,
                                                           uint64_t row_units) {
-  a2av_body<B, NT, kA2aResU>(p, R, counts, sdispls, rdispls, row_units);
+  a2av_body<B, NT, kA2aResU, kBlock>(p, R, counts, sdispls, rdispls, row_units);
 }
 
 // Rows whose size or buffers do not allow 16-byte units on every row (the
@@ -387,16 +393,17 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
   unsigned g = g_res;
   if (unit == 16) {
     if (rows_capacity > 0) {
-      const unsigned g1 = grid_for(L, (uint64_t)rows_capacity * row_units, kA2aU);
-      g = resident ? (g1 < g_res ? g1 : g_res) : g1;
+      const uint64_t units = (uint64_t)rows_capacity * row_units;
+      g = resident ? grid_for(L, units, kA2aU) : grid_tiles(units, (uint64_t)kA2aBlock * kA2aU);
+      if (resident && g > g_res) g = g_res;
     }
     if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
     if (resident)
       COLL_UNIT_SWITCH(a2av_res_kernel, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts,
                        sdispls, rdispls, row_units);
     else
-      COLL_UNIT_SWITCH(a2av_kernel, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts, sdispls,
-                       rdispls, row_units);
+      COLL_UNIT_SWITCH_BLOCK(a2av_kernel, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, R,
+                             counts, sdispls, rdispls, row_units);
   } else {
     // chunks: at most capacity bytes / 16 plus one partial chunk per block
     if (rows_capacity > 0) {

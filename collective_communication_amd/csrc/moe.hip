@@ -56,8 +56,34 @@ constexpr int kMoeTile = 1024;        // ids per layout tile (kBlock * 4)
 #ifndef COLL_COMBINE_RECV_U
 #define COLL_COMBINE_RECV_U 2
 #endif
+// Row items (one wave each) per workgroup; MI355X, 4096 x 7168 x top-8:
+// permute 4 -> 779 us, 2 -> 810, 1 -> 872; fused dispatch 4 -> 766, 2 -> 761,
+// 1 -> 786; combine 4 -> 742, 2 -> 730, 1 -> 718; fused combine 4 -> 763,
+// 2 -> 760, 1 -> 744.
+#ifndef COLL_PERMUTE_WAVES
+#define COLL_PERMUTE_WAVES 4
+#endif
+#ifndef COLL_COMBINE_WAVES
+#define COLL_COMBINE_WAVES 1
+#endif
+#ifndef COLL_DISPATCH_WAVES
+#define COLL_DISPATCH_WAVES 4
+#endif
+#ifndef COLL_COMBINE_RECV_WAVES
+#define COLL_COMBINE_RECV_WAVES 1
+#endif
+// waves (row items) per workgroup of the row-segment kernels
+constexpr int kPermuteWaves = COLL_PERMUTE_WAVES;
+constexpr int kCombineWaves = COLL_COMBINE_WAVES;
+constexpr int kDispatchWaves = COLL_DISPATCH_WAVES;
+constexpr int kCombineRecvWaves = COLL_COMBINE_RECV_WAVES;
 constexpr int kPermuteU = COLL_PERMUTE_U;     // 16-byte units per lane, permute
 constexpr int kExpertU = COLL_EXPERT_U;       // ... test expert
+#ifndef COLL_EXPERT_BLOCK
+#define COLL_EXPERT_BLOCK 256
+#endif
+// lanes per workgroup, test expert (MI355X: 256 -> 1290 us, 128 -> 1300, 64 -> 1307)
+constexpr int kExpertBlock = COLL_EXPERT_BLOCK;
 constexpr int kCombineU = COLL_COMBINE_U;     // ... combine (each gathers K rows)
 constexpr int kCombineRecvU = COLL_COMBINE_RECV_U;   // ... fused combine
 constexpr int kMaxExperts = kMoeMaxExperts;
@@ -258,9 +284,10 @@ struct RowItem {
   bool valid;
 };
 
+template <int WAVES>
 __device__ __forceinline__ RowItem row_item(int T, int nseg) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int id = (int)blockIdx.x * (kBlock / 64) + wave;     // < T * nseg + 3
+  const int id = (int)blockIdx.x * WAVES + wave;             // < T * nseg + WAVES - 1
   RowItem it;
   it.t = id / nseg;
   it.seg = id - it.t * nseg;
@@ -270,12 +297,12 @@ __device__ __forceinline__ RowItem row_item(int T, int nseg) {
 
 // send[s][pos[s][t,k]] = x[s][t] for every k.  Segment = 64 lanes x UN units.
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void moe_permute_kernel(PtrTable x, PtrTable pos,
+__global__ __launch_bounds__(64 * kPermuteWaves) void moe_permute_kernel(PtrTable x, PtrTable pos,
                                                              MutPtrTable send, int T, int K,
                                                              uint32_t upr, int nseg) {
   using U = typename UnitT<B>::T;
   constexpr int UN = kPermuteU;
-  const RowItem it = row_item(T, nseg);
+  const RowItem it = row_item<kPermuteWaves>(T, nseg);
   if (!it.valid) return;
   const int s = blockIdx.y;
   const uint32_t TK = (uint32_t)T * (uint32_t)K;
@@ -375,7 +402,7 @@ __global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_c
 // the two.  Every unit of the tile is located, then all loads issue, then the
 // scaled values are stored.
 template <int G, bool NT>
-__global__ __launch_bounds__(kBlock) void moe_expert_scale_kernel(MutPtrTable recv, int R, int E,
+__global__ __launch_bounds__(kExpertBlock) void moe_expert_scale_kernel(MutPtrTable recv, int R, int E,
                                                                   const int64_t *s_end,
                                                                   const int64_t *rb, int top,
                                                                   FastDiv64 upr) {
@@ -390,7 +417,7 @@ __global__ __launch_bounds__(kBlock) void moe_expert_scale_kernel(MutPtrTable re
   int last = N - 1;
   COLL_OPAQUE(last);
   const int64_t nrows = s_end[last];
-  const uint64_t tile = (uint64_t)kBlock * UN;
+  const uint64_t tile = (uint64_t)kExpertBlock * UN;
   for (uint64_t t0 = (uint64_t)blockIdx.x * tile;; t0 += (uint64_t)gridDim.x * tile) {
     // lo(g) = number of entries with s_end <= g = the entry holding row g;
     // rows past the total search to N and are never used
@@ -438,7 +465,7 @@ __global__ __launch_bounds__(kBlock) void moe_expert_scale_kernel(MutPtrTable re
     float sc[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t x = t0 + threadIdx.x + (uint64_t)u * kBlock;
+      const uint64_t x = t0 + threadIdx.x + (uint64_t)u * kExpertBlock;
       at[u] = nullptr;
       if (x >= total) continue;
       const int64_t g = (int64_t)fdiv64(x, upr);
@@ -492,13 +519,13 @@ __device__ __forceinline__ uint32_t slot_of(int32_t p, uint32_t TK) {
 // One wave per (token, segment of 64 x UN units); its K slots and weights
 // are scalar loads, all K x UN gathered loads issue before the fold.
 template <int G, bool NT>
-__global__ __launch_bounds__(kBlock) void moe_combine_kernel(PtrTable back, PtrTable pos,
+__global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(PtrTable back, PtrTable pos,
                                                              PtrTable wts, MutPtrTable out,
                                                              int T, int K, uint32_t upr,
                                                              int nseg) {
   constexpr int kChunk = 8;                    // gathered rows in flight per unit
   constexpr int UN = (G == 8) ? kCombineU : 1;
-  const RowItem it = row_item(T, nseg);
+  const RowItem it = row_item<kCombineWaves>(T, nseg);
   if (!it.valid) return;
   const uint32_t TK = (uint32_t)T * (uint32_t)K;
   const int s = blockIdx.y;
@@ -614,7 +641,7 @@ __device__ __forceinline__ int64_t recv_row_of(const SrcBlocks &b, int R, int64_
 // permute and the exchange in one pass (each token row read once, written K
 // times straight into its destination's receive buffer).
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void moe_dispatch_kernel(PtrTable x, PtrTable pos,
+__global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(PtrTable x, PtrTable pos,
                                                               MutPtrTable recv,
                                                               const int64_t *sendcounts,
                                                               const int64_t *sdispls,
@@ -626,7 +653,7 @@ __global__ __launch_bounds__(kBlock) void moe_dispatch_kernel(PtrTable x, PtrTab
   __shared__ SrcBlocks blk;
   const int s = blockIdx.y;
   load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls);
-  const RowItem it = row_item(T, nseg);
+  const RowItem it = row_item<kDispatchWaves>(T, nseg);
   if (!it.valid) return;
   const int lane = threadIdx.x & 63;
   const U *src = reinterpret_cast<const U *>(x.p[s]) + (size_t)it.t * upr;
@@ -669,7 +696,7 @@ __global__ __launch_bounds__(kBlock) void moe_dispatch_kernel(PtrTable x, PtrTab
 // = rne(widen(row) * (1 + e/256)) with e = ids[s][t,k], the test expert applied
 // as the row is read.  A slot that no block holds contributes +0.
 template <int G, bool NT, bool EXPERT>
-__global__ __launch_bounds__(kBlock) void moe_combine_recv_kernel(
+__global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kernel(
     PtrTable recv, PtrTable pos, PtrTable wts, PtrTable ids, MutPtrTable out,
     const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls, int R, int T, int K,
     uint32_t upr, int nseg) {
@@ -678,7 +705,7 @@ __global__ __launch_bounds__(kBlock) void moe_combine_recv_kernel(
   __shared__ SrcBlocks blk;
   const int s = blockIdx.y;
   load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls);
-  const RowItem it = row_item(T, nseg);
+  const RowItem it = row_item<kCombineRecvWaves>(T, nseg);
   if (!it.valid) return;
   const int lane = threadIdx.x & 63;
   const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
@@ -817,8 +844,8 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
   const uint64_t items = (uint64_t)T * nseg;
   if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
   const bool nt = (uint64_t)R * T * upr * unit * (1 + K) >= L.nt_bytes;
-  dim3 grid((unsigned)((items + 3) / 4), R);
-  COLL_UNIT_SWITCH(moe_permute_kernel, unit, nt, grid, L.stream, x, pos, send, T, K,
+  dim3 grid((unsigned)((items + kPermuteWaves - 1) / kPermuteWaves), R);
+  COLL_UNIT_SWITCH_BLOCK(moe_permute_kernel, unit, nt, grid, 64 * kPermuteWaves, L.stream, x, pos, send, T, K,
                    (uint32_t)upr, nseg);
   return hip_status();
 }
@@ -838,7 +865,7 @@ int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
   const size_t upr = vec ? hidden / 8 : hidden;
   // one workgroup per tile of the capacity; with no capacity, a resident grid
   // (the kernel loops over tiles either way)
-  const size_t tile = (size_t)kBlock * kExpertU;
+  const size_t tile = (size_t)kExpertBlock * kExpertU;
   const size_t cap_units = rows_capacity * upr;
   size_t g = rows_capacity ? (cap_units + tile - 1) / tile : grid_resident(L);
   if (g < 1) g = 1;
@@ -847,13 +874,13 @@ int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
   const bool nt = L.a2a_nt != 0;
   if (vec) {
     if (nt)
-      hipLaunchKernelGGL((moe_expert_scale_kernel<8, true>), dim3((unsigned)g), dim3(kBlock), 0,
+      hipLaunchKernelGGL((moe_expert_scale_kernel<8, true>), dim3((unsigned)g), dim3(kExpertBlock), 0,
                          L.stream, recv, R, E, s_end, rb, top, f);
     else
-      hipLaunchKernelGGL((moe_expert_scale_kernel<8, false>), dim3((unsigned)g), dim3(kBlock), 0,
+      hipLaunchKernelGGL((moe_expert_scale_kernel<8, false>), dim3((unsigned)g), dim3(kExpertBlock), 0,
                          L.stream, recv, R, E, s_end, rb, top, f);
   } else {
-    hipLaunchKernelGGL((moe_expert_scale_kernel<1, false>), dim3((unsigned)g), dim3(kBlock), 0,
+    hipLaunchKernelGGL((moe_expert_scale_kernel<1, false>), dim3((unsigned)g), dim3(kExpertBlock), 0,
                        L.stream, recv, R, E, s_end, rb, top, f);
   }
   return hip_status();
@@ -869,17 +896,17 @@ int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTa
   const int nseg = (int)((upr + per_seg - 1) / per_seg);
   const uint64_t items = (uint64_t)T * nseg;
   if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
-  dim3 grid((unsigned)((items + 3) / 4), R);
+  dim3 grid((unsigned)((items + kCombineWaves - 1) / kCombineWaves), R);
   const bool nt = (uint64_t)R * T * (K + 1) * hidden * 2 >= L.nt_bytes;
   if (vec) {
     if (nt)
-      hipLaunchKernelGGL((moe_combine_kernel<8, true>), grid, dim3(kBlock), 0, L.stream, back, pos,
+      hipLaunchKernelGGL((moe_combine_kernel<8, true>), grid, dim3(64 * kCombineWaves), 0, L.stream, back, pos,
                          w, out, T, K, (uint32_t)upr, nseg);
     else
-      hipLaunchKernelGGL((moe_combine_kernel<8, false>), grid, dim3(kBlock), 0, L.stream, back,
+      hipLaunchKernelGGL((moe_combine_kernel<8, false>), grid, dim3(64 * kCombineWaves), 0, L.stream, back,
                          pos, w, out, T, K, (uint32_t)upr, nseg);
   } else {
-    hipLaunchKernelGGL((moe_combine_kernel<1, false>), grid, dim3(kBlock), 0, L.stream, back, pos,
+    hipLaunchKernelGGL((moe_combine_kernel<1, false>), grid, dim3(64 * kCombineWaves), 0, L.stream, back, pos,
                        w, out, T, K, (uint32_t)upr, nseg);
   }
   return hip_status();
@@ -898,8 +925,8 @@ int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTabl
   const uint64_t items = (uint64_t)T * nseg;
   if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
   const bool nt = (uint64_t)R * T * upr * unit * (1 + K) >= L.nt_bytes;
-  dim3 grid((unsigned)((items + 3) / 4), R);
-  COLL_UNIT_SWITCH(moe_dispatch_kernel, unit, nt, grid, L.stream, x, pos, recv, sendcounts,
+  dim3 grid((unsigned)((items + kDispatchWaves - 1) / kDispatchWaves), R);
+  COLL_UNIT_SWITCH_BLOCK(moe_dispatch_kernel, unit, nt, grid, 64 * kDispatchWaves, L.stream, x, pos, recv, sendcounts,
                    sdispls, rdispls, R, T, K, (uint32_t)upr, nseg);
   return hip_status();
 }
@@ -916,12 +943,12 @@ int launch_moe_combine_recv(const Launch &L, int R, const PtrTable &recv, const 
   const int nseg = (int)((upr + per_seg - 1) / per_seg);
   const uint64_t items = (uint64_t)T * nseg;
   if (items >= (1ull << 31) - 4) return COLL_ERR_UNSUPPORTED;
-  dim3 grid((unsigned)((items + 3) / 4), R);
+  dim3 grid((unsigned)((items + kCombineRecvWaves - 1) / kCombineRecvWaves), R);
   const bool nt = (uint64_t)R * T * (K + 1) * hidden * 2 >= L.nt_bytes;
   const PtrTable none{};
   const PtrTable &idt = ids ? *ids : none;
 #define COLL_COMBINE_RECV(G, NTV, EX)                                                              \
-  hipLaunchKernelGGL((moe_combine_recv_kernel<G, NTV, EX>), grid, dim3(kBlock), 0, L.stream, recv, \
+  hipLaunchKernelGGL((moe_combine_recv_kernel<G, NTV, EX>), grid, dim3(64 * kCombineRecvWaves), 0, L.stream, recv, \
                      pos, w, idt, out, sendcounts, sdispls, rdispls, R, T, K, (uint32_t)upr, nseg)
   if (vec && nt && ids) COLL_COMBINE_RECV(8, true, true);
   else if (vec && nt) COLL_COMBINE_RECV(8, true, false);

@@ -22,10 +22,11 @@ namespace {
 // ---------------------------------------------------------------- AllReduce
 
 // Tile shape of the R-way reductions (measured on MI355X, R = 8, 16-64 MiB
-// per rank, rank buffers placed at distinct 4 KiB colours): AllReduce does
-// best with one-wave workgroups and one 16-byte unit per lane per rank (8
-// loads in flight per lane, many small tiles); ReduceScatter, whose writes are
-// 1/R of its reads, with 256 lanes x 2 units.
+// per rank, rank buffers in rank arenas): both do best with one-wave
+// workgroups and one 16-byte unit per lane per rank (8 loads in flight per
+// lane, many small tiles).  ReduceScatter [8192, 4096] x 8: 100.4 us with
+// 256 lanes x 2 units, 95.0 with 64 x 1 (Reduce of 8 x 64 MiB: 99.4 -> 94.0);
+// 64 x 2 and 128 x 1 measured the same as 256 x 2.
 #ifndef COLL_AR_BLOCK
 #define COLL_AR_BLOCK 64
 #endif
@@ -33,10 +34,10 @@ namespace {
 #define COLL_AR_U_MID 1          // units per lane for 3 <= R <= 8
 #endif
 #ifndef COLL_RS_BLOCK
-#define COLL_RS_BLOCK 256
+#define COLL_RS_BLOCK 64
 #endif
 #ifndef COLL_RS_U_MID
-#define COLL_RS_U_MID 2
+#define COLL_RS_U_MID 1
 #endif
 constexpr int kArBlock = COLL_AR_BLOCK;
 constexpr int kRsBlock = COLL_RS_BLOCK;
