@@ -70,6 +70,19 @@ __device__ __forceinline__ void st(void *base, size_t i, U v) {
 #define COLL_COPY_U 1
 #endif
 constexpr int kCopyU = COLL_COPY_U;
+// lanes per workgroup of the copy family (Broadcast, Scatter, the uniform
+// all-to-all and re-shards, the LSE merge) and of Gather.  MI355X, graph-timed:
+// 64 lanes beat 256 on the 1 GiB copy (328.5 -> 319.4 us), Scatter 8 x 64 MiB
+// (167 -> 162), seq -> heads (95 -> 92.5) and match it elsewhere; 128 and 512
+// were no better.  Gather (fp32 logits to the root) is 2% slower with 64.
+#ifndef COLL_COPY_BLOCK
+#define COLL_COPY_BLOCK 64
+#endif
+#ifndef COLL_GATHER_BLOCK
+#define COLL_GATHER_BLOCK 256
+#endif
+constexpr int kCopyBlock = COLL_COPY_BLOCK;
+constexpr int kGatherBlock = COLL_GATHER_BLOCK;
 
 // ------------------------------------------------ element formats (exact widening)
 

@@ -66,16 +66,16 @@ __global__ __launch_bounds__(kAgBlock) void ag_kernel(RankPtrs p, int R, size_t 
 // Flattened over the root's output in units: j -> (o, q, i) with two fast
 // divisions; writes are sequential, reads are runs of `upr` units per rank.
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void gather_kernel(RankPtrs p, void *out, uint32_t total,
+__global__ __launch_bounds__(kGatherBlock) void gather_kernel(RankPtrs p, void *out, uint32_t total,
                                                         FastDiv per_row, FastDiv upr) {
   using U = typename UnitT<B>::T;
   constexpr int UN = kCopyU;
-  const uint32_t tile = kBlock * UN;
+  const uint32_t tile = kGatherBlock * UN;
   for (uint32_t base = blockIdx.x * tile + threadIdx.x; base < total; base += gridDim.x * tile) {
     U v[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint32_t j = base + u * kBlock;
+      const uint32_t j = base + u * kGatherBlock;
       if (j < total) {
         const uint32_t o = fdiv(j, per_row);
         const uint32_t rem = j - o * per_row.d;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(RankPtrs p, void *out, u
     }
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint32_t j = base + u * kBlock;
+      const uint32_t j = base + u * kGatherBlock;
       if (j < total) st<U, NT>(out, j, v[u]);
     }
   }
@@ -95,17 +95,17 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(RankPtrs p, void *out, u
 // The same with 64-bit indices, for outputs of 2^31 units (32 GiB with
 // 16-byte units) and more.
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void gather_kernel64(RankPtrs p, void *out, uint64_t total,
+__global__ __launch_bounds__(kGatherBlock) void gather_kernel64(RankPtrs p, void *out, uint64_t total,
                                                           FastDiv64 per_row, FastDiv64 upr) {
   using U = typename UnitT<B>::T;
   constexpr int UN = kCopyU;
-  const uint64_t tile = (uint64_t)kBlock * UN;
+  const uint64_t tile = (uint64_t)kGatherBlock * UN;
   for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
        base += (uint64_t)gridDim.x * tile) {
     U v[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t j = base + (uint64_t)u * kBlock;
+      const uint64_t j = base + (uint64_t)u * kGatherBlock;
       if (j < total) {
         const uint64_t o = fdiv64(j, per_row);
         const uint64_t rem = j - o * per_row.d;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel64(RankPtrs p, void *out,
     }
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t j = base + (uint64_t)u * kBlock;
+      const uint64_t j = base + (uint64_t)u * kGatherBlock;
       if (j < total) st<U, NT>(out, j, v[u]);
     }
   }
@@ -124,24 +124,24 @@ __global__ __launch_bounds__(kBlock) void gather_kernel64(RankPtrs p, void *out,
 
 // --------------------------------------------------------------- Broadcast
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void bcast_kernel(const void *src, RankPtrs p, int R,
+__global__ __launch_bounds__(kCopyBlock) void bcast_kernel(const void *src, RankPtrs p, int R,
                                                        size_t nunits) {
   using U = typename UnitT<B>::T;
   constexpr int UN = kCopyU;
-  const size_t tile = (size_t)kBlock * UN;
+  const size_t tile = (size_t)kCopyBlock * UN;
   for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nunits;
        base += (size_t)gridDim.x * tile) {
     U v[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const size_t i = base + (size_t)u * kBlock;
+      const size_t i = base + (size_t)u * kCopyBlock;
       if (i < nunits) v[u] = ld<U, NT>(src, i);
     }
     for (int r = 0; r < R; r++) {
       if (p.out[r] == nullptr || p.out[r] == src) continue;
 #pragma unroll
       for (int u = 0; u < UN; u++) {
-        const size_t i = base + (size_t)u * kBlock;
+        const size_t i = base + (size_t)u * kCopyBlock;
         if (i < nunits) st<U, NT>(p.out[r], i, v[u]);
       }
     }
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(const void *src, RankPtrs
 // blockIdx.y = destination rank r: out[r][i] = root[r*n + i] (tutorial 4).
 // A rank whose buffer is its own chunk of the root buffer is skipped.
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void scatter_kernel(const void *src, RankPtrs p,
+__global__ __launch_bounds__(kCopyBlock) void scatter_kernel(const void *src, RankPtrs p,
                                                          size_t nunits) {
   using U = typename UnitT<B>::T;
   constexpr int UN = kCopyU;
@@ -160,18 +160,18 @@ __global__ __launch_bounds__(kBlock) void scatter_kernel(const void *src, RankPt
   const U *s = reinterpret_cast<const U *>(src) + (size_t)r * nunits;
   void *dst = p.out[r];
   if (dst == nullptr || dst == (const void *)s) return;
-  const size_t tile = (size_t)kBlock * UN;
+  const size_t tile = (size_t)kCopyBlock * UN;
   for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nunits;
        base += (size_t)gridDim.x * tile) {
     U v[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const size_t i = base + (size_t)u * kBlock;
+      const size_t i = base + (size_t)u * kCopyBlock;
       if (i < nunits) v[u] = ld<U, NT>(s, i);
     }
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const size_t i = base + (size_t)u * kBlock;
+      const size_t i = base + (size_t)u * kCopyBlock;
       if (i < nunits) st<U, NT>(dst, i, v[u]);
     }
   }
@@ -185,8 +185,8 @@ int launch_scatter(const Launch &L, int R, const void *src, const RankPtrs &p, s
   const int unit = copy_unit(bits);
   const size_t nunits = bytes / unit;
   const bool nt = 2 * (size_t)R * bytes >= L.nt_bytes;
-  dim3 grid(grid_for(L, nunits, kCopyU), R);
-  COLL_UNIT_SWITCH(scatter_kernel, unit, nt, grid, L.stream, src, p, nunits);
+  dim3 grid(grid_tiles(nunits, (size_t)kCopyBlock * kCopyU), R);
+  COLL_UNIT_SWITCH_BLOCK(scatter_kernel, unit, nt, grid, kCopyBlock, L.stream, src, p, nunits);
   return hip_status();
 }
 
@@ -209,17 +209,18 @@ int launch_gather(const Launch &L, int R, const RankPtrs &p, void *out, size_t o
   const size_t upr = inner_bytes / unit;            // units per rank per row
   const size_t total = outer * R * upr;
   const bool nt = 2 * total * (size_t)unit >= L.nt_bytes;
-  dim3 grid(grid_for(L, total, kCopyU));
+  dim3 grid(grid_tiles(total, (size_t)kGatherBlock * kCopyU));
   if (total < (1ull << 31)) {                        // 32-bit index space
     const FastDiv f_row = make_fastdiv((uint32_t)(R * upr));
     const FastDiv f_upr = make_fastdiv((uint32_t)upr);
     const uint32_t t = (uint32_t)total;
-    COLL_UNIT_SWITCH(gather_kernel, unit, nt, grid, L.stream, p, out, t, f_row, f_upr);
+    COLL_UNIT_SWITCH_BLOCK(gather_kernel, unit, nt, grid, kGatherBlock, L.stream, p, out, t, f_row,
+                           f_upr);
   } else {
     const FastDiv64 f_row = make_fastdiv64((uint64_t)R * upr);
     const FastDiv64 f_upr = make_fastdiv64(upr);
-    COLL_UNIT_SWITCH(gather_kernel64, unit, nt, grid, L.stream, p, out, (uint64_t)total, f_row,
-                     f_upr);
+    COLL_UNIT_SWITCH_BLOCK(gather_kernel64, unit, nt, grid, kGatherBlock, L.stream, p, out,
+                           (uint64_t)total, f_row, f_upr);
   }
   return hip_status();
 }
@@ -230,8 +231,8 @@ int launch_broadcast(const Launch &L, int R, const void *src, const RankPtrs &p,
   const int unit = copy_unit(bits);
   const size_t nunits = bytes / unit;
   const bool nt = (size_t)(R + 1) * bytes >= L.nt_bytes;
-  dim3 grid(grid_for(L, nunits, kCopyU));
-  COLL_UNIT_SWITCH(bcast_kernel, unit, nt, grid, L.stream, src, p, R, nunits);
+  dim3 grid(grid_tiles(nunits, (size_t)kCopyBlock * kCopyU));
+  COLL_UNIT_SWITCH_BLOCK(bcast_kernel, unit, nt, grid, kCopyBlock, L.stream, src, p, R, nunits);
   return hip_status();
 }
 

@@ -29,13 +29,13 @@ __device__ __forceinline__ void reshard_body(const RankPtrs &p, int R, uint64_t 
   constexpr int UN = kCopyU;
   const int y = blockIdx.y;                       // destination rank
   void *dst = p.out[y];
-  const uint64_t tile = (uint64_t)kBlock * UN;
+  const uint64_t tile = (uint64_t)kCopyBlock * UN;
   for (uint64_t base = (uint64_t)blockIdx.x * tile + threadIdx.x; base < total;
        base += (uint64_t)gridDim.x * tile) {
     U v[UN];
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t x = base + (uint64_t)u * kBlock;
+      const uint64_t x = base + (uint64_t)u * kCopyBlock;
       if (x < total) {
         const uint64_t q = fdiv64(x, cu);          // destination row
         const uint64_t j = x - q * cu.d;            // unit within the row
@@ -55,20 +55,20 @@ __device__ __forceinline__ void reshard_body(const RankPtrs &p, int R, uint64_t 
     }
 #pragma unroll
     for (int u = 0; u < UN; u++) {
-      const uint64_t x = base + (uint64_t)u * kBlock;
+      const uint64_t x = base + (uint64_t)u * kCopyBlock;
       if (x < total) st<U, NT>(dst, x, v[u]);
     }
   }
 }
 
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void to_heads_kernel(RankPtrs p, int R, uint64_t SL,
+__global__ __launch_bounds__(kCopyBlock) void to_heads_kernel(RankPtrs p, int R, uint64_t SL,
                                                           uint64_t total, FastDiv64 cu,
                                                           FastDiv64 sl) {
   reshard_body<B, NT, true>(p, R, SL, total, cu, sl);
 }
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void to_seq_kernel(RankPtrs p, int R, uint64_t SL,
+__global__ __launch_bounds__(kCopyBlock) void to_seq_kernel(RankPtrs p, int R, uint64_t SL,
                                                         uint64_t total, FastDiv64 cu,
                                                         FastDiv64 rr) {
   reshard_body<B, NT, false>(p, R, SL, total, cu, rr);
@@ -87,15 +87,15 @@ int launch_reshard(const Launch &L, int R, const RankPtrs &p, size_t seq_local,
   if (total == 0) return COLL_OK;
   const FastDiv64 fcu = make_fastdiv64(cu);
   const bool nt = 2 * (uint64_t)R * total * unit >= L.nt_bytes;
-  dim3 grid(grid_for(L, total, kCopyU), R);
+  dim3 grid(grid_tiles(total, (size_t)kCopyBlock * kCopyU), R);
   if (to_heads) {
     const FastDiv64 fsl = make_fastdiv64(seq_local);
-    COLL_UNIT_SWITCH(to_heads_kernel, unit, nt, grid, L.stream, p, R, (uint64_t)seq_local,
-                     total, fcu, fsl);
+    COLL_UNIT_SWITCH_BLOCK(to_heads_kernel, unit, nt, grid, kCopyBlock, L.stream, p, R,
+                           (uint64_t)seq_local, total, fcu, fsl);
   } else {
     const FastDiv64 fr = make_fastdiv64((uint64_t)R);
-    COLL_UNIT_SWITCH(to_seq_kernel, unit, nt, grid, L.stream, p, R, (uint64_t)seq_local, total,
-                     fcu, fr);
+    COLL_UNIT_SWITCH_BLOCK(to_seq_kernel, unit, nt, grid, kCopyBlock, L.stream, p, R,
+                           (uint64_t)seq_local, total, fcu, fr);
   }
   return hip_status();
 }

@@ -51,13 +51,13 @@ __device__ __forceinline__ void row_weights(const PtrTable &lse, int R, uint64_t
 
 // Vector path: 16-byte units (8 bf16 or 4 fp32 per unit).
 template <int DT, bool NT>
-__global__ __launch_bounds__(kBlock) void lse_merge_vec(RankPtrs o, PtrTable lse_in,
+__global__ __launch_bounds__(kCopyBlock) void lse_merge_vec(RankPtrs o, PtrTable lse_in,
                                                         MutPtrTable lse_out, int R,
                                                         uint64_t total, FastDiv64 upr) {
   using F = Fmt<DT>;
   constexpr int VL = F::kLanes;
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-  for (uint64_t x = (uint64_t)blockIdx.x * kBlock + threadIdx.x; x < total; x += stride) {
+  const uint64_t stride = (uint64_t)gridDim.x * kCopyBlock;
+  for (uint64_t x = (uint64_t)blockIdx.x * kCopyBlock + threadIdx.x; x < total; x += stride) {
     const uint64_t row = fdiv64(x, upr);
     const uint64_t j = x - row * upr.d;
     float w[COLL_MAX_RANKS], L;
@@ -97,13 +97,13 @@ __global__ __launch_bounds__(kBlock) void lse_merge_vec(RankPtrs o, PtrTable lse
 // Scalar path: one element per thread (head_dim not a multiple of the
 // vector width, or unaligned buffers).
 template <int DT>
-__global__ __launch_bounds__(kBlock) void lse_merge_scalar(RankPtrs o, PtrTable lse_in,
+__global__ __launch_bounds__(kCopyBlock) void lse_merge_scalar(RankPtrs o, PtrTable lse_in,
                                                            MutPtrTable lse_out, int R,
                                                            uint64_t total, FastDiv64 D) {
   using F = Fmt<DT>;
   using E = typename F::Elem;
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-  for (uint64_t x = (uint64_t)blockIdx.x * kBlock + threadIdx.x; x < total; x += stride) {
+  const uint64_t stride = (uint64_t)gridDim.x * kCopyBlock;
+  for (uint64_t x = (uint64_t)blockIdx.x * kCopyBlock + threadIdx.x; x < total; x += stride) {
     const uint64_t row = fdiv64(x, D);
     const uint64_t c = x - row * D.d;
     float w[COLL_MAX_RANKS], L;
@@ -132,22 +132,22 @@ int launch_lse_merge(const Launch &L, int R, const RankPtrs &o, const PtrTable &
     const uint64_t upr = D / VL;
     const uint64_t total = (uint64_t)rows * upr;
     const FastDiv64 f = make_fastdiv64(upr);
-    dim3 grid(grid_for(L, total));
+    dim3 grid(grid_tiles(total, (size_t)kCopyBlock));
     if (dt == COLL_BF16) {
-      if (nt) hipLaunchKernelGGL((lse_merge_vec<COLL_BF16, true>), grid, dim3(kBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
-      else hipLaunchKernelGGL((lse_merge_vec<COLL_BF16, false>), grid, dim3(kBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
+      if (nt) hipLaunchKernelGGL((lse_merge_vec<COLL_BF16, true>), grid, dim3(kCopyBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
+      else hipLaunchKernelGGL((lse_merge_vec<COLL_BF16, false>), grid, dim3(kCopyBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
     } else {
-      if (nt) hipLaunchKernelGGL((lse_merge_vec<COLL_FP32, true>), grid, dim3(kBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
-      else hipLaunchKernelGGL((lse_merge_vec<COLL_FP32, false>), grid, dim3(kBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
+      if (nt) hipLaunchKernelGGL((lse_merge_vec<COLL_FP32, true>), grid, dim3(kCopyBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
+      else hipLaunchKernelGGL((lse_merge_vec<COLL_FP32, false>), grid, dim3(kCopyBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
     }
   } else {
     const uint64_t total = (uint64_t)rows * D;
     const FastDiv64 f = make_fastdiv64(D);
-    dim3 grid(grid_for(L, total));
+    dim3 grid(grid_tiles(total, (size_t)kCopyBlock));
     if (dt == COLL_BF16)
-      hipLaunchKernelGGL((lse_merge_scalar<COLL_BF16>), grid, dim3(kBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
+      hipLaunchKernelGGL((lse_merge_scalar<COLL_BF16>), grid, dim3(kCopyBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
     else
-      hipLaunchKernelGGL((lse_merge_scalar<COLL_FP32>), grid, dim3(kBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
+      hipLaunchKernelGGL((lse_merge_scalar<COLL_FP32>), grid, dim3(kCopyBlock), 0, L.stream, o, lse_in, lse_out, R, total, f);
   }
   return hip_status();
 }
