@@ -731,7 +731,7 @@ def main():
     roof = None
     if dom in per_row:
         ach = nbytes[dom] / (per_row[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "a2av_kernel<16> (All-to-All-v dispatch)",
+        roof = {"bound": "hbm", "kernel": "a2av_kernel8<16> (All-to-All-v dispatch)",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(os.path.join(ROOT, "collective_communication_amd",

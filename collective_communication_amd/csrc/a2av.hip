@@ -33,6 +33,10 @@ constexpr int kA2aResU = COLL_A2A_RES_U;      // ... resident grid
 // lanes per workgroup, one-pass grid (MI355X, the MoE exchange: 256 -> 1247 us,
 // 128 -> 1275, 64 -> 1320: the workgroup shares one block-table build)
 constexpr int kA2aBlock = COLL_A2A_BLOCK;
+// 1: R <= 8 uses the one-block-per-lane table (a2av_kernel8 / a2av_res_kernel8)
+#ifndef COLL_A2A_SMALL
+#define COLL_A2A_SMALL 1
+#endif
 
 // Inclusive prefix sum across one wave64 (Hillis-Steele over lanes).
 __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
@@ -56,16 +60,38 @@ __device__ __forceinline__ __attribute__((address_space(1))) U *gmut(uint64_t a)
   return (__attribute__((address_space(1))) U *)a;
 }
 
-template <int B, bool NT, int UN, int BS>
+// SMALL: R <= 8, so the R * R <= 64 blocks fit one per lane of wave 0 and the
+// block search has a fixed depth (measured faster than the general form at
+// the MoE exchange; the general form serves R up to 16).
+template <int B, bool NT, int UN, int BS, bool SMALL>
 __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_t *counts,
                                           const int64_t *sdispls, const int64_t *rdispls,
                                           uint64_t row_units) {
   using U = typename UnitT<B>::T;
-  __shared__ uint64_t s_end[kMaxBlocks];   // inclusive end of block b in the global unit space
-  __shared__ uint64_t s_src[kMaxBlocks];   // src unit address minus block start (in units)
-  __shared__ uint64_t s_dst[kMaxBlocks];
+  constexpr int kTab = SMALL ? 64 : kMaxBlocks;
+  __shared__ uint64_t s_end[kTab];   // inclusive end of block b in the global unit space
+  __shared__ uint64_t s_src[kTab];   // src unit address minus block start (in units)
+  __shared__ uint64_t s_dst[kTab];
 
   const int nb = R * R;
+  if constexpr (SMALL) {
+    // Wave 0 builds the table, lane b owning block b; the three loads are
+    // unconditional (clamped index) so they issue together
+    if (threadIdx.x < 64) {
+      const int b = threadIdx.x;
+      const int bb = b < nb ? b : 0;
+      const int s = bb / R, d = bb - s * R;
+      const int64_t c = counts[bb], sdv = sdispls[bb], rdv = rdispls[d * R + s];
+      const uint64_t len = (b < nb && c > 0) ? (uint64_t)c * row_units : 0;
+      const uint64_t incl = wave_incl_scan(len);
+      if (b < nb) {
+        const uint64_t start = incl - len;
+        s_src[b] = reinterpret_cast<uintptr_t>(p.in[s]) / B + (uint64_t)sdv * row_units - start;
+        s_dst[b] = reinterpret_cast<uintptr_t>(p.out[d]) / B + (uint64_t)rdv * row_units - start;
+        s_end[b] = incl;
+      }
+    }
+  } else
   // Wave 0 builds the table: lane l owns blocks 4l .. 4l+3 (nb <= 256).
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -111,7 +137,9 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
 
   const uint64_t total = s_end[nb - 1];
   int top = 1;
-  while (top * 2 <= nb) top *= 2;            // largest power of two <= nb
+  if constexpr (SMALL) top = 32;             // nb <= 64: six steps
+  else
+    while (top * 2 <= nb) top *= 2;          // largest power of two <= nb
   const uint64_t tile = (uint64_t)BS * UN;
   // the current block's bounds and address bases live in registers; LDS is
   // read only when a unit falls outside them
@@ -165,7 +193,13 @@ template <int B, bool NT>
 __global__ __launch_bounds__(kA2aBlock) void a2av_kernel(RankPtrs p, int R, const int64_t *counts,
                                                       const int64_t *sdispls,
                                                       const int64_t *rdispls, uint64_t row_units) {
-  a2av_body<B, NT, kA2aU, kA2aBlock>(p, R, counts, sdispls, rdispls, row_units);
+  a2av_body<B, NT, kA2aU, kA2aBlock, false>(p, R, counts, sdispls, rdispls, row_units);
+}
+template <int B, bool NT>
+__global__ __launch_bounds__(kA2aBlock) void a2av_kernel8(RankPtrs p, int R, const int64_t *counts,
+                                                       const int64_t *sdispls,
+                                                       const int64_t *rdispls, uint64_t row_units) {
+  a2av_body<B, NT, kA2aU, kA2aBlock, true>(p, R, counts, sdispls, rdispls, row_units);
 }
 // Resident grid (up to 256 MiB): kA2aResU units per lane per tile.
 template <int B, bool NT>
@@ -174,7 +208,15 @@ __global__ __launch_bounds__(kBlock) void a2av_res_kernel(RankPtrs p, int R,
                                                           const int64_t *sdispls,
                                                           const int64_t *rdispls,
                                                           uint64_t row_units) {
-  a2av_body<B, NT, kA2aResU, kBlock>(p, R, counts, sdispls, rdispls, row_units);
+  a2av_body<B, NT, kA2aResU, kBlock, false>(p, R, counts, sdispls, rdispls, row_units);
+}
+template <int B, bool NT>
+__global__ __launch_bounds__(kBlock) void a2av_res_kernel8(RankPtrs p, int R,
+                                                           const int64_t *counts,
+                                                           const int64_t *sdispls,
+                                                           const int64_t *rdispls,
+                                                           uint64_t row_units) {
+  a2av_body<B, NT, kA2aResU, kBlock, true>(p, R, counts, sdispls, rdispls, row_units);
 }
 
 // Rows whose size or buffers do not allow 16-byte units on every row (the
@@ -398,9 +440,16 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
       if (resident && g > g_res) g = g_res;
     }
     if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
-    if (resident)
+    const bool small = COLL_A2A_SMALL && R <= 8;
+    if (resident && small)
+      COLL_UNIT_SWITCH(a2av_res_kernel8, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts,
+                       sdispls, rdispls, row_units);
+    else if (resident)
       COLL_UNIT_SWITCH(a2av_res_kernel, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts,
                        sdispls, rdispls, row_units);
+    else if (small)
+      COLL_UNIT_SWITCH_BLOCK(a2av_kernel8, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, R,
+                             counts, sdispls, rdispls, row_units);
     else
       COLL_UNIT_SWITCH_BLOCK(a2av_kernel, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, R,
                              counts, sdispls, rdispls, row_units);
