@@ -133,6 +133,31 @@ def test_gather_64bit_index_space():
     del ins, out
 
 
+def test_gather_rank_share_past_2g_units():
+    """One rank's share alone is more than 2^31 units (2-byte units, odd
+    inner): the 64-bit Gather kernel."""
+    R, outer, inner = 2, 2, (1 << 30) + 3
+    per_rank = outer * inner
+    assert per_rank > (1 << 31)
+    say("max-size gather, 64-bit share", per_rank)
+    blocks = [synth.random_bits(PERIOD, 2, 99100 + q) for q in range(R)]
+    ins = [torch.empty((outer, inner), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    for t, b in zip(ins, blocks):
+        tiled(t.view(-1), b)
+    out = torch.empty((outer, R * inner), dtype=torch.bfloat16, device="cuda")
+    coll.gather(ins, out, 0)
+    torch.cuda.synchronize()
+    total = outer * R * inner
+    idx = sample_idx(total, 4, boundary=1 << 31)
+    o, rem = idx // (R * inner), idx % (R * inner)
+    q, i = rem // inner, rem % inner
+    want = np.array([blocks[a][(oo * inner + b) % PERIOD] for oo, a, b in zip(o, q, i)],
+                    np.uint16)
+    assert bits_equal(gather_host(out.view(-1), idx), want)
+    del ins, out
+    torch.cuda.empty_cache()
+
+
 def test_broadcast_past_4gib():
     R, n = 3, (1 << 31) + 5                        # bf16: 4 GiB + 10 B per buffer
     say("max-size broadcast", n)
