@@ -13,9 +13,10 @@ HBM-resident input, R = 8 virtual ranks, bf16 unless noted:
   bcast        Broadcast int32 [256] from rank 7
   moe_layout   expert histogram / scans / stable slots, 4096 x top-8, 256 experts
   moe_permute  dispatch permute into per-destination send buffers
-  a2av_dispatch  All-to-All-v of the dispatched rows (hidden 7168)
+  a2av_dispatch  All-to-All-v of the dispatched rows (hidden 7168), with a
+               workspace (the descriptor form)
   moe_expert   the test expert y = x * (1 + e/256) on received rows
-  a2av_combine   All-to-All-v back (counts transposed)
+  a2av_combine   All-to-All-v back (counts transposed), with a workspace
   moe_combine  gate-weighted top-8 sum back to each token
 
 value = algorithmic bytes of the whole step / step time (GB/s).  Algorithmic
@@ -23,7 +24,8 @@ bytes are the minimum each row must read plus write (e.g. AllReduce 2*R*S,
 All-to-All-v 2 * rows * row_bytes).  Per-row times come from HIP events on the
 stream the kernels run on; the dominant kernel (a2av_dispatch) is reported
 against the 8 TB/s HBM roofline.  Separate sweeps: AllReduce at 8 KiB .. 64 MiB
-per rank and All-to-All-v (uniform and MoE-shaped), rotating four buffer sets
+per rank and All-to-All-v (uniform and MoE-shaped, plain and with a
+workspace), rotating four buffer sets
 from 8 MiB up so the 256 MB Infinity Cache cannot serve the large sizes.
 
 The CPU baseline times the oracle (single-threaded C) on whole passes of the
@@ -122,6 +124,12 @@ def make_inputs(torch, synth, coll):
          (R, (T * K, H), bf), (R, (T, H), bf)])
     for s, t in enumerate(W["moe_x"]):
         t.copy_(dev_bf16(synth.gaussian((T, H), 1.0, 5000 + s, "bf16")))
+    # workspaces of the two exchanges' descriptor form (block table + one
+    # descriptor per 4 KiB tile of the receive capacity)
+    W["a2a_ws_d"] = torch.empty(coll.all_to_all_v_workspace_bytes(W["send"], W["recv"], H),
+                                dtype=torch.uint8, device="cuda")
+    W["a2a_ws_c"] = torch.empty(coll.all_to_all_v_workspace_bytes(W["recv"], W["back"], H),
+                                dtype=torch.uint8, device="cuda")
     # plain-copy reference (1 GiB through the library's copy kernel), only for
     # calibrating the HBM counters; not part of the step
     W["copy_src"] = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
@@ -172,10 +180,10 @@ def step_rows(W, coll, torch):
                                                W["ec"], W["pos"], W["ws"])),
         ("moe_permute", lambda: coll.moe_permute(W["moe_x"], W["pos"], W["send"])),
         ("a2av_dispatch", lambda: coll.all_to_all_v(W["send"], W["sc"], W["sd"], W["recv"],
-                                                    W["rd"], H)),
+                                                    W["rd"], H, workspace=W["a2a_ws_d"])),
         ("moe_expert", lambda: coll.moe_expert_scale(W["recv"], W["ec"], W["rd"], E, H, W["ews"])),
         ("a2av_combine", lambda: coll.all_to_all_v(W["recv"], W["sc_t"], W["rd"], W["back"],
-                                                   W["sd"], H)),
+                                                   W["sd"], H, workspace=W["a2a_ws_c"])),
         ("moe_combine", lambda: coll.moe_combine(W["back"], W["pos"], W["moe_w"], W["out"])),
     ]
 
@@ -482,22 +490,37 @@ def ar_sweep(torch, coll, log2_sizes=range(13, 27)):
     return res
 
 
+def _a2a_entry(torch, fn, sets, iters, nb, graph_n=24, graph_reps=4):
+    pc = {}
+    med, batch = _launch_times(torch, fn, sets, iters, pc)
+    gt = _graph_time(torch, fn, sets, n=graph_n, reps=graph_reps)
+    return {"graph_us": round(gt * 1e6, 2), "graph_GBps": round(nb / gt / 1e9, 1),
+            "graph_frac": round(nb / gt / 1e9 / HBM_PEAK_GBS, 4),
+            "median_us": round(med * 1e6, 2), **pc, "GBps": round(nb / med / 1e9, 1),
+            "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
+            "batch_GBps": round(nb / batch / 1e9, 1)}
+
+
 def a2a_sweep(torch, coll, synth):
     """All-to-All-v at R=8 (bf16): (i) uniform 1-D, S = 8 KiB .. 64 MiB per
-    rank in rows of one element, equal counts; (ii) MoE-shaped, T tokens per
-    rank x top-8 of 256 experts (Zipf 1.2 routing), rows of 7168.  Buffers in
-    rank arenas; sets rotate so that a size's working set exceeds the 256 MB
-    Infinity Cache where it can.  Algorithmic bytes 2 * (rows moved) * row
-    bytes.  Reports the median per-launch time and a batch mean."""
+    rank in rows of one element, equal counts; (ii) uniform, S = 16 / 32 /
+    64 MiB per rank in rows of 8 elements (16 bytes), plain and with a
+    workspace (descriptor form); (iii) MoE-shaped, T tokens per rank x top-8
+    of 256 experts (Zipf 1.2 routing), rows of 7168, plain and with a
+    workspace.  Buffers in rank arenas; sets rotate so that a size's working
+    set exceeds the 256 MB Infinity Cache where it can.  Algorithmic bytes
+    2 * (rows moved) * row bytes.  Reports the median per-launch time, a batch
+    mean and the graph-replay time."""
     import numpy as np
     bf = torch.bfloat16
-    res = {"uniform_row1": {}, "moe_rows7168": {}}
+    res = {"uniform_row1": {}, "uniform_row8": {}, "uniform_row8_ws": {},
+           "moe_rows7168": {}, "moe_rows7168_ws": {}}
+    dc = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
     for lg in range(13, 27):
         S = 1 << lg
         n = S // 2
         c = np.full((R, R), n // R, np.int64)
         sd = np.tile(np.arange(R, dtype=np.int64) * (n // R), (R, 1))
-        dc = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
         tabs = (dc(c), dc(sd), dc(sd))          # packed: rdispls[d][s] = s * n/R
         sets = 4 if S >= (8 << 20) else 1
         bufs = []
@@ -508,18 +531,32 @@ def a2a_sweep(torch, coll, synth):
             bufs.append((snd, rcv))
         plans = [coll.prepare(coll.all_to_all_v, b[0], tabs[0], tabs[1], b[1], tabs[2], 1)
                  for b in bufs]
-        fn = lambda i: plans[i]()
-        pc = {}
-        med, batch = _launch_times(torch, fn, sets, 1000 if S < (1 << 20) else 50, pc)
-        gt = _graph_time(torch, fn, sets)
-        nb = 2 * R * S
-        res["uniform_row1"][f"{S >> 10}KiB"] = {
-            "graph_us": round(gt * 1e6, 2), "graph_GBps": round(nb / gt / 1e9, 1),
-            "graph_frac": round(nb / gt / 1e9 / HBM_PEAK_GBS, 4),
-            "median_us": round(med * 1e6, 2), **pc, "GBps": round(nb / med / 1e9, 1),
-            "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
-            "batch_GBps": round(nb / batch / 1e9, 1)}
+        res["uniform_row1"][f"{S >> 10}KiB"] = _a2a_entry(
+            torch, lambda i: plans[i](), sets, 1000 if S < (1 << 20) else 50, 2 * R * S)
         del bufs, plans
+    for lg in (24, 25, 26):
+        S = 1 << lg
+        rows = S // 16                           # rows of 8 bf16 per rank
+        c = np.full((R, R), rows // R, np.int64)
+        sd = np.tile(np.arange(R, dtype=np.int64) * (rows // R), (R, 1))
+        tabs = (dc(c), dc(sd), dc(sd))
+        sets = 4
+        bufs = []
+        for _ in range(sets):
+            snd, rcv = coll.rank_arena([(R, (rows, 8), bf), (R, (rows, 8), bf)])
+            for t in snd:
+                t.normal_()
+            bufs.append((snd, rcv))
+        ws = [torch.empty(max(coll.all_to_all_v_workspace_bytes(b[0], b[1], 8), 256),
+                          dtype=torch.uint8, device="cuda") for b in bufs]
+        for key, kw in (("uniform_row8", lambda i: {}),
+                        ("uniform_row8_ws", lambda i: {"workspace": ws[i]})):
+            plans = [coll.prepare(coll.all_to_all_v, b[0], tabs[0], tabs[1], b[1], tabs[2], 8,
+                                  **kw(i)) for i, b in enumerate(bufs)]
+            res[key][f"{S >> 10}KiB"] = _a2a_entry(torch, lambda i: plans[i](), sets, 50,
+                                                   2 * R * S)
+            del plans
+        del bufs, ws
     E, K, H = 256, 8, 7168
     for T in (16, 64, 256, 1024, 4096):
         ids = [torch.from_numpy(synth.zipf_routing(T, E, K, seed=5100 + s)[0]).cuda()
@@ -541,20 +578,19 @@ def a2a_sweep(torch, coll, synth):
             for t in snd:
                 t.normal_()
             bufs.append((snd, rcv))
-        plans = [coll.prepare(coll.all_to_all_v, b[0], sc, sdd, b[1], rdd, H) for b in bufs]
-        fn = lambda i: plans[i]()
-        pc = {}
-        med, batch = _launch_times(torch, fn, sets, 50, pc)
-        gt = _graph_time(torch, fn, sets, n=8 if T >= 4096 else 24, reps=2)
+        a2ws = [torch.empty(max(coll.all_to_all_v_workspace_bytes(b[0], b[1], H), 256),
+                            dtype=torch.uint8, device="cuda") for b in bufs]
         nb = 2 * rows * H * 2
-        res["moe_rows7168"][f"T{T}"] = {
-            "per_rank_MiB": round(T * K * H * 2 / 2**20, 2), "rows": rows,
-            "graph_us": round(gt * 1e6, 2), "graph_GBps": round(nb / gt / 1e9, 1),
-            "graph_frac": round(nb / gt / 1e9 / HBM_PEAK_GBS, 4),
-            "median_us": round(med * 1e6, 2), **pc, "GBps": round(nb / med / 1e9, 1),
-            "frac": round(nb / med / 1e9 / HBM_PEAK_GBS, 4),
-            "batch_GBps": round(nb / batch / 1e9, 1)}
-        del bufs, plans, ids, pos, ws
+        for key, kw in (("moe_rows7168", lambda i: {}),
+                        ("moe_rows7168_ws", lambda i: {"workspace": a2ws[i]})):
+            plans = [coll.prepare(coll.all_to_all_v, b[0], sc, sdd, b[1], rdd, H, **kw(i))
+                     for i, b in enumerate(bufs)]
+            res[key][f"T{T}"] = {
+                "per_rank_MiB": round(T * K * H * 2 / 2**20, 2), "rows": rows,
+                **_a2a_entry(torch, lambda i: plans[i](), sets, 50, nb,
+                             graph_n=8 if T >= 4096 else 24, graph_reps=2)}
+            del plans
+        del bufs, ids, pos, ws, a2ws
     torch.cuda.empty_cache()
     return res
 
@@ -731,7 +767,9 @@ def main():
     roof = None
     if dom in per_row:
         ach = nbytes[dom] / (per_row[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "a2av_kernel8<16> (All-to-All-v dispatch)",
+        roof = {"bound": "hbm",
+                "kernel": "a2av_desc_kernel<16> (All-to-All-v dispatch; the time also covers "
+                          "its descriptor pre-kernel)",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(os.path.join(ROOT, "collective_communication_amd",

@@ -45,6 +45,8 @@ SIGNATURES = {
     "coll_gather": (_i, [_i, _vp, _vp, _i, _sz, _sz, _i, _vp]),
     "coll_broadcast": (_i, [_i, _vp, _vp, _i, _sz, _i, _vp]),
     "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp]),
+    "coll_all_to_all_v_workspace_bytes": (_sz, [_i, _sz, _sz, _i]),
+    "coll_all_to_all_v_ws": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _sz, _vp]),
     "coll_all_to_all": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_seq_heads_reshard": (_i, [_i, _vp, _vp, _sz, _sz, _sz, _i, _i, _vp]),
     "coll_lse_merge": (_i, [_i, _vp, _vp, _vp, _vp, _sz, _sz, _i, _vp]),
@@ -318,25 +320,49 @@ def broadcast(send_root, recvs, root: int, stream=None):
                   _table(recvs, "recv"), root, n * mult, dt)
 
 
-def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
-                 stream=None):
-    """All-to-All-v with device int64 [R*R] counts (s-major), sdispls (s-major)
-    and rdispls (d-major), in rows of ``row_elems`` elements."""
-    R = _ranks(sends, "all_to_all_v")
-    for t, name in ((sendcounts, "sendcounts"), (sdispls, "sdispls"), (rdispls, "rdispls")):
-        if t.dtype != torch.int64 or t.numel() != R * R:
-            raise ValueError(f"all_to_all_v: {name} must be int64 [R*R] on the device")
+def _a2av_shape(sends, recvs, row_elems: int, what: str, capacity=None):
+    R = _ranks(sends, what)
     if len(recvs) != R:
-        raise ValueError("all_to_all_v: one recv per rank")
+        raise ValueError(f"{what}: one recv per rank")
     dt, mult = _copy_dtype(sends[0])
     for t in list(sends) + list(recvs):
         if t.dtype != sends[0].dtype:
-            raise ValueError("all_to_all_v: one dtype for every buffer")
-    # receive capacity in rows: an upper bound of the rows moved (sizes the launch)
-    capacity = sum(t.numel() // row_elems for t in recvs)
-    return _issue("coll_all_to_all_v", "all_to_all_v", stream, R, _table(sends, "send"),
-                  _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"), _table(recvs, "recv"),
-                  _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity)
+            raise ValueError(f"{what}: one dtype for every buffer")
+    # receive capacity in rows: an upper bound of the rows moved (sizes the
+    # launch only); by default the rows the receive buffers hold
+    if capacity is None:
+        capacity = sum(t.numel() // row_elems for t in recvs) if row_elems > 0 else 0
+    elif int(capacity) < 0:
+        raise ValueError(f"{what}: capacity must be >= 0")
+    return R, dt, mult, int(capacity)
+
+
+def all_to_all_v_workspace_bytes(sends, recvs, row_elems: int, capacity=None) -> int:
+    """Workspace bytes all_to_all_v(..., workspace=) needs for these buffers
+    (0: the descriptor form does not apply and no workspace is needed)."""
+    R, dt, mult, capacity = _a2av_shape(sends, recvs, row_elems, "all_to_all_v", capacity)
+    return int(lib().coll_all_to_all_v_workspace_bytes(R, capacity, row_elems * mult, dt))
+
+
+def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
+                 stream=None, workspace=None, capacity=None):
+    """All-to-All-v with device int64 [R*R] counts (s-major), sdispls (s-major)
+    and rdispls (d-major), in rows of ``row_elems`` elements.  With a device
+    ``workspace`` (all_to_all_v_workspace_bytes) large exchanges take the
+    descriptor form.  ``capacity`` (receive rows the launch is sized for;
+    default: the rows the receive buffers hold) shapes the launch, never the
+    result."""
+    R, dt, mult, capacity = _a2av_shape(sends, recvs, row_elems, "all_to_all_v", capacity)
+    for t, name in ((sendcounts, "sendcounts"), (sdispls, "sdispls"), (rdispls, "rdispls")):
+        if t.dtype != torch.int64 or t.numel() != R * R:
+            raise ValueError(f"all_to_all_v: {name} must be int64 [R*R] on the device")
+    args = (R, _table(sends, "send"), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
+            _table(recvs, "recv"), _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity)
+    if workspace is None:
+        return _issue("coll_all_to_all_v", "all_to_all_v", stream, *args)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return _issue("coll_all_to_all_v_ws", "all_to_all_v", stream, *args,
+                  _dev(workspace, "workspace"), ws_bytes)
 
 
 def all_to_all(sends, recvs, stream=None):

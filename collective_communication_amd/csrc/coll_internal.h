@@ -340,6 +340,12 @@ template <> struct UnitT<1> { typedef uint8_t T; };
 #ifndef COLL_KEEP
 #define COLL_KEEP(x) asm volatile("" ::"v"(x))
 #endif
+// COLL_UNIFORM(x): x (uniform across the wave) is taken to be rewritten in a
+// scalar register here, so its load completes through the scalar cache
+// before this point instead of being sunk into a later vector load.
+#ifndef COLL_UNIFORM
+#define COLL_UNIFORM(x) asm volatile("" : "+s"(x))
+#endif
 
 // ----------------------------------------------------------- launch helpers
 
@@ -357,7 +363,7 @@ struct Launch {
 
 // Device properties and tuning knobs (environment, read once per process:
 // COLL_WGS_PER_CU, COLL_NT_MIN_BYTES, COLL_NT_STORE_MIN_BYTES, COLL_A2A_NT,
-// COLL_A2A_GRID, COLL_AR_GRID).
+// COLL_A2A_GRID, COLL_AR_GRID, COLL_A2A_DESC_MIN_BYTES).
 Launch launch_ctx(void *stream);
 
 // One workgroup per tile of kBlock * per_thread units (single pass), capped
@@ -423,6 +429,10 @@ int launch_lse_merge(const Launch &L, int R, const RankPtrs &o, const PtrTable &
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
                 const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
                 size_t rows_capacity);
+size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_t min_bytes);
+int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
+                   const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
+                   size_t rows_capacity, void *ws);
 
 constexpr int kMoeMaxExperts = 1024;
 size_t moe_workspace_bytes(int R, int T, int K, int E);

@@ -205,6 +205,33 @@ int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *se
                       void *stream);
 
 /*
+ * All-to-All-v with a caller workspace: the same exchange and arguments as
+ * coll_all_to_all_v, faster for large exchanges.  A first kernel writes the
+ * block table and, for every tile of 256 sixteen-byte units of the receive
+ * capacity, that tile's block; the copy kernel then starts each tile with one
+ * load of it instead of building the table.  This descriptor form runs when
+ * rows are whole 16-byte units and recv_rows_capacity covers at least 192 MiB
+ * (environment variable COLL_A2A_DESC_MIN_BYTES, read once per process; below
+ * it the second launch costs more than it saves on MI355X).  Otherwise this
+ * call is coll_all_to_all_v, the workspace is not touched and may be NULL, and
+ * the size below is 0.  Its size is
+ * coll_all_to_all_v_workspace_bytes(nranks, recv_rows_capacity, row_elems,
+ * dtype): 32 bytes per block and per tile, the tiles counted in whole groups
+ * of 32, rounded up to 256 (29 MiB for a 3.5 GiB exchange).
+ * workspace: DEVICE, 256-byte aligned, overwritten; concurrent calls need
+ * workspaces of their own.  recv_rows_capacity only sizes the launch: a bound
+ * below the rows actually received costs time, not correctness.
+ * Errors: as coll_all_to_all_v, plus COLL_ERR_INVALID_ARG for a NULL or
+ * misaligned workspace or workspace_bytes below the size when one is needed.
+ */
+size_t coll_all_to_all_v_workspace_bytes(int nranks, size_t recv_rows_capacity, size_t row_elems,
+                                        coll_dtype_t dtype);
+int coll_all_to_all_v_ws(int nranks, const void *const *sendbufs, const int64_t *sendcounts,
+                         const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
+                         size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Uniform all-to-all -- all_to_all_single with equal splits (sglang PR 27492
  * digest; tutorial section 8.1's figure): sendbufs[s] holds nranks chunks of
  * count_per_peer elements, chunk d for rank d; rank d receives them ordered

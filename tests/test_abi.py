@@ -128,6 +128,35 @@ def test_moe_expert_workspace_validation(L):
     assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 0, 0, 16, NULL, 0, NULL) == 0
 
 
+def test_a2av_workspace_size_and_validation(L):
+    # rows of 7168 bf16 (896 sixteen-byte units), 262144 rows of capacity:
+    # 64 block entries + 917504 tile descriptors of 32 bytes
+    assert L.coll_all_to_all_v_workspace_bytes(8, 262144, 7168, 0) == (64 + 917504) * 32
+    assert L.coll_all_to_all_v_workspace_bytes(8, 262144, 7, 0) == 0     # 14-byte rows
+    assert L.coll_all_to_all_v_workspace_bytes(8, 0, 7168, 0) == 0       # no capacity
+    assert L.coll_all_to_all_v_workspace_bytes(17, 10, 8, 0) == 0        # R > 16
+    # the descriptor form starts at 192 MiB of receive capacity (the default
+    # of COLL_A2A_DESC_MIN_BYTES); below it no workspace is needed
+    K = (192 << 20) // 16                                                # rows of 8 bf16
+    assert "COLL_A2A_DESC_MIN_BYTES" not in os.environ
+    assert L.coll_all_to_all_v_workspace_bytes(2, K - 1, 8, 0) == 0
+    assert L.coll_all_to_all_v_workspace_bytes(2, 1, 8, 0) == 0
+    need = L.coll_all_to_all_v_workspace_bytes(2, K, 8, 0)
+    assert need == ((4 + K // 256) * 32 + 255) // 256 * 256
+    # tiles counted in whole groups of 32: one tile more adds a group
+    assert L.coll_all_to_all_v_workspace_bytes(2, K + 1, 8, 0) == \
+        ((4 + K // 256 + 32) * 32 + 255) // 256 * 256
+    t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    # a needed workspace that is NULL, misaligned or too small: rejected
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, NULL, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, 0x1010, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, 0x1000, need - 1,
+                                  NULL) == -1
+    # NULL tables rejected as in coll_all_to_all_v; rows of 0 elements: nothing to do
+    assert L.coll_all_to_all_v_ws(2, t, NULL, 0x200, t, 0x300, 8, 0, K, 0x1000, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 0, 0, K, NULL, 0, NULL) == 0
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(coll, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(coll, "_lib", None)

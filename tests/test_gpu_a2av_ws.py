@@ -1,0 +1,208 @@
+"""All-to-All-v in its descriptor form (coll_all_to_all_v_ws): the same
+exchange as coll_all_to_all_v, checked against the oracle and against the
+plain form bit for bit.
+
+The form runs from 192 MiB of receive capacity up (the default threshold);
+the capacity only sizes the launch, so small exchanges are sent through it
+with a capacity bound at the threshold.  Cases beyond the random-count
+parity tests (which run both forms):
+- rows received beyond the capacity (262 MB exchanges against a 192 MiB
+  bound: the tiles past the descriptors find their blocks in the table);
+- gapped receive layouts, all-empty counts;
+- the MoE exchange at full size (8 x 4096 x top-8, rows of 7168 bf16),
+  compared with the plain form;
+- rows that are not whole 16-byte units, and capacities below the
+  threshold: the plain form runs and the workspace is untouched;
+- HIP-graph capture and replay.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from collective_communication_amd import coll, synth
+from gpu_util import bits_equal, dev, host, poison_like, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    coll.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dc(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int64).reshape(-1)).cuda()
+
+
+def case(R, W, counts, gap=0, seed=0):
+    sd, rd = oracle.packed_displs(counts)
+    if gap:
+        rd = rd + gap * np.arange(R, dtype=np.int64)[None, :]
+    send_rows = counts.sum(axis=1)
+    recv_rows = (rd + counts.T).max(axis=1)
+    xs = [synth.random_bits(max(int(send_rows[s]), 1) * W, 2, 8100 + 31 * seed + s)
+          for s in range(R)]
+    sends = [dev(x) for x in xs]
+    recvs = [poison_like(torch.empty(max(int(recv_rows[d]), 1) * W, dtype=torch.bfloat16,
+                                     device="cuda")) for d in range(R)]
+    init = [host(r).copy() for r in recvs]
+    want = oracle.all_to_all_v([x[:int(send_rows[s]) * W] for s, x in enumerate(xs)], counts,
+                               sd, rd, [max(int(v), 1) for v in recv_rows], W,
+                               recvs=[a.copy() for a in init])
+    return sends, recvs, want, sd, rd
+
+
+DESC_MIN_BYTES = 192 << 20
+
+
+def desc_rows(row_bytes):
+    """Smallest receive capacity (rows) that takes the descriptor form."""
+    return -(-DESC_MIN_BYTES // row_bytes)
+
+
+def call_ws(R, sends, counts, sd, recvs, rd, W, capacity):
+    """coll_all_to_all_v_ws through the C ABI with an explicit capacity."""
+    L = coll.lib()
+    need = L.coll_all_to_all_v_workspace_bytes(R, capacity, W, 0)
+    ws = torch.full((max(need, 256),), 0xCD, dtype=torch.uint8, device="cuda")
+    keep = (dc(counts), dc(sd), dc(rd))
+    st = torch.cuda.current_stream().cuda_stream
+    rc = L.coll_all_to_all_v_ws(R, (ctypes.c_void_p * R)(*[t.data_ptr() for t in sends]),
+                                keep[0].data_ptr(), keep[1].data_ptr(),
+                                (ctypes.c_void_p * R)(*[t.data_ptr() for t in recvs]),
+                                keep[2].data_ptr(), W, 0, capacity, ws.data_ptr(),
+                                ws.numel(), st)
+    torch.cuda.synchronize()
+    return rc
+
+
+@pytest.mark.parametrize("R,W", [(8, 8), (16, 64)])
+def test_rows_beyond_the_capacity(R, W):
+    """About 1.3x the rows of a capacity at the threshold (262 MB moved)."""
+    say("a2av ws rows beyond capacity", R, W)
+    cap = desc_rows(W * 2)
+    g = np.random.default_rng(R * 7 + W)
+    counts = g.integers(0, 2 * (16 * cap // 10) // (R * R), size=(R, R)).astype(np.int64)
+    counts[g.random((R, R)) < 0.2] = 0
+    assert int(counts.sum()) > cap + 1024              # tiles past the last descriptor
+    sends, recvs, want, sd, rd = case(R, W, counts, seed=R)
+    assert call_ws(R, sends, counts, sd, recvs, rd, W, cap) == 0
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
+
+
+@pytest.mark.parametrize("gap,zero", [(3, False), (0, True), (5, False)])
+def test_gapped_and_empty(gap, zero):
+    R, W = 4, 8
+    say("a2av ws gapped/empty", gap, zero)
+    counts = (np.zeros((R, R), np.int64) if zero else
+              np.array([[3, 0, 2, 1], [1, 1, 1, 1], [0, 0, 0, 7], [2, 5, 0, 0]], np.int64) * 40)
+    sends, recvs, want, sd, rd = case(R, W, counts, gap=gap, seed=gap)
+    cap = max(sum(t.numel() // W for t in recvs), desc_rows(W * 2))
+    assert call_ws(R, sends, counts, sd, recvs, rd, W, cap) == 0
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
+
+
+def test_capacity_below_the_threshold_uses_the_plain_form():
+    R, W = 8, 64
+    say("a2av ws below threshold")
+    g = np.random.default_rng(4)
+    counts = g.integers(0, 60, size=(R, R)).astype(np.int64)
+    sends, recvs, want, sd, rd = case(R, W, counts, seed=4)
+    assert coll.all_to_all_v_workspace_bytes(sends, recvs, W) == 0
+    assert coll.all_to_all_v_workspace_bytes(sends, recvs, W, capacity=desc_rows(128)) > 0
+    ws = torch.full((256,), 0xCD, dtype=torch.uint8, device="cuda")
+    coll.all_to_all_v(sends, dc(counts), dc(sd), recvs, dc(rd), W, workspace=ws)
+    torch.cuda.synchronize()
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
+    assert bool((ws == 0xCD).all())               # untouched
+
+
+def test_rows_not_whole_units_use_the_plain_form():
+    R, W = 4, 3                                   # 6-byte rows
+    say("a2av ws fallback")
+    g = np.random.default_rng(2)
+    counts = g.integers(0, 50, size=(R, R)).astype(np.int64)
+    sends, recvs, want, sd, rd = case(R, W, counts, seed=2)
+    assert coll.all_to_all_v_workspace_bytes(sends, recvs, W) == 0
+    ws = torch.full((256,), 0xCD, dtype=torch.uint8, device="cuda")
+    coll.all_to_all_v(sends, dc(counts), dc(sd), recvs, dc(rd), W, workspace=ws)
+    torch.cuda.synchronize()
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), d
+    assert bool((ws == 0xCD).all())               # untouched
+
+
+def test_moe_exchange_full_size_matches_the_plain_form():
+    """8 ranks x 4096 tokens x top-8 of 256 (Zipf routing), rows of 7168 bf16:
+    dispatch and the transposed combine exchange, both forms bit for bit."""
+    R, E, T, K, H = 8, 256, 4096, 8, 7168
+    say("a2av ws moe full size")
+    ids = [synth.zipf_routing(T, E, K, seed=5100 + s)[0] for s in range(R)]
+    lay = oracle.moe_layout(ids, E)
+    sc, sd, rd = lay["sendcounts"], lay["sdispls"], lay["rdispls"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    sends = [torch.randn((T * K, H), generator=g, device="cuda").to(torch.bfloat16)
+             for _ in range(R)]
+    rows = sc.sum(axis=0)
+    a = [torch.empty((int(n), H), dtype=torch.bfloat16, device="cuda") for n in rows]
+    b = [torch.empty_like(t) for t in a]
+    ws = torch.empty(coll.all_to_all_v_workspace_bytes(sends, a, H), dtype=torch.uint8,
+                     device="cuda")
+    coll.all_to_all_v(sends, dc(sc), dc(sd), a, dc(rd), H)
+    coll.all_to_all_v(sends, dc(sc), dc(sd), b, dc(rd), H, workspace=ws)
+    torch.cuda.synchronize()
+    for d in range(R):
+        assert torch.equal(a[d].view(torch.int16), b[d].view(torch.int16)), d
+    back_a = [torch.empty_like(s) for s in sends]
+    back_b = [torch.empty_like(s) for s in sends]
+    ws2 = torch.empty(coll.all_to_all_v_workspace_bytes(b, back_b, H), dtype=torch.uint8,
+                      device="cuda")
+    coll.all_to_all_v(a, dc(sc.T), dc(rd), back_a, dc(sd), H)
+    coll.all_to_all_v(b, dc(sc.T), dc(rd), back_b, dc(sd), H, workspace=ws2)
+    torch.cuda.synchronize()
+    for s in range(R):
+        assert torch.equal(back_a[s].view(torch.int16), back_b[s].view(torch.int16)), s
+        assert torch.equal(back_b[s].view(torch.int16), sends[s].view(torch.int16)), s
+
+
+def test_graph_replays_the_descriptor_form():
+    R, W = 8, 64
+    say("a2av ws graph")
+    g = np.random.default_rng(11)
+    counts = g.integers(0, 200, size=(R, R)).astype(np.int64)
+    sends, recvs, want, sd, rd = case(R, W, counts, seed=11)
+    cap = desc_rows(W * 2)
+    ws = torch.empty(coll.all_to_all_v_workspace_bytes(sends, recvs, W, capacity=cap),
+                     dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    tabs = (dc(counts), dc(sd), dc(rd))
+    plan = coll.prepare(coll.all_to_all_v, sends, tabs[0], tabs[1], recvs, tabs[2], W,
+                        workspace=ws, capacity=cap)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        plan()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan()
+    for rep in range(3):
+        for r in recvs:
+            r.view(torch.int16).fill_(0x7FAB)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for d in range(R):
+            assert bits_equal(host(recvs[d]), want[d]), (rep, d)

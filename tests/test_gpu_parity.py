@@ -277,7 +277,7 @@ def test_broadcast(R, n, dtype, root):
 
 # ------------------------------------------------------------- All-to-All-v
 
-def a2av_case(R, W, dtype, counts, gap=0, seed=0):
+def a2av_case(R, W, dtype, counts, gap=0, seed=0, ws=False):
     sd, rd = oracle.packed_displs(counts)
     if gap:                                  # spread receive blocks apart
         rd = rd + gap * np.arange(R, dtype=np.int64)[None, :]
@@ -291,21 +291,31 @@ def a2av_case(R, W, dtype, counts, gap=0, seed=0):
     want = oracle.all_to_all_v(xs, counts, sd, rd, [max(int(v), 1) for v in recv_rows], W,
                                recvs=[a.copy() for a in init])
     dc = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int64).reshape(-1)).cuda()
-    coll.all_to_all_v(sends, dc(counts), dc(sd), recvs, dc(rd), W)
+    work = cap = None
+    if ws:                                   # the descriptor form (when it applies)
+        # a capacity bound at the form's 192 MiB threshold (it sizes the
+        # launch only), so that these small exchanges take the form too
+        row_bytes = W * sends[0].element_size()
+        if row_bytes % 16 == 0:
+            cap = max(sum(t.numel() // W for t in recvs), -(-(192 << 20) // row_bytes))
+        nb = max(coll.all_to_all_v_workspace_bytes(sends, recvs, W, capacity=cap), 256)
+        work = torch.full((nb,), 0xCD, dtype=torch.uint8, device="cuda")
+    coll.all_to_all_v(sends, dc(counts), dc(sd), recvs, dc(rd), W, workspace=work, capacity=cap)
     torch.cuda.synchronize()
     return recvs, want, sends, (counts, sd, rd)
 
 
+@pytest.mark.parametrize("ws", [False, True])
 @pytest.mark.parametrize("R", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("W", [1, 3, 8, 7168])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_a2av_random_counts(R, W, dtype):
-    say("a2av", R, W, dtype)
+def test_a2av_random_counts(R, W, dtype, ws):
+    say("a2av", R, W, dtype, ws)
     g = np.random.default_rng(R * 100 + W)
     hi = 40 if W < 1000 else 6
     counts = g.integers(0, hi + 1, size=(R, R)).astype(np.int64)
     counts[g.random((R, R)) < 0.2] = 0                   # empty blocks
-    recvs, want, _, _ = a2av_case(R, W, dtype, counts, seed=R + W)
+    recvs, want, _, _ = a2av_case(R, W, dtype, counts, seed=R + W, ws=ws)
     for d in range(R):
         assert bits_equal(host(recvs[d]), want[d]), f"dest {d}"
 
