@@ -125,7 +125,7 @@ def make_inputs(torch, synth, coll):
     for s, t in enumerate(W["moe_x"]):
         t.copy_(dev_bf16(synth.gaussian((T, H), 1.0, 5000 + s, "bf16")))
     # workspaces of the two exchanges' descriptor form (block table + one
-    # descriptor per 4 KiB tile of the receive capacity)
+    # descriptor per 1 KiB tile of the receive capacity)
     W["a2a_ws_d"] = torch.empty(coll.all_to_all_v_workspace_bytes(W["send"], W["recv"], H),
                                 dtype=torch.uint8, device="cuda")
     W["a2a_ws_c"] = torch.empty(coll.all_to_all_v_workspace_bytes(W["recv"], W["back"], H),

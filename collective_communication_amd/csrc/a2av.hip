@@ -413,28 +413,58 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
 
 // ---------------------------------------------- descriptor form (workspace)
 // For large exchanges with a caller workspace: a pre-kernel writes the block
-// table once and one descriptor per tile of kDescTile units (the tile's block:
-// its source and destination bases and its end), so a workgroup of the main
-// kernel starts with one scalar load instead of building the table itself.
-// MI355X, the MoE exchange (3.5 GiB each way): 1240 -> 1180 us for the main
-// kernel in a standalone comparison of the two.
-struct A2aDesc {
+// table once and one 16-byte descriptor per tile of kDescTile units (where
+// the tile's units come from and go to, and how many of them its first block
+// covers), so a workgroup of the main kernel starts with one scalar load
+// instead of building the table itself.
+struct A2aBlk {
   uint64_t sb, db;   // unit addresses of the block's first unit minus its start in the index space
-  uint64_t end;      // the block's end in the index space; 0: the tile is at or past the total
-  uint64_t more;     // 1 when the total runs past the last descriptor's tile (same in every entry)
+  uint64_t end;      // the block's end in the index space
+  uint64_t pad;
 };
-constexpr int kDescTile = 256;   // units per tile = lanes per workgroup (1 unit each)
+// A tile: src = unit address of its first unit (low kAddrBits) | the units
+// from there to the end of that unit's block, capped at kDescTile (high
+// bits); dst = unit address of the first unit's destination | bit 63 set when
+// the total runs past the last descriptor's tile (the same in every entry).
+// src == 0: the tile is at or past the total.
+struct A2aTile {
+  uint64_t src, dst;
+};
+constexpr int kAddrBits = 54;                   // unit addresses: byte addresses below 2^58
+constexpr uint64_t kAddrMask = (1ull << kAddrBits) - 1;
+
+// Lanes per workgroup and units per lane of the descriptor kernel.  MI355X,
+// R = 8, graph replay, the 3.5 GiB MoE exchange / 8 x 64 MiB of 16-byte rows
+// (32-byte descriptors then): 64 x 1 6405 / 6224 GB/s; 256 x 1 6347 / 6150;
+// 512 x 1 6277 / 6175; 128 x 1 6170 / 6112; 64 x 4 6333 / 6209; 256 x 2
+// 5890 / 5877.  Four one-wave workgroups sharing a 4 KiB tile's descriptor on
+// one XCD: 6346 / 6126.
+#ifndef COLL_DESC_LANES
+#define COLL_DESC_LANES 64
+#endif
+#ifndef COLL_DESC_U
+#define COLL_DESC_U 1
+#endif
+#ifndef COLL_DESC_BUILD_WGS
+#define COLL_DESC_BUILD_WGS 4
+#endif
+constexpr int kDescBuildWgs = COLL_DESC_BUILD_WGS;   // descriptor writers per CU
+constexpr int kDescLanes = COLL_DESC_LANES;
+constexpr int kDescU = COLL_DESC_U;
+constexpr int kDescTile = kDescLanes * kDescU;   // units per tile (and per descriptor)
+static_assert(kDescTile < (1 << (64 - kAddrBits)), "a tile's block coverage must fit its field");
 
 // Workgroups are handed to the 8 XCDs in turn (workgroup w to XCD w % 8), and
 // each XCD has its own L2.  Storing tile t's descriptor at desc_slot(t) puts
-// the four descriptors of one 128-byte line on tiles t, t+8, t+16, t+24 of the
-// same XCD, so each line is fetched from HBM once rather than once per XCD
-// (measured: 117 MB of extra reads on the 3.5 GiB MoE exchange in the
-// tile-order layout, the line count times 128 bytes).  A bijection on each
-// group of 32 tiles; the workspace holds whole groups.
-constexpr uint64_t kDescGroup = 32;
+// the eight descriptors of one 128-byte line on tiles t, t+8, ..., t+56 of
+// the same XCD, so each line is fetched from HBM once rather than once per
+// XCD (measured with 4 KiB tiles: 117 MB of extra reads on the 3.5 GiB MoE
+// exchange in tile order, the line count times 128 bytes).  It swaps two
+// 3-bit fields of t: a bijection on each group of 64 tiles and its own
+// inverse.  The workspace holds whole groups.
+constexpr uint64_t kDescGroup = 64;
 __device__ __forceinline__ uint64_t desc_slot(uint64_t t) {
-  return (t & ~(kDescGroup - 1)) | ((t & 7) << 2) | ((t >> 3) & 3);
+  return (t & ~(kDescGroup - 1)) | ((t & 7) << 3) | ((t >> 3) & 7);
 }
 
 // General table build (R <= 16, four blocks per lane of wave 0), as in a2av_body.
@@ -478,41 +508,54 @@ __device__ __forceinline__ void desc_table(const RankPtrs &p, int R, const int64
   }
 }
 
-// Thread t writes the descriptor of tile t; workgroup 0 also writes the
-// table (nb entries) for the main kernel's rare searches.
+// A resident grid: each workgroup builds the block table in LDS once, then
+// its threads write descriptor slots i, i + stride, ...  Workgroup 0 also
+// writes the table (nb entries) for the main kernel's rare searches.  MI355X,
+// the MoE exchange (56 MiB of descriptors): one workgroup per 256 tiles with
+// stores in tile order 28.6 us; 2 resident workgroups per CU 27.2 us; slot
+// order (contiguous stores per wave) with 4 per CU 21.6 us.
 template <int B>
 __global__ __launch_bounds__(kBlock) void a2av_desc_build(RankPtrs p, int R,
                                                           const int64_t *counts,
                                                           const int64_t *sdispls,
                                                           const int64_t *rdispls,
-                                                          uint64_t row_units, A2aDesc *desc,
-                                                          uint64_t ndesc, A2aDesc *blk) {
+                                                          uint64_t row_units, A2aTile *desc,
+                                                          uint64_t ndesc, A2aBlk *blk) {
   __shared__ uint64_t s_end[kMaxBlocks], s_src[kMaxBlocks], s_dst[kMaxBlocks];
   const int nb = R * R;
   if (threadIdx.x < 64) desc_table<B>(p, R, counts, sdispls, rdispls, row_units, s_end, s_src, s_dst);
   __syncthreads();
   if (blockIdx.x == 0)
-    for (int b = threadIdx.x; b < nb; b += kBlock) blk[b] = A2aDesc{s_src[b], s_dst[b], s_end[b], 0};
-  const uint64_t t = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (t >= ndesc) return;
-  const uint64_t x = t * kDescTile;
+    for (int b = threadIdx.x; b < nb; b += kBlock) blk[b] = A2aBlk{s_src[b], s_dst[b], s_end[b], 0};
   const uint64_t total = s_end[nb - 1];
-  const uint64_t more = total > ndesc * kDescTile ? 1 : 0;
-  A2aDesc dd{0, 0, 0, more};
-  if (x < total) {
-    int lo = 0;                                 // blocks ending at or before x
-    for (int step = kMaxBlocks; step > 0; step >>= 1) {
-      const int c = lo + step;
-      if (c <= nb && s_end[c - 1] <= x) lo = c;
+  const uint64_t more = total > ndesc * kDescTile ? 1ull << 63 : 0;
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  const uint64_t slots = (ndesc + kDescGroup - 1) / kDescGroup * kDescGroup;
+  // thread i writes slot i (a wave's stores are one contiguous 1 KiB); the
+  // slot map is its own inverse, so slot i holds tile desc_slot(i)
+  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < slots; i += stride) {
+    const uint64_t t = desc_slot(i);
+    if (t >= ndesc) continue;                   // a slot of the last group that no tile uses
+    const uint64_t x = t * kDescTile;
+    A2aTile dd{0, more};
+    if (x < total) {
+      int lo = 0;                               // blocks ending at or before x
+      for (int step = kMaxBlocks; step > 0; step >>= 1) {
+        const int c = lo + step;
+        if (c <= nb && s_end[c - 1] <= x) lo = c;
+      }
+      const uint64_t left = s_end[lo] - x;
+      const uint64_t cover = left < (uint64_t)kDescTile ? left : (uint64_t)kDescTile;
+      dd.src = ((s_src[lo] + x) & kAddrMask) | (cover << kAddrBits);
+      dd.dst = ((s_dst[lo] + x) & kAddrMask) | more;
     }
-    dd = A2aDesc{s_src[lo], s_dst[lo], s_end[lo], more};
+    desc[i] = dd;
   }
-  desc[desc_slot(t)] = dd;
 }
 
 // Block holding unit x from the table in the workspace (nb entries): the
 // index of the first block ending after x, nb when x is past the total.
-__device__ __forceinline__ int desc_find(const A2aDesc *blk, int nb, uint64_t x) {
+__device__ __forceinline__ int desc_find(const A2aBlk *blk, int nb, uint64_t x) {
   int lo = 0;
   for (int step = kMaxBlocks; step > 0; step >>= 1) {
     const int c = lo + step;
@@ -521,23 +564,41 @@ __device__ __forceinline__ int desc_find(const A2aDesc *blk, int nb, uint64_t x)
   return lo;
 }
 
-// Copies unit x of the tile whose first unit lies in block (sb, db, end); a
-// lane past the block's end finds its own block in the table.
+// Copies the lane's units x0 + u * kDescLanes of a tile whose first unit lies
+// in block (sb, db, end); a unit past the block's end finds its own block in
+// the table.  Located, then loaded, then stored.
 template <int B, bool NT>
-__device__ __forceinline__ void desc_unit(uint64_t sb, uint64_t db, uint64_t end,
-                                          const A2aDesc *blk, int nb, uint64_t x) {
+__device__ __forceinline__ void desc_units(uint64_t sb, uint64_t db, uint64_t end,
+                                           const A2aBlk *blk, int nb, uint64_t x0) {
   using U = typename UnitT<B>::T;
-  if (x >= end) {                               // the tile crosses into later blocks
-    const int lo = desc_find(blk, nb, x);
-    if (lo >= nb) return;                       // past the total
-    sb = blk[lo].sb;
-    db = blk[lo].db;
+  uint64_t sa[kDescU], da[kDescU];
+#pragma unroll
+  for (int u = 0; u < kDescU; u++) {
+    const uint64_t x = x0 + (uint64_t)u * kDescLanes;
+    uint64_t s = sb, d = db;
+    sa[u] = 0;
+    if (x >= end) {                             // the tile crosses into later blocks
+      const int lo = desc_find(blk, nb, x);
+      if (lo >= nb) continue;                   // past the total
+      s = blk[lo].sb;
+      d = blk[lo].db;
+    }
+    sa[u] = (s + x) * B;
+    da[u] = (d + x) * B;
   }
-  U v;
-  if constexpr (NT) v = __builtin_nontemporal_load(gconst<U>((sb + x) * B));
-  else v = *gconst<U>((sb + x) * B);
-  if constexpr (NT) __builtin_nontemporal_store(v, gmut<U>((db + x) * B));
-  else *gmut<U>((db + x) * B) = v;
+  U v[kDescU];
+#pragma unroll
+  for (int u = 0; u < kDescU; u++) {
+    if (!sa[u]) continue;
+    if constexpr (NT) v[u] = __builtin_nontemporal_load(gconst<U>(sa[u]));
+    else v[u] = *gconst<U>(sa[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kDescU; u++) {
+    if (!sa[u]) continue;
+    if constexpr (NT) __builtin_nontemporal_store(v[u], gmut<U>(da[u]));
+    else *gmut<U>(da[u]) = v[u];
+  }
 }
 
 // One workgroup per descriptor (the grid is exactly ndesc workgroups).  The
@@ -546,22 +607,22 @@ __device__ __forceinline__ void desc_unit(uint64_t sb, uint64_t db, uint64_t end
 // the MoE exchange).  When the capacity undercounts the rows, the tiles past
 // the last descriptor are looped over from the table.
 template <int B, bool NT>
-__global__ __launch_bounds__(kDescTile) void a2av_desc_kernel(const A2aDesc *__restrict__ desc,
-                                                              const A2aDesc *__restrict__ blk,
+__global__ __launch_bounds__(kDescLanes) void a2av_desc_kernel(const A2aTile *__restrict__ desc,
+                                                              const A2aBlk *__restrict__ blk,
                                                               int nb) {
-  const A2aDesc dd = desc[desc_slot(blockIdx.x)];
-  uint64_t sb = dd.sb, db = dd.db, end = dd.end, more = dd.more;
-  COLL_UNIFORM(sb);                             // one scalar load of the whole descriptor
-  COLL_UNIFORM(db);
-  COLL_UNIFORM(end);
-  COLL_UNIFORM(more);
-  if (end == 0) return;                         // at or past the total
-  desc_unit<B, NT>(sb, db, end, blk, nb, (uint64_t)blockIdx.x * kDescTile + threadIdx.x);
-  if (more == 0) return;
+  const A2aTile dd = desc[desc_slot(blockIdx.x)];
+  uint64_t src = dd.src, dst = dd.dst;
+  COLL_UNIFORM(src);                            // one scalar load of the whole descriptor
+  COLL_UNIFORM(dst);
+  if (src == 0) return;                         // at or past the total
+  const uint64_t t0 = (uint64_t)blockIdx.x * kDescTile;
+  desc_units<B, NT>((src & kAddrMask) - t0, (dst & kAddrMask) - t0, t0 + (src >> kAddrBits), blk,
+                    nb, t0 + threadIdx.x);
+  if ((dst >> 63) == 0) return;
   for (uint64_t t = (uint64_t)blockIdx.x + gridDim.x;; t += gridDim.x) {
     const int lo = desc_find(blk, nb, t * kDescTile);
     if (lo >= nb) return;
-    desc_unit<B, NT>(blk[lo].sb, blk[lo].db, blk[lo].end, blk, nb, t * kDescTile + threadIdx.x);
+    desc_units<B, NT>(blk[lo].sb, blk[lo].db, blk[lo].end, blk, nb, t * kDescTile + threadIdx.x);
   }
 }
 
@@ -632,33 +693,41 @@ size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_
   const uint64_t cap_units = (uint64_t)rows_capacity * (row_bytes / 16);
   const uint64_t ndesc = (cap_units + kDescTile - 1) / kDescTile;
   const uint64_t slots = (ndesc + kDescGroup - 1) / kDescGroup * kDescGroup;
-  return (((size_t)R * R + slots) * sizeof(A2aDesc) + 255) & ~(size_t)255;
+  return ((size_t)R * R * sizeof(A2aBlk) + slots * sizeof(A2aTile) + 255) & ~(size_t)255;
 }
 
 int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
                    const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
                    size_t rows_capacity, void *ws) {
-  uintptr_t bits = row_bytes;
-  for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
-  // rows that are not whole 16-byte units, or no capacity: the plain form
-  if (copy_unit(bits) != 16 || rows_capacity == 0)
+  uintptr_t bits = row_bytes, top = 0;
+  for (int r = 0; r < R; r++) {
+    bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
+    top |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
+  }
+  // rows that are not whole 16-byte units, no capacity, or buffers above the
+  // descriptors' address range: the plain form
+  if (copy_unit(bits) != 16 || rows_capacity == 0 || (top >> (kAddrBits + 3)) != 0)
     return launch_a2av(L, R, p, counts, sdispls, rdispls, row_bytes, rows_capacity);
   const uint64_t row_units = row_bytes / 16;
   const uint64_t cap_units = (uint64_t)rows_capacity * row_units;
   const uint64_t ndesc = (cap_units + kDescTile - 1) / kDescTile;
   if (ndesc == 0 || ndesc > 0x7FFFFFFFull)     // empty rows, or more tiles than one grid holds
     return launch_a2av(L, R, p, counts, sdispls, rdispls, row_bytes, rows_capacity);
-  A2aDesc *blk = reinterpret_cast<A2aDesc *>(ws);
-  A2aDesc *desc = blk + (size_t)R * R;
-  const uint64_t gb = (ndesc + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL((a2av_desc_build<16>), dim3((unsigned)(gb < 1 ? 1 : gb)), dim3(kBlock), 0,
-                     L.stream, p, R, counts, sdispls, rdispls, row_units, desc, ndesc, blk);
+  A2aBlk *blk = reinterpret_cast<A2aBlk *>(ws);
+  A2aTile *desc = reinterpret_cast<A2aTile *>(blk + (size_t)R * R);
+  // descriptor writers: a resident grid (COLL_DESC_BUILD_WGS per CU), no
+  // more workgroups than tiles' worth of threads
+  const uint64_t gneed = (ndesc + kBlock - 1) / kBlock;
+  const uint64_t gres = (uint64_t)L.num_cus * kDescBuildWgs;
+  const unsigned gb = (unsigned)(gneed < gres ? gneed : gres);
+  hipLaunchKernelGGL((a2av_desc_build<16>), dim3(gb), dim3(kBlock), 0, L.stream, p, R, counts,
+                     sdispls, rdispls, row_units, desc, ndesc, blk);
   const unsigned g = (unsigned)ndesc;
   if (L.a2a_nt)
-    hipLaunchKernelGGL((a2av_desc_kernel<16, true>), dim3(g), dim3(kDescTile), 0, L.stream, desc,
+    hipLaunchKernelGGL((a2av_desc_kernel<16, true>), dim3(g), dim3(kDescLanes), 0, L.stream, desc,
                        blk, R * R);
   else
-    hipLaunchKernelGGL((a2av_desc_kernel<16, false>), dim3(g), dim3(kDescTile), 0, L.stream, desc,
+    hipLaunchKernelGGL((a2av_desc_kernel<16, false>), dim3(g), dim3(kDescLanes), 0, L.stream, desc,
                        blk, R * R);
   return hip_status();
 }
