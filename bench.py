@@ -112,7 +112,6 @@ def make_inputs(torch, synth, coll):
     W["ec"] = torch.empty(R * E, dtype=torch.int32, device="cuda")
     W["pos"] = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(R)]
     W["ws"] = torch.empty(coll.moe_workspace_bytes(R, T, K, E), dtype=torch.uint8, device="cuda")
-    W["ews"] = torch.empty(coll.moe_expert_workspace_bytes(R, E), dtype=torch.uint8, device="cuda")
     # the routing is fixed, so the receive sizes are known once (outside timing)
     coll.moe_layout(ids, E, W["sc"], W["sd"], W["rd"], W["ec"], W["pos"], W["ws"])
     torch.cuda.synchronize()
@@ -124,6 +123,9 @@ def make_inputs(torch, synth, coll):
          (R, (T * K, H), bf), (R, (T, H), bf)])
     for s, t in enumerate(W["moe_x"]):
         t.copy_(dev_bf16(synth.gaussian((T, H), 1.0, 5000 + s, "bf16")))
+    # the test expert's workspace: entry tables + one descriptor per receive row
+    W["ews"] = torch.empty(coll.moe_expert_workspace_bytes(R, E, sum(t.shape[0] for t in W["recv"])),
+                           dtype=torch.uint8, device="cuda")
     # workspaces of the two exchanges' descriptor form (block table + one
     # descriptor per 1 KiB tile of the receive capacity)
     W["a2a_ws_d"] = torch.empty(coll.all_to_all_v_workspace_bytes(W["send"], W["recv"], H),

@@ -53,7 +53,7 @@ SIGNATURES = {
     "coll_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "coll_moe_layout": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
-    "coll_moe_expert_workspace_bytes": (_sz, [_i, _i]),
+    "coll_moe_expert_workspace_bytes": (_sz, [_i, _i, _sz]),
     "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _sz, _vp]),
     "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_dispatch": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
@@ -457,15 +457,19 @@ def moe_permute(xs, pos, sends, stream=None):
                   _table(pos, "pos"), T, K, H * mult, dt, _table(sends, "send"))
 
 
-def moe_expert_workspace_bytes(R: int, n_experts: int) -> int:
-    return int(lib().coll_moe_expert_workspace_bytes(R, n_experts))
+def moe_expert_workspace_bytes(R: int, n_experts: int, rows_capacity: int = 0) -> int:
+    """Workspace bytes of moe_expert_scale: the entry tables, plus 8 bytes per
+    receive row of ``rows_capacity`` for the row-descriptor path (the receive
+    buffers' rows together, as moe_expert_scale passes them)."""
+    return int(lib().coll_moe_expert_workspace_bytes(R, n_experts, rows_capacity))
 
 
 def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int, workspace,
                      stream=None):
     """Test expert y = rne(x * (1 + e/256)) in place on received bf16 rows.
     ``workspace``: a device tensor of at least moe_expert_workspace_bytes(R, E)
-    bytes (the layout's workspace may be reused once the layout is done)."""
+    bytes; moe_expert_workspace_bytes(R, E, rows) with rows = the receive
+    buffers' rows together selects the faster row-descriptor path."""
     R = _ranks(recvs, "moe_expert_scale")
     for r in recvs:
         if r.dtype != torch.bfloat16:

@@ -49,16 +49,6 @@ __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
   return x;
 }
 
-// Global-address-space views of an integer address (so the compiler emits
-// global_load / global_store rather than flat accesses).
-template <class U>
-__device__ __forceinline__ const __attribute__((address_space(1))) U *gconst(uint64_t a) {
-  return (const __attribute__((address_space(1))) U *)a;
-}
-template <class U>
-__device__ __forceinline__ __attribute__((address_space(1))) U *gmut(uint64_t a) {
-  return (__attribute__((address_space(1))) U *)a;
-}
 
 // SMALL: R <= 8, so the R * R <= 64 blocks fit one per lane of wave 0 and the
 // block search has a fixed depth (measured faster than the general form at

@@ -389,9 +389,10 @@ int coll_moe_permute(int R, const void *const *x, const int32_t *const *pos, int
                             hidden * dtype_size(dtype), ss);
 }
 
-size_t coll_moe_expert_workspace_bytes(int R, int n_experts) {
+size_t coll_moe_expert_workspace_bytes(int R, int n_experts, size_t recv_rows_capacity) {
   if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0) return 0;
-  return moe_expert_workspace_bytes(R, n_experts);
+  if (recv_rows_capacity > ((size_t)1 << 48)) return 0;
+  return moe_expert_workspace_bytes(R, n_experts, recv_rows_capacity);
 }
 
 int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_counts,
@@ -404,13 +405,13 @@ int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_co
   if (hidden == 0) return COLL_OK;
   if (!expert_counts || !rdispls || hidden >= ((size_t)1 << 31)) return COLL_ERR_INVALID_ARG;
   if (!workspace || ((uintptr_t)workspace & 255) != 0 ||
-      workspace_bytes < moe_expert_workspace_bytes(R, n_experts))
+      workspace_bytes < moe_expert_table_bytes(R, n_experts))
     return COLL_ERR_INVALID_ARG;
   MutPtrTable rs{};
   if (!fill_out(R, recvbufs, rs.p)) return COLL_ERR_INVALID_ARG;
   if (recv_rows_capacity > ((size_t)1 << 48) / hidden) return COLL_ERR_INVALID_ARG;
   return launch_moe_expert_scale(launch_ctx(stream), R, rs, expert_counts, rdispls, n_experts,
-                                 hidden, recv_rows_capacity, workspace);
+                                 hidden, recv_rows_capacity, workspace, workspace_bytes);
 }
 
 int coll_moe_combine(int R, const void *const *back, const int32_t *const *pos,

@@ -296,6 +296,17 @@ __device__ __forceinline__ uint64_t fdiv64(uint64_t n, const FastDiv64 &f) {
   return (__umul64hi(n, f.m) + n) >> f.s;
 }
 
+// Global-address-space views of an integer address (so the compiler emits
+// global_load / global_store rather than flat accesses).
+template <class U>
+__device__ __forceinline__ const __attribute__((address_space(1))) U *gconst(uint64_t a) {
+  return (const __attribute__((address_space(1))) U *)a;
+}
+template <class U>
+__device__ __forceinline__ __attribute__((address_space(1))) U *gmut(uint64_t a) {
+  return (__attribute__((address_space(1))) U *)a;
+}
+
 // ----------------------------------------------------------- copy units
 // Widest power-of-two unit (<= 16 bytes) a copy can use, as a type.
 template <int B> struct UnitT;
@@ -436,7 +447,8 @@ int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *cou
 
 constexpr int kMoeMaxExperts = 1024;
 size_t moe_workspace_bytes(int R, int T, int K, int E);
-size_t moe_expert_workspace_bytes(int R, int E);
+size_t moe_expert_table_bytes(int R, int E);
+size_t moe_expert_workspace_bytes(int R, int E, size_t rows_capacity);
 int launch_moe_layout(const Launch &L, int R, const PtrTable &ids, int T, int K, int E,
                       int64_t *sendcounts, int64_t *sdispls, int64_t *rdispls,
                       int32_t *expert_counts, const MutPtrTable &pos, void *ws);
@@ -444,7 +456,7 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
                        int K, size_t row_bytes, const MutPtrTable &send);
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
-                            size_t hidden, size_t rows_capacity, void *ws);
+                            size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes);
 int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTable &pos,
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
 int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,

@@ -312,8 +312,11 @@ int coll_moe_permute(int nranks, const void *const *x, const int32_t *const *pos
                      void *const *sendbufs, void *stream);
 
 /* Bytes of device workspace coll_moe_expert_scale needs (0 on invalid sizes):
- * two int64 tables of nranks * n_experts entries, rounded up to 256 bytes. */
-size_t coll_moe_expert_workspace_bytes(int nranks, int n_experts);
+ * two int64 tables of nranks * n_experts entries, rounded up to 256 bytes,
+ * then 8 bytes per row of recv_rows_capacity (rounded up to 256) for the row
+ * descriptors of the faster path.  With recv_rows_capacity = 0 the size is
+ * the tables alone, the least any call accepts. */
+size_t coll_moe_expert_workspace_bytes(int nranks, int n_experts, size_t recv_rows_capacity);
 
 /*
  * Test expert used to exercise the round trip: each received bf16 row of
@@ -323,14 +326,20 @@ size_t coll_moe_expert_workspace_bytes(int nranks, int n_experts);
  * order, expert_counts[s*E+e] rows each (expert_counts and rdispls: DEVICE
  * arrays, the outputs of coll_moe_layout).
  * workspace: DEVICE, 256-byte aligned, at least
- * coll_moe_expert_workspace_bytes(nranks, n_experts) bytes; it is
- * overwritten (a row-prefix table built on the device), so calls that may
- * run concurrently need workspaces of their own.  The layout's workspace may
- * be reused once coll_moe_layout has completed on the same stream.
+ * coll_moe_expert_workspace_bytes(nranks, n_experts, 0) bytes; it is
+ * overwritten (a row-prefix table built on the device, and row descriptors),
+ * so calls that may run concurrently need workspaces of their own.  The
+ * layout's workspace may be reused once coll_moe_layout has completed on the
+ * same stream, if it is large enough.
  * recv_rows_capacity: as for coll_all_to_all_v, an upper bound of the rows
- * received by all ranks together; it only sizes the launch (one workgroup per
- * tile of the bound, 0 = unknown: a resident grid) and never addresses
- * memory, so a wrong bound costs time, not correctness.
+ * received by all ranks together; it only sizes the launch and never
+ * addresses memory, so a wrong bound costs time, not correctness.  Rows whose
+ * hidden is a multiple of 8 with 16-byte aligned buffers, a nonzero capacity,
+ * a workspace of coll_moe_expert_workspace_bytes(nranks, n_experts,
+ * recv_rows_capacity) bytes and nranks * n_experts <= 8192 take the faster
+ * path: a pre-kernel writes one descriptor per row of the capacity and one
+ * wave per (row, 64-unit segment) scales it.  Otherwise one workgroup per
+ * tile of the bound searches the table (0 = unknown: a resident grid).
  * Errors: COLL_ERR_INVALID_ARG for a NULL or misaligned workspace, a smaller
  * workspace_bytes, n_experts outside [1, 1024] or not a multiple of nranks,
  * NULL tables or receive buffers; COLL_ERR_UNSUPPORTED for a dtype other

@@ -107,15 +107,20 @@ def test_moe_workspace_and_layout_validation(L):
 
 
 def test_moe_expert_workspace_validation(L):
-    # two int64 tables of R*E entries, rounded up to 256 bytes
-    assert L.coll_moe_expert_workspace_bytes(8, 256) == 8 * 256 * 16
-    assert L.coll_moe_expert_workspace_bytes(2, 4) == 256
-    assert L.coll_moe_expert_workspace_bytes(16, 1024) == 16 * 1024 * 16
-    assert L.coll_moe_expert_workspace_bytes(8, 250) == 0       # E % R != 0
-    assert L.coll_moe_expert_workspace_bytes(8, 2048) == 0      # E > 1024
-    assert L.coll_moe_expert_workspace_bytes(17, 17) == 0       # R > 16
+    # two int64 tables of R*E entries, rounded up to 256 bytes ...
+    assert L.coll_moe_expert_workspace_bytes(8, 256, 0) == 8 * 256 * 16
+    assert L.coll_moe_expert_workspace_bytes(2, 4, 0) == 256
+    assert L.coll_moe_expert_workspace_bytes(16, 1024, 0) == 16 * 1024 * 16
+    # ... then 8 bytes per row of the capacity, rounded up to 256
+    assert L.coll_moe_expert_workspace_bytes(8, 256, 262144) == 8 * 256 * 16 + 262144 * 8
+    assert L.coll_moe_expert_workspace_bytes(2, 4, 1) == 256 + 256
+    assert L.coll_moe_expert_workspace_bytes(2, 4, 33) == 256 + 512
+    assert L.coll_moe_expert_workspace_bytes(8, 250, 0) == 0    # E % R != 0
+    assert L.coll_moe_expert_workspace_bytes(8, 2048, 0) == 0   # E > 1024
+    assert L.coll_moe_expert_workspace_bytes(17, 17, 0) == 0    # R > 16
+    assert L.coll_moe_expert_workspace_bytes(2, 4, 1 << 62) == 0  # absurd capacity
     t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
-    need = L.coll_moe_expert_workspace_bytes(2, 4)
+    need = L.coll_moe_expert_workspace_bytes(2, 4, 0)           # the least any call accepts
     # NULL, misaligned or too small workspace -> rejected before any launch
     assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, NULL, need, NULL) == -1
     assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, 0x1008, need, NULL) == -1

@@ -380,7 +380,9 @@ def moe_gpu(xs, ids, ws, E):
     coll.all_to_all_v(sends, sc, sd, recvs, rd, H)
     torch.cuda.synchronize()
     recvs_h = [host(r).copy() for r in recvs]
-    ews = torch.empty(coll.moe_expert_workspace_bytes(R, E), dtype=torch.uint8, device="cuda")
+    rows_cap = sum(r.shape[0] for r in recvs)         # the row-descriptor path
+    ews = torch.empty(coll.moe_expert_workspace_bytes(R, E, rows_cap), dtype=torch.uint8,
+                      device="cuda")
     coll.moe_expert_scale(recvs, ec, rd, E, H, ews)
     torch.cuda.synchronize()
     ys_h = [host(r).copy() for r in recvs]
