@@ -205,8 +205,9 @@ int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *se
                       void *stream);
 
 /*
- * All-to-All-v with a caller workspace: the same exchange and arguments as
- * coll_all_to_all_v, faster for large exchanges.  A first kernel writes the
+ * All-to-All-v with a caller workspace -- tutorial sections 8.1-8.2, the same
+ * exchange, result and arguments as coll_all_to_all_v, faster for large
+ * exchanges.  A first kernel writes the
  * block table and, for every tile of 64 sixteen-byte units (1 KiB) of the
  * receive capacity, where that tile's units come from and go to; the copy
  * kernel then starts each tile with one load of it instead of building the
