@@ -701,6 +701,9 @@ __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(PtrTabl
 // The send blocks of source s (its row of the layout), staged in LDS once per
 // workgroup: send slots [lo[d], hi[d]) go to rank d, whose receive rows start
 // at rd[d].  A slot's destination is found by a wave-uniform scan over d.
+// The fused dispatch (4 waves per workgroup) stages its source's blocks in
+// LDS once per workgroup; scanning them per slot measured faster there than
+// per-wave lane copies (761 against 807 us at the MoE shape).
 struct SrcBlocks {
   int64_t lo[COLL_MAX_RANKS];
   int64_t hi[COLL_MAX_RANKS];
@@ -732,6 +735,58 @@ __device__ __forceinline__ int64_t recv_row_of(const SrcBlocks &b, int R, int64_
   }
   d = -1;
   return 0;
+}
+
+// The fused combine (one wave per workgroup): lane q < R of a wave holds
+// block q of source s: its send slots [lo, hi), the offset from a slot to its
+// receive row (rdispls[q][s] - lo) and rank q's receive buffer; the other
+// lanes hold an empty block.  Loaded per wave from clamped indices (no LDS,
+// no barrier), so locating a slot is one ballot and two lane reads, with no
+// memory access (the LDS scan waited on each read in turn, R reads per slot,
+// then loaded the buffer pointer: 751-758 against 741-745 us at the MoE
+// shape).
+struct SrcLane {
+  int64_t lo, hi, off;
+  uint64_t base;
+};
+
+template <class Table>
+__device__ __forceinline__ SrcLane load_src_lane(int R, int s, const Table &recv,
+                                                 const int64_t *sendcounts,
+                                                 const int64_t *sdispls,
+                                                 const int64_t *rdispls) {
+  const int q = threadIdx.x & 63;
+  const int qq = q < R ? q : 0;
+  const int64_t a = sdispls[s * R + qq], c = sendcounts[s * R + qq], r = rdispls[qq * R + s];
+  SrcLane b;
+  b.lo = q < R ? a : 1;
+  b.hi = q < R ? a + c : 0;
+  b.off = r - a;
+  b.base = reinterpret_cast<uintptr_t>(recv.p[qq]);
+  return b;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The receive row of the wave-uniform send slot `slot` and its buffer
+// (`base`, 0 for a rank that receives nothing); d = the first block holding
+// the slot, -1 when none does (only a corrupt layout).  The whole wave must
+// be active.
+__device__ __forceinline__ int64_t recv_row_lane(const SrcLane &b, int64_t slot, int &d,
+                                                 uint64_t &base) {
+  const uint64_t m = __ballot(slot >= b.lo && slot < b.hi);
+  if (m == 0) {
+    d = -1;
+    base = 0;
+    return 0;
+  }
+  d = (int)__builtin_ctzll(m);
+  base = readlane64(b.base, d);
+  return slot + (int64_t)readlane64((uint64_t)b.off, d);
 }
 
 // recv[d][rdispls[d][s] + pos - sdispls[s][d]] = x[s][t] for every k: the
@@ -799,11 +854,10 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
     uint32_t upr, int nseg) {
   constexpr int kChunk = 8;
   constexpr int UN = (G == 8) ? kCombineRecvU : 1;
-  __shared__ SrcBlocks blk;
   const int s = blockIdx.y;
-  load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls);
   const RowItem it = row_item<kCombineRecvWaves>(T, nseg);
   if (!it.valid) return;
+  const SrcLane bl = load_src_lane(R, s, recv, sendcounts, sdispls, rdispls);
   const int lane = threadIdx.x & 63;
   const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
   const float *wk = reinterpret_cast<const float *>(wts.p[s]) + (size_t)it.t * K;
@@ -833,11 +887,10 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
         live[c] = false;
         if (k0 + c < K) {
           int d;
-          const int64_t row = recv_row_of(blk, R, sl[c], d);
-          live[c] = d >= 0 && recv.p[__builtin_amdgcn_readfirstlane(d >= 0 ? d : 0)] != nullptr;
-          if (live[c])
-            rowp[c] = reinterpret_cast<const uint16_t *>(
-                          recv.p[__builtin_amdgcn_readfirstlane(d)]) + (size_t)row * upr * 8;
+          uint64_t bp;
+          const int64_t row = recv_row_lane(bl, sl[c], d, bp);
+          live[c] = d >= 0 && bp != 0;
+          if (live[c]) rowp[c] = reinterpret_cast<const uint16_t *>(bp) + (size_t)row * upr * 8;
           if constexpr (EXPERT) sc[c] = 1.0f + (float)ev[c] / 256.0f;
         } else {
           wgt[c] = 0.0f;
@@ -883,17 +936,15 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
     }
   } else {
     const uint32_t u = u0;
-    if (u < upr) {
+    const bool in = u < upr;
+    {
       float acc = 0.0f;
       for (int k = 0; k < K; k++) {
-        int d;
-        const int64_t row = recv_row_of(blk, R, __builtin_amdgcn_readfirstlane(pk[k]), d);
+        int d;                                     // located with the whole wave active
+        uint64_t bp;
+        const int64_t row = recv_row_lane(bl, __builtin_amdgcn_readfirstlane(pk[k]), d, bp);
         uint32_t y = 0u;
-        if (d >= 0) {
-          const uint16_t *rp = reinterpret_cast<const uint16_t *>(
-              recv.p[__builtin_amdgcn_readfirstlane(d)]);
-          if (rp) y = rp[(size_t)row * upr + u];
-        }
+        if (in && d >= 0 && bp != 0) y = reinterpret_cast<const uint16_t *>(bp)[(size_t)row * upr + u];
         if constexpr (EXPERT) {
           const float sc = 1.0f + (float)__builtin_amdgcn_readfirstlane(ek[k]) / 256.0f;
           y = pack_bf16(bf16_lo(y) * sc, 0.0f) & 0xFFFFu;
@@ -901,7 +952,7 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
         const float prod = wk[k] * bf16_lo(y);
         acc = (k == 0) ? prod : acc + prod;
       }
-      o[(size_t)it.t * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
+      if (in) o[(size_t)it.t * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
     }
   }
 }
