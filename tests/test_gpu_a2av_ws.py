@@ -11,8 +11,9 @@ parity tests (which run both forms):
 - gapped receive layouts, all-empty counts;
 - the MoE exchange at full size (8 x 4096 x top-8, rows of 7168 bf16),
   compared with the plain form;
-- rows that are not whole 16-byte units, and capacities below the
-  threshold: the plain form runs and the workspace is untouched;
+- rows that are not whole 16-byte units, buffers off 16-byte alignment,
+  and capacities below the threshold: the plain form runs and the workspace
+  is untouched;
 - HIP-graph capture and replay.
 """
 import ctypes
@@ -140,6 +141,37 @@ def test_rows_not_whole_units_use_the_plain_form():
     for d in range(R):
         assert bits_equal(host(recvs[d]), want[d]), d
     assert bool((ws == 0xCD).all())               # untouched
+
+
+def test_misaligned_buffers_use_the_plain_form():
+    """16-byte rows, a capacity above the threshold, but a receive buffer 8
+    bytes off 16-byte alignment: the plain form runs (the descriptors address
+    whole 16-byte units) and the workspace is not touched."""
+    R, W = 4, 8
+    say("a2av ws misaligned")
+    g = np.random.default_rng(6)
+    counts = g.integers(0, 50, size=(R, R)).astype(np.int64)
+    sends, recvs, want, sd, rd = case(R, W, counts, seed=6)
+    shifted = []
+    for r in recvs:                                   # same contents, 8 bytes further on
+        big = torch.empty(r.numel() + 4, dtype=torch.bfloat16, device="cuda")
+        big[4:].copy_(r)
+        shifted.append(big)
+    cap = desc_rows(W * 2)
+    need = coll.lib().coll_all_to_all_v_workspace_bytes(R, cap, W, 0)
+    assert need > 0
+    ws = torch.full((need,), 0xCD, dtype=torch.uint8, device="cuda")
+    keep = (dc(counts), dc(sd), dc(rd))
+    rc = coll.lib().coll_all_to_all_v_ws(
+        R, (ctypes.c_void_p * R)(*[t.data_ptr() for t in sends]), keep[0].data_ptr(),
+        keep[1].data_ptr(), (ctypes.c_void_p * R)(*[t.data_ptr() + 8 for t in shifted]),
+        keep[2].data_ptr(), W, 0, cap, ws.data_ptr(), need,
+        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    for d in range(R):
+        assert bits_equal(host(shifted[d][4:]), want[d]), d
+    assert bool((ws == 0xCD).all())
 
 
 def test_moe_exchange_full_size_matches_the_plain_form():
