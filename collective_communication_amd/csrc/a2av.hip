@@ -403,29 +403,22 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
 
 // ---------------------------------------------- descriptor form (workspace)
 // For large exchanges with a caller workspace: a pre-kernel writes the block
-// table once and one 16-byte descriptor per tile of kDescTile units (where
-// the tile's units come from and go to, and how many of them its first block
-// covers), so a workgroup of the main kernel starts with one scalar load
-// instead of building the table itself.
+// table once and, per tile of kDescTile units, the index of the block holding
+// the tile's first unit (16 bits; 0xFFFF: at or past the total).  A
+// workgroup of the main kernel then starts with two scalar loads in a row,
+// its tile's index and that block's 32-byte entry (a table of at most 8 KiB
+// that stays in the scalar cache), instead of building the table itself.
+// 16-byte descriptors holding both addresses (one load, 8x the bytes) measured
+// 0.2-0.8% slower at the MoE shape, 32-byte ones slower again.
 struct A2aBlk {
   uint64_t sb, db;   // unit addresses of the block's first unit minus its start in the index space
   uint64_t end;      // the block's end in the index space
-  uint64_t pad;
+  uint64_t more;     // 1 when the total runs past the last descriptor's tile (same in every entry)
 };
-// A tile: src = unit address of its first unit (low kAddrBits) | the units
-// from there to the end of that unit's block, capped at kDescTile (high
-// bits); dst = unit address of the first unit's destination | bit 63 set when
-// the total runs past the last descriptor's tile (the same in every entry).
-// src == 0: the tile is at or past the total.
-struct A2aTile {
-  uint64_t src, dst;
-};
-constexpr int kAddrBits = 54;                   // unit addresses: byte addresses below 2^58
-constexpr uint64_t kAddrMask = (1ull << kAddrBits) - 1;
 
 // Lanes per workgroup and units per lane of the descriptor kernel.  MI355X,
 // R = 8, graph replay, the 3.5 GiB MoE exchange / 8 x 64 MiB of 16-byte rows
-// (32-byte descriptors then): 64 x 1 6405 / 6224 GB/s; 256 x 1 6347 / 6150;
+// (with 32-byte descriptors): 64 x 1 6405 / 6224 GB/s; 256 x 1 6347 / 6150;
 // 512 x 1 6277 / 6175; 128 x 1 6170 / 6112; 64 x 4 6333 / 6209; 256 x 2
 // 5890 / 5877.  Four one-wave workgroups sharing a 4 KiB tile's descriptor on
 // one XCD: 6346 / 6126.
@@ -442,19 +435,20 @@ constexpr int kDescBuildWgs = COLL_DESC_BUILD_WGS;   // descriptor writers per C
 constexpr int kDescLanes = COLL_DESC_LANES;
 constexpr int kDescU = COLL_DESC_U;
 constexpr int kDescTile = kDescLanes * kDescU;   // units per tile (and per descriptor)
-static_assert(kDescTile < (1 << (64 - kAddrBits)), "a tile's block coverage must fit its field");
 
 // Workgroups are handed to the 8 XCDs in turn (workgroup w to XCD w % 8), and
-// each XCD has its own L2.  Storing tile t's descriptor at desc_slot(t) puts
-// the eight descriptors of one 128-byte line on tiles t, t+8, ..., t+56 of
-// the same XCD, so each line is fetched from HBM once rather than once per
-// XCD (measured with 4 KiB tiles: 117 MB of extra reads on the 3.5 GiB MoE
-// exchange in tile order, the line count times 128 bytes).  It swaps two
-// 3-bit fields of t: a bijection on each group of 64 tiles and its own
-// inverse.  The workspace holds whole groups.
-constexpr uint64_t kDescGroup = 64;
+// each XCD has its own L2.  Storing tile t's index at desc_slot(t) puts the
+// 64 indices of one 128-byte line on tiles t, t+8, ..., t+504 of one XCD, so
+// each line is fetched from HBM once rather than once per XCD (measured with
+// 32-byte descriptors in tile order: 117 MB of extra reads on the 3.5 GiB MoE
+// exchange, the line count times 128 bytes).  A bijection on each group of
+// 512 tiles; desc_tile is its inverse.  The workspace holds whole groups.
+constexpr uint64_t kDescGroup = 512;
 __device__ __forceinline__ uint64_t desc_slot(uint64_t t) {
-  return (t & ~(kDescGroup - 1)) | ((t & 7) << 3) | ((t >> 3) & 7);
+  return (t & ~(kDescGroup - 1)) | ((t & 7) << 6) | ((t >> 3) & 63);
+}
+__device__ __forceinline__ uint64_t desc_tile(uint64_t i) {
+  return (i & ~(kDescGroup - 1)) | ((i & 63) << 3) | ((i >> 6) & 7);
 }
 
 // General table build (R <= 16, four blocks per lane of wave 0), as in a2av_body.
@@ -495,51 +489,6 @@ __device__ __forceinline__ void desc_table(const RankPtrs &p, int R, const int64
       start += len[j];
       s_end[b] = start;
     }
-  }
-}
-
-// A resident grid: each workgroup builds the block table in LDS once, then
-// its threads write descriptor slots i, i + stride, ...  Workgroup 0 also
-// writes the table (nb entries) for the main kernel's rare searches.  MI355X,
-// the MoE exchange (56 MiB of descriptors): one workgroup per 256 tiles with
-// stores in tile order 28.6 us; 2 resident workgroups per CU 27.2 us; slot
-// order (contiguous stores per wave) with 4 per CU 21.6 us.
-template <int B>
-__global__ __launch_bounds__(kBlock) void a2av_desc_build(RankPtrs p, int R,
-                                                          const int64_t *counts,
-                                                          const int64_t *sdispls,
-                                                          const int64_t *rdispls,
-                                                          uint64_t row_units, A2aTile *desc,
-                                                          uint64_t ndesc, A2aBlk *blk) {
-  __shared__ uint64_t s_end[kMaxBlocks], s_src[kMaxBlocks], s_dst[kMaxBlocks];
-  const int nb = R * R;
-  if (threadIdx.x < 64) desc_table<B>(p, R, counts, sdispls, rdispls, row_units, s_end, s_src, s_dst);
-  __syncthreads();
-  if (blockIdx.x == 0)
-    for (int b = threadIdx.x; b < nb; b += kBlock) blk[b] = A2aBlk{s_src[b], s_dst[b], s_end[b], 0};
-  const uint64_t total = s_end[nb - 1];
-  const uint64_t more = total > ndesc * kDescTile ? 1ull << 63 : 0;
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-  const uint64_t slots = (ndesc + kDescGroup - 1) / kDescGroup * kDescGroup;
-  // thread i writes slot i (a wave's stores are one contiguous 1 KiB); the
-  // slot map is its own inverse, so slot i holds tile desc_slot(i)
-  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < slots; i += stride) {
-    const uint64_t t = desc_slot(i);
-    if (t >= ndesc) continue;                   // a slot of the last group that no tile uses
-    const uint64_t x = t * kDescTile;
-    A2aTile dd{0, more};
-    if (x < total) {
-      int lo = 0;                               // blocks ending at or before x
-      for (int step = kMaxBlocks; step > 0; step >>= 1) {
-        const int c = lo + step;
-        if (c <= nb && s_end[c - 1] <= x) lo = c;
-      }
-      const uint64_t left = s_end[lo] - x;
-      const uint64_t cover = left < (uint64_t)kDescTile ? left : (uint64_t)kDescTile;
-      dd.src = ((s_src[lo] + x) & kAddrMask) | (cover << kAddrBits);
-      dd.dst = ((s_dst[lo] + x) & kAddrMask) | more;
-    }
-    desc[i] = dd;
   }
 }
 
@@ -591,24 +540,72 @@ __device__ __forceinline__ void desc_units(uint64_t sb, uint64_t db, uint64_t en
   }
 }
 
-// One workgroup per descriptor (the grid is exactly ndesc workgroups).  The
-// descriptor is read before any store, so it comes in through the scalar
-// cache; a loop kept it a vector load behind a wait and cost 20% (MI355X,
-// the MoE exchange).  When the capacity undercounts the rows, the tiles past
-// the last descriptor are looped over from the table.
+// A resident grid: each workgroup builds the block table in LDS once, then
+// thread i writes slots 2i and 2i+1 (one 32-bit store; a wave's stores are
+// contiguous), i += stride.  Workgroup 0 also writes the table.  MI355X, the
+// MoE exchange with 16-byte descriptors: one workgroup per 256 tiles storing
+// in tile order 28.6 us; 2 resident workgroups per CU 27.2 us; slot order
+// with 4 per CU 21.6 us, and 8, 16 or one per 256 slots within 1% of that.
+template <int B>
+__global__ __launch_bounds__(kBlock) void a2av_desc_build(RankPtrs p, int R, const int64_t *counts,
+                                                         const int64_t *sdispls,
+                                                         const int64_t *rdispls,
+                                                         uint64_t row_units, uint32_t *idx,
+                                                         uint64_t ndesc, A2aBlk *blk) {
+  __shared__ uint64_t s_end[kMaxBlocks], s_src[kMaxBlocks], s_dst[kMaxBlocks];
+  const int nb = R * R;
+  if (threadIdx.x < 64) desc_table<B>(p, R, counts, sdispls, rdispls, row_units, s_end, s_src, s_dst);
+  __syncthreads();
+  const uint64_t total = s_end[nb - 1];
+  const uint64_t more = total > ndesc * kDescTile ? 1 : 0;
+  if (blockIdx.x == 0)
+    for (int b = threadIdx.x; b < nb; b += kBlock) blk[b] = A2aBlk{s_src[b], s_dst[b], s_end[b], more};
+  const uint64_t pairs = (ndesc + kDescGroup - 1) / kDescGroup * kDescGroup / 2;
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < pairs; i += stride) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint64_t t = desc_tile(2 * i + h);
+      uint32_t v = 0xFFFFu;
+      const uint64_t x = t * kDescTile;
+      if (t < ndesc && x < total) {
+        int lo = 0;                             // blocks ending at or before x
+        for (int step = kMaxBlocks; step > 0; step >>= 1) {
+          const int c = lo + step;
+          if (c <= nb && s_end[c - 1] <= x) lo = c;
+        }
+        v = (uint32_t)lo;
+      }
+      w |= v << (16 * h);
+    }
+    idx[i] = w;
+  }
+}
+
+// One workgroup per tile (the grid is exactly ndesc workgroups).  Both loads
+// are made before any store, so they go through the scalar cache: inside a
+// grid-stride loop the descriptor became a vector load behind a wait and cost
+// 20% (MI355X, the MoE exchange).  When the capacity undercounts the rows,
+// the tiles past the last descriptor are looped over from the table.
 template <int B, bool NT>
-__global__ __launch_bounds__(kDescLanes) void a2av_desc_kernel(const A2aTile *__restrict__ desc,
+__global__ __launch_bounds__(kDescLanes) void a2av_desc_kernel(const uint32_t *__restrict__ idx,
                                                               const A2aBlk *__restrict__ blk,
                                                               int nb) {
-  const A2aTile dd = desc[desc_slot(blockIdx.x)];
-  uint64_t src = dd.src, dst = dd.dst;
-  COLL_UNIFORM(src);                            // one scalar load of the whole descriptor
-  COLL_UNIFORM(dst);
-  if (src == 0) return;                         // at or past the total
+  const uint64_t sl = desc_slot(blockIdx.x);
+  uint32_t w = idx[sl >> 1];
+  COLL_UNIFORM(w);
+  const uint32_t b = (sl & 1) ? (w >> 16) : (w & 0xFFFFu);
+  if (b == 0xFFFFu) return;                     // at or past the total
+  const A2aBlk e = blk[b];
+  uint64_t sb = e.sb, db = e.db, end = e.end, more = e.more;
+  COLL_UNIFORM(sb);                             // one scalar load of the entry
+  COLL_UNIFORM(db);
+  COLL_UNIFORM(end);
+  COLL_UNIFORM(more);
   const uint64_t t0 = (uint64_t)blockIdx.x * kDescTile;
-  desc_units<B, NT>((src & kAddrMask) - t0, (dst & kAddrMask) - t0, t0 + (src >> kAddrBits), blk,
-                    nb, t0 + threadIdx.x);
-  if ((dst >> 63) == 0) return;
+  desc_units<B, NT>(sb, db, end, blk, nb, t0 + threadIdx.x);
+  if (more == 0) return;
   for (uint64_t t = (uint64_t)blockIdx.x + gridDim.x;; t += gridDim.x) {
     const int lo = desc_find(blk, nb, t * kDescTile);
     if (lo >= nb) return;
@@ -683,20 +680,16 @@ size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_
   const uint64_t cap_units = (uint64_t)rows_capacity * (row_bytes / 16);
   const uint64_t ndesc = (cap_units + kDescTile - 1) / kDescTile;
   const uint64_t slots = (ndesc + kDescGroup - 1) / kDescGroup * kDescGroup;
-  return ((size_t)R * R * sizeof(A2aBlk) + slots * sizeof(A2aTile) + 255) & ~(size_t)255;
+  return ((size_t)R * R * sizeof(A2aBlk) + slots * sizeof(uint16_t) + 255) & ~(size_t)255;
 }
 
 int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
                    const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
                    size_t rows_capacity, void *ws) {
-  uintptr_t bits = row_bytes, top = 0;
-  for (int r = 0; r < R; r++) {
-    bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
-    top |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
-  }
-  // rows that are not whole 16-byte units, no capacity, or buffers above the
-  // descriptors' address range: the plain form
-  if (copy_unit(bits) != 16 || rows_capacity == 0 || (top >> (kAddrBits + 3)) != 0)
+  uintptr_t bits = row_bytes;
+  for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
+  // rows that are not whole 16-byte units, or no capacity: the plain form
+  if (copy_unit(bits) != 16 || rows_capacity == 0)
     return launch_a2av(L, R, p, counts, sdispls, rdispls, row_bytes, rows_capacity);
   const uint64_t row_units = row_bytes / 16;
   const uint64_t cap_units = (uint64_t)rows_capacity * row_units;
@@ -704,21 +697,21 @@ int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *cou
   if (ndesc == 0 || ndesc > 0x7FFFFFFFull)     // empty rows, or more tiles than one grid holds
     return launch_a2av(L, R, p, counts, sdispls, rdispls, row_bytes, rows_capacity);
   A2aBlk *blk = reinterpret_cast<A2aBlk *>(ws);
-  A2aTile *desc = reinterpret_cast<A2aTile *>(blk + (size_t)R * R);
+  uint32_t *idx = reinterpret_cast<uint32_t *>(blk + (size_t)R * R);   // two indices per word
   // descriptor writers: a resident grid (COLL_DESC_BUILD_WGS per CU), no
-  // more workgroups than tiles' worth of threads
-  const uint64_t gneed = (ndesc + kBlock - 1) / kBlock;
+  // more workgroups than there are index pairs for their threads
+  const uint64_t pairs = (ndesc + kDescGroup - 1) / kDescGroup * kDescGroup / 2;
+  const uint64_t gneed = (pairs + kBlock - 1) / kBlock;
   const uint64_t gres = (uint64_t)L.num_cus * kDescBuildWgs;
-  const unsigned gb = (unsigned)(gneed < gres ? gneed : gres);
-  hipLaunchKernelGGL((a2av_desc_build<16>), dim3(gb), dim3(kBlock), 0, L.stream, p, R, counts,
-                     sdispls, rdispls, row_units, desc, ndesc, blk);
-  const unsigned g = (unsigned)ndesc;
+  hipLaunchKernelGGL((a2av_desc_build<16>), dim3((unsigned)(gneed < gres ? gneed : gres)),
+                     dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, row_units, idx,
+                     ndesc, blk);
   if (L.a2a_nt)
-    hipLaunchKernelGGL((a2av_desc_kernel<16, true>), dim3(g), dim3(kDescLanes), 0, L.stream, desc,
-                       blk, R * R);
+    hipLaunchKernelGGL((a2av_desc_kernel<16, true>), dim3((unsigned)ndesc), dim3(kDescLanes), 0,
+                       L.stream, idx, blk, R * R);
   else
-    hipLaunchKernelGGL((a2av_desc_kernel<16, false>), dim3(g), dim3(kDescLanes), 0, L.stream, desc,
-                       blk, R * R);
+    hipLaunchKernelGGL((a2av_desc_kernel<16, false>), dim3((unsigned)ndesc), dim3(kDescLanes), 0,
+                       L.stream, idx, blk, R * R);
   return hip_status();
 }
 

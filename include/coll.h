@@ -209,17 +209,17 @@ int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *se
  * exchange, result and arguments as coll_all_to_all_v, faster for large
  * exchanges.  A first kernel writes the
  * block table and, for every tile of 64 sixteen-byte units (1 KiB) of the
- * receive capacity, where that tile's units come from and go to; the copy
- * kernel then starts each tile with one load of it instead of building the
- * table.  This descriptor form runs when
+ * receive capacity, the index of the block holding its first unit; the copy
+ * kernel then starts each tile with that index and the block's entry instead
+ * of building the table.  This descriptor form runs when
  * rows are whole 16-byte units and recv_rows_capacity covers at least 192 MiB
  * (environment variable COLL_A2A_DESC_MIN_BYTES, read once per process; below
  * it the second launch costs more than it saves on MI355X).  Otherwise this
  * call is coll_all_to_all_v, the workspace is not touched and may be NULL, and
  * the size below is 0.  Its size is
  * coll_all_to_all_v_workspace_bytes(nranks, recv_rows_capacity, row_elems,
- * dtype): 32 bytes per block and 16 per tile, the tiles counted in whole
- * groups of 64, rounded up to 256 (56 MiB for a 3.5 GiB exchange).
+ * dtype): 32 bytes per block and 2 per tile, the tiles counted in whole
+ * groups of 512, rounded up to 256 (7 MiB for a 3.5 GiB exchange).
  * workspace: DEVICE, 256-byte aligned, overwritten; concurrent calls need
  * workspaces of their own.  recv_rows_capacity only sizes the launch: a bound
  * below the rows actually received costs time, not correctness.

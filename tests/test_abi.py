@@ -134,12 +134,12 @@ def test_moe_expert_workspace_validation(L):
 
 
 def test_a2av_workspace_size_and_validation(L):
-    def size(R, tiles):          # 32-byte block entries, 16-byte tile descriptors in
-        slots = -(-tiles // 64) * 64                      # groups of 64, rounded to 256
-        return -(-(R * R * 32 + slots * 16) // 256) * 256
+    def size(R, tiles):          # 32-byte block entries, 2-byte tile indices in
+        slots = -(-tiles // 512) * 512                    # groups of 512, rounded to 256
+        return -(-(R * R * 32 + slots * 2) // 256) * 256
     # rows of 7168 bf16 (896 sixteen-byte units), 262144 rows of capacity:
-    # 64 block entries + 3670016 descriptors of 64-unit (1 KiB) tiles
-    assert L.coll_all_to_all_v_workspace_bytes(8, 262144, 7168, 0) == 64 * 32 + 3670016 * 16
+    # 64 block entries + 3670016 indices of 64-unit (1 KiB) tiles
+    assert L.coll_all_to_all_v_workspace_bytes(8, 262144, 7168, 0) == 64 * 32 + 3670016 * 2
     assert L.coll_all_to_all_v_workspace_bytes(8, 262144, 7, 0) == 0     # 14-byte rows
     assert L.coll_all_to_all_v_workspace_bytes(8, 0, 7168, 0) == 0       # no capacity
     assert L.coll_all_to_all_v_workspace_bytes(17, 10, 8, 0) == 0        # R > 16
@@ -151,9 +151,9 @@ def test_a2av_workspace_size_and_validation(L):
     assert L.coll_all_to_all_v_workspace_bytes(2, 1, 8, 0) == 0
     need = L.coll_all_to_all_v_workspace_bytes(2, K, 8, 0)
     assert need == size(2, K // 64)
-    # one unit more: one tile more, which starts a new group of 64
+    # one unit more: one tile more, which starts a new group of 512
     assert L.coll_all_to_all_v_workspace_bytes(2, K + 1, 8, 0) == size(2, K // 64 + 1)
-    assert size(2, K // 64 + 1) == size(2, K // 64) + 64 * 16
+    assert size(2, K // 64 + 1) == size(2, K // 64) + 512 * 2
     t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     # a needed workspace that is NULL, misaligned or too small: rejected
     assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, NULL, need, NULL) == -1
