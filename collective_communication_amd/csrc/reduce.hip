@@ -47,13 +47,32 @@ constexpr int ar_u() { return R <= 2 ? 4 : (R <= 8 ? COLL_AR_U_MID : 1); }
 template <int R>
 constexpr int rs_u() { return R <= 2 ? 4 : (R <= 8 ? COLL_RS_U_MID : 1); }
 
+// Tile order.  COLL_AR_XCD = 1: workgroup b (which runs on XCD b mod 8) takes
+// tile (b mod 8) * (G / 8) + b / 8, so each XCD sweeps one contiguous eighth
+// of the range; a bijection on [0, G) (the last G mod 8 tiles keep their
+// index).  COLL_AR_ROT = 1: a wave stores its R outputs starting at rank
+// b mod R, so concurrent waves do not all write rank 0's buffer first.
+#ifndef COLL_AR_XCD
+#define COLL_AR_XCD 0
+#endif
+#ifndef COLL_AR_ROT
+#define COLL_AR_ROT 0
+#endif
+__device__ __forceinline__ size_t ar_tile_of(size_t b, size_t G) {
+  if constexpr (COLL_AR_XCD != 0) {
+    const size_t q = G >> 3;
+    if (b < (q << 3)) return (b & 7) * q + (b >> 3);
+  }
+  return b;
+}
+
 // R known at compile time: all U * R loads of a tile issue back to back.
 template <int R, int DT, int OP, bool NT>
 __global__ __launch_bounds__(kArBlock) void ar_vec(RankPtrs p, size_t nvec) {
   using F = Fmt<DT>;
   constexpr int U = ar_u<R>();
   const size_t tile = (size_t)kArBlock * U;
-  for (size_t base = (size_t)blockIdx.x * tile + threadIdx.x; base < nvec;
+  for (size_t base = ar_tile_of(blockIdx.x, gridDim.x) * tile + threadIdx.x; base < nvec;
        base += (size_t)gridDim.x * tile) {
     u32x4 v[U][R];
 #pragma unroll
@@ -72,8 +91,17 @@ __global__ __launch_bounds__(kArBlock) void ar_vec(RankPtrs p, size_t nvec) {
 #pragma unroll
         for (int r = 1; r < R; r++) F::template fold_in<OP>(a, v[u][r]);
         const u32x4 o = F::narrow(a);
+        if constexpr (COLL_AR_ROT != 0) {
+          const int rot = (int)(blockIdx.x % R);
 #pragma unroll
-        for (int r = 0; r < R; r++) st<u32x4, NT>(p.out[r], i, o);
+          for (int r = 0; r < R; r++) {
+            const int q = r + rot;
+            st<u32x4, NT>(p.out[q >= R ? q - R : q], i, o);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; r++) st<u32x4, NT>(p.out[r], i, o);
+        }
       }
     }
   }

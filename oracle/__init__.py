@@ -54,7 +54,7 @@ def _load(path: str) -> ctypes.CDLL:
     L.oracle_f32_to_bf16.restype = ctypes.c_uint16
     L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
     for name in ("oracle_f32_to_bf16_n", "oracle_bf16_to_f32_n",
-                 "oracle_f32_to_f16_n", "oracle_f16_to_f32_n"):
+                 "oracle_f32_to_f16_n", "oracle_f16_to_f32_n", "oracle_f64_to_bf16_n"):
         getattr(L, name).argtypes = [sz, vp, vp]
         getattr(L, name).restype = None
     L.oracle_allreduce.argtypes = [i32, vp, vp, sz, i32, i32]
@@ -161,6 +161,14 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
     h = np.ascontiguousarray(h, dtype=np.uint16)
     out = np.empty(h.shape, np.float32)
     lib().oracle_bf16_to_f32_n(h.size, _ptr(h), _ptr(out))
+    return out
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bits in one rounding, to nearest even (bfloat16 definition)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_f64_to_bf16_n(x.size, _ptr(x), _ptr(out))
     return out
 
 

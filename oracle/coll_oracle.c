@@ -75,6 +75,36 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+/* binary64 -> bfloat16, round to nearest, ties to even, in one step (the
+ * LSE merge accumulates in binary64; going through binary32 first would round
+ * twice).  From the format's definition: bfloat16 keeps 8 significant bits
+ * with binary32's exponent range, so scale |x| until one unit is the
+ * bfloat16 quantum of its binade, round that to an integer (rint: ties to
+ * even in the default mode) and re-encode.  The scalings are exact. */
+uint16_t oracle_f64_to_bf16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7F80u);
+    double a = fabs(x);
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: quantum 2^-133; r == 128 encodes the smallest
+         * normal (exponent field 1, fraction 0), which is the same pattern */
+        double r = rint(a * ldexp(1.0, 133));
+        return (uint16_t)(sign | (uint16_t)r);
+    }
+    int ex;
+    frexp(a, &ex);                 /* a = mant * 2^ex, mant in [0.5, 1) */
+    int e = ex - 1;                /* a in [2^e, 2^(e+1)) */
+    double r = rint(a * ldexp(1.0, 7 - e));    /* in [128, 256] */
+    if (r == 256.0) { r = 128.0; e += 1; }
+    if (e + 127 >= 255)
+        return (uint16_t)(sign | 0x7F80u);
+    return (uint16_t)(sign | (uint16_t)((e + 127) << 7) | (uint16_t)(r - 128.0));
+}
+
 /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
 float oracle_f16_to_f32(uint16_t h)
 {
@@ -485,6 +515,10 @@ void oracle_f16_to_f32_n(size_t n, const uint16_t *in, float *out)
 {
     for (size_t i = 0; i < n; i++) out[i] = oracle_f16_to_f32(in[i]);
 }
+void oracle_f64_to_bf16_n(size_t n, const double *in, uint16_t *out)
+{
+    for (size_t i = 0; i < n; i++) out[i] = oracle_f64_to_bf16(in[i]);
+}
 
 /* ------------------------------------------------------------------ */
 /* Uniform all-to-all and the sequence <-> heads re-shard              */
@@ -567,7 +601,13 @@ int oracle_lse_merge(int R, const void *const *o_parts, const float *const *lse_
             if (m != -INFINITY)
                 for (int r = 0; r < R; r++)
                     acc += (e[r] / s) * (double)load_fp(o_parts[r], i * D + c, dt);
-            for (int r = 0; r < R; r++) store_fp(o_out[r], i * D + c, dt, (float)acc);
+            /* one rounding from binary64 to the output type */
+            for (int r = 0; r < R; r++) {
+                if (dt == O_BF16)
+                    ((uint16_t *)o_out[r])[i * D + c] = oracle_f64_to_bf16(acc);
+                else
+                    ((float *)o_out[r])[i * D + c] = (float)acc;
+            }
         }
         for (int r = 0; r < R; r++)
             if (lse_out && lse_out[r]) lse_out[r][i] = (float)L;

@@ -548,3 +548,19 @@ def test_lse_merge_single_rank_is_identity_and_equal_lse_is_mean():
     o, lo = oracle.lse_merge([x] * 4, [l] * 4, "bf16")
     assert np.array_equal(o, x)
     assert np.allclose(lo, l + np.log(4.0), atol=1e-6)
+
+
+def test_lse_merge_bf16_rounds_the_exact_mean_once():
+    """Equal LSEs on 4 ranks weigh every part by exactly 1/4, so the merged
+    value is the exact mean of the parts.  Parts 4, 2^-6, 2^-26, 0 (all bf16)
+    have mean 1 + 2^-8 + 2^-28: just above the bf16 tie between 1 and 1 + 2^-7,
+    and below half an fp32 ulp above it.  Rounded once (bfloat16 definition)
+    it is 1 + 2^-7; rounded to fp32 first it would land on the tie and go to
+    1.  Without the 2^-26 part the mean is the tie itself -> 1 (even)."""
+    bf = lambda *vals: oracle.f32_to_bf16(np.array(vals, np.float32))
+    parts = [bf(4.0, -4.0, 4.0), bf(2.0 ** -6, -(2.0 ** -6), 2.0 ** -6),
+             bf(2.0 ** -26, -(2.0 ** -26), 0.0), bf(0.0, 0.0, 0.0)]
+    lse = [np.zeros(1, np.float32)] * 4
+    o, lo = oracle.lse_merge([p.reshape(1, 3) for p in parts], lse, "bf16")
+    assert o.reshape(-1).tolist() == [0x3F81, 0xBF81, 0x3F80]
+    assert np.allclose(lo, np.log(4.0), atol=1e-6)

@@ -112,6 +112,17 @@ MUTANTS = [
     ("LSE merge drops the max shift in L",
      "L = m + log(s);", "L = log(s);",
      [lambda: C.test_lse_merge_reproduces_full_attention(4, 100)]),
+    ("LSE merge rounds through fp32 before bf16 (two roundings)",
+     "((uint16_t *)o_out[r])[i * D + c] = oracle_f64_to_bf16(acc);",
+     "((uint16_t *)o_out[r])[i * D + c] = oracle_f32_to_bf16((float)acc);",
+     [lambda: C.test_lse_merge_bf16_rounds_the_exact_mean_once()]),
+    ("fp64 -> bf16 subnormal quantum off by one binade",
+     "double r = rint(a * ldexp(1.0, 133));", "double r = rint(a * ldexp(1.0, 132));",
+     [lambda: F.test_f64_to_bf16_matches_a_search_of_the_value_grid()]),
+    ("fp64 -> bf16 rounds ties away from zero",
+     "double r = rint(a * ldexp(1.0, 7 - e));    /* in [128, 256] */",
+     "double r = floor(a * ldexp(1.0, 7 - e) + 0.5);",
+     [lambda: F.test_f64_to_bf16_matches_a_search_of_the_value_grid()]),
 ]
 
 
