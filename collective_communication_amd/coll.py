@@ -107,8 +107,12 @@ def _dev(t: torch.Tensor, what: str) -> int:
     return t.data_ptr()
 
 
-def _table(ts: Sequence[torch.Tensor], what: str):
-    return (ctypes.c_void_p * len(ts))(*[_dev(t, what) for t in ts])
+def _table(ts: Sequence[torch.Tensor], what: str, R: int):
+    """R device pointers as a C array.  Every per-rank list must hold exactly
+    R entries: the library reads R pointers from each table it is given."""
+    if len(ts) != R:
+        raise ValueError(f"{what}: {len(ts)} buffers for {R} ranks (one per rank)")
+    return (ctypes.c_void_p * R)(*[_dev(t, what) for t in ts])
 
 
 def _ranks(ts, what) -> int:
@@ -248,8 +252,8 @@ def allreduce(sends, recvs, op: str = "sum", stream=None):
     _same(recvs, sends[0].dtype, n, "allreduce recv")
     if len(recvs) != R:
         raise ValueError("allreduce: one recv per rank")
-    return _issue("coll_allreduce", "allreduce", stream, R, _table(sends, "send"),
-                  _table(recvs, "recv"), n, _reduce_dtype(sends[0]), OPS[op])
+    return _issue("coll_allreduce", "allreduce", stream, R, _table(sends, "send", R),
+                  _table(recvs, "recv", R), n, _reduce_dtype(sends[0]), OPS[op])
 
 
 def reduce_scatter(sends, recvs, op: str = "sum", stream=None):
@@ -258,8 +262,8 @@ def reduce_scatter(sends, recvs, op: str = "sum", stream=None):
     n = recvs[0].numel()
     _same(sends, sends[0].dtype, R * n, "reduce_scatter send")
     _same(recvs, sends[0].dtype, n, "reduce_scatter recv")
-    return _issue("coll_reduce_scatter", "reduce_scatter", stream, R, _table(sends, "send"),
-                  _table(recvs, "recv"), n, _reduce_dtype(sends[0]), OPS[op])
+    return _issue("coll_reduce_scatter", "reduce_scatter", stream, R, _table(sends, "send", R),
+                  _table(recvs, "recv", R), n, _reduce_dtype(sends[0]), OPS[op])
 
 
 def reduce(sends, recv_root, root: int, op: str = "sum", stream=None):
@@ -268,7 +272,7 @@ def reduce(sends, recv_root, root: int, op: str = "sum", stream=None):
     n = sends[0].numel()
     _same(sends, sends[0].dtype, n, "reduce send")
     _same([recv_root], sends[0].dtype, n, "reduce recv")
-    return _issue("coll_reduce", "reduce", stream, R, _table(sends, "send"),
+    return _issue("coll_reduce", "reduce", stream, R, _table(sends, "send", R),
                   _dev(recv_root, "recv"), root, n, _reduce_dtype(sends[0]), OPS[op])
 
 
@@ -281,7 +285,7 @@ def scatter(send_root, recvs, root: int, stream=None):
         raise ValueError("scatter: the root buffer must hold R chunks")
     dt, mult = _copy_dtype(send_root)
     return _issue("coll_scatter", "scatter", stream, R, _dev(send_root, "send"),
-                  _table(recvs, "recv"), root, n * mult, dt)
+                  _table(recvs, "recv", R), root, n * mult, dt)
 
 
 def all_gather(sends, recvs, stream=None):
@@ -291,8 +295,8 @@ def all_gather(sends, recvs, stream=None):
     _same(sends, sends[0].dtype, n, "all_gather send")
     _same(recvs, sends[0].dtype, R * n, "all_gather recv")
     dt, mult = _copy_dtype(sends[0])
-    return _issue("coll_all_gather", "all_gather", stream, R, _table(sends, "send"),
-                  _table(recvs, "recv"), n * mult, dt)
+    return _issue("coll_all_gather", "all_gather", stream, R, _table(sends, "send", R),
+                  _table(recvs, "recv", R), n * mult, dt)
 
 
 def gather(sends, recv_root, root: int = 0, stream=None):
@@ -306,7 +310,7 @@ def gather(sends, recv_root, root: int = 0, stream=None):
     if recv_root.dtype != s0.dtype or recv_root.numel() != outer * R * inner:
         raise ValueError("gather: root buffer must be [outer, R*inner] of the send dtype")
     dt, mult = _copy_dtype(s0)
-    return _issue("coll_gather", "gather", stream, R, _table(sends, "send"),
+    return _issue("coll_gather", "gather", stream, R, _table(sends, "send", R),
                   _dev(recv_root, "recv"), root, outer, inner * mult, dt)
 
 
@@ -317,7 +321,7 @@ def broadcast(send_root, recvs, root: int, stream=None):
     _same(recvs, send_root.dtype, n, "broadcast recv")
     dt, mult = _copy_dtype(send_root)
     return _issue("coll_broadcast", "broadcast", stream, R, _dev(send_root, "send"),
-                  _table(recvs, "recv"), root, n * mult, dt)
+                  _table(recvs, "recv", R), root, n * mult, dt)
 
 
 def _a2av_shape(sends, recvs, row_elems: int, what: str, capacity=None):
@@ -356,8 +360,8 @@ def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
     for t, name in ((sendcounts, "sendcounts"), (sdispls, "sdispls"), (rdispls, "rdispls")):
         if t.dtype != torch.int64 or t.numel() != R * R:
             raise ValueError(f"all_to_all_v: {name} must be int64 [R*R] on the device")
-    args = (R, _table(sends, "send"), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
-            _table(recvs, "recv"), _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity)
+    args = (R, _table(sends, "send", R), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
+            _table(recvs, "recv", R), _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity)
     if workspace is None:
         return _issue("coll_all_to_all_v", "all_to_all_v", stream, *args)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -374,8 +378,8 @@ def all_to_all(sends, recvs, stream=None):
     _same(sends, sends[0].dtype, total, "all_to_all send")
     _same(recvs, sends[0].dtype, total, "all_to_all recv")
     dt, mult = _copy_dtype(sends[0])
-    return _issue("coll_all_to_all", "all_to_all", stream, R, _table(sends, "send"),
-                  _table(recvs, "recv"), total // R * mult, dt)
+    return _issue("coll_all_to_all", "all_to_all", stream, R, _table(sends, "send", R),
+                  _table(recvs, "recv", R), total // R * mult, dt)
 
 
 def seq_heads_reshard(ins, outs, heads: int, head_dim: int, to_heads: bool,
@@ -390,8 +394,8 @@ def seq_heads_reshard(ins, outs, heads: int, head_dim: int, to_heads: bool,
     _same(ins, ins[0].dtype, per, "seq_heads_reshard in")
     _same(outs, ins[0].dtype, per, "seq_heads_reshard out")
     dt, mult = _copy_dtype(ins[0])
-    return _issue("coll_seq_heads_reshard", "seq_heads_reshard", stream, R, _table(ins, "in"),
-                  _table(outs, "out"), SL, heads, head_dim * mult, dt, 1 if to_heads else 0)
+    return _issue("coll_seq_heads_reshard", "seq_heads_reshard", stream, R, _table(ins, "in", R),
+                  _table(outs, "out", R), SL, heads, head_dim * mult, dt, 1 if to_heads else 0)
 
 
 def lse_merge(o_parts, lse_parts, o_out, lse_out=None, stream=None):
@@ -409,9 +413,9 @@ def lse_merge(o_parts, lse_parts, o_out, lse_out=None, stream=None):
     lo = None
     if lse_out is not None:
         _same(lse_out, torch.float32, rows, "lse_merge lse_out")
-        lo = _table(lse_out, "lse_out")
-    return _issue("coll_lse_merge", "lse_merge", stream, R, _table(o_parts, "o"),
-                  _table(lse_parts, "lse"), _table(o_out, "out"), lo, rows, D, dt)
+        lo = _table(lse_out, "lse_out", R)
+    return _issue("coll_lse_merge", "lse_merge", stream, R, _table(o_parts, "o", R),
+                  _table(lse_parts, "lse", R), _table(o_out, "out", R), lo, rows, D, dt)
 
 
 def moe_workspace_bytes(R: int, tokens: int, topk: int, n_experts: int) -> int:
@@ -421,7 +425,7 @@ def moe_workspace_bytes(R: int, tokens: int, topk: int, n_experts: int) -> int:
 def moe_layout(topk_ids, n_experts: int, sendcounts, sdispls, rdispls, expert_counts, pos,
                workspace, stream=None):
     """MoE layout from int32 [T, K] ids per rank into device count tables and
-    int32 [T, K] send-slot positions."""
+    int32 [T, K] send-slot positions (-1: an id outside [0, E))."""
     R = _ranks(topk_ids, "moe_layout")
     T, K = topk_ids[0].shape
     for t in topk_ids:
@@ -436,13 +440,15 @@ def moe_layout(topk_ids, n_experts: int, sendcounts, sdispls, rdispls, expert_co
     if expert_counts.dtype != torch.int32 or expert_counts.numel() != R * n_experts:
         raise ValueError("moe_layout: expert_counts is int32 [R*E]")
     ws_bytes = workspace.numel() * workspace.element_size()
-    return _issue("coll_moe_layout", "moe_layout", stream, R, _table(topk_ids, "ids"), T, K,
+    return _issue("coll_moe_layout", "moe_layout", stream, R, _table(topk_ids, "ids", R), T, K,
                   n_experts, _dev(sendcounts, "sc"), _dev(sdispls, "sd"), _dev(rdispls, "rd"),
-                  _dev(expert_counts, "ec"), _table(pos, "pos"), _dev(workspace, "ws"), ws_bytes)
+                  _dev(expert_counts, "ec"), _table(pos, "pos", R), _dev(workspace, "ws"),
+                  ws_bytes)
 
 
 def moe_permute(xs, pos, sends, stream=None):
-    """sends[s][pos[s][t,k]] = xs[s][t] (x [T, H], sends [T*K, H])."""
+    """sends[s][pos[s][t,k]] = xs[s][t] (x [T, H], pos int32 [T, K], sends [T*K, H];
+    pairs with pos = -1 are skipped)."""
     R = _ranks(xs, "moe_permute")
     T, H = xs[0].shape
     K = pos[0].shape[1]
@@ -453,8 +459,8 @@ def moe_permute(xs, pos, sends, stream=None):
         if s.numel() != T * K * H or s.dtype != xs[0].dtype:
             raise ValueError("moe_permute: send buffers must be [T*K, H]")
     dt, mult = _copy_dtype(xs[0])
-    return _issue("coll_moe_permute", "moe_permute", stream, R, _table(xs, "x"),
-                  _table(pos, "pos"), T, K, H * mult, dt, _table(sends, "send"))
+    return _issue("coll_moe_permute", "moe_permute", stream, R, _table(xs, "x", R),
+                  _table(pos, "pos", R), T, K, H * mult, dt, _table(sends, "send", R))
 
 
 def moe_expert_workspace_bytes(R: int, n_experts: int, rows_capacity: int = 0) -> int:
@@ -476,7 +482,7 @@ def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
             raise ValueError("moe_expert_scale: bf16 rows only")
     capacity = sum(t.numel() // hidden for t in recvs) if hidden > 0 else 0
     ws_bytes = workspace.numel() * workspace.element_size()
-    return _issue("coll_moe_expert_scale", "moe_expert_scale", stream, R, _table(recvs, "recv"),
+    return _issue("coll_moe_expert_scale", "moe_expert_scale", stream, R, _table(recvs, "recv", R),
                   _dev(expert_counts, "ec"), _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
                   capacity, _dev(workspace, "ws"), ws_bytes)
 
@@ -495,9 +501,9 @@ def moe_combine(backs, pos, weights, outs, stream=None):
     for o in outs:
         if o.dtype != torch.bfloat16 or o.numel() != T * H:
             raise ValueError("moe_combine: outputs are bf16 [T, H]")
-    return _issue("coll_moe_combine", "moe_combine", stream, R, _table(backs, "back"),
-                  _table(pos, "pos"), _table(weights, "w"), T, K, H, COLL_BF16,
-                  _table(outs, "out"))
+    return _issue("coll_moe_combine", "moe_combine", stream, R, _table(backs, "back", R),
+                  _table(pos, "pos", R), _table(weights, "w", R), T, K, H, COLL_BF16,
+                  _table(outs, "out", R))
 
 
 def _layout_tables(R, tables, what):
@@ -522,9 +528,9 @@ def moe_dispatch(xs, pos, sendcounts, sdispls, rdispls, recvs, stream=None):
         if r.dtype != xs[0].dtype or r.numel() % max(H, 1) != 0:
             raise ValueError("moe_dispatch: receive buffers are [rows, H] of x's dtype")
     dt, mult = _copy_dtype(xs[0])
-    return _issue("coll_moe_dispatch", "moe_dispatch", stream, R, _table(xs, "x"),
-                  _table(pos, "pos"), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
-                  _dev(rdispls, "rd"), T, K, H * mult, dt, _table(recvs, "recv"))
+    return _issue("coll_moe_dispatch", "moe_dispatch", stream, R, _table(xs, "x", R),
+                  _table(pos, "pos", R), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
+                  _dev(rdispls, "rd"), T, K, H * mult, dt, _table(recvs, "recv", R))
 
 
 def moe_combine_recv(recvs, pos, sendcounts, sdispls, rdispls, weights, outs, topk_ids=None,
@@ -550,8 +556,8 @@ def moe_combine_recv(recvs, pos, sendcounts, sdispls, rdispls, weights, outs, to
         for t in topk_ids:
             if t.dtype != torch.int32 or t.numel() != T * K:
                 raise ValueError("moe_combine_recv: topk_ids are int32 [T, K]")
-        ids = _table(topk_ids, "ids")
-    return _issue("coll_moe_combine_recv", "moe_combine_recv", stream, R, _table(recvs, "recv"),
-                  _table(pos, "pos"), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
-                  _dev(rdispls, "rd"), _table(weights, "w"), ids, T, K, H, COLL_BF16,
-                  _table(outs, "out"))
+        ids = _table(topk_ids, "ids", R)
+    return _issue("coll_moe_combine_recv", "moe_combine_recv", stream, R, _table(recvs, "recv", R),
+                  _table(pos, "pos", R), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
+                  _dev(rdispls, "rd"), _table(weights, "w", R), ids, T, K, H, COLL_BF16,
+                  _table(outs, "out", R))

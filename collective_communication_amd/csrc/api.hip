@@ -142,7 +142,7 @@ const char *coll_status_string(int status) {
   }
 }
 
-int coll_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int coll_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 int coll_arena_layout(int n, const size_t *bytes, size_t *offsets, size_t *total) {
   if (n < 0 || !total || (n > 0 && (!bytes || !offsets))) return COLL_ERR_INVALID_ARG;
@@ -342,8 +342,20 @@ int coll_lse_merge(int R, const void *const *o_parts, const float *const *lse_pa
   if (!fill_in(R, o_parts, o.in) || !fill_out(R, o_out, o.out) ||
       !fill_in(R, reinterpret_cast<const void *const *>(lse_parts), li.p))
     return COLL_ERR_INVALID_ARG;
-  if (lse_out)
-    for (int r = 0; r < R; r++) lo.p[r] = lse_out[r];      // NULL entries: not written
+  if (lse_out) {
+    // An LSE output may not overlap any LSE input: a row's output is stored
+    // while workgroups of other segments of that row may still read its inputs.
+    const size_t lb = rows * sizeof(float);
+    for (int r = 0; r < R; r++) {
+      lo.p[r] = lse_out[r];                                  // NULL entries: not written
+      if (!lse_out[r]) continue;
+      const uintptr_t a = reinterpret_cast<uintptr_t>(lse_out[r]);
+      for (int q = 0; q < R; q++) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(li.p[q]);
+        if (a < b + lb && b < a + lb) return COLL_ERR_INVALID_ARG;
+      }
+    }
+  }
   return launch_lse_merge(launch_ctx(stream), R, o, li, lo, rows, head_dim, dtype);
 }
 

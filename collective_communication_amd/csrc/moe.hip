@@ -149,10 +149,9 @@ __global__ __launch_bounds__(kBlock) void moe_hist(PtrTable ids, int TK, int E, 
 }
 
 // blockDim = 1024 (one thread per expert, E <= 1024), grid = R.
-__global__ __launch_bounds__(1024) void moe_scan(int R, int E, int ntiles, int TK,
-                                                 int32_t *hist, int32_t *expert_off,
-                                                 int32_t *expert_counts, int64_t *sendcounts,
-                                                 int64_t *sdispls) {
+__global__ __launch_bounds__(1024) void moe_scan(int R, int E, int ntiles, int32_t *hist,
+                                                 int32_t *expert_off, int32_t *expert_counts,
+                                                 int64_t *sendcounts, int64_t *sdispls) {
   __shared__ int wave_tot[16];
   __shared__ int off[kMaxExperts + 1];
   const int s = blockIdx.x, e = threadIdx.x;
@@ -192,7 +191,9 @@ __global__ __launch_bounds__(1024) void moe_scan(int R, int E, int ntiles, int T
     expert_off[(size_t)s * E + e] = excl;
     expert_counts[(size_t)s * E + e] = cnt;
   }
-  if (e == 0) off[E] = TK;
+  // the rows sent: ids outside [0, E) were not counted, so this can be
+  // below T * K
+  if (e == E - 1) off[E] = excl + cnt;
   __syncthreads();
   if (e < R) {
     const int per = E / R;
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(1024) void moe_scan(int R, int E, int ntiles, int T
   }
 }
 
+// An id outside [0, E) gets pos = -1: no slot.
 __global__ __launch_bounds__(kBlock) void moe_pos(PtrTable ids, MutPtrTable pos, int R, int TK,
                                                   int E, int nbits, int ntiles,
                                                   const int32_t *hist, const int32_t *expert_off,
@@ -262,6 +264,8 @@ __global__ __launch_bounds__(kBlock) void moe_pos(PtrTable ids, MutPtrTable pos,
       int before = 0;
       for (int q = 0; q < w; q++) before += wcnt[q][e];
       out[i] = base[e] + run[e] + before + rank;
+    } else if (i < TK) {
+      out[i] = -1;                                 // no expert: no slot
     }
     __syncthreads();
     for (int x = threadIdx.x; x < E; x += kBlock) {
@@ -607,14 +611,12 @@ __global__ __launch_bounds__(64) void moe_expert_row_kernel(const uint64_t *__re
 
 // ------------------------------------------------------------------ combine
 
-// A slot outside [0, T*K) (a caller error) reads row 0 instead of memory
-// outside the buffer.
-__device__ __forceinline__ uint32_t slot_of(int32_t p, uint32_t TK) {
-  return (uint32_t)p < TK ? (uint32_t)p : 0u;
-}
-
 // One wave per (token, segment of 64 x UN units); its K slots and weights
-// are scalar loads, all K x UN gathered loads issue before the fold.
+// are scalar loads, all K x UN gathered loads issue before the fold.  A slot
+// outside [0, T*K) -- the layout's -1 for a pair with no expert -- adds no
+// term: the fold runs over the token's other pairs in order, seeded by the
+// first of them (+0 if none is left).  Slots are wave-uniform, so this never
+// diverges.
 template <int G, bool NT>
 __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(PtrTable back, PtrTable pos,
                                                              PtrTable wts, MutPtrTable out,
@@ -634,20 +636,24 @@ __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(PtrTabl
   const uint32_t u0 = (uint32_t)it.seg * (64 * UN) + lane;
   if constexpr (G == 8) {
     float acc[UN][8];
+    bool have = false;                                   // a term has seeded acc
     for (int k0 = 0; k0 < K; k0 += kChunk) {
       uint32_t slot[kChunk];
       float wgt[kChunk];
+      bool live[kChunk];
 #pragma unroll
       for (int c = 0; c < kChunk; c++) {
         const int kc = k0 + c < K ? k0 + c : K - 1;         // past K: used by nothing
-        slot[c] = slot_of(__builtin_amdgcn_readfirstlane(pk[kc]), TK);
+        const int32_t p = __builtin_amdgcn_readfirstlane(pk[kc]);
+        live[c] = k0 + c < K && (uint32_t)p < TK;
+        slot[c] = live[c] ? (uint32_t)p : 0u;
         wgt[c] = __builtin_bit_cast(
             float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wk[kc])));
       }
       u32x4 v[UN][kChunk];
 #pragma unroll
       for (int c = 0; c < kChunk; c++) {
-        if (k0 + c < K) {
+        if (live[c]) {
           const uint16_t *row = bk + (size_t)slot[c] * upr * 8;
 #pragma unroll
           for (int uu = 0; uu < UN; uu++) {
@@ -658,17 +664,18 @@ __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(PtrTabl
       }
 #pragma unroll
       for (int c = 0; c < kChunk; c++) {
-        if (k0 + c < K) {
+        if (live[c]) {
 #pragma unroll
           for (int uu = 0; uu < UN; uu++) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
               const float lo = wgt[c] * bf16_lo(v[uu][c][q]);
               const float hi = wgt[c] * bf16_hi(v[uu][c][q]);
-              if (k0 + c == 0) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
+              if (!have) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
               else { acc[uu][2 * q] = acc[uu][2 * q] + lo; acc[uu][2 * q + 1] = acc[uu][2 * q + 1] + hi; }
             }
           }
+          have = true;
         }
       }
     }
@@ -678,7 +685,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(PtrTabl
       if (u < upr) {
         u32x4 r;
 #pragma unroll
-        for (int q = 0; q < 4; q++) r[q] = pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]);
+        for (int q = 0; q < 4; q++)
+          r[q] = have ? pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]) : 0u;
         st<u32x4, NT>(o + (size_t)it.t * upr * 8, u, r);
       }
     }
@@ -686,10 +694,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(PtrTabl
     const uint32_t u = u0;
     if (u < upr) {
       float acc = 0.0f;
+      bool have = false;
       for (int k = 0; k < K; k++) {
-        const uint32_t slot = slot_of(__builtin_amdgcn_readfirstlane(pk[k]), TK);
-        const float prod = wk[k] * bf16_lo(bk[(size_t)slot * upr + u]);
-        acc = (k == 0) ? prod : acc + prod;
+        const int32_t p = __builtin_amdgcn_readfirstlane(pk[k]);
+        if ((uint32_t)p >= TK) continue;                 // a pair with no expert
+        const float prod = wk[k] * bf16_lo(bk[(size_t)p * upr + u]);
+        acc = have ? acc + prod : prod;
+        have = true;
       }
       o[(size_t)it.t * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
     }
@@ -846,7 +857,8 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(PtrTa
 // out[s][t] = rne(fold_k w[t,k] * widen(y_k)), y_k the receive row of (s,t,k)
 // (the reverse exchange is a read of the destination's buffer).  EXPERT: y_k
 // = rne(widen(row) * (1 + e/256)) with e = ids[s][t,k], the test expert applied
-// as the row is read.  A slot that no block holds contributes +0.
+// as the row is read.  A slot that no block holds (the layout's -1 for a pair
+// with no expert) adds no term, as in the unfused combine.
 template <int G, bool NT, bool EXPERT>
 __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kernel(
     PtrTable recv, PtrTable pos, PtrTable wts, PtrTable ids, MutPtrTable out,
@@ -867,6 +879,7 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
   const uint32_t u0 = (uint32_t)it.seg * (64 * UN) + lane;
   if constexpr (G == 8) {
     float acc[UN][8];
+    bool have = false;                                   // a term has seeded acc
     for (int k0 = 0; k0 < K; k0 += kChunk) {
       const uint16_t *rowp[kChunk];
       float wgt[kChunk], sc[kChunk];
@@ -908,7 +921,7 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
       }
 #pragma unroll
       for (int c = 0; c < kChunk; c++) {
-        if (k0 + c < K) {
+        if (live[c]) {
 #pragma unroll
           for (int uu = 0; uu < UN; uu++) {
 #pragma unroll
@@ -917,10 +930,11 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
               if constexpr (EXPERT) y = pack_bf16(bf16_lo(y) * sc[c], bf16_hi(y) * sc[c]);
               const float lo = wgt[c] * bf16_lo(y);
               const float hi = wgt[c] * bf16_hi(y);
-              if (k0 + c == 0) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
+              if (!have) { acc[uu][2 * q] = lo; acc[uu][2 * q + 1] = hi; }
               else { acc[uu][2 * q] = acc[uu][2 * q] + lo; acc[uu][2 * q + 1] = acc[uu][2 * q + 1] + hi; }
             }
           }
+          have = true;
         }
       }
     }
@@ -930,7 +944,8 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
       if (u < upr) {
         u32x4 r;
 #pragma unroll
-        for (int q = 0; q < 4; q++) r[q] = pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]);
+        for (int q = 0; q < 4; q++)
+          r[q] = have ? pack_bf16(acc[uu][2 * q], acc[uu][2 * q + 1]) : 0u;
         st<u32x4, NT>(o + (size_t)it.t * upr * 8, u, r);
       }
     }
@@ -939,18 +954,21 @@ __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kerne
     const bool in = u < upr;
     {
       float acc = 0.0f;
+      bool have = false;
       for (int k = 0; k < K; k++) {
         int d;                                     // located with the whole wave active
         uint64_t bp;
         const int64_t row = recv_row_lane(bl, __builtin_amdgcn_readfirstlane(pk[k]), d, bp);
+        if (d < 0 || bp == 0) continue;            // no block holds the slot: no term
         uint32_t y = 0u;
-        if (in && d >= 0 && bp != 0) y = reinterpret_cast<const uint16_t *>(bp)[(size_t)row * upr + u];
+        if (in) y = reinterpret_cast<const uint16_t *>(bp)[(size_t)row * upr + u];
         if constexpr (EXPERT) {
           const float sc = 1.0f + (float)__builtin_amdgcn_readfirstlane(ek[k]) / 256.0f;
           y = pack_bf16(bf16_lo(y) * sc, 0.0f) & 0xFFFFu;
         }
         const float prod = wk[k] * bf16_lo(y);
-        acc = (k == 0) ? prod : acc + prod;
+        acc = have ? acc + prod : prod;
+        have = true;
       }
       if (in) o[(size_t)it.t * upr + u] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
     }
@@ -973,7 +991,7 @@ int launch_moe_layout(const Launch &L, int R, const PtrTable &ids, int T, int K,
   if (ntiles > 0)
     hipLaunchKernelGGL(moe_hist, dim3(ntiles, R), dim3(kBlock), 0, L.stream, ids, TK, E, ntiles,
                        hist);
-  hipLaunchKernelGGL(moe_scan, dim3(R), dim3(1024), 0, L.stream, R, E, ntiles, TK, hist,
+  hipLaunchKernelGGL(moe_scan, dim3(R), dim3(1024), 0, L.stream, R, E, ntiles, hist,
                      expert_off, expert_counts, sendcounts, sdispls);
   hipLaunchKernelGGL(moe_pos, dim3(ntiles > 0 ? ntiles : 1, R), dim3(kBlock), 0, L.stream, ids,
                      pos, R, TK, E, nbits, ntiles, hist, expert_off, sendcounts, rdispls);

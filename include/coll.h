@@ -268,10 +268,14 @@ int coll_seq_heads_reshard(int nranks, const void *const *in, void *const *out,
  *   lse_out[r][i] = L,   for every rank r (AllReduce of the corrected terms).
  * A row whose lse are all -inf gives 0 and -inf.  o_parts/o_out: [rows,
  * head_dim] of bf16 or fp32; lse: fp32 [rows].  o_out[r] may be o_parts[r]
- * (in place); lse_out (or an entry of it) may be NULL to skip it.  exp/log
- * are the device library's fp32 functions: o differs from the exact (fp64)
- * merge rounded once by at most 2 ulps of the output type plus a few fp32
- * ulps of sum_r w_r |o_r| (cancellation); L by a few fp32 ulps.
+ * (in place); lse_out (or an entry of it) may be NULL to skip it.  No
+ * lse_out[r] may overlap any lse_parts[q] (in-place LSEs are rejected with
+ * COLL_ERR_INVALID_ARG: a long row is split over several workgroups, and the
+ * one that stores L would race the others' reads).  Each row's weights are
+ * formed once, by one lane.  exp/log are the device library's fp32
+ * functions: o differs from the exact (fp64) merge rounded once by at most
+ * 2 ulps of the output type plus a few fp32 ulps of sum_r w_r |o_r|
+ * (cancellation); L by a few fp32 ulps.
  */
 int coll_lse_merge(int nranks, const void *const *o_parts, const float *const *lse_parts,
                    void *const *o_out, float *const *lse_out, size_t rows, size_t head_dim,
@@ -283,8 +287,11 @@ int coll_lse_merge(int nranks, const void *const *o_parts, const float *const *l
  * [d*E/R, (d+1)*E/R); E must be a multiple of R.  Each (token t, slot k) pair
  * is one dispatched row; rows bound for a rank are ordered stably by
  * (expert, t, k), so within a source's send buffer the rows are sorted by
- * expert.  topk_ids are int32 in [0, E) (out-of-range ids are the caller's
- * error: they are not checked on the device).
+ * expert.  topk_ids are int32; an id outside [0, E) names no expert and its
+ * pair is skipped everywhere: it gets no send slot (pos = -1), is counted in
+ * no table, moves no row and adds no term to either combine (the tutorial
+ * routes tokens only to existing experts; such a pair is read as one that
+ * does not exist).
  * ------------------------------------------------------------------------- */
 
 /* Bytes of device workspace coll_moe_layout needs (0 on invalid sizes). */
@@ -294,7 +301,8 @@ size_t coll_moe_workspace_bytes(int nranks, int tokens, int topk, int n_experts)
  * Layout: from R device arrays topk_ids[s] (int32 [tokens, topk]) compute
  *   sendcounts[s*R+d], sdispls[s*R+d], rdispls[d*R+s]  (DEVICE int64, R*R each),
  *   expert_counts[s*E+e]  rows of expert e from source s (DEVICE int32, R*E),
- *   pos[s][t*topk+k]      slot of (t,k) in source s's send buffer (DEVICE int32).
+ *   pos[s][t*topk+k]      slot of (t,k) in source s's send buffer, -1 for a
+ *                         pair with no expert (DEVICE int32 [tokens*topk]).
  * Uses `workspace` (coll_moe_workspace_bytes, 256-byte aligned, device).
  * Supports n_experts <= 1024 and tokens * topk < 2^31.
  */
@@ -305,7 +313,8 @@ int coll_moe_layout(int nranks, const int32_t *const *topk_ids, int tokens, int 
 
 /*
  * Dispatch permute (an indexed write; the tutorial's 4.3.2 warns it is not the
- * Scatter collective): sendbufs[s][pos[s][t*topk+k]] = x[s][t] for every k.
+ * Scatter collective): sendbufs[s][pos[s][t*topk+k]] = x[s][t] for every pair
+ * with a slot (pos outside [0, tokens*topk), the layout's -1, is skipped).
  * x[s]: [tokens, hidden]; sendbufs[s]: [tokens*topk, hidden].  Any dtype.
  */
 int coll_moe_permute(int nranks, const void *const *x, const int32_t *const *pos,
@@ -356,7 +365,10 @@ int coll_moe_expert_scale(int nranks, void *const *recvbufs, const int32_t *expe
  *   out[s][t] = rne( sum_{k=0..topk-1} w[s][t*topk+k] * widen(back[s][pos[s][t*topk+k]]) )
  * with k ascending, the accumulator seeded by the k = 0 product, multiply and
  * add rounded separately (no FMA) and one final rounding: bit-identical to
- * the fold written out.  back[s]: [tokens*topk, hidden] bf16 in s's send-slot
+ * the fold written out.  A pair whose pos is outside [0, tokens*topk) (the
+ * layout's -1) adds no term: the fold runs over the token's other pairs in
+ * order, seeded by the first of them, and a token with none left gets +0.
+ * back[s]: [tokens*topk, hidden] bf16 in s's send-slot
  * order (the output of the reverse All-to-All-v); w[s]: fp32 [tokens, topk];
  * out[s]: bf16 [tokens, hidden], must not overlap back[s].
  */
@@ -376,7 +388,7 @@ int coll_moe_combine(int nranks, const void *const *back, const int32_t *const *
  *   x[s]: [tokens, hidden]; pos, counts, displacements: the outputs of
  *   coll_moe_layout (device arrays); recvbufs[d]: the receive buffers, NULL
  *   allowed for a rank that receives no rows.  Any dtype (a copy).
- * A slot that no block holds is not written (a corrupt layout); the caller
+ * A slot that no block holds (-1: a pair with no expert) is not written; the caller
  * guarantees that every receive buffer holds the rows the layout sends it.
  */
 int coll_moe_dispatch(int nranks, const void *const *x, const int32_t *const *pos,
@@ -399,7 +411,8 @@ int coll_moe_dispatch(int nranks, const void *const *x, const int32_t *const *po
  * expert op, the reverse exchange and the combine are one read of recvbufs
  * (which is not modified).  topk_ids == NULL: the rows are used as they are.
  *   bf16 only; out[s]: [tokens, hidden], must not overlap any recvbufs.
- * A slot that no block holds contributes +0 (a corrupt layout).
+ * A slot that no block holds (the layout's -1 for a pair with no expert)
+ * adds no term, as in coll_moe_combine.
  */
 int coll_moe_combine_recv(int nranks, const void *const *recvbufs, const int32_t *const *pos,
                           const int64_t *sendcounts, const int64_t *sdispls,

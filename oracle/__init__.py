@@ -309,7 +309,8 @@ def all_to_all_v(sends, counts, sdispls, rdispls, recv_rows, row_elems: int,
 
 def moe_layout(ids, E: int):
     """MoE dispatch layout (section 8.4): per-source expert histogram, counts
-    per destination rank, displacements and stable send-slot positions."""
+    per destination rank, displacements and stable send-slot positions.  Ids
+    outside [0, E) are skipped (pos = -1)."""
     ids = [np.ascontiguousarray(x, np.int32) for x in ids]
     R = len(ids)
     T, K = ids[0].shape

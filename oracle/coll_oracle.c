@@ -387,7 +387,11 @@ int oracle_all_to_all_v(int R, const void *const *send, const int64_t *counts,
  *   expert_counts[s][e] = cnt_s[e]
  *   pos[s][t*K + k]   = (sum_{e' < e} cnt_s[e'])
  *                       + number of earlier flat entries of s with expert e
- * i.e. the slot of (t,k) in s's send buffer sorted stably by expert. */
+ * i.e. the slot of (t,k) in s's send buffer sorted stably by expert.
+ * An id outside [0, E) names no expert: its pair is skipped -- no slot
+ * (pos = -1), counted nowhere, no row moved, no term in the combine.  The
+ * pages route only to existing experts; a pair with no expert is read as one
+ * that does not exist. */
 int oracle_moe_layout(int R, const int32_t *const *ids, int T, int K, int E,
                       int64_t *sendcounts, int64_t *sdispls, int64_t *rdispls,
                       int32_t *expert_counts, int32_t *const *pos)
@@ -397,16 +401,13 @@ int oracle_moe_layout(int R, const int32_t *const *ids, int T, int K, int E,
     int64_t *off = (int64_t *)calloc((size_t)E, sizeof(int64_t));
     int64_t *seen = (int64_t *)calloc((size_t)E, sizeof(int64_t));
     if (!off || !seen) { free(off); free(seen); return O_EINVAL; }
-    int rc = O_OK;
-    for (int s = 0; s < R && rc == O_OK; s++) {
+    for (int s = 0; s < R; s++) {
         int32_t *cnt = expert_counts + (size_t)s * E;
         for (int e = 0; e < E; e++) cnt[e] = 0;
         for (int64_t i = 0; i < (int64_t)T * K; i++) {
             int32_t e = ids[s][i];
-            if (e < 0 || e >= E) { rc = O_EINVAL; break; }
-            cnt[e]++;
+            if (e >= 0 && e < E) cnt[e]++;
         }
-        if (rc) break;
         for (int d = 0; d < R; d++) {
             int64_t c = 0;
             for (int e = d * per; e < (d + 1) * per; e++) c += cnt[e];
@@ -418,18 +419,18 @@ int oracle_moe_layout(int R, const int32_t *const *ids, int T, int K, int E,
         for (int e = 0; e < E; e++) { off[e] = acc; acc += cnt[e]; seen[e] = 0; }
         for (int64_t i = 0; i < (int64_t)T * K; i++) {
             int32_t e = ids[s][i];
+            if (e < 0 || e >= E) { pos[s][i] = -1; continue; }
             pos[s][i] = (int32_t)(off[e] + seen[e]);
             seen[e]++;
         }
     }
-    if (rc == O_OK)
-        for (int d = 0; d < R; d++) {
-            int64_t acc = 0;
-            for (int s = 0; s < R; s++) { rdispls[d * R + s] = acc; acc += sendcounts[s * R + d]; }
-        }
+    for (int d = 0; d < R; d++) {
+        int64_t acc = 0;
+        for (int s = 0; s < R; s++) { rdispls[d * R + s] = acc; acc += sendcounts[s * R + d]; }
+    }
     free(off);
     free(seen);
-    return rc;
+    return O_OK;
 }
 
 /* Dispatch permute (an indexed write, [Tut] 4.3.2 / 8.4): the row of token t
@@ -440,9 +441,12 @@ int oracle_moe_permute(int R, const void *const *x, const int32_t *const *pos,
     if (R < 1 || R > 64 || T < 0 || K < 1) return O_EINVAL;
     for (int s = 0; s < R; s++)
         for (int t = 0; t < T; t++)
-            for (int k = 0; k < K; k++)
-                memcpy((char *)send[s] + (size_t)pos[s][(size_t)t * K + k] * row_bytes,
+            for (int k = 0; k < K; k++) {
+                int32_t p = pos[s][(size_t)t * K + k];
+                if (p < 0) continue;                 /* a skipped pair (no expert) */
+                memcpy((char *)send[s] + (size_t)p * row_bytes,
                        (const char *)x[s] + (size_t)t * row_bytes, row_bytes);
+            }
     return O_OK;
 }
 
@@ -474,7 +478,9 @@ int oracle_moe_expert_scale(int R, void *const *recv, const int32_t *expert_coun
 /* Combine ([Tut] 8.4: results return to the token's owner): back[s] holds the
  * expert outputs in s's send-slot order; out[s][t] = rne(sum over k of
  * w[s][t,k] * widen(back[s][pos[s][t,k]])), k ascending, accumulator seeded by
- * the k = 0 product, multiply and add rounded separately, one final rounding. */
+ * the k = 0 product, multiply and add rounded separately, one final rounding.
+ * A skipped pair (pos < 0) adds no term: the fold runs over the token's other
+ * pairs in the same order, seeded by the first of them; none left gives +0. */
 int oracle_moe_combine(int R, const void *const *back, const int32_t *const *pos,
                        const float *const *w, int T, int K, size_t hidden,
                        void *const *out)
@@ -484,11 +490,14 @@ int oracle_moe_combine(int R, const void *const *back, const int32_t *const *pos
         for (int t = 0; t < T; t++)
             for (size_t c = 0; c < hidden; c++) {
                 float acc = 0.0f;
+                int have = 0;                        /* a term has seeded acc */
                 for (int k = 0; k < K; k++) {
                     size_t i = (size_t)t * K + k;
+                    if (pos[s][i] < 0) continue;     /* a skipped pair: no term */
                     const uint16_t *row = (const uint16_t *)back[s] + (size_t)pos[s][i] * hidden;
                     float prod = w[s][i] * oracle_bf16_to_f32(row[c]);
-                    acc = (k == 0) ? prod : acc + prod;
+                    acc = have ? acc + prod : prod;
+                    have = 1;
                 }
                 ((uint16_t *)out[s])[(size_t)t * hidden + c] = oracle_f32_to_bf16(acc);
             }

@@ -1,0 +1,390 @@
+"""Every entry point of the library run under CPU emulation on guarded host
+buffers and compared with the oracle -- TEST INFRASTRUCTURE ONLY.
+
+    python tests/cpuemu/cases.py <family> <start|end>
+
+runs one family of cases, printing a line per case before it starts, and
+exits non-zero on a mismatch.  A kernel that touches memory outside its
+buffers hits a guard page and the process dies with SIGSEGV: the last
+printed line names the case.  Sizes are small but span several tiles plus
+ragged tails; grids use a 4-CU machine (EMU_CUS).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, HERE)
+
+import numpy as np  # noqa: E402
+
+import oracle  # noqa: E402
+from collective_communication_amd import synth  # noqa: E402
+from collective_communication_amd.coll import SIGNATURES  # noqa: E402
+from guarded import Heap, ptr, table  # noqa: E402
+
+import build as emu_build  # noqa: E402
+
+BF16, FP16, FP32, INT32 = 0, 1, 2, 3
+DT = {"bf16": BF16, "fp16": FP16, "fp32": FP32, "int32": INT32}
+OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
+NP = {"bf16": np.uint16, "fp16": np.float16, "fp32": np.float32, "int32": np.int32}
+
+L = None
+H = None
+
+
+def load():
+    global L
+    L = ctypes.CDLL(emu_build.build())
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def case(*what):
+    print("case", *what, flush=True)
+
+
+def ok(rc, what):
+    if rc != 0:
+        raise AssertionError(f"{what}: status {rc}")
+
+
+def same(a, b, what):
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    if a.shape != b.shape or not np.array_equal(a.view(np.uint8), b.view(np.uint8)):
+        bad = np.flatnonzero(a.reshape(-1).view(np.uint8) != b.reshape(-1).view(np.uint8))
+        raise AssertionError(f"{what}: mismatch ({bad.size} bytes, first at byte {bad[:1]})")
+
+
+def gen(dtype, n, seed):
+    if dtype == "int32":
+        return synth.uniform_int32(n, -(1 << 20), 1 << 20, seed)
+    return synth.gaussian(n, 1.0, seed, dtype)
+
+
+# ------------------------------------------------------------------ families
+
+def fam_reduce():
+    for dtype in ("bf16", "fp16", "fp32", "int32"):
+        for R in (1, 2, 3, 4, 8, 16):
+            for n in (1, 9, 4100, 9000 + R):
+                case("allreduce", dtype, R, n)
+                xs = [gen(dtype, n, 17 * R + n + r) for r in range(R)]
+                want = oracle.allreduce(xs, dtype)
+                ins = [H.copy(x) for x in xs]
+                outs = [H.poison(n, NP[dtype]) for _ in range(R)]
+                ok(L.coll_allreduce(R, table(ins), table(outs), n, DT[dtype], 0, None), "allreduce")
+                for r in range(R):
+                    same(outs[r], want[r], f"allreduce rank {r}")
+    for op in ("prod", "max", "min"):
+        case("allreduce op", op)
+        xs = [gen("fp32", 5000, 300 + r) for r in range(8)]
+        want = oracle.allreduce(xs, "fp32", op)
+        ins = [H.copy(x) for x in xs]
+        outs = [H.poison(5000, np.float32) for _ in range(8)]
+        ok(L.coll_allreduce(8, table(ins), table(outs), 5000, FP32, OPS[op], None), op)
+        for r in range(8):
+            same(outs[r], want[r], op)
+    case("allreduce in place, R = 8 (staged through LDS)")
+    xs = [gen("bf16", 12345, 40 + r) for r in range(8)]
+    want = oracle.allreduce(xs, "bf16")
+    bufs = [H.copy(x) for x in xs]
+    ok(L.coll_allreduce(8, table(bufs), table(bufs), 12345, BF16, 0, None), "in place")
+    for r in range(8):
+        same(bufs[r], want[r], "in place")
+    for R, n in ((3, 9), (8, 1000), (5, 4099), (16, 64)):
+        for dtype in ("bf16", "fp32"):
+            case("reduce_scatter", dtype, R, n)
+            xs = [gen(dtype, R * n, 90 + r) for r in range(R)]
+            want = oracle.reduce_scatter(xs, dtype)
+            ins = [H.copy(x) for x in xs]
+            outs = [H.poison(n, NP[dtype]) for _ in range(R)]
+            ok(L.coll_reduce_scatter(R, table(ins), table(outs), n, DT[dtype], 0, None), "rs")
+            for r in range(R):
+                same(outs[r], want[r], f"reduce_scatter rank {r}")
+            case("reduce", dtype, R, n)
+            want = oracle.reduce(xs, R - 1, dtype)
+            out = H.poison(R * n, NP[dtype])
+            ok(L.coll_reduce(R, table(ins), ptr(out), R - 1, R * n, DT[dtype], 0, None), "reduce")
+            same(out, want, "reduce")
+
+
+def fam_copy():
+    for R, n in ((1, 7), (3, 1000), (8, 4100), (8, 8 * 1025 + 3)):
+        case("all_gather", R, n)
+        xs = [gen("bf16", n, 200 + r) for r in range(R)]
+        want = oracle.all_gather(xs)
+        ins = [H.copy(x) for x in xs]
+        outs = [H.poison(R * n, np.uint16) for _ in range(R)]
+        ok(L.coll_all_gather(R, table(ins), table(outs), n, BF16, None), "ag")
+        for r in range(R):
+            same(outs[r], want[r], "all_gather")
+        case("broadcast", R, n)
+        root = R - 1
+        src = H.copy(xs[0])
+        outs = [H.poison(n, np.uint16) for _ in range(R)]
+        outs[root] = src
+        ok(L.coll_broadcast(R, ptr(src), table(outs), root, n, BF16, None), "bcast")
+        for r in range(R):
+            same(outs[r], xs[0], "broadcast")
+        case("scatter", R, n)
+        big = gen("bf16", R * n, 77)
+        src = H.copy(big)
+        outs = [H.poison(n, np.uint16) for _ in range(R)]
+        ok(L.coll_scatter(R, ptr(src), table(outs), 0, n, BF16, None), "scatter")
+        for r, w in enumerate(oracle.scatter(big, R, 0)):
+            same(outs[r], w, "scatter")
+    for R, outer, inner in ((8, 3, 19), (8, 16, 400), (4, 1, 4099), (3, 5, 8)):
+        for dtype in ("fp32", "bf16"):
+            case("gather", R, outer, inner, dtype)
+            xs = [gen(dtype, outer * inner, 400 + r).reshape(outer, inner) for r in range(R)]
+            want = oracle.gather(xs, 0)
+            ins = [H.copy(x) for x in xs]
+            out = H.poison((outer, R * inner), NP[dtype])
+            ok(L.coll_gather(R, table(ins), ptr(out), 0, outer, inner, DT[dtype], None), "gather")
+            same(out, want, "gather")
+
+
+def _a2av_case(R, counts, W, dtype, cap=None, ws=False, gap=0):
+    counts = np.asarray(counts, np.int64)
+    sd, rd = oracle.packed_displs(counts)
+    if gap:
+        sd = sd + gap * np.arange(R)[None, :]          # a hole between blocks
+        rd = rd + gap * np.arange(R)[None, :]
+    send_rows = [int((sd[s] + counts[s]).max(initial=0)) for s in range(R)]
+    recv_rows = [int((rd[d] + counts[:, d]).max(initial=0)) for d in range(R)]
+    sends = [gen(dtype, send_rows[s] * W, 600 + s) for s in range(R)]
+    want = oracle.all_to_all_v([s.reshape(-1) for s in sends], counts, sd, rd,
+                               np.array(recv_rows), W)
+    ins = [H.copy(s) if s.size else None for s in sends]
+    outs = [H.poison(recv_rows[d] * W, NP[dtype]) if recv_rows[d] else None for d in range(R)]
+    tabs = [H.copy(np.ascontiguousarray(t).reshape(-1)) for t in (counts, sd, rd)]
+    capacity = sum(recv_rows) if cap is None else cap
+    es = np.dtype(NP[dtype]).itemsize
+    dt = BF16 if es == 2 else FP32
+    if ws:
+        need = L.coll_all_to_all_v_workspace_bytes(R, capacity, W, dt)
+        work = H.poison(max(need, 256), np.uint8) if need else None
+        ok(L.coll_all_to_all_v_ws(R, table(ins), ptr(tabs[0]), ptr(tabs[1]), table(outs),
+                                  ptr(tabs[2]), W, dt, capacity, ptr(work), need, None), "a2av_ws")
+    else:
+        ok(L.coll_all_to_all_v(R, table(ins), ptr(tabs[0]), ptr(tabs[1]), table(outs),
+                               ptr(tabs[2]), W, dt, capacity, None), "a2av")
+    for d in range(R):
+        if recv_rows[d]:
+            # rows in the gaps are not written: compare the blocks only
+            for s in range(R):
+                a, c = int(rd[d, s]) * W, int(counts[s, d]) * W
+                same(outs[d][a:a + c], want[d][a:a + c], f"a2av block {s}->{d}")
+    return sends, counts, sd, rd, outs
+
+
+def fam_a2av():
+    g = np.random.default_rng(5)
+    for R in (1, 2, 3, 8, 16):
+        for W in (1, 3, 8, 24):
+            case("a2av random", R, W)
+            _a2av_case(R, g.integers(0, 40, size=(R, R)), W, "bf16")
+    case("a2av empty blocks and an empty rank")
+    c = g.integers(0, 30, size=(4, 4))
+    c[:, 2] = 0
+    c[1, :] = 0
+    _a2av_case(4, c, 8, "bf16")
+    case("a2av gapped")
+    _a2av_case(3, g.integers(1, 20, size=(3, 3)), 8, "bf16", gap=5)
+    case("a2av odd-byte rows (chunk kernel)")
+    _a2av_case(4, g.integers(0, 50, size=(4, 4)), 5, "bf16")
+    case("a2av capacity 0 (resident grid)")
+    _a2av_case(3, g.integers(0, 50, size=(3, 3)), 8, "bf16", cap=0)
+    case("a2av capacity below the rows received")
+    _a2av_case(3, g.integers(20, 50, size=(3, 3)), 8, "bf16", cap=10)
+    # the descriptor form (COLL_A2A_DESC_MIN_BYTES=0 in this process)
+    for R, W in ((8, 8), (3, 24), (2, 8), (8, 7168 // 64)):
+        case("a2av descriptor form", R, W)
+        _a2av_case(R, g.integers(0, 60, size=(R, R)), W, "bf16", ws=True)
+    case("a2av descriptor form, capacity below the rows (tail loop)")
+    _a2av_case(4, g.integers(30, 60, size=(4, 4)), 8, "bf16", ws=True, cap=50)
+    case("a2av descriptor form, gapped")
+    _a2av_case(3, g.integers(1, 30, size=(3, 3)), 16, "bf16", ws=True, gap=7)
+
+
+def fam_exchange():
+    for R, n in ((1, 5), (3, 100), (8, 1000), (8, 8 * 1024 + 8)):
+        case("all_to_all", R, n)
+        xs = [gen("bf16", R * n, 800 + r) for r in range(R)]
+        want = oracle.all_to_all(xs)
+        ins = [H.copy(x) for x in xs]
+        outs = [H.poison(R * n, np.uint16) for _ in range(R)]
+        ok(L.coll_all_to_all(R, table(ins), table(outs), n, BF16, None), "a2a")
+        for r in range(R):
+            same(outs[r], want[r], "all_to_all")
+    for R, SL, Hh, D in ((2, 3, 4, 8), (4, 5, 8, 16), (8, 7, 16, 128), (3, 4, 6, 5)):
+        for to_heads in (True, False):
+            case("reshard", R, SL, Hh, D, to_heads)
+            xs = [gen("bf16", SL * Hh * D, 900 + r) for r in range(R)]
+            want = oracle.ulysses(xs, SL, Hh, D, to_heads)
+            ins = [H.copy(x) for x in xs]
+            outs = [H.poison(SL * Hh * D, np.uint16) for _ in range(R)]
+            ok(L.coll_seq_heads_reshard(R, table(ins), table(outs), SL, Hh, D, BF16,
+                                        1 if to_heads else 0, None), "reshard")
+            for r in range(R):
+                same(outs[r], want[r], "reshard")
+
+
+def fam_merge():
+    g = np.random.default_rng(9)
+    for R, rows, D, dtype in ((1, 10, 128, "bf16"), (2, 37, 64, "fp32"), (8, 300, 128, "bf16"),
+                              (4, 10, 5, "bf16"), (16, 30, 16, "fp32"), (3, 9, 1000, "bf16"),
+                              (8, 5, 520, "fp32")):
+        case("lse_merge", R, rows, D, dtype)
+        o = [gen(dtype, rows * D, 1000 + r) for r in range(R)]
+        lse = [(g.normal(size=rows) * 3).astype(np.float32) for _ in range(R)]
+        lse[0][:2] = -np.inf                           # rank 0 empty on two rows
+        if rows > 3:
+            for l in lse:
+                l[3] = -np.inf                         # a row with no keys anywhere
+        want_o, want_l = oracle.lse_merge(o, lse, dtype)
+        ins = [H.copy(x) for x in o]
+        lin = [H.copy(x) for x in lse]
+        outs = [H.poison(rows * D, NP[dtype]) for _ in range(R)]
+        lout = [H.poison(rows, np.float32) for _ in range(R)]
+        lout[R - 1] = None                              # a NULL entry: not written
+        ok(L.coll_lse_merge(R, table(ins), table(lin), table(outs), table(lout), rows, D,
+                            DT[dtype], None), "lse_merge")
+        f = (lambda a: oracle.bf16_to_f32(a).astype(np.float64)) if dtype == "bf16" else \
+            (lambda a: a.astype(np.float64))
+        ulp = 2.0 ** (-7 if dtype == "bf16" else -23)
+        for r in range(R):
+            got, exp = f(outs[r]), f(want_o)
+            mag = np.max(np.abs(exp)) if exp.size else 0
+            if not np.all(np.abs(got - exp) <= 2 * ulp * np.abs(exp) + 1e-5 * (mag + 1)):
+                raise AssertionError(f"lse_merge o rank {r}")
+            if lout[r] is not None and not np.allclose(lout[r], want_l, rtol=1e-5, atol=1e-5,
+                                                       equal_nan=True):
+                raise AssertionError(f"lse_merge L rank {r}")
+        if rows > 3:
+            for r in range(R):
+                if np.any(f(outs[r]).reshape(rows, D)[3] != 0):
+                    raise AssertionError("all-empty row not zero")
+
+
+def _moe(R, E, T, K, Hd, bad=False, seed=5100):
+    ids, ws, xs = [], [], []
+    for s in range(R):
+        i, w = synth.zipf_routing(T, E, K, seed=seed + s)
+        ids.append(i)
+        ws.append(w)
+        xs.append(synth.gaussian((T, Hd), 1.0, seed + 100 + s, "bf16"))
+    if bad:
+        gb = np.random.default_rng(seed)
+        for i in ids:
+            m = gb.random(i.shape) < 0.1
+            i[m] = gb.choice(np.array([-1, E, 1 << 30], np.int32), size=int(m.sum()))
+            if T > 1:
+                i[1, :] = E
+    return ids, ws, xs
+
+
+def _layout(R, E, T, K, ids):
+    id_b = [H.copy(i) for i in ids]
+    sc, sd, rd = (H.poison(R * R, np.int64) for _ in range(3))
+    ec = H.poison(R * E, np.int32)
+    pos = [H.poison((T, K), np.int32) for _ in range(R)]
+    need = L.coll_moe_workspace_bytes(R, T, K, E)
+    work = H.poison(max(need, 256), np.uint8)
+    ok(L.coll_moe_layout(R, table(id_b), T, K, E, ptr(sc), ptr(sd), ptr(rd), ptr(ec),
+                         table(pos), ptr(work), need, None), "layout")
+    return id_b, sc, sd, rd, ec, pos
+
+
+def fam_moe():
+    for R, E, T, K, Hd, bad in ((2, 4, 2, 1, 8, False), (1, 8, 100, 2, 16, False),
+                                (4, 16, 333, 3, 24, False), (8, 256, 150, 8, 64, False),
+                                (2, 8, 50, 2, 5, False), (16, 1024, 40, 8, 8, False),
+                                (2, 16, 40, 10, 16, False), (4, 16, 200, 3, 24, True),
+                                (8, 64, 100, 8, 8, True), (2, 16, 40, 10, 5, True)):
+        case("moe", R, E, T, K, Hd, "bad ids" if bad else "")
+        ids, ws, xs = _moe(R, E, T, K, Hd, bad)
+        want = oracle.moe_pipeline(xs, ids, ws, E)
+        lay = want["layout"]
+        id_b, sc, sd, rd, ec, pos = _layout(R, E, T, K, ids)
+        for key, got in (("sendcounts", sc), ("sdispls", sd), ("rdispls", rd),
+                         ("expert_counts", ec)):
+            same(got.reshape(lay[key].shape), lay[key], key)
+        for s in range(R):
+            same(pos[s], lay["pos"][s], "pos")
+        x_b = [H.copy(x) for x in xs]
+        w_b = [H.copy(w) for w in ws]
+        sends = [H.poison((T * K, Hd), np.uint16) for _ in range(R)]
+        ok(L.coll_moe_permute(R, table(x_b), table(pos), T, K, Hd, BF16, table(sends), None),
+           "permute")
+        nsend = [int(lay["sendcounts"][s].sum()) for s in range(R)]
+        for s in range(R):
+            same(sends[s][:nsend[s]], want["sends"][s][:nsend[s]], "permute")
+        rrows = lay["sendcounts"].sum(axis=0)
+        recvs = [H.poison((int(n), Hd), np.uint16) if n else None for n in rrows]
+        ok(L.coll_all_to_all_v(R, table(sends), ptr(sc), ptr(sd), table(recvs), ptr(rd), Hd,
+                               BF16, int(rrows.sum()), None), "a2av")
+        for d in range(R):
+            if rrows[d]:
+                same(recvs[d].reshape(-1), want["recvs"][d].reshape(-1)[:int(rrows[d]) * Hd], "recv")
+        for cap in (int(rrows.sum()), 0):
+            # the row-descriptor path (capacity known) and the table search (0)
+            ys = [H.copy(r) if r is not None else None for r in recvs]
+            need = L.coll_moe_expert_workspace_bytes(R, E, cap)
+            ews = H.poison(need, np.uint8)
+            ok(L.coll_moe_expert_scale(R, table(ys), ptr(ec), ptr(rd), E, Hd, BF16, cap, ptr(ews),
+                                       need, None), "expert")
+            for d in range(R):
+                if rrows[d]:
+                    same(ys[d].reshape(-1), want["ys"][d].reshape(-1)[:int(rrows[d]) * Hd],
+                         f"expert cap {cap}")
+        backs = [H.poison((T * K, Hd), np.uint16) for _ in range(R)]
+        sc_t = H.copy(np.ascontiguousarray(lay["sendcounts"].T).reshape(-1))
+        ok(L.coll_all_to_all_v(R, table(ys), ptr(sc_t), ptr(rd), table(backs), ptr(sd), Hd,
+                               BF16, T * K * R, None), "a2av back")
+        for s in range(R):
+            same(backs[s].reshape(-1)[:nsend[s] * Hd],
+                 want["backs"][s].reshape(-1)[:nsend[s] * Hd], "back")
+        outs = [H.poison((T, Hd), np.uint16) for _ in range(R)]
+        ok(L.coll_moe_combine(R, table(backs), table(pos), table(w_b), T, K, Hd, BF16,
+                              table(outs), None), "combine")
+        for s in range(R):
+            same(outs[s], want["outs"][s], "combine")
+        # the fused pair
+        recv2 = [H.poison((int(n), Hd), np.uint16) if n else None for n in rrows]
+        ok(L.coll_moe_dispatch(R, table(x_b), table(pos), ptr(sc), ptr(sd), ptr(rd), T, K, Hd,
+                               BF16, table(recv2), None), "dispatch")
+        for d in range(R):
+            if rrows[d]:
+                same(recv2[d], recvs[d], "fused dispatch")
+        outs2 = [H.poison((T, Hd), np.uint16) for _ in range(R)]
+        ok(L.coll_moe_combine_recv(R, table(recv2), table(pos), ptr(sc), ptr(sd), ptr(rd),
+                                   table(w_b), table(id_b), T, K, Hd, BF16, table(outs2), None),
+           "combine_recv")
+        for s in range(R):
+            same(outs2[s], want["outs"][s], "fused combine")
+
+
+FAMILIES = {"reduce": fam_reduce, "copy": fam_copy, "a2av": fam_a2av, "exchange": fam_exchange,
+            "merge": fam_merge, "moe": fam_moe}
+
+
+def main():
+    global H
+    family, place = sys.argv[1], sys.argv[2]
+    H = Heap(place)
+    load()
+    FAMILIES[family]()
+    print("all cases passed", flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -214,6 +214,23 @@ def test_lse_merge_validation(L):
     assert L.coll_lse_merge(0, ok, ok, ok, NULL, 16, 128, 0, NULL) == -1
 
 
+@pytest.mark.parametrize("out_ptrs", [
+    (0x10000, 0x20000),          # lse_out[r] == lse_parts[r] (in place)
+    (0x90000, 0x10000),          # lse_out[1] == lse_parts[0]
+    (0x90000, 0x20000 + 60),     # lse_out[1] starts inside lse_parts[1] (16 rows = 64 B)
+    (0x10000 - 60, 0x90000),     # lse_out[0] ends inside lse_parts[0]
+])
+def test_lse_merge_rejects_lse_outputs_overlapping_inputs(L, out_ptrs):
+    """An LSE output that overlaps any LSE input is rejected on the host
+    before any launch (a row's inputs could be read after L is stored).
+    Disjoint outputs and NULL entries pass these checks; they run in the
+    CPU-emulation and GPU tests, since here nothing may launch."""
+    o = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    lse_in = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    lse_out = (ctypes.c_void_p * 2)(*out_ptrs)
+    assert L.coll_lse_merge(2, o, lse_in, o, lse_out, 16, 128, 0, NULL) == -1
+
+
 # ------------------------------------------------------------- rank arena
 
 def _header_define(name):

@@ -107,6 +107,31 @@ def test_fused_moe_matches_unfused_oracle(R, E, T, K, H):
         assert bits_equal(host(outs[s]).reshape(-1), want["outs"][s].reshape(-1)), s
 
 
+@pytest.mark.parametrize("R,E,T,K,H", [
+    (4, 16, 333, 3, 24),
+    (8, 256, 64, 8, 7168),
+    (2, 16, 40, 10, 5),
+])
+def test_fused_moe_with_bad_expert_ids(R, E, T, K, H):
+    """Pairs whose id names no expert are skipped by the fused dispatch (no
+    row) and the fused combine (no term): receive rows and every output match
+    the oracle on the same ids."""
+    from test_gpu_parity import plant_bad_ids
+    say("moe fused bad ids", R, E, T, K, H)
+    ids, ws = routing(R, E, T, K)
+    ids = plant_bad_ids(ids, E, 91)
+    xs = [synth.gaussian((T, H), 1.0, 5600 + s, "bf16") for s in range(R)]
+    want = oracle.moe_pipeline(xs, ids, ws, E)
+    got = fused_gpu(xs, ids, ws, E)
+    lay = want["layout"]
+    for d in range(R):
+        n = int(lay["sendcounts"][:, d].sum()) * H
+        assert got["recvs"][d].size == n
+        assert bits_equal(got["recvs"][d].reshape(-1), want["recvs"][d].reshape(-1)[:n]), d
+    for s in range(R):
+        assert bits_equal(got["outs"][s].reshape(-1), want["outs"][s].reshape(-1)), s
+
+
 def test_fused_moe_ranks_that_receive_nothing():
     """Every token routes to experts of ranks 0 and 1 only: ranks 2 and 3 get
     empty (NULL) receive buffers and no write."""

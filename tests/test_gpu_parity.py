@@ -436,6 +436,61 @@ def test_moe_pipeline(R, E, T, K, H):
         assert bits_equal(got["ys"][d].reshape(-1)[:n], want["ys"][d].reshape(-1)[:n])
 
 
+def plant_bad_ids(ids, E, seed):
+    """About 7% of the pairs get an id outside [0, E); token 1 of every rank
+    gets nothing but bad ids."""
+    g = np.random.default_rng(seed)
+    bad_vals = np.array([-1, E, E + 100, 2**31 - 1, -2**31], np.int64)
+    out = []
+    for i in ids:
+        i = i.copy()
+        m = g.random(i.shape) < 0.07
+        i[m] = g.choice(bad_vals, size=int(m.sum())).astype(np.int32)
+        if i.shape[0] > 1:
+            i[1, :] = bad_vals[np.arange(i.shape[1]) % bad_vals.size].astype(np.int32)
+        out.append(i)
+    return out
+
+
+@pytest.mark.parametrize("R,E,T,K,H", [
+    (4, 16, 333, 3, 24),
+    (8, 256, 700, 8, 64),
+    (2, 16, 40, 10, 5),       # 10-byte rows, top-10
+    (8, 256, 64, 8, 7168),
+])
+def test_moe_pipeline_with_bad_expert_ids(R, E, T, K, H):
+    """Pairs whose id names no expert are skipped by every stage (no slot,
+    no count, no row, no combine term) and do not disturb any other pair:
+    every table and every row the layout sends matches the oracle on the
+    same ids, and so does every token's output."""
+    say("moe bad ids", R, E, T, K, H)
+    ids, ws = [], []
+    for s in range(R):
+        i, w = synth.zipf_routing(T, E, K, seed=5300 + s)
+        ids.append(i)
+        ws.append(w)
+    ids = plant_bad_ids(ids, E, 77)
+    xs = [synth.gaussian((T, H), 1.0, 5400 + s, "bf16") for s in range(R)]
+    want = oracle.moe_pipeline(xs, ids, ws, E)
+    got = moe_gpu(xs, ids, ws, E)
+    lay = want["layout"]
+    assert np.array_equal(got["sc"], lay["sendcounts"])
+    assert np.array_equal(got["sd"], lay["sdispls"])
+    assert np.array_equal(got["rd"], lay["rdispls"])
+    assert np.array_equal(got["ec"], lay["expert_counts"])
+    assert int(lay["sendcounts"].sum()) < R * T * K           # some pairs really were skipped
+    for s in range(R):
+        assert np.array_equal(got["pos"][s], lay["pos"][s])
+        n = int(lay["sendcounts"][s].sum()) * H               # the rows s sends
+        assert bits_equal(got["sends"][s].reshape(-1)[:n], want["sends"][s].reshape(-1)[:n])
+        assert bits_equal(got["backs"][s].reshape(-1)[:n], want["backs"][s].reshape(-1)[:n])
+        assert bits_equal(got["outs"][s].reshape(-1), want["outs"][s].reshape(-1))
+    for d in range(R):
+        n = int(lay["sendcounts"][:, d].sum()) * H
+        assert bits_equal(got["recvs"][d].reshape(-1)[:n], want["recvs"][d].reshape(-1)[:n])
+        assert bits_equal(got["ys"][d].reshape(-1)[:n], want["ys"][d].reshape(-1)[:n])
+
+
 def test_moe_layout_empty_tokens():
     R, E, K = 4, 8, 2
     say("moe layout T=0")

@@ -564,3 +564,50 @@ def test_lse_merge_bf16_rounds_the_exact_mean_once():
     o, lo = oracle.lse_merge([p.reshape(1, 3) for p in parts], lse, "bf16")
     assert o.reshape(-1).tolist() == [0x3F81, 0xBF81, 0x3F80]
     assert np.allclose(lo, np.log(4.0), atol=1e-6)
+
+
+# ------------------------------------------- expert ids outside [0, E)
+
+def _moe_inputs(R, E, T, K, H, seed):
+    ids, ws, xs = [], [], []
+    for s in range(R):
+        i, w = synth.zipf_routing(T, E, K, seed=seed + s)
+        ids.append(i)
+        ws.append(w)
+        xs.append(synth.gaussian((T, H), 1.0, seed + 50 + s, "bf16"))
+    return ids, ws, xs
+
+
+@pytest.mark.parametrize("bad", [-1, 16, 1 << 30, -(1 << 31)])
+@pytest.mark.parametrize("col", ["last", "first"])
+def test_moe_bad_ids_are_pairs_that_do_not_exist(bad, col):
+    """A pair whose id names no expert is skipped: the pipeline with a whole
+    top-k column of bad ids equals the pipeline run without that column
+    (same counts, displacements and slots, same outputs bit for bit), and
+    the bad pairs get slot -1."""
+    R, E, T, K, H = 4, 16, 37, 3, 8
+    ids, ws, xs = _moe_inputs(R, E, T, K, H, 700)
+    keep = slice(0, K - 1) if col == "last" else slice(1, K)
+    drop = K - 1 if col == "last" else 0
+    bad_ids = [i.copy() for i in ids]
+    for i in bad_ids:
+        i[:, drop] = bad
+    full = oracle.moe_pipeline(xs, bad_ids, ws, E)
+    sub = oracle.moe_pipeline(xs, [np.ascontiguousarray(i[:, keep]) for i in ids],
+                              [np.ascontiguousarray(w[:, keep]) for w in ws], E)
+    for key in ("sendcounts", "sdispls", "rdispls", "expert_counts"):
+        assert np.array_equal(full["layout"][key], sub["layout"][key]), key
+    for s in range(R):
+        assert np.all(full["layout"]["pos"][s][:, drop] == -1)
+        assert np.array_equal(full["layout"]["pos"][s][:, keep], sub["layout"]["pos"][s])
+        assert np.array_equal(full["outs"][s], sub["outs"][s])
+
+
+def test_moe_token_with_only_bad_ids_gets_zero():
+    """Every pair of a token skipped: no term, the output row is +0."""
+    R, E, T, K, H = 2, 8, 10, 2, 8
+    ids, ws, xs = _moe_inputs(R, E, T, K, H, 900)
+    ids[1][3, :] = [E, -5]
+    out = oracle.moe_pipeline(xs, ids, ws, E)["outs"]
+    assert np.all(out[1][3] == 0)
+    assert np.any(out[1][2] != 0) and np.any(out[0][3] != 0)
