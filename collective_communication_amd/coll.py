@@ -47,6 +47,8 @@ SIGNATURES = {
     "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp]),
     "coll_all_to_all_v_workspace_bytes": (_sz, [_i, _sz, _sz, _i]),
     "coll_all_to_all_v_ws": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _sz, _vp]),
+    "coll_all_to_all_v_reverse": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _sz,
+                                       _vp]),
     "coll_all_to_all": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_seq_heads_reshard": (_i, [_i, _vp, _vp, _sz, _sz, _sz, _i, _i, _vp]),
     "coll_lse_merge": (_i, [_i, _vp, _vp, _vp, _vp, _sz, _sz, _i, _vp]),
@@ -367,6 +369,28 @@ def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
     ws_bytes = workspace.numel() * workspace.element_size()
     return _issue("coll_all_to_all_v_ws", "all_to_all_v", stream, *args,
                   _dev(workspace, "workspace"), ws_bytes)
+
+
+def all_to_all_v_reverse(recvs, sendcounts, sdispls, sends, rdispls, row_elems: int,
+                         stream=None, workspace=None, capacity=None):
+    """The reverse of all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls):
+    every block of ``recvs`` goes back to its place in ``sends``, reading the
+    forward tables as they are (no transposed count matrix).  ``workspace``:
+    as all_to_all_v, sized with all_to_all_v_workspace_bytes(recvs, sends, ...).
+    ``capacity``: rows the launch is sized for (default: the rows ``sends``
+    holds)."""
+    R, dt, mult, capacity = _a2av_shape(recvs, sends, row_elems, "all_to_all_v_reverse",
+                                        capacity)
+    for t, name in ((sendcounts, "sendcounts"), (sdispls, "sdispls"), (rdispls, "rdispls")):
+        if t.dtype != torch.int64 or t.numel() != R * R:
+            raise ValueError(f"all_to_all_v_reverse: {name} must be int64 [R*R] on the device")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    return _issue("coll_all_to_all_v_reverse", "all_to_all_v_reverse", stream, R,
+                  _table(recvs, "recv", R), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
+                  _table(sends, "send", R), _dev(rdispls, "rdispls"), row_elems * mult, dt,
+                  capacity, ws_ptr, ws_bytes)
 
 
 def all_to_all(sends, recvs, stream=None):

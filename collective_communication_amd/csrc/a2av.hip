@@ -19,6 +19,16 @@ namespace coll {
 namespace {
 
 constexpr int kMaxBlocks = COLL_MAX_RANKS * COLL_MAX_RANKS;   // 256
+
+// Count of block (s, d) -- the rows source s sends to destination d: entry
+// s*R+d of the count table, or d*R+s when the tables are those of the forward
+// exchange and this call is its reverse (ct = 1).  The displacements are read
+// as sdispls[s*R+d] (source side) and rdispls[d*R+s] (destination side) in
+// both cases: the reverse passes the forward rdispls as its sdispls and the
+// forward sdispls as its rdispls.
+__device__ __forceinline__ int count_index(int ct, int R, int s, int d) {
+  return ct ? d * R + s : s * R + d;
+}
 #ifndef COLL_A2A_U
 #define COLL_A2A_U 4
 #endif
@@ -56,7 +66,7 @@ __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
 template <int B, bool NT, int UN, int BS, bool SMALL>
 __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_t *counts,
                                           const int64_t *sdispls, const int64_t *rdispls,
-                                          uint64_t row_units) {
+                                          int ct, uint64_t row_units) {
   using U = typename UnitT<B>::T;
   constexpr int kTab = SMALL ? 64 : kMaxBlocks;
   __shared__ uint64_t s_end[kTab];   // inclusive end of block b in the global unit space
@@ -71,7 +81,8 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
       const int b = threadIdx.x;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
-      const int64_t c = counts[bb], sdv = sdispls[bb], rdv = rdispls[d * R + s];
+      const int64_t c = counts[count_index(ct, R, s, d)], sdv = sdispls[bb],
+                    rdv = rdispls[d * R + s];
       const uint64_t len = (b < nb && c > 0) ? (uint64_t)c * row_units : 0;
       const uint64_t incl = wave_incl_scan(len);
       if (b < nb) {
@@ -97,7 +108,7 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
       const int b = lane * 4 + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
-      cnt[j] = counts[bb];
+      cnt[j] = counts[count_index(ct, R, s, d)];
       sdv[j] = sdispls[bb];
       rdv[j] = rdispls[d * R + s];
     }
@@ -182,31 +193,31 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
 template <int B, bool NT>
 __global__ __launch_bounds__(kA2aBlock) void a2av_kernel(RankPtrs p, int R, const int64_t *counts,
                                                       const int64_t *sdispls,
-                                                      const int64_t *rdispls, uint64_t row_units) {
-  a2av_body<B, NT, kA2aU, kA2aBlock, false>(p, R, counts, sdispls, rdispls, row_units);
+                                                      const int64_t *rdispls, int ct, uint64_t row_units) {
+  a2av_body<B, NT, kA2aU, kA2aBlock, false>(p, R, counts, sdispls, rdispls, ct, row_units);
 }
 template <int B, bool NT>
 __global__ __launch_bounds__(kA2aBlock) void a2av_kernel8(RankPtrs p, int R, const int64_t *counts,
                                                        const int64_t *sdispls,
-                                                       const int64_t *rdispls, uint64_t row_units) {
-  a2av_body<B, NT, kA2aU, kA2aBlock, true>(p, R, counts, sdispls, rdispls, row_units);
+                                                       const int64_t *rdispls, int ct, uint64_t row_units) {
+  a2av_body<B, NT, kA2aU, kA2aBlock, true>(p, R, counts, sdispls, rdispls, ct, row_units);
 }
 // Resident grid (up to 256 MiB): kA2aResU units per lane per tile.
 template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void a2av_res_kernel(RankPtrs p, int R,
                                                           const int64_t *counts,
                                                           const int64_t *sdispls,
-                                                          const int64_t *rdispls,
+                                                          const int64_t *rdispls, int ct,
                                                           uint64_t row_units) {
-  a2av_body<B, NT, kA2aResU, kBlock, false>(p, R, counts, sdispls, rdispls, row_units);
+  a2av_body<B, NT, kA2aResU, kBlock, false>(p, R, counts, sdispls, rdispls, ct, row_units);
 }
 template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void a2av_res_kernel8(RankPtrs p, int R,
                                                            const int64_t *counts,
                                                            const int64_t *sdispls,
-                                                           const int64_t *rdispls,
+                                                           const int64_t *rdispls, int ct,
                                                            uint64_t row_units) {
-  a2av_body<B, NT, kA2aResU, kBlock, true>(p, R, counts, sdispls, rdispls, row_units);
+  a2av_body<B, NT, kA2aResU, kBlock, true>(p, R, counts, sdispls, rdispls, ct, row_units);
 }
 
 // Rows whose size or buffers do not allow 16-byte units on every row (the
@@ -242,7 +253,7 @@ template <bool NT, int UN, bool FAST>
 __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
                                                             const int64_t *counts,
                                                             const int64_t *sdispls,
-                                                            const int64_t *rdispls,
+                                                            const int64_t *rdispls, int ct,
                                                             uint64_t row_bytes) {
   __shared__ uint64_t s_end[kMaxBlocks];   // inclusive end of block b, in chunks
   __shared__ uint64_t s_src[kMaxBlocks];   // source byte address of the block's chunk 0
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
       const int b = lane * 4 + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
-      cnt[j] = counts[bb];
+      cnt[j] = counts[count_index(ct, R, s, d)];
       sdv[j] = sdispls[bb];
       rdv[j] = rdispls[d * R + s];
     }
@@ -454,7 +465,7 @@ __device__ __forceinline__ uint64_t desc_tile(uint64_t i) {
 // General table build (R <= 16, four blocks per lane of wave 0), as in a2av_body.
 template <int B>
 __device__ __forceinline__ void desc_table(const RankPtrs &p, int R, const int64_t *counts,
-                                           const int64_t *sdispls, const int64_t *rdispls,
+                                           const int64_t *sdispls, const int64_t *rdispls, int ct,
                                            uint64_t row_units, uint64_t *s_end, uint64_t *s_src,
                                            uint64_t *s_dst) {
   const int nb = R * R;
@@ -467,7 +478,7 @@ __device__ __forceinline__ void desc_table(const RankPtrs &p, int R, const int64
     const int b = lane * 4 + j;
     const int bb = b < nb ? b : 0;
     const int s = bb / R, d = bb - s * R;
-    cnt[j] = counts[bb];
+    cnt[j] = counts[count_index(ct, R, s, d)];
     sdv[j] = sdispls[bb];
     rdv[j] = rdispls[d * R + s];
   }
@@ -549,12 +560,13 @@ __device__ __forceinline__ void desc_units(uint64_t sb, uint64_t db, uint64_t en
 template <int B>
 __global__ __launch_bounds__(kBlock) void a2av_desc_build(RankPtrs p, int R, const int64_t *counts,
                                                          const int64_t *sdispls,
-                                                         const int64_t *rdispls,
+                                                         const int64_t *rdispls, int ct,
                                                          uint64_t row_units, uint32_t *idx,
                                                          uint64_t ndesc, A2aBlk *blk) {
   __shared__ uint64_t s_end[kMaxBlocks], s_src[kMaxBlocks], s_dst[kMaxBlocks];
   const int nb = R * R;
-  if (threadIdx.x < 64) desc_table<B>(p, R, counts, sdispls, rdispls, row_units, s_end, s_src, s_dst);
+  if (threadIdx.x < 64)
+    desc_table<B>(p, R, counts, sdispls, rdispls, ct, row_units, s_end, s_src, s_dst);
   __syncthreads();
   const uint64_t total = s_end[nb - 1];
   const uint64_t more = total > ndesc * kDescTile ? 1 : 0;
@@ -616,7 +628,7 @@ __global__ __launch_bounds__(kDescLanes) void a2av_desc_kernel(const uint32_t *_
 }  // namespace
 
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
+                const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
                 size_t rows_capacity) {
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
@@ -645,16 +657,16 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
     const bool small = COLL_A2A_SMALL && R <= 8;
     if (resident && small)
       COLL_UNIT_SWITCH(a2av_res_kernel8, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts,
-                       sdispls, rdispls, row_units);
+                       sdispls, rdispls, ct, row_units);
     else if (resident)
       COLL_UNIT_SWITCH(a2av_res_kernel, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts,
-                       sdispls, rdispls, row_units);
+                       sdispls, rdispls, ct, row_units);
     else if (small)
       COLL_UNIT_SWITCH_BLOCK(a2av_kernel8, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, R,
-                             counts, sdispls, rdispls, row_units);
+                             counts, sdispls, rdispls, ct, row_units);
     else
       COLL_UNIT_SWITCH_BLOCK(a2av_kernel, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, R,
-                             counts, sdispls, rdispls, row_units);
+                             counts, sdispls, rdispls, ct, row_units);
   } else {
     // chunks: at most capacity bytes / 16 plus one partial chunk per block
     if (rows_capacity > 0) {
@@ -664,7 +676,7 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
     if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
 #define COLL_A2A_CHUNK(NTV, UNV, FASTV)                                                          \
   hipLaunchKernelGGL((a2av_chunk_kernel<NTV, UNV, FASTV>), dim3(g), dim3(kBlock), 0, L.stream,  \
-                     p, R, counts, sdispls, rdispls, (uint64_t)row_bytes)
+                     p, R, counts, sdispls, rdispls, ct, (uint64_t)row_bytes)
     if (L.a2a_nt && resident) COLL_A2A_CHUNK(true, kA2aResU, true);
     else if (L.a2a_nt) COLL_A2A_CHUNK(true, kA2aU, false);
     else if (resident) COLL_A2A_CHUNK(false, kA2aResU, true);
@@ -684,18 +696,18 @@ size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_
 }
 
 int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                   const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
+                   const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
                    size_t rows_capacity, void *ws) {
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
   // rows that are not whole 16-byte units, or no capacity: the plain form
   if (copy_unit(bits) != 16 || rows_capacity == 0)
-    return launch_a2av(L, R, p, counts, sdispls, rdispls, row_bytes, rows_capacity);
+    return launch_a2av(L, R, p, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
   const uint64_t row_units = row_bytes / 16;
   const uint64_t cap_units = (uint64_t)rows_capacity * row_units;
   const uint64_t ndesc = (cap_units + kDescTile - 1) / kDescTile;
   if (ndesc == 0 || ndesc > 0x7FFFFFFFull)     // empty rows, or more tiles than one grid holds
-    return launch_a2av(L, R, p, counts, sdispls, rdispls, row_bytes, rows_capacity);
+    return launch_a2av(L, R, p, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
   A2aBlk *blk = reinterpret_cast<A2aBlk *>(ws);
   uint32_t *idx = reinterpret_cast<uint32_t *>(blk + (size_t)R * R);   // two indices per word
   // descriptor writers: a resident grid (COLL_DESC_BUILD_WGS per CU), no
@@ -704,7 +716,7 @@ int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *cou
   const uint64_t gneed = (pairs + kBlock - 1) / kBlock;
   const uint64_t gres = (uint64_t)L.num_cus * kDescBuildWgs;
   hipLaunchKernelGGL((a2av_desc_build<16>), dim3((unsigned)(gneed < gres ? gneed : gres)),
-                     dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, row_units, idx,
+                     dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, ct, row_units, idx,
                      ndesc, blk);
   if (L.a2a_nt)
     hipLaunchKernelGGL((a2av_desc_kernel<16, true>), dim3((unsigned)ndesc), dim3(kDescLanes), 0,

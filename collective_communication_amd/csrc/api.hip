@@ -262,7 +262,7 @@ int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcou
   }
   if (recv_rows_capacity > ((size_t)1 << 48) / (row_elems * dtype_size(dtype)))
     return COLL_ERR_INVALID_ARG;
-  return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls,
+  return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, 0,
                      row_elems * dtype_size(dtype), recv_rows_capacity);
 }
 
@@ -275,10 +275,13 @@ size_t coll_all_to_all_v_workspace_bytes(int R, size_t recv_rows_capacity, size_
   return a2av_workspace_bytes(R, recv_rows_capacity, row_bytes, knobs().a2a_desc_bytes);
 }
 
-int coll_all_to_all_v_ws(int R, const void *const *sendbufs, const int64_t *sendcounts,
-                         const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
-                         size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+// The workspace form, forward (ct = 0) or reverse (ct = 1: the tables are the
+// forward exchange's, sendbufs are its receive buffers and recvbufs its send
+// buffers, sdispls its rdispls and rdispls its sdispls).
+static int a2av_ws_call(int R, const void *const *sendbufs, const int64_t *sendcounts,
+                        const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
+                        int ct, size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
+                        void *workspace, size_t workspace_bytes, void *stream) {
   if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
   if (row_elems == 0) return COLL_OK;
   if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
@@ -296,10 +299,48 @@ int coll_all_to_all_v_ws(int R, const void *const *sendbufs, const int64_t *send
     p.out[r] = recvbufs[r];
   }
   if (need == 0)
-    return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, row_bytes,
+    return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, ct, row_bytes,
                        recv_rows_capacity);
-  return launch_a2av_ws(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, row_bytes,
+  return launch_a2av_ws(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, ct, row_bytes,
                         recv_rows_capacity, workspace);
+}
+
+int coll_all_to_all_v_ws(int R, const void *const *sendbufs, const int64_t *sendcounts,
+                         const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
+                         size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  return a2av_ws_call(R, sendbufs, sendcounts, sdispls, recvbufs, rdispls, 0, row_elems, dtype,
+                      recv_rows_capacity, workspace, workspace_bytes, stream);
+}
+
+int coll_all_to_all_v_reverse(int R, const void *const *recvbufs, const int64_t *sendcounts,
+                              const int64_t *sdispls, void *const *sendbufs,
+                              const int64_t *rdispls, size_t row_elems, coll_dtype_t dtype,
+                              size_t send_rows_capacity, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  // data moves from the forward receive buffers back to the forward send
+  // buffers: the forward rdispls locate the source rows, sdispls the
+  // destination rows, and the counts are read transposed.  No workspace:
+  // the plain form.
+  if (!workspace && workspace_bytes == 0) {
+    if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+    if (row_elems == 0) return COLL_OK;
+    if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
+      return COLL_ERR_INVALID_ARG;
+    if (!sendbufs || !recvbufs) return COLL_ERR_INVALID_ARG;
+    const size_t row_bytes = row_elems * dtype_size(dtype);
+    if (send_rows_capacity > ((size_t)1 << 48) / row_bytes) return COLL_ERR_INVALID_ARG;
+    RankPtrs p{};
+    for (int r = 0; r < R; r++) {     // NULL is allowed: a rank that moves no rows
+      p.in[r] = recvbufs[r];
+      p.out[r] = sendbufs[r];
+    }
+    return launch_a2av(launch_ctx(stream), R, p, sendcounts, rdispls, sdispls, 1, row_bytes,
+                       send_rows_capacity);
+  }
+  return a2av_ws_call(R, reinterpret_cast<const void *const *>(recvbufs), sendcounts, rdispls,
+                      sendbufs, sdispls, 1, row_elems, dtype, send_rows_capacity, workspace,
+                      workspace_bytes, stream);
 }
 
 int coll_all_to_all(int R, const void *const *sendbufs, void *const *recvbufs,

@@ -437,12 +437,14 @@ int launch_reshard(const Launch &L, int R, const RankPtrs &p, size_t seq_local,
                    size_t chunk_bytes, bool to_heads);
 int launch_lse_merge(const Launch &L, int R, const RankPtrs &o, const PtrTable &lse_in,
                      const MutPtrTable &lse_out, size_t rows, size_t D, int dt);
+// ct = 1: counts is read transposed (the reverse of the exchange whose
+// tables these are; see count_index in a2av.hip)
 int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
+                const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
                 size_t rows_capacity);
 size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_t min_bytes);
 int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                   const int64_t *sdispls, const int64_t *rdispls, size_t row_bytes,
+                   const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
                    size_t rows_capacity, void *ws);
 
 constexpr int kMoeMaxExperts = 1024;

@@ -234,6 +234,29 @@ int coll_all_to_all_v_ws(int nranks, const void *const *sendbufs, const int64_t 
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The reverse of an All-to-All-v, from that exchange's own tables -- tutorial
+ * section 8.4 (after the experts, results return to the token's owner in one
+ * more exchange).  With the forward call's sendcounts, sdispls and rdispls:
+ *   sendbufs[s][(sdispls[s*R+d] + j) * row_elems + c]
+ *        = recvbufs[d][(rdispls[d*R+s] + j) * row_elems + c],  j < sendcounts[s*R+d],
+ * i.e. every block goes back to where it came from.  This equals
+ * coll_all_to_all_v with the count matrix transposed and the two displacement
+ * tables swapped, without building the transposed matrix (no extra launch).
+ *   recvbufs: the forward exchange's receive buffers (read here);
+ *   sendbufs: the forward exchange's send buffers (written here);
+ *   send_rows_capacity: an upper bound of the rows moved, here the rows of
+ *   the send buffers together (launch shape only, as recv_rows_capacity).
+ * workspace / workspace_bytes: as coll_all_to_all_v_ws (size from
+ * coll_all_to_all_v_workspace_bytes with send_rows_capacity); NULL and 0
+ * select the plain form.  Errors as coll_all_to_all_v_ws.
+ */
+int coll_all_to_all_v_reverse(int nranks, const void *const *recvbufs, const int64_t *sendcounts,
+                              const int64_t *sdispls, void *const *sendbufs,
+                              const int64_t *rdispls, size_t row_elems, coll_dtype_t dtype,
+                              size_t send_rows_capacity, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
  * Uniform all-to-all -- all_to_all_single with equal splits (sglang PR 27492
  * digest; tutorial section 8.1's figure): sendbufs[s] holds nranks chunks of
  * count_per_peer elements, chunk d for rank d; rank d receives them ordered

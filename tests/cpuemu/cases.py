@@ -183,6 +183,21 @@ def _a2av_case(R, counts, W, dtype, cap=None, ws=False, gap=0):
             for s in range(R):
                 a, c = int(rd[d, s]) * W, int(counts[s, d]) * W
                 same(outs[d][a:a + c], want[d][a:a + c], f"a2av block {s}->{d}")
+    # the reverse from the same tables restores every block of the send buffers
+    backs = [H.poison(send_rows[s] * W, NP[dtype]) if send_rows[s] else None for s in range(R)]
+    bcap = sum(send_rows) if cap is None else cap
+    work = None
+    need = 0
+    if ws:
+        need = L.coll_all_to_all_v_workspace_bytes(R, bcap, W, dt)
+        work = H.poison(max(need, 256), np.uint8) if need else None
+    ok(L.coll_all_to_all_v_reverse(R, table(outs), ptr(tabs[0]), ptr(tabs[1]), table(backs),
+                                   ptr(tabs[2]), W, dt, bcap, ptr(work), need, None), "reverse")
+    for s in range(R):
+        for d in range(R):
+            a, c = int(sd[s, d]) * W, int(counts[s, d]) * W
+            if c:
+                same(backs[s][a:a + c], sends[s].reshape(-1)[a:a + c], f"reverse block {d}->{s}")
     return sends, counts, sd, rd, outs
 
 
@@ -353,6 +368,17 @@ def fam_moe():
         for s in range(R):
             same(backs[s].reshape(-1)[:nsend[s] * Hd],
                  want["backs"][s].reshape(-1)[:nsend[s] * Hd], "back")
+        # the same return through the reverse call on the forward tables, plain
+        # and with a workspace (the descriptor form in this process)
+        for use_ws in (False, True):
+            backs2 = [H.poison((T * K, Hd), np.uint16) for _ in range(R)]
+            need = L.coll_all_to_all_v_workspace_bytes(R, T * K * R, Hd, BF16) if use_ws else 0
+            work = H.poison(max(need, 256), np.uint8) if need else None
+            ok(L.coll_all_to_all_v_reverse(R, table(ys), ptr(sc), ptr(sd), table(backs2), ptr(rd),
+                                           Hd, BF16, T * K * R, ptr(work), need, None), "reverse")
+            for s in range(R):
+                same(backs2[s].reshape(-1)[:nsend[s] * Hd],
+                     want["backs"][s].reshape(-1)[:nsend[s] * Hd], f"reverse ws={use_ws}")
         outs = [H.poison((T, Hd), np.uint16) for _ in range(R)]
         ok(L.coll_moe_combine(R, table(backs), table(pos), table(w_b), T, K, Hd, BF16,
                               table(outs), None), "combine")
