@@ -54,6 +54,7 @@ SIGNATURES = {
     "coll_lse_merge": (_i, [_i, _vp, _vp, _vp, _vp, _sz, _sz, _i, _vp]),
     "coll_moe_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "coll_moe_layout": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "coll_moe_layout_noalloc": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_expert_workspace_bytes": (_sz, [_i, _i, _sz]),
     "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _sz, _vp]),
@@ -468,6 +469,30 @@ def moe_layout(topk_ids, n_experts: int, sendcounts, sdispls, rdispls, expert_co
                   n_experts, _dev(sendcounts, "sc"), _dev(sdispls, "sd"), _dev(rdispls, "rd"),
                   _dev(expert_counts, "ec"), _table(pos, "pos", R), _dev(workspace, "ws"),
                   ws_bytes)
+
+
+def moe_layout_noalloc(topk_ids, n_experts: int, sendcounts, sdispls, rdispls, expert_counts,
+                       pos, stream=None):
+    """moe_layout without a workspace: the scratch is the library's per-GPU
+    device array (at most COLL_MOE_NOALLOC_MAX_BYTES of layout workspace);
+    nothing is allocated.  Calls that overlap on one GPU must not be issued."""
+    R = _ranks(topk_ids, "moe_layout_noalloc")
+    T, K = topk_ids[0].shape
+    for t in topk_ids:
+        if t.dtype != torch.int32 or tuple(t.shape) != (T, K):
+            raise ValueError("moe_layout_noalloc: ids must be int32 [T, K] on every rank")
+    for t in pos:
+        if t.dtype != torch.int32 or t.numel() != T * K:
+            raise ValueError("moe_layout_noalloc: pos must be int32 [T, K] on every rank")
+    for t in (sendcounts, sdispls, rdispls):
+        if t.dtype != torch.int64 or t.numel() != R * R:
+            raise ValueError("moe_layout_noalloc: count tables are int64 [R*R]")
+    if expert_counts.dtype != torch.int32 or expert_counts.numel() != R * n_experts:
+        raise ValueError("moe_layout_noalloc: expert_counts is int32 [R*E]")
+    return _issue("coll_moe_layout_noalloc", "moe_layout_noalloc", stream, R,
+                  _table(topk_ids, "ids", R), T, K, n_experts, _dev(sendcounts, "sc"),
+                  _dev(sdispls, "sd"), _dev(rdispls, "rd"), _dev(expert_counts, "ec"),
+                  _table(pos, "pos", R))
 
 
 def moe_permute(xs, pos, sends, stream=None):

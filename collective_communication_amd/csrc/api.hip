@@ -427,6 +427,26 @@ int coll_moe_layout(int R, const int32_t *const *topk_ids, int tokens, int topk,
                            sdispls, rdispls, expert_counts, ps, workspace);
 }
 
+int coll_moe_layout_noalloc(int R, const int32_t *const *topk_ids, int tokens, int topk,
+                            int n_experts, int64_t *sendcounts, int64_t *sdispls,
+                            int64_t *rdispls, int32_t *expert_counts, int32_t *const *pos,
+                            void *stream) {
+  const size_t need = coll_moe_workspace_bytes(R, tokens, topk, n_experts);
+  if (need == 0 || need > kMoeStaticBytes) return COLL_ERR_INVALID_ARG;
+  if (!sendcounts || !sdispls || !rdispls || !expert_counts) return COLL_ERR_INVALID_ARG;
+  PtrTable ids{};
+  MutPtrTable ps{};
+  if (tokens > 0) {
+    if (!fill_in(R, reinterpret_cast<const void *const *>(topk_ids), ids.p) ||
+        !fill_out(R, reinterpret_cast<void *const *>(pos), ps.p))
+      return COLL_ERR_INVALID_ARG;
+  }
+  void *scratch = moe_static_scratch();
+  if (!scratch) return COLL_ERR_HIP;
+  return launch_moe_layout(launch_ctx(stream), R, ids, tokens, topk, n_experts, sendcounts,
+                           sdispls, rdispls, expert_counts, ps, scratch);
+}
+
 int coll_moe_permute(int R, const void *const *x, const int32_t *const *pos, int tokens, int topk,
                      size_t hidden, coll_dtype_t dtype, void *const *sendbufs, void *stream) {
   if (!ranks_ok(R) || !dtype_ok(dtype) || tokens < 0 || topk < 1) return COLL_ERR_INVALID_ARG;

@@ -448,6 +448,10 @@ int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *cou
                    size_t rows_capacity, void *ws);
 
 constexpr int kMoeMaxExperts = 1024;
+// Scratch of coll_moe_layout_noalloc: a device array of this many bytes per
+// GPU, and its device address on the current device (NULL on failure).
+constexpr size_t kMoeStaticBytes = 4u << 20;
+void *moe_static_scratch();
 size_t moe_workspace_bytes(int R, int T, int K, int E);
 size_t moe_expert_table_bytes(int R, int E);
 size_t moe_expert_workspace_bytes(int R, int E, size_t rows_capacity);

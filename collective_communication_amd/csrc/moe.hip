@@ -998,6 +998,32 @@ int launch_moe_layout(const Launch &L, int R, const PtrTable &ids, int T, int K,
   return hip_status();
 }
 
+// ------------------------------------------------- layout without a workspace
+// The layout's scratch for callers that cannot allocate: a device array of
+// kMoeStaticBytes that each GPU holds for the life of the process.  In host
+// code `moe_scratch` names a host-side stand-in, not device memory, so its
+// device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and only that address is passed to kernels.  Every
+// call on a GPU shares its array: calls that overlap on one GPU race, and
+// nothing in it needs clearing (the histogram kernel writes every count the
+// later kernels read).
+namespace {
+static __device__ __align__(256) unsigned char moe_scratch[kMoeStaticBytes];
+constexpr int kMaxScratchDevices = 64;
+void *g_moe_scratch[kMaxScratchDevices];
+}  // namespace
+
+void *moe_static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void *p = __atomic_load_n(&g_moe_scratch[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(moe_scratch)) != hipSuccess || !p) return nullptr;
+    __atomic_store_n(&g_moe_scratch[dev], p, __ATOMIC_RELEASE);
+  }
+  return p;
+}
+
 int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable &pos, int T,
                        int K, size_t row_bytes, const MutPtrTable &send) {
   uintptr_t bits = row_bytes;

@@ -335,6 +335,25 @@ int coll_moe_layout(int nranks, const int32_t *const *topk_ids, int tokens, int 
                     size_t workspace_bytes, void *stream);
 
 /*
+ * The layout with no workspace argument, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as coll_moe_layout
+ * without workspace/workspace_bytes; its scratch is a device array of
+ * COLL_MOE_NOALLOC_MAX_BYTES that the library holds on each GPU it runs on
+ * until the process ends (nothing is allocated per call).  Sizes whose
+ * coll_moe_workspace_bytes exceeds that maximum return COLL_ERR_INVALID_ARG
+ * (it holds e.g. 8 ranks x 65,000 tokens x top-8 of 256 experts).  Every call
+ * on one GPU uses the same array: calls that may overlap on a GPU (other
+ * streams, other threads) race and must not be issued.  COLL_ERR_HIP if the
+ * array's device address cannot be obtained.
+ */
+#define COLL_MOE_NOALLOC_MAX_BYTES (4u << 20)
+int coll_moe_layout_noalloc(int nranks, const int32_t *const *topk_ids, int tokens, int topk,
+                            int n_experts, int64_t *sendcounts, int64_t *sdispls,
+                            int64_t *rdispls, int32_t *expert_counts, int32_t *const *pos,
+                            void *stream);
+
+/*
  * Dispatch permute (an indexed write; the tutorial's 4.3.2 warns it is not the
  * Scatter collective): sendbufs[s][pos[s][t*topk+k]] = x[s][t] for every pair
  * with a slot (pos outside [0, tokens*topk), the layout's -1, is skipped).

@@ -335,6 +335,15 @@ def fam_moe():
             same(got.reshape(lay[key].shape), lay[key], key)
         for s in range(R):
             same(pos[s], lay["pos"][s], "pos")
+        # the layout without a workspace (the library's static scratch)
+        tabs2 = [H.poison(R * R, np.int64) for _ in range(3)] + [H.poison(R * E, np.int32)]
+        pos2 = [H.poison((T, K), np.int32) for _ in range(R)]
+        ok(L.coll_moe_layout_noalloc(R, table(id_b), T, K, E, *[ptr(t) for t in tabs2],
+                                     table(pos2), None), "layout_noalloc")
+        for a, b in zip(tabs2, (sc, sd, rd, ec)):
+            same(a, b, "layout_noalloc tables")
+        for s in range(R):
+            same(pos2[s], pos[s], "layout_noalloc pos")
         x_b = [H.copy(x) for x in xs]
         w_b = [H.copy(w) for w in ws]
         sends = [H.poison((T * K, Hd), np.uint16) for _ in range(R)]

@@ -106,6 +106,23 @@ def test_moe_workspace_and_layout_validation(L):
     assert L.coll_moe_layout(2, t, 10, 2, 4, 0x100, 0x200, 0x300, 0x400, t, 0x1008, need, NULL) == -1
 
 
+def test_moe_layout_noalloc_validation(L):
+    """The no-allocation layout refuses, on the host, any size whose workspace
+    would exceed its per-GPU array, and the usual bad arguments."""
+    assert _header_define("COLL_MOE_NOALLOC_MAX_BYTES").strip() == "(4u << 20)"
+    limit = 4 << 20
+    t16 = (ctypes.c_void_p * 16)(*range(0x1000, 0x11000, 0x1000))
+    assert L.coll_moe_workspace_bytes(16, 10000, 8, 1024) > limit
+    assert L.coll_moe_layout_noalloc(16, t16, 10000, 8, 1024, 0x100, 0x200, 0x300, 0x400, t16,
+                                     NULL) == -1
+    assert L.coll_moe_workspace_bytes(8, 65000, 8, 256) <= limit       # the header's example
+    assert L.coll_moe_workspace_bytes(8, 65409, 8, 256) > limit
+    t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.coll_moe_layout_noalloc(2, t, 10, 2, 3, 0x100, 0x200, 0x300, 0x400, t, NULL) == -1
+    assert L.coll_moe_layout_noalloc(2, t, 10, 2, 4, NULL, 0x200, 0x300, 0x400, t, NULL) == -1
+    assert L.coll_moe_layout_noalloc(0, t, 10, 2, 4, 0x100, 0x200, 0x300, 0x400, t, NULL) == -1
+
+
 def test_moe_expert_workspace_validation(L):
     # two int64 tables of R*E entries, rounded up to 256 bytes ...
     assert L.coll_moe_expert_workspace_bytes(8, 256, 0) == 8 * 256 * 16
