@@ -529,6 +529,10 @@ def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
     for r in recvs:
         if r.dtype != torch.bfloat16:
             raise ValueError("moe_expert_scale: bf16 rows only")
+    if expert_counts.dtype != torch.int32 or expert_counts.numel() != R * n_experts:
+        raise ValueError("moe_expert_scale: expert_counts must be int32 [R*E] (one row per rank)")
+    if rdispls.dtype != torch.int64 or rdispls.numel() != R * R:
+        raise ValueError("moe_expert_scale: rdispls must be int64 [R*R]")
     capacity = sum(t.numel() // hidden for t in recvs) if hidden > 0 else 0
     ws_bytes = workspace.numel() * workspace.element_size()
     return _issue("coll_moe_expert_scale", "moe_expert_scale", stream, R, _table(recvs, "recv", R),
