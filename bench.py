@@ -425,23 +425,34 @@ def copy_ceiling(torch, coll, W):
 
 
 def latency_rows_graph(torch, coll, W, per_row_us):
-    """The latency-bound rows of the step timed by HIP-graph replay, beside
-    their eager per-launch times as prepared calls (the step's rows) and as
-    plain binding calls (argument checks and marshalling on every call)."""
+    """The latency-bound rows of the step: HIP-graph replay beside the eager
+    costs.  `eager_prepared_us` is one back-to-back prepared call (a decode
+    loop issuing the collective: 2000 calls between one event pair, so the
+    host's issue cost and the GPU time overlap as they would there);
+    `eager_prepared_median_us` is the median of single calls each between its
+    own event pair; `eager_plain_*` the same for plain binding calls (argument
+    checks and marshalling every call); `in_step_us` the row inside the timed
+    step, whose per-row event pairs add their own cost."""
     E, T, K, H = W["moe"]
     rows = {
-        "ar_160k": lambda i: coll.allreduce(W["ar160_in"], W["ar160_out"]),
-        "ar_decode": lambda i: coll.allreduce(W["ard_in"], W["ard_out"]),
-        "bcast": lambda i: coll.broadcast(W["bc_src"], W["bc_out"], 7),
-        "moe_layout": lambda i: coll.moe_layout(W["moe_ids"], E, W["sc"], W["sd"], W["rd"],
-                                                W["ec"], W["pos"], W["ws"]),
+        "ar_160k": (coll.allreduce, (W["ar160_in"], W["ar160_out"])),
+        "ar_decode": (coll.allreduce, (W["ard_in"], W["ard_out"])),
+        "bcast": (coll.broadcast, (W["bc_src"], W["bc_out"], 7)),
+        "moe_layout": (coll.moe_layout, (W["moe_ids"], E, W["sc"], W["sd"], W["rd"], W["ec"],
+                                         W["pos"], W["ws"])),
     }
     res = {}
-    for name, fn in rows.items():
-        t = _graph_time(torch, fn, 1)
-        plain, _ = _launch_times(torch, fn, 1, 200)
-        res[name] = {"graph_us": round(t * 1e6, 2), "eager_prepared_us": per_row_us[name],
-                     "eager_plain_us": round(plain * 1e6, 2)}
+    for name, (call, args) in rows.items():
+        plan = coll.prepare(call, *args)
+        t = _graph_time(torch, lambda i: plan(), 1)
+        med_p, batch_p = _launch_times(torch, lambda i: plan(), 1, 2000)
+        med_plain, batch_plain = _launch_times(torch, lambda i: call(*args), 1, 500)
+        res[name] = {"graph_us": round(t * 1e6, 2),
+                     "eager_prepared_us": round(batch_p * 1e6, 2),
+                     "eager_prepared_median_us": round(med_p * 1e6, 2),
+                     "eager_plain_us": round(batch_plain * 1e6, 2),
+                     "eager_plain_median_us": round(med_plain * 1e6, 2),
+                     "in_step_us": per_row_us[name]}
     return res
 
 
