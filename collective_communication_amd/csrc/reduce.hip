@@ -48,44 +48,44 @@ template <int R>
 constexpr int rs_u() { return R <= 2 ? 4 : (R <= 8 ? COLL_RS_U_MID : 1); }
 
 // AllReduce staged through LDS (SUM, kArLdsMinR <= R <= 16): a workgroup of R
-// waves owns a tile of kArLdsTile units of every rank, and wave r streams rank
-// r: it loads the tile of sendbufs[r] into LDS (two 1 KiB runs per wave); after
-// a barrier, one thread per unit folds the R ranks in ascending order and
-// writes the narrowed sum back to LDS; after a second barrier, wave r stores
-// the summed tile to recvbufs[r].  Per wave this is a copy-like stream (one
-// source, one destination, 2 KiB runs) instead of R loads and R stores whose
-// stores all wait for the slowest load.  MI355X, R = 8, graph replay, rank
-// buffers in an arena, the access pattern alone (integer adds): 16 / 32 /
-// 64 MiB per rank 70.7 / 71.1 / 77.1% of the HBM peak, against 70.3 / 70.5 /
-// 71.9% for one wave loading and storing all R ranks (1 KiB runs: 61-63%;
-// 4 KiB: 68-74%).  Every unit of a tile is read into LDS before any is
-// stored, so in-place calls are safe.
-#ifndef COLL_AR_LDS_U
-#define COLL_AR_LDS_U 2
-#endif
+// waves owns a tile of 64*U units of every rank, and wave r streams rank r: it
+// loads the tile of sendbufs[r] into LDS (U runs of 1 KiB per wave); after a
+// barrier, one thread per unit folds the R ranks in ascending order and writes
+// the narrowed sum back to LDS; after a second barrier, wave r stores the
+// summed tile to recvbufs[r].  Per wave this is a copy-like stream (one
+// source, one destination) instead of R loads and R stores whose stores all
+// wait for the slowest load.  The tile is picked by size: on MI355X, R = 8
+// bf16, median of back-to-back launches, 16 / 32 / 64 MiB per rank reach
+// 69.7 / 71.5 / 75.0% of the HBM peak with U = 1 and 68.5 / 70.7 / 76.1% with
+// U = 2 (U = 3: 65.3 / 67.3 / 71.3%); a single wave loading and storing all R
+// ranks reached 70.3 / 70.5 / 71.9% on the access pattern alone in graph
+// replay.  Every unit of a tile is read into LDS before any is stored, so
+// in-place calls are safe.
 #ifndef COLL_AR_LDS_MIN_R
 #define COLL_AR_LDS_MIN_R 4
 #endif
-constexpr int kArLdsU = COLL_AR_LDS_U;
-constexpr int kArLdsTile = 64 * kArLdsU;          // units per rank per tile
+#ifndef COLL_AR_LDS_BIG_BYTES
+#define COLL_AR_LDS_BIG_BYTES (48u << 20)
+#endif
 constexpr int kArLdsMinR = COLL_AR_LDS_MIN_R;
+constexpr size_t kArLdsBigBytes = COLL_AR_LDS_BIG_BYTES;   // per rank: U = 2 from here
 
-template <int R, int DT, int OP, bool NT>
+template <int R, int DT, int OP, bool NT, int U>
 __global__ __launch_bounds__(64 * R) void ar_lds(RankPtrs p, size_t nvec) {
   using F = Fmt<DT>;
-  __shared__ u32x4 s_in[R][kArLdsTile];
-  __shared__ u32x4 s_sum[kArLdsTile];
+  constexpr int kTile = 64 * U;                   // units per rank per tile
+  __shared__ u32x4 s_in[R][kTile];
+  __shared__ u32x4 s_sum[kTile];
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // the wave's rank
   const int lane = threadIdx.x & 63;
-  for (size_t t0 = (size_t)blockIdx.x * kArLdsTile; t0 < nvec;
-       t0 += (size_t)gridDim.x * kArLdsTile) {
+  for (size_t t0 = (size_t)blockIdx.x * kTile; t0 < nvec; t0 += (size_t)gridDim.x * kTile) {
 #pragma unroll
-    for (int u = 0; u < kArLdsU; u++) {
+    for (int u = 0; u < U; u++) {
       const size_t i = t0 + (size_t)u * 64 + lane;
       if (i < nvec) s_in[w][u * 64 + lane] = ld<u32x4, NT>(p.in[w], i);
     }
     __syncthreads();
-    if (threadIdx.x < kArLdsTile && t0 + threadIdx.x < nvec) {
+    if (threadIdx.x < kTile && t0 + threadIdx.x < nvec) {
       typename F::Acc a = F::widen(s_in[0][threadIdx.x]);
 #pragma unroll
       for (int r = 1; r < R; r++) F::template fold_in<OP>(a, s_in[r][threadIdx.x]);
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * R) void ar_lds(RankPtrs p, size_t nvec) {
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kArLdsU; u++) {
+    for (int u = 0; u < U; u++) {
       const size_t i = t0 + (size_t)u * 64 + lane;
       if (i < nvec) st<u32x4, NT>(p.out[w], i, s_sum[u * 64 + lane]);
     }
@@ -253,8 +253,13 @@ __global__ __launch_bounds__(kBlock) void rs_scalar(RankPtrs p, int R, size_t se
 template <int R, int DT, int OP, bool NT>
 void launch_ar_r(const Launch &L, const RankPtrs &p, size_t nvec) {
   if constexpr (R >= kArLdsMinR) {
-    dim3 grid(L.ar_grid > 0 ? (unsigned)L.ar_grid : grid_tiles(nvec, (size_t)kArLdsTile));
-    hipLaunchKernelGGL((ar_lds<R, DT, OP, NT>), grid, dim3(64 * R), 0, L.stream, p, nvec);
+    if (nvec * sizeof(u32x4) >= kArLdsBigBytes) {
+      dim3 grid(L.ar_grid > 0 ? (unsigned)L.ar_grid : grid_tiles(nvec, (size_t)128));
+      hipLaunchKernelGGL((ar_lds<R, DT, OP, NT, 2>), grid, dim3(64 * R), 0, L.stream, p, nvec);
+    } else {
+      dim3 grid(L.ar_grid > 0 ? (unsigned)L.ar_grid : grid_tiles(nvec, (size_t)64));
+      hipLaunchKernelGGL((ar_lds<R, DT, OP, NT, 1>), grid, dim3(64 * R), 0, L.stream, p, nvec);
+    }
   } else {
     dim3 grid(L.ar_grid > 0 ? (unsigned)L.ar_grid
                             : grid_tiles(nvec, (size_t)ar_u<R>() * kArBlock));

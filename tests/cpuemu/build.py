@@ -25,7 +25,10 @@ CXX = os.environ.get("EMU_CXX") or next(
     "clang++")
 FLAGS = ["-x", "c++", "-std=c++17", "-O1", "-g", "-fPIC", "-ffp-contract=off",
          "-fno-omit-frame-pointer", "-Wno-unused-function", "-Wno-unknown-attributes",
-         "-I", HERE, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+         "-I", HERE, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+         # the AllReduce switches to its 2 KiB-per-rank LDS tile from 16 KiB per
+         # rank here (48 MiB on the GPU), so both tiles meet the emulator's sizes
+         "-DCOLL_AR_LDS_BIG_BYTES=16384u"]
 
 
 def sources():
