@@ -693,8 +693,8 @@ def test_uniform_all_to_all(R, n, dtype):
         assert bits_equal(host(recvs[d]), want[d]), f"dest {d}"
 
 
-@pytest.mark.parametrize("R,SL,H,D", [(1, 3, 4, 8), (2, 5, 4, 3), (4, 17, 8, 16),
-                                      (8, 512, 32, 128), (8, 3, 16, 5)])
+@pytest.mark.parametrize("R,SL,H,D", [(1, 3, 4, 8), (2, 5, 4, 3), (4, 17, 8, 16), (4, 1, 8, 16),
+                                      (8, 512, 32, 128), (8, 3, 16, 5), (8, 4096, 32, 128)])
 def test_seq_heads_reshard_round_trip(R, SL, H, D):
     say("reshard", R, SL, H, D)
     xs = [synth.gaussian((SL, H, D), 1.0, 1800 + s, "bf16") for s in range(R)]
