@@ -67,5 +67,22 @@ def build(force: bool = False) -> str:
     return LIB
 
 
+def build_selftest() -> str:
+    """The emulator's own self-test library: selftest.cpp + emu.cpp."""
+    lib = os.path.join(BUILD, "libemu_selftest.so")
+    src = os.path.join(HERE, "selftest.cpp")
+    inputs = [src, os.path.join(HERE, "emu.cpp"), os.path.join(HERE, "hip", "hip_runtime.h")]
+    if os.path.exists(lib) and os.path.getmtime(lib) >= max(os.path.getmtime(f) for f in inputs):
+        return lib
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = lib + ".tmp%d" % os.getpid()
+    r = subprocess.run([CXX, *FLAGS, src, os.path.join(HERE, "emu.cpp"), "-shared", "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"emulator self-test build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(force=True))

@@ -110,6 +110,13 @@ void resolve_wave(Lane *w, int n) {
         break;
       }
       case EMU_FIRSTLANE:
+      case EMU_UNIFORM:
+        if (x.val != w[first].val) {
+          describe_site("first", first, w[first]);
+          describe_site("other", l, x);
+          die(op == EMU_UNIFORM ? "COLL_UNIFORM of a value that differs across lanes"
+                                : "readfirstlane of a value that differs across lanes");
+        }
         x.result = w[first].val;
         break;
       case EMU_READLANE: {

@@ -26,10 +26,13 @@
 // kernel that reads LDS it did not write first computes garbage.
 #define __shared__ __attribute__((section("emu_lds"))) static
 
-// the library's scheduling fences emit nothing on the CPU
+// the library's scheduling fences emit nothing on the CPU; COLL_UNIFORM, which
+// on the GPU moves its value into a scalar register (lane 0's copy wins if the
+// lanes disagree), is checked instead: every active lane must hold the same
+// bits, or the run aborts naming the site (see the wave ops below)
 #define COLL_OPAQUE(x) ((void)0)
 #define COLL_KEEP(x) ((void)0)
-#define COLL_UNIFORM(x) ((void)0)
+#define COLL_UNIFORM(x) emu_uniform_at(emu_bits(x), __FILE__, __LINE__)
 
 // ------------------------------------------------------------- runtime types
 typedef int hipError_t;
@@ -73,7 +76,12 @@ static inline hipError_t hipGetSymbolAddress(void **p, const void *sym) {
 // --------------------------------------------------------------- wave ops
 // Each op is a rendezvous of the wave's active lanes at one source position
 // (file, line): the same position however the compiler duplicates its code.
-enum { EMU_BALLOT = 1, EMU_SHFL = 2, EMU_SHFL_UP = 3, EMU_FIRSTLANE = 4, EMU_READLANE = 5 };
+// readfirstlane and COLL_UNIFORM also check that every active lane holds the
+// same value: the library uses both only on values it takes to be uniform
+// (slots, ranks and descriptors loaded from one address), and a lane that
+// disagreed would go on with lane 0's address on the GPU.
+enum { EMU_BALLOT = 1, EMU_SHFL = 2, EMU_SHFL_UP = 3, EMU_FIRSTLANE = 4, EMU_READLANE = 5,
+       EMU_UNIFORM = 6 };
 
 template <class T>
 static inline uint64_t emu_bits(T v) {
@@ -104,6 +112,9 @@ static inline T emu_shfl_up_at(T v, unsigned delta, int width, const char *f, in
 }
 static inline int emu_readfirstlane_at(int v, const char *f, int l) {
   return (int)emu_wave_op(EMU_FIRSTLANE, (uint32_t)v, 0, f, l);
+}
+static inline void emu_uniform_at(uint64_t bits, const char *f, int l) {
+  (void)emu_wave_op(EMU_UNIFORM, bits, 0, f, l);
 }
 static inline int emu_readlane_at(int v, int lane, const char *f, int l) {
   return (int)emu_wave_op(EMU_READLANE, (uint32_t)v, lane, f, l);

@@ -11,6 +11,13 @@ tails, and its outputs are compared with the oracle.  Buffers sit flush
 against inaccessible pages, once at their end and once at their start, so an
 access one byte outside any buffer kills the run; each family runs in a
 subprocess, whose last printed line then names the case.
+
+The emulator checks two more rules at every site: a value the kernel moves
+into a scalar register (readfirstlane, COLL_UNIFORM) must be equal in every
+active lane, since on the GPU the other lanes would go on with lane 0's value
+(an address, a slot, a descriptor); and LDS is read back poisoned, not zeroed,
+if a kernel reads it before writing.  Its self-test plants each mistake in a
+small kernel of its own and expects the run to stop.
 """
 import os
 import subprocess
@@ -42,3 +49,35 @@ def test_kernels_on_guarded_buffers(emu_lib, family, place):
     tail = "\n".join((r.stdout + r.stderr).strip().splitlines()[-8:])
     assert r.returncode == 0, f"{family}/{place} exited with {r.returncode}:\n{tail}"
     assert "all cases passed" in r.stdout, tail
+
+
+SELFTEST = os.path.join(HERE, "cpuemu", "selftest.py")
+# which -> (what the planted mistake is, how the run must end, message it prints)
+SELF_CASES = {
+    0: ("COLL_UNIFORM of a per-lane value", -6, "COLL_UNIFORM of a value that differs"),
+    1: ("readfirstlane of a per-lane value", -6, "readfirstlane of a value that differs"),
+    2: ("ballot reached by half of a wave", -6, "divergent control flow"),
+    3: ("store one element past a buffer", -11, None),
+    4: ("LDS read before it is written", 0, None),
+}
+
+
+def _selftest(which, bad):
+    r = subprocess.run([sys.executable, SELFTEST, str(which), str(bad)], capture_output=True,
+                       text=True, timeout=120)
+    return r.returncode, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("which", sorted(SELF_CASES))
+def test_emulator_stops_a_planted_mistake(emu_lib, which):
+    what, code, msg = SELF_CASES[which]
+    rc, text = _selftest(which, 0)
+    assert rc == 0 and "rc 0" in text, f"clean form of {what}: {text[-400:]}"
+    rc, text = _selftest(which, 1)
+    if which == 4:
+        vals = [int(v) for v in text.split("out")[-1].split()]
+        assert rc == 0 and vals and all(v == -1515870811 for v in vals), text[-400:]  # 0xA5A5A5A5
+        return
+    assert rc == code, f"{what}: exit {rc}\n{text[-400:]}"
+    if msg:
+        assert msg in text, text[-400:]
