@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--only", default="", help="comma list of rows to run (profiling)")
+    p.add_argument("--report", default="",
+                   help="print the markdown tables of a saved JSON line (file) and exit")
     return p.parse_args()
 
 
@@ -717,11 +719,104 @@ def counter_traffic(kernel_src: str):
     return int(m_b.group(1))
 
 
+def _pct(f):
+    return "—" if f is None else f"{100 * f:.1f}%"
+
+
+def report(path):
+    """Markdown tables of one saved JSON line of this benchmark (the last line
+    of the file): the step, its rows, the sweeps and the side measurements, in
+    the form the documentation quotes them, so that every figure there can be
+    traced back to one run."""
+    d = json.loads(open(path).read().strip().splitlines()[-1])
+    o = []
+    rf = d["roofline"] or {}
+    tr = rf.get("traffic")
+    o += ["| Step | value |", "|---|---|",
+          f"| whole step (`value`) | {d['value']:.1f} GB/s = {_pct(d['value'] / HBM_PEAK_GBS)}, "
+          f"{d['ms_per_step']} ms per step |"]
+    if d.get("step_graph_replay"):
+        g = d["step_graph_replay"]
+        o.append(f"| the same step by graph replay | {g['GBps']} GB/s = {_pct(g['frac'])}, "
+                 f"{g['ms_per_step']} ms |")
+    if rf:
+        o.append(f"| dominant kernel ({rf['kernel'].split(' ')[0]}) | {rf['achieved']} GB/s = "
+                 f"{_pct(rf['frac'])}, {rf['avg_launch_us']} µs per launch; counter traffic "
+                 + (f"{tr / rf['bytes_per_launch']:.4f}× the algorithmic bytes |" if tr else "n/a |"))
+    if d.get("cpu_baseline"):
+        c = d["cpu_baseline"]
+        o.append(f"| CPU baseline (oracle, {c['cores']} core) | {c['value']} GB/s |")
+    o += ["", "| Step row | µs | GB/s | % of peak |", "|---|---|---|---|"]
+    for k, v in d["rows"].items():
+        o.append(f"| {k} | {v['us']} | {v['GBps']} | {_pct(v['frac'])} |")
+    sw = d.get("allreduce_sweep")
+    if sw:
+        o += ["", "| AllReduce R=8 bf16, per rank | graph µs | graph | median µs | median |",
+              "|---|---|---|---|---|"]
+        for k, v in sw.items():
+            if isinstance(v, dict) and "graph_us" in v and v["graph_frac"] >= 0.3:
+                o.append(f"| {k} | {v['graph_us']} | {_pct(v['graph_frac'])} | {v['median_us']} "
+                         f"| {_pct(v['frac'])} |")
+    a2 = d.get("all_to_all_v_sweep")
+    if a2:
+        o += ["", "| All-to-All-v R=8 | size | graph µs | graph | median |", "|---|---|---|---|---|"]
+        for series, pts in a2.items():
+            if not isinstance(pts, dict):
+                continue
+            for k, v in pts.items():
+                if not (isinstance(v, dict) and "graph_us" in v):
+                    continue
+                big = (series.startswith("moe") and k in ("T256", "T1024", "T4096")) or \
+                      (k.endswith("KiB") and int(k[:-3]) >= 16384)
+                if big:
+                    o.append(f"| {series} | {k} | {v['graph_us']} | {_pct(v['graph_frac'])} | "
+                             f"{_pct(v['frac'])} |")
+    if d.get("next_rows"):
+        o += ["", "| Further row | µs | GB/s | % of peak |", "|---|---|---|---|"]
+        for k, v in d["next_rows"].items():
+            o.append(f"| {k} | {v['us']} | {v['GBps']} | {_pct(v['frac'])} |")
+    f = d.get("moe_fused")
+    if f:
+        o += ["", "| Fused MoE path | value |", "|---|---|",
+              f"| dispatch (permute + All-to-All-v) | {f['dispatch']['us']} µs, {_pct(f['dispatch']['frac'])} |",
+              f"| combine (expert + reverse All-to-All-v + combine) | {f['combine']['us']} µs, "
+              f"{_pct(f['combine']['frac'])} |",
+              f"| pipeline (layout + dispatch + combine) | {f['pipeline_us']} µs against "
+              f"{f['unfused_pipeline_us']} µs unfused ({f['speedup_vs_unfused']}×); outputs bitwise "
+              f"equal: {f['outputs_bitwise_equal_unfused']} |"]
+    lat = d.get("latency_rows_graph")
+    if lat:
+        o += ["", "| Latency row | graph µs | eager prepared µs (back to back) | eager plain µs "
+                  "(back to back) | in the step (event pair) µs |", "|---|---|---|---|---|"]
+        for k, v in lat.items():
+            o.append(f"| {k} | {v['graph_us']} | {v['eager_prepared_us']} | {v['eager_plain_us']} | "
+                     f"{v['in_step_us']} |")
+    ex = []
+    if d.get("copy_ceiling_1gib"):
+        c = d["copy_ceiling_1gib"]
+        ex.append(f"| plain 1 GiB copy (graph) | {c['us']} µs, {c['GBps']} GB/s = {_pct(c['frac'])} |")
+    if d.get("allreduce_16mib_layout_ab"):
+        a = d["allreduce_16mib_layout_ab"]
+        ex.append(f"| AllReduce 16 MiB × 8, torch allocations vs rank arena | "
+                  f"{a['torch_alloc']['GBps']} vs {a['rank_arena']['GBps']} GB/s (median) |")
+    if d.get("broadcast_vs_padded_allgather"):
+        b = d["broadcast_vs_padded_allgather"]
+        ex.append("| broadcast vs pad-to-max AllGather, tokens: speedup | "
+                  + ", ".join(f"{k}: {v['speedup']}×" for k, v in b.items())
+                  + f"; bitwise equal: {all(v['bitwise_equal'] for v in b.values())} |")
+    if ex:
+        o += ["", "| Other | value |", "|---|---|"] + ex
+    print("\n".join(o))
+
+
 def main():
     args = parse()
+    if args.report:
+        report(args.report)
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the R ranks are virtual "
-                                   "ranks in one GPU's HBM; --gpus must be 1"}))
+        print(json.dumps({"error": "libcoll runs its R ranks as virtual ranks in one GPU's "
+                                   "HBM; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
