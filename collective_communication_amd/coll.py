@@ -44,11 +44,12 @@ SIGNATURES = {
     "coll_all_gather": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_gather": (_i, [_i, _vp, _vp, _i, _sz, _sz, _i, _vp]),
     "coll_broadcast": (_i, [_i, _vp, _vp, _i, _sz, _i, _vp]),
-    "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp]),
+    "coll_all_to_all_v": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _vp, _vp]),
     "coll_all_to_all_v_workspace_bytes": (_sz, [_i, _sz, _sz, _i]),
-    "coll_all_to_all_v_ws": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _sz, _vp]),
-    "coll_all_to_all_v_reverse": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _sz,
-                                       _vp]),
+    "coll_all_to_all_v_ws": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _vp, _vp,
+                                  _sz, _vp]),
+    "coll_all_to_all_v_reverse": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _vp, _vp,
+                                       _sz, _vp]),
     "coll_all_to_all": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_seq_heads_reshard": (_i, [_i, _vp, _vp, _sz, _sz, _sz, _i, _i, _vp]),
     "coll_lse_merge": (_i, [_i, _vp, _vp, _vp, _vp, _sz, _sz, _i, _vp]),
@@ -59,9 +60,9 @@ SIGNATURES = {
     "coll_moe_expert_workspace_bytes": (_sz, [_i, _i, _sz]),
     "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _sz, _vp]),
     "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
-    "coll_moe_dispatch": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
+    "coll_moe_dispatch": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp, _vp]),
     "coll_moe_combine_recv": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp,
-                                   _vp]),
+                                   _vp, _vp]),
 }
 
 
@@ -129,6 +130,13 @@ def _table(ts: Sequence[torch.Tensor], what: str, R: int):
     if len(ts) != R:
         raise ValueError(f"{what}: {len(ts)} buffers for {R} ranks (one per rank)")
     return (ctypes.c_void_p * R)(*[_dev(t, what) for t in ts])
+
+
+def _rows(ts: Sequence[torch.Tensor], row_elems: int):
+    """Rows each rank's buffer holds, as the C array of int64 the exchanges
+    bound their blocks by (a block whose rows do not all exist is not moved)."""
+    return (ctypes.c_int64 * len(ts))(
+        *[t.numel() // row_elems if row_elems > 0 else 0 for t in ts])
 
 
 def _ranks(ts, what) -> int:
@@ -382,7 +390,8 @@ def all_to_all_v(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int,
         if t.dtype != torch.int64 or t.numel() != R * R:
             raise ValueError(f"all_to_all_v: {name} must be int64 [R*R] on the device")
     args = (R, _table(sends, "send", R), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
-            _table(recvs, "recv", R), _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity)
+            _table(recvs, "recv", R), _dev(rdispls, "rdispls"), row_elems * mult, dt, capacity,
+            _rows(sends, row_elems), _rows(recvs, row_elems))
     if workspace is None:
         return _issue("coll_all_to_all_v", "all_to_all_v", stream, *args)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -409,7 +418,7 @@ def all_to_all_v_reverse(recvs, sendcounts, sdispls, sends, rdispls, row_elems: 
     return _issue("coll_all_to_all_v_reverse", "all_to_all_v_reverse", stream, R,
                   _table(recvs, "recv", R), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
                   _table(sends, "send", R), _dev(rdispls, "rdispls"), row_elems * mult, dt,
-                  capacity, ws_ptr, ws_bytes)
+                  capacity, _rows(sends, row_elems), _rows(recvs, row_elems), ws_ptr, ws_bytes)
 
 
 def all_to_all(sends, recvs, stream=None):
@@ -601,7 +610,8 @@ def moe_dispatch(xs, pos, sendcounts, sdispls, rdispls, recvs, stream=None):
     dt, mult = _copy_dtype(xs[0])
     return _issue("coll_moe_dispatch", "moe_dispatch", stream, R, _table(xs, "x", R),
                   _table(pos, "pos", R), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
-                  _dev(rdispls, "rd"), T, K, H * mult, dt, _table(recvs, "recv", R))
+                  _dev(rdispls, "rd"), T, K, H * mult, dt, _table(recvs, "recv", R),
+                  _rows(recvs, H))
 
 
 def moe_combine_recv(recvs, pos, sendcounts, sdispls, rdispls, weights, outs, topk_ids=None,
@@ -631,4 +641,4 @@ def moe_combine_recv(recvs, pos, sendcounts, sdispls, rdispls, weights, outs, to
     return _issue("coll_moe_combine_recv", "moe_combine_recv", stream, R, _table(recvs, "recv", R),
                   _table(pos, "pos", R), _dev(sendcounts, "sc"), _dev(sdispls, "sd"),
                   _dev(rdispls, "rd"), _table(weights, "w", R), ids, T, K, H, COLL_BF16,
-                  _table(outs, "out", R))
+                  _table(outs, "out", R), _rows(recvs, H))

@@ -43,6 +43,10 @@ constexpr int kA2aResU = COLL_A2A_RES_U;      // ... resident grid
 // lanes per workgroup, one-pass grid (MI355X, the MoE exchange: 256 -> 1247 us,
 // 128 -> 1275, 64 -> 1320: the workgroup shares one block-table build)
 constexpr int kA2aBlock = COLL_A2A_BLOCK;
+// receive capacity up to which the plain form runs a resident grid
+#ifndef COLL_A2A_RESIDENT_MAX_BYTES
+#define COLL_A2A_RESIDENT_MAX_BYTES (256ull << 20)
+#endif
 // 1: R <= 8 uses the one-block-per-lane table (a2av_kernel8 / a2av_res_kernel8)
 #ifndef COLL_A2A_SMALL
 #define COLL_A2A_SMALL 1
@@ -64,9 +68,9 @@ __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
 // block search has a fixed depth (measured faster than the general form at
 // the MoE exchange; the general form serves R up to 16).
 template <int B, bool NT, int UN, int BS, bool SMALL>
-__device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_t *counts,
-                                          const int64_t *sdispls, const int64_t *rdispls,
-                                          int ct, uint64_t row_units) {
+__device__ __forceinline__ void a2av_body(const RankPtrs &p, const RowLimits &lim, int R,
+                                          const int64_t *counts, const int64_t *sdispls,
+                                          const int64_t *rdispls, int ct, uint64_t row_units) {
   using U = typename UnitT<B>::T;
   constexpr int kTab = SMALL ? 64 : kMaxBlocks;
   __shared__ uint64_t s_end[kTab];   // inclusive end of block b in the global unit space
@@ -83,7 +87,9 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
       const int s = bb / R, d = bb - s * R;
       const int64_t c = counts[count_index(ct, R, s, d)], sdv = sdispls[bb],
                     rdv = rdispls[d * R + s];
-      const uint64_t len = (b < nb && c > 0) ? (uint64_t)c * row_units : 0;
+      const uint64_t len =
+          (b < nb && block_fits(c, sdv, rdv, lim.in.n[s], lim.out.n[d])) ? (uint64_t)c * row_units
+                                                                          : 0;
       const uint64_t incl = wave_incl_scan(len);
       if (b < nb) {
         const uint64_t start = incl - len;
@@ -115,7 +121,10 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int b = lane * 4 + j;
-      len[j] = (b < nb && cnt[j] > 0) ? (uint64_t)cnt[j] * row_units : 0;
+      const int bb = b < nb ? b : 0;
+      const int s = bb / R, d = bb - s * R;
+      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], lim.in.n[s], lim.out.n[d]);
+      len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_units : 0;
       local += len[j];
     }
     const uint64_t incl = wave_incl_scan(local);
@@ -191,33 +200,33 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, int R, const int64_
 
 // One-pass grid (large exchanges): kA2aU units per lane per tile.
 template <int B, bool NT>
-__global__ __launch_bounds__(kA2aBlock) void a2av_kernel(RankPtrs p, int R, const int64_t *counts,
+__global__ __launch_bounds__(kA2aBlock) void a2av_kernel(RankPtrs p, RowLimits lim, int R, const int64_t *counts,
                                                       const int64_t *sdispls,
                                                       const int64_t *rdispls, int ct, uint64_t row_units) {
-  a2av_body<B, NT, kA2aU, kA2aBlock, false>(p, R, counts, sdispls, rdispls, ct, row_units);
+  a2av_body<B, NT, kA2aU, kA2aBlock, false>(p, lim, R, counts, sdispls, rdispls, ct, row_units);
 }
 template <int B, bool NT>
-__global__ __launch_bounds__(kA2aBlock) void a2av_kernel8(RankPtrs p, int R, const int64_t *counts,
+__global__ __launch_bounds__(kA2aBlock) void a2av_kernel8(RankPtrs p, RowLimits lim, int R, const int64_t *counts,
                                                        const int64_t *sdispls,
                                                        const int64_t *rdispls, int ct, uint64_t row_units) {
-  a2av_body<B, NT, kA2aU, kA2aBlock, true>(p, R, counts, sdispls, rdispls, ct, row_units);
+  a2av_body<B, NT, kA2aU, kA2aBlock, true>(p, lim, R, counts, sdispls, rdispls, ct, row_units);
 }
 // Resident grid (up to 256 MiB): kA2aResU units per lane per tile.
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void a2av_res_kernel(RankPtrs p, int R,
+__global__ __launch_bounds__(kBlock) void a2av_res_kernel(RankPtrs p, RowLimits lim, int R,
                                                           const int64_t *counts,
                                                           const int64_t *sdispls,
                                                           const int64_t *rdispls, int ct,
                                                           uint64_t row_units) {
-  a2av_body<B, NT, kA2aResU, kBlock, false>(p, R, counts, sdispls, rdispls, ct, row_units);
+  a2av_body<B, NT, kA2aResU, kBlock, false>(p, lim, R, counts, sdispls, rdispls, ct, row_units);
 }
 template <int B, bool NT>
-__global__ __launch_bounds__(kBlock) void a2av_res_kernel8(RankPtrs p, int R,
+__global__ __launch_bounds__(kBlock) void a2av_res_kernel8(RankPtrs p, RowLimits lim, int R,
                                                            const int64_t *counts,
                                                            const int64_t *sdispls,
                                                            const int64_t *rdispls, int ct,
                                                            uint64_t row_units) {
-  a2av_body<B, NT, kA2aResU, kBlock, true>(p, R, counts, sdispls, rdispls, ct, row_units);
+  a2av_body<B, NT, kA2aResU, kBlock, true>(p, lim, R, counts, sdispls, rdispls, ct, row_units);
 }
 
 // Rows whose size or buffers do not allow 16-byte units on every row (the
@@ -250,7 +259,7 @@ __device__ __forceinline__ void copy_chunk_narrow(uint64_t src, uint64_t dst, ui
 }
 
 template <bool NT, int UN, bool FAST>
-__global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
+__global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimits lim, int R,
                                                             const int64_t *counts,
                                                             const int64_t *sdispls,
                                                             const int64_t *rdispls, int ct,
@@ -281,7 +290,10 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, int R,
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int b = lane * 4 + j;
-      len[j] = (b < nb && cnt[j] > 0) ? (uint64_t)cnt[j] * row_bytes : 0;
+      const int bb = b < nb ? b : 0;
+      const int s = bb / R, d = bb - s * R;
+      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], lim.in.n[s], lim.out.n[d]);
+      len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_bytes : 0;
       nch[j] = (len[j] + 15) / 16;
       local += nch[j];
     }
@@ -464,7 +476,8 @@ __device__ __forceinline__ uint64_t desc_tile(uint64_t i) {
 
 // General table build (R <= 16, four blocks per lane of wave 0), as in a2av_body.
 template <int B>
-__device__ __forceinline__ void desc_table(const RankPtrs &p, int R, const int64_t *counts,
+__device__ __forceinline__ void desc_table(const RankPtrs &p, const RowLimits &lim, int R,
+                                           const int64_t *counts,
                                            const int64_t *sdispls, const int64_t *rdispls, int ct,
                                            uint64_t row_units, uint64_t *s_end, uint64_t *s_src,
                                            uint64_t *s_dst) {
@@ -485,7 +498,10 @@ __device__ __forceinline__ void desc_table(const RankPtrs &p, int R, const int64
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int b = lane * 4 + j;
-    len[j] = (b < nb && cnt[j] > 0) ? (uint64_t)cnt[j] * row_units : 0;
+    const int bb = b < nb ? b : 0;
+    const int s = bb / R, d = bb - s * R;
+    const bool fits = block_fits(cnt[j], sdv[j], rdv[j], lim.in.n[s], lim.out.n[d]);
+    len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_units : 0;
     local += len[j];
   }
   const uint64_t incl = wave_incl_scan(local);
@@ -558,7 +574,7 @@ __device__ __forceinline__ void desc_units(uint64_t sb, uint64_t db, uint64_t en
 // in tile order 28.6 us; 2 resident workgroups per CU 27.2 us; slot order
 // with 4 per CU 21.6 us, and 8, 16 or one per 256 slots within 1% of that.
 template <int B>
-__global__ __launch_bounds__(kBlock) void a2av_desc_build(RankPtrs p, int R, const int64_t *counts,
+__global__ __launch_bounds__(kBlock) void a2av_desc_build(RankPtrs p, RowLimits lim, int R, const int64_t *counts,
                                                          const int64_t *sdispls,
                                                          const int64_t *rdispls, int ct,
                                                          uint64_t row_units, uint32_t *idx,
@@ -566,7 +582,7 @@ __global__ __launch_bounds__(kBlock) void a2av_desc_build(RankPtrs p, int R, con
   __shared__ uint64_t s_end[kMaxBlocks], s_src[kMaxBlocks], s_dst[kMaxBlocks];
   const int nb = R * R;
   if (threadIdx.x < 64)
-    desc_table<B>(p, R, counts, sdispls, rdispls, ct, row_units, s_end, s_src, s_dst);
+    desc_table<B>(p, lim, R, counts, sdispls, rdispls, ct, row_units, s_end, s_src, s_dst);
   __syncthreads();
   const uint64_t total = s_end[nb - 1];
   const uint64_t more = total > ndesc * kDescTile ? 1 : 0;
@@ -627,9 +643,9 @@ __global__ __launch_bounds__(kDescLanes) void a2av_desc_kernel(const uint32_t *_
 
 }  // namespace
 
-int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
-                size_t rows_capacity) {
+int launch_a2av(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
+                const int64_t *counts, const int64_t *sdispls, const int64_t *rdispls, int ct,
+                size_t row_bytes, size_t rows_capacity) {
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
   const int unit = copy_unit(bits);
@@ -640,7 +656,7 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
   // grid of 4 workgroups per CU looping over tiles of kA2aResU units per lane,
   // which builds the block table once per workgroup (measured on MI355X at
   // R = 8: +4..8% at 16-32 MiB per rank, -2..4% from 64 MiB per rank up).
-  constexpr uint64_t kResidentMaxBytes = 256ull << 20;
+  constexpr uint64_t kResidentMaxBytes = COLL_A2A_RESIDENT_MAX_BYTES;
   const uint64_t cap_bytes = (uint64_t)rows_capacity * row_bytes;
   const bool resident = rows_capacity == 0 || cap_bytes <= kResidentMaxBytes;
   // (never more workgroups than the one-pass grid would have: small
@@ -656,16 +672,16 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
     if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
     const bool small = COLL_A2A_SMALL && R <= 8;
     if (resident && small)
-      COLL_UNIT_SWITCH(a2av_res_kernel8, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts,
+      COLL_UNIT_SWITCH(a2av_res_kernel8, unit, L.a2a_nt, dim3(g), L.stream, p, lim, R, counts,
                        sdispls, rdispls, ct, row_units);
     else if (resident)
-      COLL_UNIT_SWITCH(a2av_res_kernel, unit, L.a2a_nt, dim3(g), L.stream, p, R, counts,
+      COLL_UNIT_SWITCH(a2av_res_kernel, unit, L.a2a_nt, dim3(g), L.stream, p, lim, R, counts,
                        sdispls, rdispls, ct, row_units);
     else if (small)
-      COLL_UNIT_SWITCH_BLOCK(a2av_kernel8, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, R,
+      COLL_UNIT_SWITCH_BLOCK(a2av_kernel8, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, lim, R,
                              counts, sdispls, rdispls, ct, row_units);
     else
-      COLL_UNIT_SWITCH_BLOCK(a2av_kernel, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, R,
+      COLL_UNIT_SWITCH_BLOCK(a2av_kernel, unit, L.a2a_nt, dim3(g), kA2aBlock, L.stream, p, lim, R,
                              counts, sdispls, rdispls, ct, row_units);
   } else {
     // chunks: at most capacity bytes / 16 plus one partial chunk per block
@@ -676,7 +692,7 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts
     if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
 #define COLL_A2A_CHUNK(NTV, UNV, FASTV)                                                          \
   hipLaunchKernelGGL((a2av_chunk_kernel<NTV, UNV, FASTV>), dim3(g), dim3(kBlock), 0, L.stream,  \
-                     p, R, counts, sdispls, rdispls, ct, (uint64_t)row_bytes)
+                     p, lim, R, counts, sdispls, rdispls, ct, (uint64_t)row_bytes)
     if (L.a2a_nt && resident) COLL_A2A_CHUNK(true, kA2aResU, true);
     else if (L.a2a_nt) COLL_A2A_CHUNK(true, kA2aU, false);
     else if (resident) COLL_A2A_CHUNK(false, kA2aResU, true);
@@ -695,19 +711,20 @@ size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_
   return ((size_t)R * R * sizeof(A2aBlk) + slots * sizeof(uint16_t) + 255) & ~(size_t)255;
 }
 
-int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
+int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
+                   const int64_t *counts,
                    const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
                    size_t rows_capacity, void *ws) {
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
   // rows that are not whole 16-byte units, or no capacity: the plain form
   if (copy_unit(bits) != 16 || rows_capacity == 0)
-    return launch_a2av(L, R, p, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
+    return launch_a2av(L, R, p, lim, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
   const uint64_t row_units = row_bytes / 16;
   const uint64_t cap_units = (uint64_t)rows_capacity * row_units;
   const uint64_t ndesc = (cap_units + kDescTile - 1) / kDescTile;
   if (ndesc == 0 || ndesc > 0x7FFFFFFFull)     // empty rows, or more tiles than one grid holds
-    return launch_a2av(L, R, p, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
+    return launch_a2av(L, R, p, lim, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
   A2aBlk *blk = reinterpret_cast<A2aBlk *>(ws);
   uint32_t *idx = reinterpret_cast<uint32_t *>(blk + (size_t)R * R);   // two indices per word
   // descriptor writers: a resident grid (COLL_DESC_BUILD_WGS per CU), no
@@ -716,7 +733,7 @@ int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *cou
   const uint64_t gneed = (pairs + kBlock - 1) / kBlock;
   const uint64_t gres = (uint64_t)L.num_cus * kDescBuildWgs;
   hipLaunchKernelGGL((a2av_desc_build<16>), dim3((unsigned)(gneed < gres ? gneed : gres)),
-                     dim3(kBlock), 0, L.stream, p, R, counts, sdispls, rdispls, ct, row_units, idx,
+                     dim3(kBlock), 0, L.stream, p, lim, R, counts, sdispls, rdispls, ct, row_units, idx,
                      ndesc, blk);
   if (L.a2a_nt)
     hipLaunchKernelGGL((a2av_desc_kernel<16, true>), dim3((unsigned)ndesc), dim3(kDescLanes), 0,

@@ -246,10 +246,25 @@ int coll_broadcast(int R, const void *sendbuf_root, void *const *recvbufs, int r
   return launch_broadcast(launch_ctx(stream), R, sendbuf_root, p, count * dtype_size(dtype));
 }
 
+// Rows each rank's buffer holds, from the caller's host array (NULL: that
+// side is not bounded); a NULL buffer holds no rows whatever the array says.
+// false for a negative entry.
+static bool fill_rows(int R, const int64_t *rows, const void *const *bufs, RankRows &out) {
+  for (int r = 0; r < COLL_MAX_RANKS; r++) out.n[r] = INT64_MAX;
+  for (int r = 0; r < R; r++) {
+    if (rows) {
+      if (rows[r] < 0) return false;
+      out.n[r] = rows[r];
+    }
+    if (!bufs[r]) out.n[r] = 0;
+  }
+  return true;
+}
+
 int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcounts,
                       const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
                       size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
-                      void *stream) {
+                      const int64_t *send_rows, const int64_t *recv_rows, void *stream) {
   if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
   if (row_elems == 0) return COLL_OK;
   if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
@@ -262,7 +277,11 @@ int coll_all_to_all_v(int R, const void *const *sendbufs, const int64_t *sendcou
   }
   if (recv_rows_capacity > ((size_t)1 << 48) / (row_elems * dtype_size(dtype)))
     return COLL_ERR_INVALID_ARG;
-  return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, 0,
+  RowLimits lim;
+  if (!fill_rows(R, send_rows, sendbufs, lim.in) ||
+      !fill_rows(R, recv_rows, reinterpret_cast<const void *const *>(recvbufs), lim.out))
+    return COLL_ERR_INVALID_ARG;
+  return launch_a2av(launch_ctx(stream), R, p, lim, sendcounts, sdispls, rdispls, 0,
                      row_elems * dtype_size(dtype), recv_rows_capacity);
 }
 
@@ -277,11 +296,13 @@ size_t coll_all_to_all_v_workspace_bytes(int R, size_t recv_rows_capacity, size_
 
 // The workspace form, forward (ct = 0) or reverse (ct = 1: the tables are the
 // forward exchange's, sendbufs are its receive buffers and recvbufs its send
-// buffers, sdispls its rdispls and rdispls its sdispls).
+// buffers, sdispls its rdispls and rdispls its sdispls, send_rows the rows
+// of its receive buffers and recv_rows those of its send buffers).
 static int a2av_ws_call(int R, const void *const *sendbufs, const int64_t *sendcounts,
                         const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
                         int ct, size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+                        const int64_t *send_rows, const int64_t *recv_rows, void *workspace,
+                        size_t workspace_bytes, void *stream) {
   if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
   if (row_elems == 0) return COLL_OK;
   if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
@@ -298,25 +319,32 @@ static int a2av_ws_call(int R, const void *const *sendbufs, const int64_t *sendc
     p.in[r] = sendbufs[r];
     p.out[r] = recvbufs[r];
   }
+  RowLimits lim;
+  if (!fill_rows(R, send_rows, sendbufs, lim.in) ||
+      !fill_rows(R, recv_rows, reinterpret_cast<const void *const *>(recvbufs), lim.out))
+    return COLL_ERR_INVALID_ARG;
   if (need == 0)
-    return launch_a2av(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, ct, row_bytes,
-                       recv_rows_capacity);
-  return launch_a2av_ws(launch_ctx(stream), R, p, sendcounts, sdispls, rdispls, ct, row_bytes,
-                        recv_rows_capacity, workspace);
+    return launch_a2av(launch_ctx(stream), R, p, lim, sendcounts, sdispls, rdispls, ct,
+                       row_bytes, recv_rows_capacity);
+  return launch_a2av_ws(launch_ctx(stream), R, p, lim, sendcounts, sdispls, rdispls, ct,
+                        row_bytes, recv_rows_capacity, workspace);
 }
 
 int coll_all_to_all_v_ws(int R, const void *const *sendbufs, const int64_t *sendcounts,
                          const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
                          size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+                         const int64_t *send_rows, const int64_t *recv_rows, void *workspace,
+                         size_t workspace_bytes, void *stream) {
   return a2av_ws_call(R, sendbufs, sendcounts, sdispls, recvbufs, rdispls, 0, row_elems, dtype,
-                      recv_rows_capacity, workspace, workspace_bytes, stream);
+                      recv_rows_capacity, send_rows, recv_rows, workspace, workspace_bytes,
+                      stream);
 }
 
 int coll_all_to_all_v_reverse(int R, const void *const *recvbufs, const int64_t *sendcounts,
                               const int64_t *sdispls, void *const *sendbufs,
                               const int64_t *rdispls, size_t row_elems, coll_dtype_t dtype,
-                              size_t send_rows_capacity, void *workspace, size_t workspace_bytes,
+                              size_t send_rows_capacity, const int64_t *send_rows,
+                              const int64_t *recv_rows, void *workspace, size_t workspace_bytes,
                               void *stream) {
   // data moves from the forward receive buffers back to the forward send
   // buffers: the forward rdispls locate the source rows, sdispls the
@@ -335,12 +363,16 @@ int coll_all_to_all_v_reverse(int R, const void *const *recvbufs, const int64_t 
       p.in[r] = recvbufs[r];
       p.out[r] = sendbufs[r];
     }
-    return launch_a2av(launch_ctx(stream), R, p, sendcounts, rdispls, sdispls, 1, row_bytes,
+    RowLimits lim;            // rows are read from recvbufs and written to sendbufs
+    if (!fill_rows(R, recv_rows, reinterpret_cast<const void *const *>(recvbufs), lim.in) ||
+        !fill_rows(R, send_rows, reinterpret_cast<const void *const *>(sendbufs), lim.out))
+      return COLL_ERR_INVALID_ARG;
+    return launch_a2av(launch_ctx(stream), R, p, lim, sendcounts, rdispls, sdispls, 1, row_bytes,
                        send_rows_capacity);
   }
   return a2av_ws_call(R, reinterpret_cast<const void *const *>(recvbufs), sendcounts, rdispls,
-                      sendbufs, sdispls, 1, row_elems, dtype, send_rows_capacity, workspace,
-                      workspace_bytes, stream);
+                      sendbufs, sdispls, 1, row_elems, dtype, send_rows_capacity, recv_rows,
+                      send_rows, workspace, workspace_bytes, stream);
 }
 
 int coll_all_to_all(int R, const void *const *sendbufs, void *const *recvbufs,
@@ -514,7 +546,7 @@ static bool fill_recv(int R, const void *const *src, const void **dst) {
 int coll_moe_dispatch(int R, const void *const *x, const int32_t *const *pos,
                       const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
                       int tokens, int topk, size_t hidden, coll_dtype_t dtype,
-                      void *const *recvbufs, void *stream) {
+                      void *const *recvbufs, const int64_t *recv_rows, void *stream) {
   if (!ranks_ok(R) || !dtype_ok(dtype) || tokens < 0 || topk < 1) return COLL_ERR_INVALID_ARG;
   if (tokens == 0 || hidden == 0) return COLL_OK;
   if ((int64_t)tokens * topk >= ((int64_t)1 << 31) || !bytes_ok(hidden, dtype_size(dtype), 1))
@@ -526,15 +558,18 @@ int coll_moe_dispatch(int R, const void *const *x, const int32_t *const *pos,
     return COLL_ERR_INVALID_ARG;
   MutPtrTable out{};
   for (int r = 0; r < R; r++) out.p[r] = const_cast<void *>(rs.p[r]);
+  RankRows rows;
+  if (!fill_rows(R, recv_rows, rs.p, rows)) return COLL_ERR_INVALID_ARG;
   return launch_moe_dispatch(launch_ctx(stream), R, xs, ps, sendcounts, sdispls, rdispls, tokens,
-                             topk, hidden * dtype_size(dtype), out);
+                             topk, hidden * dtype_size(dtype), out, rows);
 }
 
 int coll_moe_combine_recv(int R, const void *const *recvbufs, const int32_t *const *pos,
                           const int64_t *sendcounts, const int64_t *sdispls,
                           const int64_t *rdispls, const float *const *topk_w,
                           const int32_t *const *topk_ids, int tokens, int topk, size_t hidden,
-                          coll_dtype_t dtype, void *const *out, void *stream) {
+                          coll_dtype_t dtype, void *const *out, const int64_t *recv_rows,
+                          void *stream) {
   if (!ranks_ok(R) || tokens < 0 || topk < 1) return COLL_ERR_INVALID_ARG;
   if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
   if (tokens == 0 || hidden == 0) return COLL_OK;
@@ -549,8 +584,10 @@ int coll_moe_combine_recv(int R, const void *const *recvbufs, const int32_t *con
     return COLL_ERR_INVALID_ARG;
   if (topk_ids && !fill_in(R, reinterpret_cast<const void *const *>(topk_ids), is.p))
     return COLL_ERR_INVALID_ARG;
+  RankRows rows;
+  if (!fill_rows(R, recv_rows, rs.p, rows)) return COLL_ERR_INVALID_ARG;
   return launch_moe_combine_recv(launch_ctx(stream), R, rs, ps, sendcounts, sdispls, rdispls, ws,
-                                 topk_ids ? &is : nullptr, tokens, topk, hidden, os);
+                                 topk_ids ? &is : nullptr, tokens, topk, hidden, os, rows);
 }
 
 }  // extern "C"

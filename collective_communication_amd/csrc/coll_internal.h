@@ -23,6 +23,25 @@ struct RankPtrs {
   void *out[COLL_MAX_RANKS];
 };
 
+// Rows each rank's buffer holds, one table per buffer role of the exchange
+// (in: read, out: written).  A block of an All-to-All-v moves only when all
+// its rows lie inside both of its buffers; INT64_MAX marks a side the caller
+// does not bound.  Passed by value (256 bytes), like RankPtrs.
+struct RankRows {
+  int64_t n[COLL_MAX_RANKS];
+};
+struct RowLimits {
+  RankRows in, out;
+};
+
+// Rows [sdv, sdv + c) of a buffer of lin rows and [rdv, rdv + c) of one of
+// lout rows all exist, and there is at least one (no sum can overflow:
+// lin, lout >= 0).
+__host__ __device__ __forceinline__ bool block_fits(int64_t c, int64_t sdv, int64_t rdv,
+                                                    int64_t lin, int64_t lout) {
+  return c > 0 && sdv >= 0 && rdv >= 0 && sdv <= lin - c && rdv <= lout - c;
+}
+
 // One pointer per rank for a single buffer role (MoE helpers).
 struct PtrTable {
   const void *p[COLL_MAX_RANKS];
@@ -439,13 +458,13 @@ int launch_lse_merge(const Launch &L, int R, const RankPtrs &o, const PtrTable &
                      const MutPtrTable &lse_out, size_t rows, size_t D, int dt);
 // ct = 1: counts is read transposed (the reverse of the exchange whose
 // tables these are; see count_index in a2av.hip)
-int launch_a2av(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
-                size_t rows_capacity);
+int launch_a2av(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
+                const int64_t *counts, const int64_t *sdispls, const int64_t *rdispls, int ct,
+                size_t row_bytes, size_t rows_capacity);
 size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_t min_bytes);
-int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const int64_t *counts,
-                   const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
-                   size_t rows_capacity, void *ws);
+int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
+                   const int64_t *counts, const int64_t *sdispls, const int64_t *rdispls, int ct,
+                   size_t row_bytes, size_t rows_capacity, void *ws);
 
 constexpr int kMoeMaxExperts = 1024;
 // Scratch of coll_moe_layout_noalloc: a device array of this many bytes per
@@ -467,10 +486,12 @@ int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTa
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
 int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,
                         const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
-                        int T, int K, size_t row_bytes, const MutPtrTable &recv);
+                        int T, int K, size_t row_bytes, const MutPtrTable &recv,
+                        const RankRows &recv_rows);
 int launch_moe_combine_recv(const Launch &L, int R, const PtrTable &recv, const PtrTable &pos,
                             const int64_t *sendcounts, const int64_t *sdispls,
                             const int64_t *rdispls, const PtrTable &w, const PtrTable *ids, int T,
-                            int K, size_t hidden, const MutPtrTable &out);
+                            int K, size_t hidden, const MutPtrTable &out,
+                            const RankRows &recv_rows);
 
 }  // namespace coll

@@ -721,16 +721,20 @@ struct SrcBlocks {
   int64_t rd[COLL_MAX_RANKS];
 };
 
+// A block whose receive rows do not all lie inside rank d's buffer (recv_rows)
+// is staged empty: its slots are then held by no block and not written.
 __device__ __forceinline__ void load_src_blocks(SrcBlocks &b, int R, int s,
                                                 const int64_t *sendcounts,
                                                 const int64_t *sdispls,
-                                                const int64_t *rdispls) {
+                                                const int64_t *rdispls,
+                                                const RankRows &recv_rows) {
   if ((int)threadIdx.x < R) {
     const int d = threadIdx.x;
-    const int64_t a = sdispls[s * R + d];
-    b.lo[d] = a;
-    b.hi[d] = a + sendcounts[s * R + d];
-    b.rd[d] = rdispls[d * R + s];
+    const int64_t a = sdispls[s * R + d], c = sendcounts[s * R + d], r = rdispls[d * R + s];
+    const bool ok = block_fits(c, a, r, INT64_MAX, recv_rows.n[d]);
+    b.lo[d] = ok ? a : 1;
+    b.hi[d] = ok ? a + c : 0;
+    b.rd[d] = r;
   }
   __syncthreads();
 }
@@ -761,17 +765,21 @@ struct SrcLane {
   uint64_t base;
 };
 
+// (a block whose receive rows do not all lie inside rank q's buffer is held
+// empty, as in load_src_blocks)
 template <class Table>
 __device__ __forceinline__ SrcLane load_src_lane(int R, int s, const Table &recv,
                                                  const int64_t *sendcounts,
                                                  const int64_t *sdispls,
-                                                 const int64_t *rdispls) {
+                                                 const int64_t *rdispls,
+                                                 const RankRows &recv_rows) {
   const int q = threadIdx.x & 63;
   const int qq = q < R ? q : 0;
   const int64_t a = sdispls[s * R + qq], c = sendcounts[s * R + qq], r = rdispls[qq * R + s];
+  const bool ok = q < R && block_fits(c, a, r, INT64_MAX, recv_rows.n[qq]);
   SrcLane b;
-  b.lo = q < R ? a : 1;
-  b.hi = q < R ? a + c : 0;
+  b.lo = ok ? a : 1;
+  b.hi = ok ? a + c : 0;
   b.off = r - a;
   b.base = reinterpret_cast<uintptr_t>(recv.p[qq]);
   return b;
@@ -808,14 +816,15 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(PtrTa
                                                               MutPtrTable recv,
                                                               const int64_t *sendcounts,
                                                               const int64_t *sdispls,
-                                                              const int64_t *rdispls, int R,
+                                                              const int64_t *rdispls,
+                                                              RankRows recv_rows, int R,
                                                               int T, int K, uint32_t upr,
                                                               int nseg) {
   using U = typename UnitT<B>::T;
   constexpr int UN = kPermuteU;
   __shared__ SrcBlocks blk;
   const int s = blockIdx.y;
-  load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls);
+  load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls, recv_rows);
   const RowItem it = row_item<kDispatchWaves>(T, nseg);
   if (!it.valid) return;
   const int lane = threadIdx.x & 63;
@@ -862,14 +871,14 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(PtrTa
 template <int G, bool NT, bool EXPERT>
 __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kernel(
     PtrTable recv, PtrTable pos, PtrTable wts, PtrTable ids, MutPtrTable out,
-    const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls, int R, int T, int K,
-    uint32_t upr, int nseg) {
+    const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls, RankRows recv_rows,
+    int R, int T, int K, uint32_t upr, int nseg) {
   constexpr int kChunk = 8;
   constexpr int UN = (G == 8) ? kCombineRecvU : 1;
   const int s = blockIdx.y;
   const RowItem it = row_item<kCombineRecvWaves>(T, nseg);
   if (!it.valid) return;
-  const SrcLane bl = load_src_lane(R, s, recv, sendcounts, sdispls, rdispls);
+  const SrcLane bl = load_src_lane(R, s, recv, sendcounts, sdispls, rdispls, recv_rows);
   const int lane = threadIdx.x & 63;
   const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
   const float *wk = reinterpret_cast<const float *>(wts.p[s]) + (size_t)it.t * K;
@@ -1136,7 +1145,8 @@ int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTa
 
 int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,
                         const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
-                        int T, int K, size_t row_bytes, const MutPtrTable &recv) {
+                        int T, int K, size_t row_bytes, const MutPtrTable &recv,
+                        const RankRows &recv_rows) {
   uintptr_t bits = row_bytes;
   for (int r = 0; r < R; r++) bits |= (uintptr_t)x.p[r] | (uintptr_t)recv.p[r];
   const int unit = copy_unit(bits);
@@ -1149,14 +1159,15 @@ int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTabl
   const bool nt = (uint64_t)R * T * upr * unit * (1 + K) >= L.nt_bytes;
   dim3 grid((unsigned)((items + kDispatchWaves - 1) / kDispatchWaves), R);
   COLL_UNIT_SWITCH_BLOCK(moe_dispatch_kernel, unit, nt, grid, 64 * kDispatchWaves, L.stream, x, pos, recv, sendcounts,
-                   sdispls, rdispls, R, T, K, (uint32_t)upr, nseg);
+                   sdispls, rdispls, recv_rows, R, T, K, (uint32_t)upr, nseg);
   return hip_status();
 }
 
 int launch_moe_combine_recv(const Launch &L, int R, const PtrTable &recv, const PtrTable &pos,
                             const int64_t *sendcounts, const int64_t *sdispls,
                             const int64_t *rdispls, const PtrTable &w, const PtrTable *ids, int T,
-                            int K, size_t hidden, const MutPtrTable &out) {
+                            int K, size_t hidden, const MutPtrTable &out,
+                            const RankRows &recv_rows) {
   bool vec = (hidden % 8) == 0;
   for (int r = 0; r < R; r++) vec = vec && aligned16(recv.p[r]) && aligned16(out.p[r]);
   if (T == 0) return COLL_OK;
@@ -1171,7 +1182,8 @@ int launch_moe_combine_recv(const Launch &L, int R, const PtrTable &recv, const 
   const PtrTable &idt = ids ? *ids : none;
 #define COLL_COMBINE_RECV(G, NTV, EX)                                                              \
   hipLaunchKernelGGL((moe_combine_recv_kernel<G, NTV, EX>), grid, dim3(64 * kCombineRecvWaves), 0, L.stream, recv, \
-                     pos, w, idt, out, sendcounts, sdispls, rdispls, R, T, K, (uint32_t)upr, nseg)
+                     pos, w, idt, out, sendcounts, sdispls, rdispls, recv_rows, R, T, K,          \
+                     (uint32_t)upr, nseg)
   if (vec && nt && ids) COLL_COMBINE_RECV(8, true, true);
   else if (vec && nt) COLL_COMBINE_RECV(8, true, false);
   else if (vec && ids) COLL_COMBINE_RECV(8, false, true);

@@ -185,13 +185,22 @@ int coll_broadcast(int nranks, const void *sendbuf_root, void *const *recvbufs, 
  *   recvbufs[d][(rdispls[d*R+s] + j) * row_elems + c]
  *        = sendbufs[s][(sdispls[s*R+d] + j) * row_elems + c],  j < sendcounts[s*R+d].
  * Counts live on the device so a layout kernel can feed this call with no
- * host synchronisation; consequently they are not validated on the host: the
- * caller guarantees every block lies inside its buffers and receive blocks do
- * not overlap.  Send and receive buffers must not overlap.  A rank that sends
- * (or receives) no rows may pass NULL for its buffer; the arrays themselves
- * must not be NULL.
- * The reverse exchange (MoE combine) is the same call with the count matrix
- * transposed and the two displacement tables swapped.
+ * host synchronisation; the host cannot read them.  Instead the kernels bound
+ * every block by the buffers' sizes:
+ *   send_rows[s], recv_rows[d]: rows the buffers sendbufs[s] and recvbufs[d]
+ *   hold (HOST int64 arrays of nranks entries, read during the call; NULL
+ *   leaves that side unbounded, and a NULL buffer holds 0 rows).
+ * Block (s, d) moves only if its count is positive, both displacements are
+ * non-negative and all its rows exist: sdispls[s*R+d] + count <= send_rows[s]
+ * and rdispls[d*R+s] + count <= recv_rows[d].  Otherwise it moves nothing and
+ * the receive rows it names keep their contents; the other blocks are not
+ * affected.  So a wrong table can give a wrong result but never touches
+ * memory outside the buffers.  Receive blocks that overlap each other, or
+ * send and receive buffers that overlap, are the caller's to avoid.  A rank
+ * that sends (or receives) no rows may pass NULL for its buffer; the pointer
+ * arrays themselves must not be NULL.
+ * The reverse exchange (MoE combine) is coll_all_to_all_v_reverse on the same
+ * tables.
  *   recv_rows_capacity: the rows of all receive buffers together, an upper
  *   bound of the rows moved that the host knows without reading the counts.
  *   It only shapes the launch, never the result or the memory addressed.
@@ -202,7 +211,7 @@ int coll_broadcast(int nranks, const void *sendbuf_root, void *const *recvbufs, 
 int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *sendcounts,
                       const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
                       size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
-                      void *stream);
+                      const int64_t *send_rows, const int64_t *recv_rows, void *stream);
 
 /*
  * All-to-All-v with a caller workspace -- tutorial sections 8.1-8.2, the same
@@ -225,13 +234,15 @@ int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *se
  * below the rows actually received costs time, not correctness.
  * Errors: as coll_all_to_all_v, plus COLL_ERR_INVALID_ARG for a NULL or
  * misaligned workspace or workspace_bytes below the size when one is needed.
+ * send_rows / recv_rows bound the blocks as in coll_all_to_all_v.
  */
 size_t coll_all_to_all_v_workspace_bytes(int nranks, size_t recv_rows_capacity, size_t row_elems,
                                         coll_dtype_t dtype);
 int coll_all_to_all_v_ws(int nranks, const void *const *sendbufs, const int64_t *sendcounts,
                          const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
                          size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
-                         void *workspace, size_t workspace_bytes, void *stream);
+                         const int64_t *send_rows, const int64_t *recv_rows, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * The reverse of an All-to-All-v, from that exchange's own tables -- tutorial
@@ -245,7 +256,10 @@ int coll_all_to_all_v_ws(int nranks, const void *const *sendbufs, const int64_t 
  *   recvbufs: the forward exchange's receive buffers (read here);
  *   sendbufs: the forward exchange's send buffers (written here);
  *   send_rows_capacity: an upper bound of the rows moved, here the rows of
- *   the send buffers together (launch shape only, as recv_rows_capacity).
+ *   the send buffers together (launch shape only, as recv_rows_capacity);
+ *   send_rows / recv_rows: the rows of sendbufs[s] / recvbufs[d], as in the
+ *   forward call (HOST, NULL = unbounded); a block moves only if all its rows
+ *   exist on both sides, as in coll_all_to_all_v.
  * workspace / workspace_bytes: as coll_all_to_all_v_ws (size from
  * coll_all_to_all_v_workspace_bytes with send_rows_capacity); NULL and 0
  * select the plain form.  Errors as coll_all_to_all_v_ws.
@@ -253,7 +267,8 @@ int coll_all_to_all_v_ws(int nranks, const void *const *sendbufs, const int64_t 
 int coll_all_to_all_v_reverse(int nranks, const void *const *recvbufs, const int64_t *sendcounts,
                               const int64_t *sdispls, void *const *sendbufs,
                               const int64_t *rdispls, size_t row_elems, coll_dtype_t dtype,
-                              size_t send_rows_capacity, void *workspace, size_t workspace_bytes,
+                              size_t send_rows_capacity, const int64_t *send_rows,
+                              const int64_t *recv_rows, void *workspace, size_t workspace_bytes,
                               void *stream);
 
 /*
@@ -430,13 +445,15 @@ int coll_moe_combine(int nranks, const void *const *back, const int32_t *const *
  *   x[s]: [tokens, hidden]; pos, counts, displacements: the outputs of
  *   coll_moe_layout (device arrays); recvbufs[d]: the receive buffers, NULL
  *   allowed for a rank that receives no rows.  Any dtype (a copy).
- * A slot that no block holds (-1: a pair with no expert) is not written; the caller
- * guarantees that every receive buffer holds the rows the layout sends it.
+ * A slot that no block holds (-1: a pair with no expert) is not written.
+ *   recv_rows[d]: rows recvbufs[d] holds (HOST int64, nranks entries; NULL =
+ *   unbounded): a block whose receive rows do not all exist holds no slot, so
+ *   its rows are not written (as coll_all_to_all_v bounds its blocks).
  */
 int coll_moe_dispatch(int nranks, const void *const *x, const int32_t *const *pos,
                       const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls,
                       int tokens, int topk, size_t hidden, coll_dtype_t dtype,
-                      void *const *recvbufs, void *stream);
+                      void *const *recvbufs, const int64_t *recv_rows, void *stream);
 
 /*
  * Fused combine -- the tutorial's 8.4 combine (results return to the token's
@@ -446,7 +463,7 @@ int coll_moe_dispatch(int nranks, const void *const *x, const int32_t *const *po
  *   out[s][t] = rne( sum_{k ascending} w[s][t*topk+k] * widen(y_k) ),
  *   y_k = recvbufs[d][rdispls[d*R+s] + p - sdispls[s*R+d]]  (p, d as above),
  * with the fold, rounding and no-FMA rule of coll_moe_combine: bit-identical
- * to coll_all_to_all_v with transposed counts followed by coll_moe_combine.
+ * to coll_all_to_all_v_reverse followed by coll_moe_combine.
  * topk_ids != NULL (the routing, [tokens, topk] int32 per rank): the test
  * expert of coll_moe_expert_scale is applied to each row as it is read,
  * y_k = rne(widen(row) * (1 + e/256)) with e = topk_ids[s][t*topk+k], so the
@@ -455,12 +472,16 @@ int coll_moe_dispatch(int nranks, const void *const *x, const int32_t *const *po
  *   bf16 only; out[s]: [tokens, hidden], must not overlap any recvbufs.
  * A slot that no block holds (the layout's -1 for a pair with no expert)
  * adds no term, as in coll_moe_combine.
+ *   recv_rows[d]: rows recvbufs[d] holds (HOST int64, nranks entries; NULL =
+ *   unbounded): a block whose receive rows do not all exist holds no slot, so
+ *   its rows are not read and add no term.
  */
 int coll_moe_combine_recv(int nranks, const void *const *recvbufs, const int32_t *const *pos,
                           const int64_t *sendcounts, const int64_t *sdispls,
                           const int64_t *rdispls, const float *const *topk_w,
                           const int32_t *const *topk_ids, int tokens, int topk, size_t hidden,
-                          coll_dtype_t dtype, void *const *out, void *stream);
+                          coll_dtype_t dtype, void *const *out, const int64_t *recv_rows,
+                          void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,11 @@ FLAGS = ["-x", "c++", "-std=c++17", "-O1", "-g", "-fPIC", "-ffp-contract=off",
          "-I", HERE, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
          # the AllReduce switches to its 2 KiB-per-rank LDS tile from 16 KiB per
          # rank here (48 MiB on the GPU), so both tiles meet the emulator's sizes
-         "-DCOLL_AR_LDS_BIG_BYTES=16384u"]
+         "-DCOLL_AR_LDS_BIG_BYTES=16384u",
+         # the plain All-to-All-v leaves its resident grid above 64 KiB of
+         # receive capacity here (256 MiB on the GPU), so the emulator's cases
+         # run both grids
+         "-DCOLL_A2A_RESIDENT_MAX_BYTES=65536ull"]
 
 
 def sources():

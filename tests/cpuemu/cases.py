@@ -47,6 +47,11 @@ def load():
         fn.argtypes = args
 
 
+def rows(ns):
+    """Per-rank buffer rows as the C ABI's host int64 array."""
+    return (ctypes.c_int64 * len(ns))(*[int(n) for n in ns])
+
+
 def case(*what):
     print("case", *what, flush=True)
 
@@ -173,10 +178,12 @@ def _a2av_case(R, counts, W, dtype, cap=None, ws=False, gap=0):
         need = L.coll_all_to_all_v_workspace_bytes(R, capacity, W, dt)
         work = H.poison(max(need, 256), np.uint8) if need else None
         ok(L.coll_all_to_all_v_ws(R, table(ins), ptr(tabs[0]), ptr(tabs[1]), table(outs),
-                                  ptr(tabs[2]), W, dt, capacity, ptr(work), need, None), "a2av_ws")
+                                  ptr(tabs[2]), W, dt, capacity, rows(send_rows),
+                                  rows(recv_rows), ptr(work), need, None), "a2av_ws")
     else:
         ok(L.coll_all_to_all_v(R, table(ins), ptr(tabs[0]), ptr(tabs[1]), table(outs),
-                               ptr(tabs[2]), W, dt, capacity, None), "a2av")
+                               ptr(tabs[2]), W, dt, capacity, rows(send_rows), rows(recv_rows),
+                               None), "a2av")
     for d in range(R):
         if recv_rows[d]:
             # rows in the gaps are not written: compare the blocks only
@@ -192,13 +199,129 @@ def _a2av_case(R, counts, W, dtype, cap=None, ws=False, gap=0):
         need = L.coll_all_to_all_v_workspace_bytes(R, bcap, W, dt)
         work = H.poison(max(need, 256), np.uint8) if need else None
     ok(L.coll_all_to_all_v_reverse(R, table(outs), ptr(tabs[0]), ptr(tabs[1]), table(backs),
-                                   ptr(tabs[2]), W, dt, bcap, ptr(work), need, None), "reverse")
+                                   ptr(tabs[2]), W, dt, bcap, rows(send_rows), rows(recv_rows),
+                                   ptr(work), need, None), "reverse")
     for s in range(R):
         for d in range(R):
             a, c = int(sd[s, d]) * W, int(counts[s, d]) * W
             if c:
                 same(backs[s][a:a + c], sends[s].reshape(-1)[a:a + c], f"reverse block {d}->{s}")
     return sends, counts, sd, rd, outs
+
+
+POISON = 0xAB
+
+
+def _a2av_bad_case(R, W, ws):
+    """Tables that name rows outside the buffers: each bad block moves nothing
+    (its receive rows keep their contents), every other block is exact, and
+    the guard pages show that nothing outside the buffers is touched.  The
+    reverse call on the same tables skips the same blocks."""
+    g = np.random.default_rng(77 + R + W)
+    counts = g.integers(1, 30, size=(R, R)).astype(np.int64)
+    sd, rd = oracle.packed_displs(counts)
+    send_rows = [int(counts[s].sum()) for s in range(R)]
+    recv_rows = [int(counts[:, d].sum()) for d in range(R)]
+    bad_c, bad_sd, bad_rd = counts.copy(), sd.copy(), rd.copy()
+    bad = set()
+    # a count that runs past the receive buffer; a negative send displacement;
+    # a receive displacement whose block ends one row past the buffer; a count
+    # that runs past the send buffer; a negative count (a block of nothing)
+    picks = [(0, R - 1), (R - 1, 0), (R // 2, R // 2), (1 % R, (R - 2) % R), (R - 1, R - 1)]
+    for i, (s, d) in enumerate(picks):
+        if (s, d) in bad:
+            continue
+        if i == 0:
+            bad_c[s, d] = counts[s, d] + recv_rows[d]
+        elif i == 1:
+            bad_sd[s, d] = -3
+        elif i == 2:
+            bad_rd[d, s] = recv_rows[d] - counts[s, d] + 1
+        elif i == 3:
+            bad_c[s, d] = send_rows[s] + 1
+        else:
+            bad_c[s, d] = -5
+        bad.add((s, d))
+    sends = [gen("bf16", send_rows[s] * W, 900 + s) for s in range(R)]
+    eff = counts.copy()
+    for s, d in bad:
+        eff[s, d] = 0
+    want = oracle.all_to_all_v([x.reshape(-1) for x in sends], eff, sd, rd, np.array(recv_rows), W)
+    ins = [H.copy(x) for x in sends]
+    outs = [H.poison(recv_rows[d] * W, np.uint16) for d in range(R)]
+    tabs = [H.copy(np.ascontiguousarray(t).reshape(-1)) for t in (bad_c, bad_sd, bad_rd)]
+    cap = sum(recv_rows)
+    work, need = None, 0
+    if ws:
+        need = L.coll_all_to_all_v_workspace_bytes(R, cap, W, BF16)
+        work = H.poison(max(need, 256), np.uint8) if need else None
+        ok(L.coll_all_to_all_v_ws(R, table(ins), ptr(tabs[0]), ptr(tabs[1]), table(outs),
+                                  ptr(tabs[2]), W, BF16, cap, rows(send_rows), rows(recv_rows),
+                                  ptr(work), need, None), "a2av_ws bad tables")
+    else:
+        ok(L.coll_all_to_all_v(R, table(ins), ptr(tabs[0]), ptr(tabs[1]), table(outs),
+                               ptr(tabs[2]), W, BF16, cap, rows(send_rows), rows(recv_rows), None),
+           "a2av bad tables")
+    for s in range(R):
+        for d in range(R):
+            a, c = int(rd[d, s]) * W, int(counts[s, d]) * W
+            if (s, d) in bad:
+                assert np.all(outs[d][a:a + c].view(np.uint8) == POISON), f"bad block {s}->{d} written"
+            else:
+                same(outs[d][a:a + c], want[d][a:a + c], f"good block {s}->{d}")
+    backs = [H.poison(send_rows[s] * W, np.uint16) for s in range(R)]
+    ok(L.coll_all_to_all_v_reverse(R, table(outs), ptr(tabs[0]), ptr(tabs[1]), table(backs),
+                                   ptr(tabs[2]), W, BF16, sum(send_rows), rows(send_rows),
+                                   rows(recv_rows), ptr(work), need, None), "reverse bad tables")
+    for s in range(R):
+        for d in range(R):
+            a, c = int(sd[s, d]) * W, int(counts[s, d]) * W
+            if (s, d) in bad:
+                assert np.all(backs[s][a:a + c].view(np.uint8) == POISON), f"bad block {d}->{s} back"
+            else:
+                same(backs[s][a:a + c], sends[s].reshape(-1)[a:a + c], f"good block back {d}->{s}")
+
+
+def _moe_fused_bad_block(R, T, K, Hd, lay, x_b, pos, w_b, id_b, want, rrows):
+    """The fused pair with one block's receive displacement past its buffer:
+    that block's rows are neither written by the dispatch nor read by the
+    combine (its pairs add no term); everything else is exact."""
+    sc_h, sd_h, rd_h = (np.array(lay[k], np.int64) for k in ("sendcounts", "sdispls", "rdispls"))
+    cand = [(s, d) for s in range(R) for d in range(R) if sc_h[s, d] > 0]
+    s0, d0 = cand[len(cand) // 2]
+    bad_rd = rd_h.copy()
+    bad_rd[d0, s0] = int(rrows[d0]) - int(sc_h[s0, d0]) + 1
+    sc, sd, rd = (H.copy(np.ascontiguousarray(t).reshape(-1)) for t in (sc_h, sd_h, bad_rd))
+    recv = [H.poison((int(n), Hd), np.uint16) if n else None for n in rrows]
+    ok(L.coll_moe_dispatch(R, table(x_b), table(pos), ptr(sc), ptr(sd), ptr(rd), T, K, Hd, BF16,
+                           table(recv), rows(rrows), None), "dispatch, bad block")
+    for d in range(R):
+        for s in range(R):
+            a, c = int(rd_h[d, s]), int(sc_h[s, d])
+            if not c:
+                continue
+            got = recv[d][a:a + c]
+            if (s, d) == (s0, d0):
+                assert np.all(got.view(np.uint8) == POISON), "bad block written by the dispatch"
+            else:
+                same(got, want["recvs"][d].reshape(-1, Hd)[a:a + c], f"dispatch block {s}->{d}")
+    # the combine: pairs whose slot lies in the bad block are dropped
+    lo, hi = int(sd_h[s0, d0]), int(sd_h[s0, d0] + sc_h[s0, d0])
+    pos_eff = [np.array(lay["pos"][s]) for s in range(R)]
+    m = (pos_eff[s0] >= lo) & (pos_eff[s0] < hi)
+    pos_eff[s0] = np.where(m, -1, pos_eff[s0]).astype(np.int32)
+    good = [H.copy(np.asarray(r)) if r is not None else None for r in recv]
+    for d in range(R):          # fill the bad block's rows with the correct data first: the
+        if rrows[d]:            # combine must still skip them
+            good[d][...] = want["recvs"][d].reshape(-1, Hd)[:int(rrows[d])]
+    outs = [H.poison((T, Hd), np.uint16) for _ in range(R)]
+    ok(L.coll_moe_combine_recv(R, table(good), table(pos), ptr(sc), ptr(sd), ptr(rd), table(w_b),
+                               table(id_b), T, K, Hd, BF16, table(outs), rows(rrows), None),
+       "combine_recv, bad block")
+    expect = oracle.moe_combine([np.asarray(b) for b in want["backs"]], pos_eff,
+                                [np.asarray(w) for w in w_b], Hd)
+    for s in range(R):
+        same(outs[s], expect[s], f"fused combine with a bad block, rank {s}")
 
 
 def fam_a2av():
@@ -228,6 +351,10 @@ def fam_a2av():
     _a2av_case(4, g.integers(30, 60, size=(4, 4)), 8, "bf16", ws=True, cap=50)
     case("a2av descriptor form, gapped")
     _a2av_case(3, g.integers(1, 30, size=(3, 3)), 16, "bf16", ws=True, gap=7)
+    for R, W in ((8, 8), (4, 5), (3, 24), (16, 8), (8, 64), (16, 64)):
+        for ws in (False, True):
+            case("a2av tables that name rows outside the buffers", R, W, "ws" if ws else "plain")
+            _a2av_bad_case(R, W, ws)
 
 
 def fam_exchange():
@@ -355,7 +482,8 @@ def fam_moe():
         rrows = lay["sendcounts"].sum(axis=0)
         recvs = [H.poison((int(n), Hd), np.uint16) if n else None for n in rrows]
         ok(L.coll_all_to_all_v(R, table(sends), ptr(sc), ptr(sd), table(recvs), ptr(rd), Hd,
-                               BF16, int(rrows.sum()), None), "a2av")
+                               BF16, int(rrows.sum()), rows([T * K] * R), rows(rrows), None),
+           "a2av")
         for d in range(R):
             if rrows[d]:
                 same(recvs[d].reshape(-1), want["recvs"][d].reshape(-1)[:int(rrows[d]) * Hd], "recv")
@@ -373,7 +501,8 @@ def fam_moe():
         backs = [H.poison((T * K, Hd), np.uint16) for _ in range(R)]
         sc_t = H.copy(np.ascontiguousarray(lay["sendcounts"].T).reshape(-1))
         ok(L.coll_all_to_all_v(R, table(ys), ptr(sc_t), ptr(rd), table(backs), ptr(sd), Hd,
-                               BF16, T * K * R, None), "a2av back")
+                               BF16, T * K * R, rows(rrows), rows([T * K] * R), None),
+           "a2av back")
         for s in range(R):
             same(backs[s].reshape(-1)[:nsend[s] * Hd],
                  want["backs"][s].reshape(-1)[:nsend[s] * Hd], "back")
@@ -384,7 +513,8 @@ def fam_moe():
             need = L.coll_all_to_all_v_workspace_bytes(R, T * K * R, Hd, BF16) if use_ws else 0
             work = H.poison(max(need, 256), np.uint8) if need else None
             ok(L.coll_all_to_all_v_reverse(R, table(ys), ptr(sc), ptr(sd), table(backs2), ptr(rd),
-                                           Hd, BF16, T * K * R, ptr(work), need, None), "reverse")
+                                           Hd, BF16, T * K * R, rows([T * K] * R), rows(rrows),
+                                           ptr(work), need, None), "reverse")
             for s in range(R):
                 same(backs2[s].reshape(-1)[:nsend[s] * Hd],
                      want["backs"][s].reshape(-1)[:nsend[s] * Hd], f"reverse ws={use_ws}")
@@ -396,16 +526,17 @@ def fam_moe():
         # the fused pair
         recv2 = [H.poison((int(n), Hd), np.uint16) if n else None for n in rrows]
         ok(L.coll_moe_dispatch(R, table(x_b), table(pos), ptr(sc), ptr(sd), ptr(rd), T, K, Hd,
-                               BF16, table(recv2), None), "dispatch")
+                               BF16, table(recv2), rows(rrows), None), "dispatch")
         for d in range(R):
             if rrows[d]:
                 same(recv2[d], recvs[d], "fused dispatch")
         outs2 = [H.poison((T, Hd), np.uint16) for _ in range(R)]
         ok(L.coll_moe_combine_recv(R, table(recv2), table(pos), ptr(sc), ptr(sd), ptr(rd),
-                                   table(w_b), table(id_b), T, K, Hd, BF16, table(outs2), None),
-           "combine_recv")
+                                   table(w_b), table(id_b), T, K, Hd, BF16, table(outs2),
+                                   rows(rrows), None), "combine_recv")
         for s in range(R):
             same(outs2[s], want["outs"][s], "fused combine")
+        _moe_fused_bad_block(R, T, K, Hd, lay, x_b, pos, w_b, id_b, want, rrows)
 
 
 FAMILIES = {"reduce": fam_reduce, "copy": fam_copy, "a2av": fam_a2av, "exchange": fam_exchange,

@@ -50,7 +50,7 @@ def test_rank_count_rejected(L, R):
     assert L.coll_all_gather(R, NULL, NULL, 8, 0, NULL) == -1
     assert L.coll_gather(R, NULL, NULL, 0, 1, 8, 0, NULL) == -1
     assert L.coll_broadcast(R, NULL, NULL, 0, 8, 0, NULL) == -1
-    assert L.coll_all_to_all_v(R, NULL, NULL, NULL, NULL, NULL, 8, 0, 0, NULL) == -1
+    assert L.coll_all_to_all_v(R, NULL, NULL, NULL, NULL, NULL, 8, 0, 0, NULL, NULL, NULL) == -1
 
 
 def test_zero_count_is_a_no_op(L):
@@ -173,13 +173,13 @@ def test_a2av_workspace_size_and_validation(L):
     assert size(2, K // 64 + 1) == size(2, K // 64) + 512 * 2
     t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     # a needed workspace that is NULL, misaligned or too small: rejected
-    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, NULL, need, NULL) == -1
-    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, 0x1010, need, NULL) == -1
-    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, 0x1000, need - 1,
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, NULL, NULL, NULL, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, NULL, NULL, 0x1010, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, NULL, NULL, 0x1000, need - 1,
                                   NULL) == -1
     # NULL tables rejected as in coll_all_to_all_v; rows of 0 elements: nothing to do
-    assert L.coll_all_to_all_v_ws(2, t, NULL, 0x200, t, 0x300, 8, 0, K, 0x1000, need, NULL) == -1
-    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 0, 0, K, NULL, 0, NULL) == 0
+    assert L.coll_all_to_all_v_ws(2, t, NULL, 0x200, t, 0x300, 8, 0, K, NULL, NULL, 0x1000, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws(2, t, 0x100, 0x200, t, 0x300, 0, 0, K, NULL, NULL, NULL, 0, NULL) == 0
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -191,13 +191,19 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def test_a2av_null_arrays_rejected_but_null_entries_allowed_on_host(L):
     # the pointer arrays themselves are required
-    assert L.coll_all_to_all_v(2, NULL, 0x10, 0x20, NULL, 0x30, 8, 0, 0, NULL) == -1
+    assert L.coll_all_to_all_v(2, NULL, 0x10, 0x20, NULL, 0x30, 8, 0, 0, NULL, NULL, NULL) == -1
     # device count tables are required
     ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
-    assert L.coll_all_to_all_v(2, ok, NULL, 0x20, ok, 0x30, 8, 0, 0, NULL) == -1
-    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, NULL, 8, 0, 0, NULL) == -1
+    assert L.coll_all_to_all_v(2, ok, NULL, 0x20, ok, 0x30, 8, 0, 0, NULL, NULL, NULL) == -1
+    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, NULL, 8, 0, 0, NULL, NULL, NULL) == -1
+    # negative buffer rows are rejected on either side (rows only bound blocks)
+    neg = (ctypes.c_int64 * 2)(4, -1)
+    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, 0x30, 8, 0, 0, neg, NULL, NULL) == -1
+    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, 0x30, 8, 0, 0, NULL, neg, NULL) == -1
+    assert L.coll_all_to_all_v_reverse(2, ok, 0x10, 0x20, ok, 0x30, 8, 0, 0, neg, NULL, NULL, 0,
+                                       NULL) == -1
     # an absurd capacity is rejected (it would overflow the launch size)
-    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, 0x30, 8, 0, 1 << 62, NULL) == -1
+    assert L.coll_all_to_all_v(2, ok, 0x10, 0x20, ok, 0x30, 8, 0, 1 << 62, NULL, NULL, NULL) == -1
 
 
 def test_reduce_and_scatter_validation(L):
@@ -346,22 +352,23 @@ def test_fused_moe_entry_points_validate_on_host(L):
     ok = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     tab = 0x3000                                       # a (never dereferenced) device table
     # bad rank count, topk, tokens
-    assert L.coll_moe_dispatch(0, ok, ok, tab, tab, tab, 4, 2, 8, 0, ok, NULL) == -1
-    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 0, 8, 0, ok, NULL) == -1
-    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, -1, 2, 8, 0, ok, NULL) == -1
+    assert L.coll_moe_dispatch(0, ok, ok, tab, tab, tab, 4, 2, 8, 0, ok, NULL, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 0, 8, 0, ok, NULL, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, -1, 2, 8, 0, ok, NULL, NULL) == -1
     # zero tokens / zero hidden: no-op
-    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 0, 2, 8, 0, ok, NULL) == 0
-    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 2, 0, 0, ok, NULL) == 0
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 0, 2, 8, 0, ok, NULL, NULL) == 0
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 2, 0, 0, ok, NULL, NULL) == 0
     # missing layout tables or buffers
-    assert L.coll_moe_dispatch(2, ok, ok, NULL, tab, tab, 4, 2, 8, 0, ok, NULL) == -1
-    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, NULL, 4, 2, 8, 0, ok, NULL) == -1
-    assert L.coll_moe_dispatch(2, NULL, ok, tab, tab, tab, 4, 2, 8, 0, ok, NULL) == -1
-    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 2, 8, 0, NULL, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, NULL, tab, tab, 4, 2, 8, 0, ok, NULL, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, NULL, 4, 2, 8, 0, ok, NULL, NULL) == -1
+    assert L.coll_moe_dispatch(2, NULL, ok, tab, tab, tab, 4, 2, 8, 0, ok, NULL, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 2, 8, 0, NULL, NULL, NULL) == -1
     # T*K must stay below 2^31
-    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 1 << 28, 8, 8, 0, ok, NULL) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 1 << 28, 8, 8, 0, ok, NULL, NULL) == -1
 
-    def cr(R=2, recv=ok, pos=ok, sc=tab, w=ok, ids=NULL, T=4, K=2, H=8, dt=0, out=ok):
-        return L.coll_moe_combine_recv(R, recv, pos, sc, tab, tab, w, ids, T, K, H, dt, out, NULL)
+    def cr(R=2, recv=ok, pos=ok, sc=tab, w=ok, ids=NULL, T=4, K=2, H=8, dt=0, out=ok, rows=NULL):
+        return L.coll_moe_combine_recv(R, recv, pos, sc, tab, tab, w, ids, T, K, H, dt, out, rows,
+                                       NULL)
     assert cr(R=17) == -1
     assert cr(K=0) == -1
     assert cr(dt=2) == -2                              # bf16 only
@@ -372,6 +379,10 @@ def test_fused_moe_entry_points_validate_on_host(L):
     assert cr(pos=NULL) == -1
     half = (ctypes.c_void_p * 2)(0x1000, 0)
     assert cr(ids=half) == -1                          # ids given: every rank needs them
+    # receive rows: a negative entry is rejected, any non-negative one accepted
+    assert cr(rows=(ctypes.c_int64 * 2)(5, -1)) == -1
+    assert L.coll_moe_dispatch(2, ok, ok, tab, tab, tab, 4, 2, 8, 0, ok,
+                               (ctypes.c_int64 * 2)(-3, 0), NULL) == -1
 
 
 def test_prepare_rejects_a_non_collective():

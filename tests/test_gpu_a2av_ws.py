@@ -68,6 +68,11 @@ def desc_rows(row_bytes):
     return -(-DESC_MIN_BYTES // row_bytes)
 
 
+def rows_of(bufs, W):
+    """Rows of W bf16 each buffer holds, as the C ABI's host int64 array."""
+    return (ctypes.c_int64 * len(bufs))(*[t.numel() // W for t in bufs])
+
+
 def call_ws(R, sends, counts, sd, recvs, rd, W, capacity):
     """coll_all_to_all_v_ws through the C ABI with an explicit capacity."""
     L = coll.lib()
@@ -78,8 +83,8 @@ def call_ws(R, sends, counts, sd, recvs, rd, W, capacity):
     rc = L.coll_all_to_all_v_ws(R, (ctypes.c_void_p * R)(*[t.data_ptr() for t in sends]),
                                 keep[0].data_ptr(), keep[1].data_ptr(),
                                 (ctypes.c_void_p * R)(*[t.data_ptr() for t in recvs]),
-                                keep[2].data_ptr(), W, 0, capacity, ws.data_ptr(),
-                                ws.numel(), st)
+                                keep[2].data_ptr(), W, 0, capacity, rows_of(sends, W),
+                                rows_of(recvs, W), ws.data_ptr(), ws.numel(), st)
     torch.cuda.synchronize()
     return rc
 
@@ -165,7 +170,8 @@ def test_misaligned_buffers_use_the_plain_form():
     rc = coll.lib().coll_all_to_all_v_ws(
         R, (ctypes.c_void_p * R)(*[t.data_ptr() for t in sends]), keep[0].data_ptr(),
         keep[1].data_ptr(), (ctypes.c_void_p * R)(*[t.data_ptr() + 8 for t in shifted]),
-        keep[2].data_ptr(), W, 0, cap, ws.data_ptr(), need,
+        keep[2].data_ptr(), W, 0, cap, rows_of(sends, W),
+        (ctypes.c_int64 * R)(*[(t.numel() - 4) // W for t in shifted]), ws.data_ptr(), need,
         torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0
