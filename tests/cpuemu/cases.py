@@ -382,9 +382,12 @@ def fam_exchange():
 
 def fam_merge():
     g = np.random.default_rng(9)
+    # whole rows per wave (at most 64 units) and segments of longer rows,
+    # vector and scalar forms, ragged last workgroups
     for R, rows, D, dtype in ((1, 10, 128, "bf16"), (2, 37, 64, "fp32"), (8, 300, 128, "bf16"),
                               (4, 10, 5, "bf16"), (16, 30, 16, "fp32"), (3, 9, 1000, "bf16"),
-                              (8, 5, 520, "fp32")):
+                              (8, 5, 520, "fp32"), (4, 1000, 8, "bf16"), (8, 77, 256, "bf16"),
+                              (5, 63, 64, "fp32"), (16, 200, 512, "bf16"), (6, 3, 8, "fp32")):
         case("lse_merge", R, rows, D, dtype)
         o = [gen(dtype, rows * D, 1000 + r) for r in range(R)]
         lse = [(g.normal(size=rows) * 3).astype(np.float32) for _ in range(R)]
@@ -415,6 +418,23 @@ def fam_merge():
             for r in range(R):
                 if np.any(f(outs[r]).reshape(rows, D)[3] != 0):
                     raise AssertionError("all-empty row not zero")
+    case("lse_merge in place, R = 8")
+    R, rows, D = 8, 130, 128
+    o = [gen("bf16", rows * D, 1100 + r) for r in range(R)]
+    lse = [(g.normal(size=rows) * 3).astype(np.float32) for _ in range(R)]
+    want_o, want_l = oracle.lse_merge(o, lse, "bf16")
+    bufs = [H.copy(x) for x in o]
+    lin = [H.copy(x) for x in lse]
+    lout = [H.poison(rows, np.float32) for _ in range(R)]
+    ok(L.coll_lse_merge(R, table(bufs), table(lin), table(bufs), table(lout), rows, D, BF16,
+                        None), "lse_merge in place")
+    exp = oracle.bf16_to_f32(want_o).astype(np.float64)
+    for r in range(R):
+        got = oracle.bf16_to_f32(bufs[r]).astype(np.float64)
+        if not np.all(np.abs(got - exp) <= 2 * 2.0 ** -7 * np.abs(exp) + 1e-5 * (np.max(np.abs(exp)) + 1)):
+            raise AssertionError(f"lse_merge in place rank {r}")
+        if not np.allclose(lout[r], want_l, rtol=1e-5, atol=1e-5):
+            raise AssertionError(f"lse_merge in place L rank {r}")
 
 
 def _moe(R, E, T, K, Hd, bad=False, seed=5100):
