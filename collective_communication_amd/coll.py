@@ -58,7 +58,7 @@ SIGNATURES = {
     "coll_moe_layout_noalloc": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_expert_workspace_bytes": (_sz, [_i, _i, _sz]),
-    "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _sz, _vp]),
+    "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _vp, _sz, _vp]),
     "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_dispatch": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp, _vp]),
     "coll_moe_combine_recv": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp,
@@ -564,7 +564,7 @@ def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
     ws_bytes = workspace.numel() * workspace.element_size()
     return _issue("coll_moe_expert_scale", "moe_expert_scale", stream, R, _table(recvs, "recv", R),
                   _dev(expert_counts, "ec"), _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
-                  capacity, _dev(workspace, "ws"), ws_bytes)
+                  capacity, _rows(recvs, hidden), _dev(workspace, "ws"), ws_bytes)
 
 
 def moe_combine(backs, pos, weights, outs, stream=None):

@@ -502,8 +502,9 @@ size_t coll_moe_expert_workspace_bytes(int R, int n_experts, size_t recv_rows_ca
 
 int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
-                          coll_dtype_t dtype, size_t recv_rows_capacity, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+                          coll_dtype_t dtype, size_t recv_rows_capacity,
+                          const int64_t *recv_rows, void *workspace, size_t workspace_bytes,
+                          void *stream) {
   if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0)
     return COLL_ERR_INVALID_ARG;
   if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
@@ -515,8 +516,11 @@ int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_co
   MutPtrTable rs{};
   if (!fill_out(R, recvbufs, rs.p)) return COLL_ERR_INVALID_ARG;
   if (recv_rows_capacity > ((size_t)1 << 48) / hidden) return COLL_ERR_INVALID_ARG;
+  RankRows rows;
+  if (!fill_rows(R, recv_rows, reinterpret_cast<const void *const *>(recvbufs), rows))
+    return COLL_ERR_INVALID_ARG;
   return launch_moe_expert_scale(launch_ctx(stream), R, rs, expert_counts, rdispls, n_experts,
-                                 hidden, recv_rows_capacity, workspace, workspace_bytes);
+                                 hidden, recv_rows_capacity, workspace, workspace_bytes, rows);
 }
 
 int coll_moe_combine(int R, const void *const *back, const int32_t *const *pos,

@@ -481,7 +481,8 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
                        int K, size_t row_bytes, const MutPtrTable &send);
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
-                            size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes);
+                            size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes,
+                            const RankRows &recv_rows);
 int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTable &pos,
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
 int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,

@@ -356,18 +356,36 @@ __global__ __launch_bounds__(64 * kPermuteWaves) void moe_permute_kernel(PtrTabl
 //              iff s_end[j-1] <= g < s_end[j];
 //   rb[j]    = rdispls[d*R+s] - (rows in entries before (d, s)'s first),
 //              so the receive row of g in recv[d] is rb[j] + g.
+// A (d, s) block with a negative expert count, or whose rows do not all lie
+// inside recv[d] (recv_rows), counts as empty: no row of it is numbered, so
+// the kernels that follow never address it and its rows keep their values.
 __global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_counts,
                                                          const int64_t *rdispls, int R, int E,
-                                                         int64_t *s_end, int64_t *rb) {
+                                                         RankRows recv_rows, int64_t *s_end,
+                                                         int64_t *rb) {
   __shared__ int64_t wsum[16];
   __shared__ int64_t first_end[COLL_MAX_RANKS * COLL_MAX_RANKS];   // rows before (d, s)
+  __shared__ int s_ok[COLL_MAX_RANKS * COLL_MAX_RANKS];
   const int per = E / R;
   const int N = R * E;
   const int chunk = (N + 1023) / 1024;           // <= 16 (R <= 16, E <= 1024)
   const int j0 = (int)threadIdx.x * chunk;
+  if ((int)threadIdx.x < R * R) {
+    const int d = threadIdx.x / R, s = threadIdx.x - d * R;
+    int64_t sum = 0;
+    bool neg = false;
+    for (int el = 0; el < per; el++) {
+      const int64_t c = expert_counts[(size_t)s * E + d * per + el];
+      neg = neg || c < 0;
+      sum += c < 0 ? 0 : c;
+    }
+    s_ok[threadIdx.x] =
+        !neg && (sum == 0 || block_fits(sum, 0, rdispls[d * R + s], INT64_MAX, recv_rows.n[d]));
+  }
+  __syncthreads();
   auto count_of = [&](int j) -> int64_t {
     const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
-    return (int64_t)expert_counts[(size_t)s * E + d * per + el];
+    return s_ok[d * R + s] ? (int64_t)expert_counts[(size_t)s * E + d * per + el] : 0;
   };
   int64_t local = 0;
   for (int c = 0; c < chunk; c++)
@@ -1053,12 +1071,13 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
 
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
-                            size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes) {
+                            size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes,
+                            const RankRows &recv_rows) {
   const int N = R * E;
   int64_t *s_end = reinterpret_cast<int64_t *>(ws);
   int64_t *rb = s_end + N;
   hipLaunchKernelGGL(moe_expert_table, dim3(1), dim3(1024), 0, L.stream, expert_counts, rdispls,
-                     R, E, s_end, rb);
+                     R, E, recv_rows, s_end, rb);
   int top = 1;
   while (top * 64 < N) top *= 64;
   bool vec = (hidden % 8) == 0;

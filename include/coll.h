@@ -400,7 +400,12 @@ size_t coll_moe_expert_workspace_bytes(int nranks, int n_experts, size_t recv_ro
  * same stream, if it is large enough.
  * recv_rows_capacity: as for coll_all_to_all_v, an upper bound of the rows
  * received by all ranks together; it only sizes the launch and never
- * addresses memory, so a wrong bound costs time, not correctness.  Rows whose
+ * addresses memory, so a wrong bound costs time, not correctness.
+ * recv_rows[d]: rows recvbufs[d] holds (HOST int64, nranks entries; NULL =
+ * unbounded).  A (d, s) block -- the rows s sent to d, every one of d's
+ * experts -- with a negative expert count, or whose rows do not all lie
+ * inside recvbufs[d], is left as it is, as coll_all_to_all_v bounds its
+ * blocks.  Rows whose
  * hidden is a multiple of 8 with 16-byte aligned buffers, a nonzero capacity,
  * a workspace of coll_moe_expert_workspace_bytes(nranks, n_experts,
  * recv_rows_capacity) bytes and nranks * n_experts <= 8192 take the faster
@@ -414,8 +419,9 @@ size_t coll_moe_expert_workspace_bytes(int nranks, int n_experts, size_t recv_ro
  */
 int coll_moe_expert_scale(int nranks, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
-                          coll_dtype_t dtype, size_t recv_rows_capacity, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          coll_dtype_t dtype, size_t recv_rows_capacity,
+                          const int64_t *recv_rows, void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /*
  * Combine (results return to the token's owner and are gate-weighted):

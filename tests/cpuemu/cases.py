@@ -282,6 +282,43 @@ def _a2av_bad_case(R, W, ws):
                 same(backs[s][a:a + c], sends[s].reshape(-1)[a:a + c], f"good block back {d}->{s}")
 
 
+def _expert_bad_block(R, E, Hd, recvs, lay, want, rrows):
+    """The test expert on tables with one bad (d, s) block -- a negative
+    expert count, or a receive displacement that runs past recv[d]: that
+    block's rows keep their values, every other row is scaled exactly, on
+    both the row-descriptor path and the table search."""
+    per = E // R
+    ec_h = np.array(lay["expert_counts"], np.int32).reshape(R, E)
+    rd_h = np.array(lay["rdispls"], np.int64)
+    blocks = [(s, d) for s in range(R) for d in range(R)
+              if ec_h[s, d * per:(d + 1) * per].sum() > 0]
+    s0, d0 = blocks[len(blocks) // 2]
+    n0 = int(ec_h[s0, d0 * per:(d0 + 1) * per].sum())
+    for kind in ("negative count", "displacement past the buffer"):
+        ec2, rd2 = ec_h.copy(), rd_h.copy()
+        if kind == "negative count":
+            ec2[s0, d0 * per] = -1
+        else:
+            rd2[d0, s0] = int(rrows[d0]) - n0 + 1
+        for cap in (int(rrows.sum()), 0):
+            case("expert with a bad block", kind, "cap", cap)
+            ys = [H.copy(r) if r is not None else None for r in recvs]
+            ec_b = H.copy(np.ascontiguousarray(ec2).reshape(-1))
+            rd_b = H.copy(np.ascontiguousarray(rd2).reshape(-1))
+            need = L.coll_moe_expert_workspace_bytes(R, E, cap)
+            ews = H.poison(need, np.uint8)
+            ok(L.coll_moe_expert_scale(R, table(ys), ptr(ec_b), ptr(rd_b), E, Hd, BF16, cap,
+                                       rows(rrows), ptr(ews), need, None), "expert, bad block")
+            for d in range(R):
+                if not rrows[d]:
+                    continue
+                exp = want["ys"][d].reshape(-1, Hd)[:int(rrows[d])].copy()
+                if d == d0:
+                    a = int(rd_h[d0, s0])
+                    exp[a:a + n0] = recvs[d0][a:a + n0]
+                same(ys[d], exp, f"expert with a bad block ({kind}), rank {d}")
+
+
 def _moe_fused_bad_block(R, T, K, Hd, lay, x_b, pos, w_b, id_b, want, rrows):
     """The fused pair with one block's receive displacement past its buffer:
     that block's rows are neither written by the dispatch nor read by the
@@ -512,12 +549,14 @@ def fam_moe():
             ys = [H.copy(r) if r is not None else None for r in recvs]
             need = L.coll_moe_expert_workspace_bytes(R, E, cap)
             ews = H.poison(need, np.uint8)
-            ok(L.coll_moe_expert_scale(R, table(ys), ptr(ec), ptr(rd), E, Hd, BF16, cap, ptr(ews),
+            ok(L.coll_moe_expert_scale(R, table(ys), ptr(ec), ptr(rd), E, Hd, BF16, cap,
+                                       rows(rrows), ptr(ews),
                                        need, None), "expert")
             for d in range(R):
                 if rrows[d]:
                     same(ys[d].reshape(-1), want["ys"][d].reshape(-1)[:int(rrows[d]) * Hd],
                          f"expert cap {cap}")
+        _expert_bad_block(R, E, Hd, recvs, lay, want, rrows)
         backs = [H.poison((T * K, Hd), np.uint16) for _ in range(R)]
         sc_t = H.copy(np.ascontiguousarray(lay["sendcounts"].T).reshape(-1))
         ok(L.coll_all_to_all_v(R, table(ys), ptr(sc_t), ptr(rd), table(backs), ptr(sd), Hd,

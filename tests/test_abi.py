@@ -83,7 +83,7 @@ def test_dtype_and_op_rejected(L):
     assert L.coll_allreduce(2, NULL, NULL, 8, 7, 0, NULL) == -1
     assert L.coll_allreduce(2, NULL, NULL, 8, 0, 9, NULL) == -2
     assert L.coll_reduce_scatter(2, NULL, NULL, 8, 0, -1, NULL) == -2
-    assert L.coll_moe_expert_scale(2, NULL, NULL, NULL, 4, 8, 2, 0, NULL, 0, NULL) == -2   # fp32
+    assert L.coll_moe_expert_scale(2, NULL, NULL, NULL, 4, 8, 2, 0, NULL, NULL, 0, NULL) == -2   # fp32
     assert L.coll_moe_combine(2, NULL, NULL, NULL, 4, 2, 8, 1, NULL, NULL) == -2
 
 
@@ -139,15 +139,15 @@ def test_moe_expert_workspace_validation(L):
     t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     need = L.coll_moe_expert_workspace_bytes(2, 4, 0)           # the least any call accepts
     # NULL, misaligned or too small workspace -> rejected before any launch
-    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, NULL, need, NULL) == -1
-    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, 0x1008, need, NULL) == -1
-    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, 0x1000, need - 1, NULL) == -1
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, NULL, NULL, need, NULL) == -1
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, NULL, 0x1008, need, NULL) == -1
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 8, 0, 16, NULL, 0x1000, need - 1, NULL) == -1
     # NULL receive buffer / tables
     z = (ctypes.c_void_p * 2)(0x1000, None)
-    assert L.coll_moe_expert_scale(2, z, 0x100, 0x200, 4, 8, 0, 16, 0x1000, need, NULL) == -1
-    assert L.coll_moe_expert_scale(2, t, NULL, 0x200, 4, 8, 0, 16, 0x1000, need, NULL) == -1
+    assert L.coll_moe_expert_scale(2, z, 0x100, 0x200, 4, 8, 0, 16, NULL, 0x1000, need, NULL) == -1
+    assert L.coll_moe_expert_scale(2, t, NULL, 0x200, 4, 8, 0, 16, NULL, 0x1000, need, NULL) == -1
     # hidden 0: nothing to do, nothing launched
-    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 0, 0, 16, NULL, 0, NULL) == 0
+    assert L.coll_moe_expert_scale(2, t, 0x100, 0x200, 4, 0, 0, 16, NULL, NULL, 0, NULL) == 0
 
 
 def test_a2av_workspace_size_and_validation(L):

@@ -165,3 +165,46 @@ def test_fused_moe_skips_a_block_past_its_receive_buffer():
     expect = oracle.moe_combine(want["backs"], pos_eff, ws, H)
     for s in range(R):
         assert bits_equal(host(outs[s]), expect[s]), f"rank {s}"
+
+
+@pytest.mark.parametrize("kind", ["negative count", "displacement past the buffer"])
+@pytest.mark.parametrize("path", ["row descriptors", "table search"])
+def test_expert_leaves_a_bad_block_as_it_is(kind, path):
+    R, E, T, K, H = 8, 256, 700, 8, 64
+    say("expert, a bad block", kind, path)
+    ids, ws, xs = [], [], []
+    for s in range(R):
+        i, w = synth.zipf_routing(T, E, K, seed=5200 + s)
+        ids.append(i)
+        ws.append(w)
+        xs.append(synth.gaussian((T, H), 1.0, 5300 + s, "bf16"))
+    want = oracle.moe_pipeline(xs, ids, ws, E)
+    lay = want["layout"]
+    per = E // R
+    ec_h = np.array(lay["expert_counts"], np.int32).reshape(R, E)
+    rd_h = np.array(lay["rdispls"], np.int64)
+    rrows = np.array(lay["sendcounts"], np.int64).sum(axis=0)
+    blocks = [(s, d) for s in range(R) for d in range(R) if ec_h[s, d * per:(d + 1) * per].sum()]
+    s0, d0 = blocks[len(blocks) // 2]
+    n0 = int(ec_h[s0, d0 * per:(d0 + 1) * per].sum())
+    ec2, rd2 = ec_h.copy(), rd_h.copy()
+    if kind == "negative count":
+        ec2[s0, d0 * per] = -1
+    else:
+        rd2[d0, s0] = int(rrows[d0]) - n0 + 1
+    recv_h = [np.ascontiguousarray(want["recvs"][d].reshape(-1, H)[:int(rrows[d])])
+              for d in range(R)]
+    recvs = [dev(r) for r in recv_h]
+    # a workspace for the row descriptors selects that path; one for the
+    # table alone, the table search
+    cap = int(rrows.sum()) if path == "row descriptors" else 0
+    work = torch.empty(coll.moe_expert_workspace_bytes(R, E, cap), dtype=torch.uint8,
+                       device="cuda")
+    coll.moe_expert_scale(recvs, torch.from_numpy(ec2.reshape(-1)).cuda(), dc(rd2), E, H, work)
+    torch.cuda.synchronize()
+    for d in range(R):
+        exp = want["ys"][d].reshape(-1, H)[:int(rrows[d])].copy()
+        if d == d0:
+            a = int(rd_h[d0, s0])
+            exp[a:a + n0] = recv_h[d0][a:a + n0]
+        assert bits_equal(host(recvs[d]), exp), f"rank {d}"

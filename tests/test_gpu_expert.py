@@ -92,8 +92,9 @@ def test_expert_matches_oracle(R, E, H, maxc, zero_frac, gap, cap, shift, ws_kin
     capv = {"exact": total, "zero": 0, "big": 3 * total + 17, "small": max(total // 3, 1)}[cap]
     wsb = coll.moe_expert_workspace_bytes(R, E, capv if ws_kind == "rows" else 0)
     ws = torch.full((wsb,), 0xCD, dtype=torch.uint8, device="cuda")   # contents never read
+    rows = (ctypes.c_int64 * R)(*[r.size // H for r in recvs])
     rc = coll.lib().coll_moe_expert_scale(R, ptrs, ec_d.data_ptr(), rd_d.data_ptr(), E, H, 0,
-                                          capv, ws.data_ptr(), wsb, None)
+                                          capv, rows, ws.data_ptr(), wsb, None)
     torch.cuda.synchronize()
     assert rc == 0
     for d in range(R):
