@@ -719,7 +719,7 @@ def counter_traffic(kernel_src: str):
     return int(m_b.group(1))
 
 
-def _pct(f):
+def _as_pct(f):
     return "—" if f is None else f"{100 * f:.1f}%"
 
 
@@ -733,30 +733,30 @@ def report(path):
     rf = d["roofline"] or {}
     tr = rf.get("traffic")
     o += ["| Step | value |", "|---|---|",
-          f"| whole step (`value`) | {d['value']:.1f} GB/s = {_pct(d['value'] / HBM_PEAK_GBS)}, "
+          f"| whole step (`value`) | {d['value']:.1f} GB/s = {_as_pct(d['value'] / HBM_PEAK_GBS)}, "
           f"{d['ms_per_step']} ms per step |"]
     if d.get("step_graph_replay"):
         g = d["step_graph_replay"]
-        o.append(f"| the same step by graph replay | {g['GBps']} GB/s = {_pct(g['frac'])}, "
+        o.append(f"| the same step by graph replay | {g['GBps']} GB/s = {_as_pct(g['frac'])}, "
                  f"{g['ms_per_step']} ms |")
     if rf:
         o.append(f"| dominant kernel ({rf['kernel'].split(' ')[0]}) | {rf['achieved']} GB/s = "
-                 f"{_pct(rf['frac'])}, {rf['avg_launch_us']} µs per launch; counter traffic "
+                 f"{_as_pct(rf['frac'])}, {rf['avg_launch_us']} µs per launch; counter traffic "
                  + (f"{tr / rf['bytes_per_launch']:.4f}× the algorithmic bytes |" if tr else "n/a |"))
     if d.get("cpu_baseline"):
         c = d["cpu_baseline"]
         o.append(f"| CPU baseline (oracle, {c['cores']} core) | {c['value']} GB/s |")
     o += ["", "| Step row | µs | GB/s | % of peak |", "|---|---|---|---|"]
     for k, v in d["rows"].items():
-        o.append(f"| {k} | {v['us']} | {v['GBps']} | {_pct(v['frac'])} |")
+        o.append(f"| {k} | {v['us']} | {v['GBps']} | {_as_pct(v['frac'])} |")
     sw = d.get("allreduce_sweep")
     if sw:
         o += ["", "| AllReduce R=8 bf16, per rank | graph µs | graph | median µs | median |",
               "|---|---|---|---|---|"]
         for k, v in sw.items():
             if isinstance(v, dict) and "graph_us" in v and v["graph_frac"] >= 0.3:
-                o.append(f"| {k} | {v['graph_us']} | {_pct(v['graph_frac'])} | {v['median_us']} "
-                         f"| {_pct(v['frac'])} |")
+                o.append(f"| {k} | {v['graph_us']} | {_as_pct(v['graph_frac'])} | {v['median_us']} "
+                         f"| {_as_pct(v['frac'])} |")
     a2 = d.get("all_to_all_v_sweep")
     if a2:
         o += ["", "| All-to-All-v R=8 | size | graph µs | graph | median |", "|---|---|---|---|---|"]
@@ -769,18 +769,18 @@ def report(path):
                 big = (series.startswith("moe") and k in ("T256", "T1024", "T4096")) or \
                       (k.endswith("KiB") and int(k[:-3]) >= 16384)
                 if big:
-                    o.append(f"| {series} | {k} | {v['graph_us']} | {_pct(v['graph_frac'])} | "
-                             f"{_pct(v['frac'])} |")
+                    o.append(f"| {series} | {k} | {v['graph_us']} | {_as_pct(v['graph_frac'])} | "
+                             f"{_as_pct(v['frac'])} |")
     if d.get("next_rows"):
         o += ["", "| Further row | µs | GB/s | % of peak |", "|---|---|---|---|"]
         for k, v in d["next_rows"].items():
-            o.append(f"| {k} | {v['us']} | {v['GBps']} | {_pct(v['frac'])} |")
+            o.append(f"| {k} | {v['us']} | {v['GBps']} | {_as_pct(v['frac'])} |")
     f = d.get("moe_fused")
     if f:
         o += ["", "| Fused MoE path | value |", "|---|---|",
-              f"| dispatch (permute + All-to-All-v) | {f['dispatch']['us']} µs, {_pct(f['dispatch']['frac'])} |",
+              f"| dispatch (permute + All-to-All-v) | {f['dispatch']['us']} µs, {_as_pct(f['dispatch']['frac'])} |",
               f"| combine (expert + reverse All-to-All-v + combine) | {f['combine']['us']} µs, "
-              f"{_pct(f['combine']['frac'])} |",
+              f"{_as_pct(f['combine']['frac'])} |",
               f"| pipeline (layout + dispatch + combine) | {f['pipeline_us']} µs against "
               f"{f['unfused_pipeline_us']} µs unfused ({f['speedup_vs_unfused']}×); outputs bitwise "
               f"equal: {f['outputs_bitwise_equal_unfused']} |"]
@@ -794,7 +794,7 @@ def report(path):
     ex = []
     if d.get("copy_ceiling_1gib"):
         c = d["copy_ceiling_1gib"]
-        ex.append(f"| plain 1 GiB copy (graph) | {c['us']} µs, {c['GBps']} GB/s = {_pct(c['frac'])} |")
+        ex.append(f"| plain 1 GiB copy (graph) | {c['us']} µs, {c['GBps']} GB/s = {_as_pct(c['frac'])} |")
     if d.get("allreduce_16mib_layout_ab"):
         a = d["allreduce_16mib_layout_ab"]
         ex.append(f"| AllReduce 16 MiB × 8, torch allocations vs rank arena | "

@@ -29,3 +29,25 @@ def test_report_renders_the_committed_run():
     for row, v in line["rows"].items():
         assert f"| {row} | {v['us']} |" in out
     assert "| 16MiB |" in out and "moe_rows7168_ws" in out
+
+
+def test_no_top_level_name_is_defined_twice():
+    """A second definition silently replaces the first (a report helper once
+    shadowed the sweeps' percentile function, and only the GPU run with the
+    sweeps would have failed)."""
+    import ast
+    tree = ast.parse(open(BENCH).read())
+    names = [n.name for n in tree.body if isinstance(n, (ast.FunctionDef, ast.ClassDef))]
+    dup = sorted({n for n in names if names.count(n) > 1})
+    assert not dup, dup
+
+
+def test_sweep_percentiles():
+    sys.path.insert(0, ROOT)
+    try:
+        import bench
+    finally:
+        sys.path.pop(0)
+    ts = [float(v) for v in range(1, 101)]
+    assert bench._pct(ts, 0.1) <= bench._pct(ts, 0.5) <= bench._pct(ts, 0.9)
+    assert bench._pct(ts, 0.0) == 1.0 and bench._pct(ts, 1.0) == 100.0
