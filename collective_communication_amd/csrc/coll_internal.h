@@ -377,6 +377,13 @@ template <> struct UnitT<1> { typedef uint8_t T; };
 #define COLL_UNIFORM(x) asm volatile("" : "+s"(x))
 #endif
 
+// Lane l's 64-bit x (l the same in every lane).
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // ----------------------------------------------------------- launch helpers
 
 struct Launch {

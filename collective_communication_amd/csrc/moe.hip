@@ -803,11 +803,6 @@ __device__ __forceinline__ SrcLane load_src_lane(int R, int s, const Table &recv
   return b;
 }
 
-__device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
 
 // The receive row of the wave-uniform send slot `slot` and its buffer
 // (`base`, 0 for a rank that receives nothing); d = the first block holding

@@ -388,6 +388,16 @@ def fam_a2av():
     _a2av_case(4, g.integers(30, 60, size=(4, 4)), 8, "bf16", ws=True, cap=50)
     case("a2av descriptor form, gapped")
     _a2av_case(3, g.integers(1, 30, size=(3, 3)), 16, "bf16", ws=True, gap=7)
+    # blocks much longer than a wave, so that waves locate their units from
+    # the block ends held in registers (at most 64 blocks) and only waves that
+    # straddle a boundary search: resident grid (capacity 0) and one-pass grid
+    for R, W, lo, hi in ((8, 8, 200, 400), (8, 1, 1600, 3200), (4, 8, 100, 300),
+                         (2, 24, 50, 90), (16, 8, 70, 150)):
+        for cap in (0, None):
+            case("a2av long blocks", R, W, "cap", cap)
+            _a2av_case(R, g.integers(lo, hi, size=(R, R)), W, "bf16", cap=cap)
+    case("a2av long uniform blocks of one-bf16 rows (the aligned chunk path)")
+    _a2av_case(8, np.full((8, 8), 2048), 1, "bf16", cap=0)
     for R, W in ((8, 8), (4, 5), (3, 24), (16, 8), (8, 64), (16, 64)):
         for ws in (False, True):
             case("a2av tables that name rows outside the buffers", R, W, "ws" if ws else "plain")
