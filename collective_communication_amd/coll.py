@@ -50,6 +50,11 @@ SIGNATURES = {
                                   _sz, _vp]),
     "coll_all_to_all_v_reverse": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _vp, _vp,
                                        _sz, _vp]),
+    "coll_all_to_all_v_ws_build": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp, _vp,
+                                        _vp, _sz, _vp]),
+    "coll_all_to_all_v_reverse_build": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _sz, _i, _sz, _vp,
+                                             _vp, _vp, _sz, _vp]),
+    "coll_all_to_all_v_ws_copy": (_i, [_i, _sz, _i, _sz, _vp, _sz, _vp]),
     "coll_all_to_all": (_i, [_i, _vp, _vp, _sz, _i, _vp]),
     "coll_seq_heads_reshard": (_i, [_i, _vp, _vp, _sz, _sz, _sz, _i, _i, _vp]),
     "coll_lse_merge": (_i, [_i, _vp, _vp, _vp, _vp, _sz, _sz, _i, _vp]),
@@ -419,6 +424,63 @@ def all_to_all_v_reverse(recvs, sendcounts, sdispls, sends, rdispls, row_elems: 
                   _table(recvs, "recv", R), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
                   _table(sends, "send", R), _dev(rdispls, "rdispls"), row_elems * mult, dt,
                   capacity, _rows(sends, row_elems), _rows(recvs, row_elems), ws_ptr, ws_bytes)
+
+
+def _desc_need(R, dt, row_bytes_elems, capacity, what):
+    need = int(lib().coll_all_to_all_v_workspace_bytes(R, capacity, row_bytes_elems, dt))
+    if need == 0:
+        raise ValueError(f"{what}: the descriptor form does not apply to these sizes "
+                         "(all_to_all_v_workspace_bytes is 0); call the one-call form")
+    return need
+
+
+def all_to_all_v_build(sends, sendcounts, sdispls, recvs, rdispls, row_elems: int, workspace,
+                       stream=None, capacity=None):
+    """First half of all_to_all_v(..., workspace=): writes the descriptor
+    tables (block table with these buffers' addresses, one block index per
+    tile) into ``workspace`` and moves nothing.  It needs only the tables and
+    the buffers' addresses, so it may run before the send buffers are written,
+    e.g. on a second stream.  all_to_all_v_copy(sends, recvs, ...) then moves
+    the rows.  Raises ValueError where the descriptor form does not apply."""
+    R, dt, mult, capacity = _a2av_shape(sends, recvs, row_elems, "all_to_all_v_build", capacity)
+    _layout_tables(R, (sendcounts, sdispls, rdispls), "all_to_all_v_build")
+    _desc_need(R, dt, row_elems * mult, capacity, "all_to_all_v_build")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return _issue("coll_all_to_all_v_ws_build", "all_to_all_v_build", stream, R,
+                  _table(sends, "send", R), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
+                  _table(recvs, "recv", R), _dev(rdispls, "rdispls"), row_elems * mult, dt,
+                  capacity, _rows(sends, row_elems), _rows(recvs, row_elems),
+                  _dev(workspace, "workspace"), ws_bytes)
+
+
+def all_to_all_v_reverse_build(recvs, sendcounts, sdispls, sends, rdispls, row_elems: int,
+                               workspace, stream=None, capacity=None):
+    """First half of all_to_all_v_reverse(..., workspace=), as
+    all_to_all_v_build; all_to_all_v_copy(recvs, sends, ...) then moves the
+    rows back."""
+    R, dt, mult, capacity = _a2av_shape(recvs, sends, row_elems, "all_to_all_v_reverse_build",
+                                        capacity)
+    _layout_tables(R, (sendcounts, sdispls, rdispls), "all_to_all_v_reverse_build")
+    _desc_need(R, dt, row_elems * mult, capacity, "all_to_all_v_reverse_build")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return _issue("coll_all_to_all_v_reverse_build", "all_to_all_v_reverse_build", stream, R,
+                  _table(recvs, "recv", R), _dev(sendcounts, "counts"), _dev(sdispls, "sdispls"),
+                  _table(sends, "send", R), _dev(rdispls, "rdispls"), row_elems * mult, dt,
+                  capacity, _rows(sends, row_elems), _rows(recvs, row_elems),
+                  _dev(workspace, "workspace"), ws_bytes)
+
+
+def all_to_all_v_copy(sources, dests, row_elems: int, workspace, stream=None, capacity=None):
+    """Second half of the descriptor form: the rows move between the buffers
+    that the build on ``workspace`` was given.  ``sources`` / ``dests``: those
+    buffers in the build's order (sends, recvs for all_to_all_v_build; recvs,
+    sends for all_to_all_v_reverse_build); only their sizes and dtype are used
+    here, to find the launch's shape."""
+    R, dt, mult, capacity = _a2av_shape(sources, dests, row_elems, "all_to_all_v_copy", capacity)
+    _desc_need(R, dt, row_elems * mult, capacity, "all_to_all_v_copy")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return _issue("coll_all_to_all_v_ws_copy", "all_to_all_v_copy", stream, R, row_elems * mult,
+                  dt, capacity, _dev(workspace, "workspace"), ws_bytes)
 
 
 def all_to_all(sends, recvs, stream=None):

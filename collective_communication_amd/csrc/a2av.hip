@@ -771,20 +771,24 @@ size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_
   return ((size_t)R * R * sizeof(A2aBlk) + slots * sizeof(uint16_t) + 255) & ~(size_t)255;
 }
 
-int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
-                   const int64_t *counts,
-                   const int64_t *sdispls, const int64_t *rdispls, int ct, size_t row_bytes,
-                   size_t rows_capacity, void *ws) {
+// Tiles of 64 units of the descriptor form for this capacity; 0 when the form
+// does not apply (rows not whole 16-byte units on every buffer, no capacity,
+// or more tiles than one grid holds).
+static uint64_t desc_tiles(int R, const RankPtrs *p, size_t row_bytes, size_t rows_capacity) {
   uintptr_t bits = row_bytes;
-  for (int r = 0; r < R; r++) bits |= (uintptr_t)p.in[r] | (uintptr_t)p.out[r];
-  // rows that are not whole 16-byte units, or no capacity: the plain form
-  if (copy_unit(bits) != 16 || rows_capacity == 0)
-    return launch_a2av(L, R, p, lim, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
-  const uint64_t row_units = row_bytes / 16;
-  const uint64_t cap_units = (uint64_t)rows_capacity * row_units;
+  if (p)
+    for (int r = 0; r < R; r++) bits |= (uintptr_t)p->in[r] | (uintptr_t)p->out[r];
+  if (copy_unit(bits) != 16 || rows_capacity == 0) return 0;
+  const uint64_t cap_units = (uint64_t)rows_capacity * (row_bytes / 16);
   const uint64_t ndesc = (cap_units + kDescTile - 1) / kDescTile;
-  if (ndesc == 0 || ndesc > 0x7FFFFFFFull)     // empty rows, or more tiles than one grid holds
-    return launch_a2av(L, R, p, lim, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
+  return ndesc > 0x7FFFFFFFull ? 0 : ndesc;
+}
+
+int launch_a2av_ws_build(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
+                         const int64_t *counts, const int64_t *sdispls, const int64_t *rdispls,
+                         int ct, size_t row_bytes, size_t rows_capacity, void *ws) {
+  const uint64_t ndesc = desc_tiles(R, &p, row_bytes, rows_capacity);
+  if (ndesc == 0) return COLL_ERR_UNSUPPORTED;
   A2aBlk *blk = reinterpret_cast<A2aBlk *>(ws);
   uint32_t *idx = reinterpret_cast<uint32_t *>(blk + (size_t)R * R);   // two indices per word
   // descriptor writers: a resident grid (COLL_DESC_BUILD_WGS per CU), no
@@ -793,8 +797,17 @@ int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const RowLimits &l
   const uint64_t gneed = (pairs + kBlock - 1) / kBlock;
   const uint64_t gres = (uint64_t)L.num_cus * kDescBuildWgs;
   hipLaunchKernelGGL((a2av_desc_build<16>), dim3((unsigned)(gneed < gres ? gneed : gres)),
-                     dim3(kBlock), 0, L.stream, p, lim, R, counts, sdispls, rdispls, ct, row_units, idx,
-                     ndesc, blk);
+                     dim3(kBlock), 0, L.stream, p, lim, R, counts, sdispls, rdispls, ct,
+                     (uint64_t)(row_bytes / 16), idx, ndesc, blk);
+  return hip_status();
+}
+
+int launch_a2av_ws_copy(const Launch &L, int R, size_t row_bytes, size_t rows_capacity,
+                        void *ws) {
+  const uint64_t ndesc = desc_tiles(R, nullptr, row_bytes, rows_capacity);
+  if (ndesc == 0) return COLL_ERR_UNSUPPORTED;
+  A2aBlk *blk = reinterpret_cast<A2aBlk *>(ws);
+  uint32_t *idx = reinterpret_cast<uint32_t *>(blk + (size_t)R * R);
   if (L.a2a_nt)
     hipLaunchKernelGGL((a2av_desc_kernel<16, true>), dim3((unsigned)ndesc), dim3(kDescLanes), 0,
                        L.stream, idx, blk, R * R);
@@ -802,6 +815,19 @@ int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const RowLimits &l
     hipLaunchKernelGGL((a2av_desc_kernel<16, false>), dim3((unsigned)ndesc), dim3(kDescLanes), 0,
                        L.stream, idx, blk, R * R);
   return hip_status();
+}
+
+int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
+                   const int64_t *counts, const int64_t *sdispls, const int64_t *rdispls, int ct,
+                   size_t row_bytes, size_t rows_capacity, void *ws) {
+  // rows that are not whole 16-byte units, no capacity, or more tiles than a
+  // grid holds: the plain form
+  if (desc_tiles(R, &p, row_bytes, rows_capacity) == 0)
+    return launch_a2av(L, R, p, lim, counts, sdispls, rdispls, ct, row_bytes, rows_capacity);
+  const int rc = launch_a2av_ws_build(L, R, p, lim, counts, sdispls, rdispls, ct, row_bytes,
+                                      rows_capacity, ws);
+  if (rc != COLL_OK) return rc;
+  return launch_a2av_ws_copy(L, R, row_bytes, rows_capacity, ws);
 }
 
 }  // namespace coll

@@ -298,11 +298,13 @@ size_t coll_all_to_all_v_workspace_bytes(int R, size_t recv_rows_capacity, size_
 // forward exchange's, sendbufs are its receive buffers and recvbufs its send
 // buffers, sdispls its rdispls and rdispls its sdispls, send_rows the rows
 // of its receive buffers and recv_rows those of its send buffers).
+// build_only: the first kernel alone (coll_all_to_all_v_ws_build), which
+// needs the descriptor form to apply.
 static int a2av_ws_call(int R, const void *const *sendbufs, const int64_t *sendcounts,
                         const int64_t *sdispls, void *const *recvbufs, const int64_t *rdispls,
                         int ct, size_t row_elems, coll_dtype_t dtype, size_t recv_rows_capacity,
                         const int64_t *send_rows, const int64_t *recv_rows, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        size_t workspace_bytes, void *stream, bool build_only = false) {
   if (!ranks_ok(R) || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
   if (row_elems == 0) return COLL_OK;
   if (!sendcounts || !sdispls || !rdispls || !bytes_ok(row_elems, dtype_size(dtype), 1))
@@ -323,6 +325,11 @@ static int a2av_ws_call(int R, const void *const *sendbufs, const int64_t *sendc
   if (!fill_rows(R, send_rows, sendbufs, lim.in) ||
       !fill_rows(R, recv_rows, reinterpret_cast<const void *const *>(recvbufs), lim.out))
     return COLL_ERR_INVALID_ARG;
+  if (build_only) {
+    if (need == 0) return COLL_ERR_UNSUPPORTED;
+    return launch_a2av_ws_build(launch_ctx(stream), R, p, lim, sendcounts, sdispls, rdispls, ct,
+                                row_bytes, recv_rows_capacity, workspace);
+  }
   if (need == 0)
     return launch_a2av(launch_ctx(stream), R, p, lim, sendcounts, sdispls, rdispls, ct,
                        row_bytes, recv_rows_capacity);
@@ -338,6 +345,46 @@ int coll_all_to_all_v_ws(int R, const void *const *sendbufs, const int64_t *send
   return a2av_ws_call(R, sendbufs, sendcounts, sdispls, recvbufs, rdispls, 0, row_elems, dtype,
                       recv_rows_capacity, send_rows, recv_rows, workspace, workspace_bytes,
                       stream);
+}
+
+int coll_all_to_all_v_ws_build(int R, const void *const *sendbufs, const int64_t *sendcounts,
+                               const int64_t *sdispls, void *const *recvbufs,
+                               const int64_t *rdispls, size_t row_elems, coll_dtype_t dtype,
+                               size_t recv_rows_capacity, const int64_t *send_rows,
+                               const int64_t *recv_rows, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  if (row_elems == 0) return COLL_ERR_UNSUPPORTED;
+  return a2av_ws_call(R, sendbufs, sendcounts, sdispls, recvbufs, rdispls, 0, row_elems, dtype,
+                      recv_rows_capacity, send_rows, recv_rows, workspace, workspace_bytes,
+                      stream, true);
+}
+
+int coll_all_to_all_v_reverse_build(int R, const void *const *recvbufs,
+                                    const int64_t *sendcounts, const int64_t *sdispls,
+                                    void *const *sendbufs, const int64_t *rdispls,
+                                    size_t row_elems, coll_dtype_t dtype,
+                                    size_t send_rows_capacity, const int64_t *send_rows,
+                                    const int64_t *recv_rows, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  if (row_elems == 0) return COLL_ERR_UNSUPPORTED;
+  return a2av_ws_call(R, recvbufs, sendcounts, rdispls, sendbufs, sdispls, 1, row_elems, dtype,
+                      send_rows_capacity, recv_rows, send_rows, workspace, workspace_bytes,
+                      stream, true);
+}
+
+int coll_all_to_all_v_ws_copy(int R, size_t row_elems, coll_dtype_t dtype,
+                              size_t rows_capacity, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (!ranks_ok(R) || !dtype_ok(dtype) || row_elems == 0 ||
+      !bytes_ok(row_elems, dtype_size(dtype), 1))
+    return COLL_ERR_INVALID_ARG;
+  const size_t row_bytes = row_elems * dtype_size(dtype);
+  if (rows_capacity > ((size_t)1 << 48) / row_bytes) return COLL_ERR_INVALID_ARG;
+  const size_t need = a2av_workspace_bytes(R, rows_capacity, row_bytes, knobs().a2a_desc_bytes);
+  if (need == 0) return COLL_ERR_UNSUPPORTED;
+  if (!workspace || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < need)
+    return COLL_ERR_INVALID_ARG;
+  return launch_a2av_ws_copy(launch_ctx(stream), R, row_bytes, rows_capacity, workspace);
 }
 
 int coll_all_to_all_v_reverse(int R, const void *const *recvbufs, const int64_t *sendcounts,

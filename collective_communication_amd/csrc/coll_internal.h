@@ -472,6 +472,12 @@ size_t a2av_workspace_bytes(int R, size_t rows_capacity, size_t row_bytes, size_
 int launch_a2av_ws(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
                    const int64_t *counts, const int64_t *sdispls, const int64_t *rdispls, int ct,
                    size_t row_bytes, size_t rows_capacity, void *ws);
+// the two halves of launch_a2av_ws: COLL_ERR_UNSUPPORTED where the descriptor
+// form does not apply (nothing launched)
+int launch_a2av_ws_build(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
+                         const int64_t *counts, const int64_t *sdispls, const int64_t *rdispls,
+                         int ct, size_t row_bytes, size_t rows_capacity, void *ws);
+int launch_a2av_ws_copy(const Launch &L, int R, size_t row_bytes, size_t rows_capacity, void *ws);
 
 constexpr int kMoeMaxExperts = 1024;
 // Scratch of coll_moe_layout_noalloc: a device array of this many bytes per

@@ -245,6 +245,47 @@ int coll_all_to_all_v_ws(int nranks, const void *const *sendbufs, const int64_t 
                          size_t workspace_bytes, void *stream);
 
 /*
+ * The descriptor form of coll_all_to_all_v_ws as two calls, so that its first
+ * kernel can run off the critical path: it depends only on the count and
+ * displacement tables and on the buffers' addresses, not on the rows, so a
+ * caller can issue it (for instance on a second stream) while the send
+ * buffers are still being written.
+ *   coll_all_to_all_v_ws_build: the arguments of coll_all_to_all_v_ws; writes
+ *   the workspace (the block table, with the buffers' addresses, and a block
+ *   index per tile) and moves nothing.  Returns COLL_ERR_UNSUPPORTED, with
+ *   nothing launched, where coll_all_to_all_v_ws would take the plain form
+ *   (coll_all_to_all_v_workspace_bytes is 0 for the call, or the buffers are
+ *   not 16-byte aligned): call coll_all_to_all_v_ws then.
+ *   coll_all_to_all_v_reverse_build: the same for coll_all_to_all_v_reverse
+ *   (its arguments; rows_capacity = its send_rows_capacity).
+ *   coll_all_to_all_v_ws_copy: the copy kernel alone, from a workspace that
+ *   a build wrote for the same nranks, row size and capacity.  It moves the
+ *   rows between the buffers the build was given, as the one-call form
+ *   would.  The caller orders it after the build (same stream, or an event)
+ *   and after the writes to the send buffers, and does not reuse the
+ *   workspace until the copy completes.
+ * Errors: as coll_all_to_all_v_ws; the copy returns COLL_ERR_INVALID_ARG for
+ * a NULL or misaligned workspace or one below the size, and
+ * COLL_ERR_UNSUPPORTED where no descriptor form exists for its sizes.
+ */
+int coll_all_to_all_v_ws_build(int nranks, const void *const *sendbufs, const int64_t *sendcounts,
+                               const int64_t *sdispls, void *const *recvbufs,
+                               const int64_t *rdispls, size_t row_elems, coll_dtype_t dtype,
+                               size_t recv_rows_capacity, const int64_t *send_rows,
+                               const int64_t *recv_rows, void *workspace, size_t workspace_bytes,
+                               void *stream);
+int coll_all_to_all_v_reverse_build(int nranks, const void *const *recvbufs,
+                                    const int64_t *sendcounts, const int64_t *sdispls,
+                                    void *const *sendbufs, const int64_t *rdispls,
+                                    size_t row_elems, coll_dtype_t dtype,
+                                    size_t send_rows_capacity, const int64_t *send_rows,
+                                    const int64_t *recv_rows, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+int coll_all_to_all_v_ws_copy(int nranks, size_t row_elems, coll_dtype_t dtype,
+                              size_t rows_capacity, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
  * The reverse of an All-to-All-v, from that exchange's own tables -- tutorial
  * section 8.4 (after the experts, results return to the token's owner in one
  * more exchange).  With the forward call's sendcounts, sdispls and rdispls:

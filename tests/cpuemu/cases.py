@@ -212,6 +212,43 @@ def _a2av_case(R, counts, W, dtype, cap=None, ws=False, gap=0):
 POISON = 0xAB
 
 
+def _a2av_split_case(R, W, g):
+    """coll_all_to_all_v_ws_build + _copy (and the reverse build + copy) give
+    the same bytes as the one-call descriptor form."""
+    counts = g.integers(0, 60, size=(R, R)).astype(np.int64)
+    sd, rd = oracle.packed_displs(counts)
+    send_rows = [int(counts[s].sum()) for s in range(R)]
+    recv_rows = [int(counts[:, d].sum()) for d in range(R)]
+    sends = [gen("bf16", send_rows[s] * W, 950 + s) for s in range(R)]
+    want = oracle.all_to_all_v([x.reshape(-1) for x in sends], counts, sd, rd,
+                               np.array(recv_rows), W)
+    ins = [H.copy(x) if x.size else None for x in sends]
+    outs = [H.poison(recv_rows[d] * W, np.uint16) if recv_rows[d] else None for d in range(R)]
+    tabs = [H.copy(np.ascontiguousarray(t).reshape(-1)) for t in (counts, sd, rd)]
+    cap = sum(recv_rows)
+    need = L.coll_all_to_all_v_workspace_bytes(R, cap, W, BF16)
+    assert need > 0
+    work = H.poison(need, np.uint8)
+    ok(L.coll_all_to_all_v_ws_build(R, table(ins), ptr(tabs[0]), ptr(tabs[1]), table(outs),
+                                    ptr(tabs[2]), W, BF16, cap, rows(send_rows), rows(recv_rows),
+                                    ptr(work), need, None), "build")
+    ok(L.coll_all_to_all_v_ws_copy(R, W, BF16, cap, ptr(work), need, None), "copy")
+    for d in range(R):
+        if recv_rows[d]:
+            same(outs[d], want[d].reshape(-1)[:recv_rows[d] * W], f"split form, rank {d}")
+    backs = [H.poison(send_rows[s] * W, np.uint16) if send_rows[s] else None for s in range(R)]
+    bcap = sum(send_rows)
+    bneed = L.coll_all_to_all_v_workspace_bytes(R, bcap, W, BF16)
+    bwork = H.poison(bneed, np.uint8)
+    ok(L.coll_all_to_all_v_reverse_build(R, table(outs), ptr(tabs[0]), ptr(tabs[1]), table(backs),
+                                         ptr(tabs[2]), W, BF16, bcap, rows(send_rows),
+                                         rows(recv_rows), ptr(bwork), bneed, None), "reverse build")
+    ok(L.coll_all_to_all_v_ws_copy(R, W, BF16, bcap, ptr(bwork), bneed, None), "reverse copy")
+    for s in range(R):
+        if send_rows[s]:
+            same(backs[s], sends[s].reshape(-1), f"split reverse, rank {s}")
+
+
 def _a2av_bad_case(R, W, ws):
     """Tables that name rows outside the buffers: each bad block moves nothing
     (its receive rows keep their contents), every other block is exact, and
@@ -386,6 +423,9 @@ def fam_a2av():
         _a2av_case(R, g.integers(0, 60, size=(R, R)), W, "bf16", ws=True)
     case("a2av descriptor form, capacity below the rows (tail loop)")
     _a2av_case(4, g.integers(30, 60, size=(4, 4)), 8, "bf16", ws=True, cap=50)
+    for R, W in ((8, 8), (3, 24)):
+        case("a2av descriptor form in two calls (build, then copy)", R, W)
+        _a2av_split_case(R, W, g)
     case("a2av descriptor form, gapped")
     _a2av_case(3, g.integers(1, 30, size=(3, 3)), 16, "bf16", ws=True, gap=7)
     # blocks much longer than a wave, so that waves locate their units from

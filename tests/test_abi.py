@@ -411,3 +411,32 @@ def test_plan_keeps_the_arguments_it_was_made_from():
     del plan, fake
     gc.collect()
     assert ref() is None
+
+
+def test_a2av_split_descriptor_form_validation(L):
+    """coll_all_to_all_v_ws_build / _reverse_build / _ws_copy: the form must
+    apply (capacity from the descriptor threshold up, 16-byte rows), and the
+    copy checks its workspace as the one-call form does.  Nothing is launched
+    in any of these cases."""
+    K = (192 << 20) // 16                                   # rows of 8 bf16: the threshold
+    need = L.coll_all_to_all_v_workspace_bytes(2, K, 8, 0)
+    assert need > 0
+    t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    # below the threshold, or rows of 10 bytes: no descriptor form
+    assert L.coll_all_to_all_v_ws_build(2, t, 0x100, 0x200, t, 0x300, 8, 0, K - 1, NULL, NULL,
+                                        0x1000, need, NULL) == -2
+    assert L.coll_all_to_all_v_ws_build(2, t, 0x100, 0x200, t, 0x300, 5, 0, K, NULL, NULL,
+                                        0x1000, need, NULL) == -2
+    assert L.coll_all_to_all_v_reverse_build(2, t, 0x100, 0x200, t, 0x300, 8, 0, K - 1, NULL,
+                                             NULL, 0x1000, need, NULL) == -2
+    assert L.coll_all_to_all_v_ws_copy(2, 8, 0, K - 1, 0x1000, need, NULL) == -2
+    assert L.coll_all_to_all_v_ws_copy(2, 5, 0, K, 0x1000, need, NULL) == -2
+    # workspace NULL, misaligned or small; bad ranks; NULL tables
+    assert L.coll_all_to_all_v_ws_build(2, t, 0x100, 0x200, t, 0x300, 8, 0, K, NULL, NULL,
+                                        NULL, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws_copy(2, 8, 0, K, NULL, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws_copy(2, 8, 0, K, 0x1010, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws_copy(2, 8, 0, K, 0x1000, need - 1, NULL) == -1
+    assert L.coll_all_to_all_v_ws_copy(17, 8, 0, K, 0x1000, need, NULL) == -1
+    assert L.coll_all_to_all_v_ws_build(2, t, NULL, 0x200, t, 0x300, 8, 0, K, NULL, NULL,
+                                        0x1000, need, NULL) == -1

@@ -103,3 +103,41 @@ def test_one_rank_buffers_for_scatter_broadcast_gather_reduce(issued):
     coll.gather([bf(2, 3) for _ in range(R)], bf(2, 3 * R), 0)
     coll.reduce([bf(4) for _ in range(R)], bf(4), 0)
     assert issued == ["coll_scatter", "coll_broadcast", "coll_gather", "coll_reduce"]
+
+
+BIG = 1 << 24          # rows of 8 bf16: 256 MiB of capacity, above the descriptor threshold
+SPLIT = {
+    # wrapper -> (C entry point, builder of valid arguments, indices of per-rank lists)
+    "all_to_all_v_build": ("coll_all_to_all_v_ws_build",
+                           lambda: ([bf(8) for _ in range(R)], i64(R * R), i64(R * R),
+                                    [bf(8) for _ in range(R)], i64(R * R), 8,
+                                    torch.zeros(256, dtype=torch.uint8), None, BIG), (0, 3)),
+    "all_to_all_v_reverse_build": ("coll_all_to_all_v_reverse_build",
+                                   lambda: ([bf(8) for _ in range(R)], i64(R * R), i64(R * R),
+                                            [bf(8) for _ in range(R)], i64(R * R), 8,
+                                            torch.zeros(256, dtype=torch.uint8), None, BIG),
+                                   (0, 3)),
+    "all_to_all_v_copy": ("coll_all_to_all_v_ws_copy",
+                          lambda: ([bf(8) for _ in range(R)], [bf(8) for _ in range(R)], 8,
+                                   torch.zeros(256, dtype=torch.uint8), None, BIG), (0, 1)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT))
+def test_split_descriptor_form_wrappers(issued, name):
+    entry, build, lists = SPLIT[name]
+    getattr(coll, name)(*build())
+    assert issued == [entry]
+    for idx in lists:
+        for delta in (-1, +1):
+            args = list(build())
+            lst = list(args[idx])
+            args[idx] = lst[:-1] if delta < 0 else lst + [lst[0]]
+            with pytest.raises(ValueError):
+                getattr(coll, name)(*args)
+    assert issued == [entry]
+    # sizes without a descriptor form are refused before the C call
+    args = list(build())
+    args[-1] = 16
+    with pytest.raises(ValueError):
+        getattr(coll, name)(*args)

@@ -256,3 +256,56 @@ def test_graph_replays_the_descriptor_form():
         torch.cuda.synchronize()
         for d in range(R):
             assert bits_equal(host(recvs[d]), want[d]), (rep, d)
+
+
+@pytest.mark.parametrize("R,W,lo,hi", [(8, 2048, 600, 1000), (4, 8192, 750, 1000)])
+def test_build_on_a_second_stream_then_copy(R, W, lo, hi):
+    """The descriptor form in two calls, used as intended: the build runs on
+    a second stream before the send buffers are written (it reads only the
+    tables and the buffers' addresses); the copy runs after both.  Forward and
+    reverse, against the oracle."""
+    say("a2av build/copy", R, W)
+    g = np.random.default_rng(77 + R)
+    counts = g.integers(lo, hi, size=(R, R)).astype(np.int64)
+    sd, rd = oracle.packed_displs(counts)
+    send_rows = counts.sum(axis=1)
+    recv_rows = counts.sum(axis=0)
+    assert int(recv_rows.sum()) * W * 2 >= DESC_MIN_BYTES
+    xs = [synth.gaussian(int(send_rows[s]) * W, 1.0, 8800 + s, "bf16") for s in range(R)]
+    want = oracle.all_to_all_v(xs, counts, sd, rd, recv_rows, W)
+    sends = [torch.empty(int(n) * W, dtype=torch.bfloat16, device="cuda") for n in send_rows]
+    recvs = [poison_like(torch.empty(int(n) * W, dtype=torch.bfloat16, device="cuda"))
+             for n in recv_rows]
+    tabs = (dc(counts), dc(sd), dc(rd))
+    ws = torch.empty(coll.all_to_all_v_workspace_bytes(sends, recvs, W), dtype=torch.uint8,
+                     device="cuda")
+    bws = torch.empty(coll.all_to_all_v_workspace_bytes(recvs, sends, W), dtype=torch.uint8,
+                      device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        coll.all_to_all_v_build(sends, *tabs[:2], recvs, tabs[2], W, ws)
+        coll.all_to_all_v_reverse_build(recvs, *tabs[:2], sends, tabs[2], W, bws)
+    built = torch.cuda.Event()
+    built.record(side)
+    for t, x in zip(sends, xs):                 # the send rows arrive after the build
+        t.copy_(dev(x))
+    torch.cuda.current_stream().wait_event(built)
+    coll.all_to_all_v_copy(sends, recvs, W, ws)
+    torch.cuda.synchronize()
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), f"rank {d}"
+    for t in sends:
+        t.view(torch.int16).fill_(0x7FAB)
+    coll.all_to_all_v_copy(recvs, sends, W, bws)
+    torch.cuda.synchronize()
+    for s in range(R):
+        assert bits_equal(host(sends[s]), xs[s]), f"returned rank {s}"
+
+
+def test_copy_refuses_sizes_without_a_descriptor_form():
+    sends = [torch.empty(64, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    recvs = [torch.empty(64, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        coll.all_to_all_v_copy(sends, recvs, 8, ws)
