@@ -328,7 +328,9 @@ __global__ __launch_bounds__(64 * kPermuteWaves) void moe_permute_kernel(PtrTabl
   }
   // One slot at a time: each slot's scalar load overlaps the previous slot's
   // stores.  Loading a chunk of slots first (as the other MoE kernels do)
-  // measured 9% slower here (848 vs 777 us at the MoE shape).
+  // measured 9% slower here (848 vs 777 us at the MoE shape).  A row form --
+  // one workgroup per token, wave k writing slot k's whole 14 KiB row in one
+  // run from cacheable loads of the token row -- measured 835 against 785 us.
   for (int k = 0; k < K; k++) {
     const int32_t slot = __builtin_amdgcn_readfirstlane(pk[k]);
     if ((uint32_t)slot >= TK) continue;                      // never write outside

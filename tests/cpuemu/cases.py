@@ -558,7 +558,10 @@ def fam_moe():
                                 (4, 16, 333, 3, 24, False), (8, 256, 150, 8, 64, False),
                                 (2, 8, 50, 2, 5, False), (16, 1024, 40, 8, 8, False),
                                 (2, 16, 40, 10, 16, False), (4, 16, 200, 3, 24, True),
-                                (8, 64, 100, 8, 8, True), (2, 16, 40, 10, 5, True)):
+                                (8, 64, 100, 8, 8, True), (2, 16, 40, 10, 5, True),
+                                # top-17 (a second chunk of slots in the combines);
+                                # rows of 1025 units (a ragged last segment)
+                                (2, 32, 30, 17, 16, False), (2, 8, 6, 2, 8200, False)):
         case("moe", R, E, T, K, Hd, "bad ids" if bad else "")
         ids, ws, xs = _moe(R, E, T, K, Hd, bad)
         want = oracle.moe_pipeline(xs, ids, ws, E)
