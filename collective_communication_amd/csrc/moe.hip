@@ -361,37 +361,9 @@ __global__ __launch_bounds__(64 * kPermuteWaves) void moe_permute_kernel(PtrTabl
 // A (d, s) block with a negative expert count, or whose rows do not all lie
 // inside recv[d] (recv_rows), counts as empty: no row of it is numbered, so
 // the kernels that follow never address it and its rows keep their values.
-__global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_counts,
-                                                         const int64_t *rdispls, int R, int E,
-                                                         RankRows recv_rows, int64_t *s_end,
-                                                         int64_t *rb) {
-  __shared__ int64_t wsum[16];
-  __shared__ int64_t first_end[COLL_MAX_RANKS * COLL_MAX_RANKS];   // rows before (d, s)
-  __shared__ int s_ok[COLL_MAX_RANKS * COLL_MAX_RANKS];
-  const int per = E / R;
-  const int N = R * E;
-  const int chunk = (N + 1023) / 1024;           // <= 16 (R <= 16, E <= 1024)
-  const int j0 = (int)threadIdx.x * chunk;
-  if ((int)threadIdx.x < R * R) {
-    const int d = threadIdx.x / R, s = threadIdx.x - d * R;
-    int64_t sum = 0;
-    bool neg = false;
-    for (int el = 0; el < per; el++) {
-      const int64_t c = expert_counts[(size_t)s * E + d * per + el];
-      neg = neg || c < 0;
-      sum += c < 0 ? 0 : c;
-    }
-    s_ok[threadIdx.x] =
-        !neg && (sum == 0 || block_fits(sum, 0, rdispls[d * R + s], INT64_MAX, recv_rows.n[d]));
-  }
-  __syncthreads();
-  auto count_of = [&](int j) -> int64_t {
-    const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
-    return s_ok[d * R + s] ? (int64_t)expert_counts[(size_t)s * E + d * per + el] : 0;
-  };
-  int64_t local = 0;
-  for (int c = 0; c < chunk; c++)
-    if (j0 + c < N) local += count_of(j0 + c);
+// Inclusive scan over the workgroup's 1024 threads (entries in thread order);
+// returns the exclusive prefix of the thread's `local`.
+__device__ __forceinline__ int64_t table_scan(int64_t local, int64_t *wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int64_t incl = local;
 #pragma unroll
@@ -403,15 +375,89 @@ __global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_c
   __syncthreads();
   int64_t run = incl - local;
   for (int q = 0; q < w; q++) run += wsum[q];
+  __syncthreads();                               // wsum is reused by the next scan
+  return run;
+}
+
+// Entry j = d*E + s*per + el of the receive-order table (a (d, s) block's
+// entries are consecutive): its count.
+__device__ __forceinline__ int64_t entry_count(const int32_t *expert_counts, int E, int per,
+                                               int j) {
+  const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
+  return (int64_t)expert_counts[(size_t)s * E + d * per + el];
+}
+
+__global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_counts,
+                                                         const int64_t *rdispls, int R, int E,
+                                                         RankRows recv_rows, int64_t *s_end,
+                                                         int64_t *rb) {
+  // a negative count, in the first scan: above any sum of non-negative int32
+  // counts over 2^14 entries (< 2^45), and 2^14 of them still fit in int64
+  constexpr int64_t kNeg = (int64_t)1 << 46;
+  __shared__ int64_t wsum[16];
+  __shared__ int64_t first_end[COLL_MAX_RANKS * COLL_MAX_RANKS];   // rows before (d, s)
+  __shared__ int64_t s_b1[COLL_MAX_RANKS * COLL_MAX_RANKS];        // scan after (d, s)
+  __shared__ int s_ok[COLL_MAX_RANKS * COLL_MAX_RANKS];
+  __shared__ int s_bad;
+  const int per = E / R;
+  const int N = R * E;
+  const int chunk = (N + 1023) / 1024;           // <= 16 (R <= 16, E <= 1024)
+  const int j0 = (int)threadIdx.x * chunk;
+  // 1. the scan of the counts (a negative one as kNeg) is the table when every
+  //    block fits, the usual case; it also gives each block's total (and
+  //    whether it holds a negative count) from the scan before its first and
+  //    after its last entry.  Counts are re-read in each loop (L2 hits):
+  //    keeping them in registers spilled to scratch at 1024 threads.
+  int64_t local = 0;
+  for (int c = 0; c < chunk; c++) {
+    if (j0 + c >= N) break;
+    const int64_t v = entry_count(expert_counts, E, per, j0 + c);
+    local += v < 0 ? kNeg : v;
+  }
+  int64_t run = table_scan(local, wsum);
   for (int c = 0; c < chunk; c++) {
     const int j = j0 + c;
     if (j >= N) break;
     const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
     if (el == 0) first_end[d * R + s] = run;
-    run += count_of(j);
+    const int64_t v = entry_count(expert_counts, E, per, j);
+    run += v < 0 ? kNeg : v;
     s_end[j] = run;
+    if (el == per - 1) s_b1[d * R + s] = run;
+  }
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < R * R) {
+    const int d = threadIdx.x / R, s = threadIdx.x - d * R;
+    const int64_t sum = s_b1[threadIdx.x] - first_end[threadIdx.x];
+    const bool ok = sum < kNeg && (sum == 0 || block_fits(sum, 0, rdispls[d * R + s],
+                                                          INT64_MAX, recv_rows.n[d]));
+    s_ok[threadIdx.x] = ok;
+    if (!ok) s_bad = 1;
   }
   __syncthreads();
+  if (s_bad) {
+    // 2. a block does not fit: the table again, over the blocks that do
+    auto kept = [&](int j) -> int64_t {
+      const int d = j / E, s = (j - d * E) / per;
+      return s_ok[d * R + s] ? entry_count(expert_counts, E, per, j) : 0;
+    };
+    local = 0;
+    for (int c = 0; c < chunk; c++) {
+      if (j0 + c >= N) break;
+      local += kept(j0 + c);
+    }
+    run = table_scan(local, wsum);
+    for (int c = 0; c < chunk; c++) {
+      const int j = j0 + c;
+      if (j >= N) break;
+      const int d = j / E, rem = j - d * E, s = rem / per, el = rem - s * per;
+      if (el == 0) first_end[d * R + s] = run;
+      run += kept(j);
+      s_end[j] = run;
+    }
+    __syncthreads();
+  }
   for (int c = 0; c < chunk; c++) {
     const int j = j0 + c;
     if (j >= N) break;
