@@ -112,7 +112,7 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, const RowLimits &li
       const int64_t c = counts[count_index(ct, R, s, d)], sdv = sdispls[bb],
                     rdv = rdispls[d * R + s];
       const uint64_t len =
-          (b < nb && block_fits(c, sdv, rdv, lim.in.n[s], lim.out.n[d])) ? (uint64_t)c * row_units
+          (b < nb && block_fits(c, sdv, rdv, pick_rows(lim.in, s), pick_rows(lim.out, d))) ? (uint64_t)c * row_units
                                                                           : 0;
       const uint64_t incl = wave_incl_scan(len);
       if (b < nb) {
@@ -147,7 +147,7 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, const RowLimits &li
       const int b = lane * 4 + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
-      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], lim.in.n[s], lim.out.n[d]);
+      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], pick_rows(lim.in, s), pick_rows(lim.out, d));
       len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_units : 0;
       local += len[j];
     }
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimit
       const int b = lane * 4 + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
-      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], lim.in.n[s], lim.out.n[d]);
+      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], pick_rows(lim.in, s), pick_rows(lim.out, d));
       len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_bytes : 0;
       nch[j] = (len[j] + 15) / 16;
       local += nch[j];
@@ -560,7 +560,7 @@ __device__ __forceinline__ void desc_table(const RankPtrs &p, const RowLimits &l
     const int b = lane * 4 + j;
     const int bb = b < nb ? b : 0;
     const int s = bb / R, d = bb - s * R;
-    const bool fits = block_fits(cnt[j], sdv[j], rdv[j], lim.in.n[s], lim.out.n[d]);
+    const bool fits = block_fits(cnt[j], sdv[j], rdv[j], pick_rows(lim.in, s), pick_rows(lim.out, d));
     len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_units : 0;
     local += len[j];
   }

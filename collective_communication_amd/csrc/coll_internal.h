@@ -34,6 +34,7 @@ struct RowLimits {
   RankRows in, out;
 };
 
+
 // Rows [sdv, sdv + c) of a buffer of lin rows and [rdv, rdv + c) of one of
 // lout rows all exist, and there is at least one (no sum can overflow:
 // lin, lout >= 0).
@@ -376,6 +377,27 @@ template <> struct UnitT<1> { typedef uint8_t T; };
 #ifndef COLL_UNIFORM
 #define COLL_UNIFORM(x) asm volatile("" : "+s"(x))
 #endif
+// COLL_SCALAR(x): the same fence for a value uniform by construction (a
+// kernel argument), where it may sit under divergent control flow.
+#ifndef COLL_SCALAR
+#define COLL_SCALAR(x) asm volatile("" : "+s"(x))
+#endif
+
+// rows.n[i] for a lane-dependent i: a select chain over the table, which the
+// kernel loads through the scalar unit.  Indexed directly, the by-value table
+// becomes a vector load from the argument segment per lane, a round trip the
+// table-building code then waits on (MoE fused dispatch, MI355X: 825 against
+// 776-803 us).
+__device__ __forceinline__ int64_t pick_rows(const RankRows &rows, int i) {
+  int64_t v = 0;
+#pragma unroll
+  for (int q = 0; q < COLL_MAX_RANKS; q++) {
+    int64_t x = rows.n[q];
+    COLL_SCALAR(x);             // kept in a scalar register: no indexed reload
+    v = i == q ? x : v;
+  }
+  return v;
+}
 
 // Lane l's 64-bit x (l the same in every lane).
 __device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {

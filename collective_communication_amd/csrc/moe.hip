@@ -431,7 +431,7 @@ __global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_c
     const int d = threadIdx.x / R, s = threadIdx.x - d * R;
     const int64_t sum = s_b1[threadIdx.x] - first_end[threadIdx.x];
     const bool ok = sum < kNeg && (sum == 0 || block_fits(sum, 0, rdispls[d * R + s],
-                                                          INT64_MAX, recv_rows.n[d]));
+                                                          INT64_MAX, pick_rows(recv_rows, d)));
     s_ok[threadIdx.x] = ok;
     if (!ok) s_bad = 1;
   }
@@ -797,7 +797,7 @@ __device__ __forceinline__ void load_src_blocks(SrcBlocks &b, int R, int s,
   if ((int)threadIdx.x < R) {
     const int d = threadIdx.x;
     const int64_t a = sdispls[s * R + d], c = sendcounts[s * R + d], r = rdispls[d * R + s];
-    const bool ok = block_fits(c, a, r, INT64_MAX, recv_rows.n[d]);
+    const bool ok = block_fits(c, a, r, INT64_MAX, pick_rows(recv_rows, d));
     b.lo[d] = ok ? a : 1;
     b.hi[d] = ok ? a + c : 0;
     b.rd[d] = r;
@@ -842,7 +842,7 @@ __device__ __forceinline__ SrcLane load_src_lane(int R, int s, const Table &recv
   const int q = threadIdx.x & 63;
   const int qq = q < R ? q : 0;
   const int64_t a = sdispls[s * R + qq], c = sendcounts[s * R + qq], r = rdispls[qq * R + s];
-  const bool ok = q < R && block_fits(c, a, r, INT64_MAX, recv_rows.n[qq]);
+  const bool ok = q < R && block_fits(c, a, r, INT64_MAX, pick_rows(recv_rows, qq));
   SrcLane b;
   b.lo = ok ? a : 1;
   b.hi = ok ? a + c : 0;

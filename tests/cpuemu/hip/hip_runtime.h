@@ -32,6 +32,7 @@
 // bits, or the run aborts naming the site (see the wave ops below)
 #define COLL_OPAQUE(x) ((void)0)
 #define COLL_KEEP(x) ((void)0)
+#define COLL_SCALAR(x) ((void)0)
 #define COLL_UNIFORM(x) emu_uniform_at(emu_bits(x), __FILE__, __LINE__)
 
 // ------------------------------------------------------------- runtime types
