@@ -111,9 +111,10 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, const RowLimits &li
       const int s = bb / R, d = bb - s * R;
       const int64_t c = counts[count_index(ct, R, s, d)], sdv = sdispls[bb],
                     rdv = rdispls[d * R + s];
+      const int64_t lin = rows_from_lane(lane_rows(lim.in), s);
+      const int64_t lout = rows_from_lane(lane_rows(lim.out), d);
       const uint64_t len =
-          (b < nb && block_fits(c, sdv, rdv, pick_rows(lim.in, s), pick_rows(lim.out, d))) ? (uint64_t)c * row_units
-                                                                          : 0;
+          (b < nb && block_fits(c, sdv, rdv, lin, lout)) ? (uint64_t)c * row_units : 0;
       const uint64_t incl = wave_incl_scan(len);
       if (b < nb) {
         const uint64_t start = incl - len;
@@ -129,6 +130,7 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, const RowLimits &li
     uint64_t len[4];
     int64_t cnt[4], sdv[4], rdv[4];
     uint64_t local = 0;
+    const int64_t my_in = lane_rows(lim.in), my_out = lane_rows(lim.out);
     // all three tables are loaded before the scan: one round trip to L2.  The
     // loads are unconditional (a lane past the last block reads block 0 and
     // discards it): a load under `if (b < nb)` made the compiler wait for it
@@ -147,7 +149,8 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, const RowLimits &li
       const int b = lane * 4 + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
-      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], pick_rows(lim.in, s), pick_rows(lim.out, d));
+      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], rows_from_lane(my_in, s),
+                                   rows_from_lane(my_out, d));
       len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_units : 0;
       local += len[j];
     }
@@ -318,6 +321,7 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimit
     uint64_t len[4], nch[4];
     int64_t cnt[4], sdv[4], rdv[4];
     uint64_t local = 0;
+    const int64_t my_in = lane_rows(lim.in), my_out = lane_rows(lim.out);
     bool misaligned = false;
     // unconditional loads (clamped index), then the bounds: one round trip
 #pragma unroll
@@ -334,7 +338,8 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimit
       const int b = lane * 4 + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
-      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], pick_rows(lim.in, s), pick_rows(lim.out, d));
+      const bool fits = block_fits(cnt[j], sdv[j], rdv[j], rows_from_lane(my_in, s),
+                                   rows_from_lane(my_out, d));
       len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_bytes : 0;
       nch[j] = (len[j] + 15) / 16;
       local += nch[j];
@@ -546,6 +551,7 @@ __device__ __forceinline__ void desc_table(const RankPtrs &p, const RowLimits &l
   uint64_t len[4];
   int64_t cnt[4], sdv[4], rdv[4];
   uint64_t local = 0;
+  const int64_t my_in = lane_rows(lim.in), my_out = lane_rows(lim.out);
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int b = lane * 4 + j;
@@ -560,7 +566,8 @@ __device__ __forceinline__ void desc_table(const RankPtrs &p, const RowLimits &l
     const int b = lane * 4 + j;
     const int bb = b < nb ? b : 0;
     const int s = bb / R, d = bb - s * R;
-    const bool fits = block_fits(cnt[j], sdv[j], rdv[j], pick_rows(lim.in, s), pick_rows(lim.out, d));
+    const bool fits = block_fits(cnt[j], sdv[j], rdv[j], rows_from_lane(my_in, s),
+                                 rows_from_lane(my_out, d));
     len[j] = (b < nb && fits) ? (uint64_t)cnt[j] * row_units : 0;
     local += len[j];
   }

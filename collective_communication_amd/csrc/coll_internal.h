@@ -399,6 +399,16 @@ __device__ __forceinline__ int64_t pick_rows(const RankRows &rows, int i) {
   return v;
 }
 
+// For code where a whole wave looks up the limits of many blocks: lane l
+// (l < 16) selects rank l's limit once, and a lane reads rank r's from lane r
+// with a shuffle (two 32-bit permutes) instead of its own select chain.
+__device__ __forceinline__ int64_t lane_rows(const RankRows &rows) {
+  return pick_rows(rows, (int)(threadIdx.x & (COLL_MAX_RANKS - 1)));
+}
+__device__ __forceinline__ int64_t rows_from_lane(int64_t mine, int r) {
+  return __shfl(mine, r, 64);
+}
+
 // Lane l's 64-bit x (l the same in every lane).
 __device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
