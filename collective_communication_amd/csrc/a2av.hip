@@ -51,6 +51,13 @@ constexpr int kA2aBlock = COLL_A2A_BLOCK;
 #ifndef COLL_A2A_SMALL
 #define COLL_A2A_SMALL 1
 #endif
+// 1: ... and the chunk kernel (rows not in 16-byte units) likewise.  MI355X,
+// R = 8, rows of one bf16, graph replay: 8 KiB / 1 MiB / 16 / 64 MiB per
+// rank 4.1 / 5.8 / 48.4 / 181.0 us against 5.1 / 6.9 / 49.4 / 184.4 us with
+// four blocks per lane
+#ifndef COLL_A2A_CHUNK_SMALL
+#define COLL_A2A_CHUNK_SMALL 1
+#endif
 
 // 1: with at most 64 blocks, waves locate their units with one ballot over
 // block ends held in registers (wave_block) instead of a per-lane search.
@@ -303,30 +310,33 @@ __device__ __forceinline__ void copy_chunk_narrow(uint64_t src, uint64_t dst, ui
   else copy_pieces<uint8_t>(src, dst, n);
 }
 
-template <bool NT, int UN, bool FAST>
+// BPL: blocks per lane of the table-building wave: 4 (up to 256 blocks) or 1
+// (R <= 8: smaller LDS tables, one load round of three words per lane)
+template <bool NT, int UN, bool FAST, int BPL>
 __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimits lim, int R,
                                                             const int64_t *counts,
                                                             const int64_t *sdispls,
                                                             const int64_t *rdispls, int ct,
                                                             uint64_t row_bytes) {
-  __shared__ uint64_t s_end[kMaxBlocks];   // inclusive end of block b, in chunks
-  __shared__ uint64_t s_src[kMaxBlocks];   // source byte address of the block's chunk 0
-  __shared__ uint64_t s_dst[kMaxBlocks];
-  __shared__ uint64_t s_len[kMaxBlocks];   // block length in bytes
+  constexpr int kTab = 64 * BPL;
+  __shared__ uint64_t s_end[kTab];         // inclusive end of block b, in chunks
+  __shared__ uint64_t s_src[kTab];         // source byte address of the block's chunk 0
+  __shared__ uint64_t s_dst[kTab];
+  __shared__ uint64_t s_len[kTab];         // block length in bytes
   __shared__ int s_allvec;                 // every block moves as whole 16-byte chunks
 
   const int nb = R * R;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    uint64_t len[4], nch[4];
-    int64_t cnt[4], sdv[4], rdv[4];
+    uint64_t len[BPL], nch[BPL];
+    int64_t cnt[BPL], sdv[BPL], rdv[BPL];
     uint64_t local = 0;
     const int64_t my_in = lane_rows(lim.in), my_out = lane_rows(lim.out);
     bool misaligned = false;
     // unconditional loads (clamped index), then the bounds: one round trip
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int b = lane * 4 + j;
+    for (int j = 0; j < BPL; j++) {
+      const int b = lane * BPL + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
       cnt[j] = counts[count_index(ct, R, s, d)];
@@ -334,8 +344,8 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimit
       rdv[j] = rdispls[d * R + s];
     }
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int b = lane * 4 + j;
+    for (int j = 0; j < BPL; j++) {
+      const int b = lane * BPL + j;
       const int bb = b < nb ? b : 0;
       const int s = bb / R, d = bb - s * R;
       const bool fits = block_fits(cnt[j], sdv[j], rdv[j], rows_from_lane(my_in, s),
@@ -347,8 +357,8 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimit
     const uint64_t incl = wave_incl_scan(local);
     uint64_t start = incl - local;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int b = lane * 4 + j;
+    for (int j = 0; j < BPL; j++) {
+      const int b = lane * BPL + j;
       if (b < nb) {
         const int s = b / R, d = b - s * R;
         s_src[b] = reinterpret_cast<uintptr_t>(p.in[s]) + (uint64_t)sdv[j] * row_bytes;
@@ -757,14 +767,20 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
       g = resident ? (g1 < g_res ? g1 : g_res) : g1;
     }
     if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
+#define COLL_A2A_CHUNK_B(NTV, UNV, FASTV, BPLV)                                                  \
+  hipLaunchKernelGGL((a2av_chunk_kernel<NTV, UNV, FASTV, BPLV>), dim3(g), dim3(kBlock), 0,       \
+                     L.stream, p, lim, R, counts, sdispls, rdispls, ct, (uint64_t)row_bytes)
 #define COLL_A2A_CHUNK(NTV, UNV, FASTV)                                                          \
-  hipLaunchKernelGGL((a2av_chunk_kernel<NTV, UNV, FASTV>), dim3(g), dim3(kBlock), 0, L.stream,  \
-                     p, lim, R, counts, sdispls, rdispls, ct, (uint64_t)row_bytes)
+  do {                                                                                         \
+    if (COLL_A2A_CHUNK_SMALL && R <= 8) COLL_A2A_CHUNK_B(NTV, UNV, FASTV, 1);                    \
+    else COLL_A2A_CHUNK_B(NTV, UNV, FASTV, 4);                                                  \
+  } while (0)
     if (L.a2a_nt && resident) COLL_A2A_CHUNK(true, kA2aResU, true);
     else if (L.a2a_nt) COLL_A2A_CHUNK(true, kA2aU, false);
     else if (resident) COLL_A2A_CHUNK(false, kA2aResU, true);
     else COLL_A2A_CHUNK(false, kA2aU, false);
 #undef COLL_A2A_CHUNK
+#undef COLL_A2A_CHUNK_B
   }
   return hip_status();
 }
