@@ -136,3 +136,90 @@ def test_graph_replays_fused_moe_pipeline():
         want = oracle.moe_pipeline(xs, ids, wts, E)
         for r in range(R):
             assert bits_equal(host(outs[r]).reshape(-1), want["outs"][r].reshape(-1)), (it, r)
+
+
+def test_graph_replays_moe_step_with_descriptor_builds_on_a_second_stream():
+    """The unfused MoE sequence as the benchmark step runs it: the layout
+    marks an event, the permute runs, a second stream waits for that event
+    and builds both exchanges' descriptor tables, the main stream waits for
+    them and runs the two copies around the test expert, then the combine.
+    Captured once (fork and join by events), replayed with new routing and
+    tokens each time.  Each receive buffer holds the most rows any of the
+    routings sends it; both directions' capacities (256 MiB and more) are
+    above the descriptor form's threshold."""
+    R, E, T, K, H = 8, 64, 1024, 4, 4096
+    say("graph: moe step, split descriptor form, two streams")
+    bf = torch.bfloat16
+    id_d = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(R)]
+    w_d = [torch.empty((T, K), dtype=torch.float32, device="cuda") for _ in range(R)]
+    x_d = [torch.empty((T, H), dtype=bf, device="cuda") for _ in range(R)]
+    sc = torch.empty(R * R, dtype=torch.int64, device="cuda")
+    sdd, rdd = torch.empty_like(sc), torch.empty_like(sc)
+    ec = torch.empty(R * E, dtype=torch.int32, device="cuda")
+    pos = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(R)]
+    ws = torch.empty(coll.moe_workspace_bytes(R, T, K, E), dtype=torch.uint8, device="cuda")
+    send = [torch.empty((T * K, H), dtype=bf, device="cuda") for _ in range(R)]
+    per = E // R
+    routes = [[synth.zipf_routing(T, E, K, seed=66000 + 100 * it + s) for s in range(R)]
+              for it in range(5)]
+    need = [max(sum(int(np.count_nonzero(i // per == d)) for i, _ in rt) for rt in routes)
+            for d in range(R)]
+    recv = [torch.empty((need[d], H), dtype=bf, device="cuda") for d in range(R)]
+    back = [torch.empty((T * K, H), dtype=bf, device="cuda") for _ in range(R)]
+    outs = [torch.empty((T, H), dtype=bf, device="cuda") for _ in range(R)]
+    wsd = torch.empty(coll.all_to_all_v_workspace_bytes(send, recv, H), dtype=torch.uint8,
+                      device="cuda")
+    wsc = torch.empty(coll.all_to_all_v_workspace_bytes(recv, back, H), dtype=torch.uint8,
+                      device="cuda")
+    assert wsd.numel() > 0 and wsc.numel() > 0
+    ews = torch.empty(coll.moe_expert_workspace_bytes(R, E, R * R * T * K), dtype=torch.uint8,
+                      device="cuda")
+    side = torch.cuda.Stream()
+    laid_out, built = torch.cuda.Event(), torch.cuda.Event()
+
+    def feed(it):
+        ids, wts, xs = [], [], []
+        for s in range(R):
+            i, w = routes[it][s]
+            ids.append(i)
+            wts.append(w)
+            xs.append(synth.gaussian((T, H), 1.0, 67000 + 100 * it + s, "bf16"))
+            id_d[s].copy_(torch.from_numpy(i))
+            w_d[s].copy_(torch.from_numpy(w))
+            x_d[s].copy_(dev(xs[s]))
+            outs[s].view(torch.int16).fill_(0x7FAB)
+        torch.cuda.synchronize()
+        return xs, ids, wts
+
+    def calls():
+        coll.moe_layout(id_d, E, sc, sdd, rdd, ec, pos, ws)
+        laid_out.record()
+        coll.moe_permute(x_d, pos, send)
+        side.wait_event(laid_out)
+        with torch.cuda.stream(side):
+            coll.all_to_all_v_build(send, sc, sdd, recv, rdd, H, wsd)
+            coll.all_to_all_v_reverse_build(recv, sc, sdd, back, rdd, H, wsc)
+        built.record(side)
+        torch.cuda.current_stream().wait_event(built)
+        coll.all_to_all_v_copy(send, recv, H, wsd)
+        coll.moe_expert_scale(recv, ec, rdd, E, H, ews)
+        coll.all_to_all_v_copy(recv, back, H, wsc)
+        coll.moe_combine(back, pos, w_d, outs)
+
+    feed(0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for it in range(1, 5):
+        xs, ids, wts = feed(it)
+        g.replay()
+        torch.cuda.synchronize()
+        want = oracle.moe_pipeline(xs, ids, wts, E)
+        for r in range(R):
+            assert bits_equal(host(outs[r]).reshape(-1), want["outs"][r].reshape(-1)), (it, r)
