@@ -474,7 +474,7 @@ def _graph_time(torch, fn, sets, n=24, reps=4):
 
 
 def copy_ceiling(torch, coll, W):
-    """Practical HBM ceiling on this machine: a plain 1 GiB -> 1 GiB copy through
+    """Practical HBM ceiling of this GPU: a plain 1 GiB -> 1 GiB copy through
     the library's copy kernel (2 GiB moved), graph-timed."""
     t = _graph_time(torch, lambda i: coll.broadcast(W["copy_src"], W["copy_dst"], 0), 1,
                     n=8, reps=2)

@@ -103,8 +103,8 @@ def _check(status: int, what: str) -> None:
 
 
 # The current stream's raw handle for a device index.  torch's own accessor
-# returns it without building a Stream object: 0.06 us per call on the MI355X
-# box, against 2.7 us for torch.cuda.current_stream(), which was most of a
+# returns it without building a Stream object: 0.06 us per call on an MI355X
+# host, against 2.7 us for torch.cuda.current_stream(), which was most of a
 # decode-sized call's host cost.  Falls back to the public API if absent.
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 

@@ -20,7 +20,7 @@
 // Data movement:
 //   moe_permute   send[s][pos[t,k]] = x[s][t]: each token row is read once and
 //                 written topk times, 16-byte units.
-//   moe_expert_scale  the harness's test expert y = rne(x * (1 + e/256)), in
+//   moe_expert_scale  the test expert y = rne(x * (1 + e/256)), in
 //                 place: a one-workgroup table of row prefixes, then one
 //                 workgroup per tile of received units.
 //   moe_combine   one wave per token: topk rows gathered by pos, fp32

@@ -4,7 +4,7 @@ every output element of every stage compared against the oracle.
 
 The oracle runs the whole exchange once (tutorial section 8.4: layout,
 permute, All-to-All-v, test expert, the reverse All-to-All-v, combine; about
-20 s of CPU on the GPU machine's host).  Each stage on the GPU is then fed the
+20 s of CPU on the host that drives the GPU).  Each stage on the GPU is then fed the
 oracle's output of the stage before it and its own output, poison-filled
 first, is compared in full: the layout tables and slots; the permute's send
 buffers; the exchange in both forms (the plain one-pass grid and the
