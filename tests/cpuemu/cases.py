@@ -418,12 +418,12 @@ def fam_a2av():
     case("a2av capacity below the rows received")
     _a2av_case(3, g.integers(20, 50, size=(3, 3)), 8, "bf16", cap=10)
     # the descriptor form (COLL_A2A_DESC_MIN_BYTES=0 in this process)
-    for R, W in ((8, 8), (3, 24), (2, 8), (8, 7168 // 64)):
+    for R, W in ((8, 8), (3, 24), (2, 8), (8, 7168 // 64), (16, 8), (1, 16)):
         case("a2av descriptor form", R, W)
         _a2av_case(R, g.integers(0, 60, size=(R, R)), W, "bf16", ws=True)
     case("a2av descriptor form, capacity below the rows (tail loop)")
     _a2av_case(4, g.integers(30, 60, size=(4, 4)), 8, "bf16", ws=True, cap=50)
-    for R, W in ((8, 8), (3, 24)):
+    for R, W in ((8, 8), (3, 24), (16, 8), (1, 16)):
         case("a2av descriptor form in two calls (build, then copy)", R, W)
         _a2av_split_case(R, W, g)
     case("a2av descriptor form, gapped")

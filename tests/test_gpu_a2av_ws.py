@@ -258,7 +258,9 @@ def test_graph_replays_the_descriptor_form():
             assert bits_equal(host(recvs[d]), want[d]), (rep, d)
 
 
-@pytest.mark.parametrize("R,W,lo,hi", [(8, 2048, 600, 1000), (4, 8192, 750, 1000)])
+@pytest.mark.parametrize("R,W,lo,hi", [(8, 2048, 600, 1000), (4, 8192, 750, 1000),
+                                       (16, 1024, 400, 520), (3, 4096, 3000, 4000),
+                                       (1, 8192, 13000, 14000)])
 def test_build_on_a_second_stream_then_copy(R, W, lo, hi):
     """The descriptor form in two calls, used as intended: the build runs on
     a second stream before the send buffers are written (it reads only the
