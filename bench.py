@@ -141,7 +141,10 @@ def make_inputs(torch, synth, coll):
                                 W["rd"], H, W["a2a_ws_d"])
     W["build_c"] = coll.prepare(coll.all_to_all_v_reverse_build, W["recv"], W["sc"], W["sd"],
                                 W["back"], W["rd"], H, W["a2a_ws_c"])
-    W["build_d"](), W["build_c"]()
+    # the test expert's row descriptors likewise depend only on the layout
+    W["build_e"] = coll.prepare(coll.moe_expert_scale_build, W["recv"], W["ec"], W["rd"], E, H,
+                                W["ews"])
+    W["build_d"](), W["build_c"](), W["build_e"]()
     torch.cuda.synchronize()
     W["side"] = torch.cuda.Stream()          # default priority
     W["built"] = [None]
@@ -193,9 +196,10 @@ def _composite(fn):
 
 def step_rows(W, coll, torch):
     """(name, callable) for every row of one step, in order.  The two
-    All-to-All-v rows run the descriptor form's copy kernel; their descriptor
-    builds wait only for the layout and run on a second stream beside the
-    permute, and the dispatch row waits for them."""
+    All-to-All-v rows run the descriptor form's copy kernel and the expert row
+    its scaling kernel; their descriptor builds wait only for the layout and
+    run on a second stream beside the permute, and the dispatch row waits for
+    them."""
     E, T, K, H = W["moe"]
     layout = coll.prepare(coll.moe_layout, W["moe_ids"], E, W["sc"], W["sd"], W["rd"], W["ec"],
                           W["pos"], W["ws"])
@@ -221,6 +225,7 @@ def step_rows(W, coll, torch):
         with torch.cuda.stream(side):
             W["build_d"]()
             W["build_c"]()
+            W["build_e"]()
         W["ev_built"].record(side)
         W["built"][0] = W["ev_built"]
 
@@ -241,7 +246,7 @@ def step_rows(W, coll, torch):
         ("moe_layout", layout_then_mark),
         ("moe_permute", permute_then_builds),
         ("a2av_dispatch", dispatch),
-        ("moe_expert", lambda: coll.moe_expert_scale(W["recv"], W["ec"], W["rd"], E, H, W["ews"])),
+        ("moe_expert", lambda: coll.moe_expert_scale_apply(W["recv"], E, H, W["ews"])),
         ("a2av_combine", lambda: coll.all_to_all_v_copy(W["recv"], W["back"], H,
                                                         workspace=W["a2a_ws_c"])),
         ("moe_combine", lambda: coll.moe_combine(W["back"], W["pos"], W["moe_w"], W["out"])),

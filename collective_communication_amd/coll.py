@@ -64,6 +64,9 @@ SIGNATURES = {
     "coll_moe_permute": (_i, [_i, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_expert_workspace_bytes": (_sz, [_i, _i, _sz]),
     "coll_moe_expert_scale": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _vp, _sz, _vp]),
+    "coll_moe_expert_scale_build": (_i, [_i, _vp, _vp, _vp, _i, _sz, _i, _sz, _vp, _vp, _sz,
+                                         _vp]),
+    "coll_moe_expert_scale_apply": (_i, [_i, _vp, _i, _sz, _i, _sz, _vp, _sz, _vp]),
     "coll_moe_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp]),
     "coll_moe_dispatch": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp, _vp, _vp]),
     "coll_moe_combine_recv": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _sz, _i, _vp,
@@ -627,6 +630,55 @@ def moe_expert_scale(recvs, expert_counts, rdispls, n_experts: int, hidden: int,
     return _issue("coll_moe_expert_scale", "moe_expert_scale", stream, R, _table(recvs, "recv", R),
                   _dev(expert_counts, "ec"), _dev(rdispls, "rd"), n_experts, hidden, COLL_BF16,
                   capacity, _rows(recvs, hidden), _dev(workspace, "ws"), ws_bytes)
+
+
+def _expert_split(recvs, n_experts, hidden, workspace, what):
+    """Checks shared by the two halves of the row-descriptor path; returns
+    (R, capacity, workspace bytes)."""
+    R = _ranks(recvs, what)
+    for r in recvs:
+        if r.dtype != torch.bfloat16:
+            raise ValueError(f"{what}: bf16 rows only")
+    if n_experts < 1 or n_experts % R:
+        raise ValueError(f"{what}: n_experts must be a positive multiple of the rank count")
+    capacity = sum(t.numel() // hidden for t in recvs) if hidden > 0 else 0
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if hidden <= 0 or hidden % 8 or capacity == 0 or R * n_experts > 8192 or \
+            ws_bytes < moe_expert_workspace_bytes(R, n_experts, capacity):
+        raise ValueError(f"{what}: the row-descriptor path does not apply (16-byte rows, a "
+                         "nonzero capacity, R*E <= 8192 and a workspace of "
+                         "moe_expert_workspace_bytes(R, E, capacity) bytes); call moe_expert_scale")
+    return R, capacity, ws_bytes
+
+
+def moe_expert_scale_build(recvs, expert_counts, rdispls, n_experts: int, hidden: int, workspace,
+                           stream=None):
+    """First half of moe_expert_scale's row-descriptor path: writes the row
+    table and one descriptor per receive row into ``workspace`` and touches no
+    row.  It needs only the layout's tables and the buffers' addresses, so it
+    may run while the rows are still being exchanged, e.g. on a second stream.
+    moe_expert_scale_apply(recvs, ...) then scales the rows.  Raises
+    ValueError where that path does not apply."""
+    R, capacity, ws_bytes = _expert_split(recvs, n_experts, hidden, workspace,
+                                          "moe_expert_scale_build")
+    if expert_counts.dtype != torch.int32 or expert_counts.numel() != R * n_experts:
+        raise ValueError("moe_expert_scale_build: expert_counts must be int32 [R*E]")
+    if rdispls.dtype != torch.int64 or rdispls.numel() != R * R:
+        raise ValueError("moe_expert_scale_build: rdispls must be int64 [R*R]")
+    return _issue("coll_moe_expert_scale_build", "moe_expert_scale_build", stream, R,
+                  _table(recvs, "recv", R), _dev(expert_counts, "ec"), _dev(rdispls, "rd"),
+                  n_experts, hidden, COLL_BF16, capacity, _rows(recvs, hidden),
+                  _dev(workspace, "ws"), ws_bytes)
+
+
+def moe_expert_scale_apply(recvs, n_experts: int, hidden: int, workspace, stream=None):
+    """Second half: scales the received rows from the descriptors a
+    moe_expert_scale_build on the same buffers wrote into ``workspace``."""
+    R, capacity, ws_bytes = _expert_split(recvs, n_experts, hidden, workspace,
+                                          "moe_expert_scale_apply")
+    return _issue("coll_moe_expert_scale_apply", "moe_expert_scale_apply", stream, R,
+                  _table(recvs, "recv", R), n_experts, hidden, COLL_BF16, capacity,
+                  _dev(workspace, "ws"), ws_bytes)
 
 
 def moe_combine(backs, pos, weights, outs, stream=None):

@@ -547,27 +547,65 @@ size_t coll_moe_expert_workspace_bytes(int R, int n_experts, size_t recv_rows_ca
   return moe_expert_workspace_bytes(R, n_experts, recv_rows_capacity);
 }
 
+// coll_moe_expert_scale (how = 0), its build (1) or its apply (2; the
+// tables and recv_rows are not read).
+static int expert_call(int how, int R, void *const *recvbufs, const int32_t *expert_counts,
+                       const int64_t *rdispls, int n_experts, size_t hidden, coll_dtype_t dtype,
+                       size_t recv_rows_capacity, const int64_t *recv_rows, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0)
+    return COLL_ERR_INVALID_ARG;
+  if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
+  if (hidden == 0) return how == 0 ? COLL_OK : COLL_ERR_UNSUPPORTED;
+  if ((how != 2 && (!expert_counts || !rdispls)) || hidden >= ((size_t)1 << 31))
+    return COLL_ERR_INVALID_ARG;
+  const size_t need = how == 2 ? moe_expert_workspace_bytes(R, n_experts, recv_rows_capacity)
+                               : moe_expert_table_bytes(R, n_experts);
+  if (!workspace || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < need)
+    return COLL_ERR_INVALID_ARG;
+  MutPtrTable rs{};
+  if (!fill_out(R, recvbufs, rs.p)) return COLL_ERR_INVALID_ARG;
+  if (recv_rows_capacity > ((size_t)1 << 48) / hidden) return COLL_ERR_INVALID_ARG;
+  if (how != 0 && !moe_expert_rows_apply(R, rs, n_experts, hidden, recv_rows_capacity,
+                                         workspace_bytes))
+    return COLL_ERR_UNSUPPORTED;
+  if (how == 2)
+    return launch_moe_expert_apply(launch_ctx(stream), R, rs, n_experts, hidden,
+                                   recv_rows_capacity, workspace, workspace_bytes);
+  RankRows rows;
+  if (!fill_rows(R, recv_rows, reinterpret_cast<const void *const *>(recvbufs), rows))
+    return COLL_ERR_INVALID_ARG;
+  const Launch L = launch_ctx(stream);
+  if (how == 1)
+    return launch_moe_expert_build(L, R, rs, expert_counts, rdispls, n_experts, hidden,
+                                   recv_rows_capacity, workspace, workspace_bytes, rows);
+  return launch_moe_expert_scale(L, R, rs, expert_counts, rdispls, n_experts, hidden,
+                                 recv_rows_capacity, workspace, workspace_bytes, rows);
+}
+
 int coll_moe_expert_scale(int R, void *const *recvbufs, const int32_t *expert_counts,
                           const int64_t *rdispls, int n_experts, size_t hidden,
                           coll_dtype_t dtype, size_t recv_rows_capacity,
                           const int64_t *recv_rows, void *workspace, size_t workspace_bytes,
                           void *stream) {
-  if (!ranks_ok(R) || n_experts < 1 || n_experts > kMoeMaxExperts || n_experts % R != 0)
-    return COLL_ERR_INVALID_ARG;
-  if (dtype != COLL_BF16) return COLL_ERR_UNSUPPORTED;
-  if (hidden == 0) return COLL_OK;
-  if (!expert_counts || !rdispls || hidden >= ((size_t)1 << 31)) return COLL_ERR_INVALID_ARG;
-  if (!workspace || ((uintptr_t)workspace & 255) != 0 ||
-      workspace_bytes < moe_expert_table_bytes(R, n_experts))
-    return COLL_ERR_INVALID_ARG;
-  MutPtrTable rs{};
-  if (!fill_out(R, recvbufs, rs.p)) return COLL_ERR_INVALID_ARG;
-  if (recv_rows_capacity > ((size_t)1 << 48) / hidden) return COLL_ERR_INVALID_ARG;
-  RankRows rows;
-  if (!fill_rows(R, recv_rows, reinterpret_cast<const void *const *>(recvbufs), rows))
-    return COLL_ERR_INVALID_ARG;
-  return launch_moe_expert_scale(launch_ctx(stream), R, rs, expert_counts, rdispls, n_experts,
-                                 hidden, recv_rows_capacity, workspace, workspace_bytes, rows);
+  return expert_call(0, R, recvbufs, expert_counts, rdispls, n_experts, hidden, dtype,
+                     recv_rows_capacity, recv_rows, workspace, workspace_bytes, stream);
+}
+
+int coll_moe_expert_scale_build(int R, void *const *recvbufs, const int32_t *expert_counts,
+                                const int64_t *rdispls, int n_experts, size_t hidden,
+                                coll_dtype_t dtype, size_t recv_rows_capacity,
+                                const int64_t *recv_rows, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  return expert_call(1, R, recvbufs, expert_counts, rdispls, n_experts, hidden, dtype,
+                     recv_rows_capacity, recv_rows, workspace, workspace_bytes, stream);
+}
+
+int coll_moe_expert_scale_apply(int R, void *const *recvbufs, int n_experts, size_t hidden,
+                                coll_dtype_t dtype, size_t recv_rows_capacity, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  return expert_call(2, R, recvbufs, nullptr, nullptr, n_experts, hidden, dtype,
+                     recv_rows_capacity, nullptr, workspace, workspace_bytes, stream);
 }
 
 int coll_moe_combine(int R, const void *const *back, const int32_t *const *pos,

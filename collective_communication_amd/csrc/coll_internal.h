@@ -528,6 +528,16 @@ int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
                             size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes,
                             const RankRows &recv_rows);
+// the row-descriptor path of the test expert in two calls (COLL_ERR_UNSUPPORTED
+// where that path does not apply; moe_expert_rows_apply tells on the host)
+bool moe_expert_rows_apply(int R, const MutPtrTable &recv, int E, size_t hidden,
+                           size_t rows_capacity, size_t ws_bytes);
+int launch_moe_expert_build(const Launch &L, int R, const MutPtrTable &recv,
+                            const int32_t *expert_counts, const int64_t *rdispls, int E,
+                            size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes,
+                            const RankRows &recv_rows);
+int launch_moe_expert_apply(const Launch &L, int R, const MutPtrTable &recv, int E, size_t hidden,
+                            size_t rows_capacity, void *ws, size_t ws_bytes);
 int launch_moe_combine(const Launch &L, int R, const PtrTable &back, const PtrTable &pos,
                        const PtrTable &w, int T, int K, size_t hidden, const MutPtrTable &out);
 int launch_moe_dispatch(const Launch &L, int R, const PtrTable &x, const PtrTable &pos,

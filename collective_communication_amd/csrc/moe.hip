@@ -1112,10 +1112,94 @@ int launch_moe_permute(const Launch &L, int R, const PtrTable &x, const PtrTable
   return hip_status();
 }
 
+// The row-descriptor path applies: 16-byte units, a known capacity, a
+// workspace that holds the descriptors, a table that fits in LDS, buffers
+// inside the descriptors' address range and a grid of at most 2^31 - 1
+// workgroups.  Sets vec (rows move in 16-byte units), upr (units per row)
+// and nseg (64-unit segments per row).
+static bool expert_rows_apply(int R, const MutPtrTable &recv, int E, size_t hidden,
+                              size_t rows_capacity, size_t ws_bytes, bool &vec, uint64_t &upr,
+                              uint64_t &nseg) {
+  vec = (hidden % 8) == 0;
+  uintptr_t top_addr = 0;
+  for (int r = 0; r < R; r++) {
+    vec = vec && aligned16(recv.p[r]);
+    top_addr |= (uintptr_t)recv.p[r];
+  }
+  upr = vec ? hidden / 8 : hidden;
+  nseg = (upr + 63) / 64;
+  return vec && rows_capacity > 0 && ws_bytes >= moe_expert_workspace_bytes(R, E, rows_capacity) &&
+         R * E <= kRowTableMax && (top_addr >> (kRowAddrBits + 3)) == 0 &&
+         rows_capacity * nseg <= 0x7FFFFFFFull;
+}
+
+bool moe_expert_rows_apply(int R, const MutPtrTable &recv, int E, size_t hidden,
+                           size_t rows_capacity, size_t ws_bytes) {
+  bool vec;
+  uint64_t upr, nseg;
+  return expert_rows_apply(R, recv, E, hidden, rows_capacity, ws_bytes, vec, upr, nseg);
+}
+
+// First half of the row-descriptor path: the row-prefix table, then one
+// descriptor per receive row of the capacity.  Reads only the count tables
+// and the buffers' addresses, so it may run before the rows arrive.
+int launch_moe_expert_build(const Launch &L, int R, const MutPtrTable &recv,
+                            const int32_t *expert_counts, const int64_t *rdispls, int E,
+                            size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes,
+                            const RankRows &recv_rows) {
+  bool vec;
+  uint64_t upr, nseg;
+  if (!expert_rows_apply(R, recv, E, hidden, rows_capacity, ws_bytes, vec, upr, nseg))
+    return COLL_ERR_UNSUPPORTED;
+  const int N = R * E;
+  int64_t *s_end = reinterpret_cast<int64_t *>(ws);
+  int64_t *rb = s_end + N;
+  hipLaunchKernelGGL(moe_expert_table, dim3(1), dim3(1024), 0, L.stream, expert_counts, rdispls,
+                     R, E, recv_rows, s_end, rb);
+  uint64_t *rdesc =
+      reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + moe_expert_table_bytes(R, E));
+  const uint64_t gneed = (rows_capacity + kBlock - 1) / kBlock;
+  const uint64_t gres = (uint64_t)L.num_cus * 2;   // 64 KiB of LDS each: two per CU
+  hipLaunchKernelGGL(moe_expert_rows, dim3((unsigned)(gneed < gres ? gneed : gres)), dim3(kBlock),
+                     0, L.stream, s_end, rb, R, E, recv, upr, (uint64_t)rows_capacity, rdesc);
+  return hip_status();
+}
+
+// Second half: one 64-lane workgroup per (row, segment) of the capacity.
+int launch_moe_expert_apply(const Launch &L, int R, const MutPtrTable &recv, int E, size_t hidden,
+                            size_t rows_capacity, void *ws, size_t ws_bytes) {
+  bool vec;
+  uint64_t upr, nseg;
+  if (!expert_rows_apply(R, recv, E, hidden, rows_capacity, ws_bytes, vec, upr, nseg))
+    return COLL_ERR_UNSUPPORTED;
+  const int64_t *s_end = reinterpret_cast<const int64_t *>(ws);
+  const int64_t *rb = s_end + R * E;
+  const uint64_t *rdesc = reinterpret_cast<const uint64_t *>(static_cast<const char *>(ws) +
+                                                             moe_expert_table_bytes(R, E));
+  const FastDiv64 fs = make_fastdiv64(nseg);
+  const unsigned g = (unsigned)(rows_capacity * nseg);
+  if (L.a2a_nt)
+    hipLaunchKernelGGL((moe_expert_row_kernel<true>), dim3(g), dim3(64), 0, L.stream, rdesc, s_end,
+                       rb, recv, R, E, (uint32_t)upr, (uint32_t)nseg, fs, (uint64_t)rows_capacity);
+  else
+    hipLaunchKernelGGL((moe_expert_row_kernel<false>), dim3(g), dim3(64), 0, L.stream, rdesc,
+                       s_end, rb, recv, R, E, (uint32_t)upr, (uint32_t)nseg, fs,
+                       (uint64_t)rows_capacity);
+  return hip_status();
+}
+
 int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                             const int32_t *expert_counts, const int64_t *rdispls, int E,
                             size_t hidden, size_t rows_capacity, void *ws, size_t ws_bytes,
                             const RankRows &recv_rows) {
+  bool vec;
+  uint64_t upr, nseg;
+  if (expert_rows_apply(R, recv, E, hidden, rows_capacity, ws_bytes, vec, upr, nseg)) {
+    const int rc = launch_moe_expert_build(L, R, recv, expert_counts, rdispls, E, hidden,
+                                           rows_capacity, ws, ws_bytes, recv_rows);
+    if (rc != COLL_OK) return rc;
+    return launch_moe_expert_apply(L, R, recv, E, hidden, rows_capacity, ws, ws_bytes);
+  }
   const int N = R * E;
   int64_t *s_end = reinterpret_cast<int64_t *>(ws);
   int64_t *rb = s_end + N;
@@ -1123,41 +1207,8 @@ int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
                      R, E, recv_rows, s_end, rb);
   int top = 1;
   while (top * 64 < N) top *= 64;
-  bool vec = (hidden % 8) == 0;
-  uintptr_t top_addr = 0;
-  for (int r = 0; r < R; r++) {
-    vec = vec && aligned16(recv.p[r]);
-    top_addr |= (uintptr_t)recv.p[r];
-  }
-  const size_t upr = vec ? hidden / 8 : hidden;
-  // Row descriptors: 16-byte units, a known capacity, a workspace that holds
-  // them, a table that fits in LDS, buffers inside the descriptors' range and
-  // a grid of at most 2^31 - 1 workgroups.
-  const uint64_t nseg = (upr + 63) / 64;
-  if (vec && rows_capacity > 0 && ws_bytes >= moe_expert_workspace_bytes(R, E, rows_capacity) &&
-      N <= kRowTableMax && (top_addr >> (kRowAddrBits + 3)) == 0 &&
-      rows_capacity * nseg <= 0x7FFFFFFFull) {
-    uint64_t *rdesc = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) +
-                                                   moe_expert_table_bytes(R, E));
-    const uint64_t gneed = (rows_capacity + kBlock - 1) / kBlock;
-    const uint64_t gres = (uint64_t)L.num_cus * 2;   // 64 KiB of LDS each: two per CU
-    hipLaunchKernelGGL(moe_expert_rows, dim3((unsigned)(gneed < gres ? gneed : gres)),
-                       dim3(kBlock), 0, L.stream, s_end, rb, R, E, recv, (uint64_t)upr,
-                       (uint64_t)rows_capacity, rdesc);
-    const FastDiv64 fs = make_fastdiv64(nseg);
-    const unsigned g = (unsigned)(rows_capacity * nseg);
-    if (L.a2a_nt)
-      hipLaunchKernelGGL((moe_expert_row_kernel<true>), dim3(g), dim3(64), 0, L.stream, rdesc,
-                         s_end, rb, recv, R, E, (uint32_t)upr, (uint32_t)nseg, fs,
-                         (uint64_t)rows_capacity);
-    else
-      hipLaunchKernelGGL((moe_expert_row_kernel<false>), dim3(g), dim3(64), 0, L.stream, rdesc,
-                         s_end, rb, recv, R, E, (uint32_t)upr, (uint32_t)nseg, fs,
-                         (uint64_t)rows_capacity);
-    return hip_status();
-  }
-  // one workgroup per tile of the capacity; with no capacity, a resident grid
-  // (the kernel loops over tiles either way)
+  // the table-search path: one workgroup per tile of the capacity; with no
+  // capacity, a resident grid (the kernel loops over tiles either way)
   const size_t tile = (size_t)kExpertBlock * kExpertU;
   const size_t cap_units = rows_capacity * upr;
   size_t g = rows_capacity ? (cap_units + tile - 1) / tile : grid_resident(L);

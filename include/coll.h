@@ -465,6 +465,37 @@ int coll_moe_expert_scale(int nranks, void *const *recvbufs, const int32_t *expe
                           void *stream);
 
 /*
+ * The faster path of coll_moe_expert_scale as two calls, so that its
+ * pre-kernels can run off the critical path: they read only expert_counts,
+ * rdispls and the receive buffers' addresses, not the rows, so a caller can
+ * issue the build (for instance on a second stream) once coll_moe_layout has
+ * completed, while the rows are still being exchanged.
+ *   coll_moe_expert_scale_build: the arguments of coll_moe_expert_scale;
+ *   writes the workspace (the row-prefix table and one descriptor per row of
+ *   recv_rows_capacity, holding the row's address and expert) and touches no
+ *   row.  Returns COLL_ERR_UNSUPPORTED, with nothing launched, where
+ *   coll_moe_expert_scale would not take the faster path (its conditions
+ *   above): call coll_moe_expert_scale then.
+ *   coll_moe_expert_scale_apply: scales the rows from a workspace that a
+ *   build wrote for the same nranks, n_experts, hidden, receive buffers and
+ *   capacity; the rows end as the one-call form leaves them.  The caller
+ *   orders it after the build (same stream, or an event) and after the rows
+ *   have arrived, and does not reuse the workspace until it completes.
+ * Errors: as coll_moe_expert_scale; the apply returns COLL_ERR_INVALID_ARG
+ * for NULL receive buffers, a NULL or misaligned workspace or one below
+ * coll_moe_expert_workspace_bytes(nranks, n_experts, recv_rows_capacity),
+ * and COLL_ERR_UNSUPPORTED where the faster path does not apply.
+ */
+int coll_moe_expert_scale_build(int nranks, void *const *recvbufs, const int32_t *expert_counts,
+                                const int64_t *rdispls, int n_experts, size_t hidden,
+                                coll_dtype_t dtype, size_t recv_rows_capacity,
+                                const int64_t *recv_rows, void *workspace,
+                                size_t workspace_bytes, void *stream);
+int coll_moe_expert_scale_apply(int nranks, void *const *recvbufs, int n_experts, size_t hidden,
+                                coll_dtype_t dtype, size_t recv_rows_capacity, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * Combine (results return to the token's owner and are gate-weighted):
  *   out[s][t] = rne( sum_{k=0..topk-1} w[s][t*topk+k] * widen(back[s][pos[s][t*topk+k]]) )
  * with k ascending, the accumulator seeded by the k = 0 product, multiply and

@@ -323,7 +323,7 @@ def _expert_bad_block(R, E, Hd, recvs, lay, want, rrows):
     """The test expert on tables with one bad (d, s) block -- a negative
     expert count, or a receive displacement that runs past recv[d]: that
     block's rows keep their values, every other row is scaled exactly, on
-    both the row-descriptor path and the table search."""
+    the row-descriptor path (in one call and in two) and the table search."""
     per = E // R
     ec_h = np.array(lay["expert_counts"], np.int32).reshape(R, E)
     rd_h = np.array(lay["rdispls"], np.int64)
@@ -337,15 +337,27 @@ def _expert_bad_block(R, E, Hd, recvs, lay, want, rrows):
             ec2[s0, d0 * per] = -1
         else:
             rd2[d0, s0] = int(rrows[d0]) - n0 + 1
-        for cap in (int(rrows.sum()), 0):
-            case("expert with a bad block", kind, "cap", cap)
+        # the row-descriptor path (capacity known), the table search (0), and
+        # the row-descriptor path in two calls where it applies
+        forms = [(int(rrows.sum()), False), (0, False)]
+        if Hd % 8 == 0 and R * E <= 8192:
+            forms.append((int(rrows.sum()), True))
+        for cap, split in forms:
+            case("expert with a bad block", kind, "cap", cap, "two calls" if split else "")
             ys = [H.copy(r) if r is not None else None for r in recvs]
             ec_b = H.copy(np.ascontiguousarray(ec2).reshape(-1))
             rd_b = H.copy(np.ascontiguousarray(rd2).reshape(-1))
             need = L.coll_moe_expert_workspace_bytes(R, E, cap)
             ews = H.poison(need, np.uint8)
-            ok(L.coll_moe_expert_scale(R, table(ys), ptr(ec_b), ptr(rd_b), E, Hd, BF16, cap,
-                                       rows(rrows), ptr(ews), need, None), "expert, bad block")
+            if split:                                   # the two-call form of that path
+                ok(L.coll_moe_expert_scale_build(R, table(ys), ptr(ec_b), ptr(rd_b), E, Hd, BF16,
+                                                 cap, rows(rrows), ptr(ews), need, None),
+                   "expert build, bad block")
+                ok(L.coll_moe_expert_scale_apply(R, table(ys), E, Hd, BF16, cap, ptr(ews), need,
+                                                 None), "expert apply, bad block")
+            else:
+                ok(L.coll_moe_expert_scale(R, table(ys), ptr(ec_b), ptr(rd_b), E, Hd, BF16, cap,
+                                           rows(rrows), ptr(ews), need, None), "expert, bad block")
             for d in range(R):
                 if not rrows[d]:
                     continue
@@ -609,6 +621,21 @@ def fam_moe():
                 if rrows[d]:
                     same(ys[d].reshape(-1), want["ys"][d].reshape(-1)[:int(rrows[d]) * Hd],
                          f"expert cap {cap}")
+        if Hd % 8 == 0 and R * E <= 8192:
+            # the row-descriptor path in two calls: build, then apply
+            case("expert in two calls (build, then apply)")
+            ys2 = [H.copy(r) if r is not None else None for r in recvs]
+            cap = int(rrows.sum())
+            need = L.coll_moe_expert_workspace_bytes(R, E, cap)
+            ews = H.poison(need, np.uint8)
+            ok(L.coll_moe_expert_scale_build(R, table(ys2), ptr(ec), ptr(rd), E, Hd, BF16, cap,
+                                             rows(rrows), ptr(ews), need, None), "expert build")
+            ok(L.coll_moe_expert_scale_apply(R, table(ys2), E, Hd, BF16, cap, ptr(ews), need,
+                                             None), "expert apply")
+            for d in range(R):
+                if rrows[d]:
+                    same(ys2[d].reshape(-1), want["ys"][d].reshape(-1)[:int(rrows[d]) * Hd],
+                         "expert in two calls")
         _expert_bad_block(R, E, Hd, recvs, lay, want, rrows)
         backs = [H.poison((T * K, Hd), np.uint16) for _ in range(R)]
         sc_t = H.copy(np.ascontiguousarray(lay["sendcounts"].T).reshape(-1))

@@ -413,6 +413,55 @@ def test_plan_keeps_the_arguments_it_was_made_from():
     assert ref() is None
 
 
+def test_moe_expert_split_validation(L):
+    """coll_moe_expert_scale_build / _apply: the row-descriptor path must
+    apply (16-byte rows and buffers, a nonzero capacity, R*E <= 8192, a
+    workspace that holds the descriptors); the apply checks its workspace
+    against the full size.  Nothing is launched in any of these cases."""
+    t = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    cap = 16
+    full = L.coll_moe_expert_workspace_bytes(2, 4, cap)
+    table = L.coll_moe_expert_workspace_bytes(2, 4, 0)
+    assert full > table > 0
+    b = L.coll_moe_expert_scale_build
+    a = L.coll_moe_expert_scale_apply
+    # the path does not apply: no capacity, rows of 5 bf16, a workspace of the
+    # tables alone, a buffer off 16-byte alignment
+    assert b(2, t, 0x100, 0x200, 4, 8, 0, 0, NULL, 0x1000, full, NULL) == -2
+    assert b(2, t, 0x100, 0x200, 4, 5, 0, cap, NULL, 0x1000, full, NULL) == -2
+    assert b(2, t, 0x100, 0x200, 4, 8, 0, cap, NULL, 0x1000, table, NULL) == -2
+    m = (ctypes.c_void_p * 2)(0x1000, 0x2008)
+    assert b(2, m, 0x100, 0x200, 4, 8, 0, cap, NULL, 0x1000, full, NULL) == -2
+    assert a(2, t, 4, 8, 0, 0, 0x1000, full, NULL) == -2
+    assert a(2, t, 4, 5, 0, cap, 0x1000, full, NULL) == -2
+    assert a(2, m, 4, 8, 0, cap, 0x1000, full, NULL) == -2
+    # R * E above the LDS table (16 x 1024 entries)
+    t16 = (ctypes.c_void_p * 16)(*[0x100000 * (r + 1) for r in range(16)])
+    big = L.coll_moe_expert_workspace_bytes(16, 1024, cap)
+    assert b(16, t16, 0x100, 0x200, 1024, 8, 0, cap, NULL, 0x1000, big, NULL) == -2
+    assert a(16, t16, 1024, 8, 0, cap, 0x1000, big, NULL) == -2
+    # bf16 only
+    assert b(2, t, 0x100, 0x200, 4, 8, 2, cap, NULL, 0x1000, full, NULL) == -2
+    assert a(2, t, 4, 8, 2, cap, 0x1000, full, NULL) == -2
+    # workspace NULL, misaligned or below the size; the apply needs the full size
+    assert b(2, t, 0x100, 0x200, 4, 8, 0, cap, NULL, NULL, full, NULL) == -1
+    assert b(2, t, 0x100, 0x200, 4, 8, 0, cap, NULL, 0x1010, full, NULL) == -1
+    assert a(2, t, 4, 8, 0, cap, NULL, full, NULL) == -1
+    assert a(2, t, 4, 8, 0, cap, 0x1010, full, NULL) == -1
+    assert a(2, t, 4, 8, 0, cap, 0x1000, full - 1, NULL) == -1
+    # bad ranks or experts; NULL tables (build) or receive buffers
+    assert b(17, t, 0x100, 0x200, 4, 8, 0, cap, NULL, 0x1000, full, NULL) == -1
+    assert a(2, t, 3, 8, 0, cap, 0x1000, full, NULL) == -1
+    assert b(2, t, NULL, 0x200, 4, 8, 0, cap, NULL, 0x1000, full, NULL) == -1
+    assert b(2, t, 0x100, NULL, 4, 8, 0, cap, NULL, 0x1000, full, NULL) == -1
+    z = (ctypes.c_void_p * 2)(0x1000, None)
+    assert b(2, z, 0x100, 0x200, 4, 8, 0, cap, NULL, 0x1000, full, NULL) == -1
+    assert a(2, z, 4, 8, 0, cap, 0x1000, full, NULL) == -1
+    # negative receive rows
+    neg = (ctypes.c_int64 * 2)(4, -1)
+    assert b(2, t, 0x100, 0x200, 4, 8, 0, cap, neg, 0x1000, full, NULL) == -1
+
+
 def test_a2av_split_descriptor_form_validation(L):
     """coll_all_to_all_v_ws_build / _reverse_build / _ws_copy: the form must
     apply (capacity from the descriptor threshold up, 16-byte rows), and the

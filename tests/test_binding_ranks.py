@@ -141,3 +141,34 @@ def test_split_descriptor_form_wrappers(issued, name):
     args[-1] = 16
     with pytest.raises(ValueError):
         getattr(coll, name)(*args)
+
+
+def _expert_args(split_rows=T * K):
+    ws = torch.zeros(coll.moe_expert_workspace_bytes(R, E, R * split_rows), dtype=torch.uint8)
+    return [bf(split_rows, H) for _ in range(R)], i32(R * E), i64(R * R), E, H, ws
+
+
+@pytest.mark.parametrize("name,entry", [("moe_expert_scale_build", "coll_moe_expert_scale_build"),
+                                        ("moe_expert_scale_apply", "coll_moe_expert_scale_apply")])
+def test_expert_split_wrappers(issued, name, entry):
+    def build(rows=T * K, ws=None):
+        recvs, ec, rd, e, h, w = _expert_args(rows)
+        w = w if ws is None else ws
+        return [recvs, ec, rd, e, h, w] if name.endswith("build") else [recvs, e, h, w]
+
+    getattr(coll, name)(*build())
+    assert issued == [entry]
+    for delta in (-1, +1):
+        args = build()
+        lst = list(args[0])
+        args[0] = lst[:-1] if delta < 0 else lst + [lst[0]]
+        with pytest.raises(ValueError):
+            getattr(coll, name)(*args)
+    # the row-descriptor path does not apply: a workspace of the tables alone,
+    # or no receive rows at all
+    with pytest.raises(ValueError):
+        getattr(coll, name)(*build(ws=torch.zeros(coll.moe_expert_workspace_bytes(R, E, 0),
+                                                  dtype=torch.uint8)))
+    with pytest.raises(ValueError):
+        getattr(coll, name)(*build(rows=0))
+    assert issued == [entry]

@@ -171,3 +171,62 @@ def test_expert_moe_full_size_paths_agree():
             want = oracle.moe_expert_scale([xr.copy()], one.reshape(-1), np.zeros(1, np.int64),
                                            E, H)[0]
             assert bits_equal(host(a[d][j]).reshape(-1), want.reshape(-1)), (d, j)
+
+
+# the cases the row-descriptor path takes: 16-byte rows, a nonzero capacity
+# (so not the all-empty one), aligned buffers, at most 8192 table entries
+SPLIT_CASES = [c for c in CASES if c[2] % 8 == 0 and c[6] != "zero" and c[4] < 1.0
+               and c[7] == 0 and c[0] * c[1] <= 8192]
+
+
+@pytest.mark.parametrize("R,E,H,maxc,zero_frac,gap,cap,shift", SPLIT_CASES)
+def test_expert_in_two_calls_matches_oracle(R, E, H, maxc, zero_frac, gap, cap, shift):
+    """The row-descriptor path as coll_moe_expert_scale_build on a second
+    stream, issued before the rows are written, then
+    coll_moe_expert_scale_apply once both are done: the same bits as the
+    oracle."""
+    say("expert build/apply", R, E, H, maxc, zero_frac, gap, cap)
+    ec, rd, recvs, total = make_case(R, E, H, maxc, zero_frac, gap, seed=R * 1000 + E + H)
+    want = oracle.moe_expert_scale([r.copy() for r in recvs], ec, rd.reshape(-1), E, H)
+    bufs = [torch.empty(r.shape, dtype=torch.bfloat16, device="cuda") for r in recvs]
+    ptrs = (ctypes.c_void_p * R)(*[b.data_ptr() for b in bufs])
+    ec_d, rd_d = dev(ec), dev(rd.reshape(-1))
+    capv = {"exact": total, "big": 3 * total + 17, "small": max(total // 3, 1)}[cap]
+    wsb = coll.moe_expert_workspace_bytes(R, E, capv)
+    ws = torch.full((wsb,), 0xCD, dtype=torch.uint8, device="cuda")
+    rows = (ctypes.c_int64 * R)(*[r.size // H for r in recvs])
+    L = coll.lib()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rc = L.coll_moe_expert_scale_build(R, ptrs, ec_d.data_ptr(), rd_d.data_ptr(), E, H, 0,
+                                           capv, rows, ws.data_ptr(), wsb, side.cuda_stream)
+    built = torch.cuda.Event()
+    built.record(side)
+    for b, r in zip(bufs, recvs):               # the rows arrive after the build
+        b.copy_(dev(r))
+    torch.cuda.current_stream().wait_event(built)
+    rc2 = L.coll_moe_expert_scale_apply(R, ptrs, E, H, 0, capv, ws.data_ptr(), wsb,
+                                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0 and rc2 == 0
+    for d in range(R):
+        assert bits_equal(host(bufs[d]).reshape(-1), want[d].reshape(-1)), d
+
+
+def test_expert_split_refuses_the_table_search():
+    """Without a workspace for the descriptors the two-call form does not
+    apply: the binding refuses, and the C entry points return
+    COLL_ERR_UNSUPPORTED without launching."""
+    R, E, H = 2, 4, 8
+    ec, rd, recvs, total = make_case(R, E, H, 3, 0.0, 0, 3)
+    bufs = [dev(r) for r in recvs]
+    small = torch.empty(coll.moe_expert_workspace_bytes(R, E, 0), dtype=torch.uint8,
+                        device="cuda")
+    with pytest.raises(ValueError):
+        coll.moe_expert_scale_build(bufs, dev(ec), dev(rd.reshape(-1)), E, H, small)
+    with pytest.raises(ValueError):
+        coll.moe_expert_scale_apply(bufs, E, H, small)
+    ptrs = (ctypes.c_void_p * R)(*[b.data_ptr() for b in bufs])
+    assert coll.lib().coll_moe_expert_scale_apply(R, ptrs, E, H, 0, 0, small.data_ptr(),
+                                                  small.numel(), None) == -2

@@ -141,8 +141,9 @@ def test_graph_replays_fused_moe_pipeline():
 def test_graph_replays_moe_step_with_descriptor_builds_on_a_second_stream():
     """The unfused MoE sequence as the benchmark step runs it: the layout
     marks an event, the permute runs, a second stream waits for that event
-    and builds both exchanges' descriptor tables, the main stream waits for
-    them and runs the two copies around the test expert, then the combine.
+    and builds both exchanges' descriptor tables and the test expert's row
+    descriptors, the main stream waits for them and runs the two copies
+    around the expert's scaling, then the combine.
     Captured once (fork and join by events), replayed with new routing and
     tokens each time.  Each receive buffer holds the most rows any of the
     routings sends it; both directions' capacities (256 MiB and more) are
@@ -172,7 +173,7 @@ def test_graph_replays_moe_step_with_descriptor_builds_on_a_second_stream():
     wsc = torch.empty(coll.all_to_all_v_workspace_bytes(recv, back, H), dtype=torch.uint8,
                       device="cuda")
     assert wsd.numel() > 0 and wsc.numel() > 0
-    ews = torch.empty(coll.moe_expert_workspace_bytes(R, E, R * R * T * K), dtype=torch.uint8,
+    ews = torch.empty(coll.moe_expert_workspace_bytes(R, E, sum(need)), dtype=torch.uint8,
                       device="cuda")
     side = torch.cuda.Stream()
     laid_out, built = torch.cuda.Event(), torch.cuda.Event()
@@ -199,10 +200,11 @@ def test_graph_replays_moe_step_with_descriptor_builds_on_a_second_stream():
         with torch.cuda.stream(side):
             coll.all_to_all_v_build(send, sc, sdd, recv, rdd, H, wsd)
             coll.all_to_all_v_reverse_build(recv, sc, sdd, back, rdd, H, wsc)
+            coll.moe_expert_scale_build(recv, ec, rdd, E, H, ews)
         built.record(side)
         torch.cuda.current_stream().wait_event(built)
         coll.all_to_all_v_copy(send, recv, H, wsd)
-        coll.moe_expert_scale(recv, ec, rdd, E, H, ews)
+        coll.moe_expert_scale_apply(recv, E, H, ews)
         coll.all_to_all_v_copy(recv, back, H, wsc)
         coll.moe_combine(back, pos, w_d, outs)
 
