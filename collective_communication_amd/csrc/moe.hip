@@ -21,10 +21,14 @@
 //   moe_permute   send[s][pos[t,k]] = x[s][t]: each token row is read once and
 //                 written topk times, 16-byte units.
 //   moe_expert_scale  the test expert y = rne(x * (1 + e/256)), in
-//                 place: a one-workgroup table of row prefixes, then one
-//                 workgroup per tile of received units.
-//   moe_combine   one wave per token: topk rows gathered by pos, fp32
-//                 fold k = 0..K-1 of separately rounded products, one RNE.
+//                 place: a one-workgroup table of row prefixes, then either
+//                 one descriptor per received row and one wave per (row,
+//                 1 KiB segment) -- a path that also runs as two calls, the
+//                 descriptors built ahead from the tables alone -- or one
+//                 workgroup per tile of received units searching the table.
+//   moe_combine   one wave per (token, 1 KiB segment): topk rows gathered by
+//                 pos, fp32 fold k = 0..K-1 of separately rounded products,
+//                 one RNE.
 #include "coll_internal.h"
 
 #pragma clang fp contract(off)
