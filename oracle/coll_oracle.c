@@ -35,8 +35,10 @@
  * forms, library routines (numpy / torch casts, concatenate, argsort),
  * invariants from the pages (AllReduce = AllGather after ReduceScatter, Gather
  * after Scatter = identity, A2A-v with transposed counts = identity) and brute
- * force on tiny inputs.  MAX/MIN semantics for NaN and signed zero are parity
- * unpinned: the pages fix none of it.
+ * force on tiny inputs.  The pages fix no MAX/MIN semantics for NaN and
+ * signed zero; these follow the maximum / minimum operations of IEEE 754-2019
+ * (a NaN operand gives NaN, -0 orders below +0), pinned to that standard's
+ * special cases.
  */
 #include <math.h>
 #include <stddef.h>

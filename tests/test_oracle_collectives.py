@@ -151,6 +151,62 @@ def test_allreduce_max_min_match_numpy(dtype):
     assert np.array_equal(get(mn), np.minimum.reduce(ref))
 
 
+# IEEE 754-2019 section 9.6: maximum / minimum propagate a NaN operand and
+# order -0 below +0 (so the result does not depend on operand order).  The
+# pages fix none of this; the oracle follows that standard, and these are its
+# special cases written out value by value.
+_NAN, _INF = float("nan"), float("inf")
+IEEE_2019_CASES = [
+    # rank values, maximum, minimum
+    ([+0.0, -0.0], +0.0, -0.0),
+    ([-0.0, +0.0], +0.0, -0.0),
+    ([-0.0, -0.0], -0.0, -0.0),
+    ([+0.0, +0.0], +0.0, +0.0),
+    ([1.0, _NAN, 2.0], _NAN, _NAN),
+    ([_NAN, 1.0], _NAN, _NAN),
+    ([3.0, _NAN], _NAN, _NAN),
+    ([_INF, _NAN], _NAN, _NAN),
+    ([-_INF, 3.0], 3.0, -_INF),
+    ([-1.5, -0.0, -2.5], -0.0, -2.5),
+    ([-0.0, 0.5, +0.0], 0.5, -0.0),
+]
+
+
+def _same_value(got, want):
+    """Equal as IEEE values, with the sign of zero significant and any NaN
+    matching any NaN (payloads are not fixed)."""
+    if np.isnan(want):
+        return bool(np.isnan(got))
+    return got == want and np.signbit(got) == np.signbit(want)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("vals,mx,mn", IEEE_2019_CASES)
+def test_allreduce_max_min_special_values_follow_ieee754_2019(dtype, vals, mx, mn):
+    xs = [from_f32_lib(np.array([v], np.float32), dtype) for v in vals]
+    got_mx = to_f64(oracle.allreduce(xs, dtype, "max")[0], dtype)[0]
+    got_mn = to_f64(oracle.allreduce(xs, dtype, "min")[0], dtype)[0]
+    assert _same_value(got_mx, mx), (vals, got_mx)
+    assert _same_value(got_mn, mn), (vals, got_mn)
+
+
+def test_allreduce_max_min_propagate_nan_like_numpy():
+    """A NaN anywhere among the ranks gives NaN at that element, as
+    numpy.maximum / numpy.minimum document for a NaN operand; elsewhere the
+    values are numpy's."""
+    g = np.random.default_rng(12)
+    xs = [g.standard_normal(4000).astype(np.float32) for _ in range(5)]
+    for r, x in enumerate(xs):
+        x[g.random(4000) < 0.02] = np.nan
+    ref_mx, ref_mn = np.maximum.reduce(xs), np.minimum.reduce(xs)
+    mx = oracle.allreduce(xs, "fp32", "max")[0]
+    mn = oracle.allreduce(xs, "fp32", "min")[0]
+    assert np.array_equal(np.isnan(mx), np.isnan(ref_mx))
+    assert np.array_equal(np.isnan(mn), np.isnan(ref_mn))
+    ok = ~np.isnan(ref_mx)
+    assert np.array_equal(mx[ok], ref_mx[ok]) and np.array_equal(mn[ok], ref_mn[ok])
+
+
 def test_allreduce_prod_powers_of_two_exact():
     g = np.random.default_rng(3)
     xs = [(2.0 ** g.integers(-6, 7, size=999) * g.choice([-1, 1], size=999)).astype(np.float32)

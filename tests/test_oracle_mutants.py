@@ -42,6 +42,18 @@ MUTANTS = [
     ("max and min swapped",
      "case O_MAX:  return fmax_def(acc, x);", "case O_MAX:  return fmin_def(acc, x);",
      [lambda: C.test_allreduce_max_min_match_numpy("bf16")]),
+    ("max ignores a NaN operand (IEEE 754-2008 maxNum)",
+     "static float fmax_def(float a, float b)\n{\n    if (isnan(a) || isnan(b)) return bits_to_f32(0x7FC00000u);",
+     "static float fmax_def(float a, float b)\n{\n    if (isnan(a)) return b;\n    if (isnan(b)) return a;",
+     [lambda: C.test_allreduce_max_min_propagate_nan_like_numpy()]),
+    ("max of equal zeros keeps the first operand",
+     "if (a == b) return signbit(a) ? b : a;", "if (a == b) return a;",
+     [lambda: C.test_allreduce_max_min_special_values_follow_ieee754_2019(
+         "fp32", [-0.0, +0.0], +0.0, -0.0)]),
+    ("min of equal zeros keeps the first operand",
+     "if (a == b) return signbit(a) ? a : b;", "if (a == b) return a;",
+     [lambda: C.test_allreduce_max_min_special_values_follow_ieee754_2019(
+         "fp32", [+0.0, -0.0], +0.0, -0.0)]),
     ("ReduceScatter chunk index transposed",
      "reduce_element(R, in, (size_t)r * recvcount + i, out[r], i, dt, op);",
      "reduce_element(R, in, i * (size_t)R + (size_t)r, out[r], i, dt, op);",
