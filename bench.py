@@ -480,11 +480,17 @@ def _graph_time(torch, fn, sets, n=24, reps=4):
 
 def copy_ceiling(torch, coll, W):
     """Practical HBM ceiling of this GPU: a plain 1 GiB -> 1 GiB copy through
-    the library's copy kernel (2 GiB moved), graph-timed."""
+    the library's copy kernel (2 GiB moved), graph-timed; beside it the same
+    copy by the HIP runtime's own device-to-device copy (torch's copy_ of one
+    contiguous tensor into another), for comparison."""
     t = _graph_time(torch, lambda i: coll.broadcast(W["copy_src"], W["copy_dst"], 0), 1,
                     n=8, reps=2)
     gbs = (2 << 30) / t / 1e9
-    return {"us": round(t * 1e6, 2), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    tr = _graph_time(torch, lambda i: W["copy_dst"][0].copy_(W["copy_src"]), 1, n=8, reps=2)
+    gbr = (2 << 30) / tr / 1e9
+    return {"us": round(t * 1e6, 2), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "runtime_copy_us": round(tr * 1e6, 2), "runtime_copy_GBps": round(gbr, 1),
+            "runtime_copy_frac": round(gbr / HBM_PEAK_GBS, 4)}
 
 
 def latency_rows_graph(torch, coll, W, per_row_us):
@@ -856,6 +862,10 @@ def report(path):
     if d.get("copy_ceiling_1gib"):
         c = d["copy_ceiling_1gib"]
         ex.append(f"| plain 1 GiB copy (graph) | {c['us']} µs, {c['GBps']} GB/s = {_as_pct(c['frac'])} |")
+        if "runtime_copy_us" in c:
+            ex.append(f"| the same copy by the HIP runtime's device-to-device copy (graph) | "
+                      f"{c['runtime_copy_us']} µs, {c['runtime_copy_GBps']} GB/s = "
+                      f"{_as_pct(c['runtime_copy_frac'])} |")
     if d.get("allreduce_16mib_layout_ab"):
         a = d["allreduce_16mib_layout_ab"]
         ex.append(f"| AllReduce 16 MiB × 8, torch allocations vs rank arena | "

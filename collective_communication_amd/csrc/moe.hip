@@ -357,7 +357,7 @@ __global__ __launch_bounds__(64 * kPermuteWaves) void moe_permute_kernel(PtrTabl
 // of them.  Numbering every received row of every rank in entry order (global
 // row g) balances the work over ranks however skewed the routing is.
 //
-// moe_expert_table: one 1024-thread workgroup writes two int64 tables:
+// moe_expert_table: one workgroup of kTableThreads writes two int64 tables:
 //   s_end[j] = rows in entries 0..j (inclusive prefix), so g is in entry j
 //              iff s_end[j-1] <= g < s_end[j];
 //   rb[j]    = rdispls[d*R+s] - (rows in entries before (d, s)'s first),
@@ -365,8 +365,8 @@ __global__ __launch_bounds__(64 * kPermuteWaves) void moe_permute_kernel(PtrTabl
 // A (d, s) block with a negative expert count, or whose rows do not all lie
 // inside recv[d] (recv_rows), counts as empty: no row of it is numbered, so
 // the kernels that follow never address it and its rows keep their values.
-// Inclusive scan over the workgroup's 1024 threads (entries in thread order);
-// returns the exclusive prefix of the thread's `local`.
+// Inclusive scan over the workgroup's threads (at most 1024; entries in thread
+// order); returns the exclusive prefix of the thread's `local`.
 __device__ __forceinline__ int64_t table_scan(int64_t local, int64_t *wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int64_t incl = local;
@@ -391,7 +391,20 @@ __device__ __forceinline__ int64_t entry_count(const int32_t *expert_counts, int
   return (int64_t)expert_counts[(size_t)s * E + d * per + el];
 }
 
-__global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_counts,
+// Threads of the table's one workgroup.  256, the size of the permute's
+// workgroups: the table is built on a second stream while the permute fills
+// the GPU, and there a 1024-thread workgroup waited for 16 free wave slots on
+// one CU for 13 to 612 us (MI355X, the MoE step), where a 256-thread one
+// takes the first slot a permute workgroup frees.
+#ifndef COLL_EXPERT_TABLE_THREADS
+#define COLL_EXPERT_TABLE_THREADS 256
+#endif
+constexpr int kTableThreads = COLL_EXPERT_TABLE_THREADS;
+static_assert(kTableThreads >= COLL_MAX_RANKS * COLL_MAX_RANKS && kTableThreads <= 1024 &&
+                  kTableThreads % 64 == 0,
+              "one thread per (d, s) block, at most 16 waves");
+
+__global__ __launch_bounds__(kTableThreads) void moe_expert_table(const int32_t *expert_counts,
                                                          const int64_t *rdispls, int R, int E,
                                                          RankRows recv_rows, int64_t *s_end,
                                                          int64_t *rb) {
@@ -405,7 +418,7 @@ __global__ __launch_bounds__(1024) void moe_expert_table(const int32_t *expert_c
   __shared__ int s_bad;
   const int per = E / R;
   const int N = R * E;
-  const int chunk = (N + 1023) / 1024;           // <= 16 (R <= 16, E <= 1024)
+  const int chunk = (N + kTableThreads - 1) / kTableThreads;   // <= 2^14 / kTableThreads
   const int j0 = (int)threadIdx.x * chunk;
   // 1. the scan of the counts (a negative one as kNeg) is the table when every
   //    block fits, the usual case; it also gives each block's total (and
@@ -1158,7 +1171,7 @@ int launch_moe_expert_build(const Launch &L, int R, const MutPtrTable &recv,
   const int N = R * E;
   int64_t *s_end = reinterpret_cast<int64_t *>(ws);
   int64_t *rb = s_end + N;
-  hipLaunchKernelGGL(moe_expert_table, dim3(1), dim3(1024), 0, L.stream, expert_counts, rdispls,
+  hipLaunchKernelGGL(moe_expert_table, dim3(1), dim3(kTableThreads), 0, L.stream, expert_counts, rdispls,
                      R, E, recv_rows, s_end, rb);
   uint64_t *rdesc =
       reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + moe_expert_table_bytes(R, E));
@@ -1207,7 +1220,7 @@ int launch_moe_expert_scale(const Launch &L, int R, const MutPtrTable &recv,
   const int N = R * E;
   int64_t *s_end = reinterpret_cast<int64_t *>(ws);
   int64_t *rb = s_end + N;
-  hipLaunchKernelGGL(moe_expert_table, dim3(1), dim3(1024), 0, L.stream, expert_counts, rdispls,
+  hipLaunchKernelGGL(moe_expert_table, dim3(1), dim3(kTableThreads), 0, L.stream, expert_counts, rdispls,
                      R, E, recv_rows, s_end, rb);
   int top = 1;
   while (top * 64 < N) top *= 64;
