@@ -51,6 +51,15 @@ constexpr int kA2aBlock = COLL_A2A_BLOCK;
 #ifndef COLL_A2A_SMALL
 #define COLL_A2A_SMALL 1
 #endif
+// Resident workgroups per CU of the chunk kernel (the 16-byte kernels keep 4).
+// MI355X, R = 8, rows of one bf16, graph replay: 8 / 16 / 32 MiB per rank
+// 26.1 / 48.6 / 92.9 us with 4, 25.7 / 47.6 / 91.4 with 5, 25.6 / 47.6 /
+// 91.2 with 6, 25.4 / 48.2 / 91.7 with 7; with 8, 12 and 16 the 16 / 32 MiB
+// launches took 54.6 / 105.7, 49.7 / 96.2 and 50.0 / 94.8 us.  The 16-byte
+// resident kernel lost 4% with 6 (48.0 -> 50.1 us at 16 MiB).
+#ifndef COLL_A2A_CHUNK_RES_PER_CU
+#define COLL_A2A_CHUNK_RES_PER_CU 6
+#endif
 // 1: ... and the chunk kernel (rows not in 16-byte units) likewise.  MI355X,
 // R = 8, rows of one bf16, graph replay: 8 KiB / 1 MiB / 16 / 64 MiB per
 // rank 4.1 / 5.8 / 48.4 / 181.0 us against 5.1 / 6.9 / 49.4 / 184.4 us with
@@ -762,9 +771,11 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
                              counts, sdispls, rdispls, ct, row_units);
   } else {
     // chunks: at most capacity bytes / 16 plus one partial chunk per block
+    const unsigned g_res_c = (unsigned)L.num_cus * COLL_A2A_CHUNK_RES_PER_CU;
+    g = g_res_c;
     if (rows_capacity > 0) {
       const unsigned g1 = grid_for(L, (cap_bytes + 15) / 16 + (uint64_t)R * R, kA2aU);
-      g = resident ? (g1 < g_res ? g1 : g_res) : g1;
+      g = resident ? (g1 < g_res_c ? g1 : g_res_c) : g1;
     }
     if (L.a2a_grid > 0) g = (unsigned)L.a2a_grid;
 #define COLL_A2A_CHUNK_B(NTV, UNV, FASTV, BPLV)                                                  \
