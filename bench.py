@@ -427,9 +427,10 @@ def _pct(ts, q):
 def _launch_times(torch, fn, sets, iters, pcts=None):
     """(median of per-launch event pairs, mean over one event pair around
     `iters` back-to-back launches), seconds; launch i uses buffer set i % sets.
+    At least 5 warm-up launches come first, every buffer set at least once.
     If `pcts` is a dict, the p10 / p90 of the per-launch times go into it."""
-    for i in range(sets):
-        fn(i)
+    for i in range(max(sets, 5)):
+        fn(i % sets)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
