@@ -61,7 +61,7 @@ constexpr int kMoeTile = 1024;        // ids per layout tile (kBlock * 4)
 #define COLL_COMBINE_RECV_U 2
 #endif
 // Row items (one wave each) per workgroup; MI355X, 4096 x 7168 x top-8:
-// permute 4 -> 779 us, 2 -> 810, 1 -> 872; fused dispatch 4 -> 766, 2 -> 761,
+// permute 16 -> 878 us, 8 -> 840, 4 -> 779, 2 -> 810, 1 -> 872; fused dispatch 4 -> 766, 2 -> 761,
 // 1 -> 786; combine 4 -> 742, 2 -> 730, 1 -> 718; fused combine 4 -> 763,
 // 2 -> 760, 1 -> 744.
 #ifndef COLL_PERMUTE_WAVES
