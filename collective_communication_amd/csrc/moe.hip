@@ -835,8 +835,8 @@ __device__ __forceinline__ int64_t recv_row_of(const SrcBlocks &b, int R, int64_
   return 0;
 }
 
-// The fused combine (one wave per workgroup): lane q < R of a wave holds
-// block q of source s: its send slots [lo, hi), the offset from a slot to its
+// The fused combine and dispatch: lane q < R of a wave holds block q of
+// source s: its send slots [lo, hi), the offset from a slot to its
 // receive row (rdispls[q][s] - lo) and rank q's receive buffer; the other
 // lanes hold an empty block.  Loaded per wave from clamped indices (no LDS,
 // no barrier), so locating a slot is one ballot and two lane reads, with no
@@ -850,6 +850,15 @@ struct SrcLane {
 
 // (a block whose receive rows do not all lie inside rank q's buffer is held
 // empty, as in load_src_blocks)
+// 1: the fused dispatch locates slots like the fused combine (lane-held
+// blocks, one ballot per slot) instead of scanning blocks staged in LDS
+// (MI355X, the MoE shape: 785-787 against 792-800 us)
+#ifndef COLL_DISPATCH_LANE
+#define COLL_DISPATCH_LANE 1
+#endif
+#ifndef COLL_SRC_LANE_SCALAR
+#define COLL_SRC_LANE_SCALAR 1
+#endif
 template <class Table>
 __device__ __forceinline__ SrcLane load_src_lane(int R, int s, const Table &recv,
                                                  const int64_t *sendcounts,
@@ -858,13 +867,44 @@ __device__ __forceinline__ SrcLane load_src_lane(int R, int s, const Table &recv
                                                  const RankRows &recv_rows) {
   const int q = threadIdx.x & 63;
   const int qq = q < R ? q : 0;
+#if COLL_SRC_LANE_SCALAR
+  // The entries are the same for the whole workgroup (its source s): they
+  // come in through the scalar cache, entry i pinned in scalar registers
+  // (clamped index, so every load is unconditional), and lane q selects
+  // entry q.  Loaded per lane, they were a vector round trip before any row
+  // could be addressed.
+  int64_t a = 0, c = 0, r = 0;
+#pragma unroll
+  for (int i = 0; i < COLL_MAX_RANKS; i++) {
+    const int ii = i < R ? i : 0;
+    int64_t ai = sdispls[s * R + ii], ci = sendcounts[s * R + ii], ri = rdispls[ii * R + s];
+    COLL_SCALAR(ai);
+    COLL_SCALAR(ci);
+    COLL_SCALAR(ri);
+    a = qq == i ? ai : a;
+    c = qq == i ? ci : c;
+    r = qq == i ? ri : r;
+  }
+#else
   const int64_t a = sdispls[s * R + qq], c = sendcounts[s * R + qq], r = rdispls[qq * R + s];
+#endif
   const bool ok = q < R && block_fits(c, a, r, INT64_MAX, pick_rows(recv_rows, qq));
   SrcLane b;
   b.lo = ok ? a : 1;
   b.hi = ok ? a + c : 0;
   b.off = r - a;
+#if COLL_SRC_LANE_SCALAR
+  uint64_t base = 0;
+#pragma unroll
+  for (int i = 0; i < COLL_MAX_RANKS; i++) {
+    uint64_t bi = reinterpret_cast<uintptr_t>(recv.p[i]);
+    COLL_SCALAR(bi);
+    base = qq == i ? bi : base;
+  }
+  b.base = base;
+#else
   b.base = reinterpret_cast<uintptr_t>(recv.p[qq]);
+#endif
   return b;
 }
 
@@ -890,21 +930,23 @@ __device__ __forceinline__ int64_t recv_row_lane(const SrcLane &b, int64_t slot,
 // permute and the exchange in one pass (each token row read once, written K
 // times straight into its destination's receive buffer).
 template <int B, bool NT>
-__global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(PtrTable x, PtrTable pos,
-                                                              MutPtrTable recv,
-                                                              const int64_t *sendcounts,
-                                                              const int64_t *sdispls,
-                                                              const int64_t *rdispls,
-                                                              RankRows recv_rows, int R,
-                                                              int T, int K, uint32_t upr,
-                                                              int nseg) {
+__global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(
+    PtrTable x, PtrTable pos, MutPtrTable recv, const int64_t *__restrict__ sendcounts,
+    const int64_t *__restrict__ sdispls, const int64_t *__restrict__ rdispls, RankRows recv_rows,
+    int R, int T, int K, uint32_t upr, int nseg) {
   using U = typename UnitT<B>::T;
   constexpr int UN = kPermuteU;
-  __shared__ SrcBlocks blk;
   const int s = blockIdx.y;
+#if COLL_DISPATCH_LANE
+  const RowItem it = row_item<kDispatchWaves>(T, nseg);
+  if (!it.valid) return;
+  const SrcLane bl = load_src_lane(R, s, recv, sendcounts, sdispls, rdispls, recv_rows);
+#else
+  __shared__ SrcBlocks blk;
   load_src_blocks(blk, R, s, sendcounts, sdispls, rdispls, recv_rows);
   const RowItem it = row_item<kDispatchWaves>(T, nseg);
   if (!it.valid) return;
+#endif
   const int lane = threadIdx.x & 63;
   const U *src = reinterpret_cast<const U *>(x.p[s]) + (size_t)it.t * upr;
   const int32_t *pk = reinterpret_cast<const int32_t *>(pos.p[s]) + (size_t)it.t * K;
@@ -924,10 +966,17 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(PtrTa
     for (int c = 0; c < kSlotChunk; c++) {
       if (k0 + c >= K) break;
       int d;
+#if COLL_DISPATCH_LANE
+      uint64_t bp;
+      const int64_t row = recv_row_lane(bl, sl[c], d, bp);
+      if (d < 0 || bp == 0) continue;     // no block holds the slot / a rank receiving nothing
+      U *base = reinterpret_cast<U *>(bp);
+#else
       const int64_t row = recv_row_of(blk, R, sl[c], d);
       if (d < 0) continue;                                   // never write outside
       U *base = reinterpret_cast<U *>(recv.p[__builtin_amdgcn_readfirstlane(d)]);
       if (!base) continue;                                   // a rank that receives nothing
+#endif
       U *dst = base + (size_t)row * upr;
 #pragma unroll
       for (int u = 0; u < UN; u++) {
@@ -949,8 +998,9 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(PtrTa
 template <int G, bool NT, bool EXPERT>
 __global__ __launch_bounds__(64 * kCombineRecvWaves) void moe_combine_recv_kernel(
     PtrTable recv, PtrTable pos, PtrTable wts, PtrTable ids, MutPtrTable out,
-    const int64_t *sendcounts, const int64_t *sdispls, const int64_t *rdispls, RankRows recv_rows,
-    int R, int T, int K, uint32_t upr, int nseg) {
+    const int64_t *__restrict__ sendcounts, const int64_t *__restrict__ sdispls,
+    const int64_t *__restrict__ rdispls, RankRows recv_rows, int R, int T, int K, uint32_t upr,
+    int nseg) {
   constexpr int kChunk = 8;
   constexpr int UN = (G == 8) ? kCombineRecvU : 1;
   const int s = blockIdx.y;
