@@ -383,6 +383,18 @@ template <> struct UnitT<1> { typedef uint8_t T; };
 #define COLL_SCALAR(x) asm volatile("" : "+s"(x))
 #endif
 
+// ld_scalar(p, i): p[i] for an address uniform across the wave, from memory
+// the kernel never writes, read through the scalar cache (the constant
+// address space).  Vector stores and loads share one in-order counter on
+// this GPU, so a vector load issued after stores can only be waited on by
+// waiting for those stores too; a scalar load has a counter of its own.
+#ifndef COLL_HAVE_LD_SCALAR
+template <class T>
+__device__ __forceinline__ T ld_scalar(const T *p, size_t i) {
+  return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+#endif
+
 // rows.n[i] for a lane-dependent i: a select chain over the table, which the
 // kernel loads through the scalar unit.  Indexed directly, the by-value table
 // becomes a vector load from the argument segment per lane, a round trip the

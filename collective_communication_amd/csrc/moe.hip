@@ -330,9 +330,14 @@ __global__ __launch_bounds__(64 * kPermuteWaves) void moe_permute_kernel(PtrTabl
     const uint32_t x_u = u0 + u * 64;
     if (x_u < upr) v[u] = NT ? __builtin_nontemporal_load(src + x_u) : src[x_u];
   }
-  // One slot at a time: each slot's scalar load overlaps the previous slot's
-  // stores.  Loading a chunk of slots first (as the other MoE kernels do)
-  // measured 9% slower here (848 vs 777 us at the MoE shape).  A row form --
+  // One slot at a time, each slot read by a vector load issued after the
+  // previous slot's stores.  Vector loads and stores share one in-order
+  // counter, so the wave waits for those stores before it stores again: at
+  // most one slot (1 KiB) of stores per wave in flight, and the fan-out
+  // runs faster that way.  Loading a chunk of slots first (as the other MoE
+  // kernels do) measured 9% slower here (848 vs 777 us at the MoE shape), and
+  // reading each slot through the scalar cache, which leaves all K slots'
+  // stores in flight, 10% slower (855-863 vs 779-783 us).  A row form --
   // one workgroup per token, wave k writing slot k's whole 14 KiB row in one
   // run from cacheable loads of the token row -- measured 835 against 785 us.
   for (int k = 0; k < K; k++) {
@@ -961,7 +966,8 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(
     int32_t sl[kSlotChunk];
 #pragma unroll
     for (int c = 0; c < kSlotChunk; c++)
-      sl[c] = __builtin_amdgcn_readfirstlane(pk[k0 + c < K ? k0 + c : K - 1]);
+      // through the scalar cache: 778-781 against 786-789 us with vector loads
+      sl[c] = ld_scalar(pk, (size_t)(k0 + c < K ? k0 + c : K - 1));
 #pragma unroll
     for (int c = 0; c < kSlotChunk; c++) {
       if (k0 + c >= K) break;

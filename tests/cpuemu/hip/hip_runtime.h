@@ -33,6 +33,11 @@
 #define COLL_OPAQUE(x) ((void)0)
 #define COLL_KEEP(x) ((void)0)
 #define COLL_SCALAR(x) ((void)0)
+// ld_scalar: the GPU reads through the scalar cache, which needs the address
+// to be the same in every lane; here it is a plain load, after checking that
+// every active lane asks for the same address (defined below emu_uniform_at)
+#define COLL_HAVE_LD_SCALAR 1
+#define ld_scalar(p, i) emu_ld_scalar((p), (size_t)(i), __FILE__, __LINE__)
 #define COLL_UNIFORM(x) emu_uniform_at(emu_bits(x), __FILE__, __LINE__)
 
 // ------------------------------------------------------------- runtime types
@@ -116,6 +121,12 @@ static inline int emu_readfirstlane_at(int v, const char *f, int l) {
 }
 static inline void emu_uniform_at(uint64_t bits, const char *f, int l) {
   (void)emu_wave_op(EMU_UNIFORM, bits, 0, f, l);
+}
+
+template <class T>
+static inline T emu_ld_scalar(const T *p, size_t i, const char *f, int l) {
+  emu_uniform_at((uint64_t)(uintptr_t)(p + i), f, l);
+  return p[i];
 }
 static inline int emu_readlane_at(int v, int lane, const char *f, int l) {
   return (int)emu_wave_op(EMU_READLANE, (uint32_t)v, lane, f, l);
