@@ -982,6 +982,7 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(
       if (d < 0) continue;                                   // never write outside
       U *base = reinterpret_cast<U *>(recv.p[__builtin_amdgcn_readfirstlane(d)]);
       if (!base) continue;                                   // a rank that receives nothing
+#endif
       U *dst = base + (size_t)row * upr;
 #pragma unroll
       for (int u = 0; u < UN; u++) {
@@ -993,7 +994,6 @@ __global__ __launch_bounds__(64 * kDispatchWaves) void moe_dispatch_kernel(
       }
     }
   }
-#endif
 }
 
 // out[s][t] = rne(fold_k w[t,k] * widen(y_k)), y_k the receive row of (s,t,k)
