@@ -494,6 +494,31 @@ def copy_ceiling(torch, coll, W):
             "runtime_copy_frac": round(gbr / HBM_PEAK_GBS, 4)}
 
 
+def fanout_ceiling(torch, coll):
+    """The 1 -> 8 fan-out pattern alone, at the MoE permute's volume: the
+    library's Broadcast from one 448 MiB buffer to 8 others (4096 tokens x
+    7168 bf16 x 8 sources read once, 3.5 GiB written), graph-timed.  Its
+    destinations are contiguous, so it is the permute's pattern without the
+    row scatter; the outputs are checked against the source."""
+    E, T, K, H = 256, 4096, 8, 7168
+    n = T * H * R
+    bufs = coll.rank_arena([(R + 1, n, torch.bfloat16)])[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(91)
+    bufs[0].copy_(torch.randn(n, generator=g, device="cuda"))
+    bc = coll.prepare(coll.broadcast, bufs[0], bufs, 0)
+    bc()
+    torch.cuda.synchronize()
+    ok = all(torch.equal(b.view(torch.int16), bufs[0].view(torch.int16)) for b in bufs[1:])
+    t = _graph_time(torch, lambda i: bc(), 1, n=8, reps=3)
+    nb = (R + 1) * n * 2
+    del bufs, bc
+    torch.cuda.empty_cache()
+    return {"read_bytes": n * 2, "written_bytes": R * n * 2, "us": round(t * 1e6, 2),
+            "GBps": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
+            "outputs_equal_source": bool(ok)}
+
+
 def latency_rows_graph(torch, coll, W, per_row_us):
     """The latency-bound rows of the step: HIP-graph replay beside the eager
     costs.  `eager_prepared_us` is one back-to-back prepared call (a decode
@@ -867,6 +892,10 @@ def report(path):
             ex.append(f"| the same copy by the HIP runtime's device-to-device copy (graph) | "
                       f"{c['runtime_copy_us']} µs, {c['runtime_copy_GBps']} GB/s = "
                       f"{_as_pct(c['runtime_copy_frac'])} |")
+    if d.get("fanout_ceiling_1to8"):
+        f = d["fanout_ceiling_1to8"]
+        ex.append(f"| 1 → 8 fan-out at the permute's volume (Broadcast, 448 MiB to 8 buffers, graph) | "
+                  f"{f['us']} µs, {f['GBps']} GB/s = {_as_pct(f['frac'])} |")
     if d.get("allreduce_16mib_layout_ab"):
         a = d["allreduce_16mib_layout_ab"]
         ex.append(f"| AllReduce 16 MiB × 8, torch allocations vs rank arena | "
@@ -1008,7 +1037,7 @@ def main():
                       "frac": round(step_bytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del g
 
-    fused = lat = ceil_ = None
+    fused = lat = ceil_ = fan = None
     if not args.only:
         print("[bench] fused MoE path", file=sys.stderr, flush=True)
         fused = moe_fused(torch, coll, W, {n: rows_out[n]["us"] for n in names})
@@ -1016,6 +1045,7 @@ def main():
             print("[bench] latency rows by graph replay", file=sys.stderr, flush=True)
             lat = latency_rows_graph(torch, coll, W, {n: rows_out[n]["us"] for n in names})
             ceil_ = copy_ceiling(torch, coll, W)
+            fan = fanout_ceiling(torch, coll)
 
     ab = extra = None
     if not args.no_sweep and not args.only:
@@ -1055,6 +1085,7 @@ def main():
         "moe_fused": fused,
         "latency_rows_graph": lat,
         "copy_ceiling_1gib": ceil_,
+        "fanout_ceiling_1to8": fan,
     }
     print(json.dumps(out))
 
