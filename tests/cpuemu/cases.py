@@ -450,6 +450,14 @@ def fam_a2av():
             _a2av_case(R, g.integers(lo, hi, size=(R, R)), W, "bf16", cap=cap)
     case("a2av long uniform blocks of one-bf16 rows (the aligned chunk path)")
     _a2av_case(8, np.full((8, 8), 2048), 1, "bf16", cap=0)
+    # 257 chunks per block: whole tiles, then one that reaches the total
+    case("a2av aligned chunk path with a last partial tile")
+    _a2av_case(8, np.full((8, 8), 2056), 1, "bf16", cap=0)
+    _a2av_case(3, np.full((3, 3), 1000), 1, "bf16", cap=0)
+    # small enough for the resident grid: 63 chunks per block, 7 whole tiles
+    # and a partial one
+    for cap in (0, None):
+        _a2av_case(8, np.full((8, 8), 504), 1, "bf16", cap=cap)
     for R, W in ((8, 8), (4, 5), (3, 24), (16, 8), (8, 64), (16, 64)):
         for ws in (False, True):
             case("a2av tables that name rows outside the buffers", R, W, "ws" if ws else "plain")
