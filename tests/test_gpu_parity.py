@@ -272,7 +272,7 @@ def test_broadcast(R, n, dtype, root):
 
 # ------------------------------------------------------------- All-to-All-v
 
-def a2av_case(R, W, dtype, counts, gap=0, seed=0, ws=False):
+def a2av_case(R, W, dtype, counts, gap=0, seed=0, ws=False, cap=None):
     sd, rd = oracle.packed_displs(counts)
     if gap:                                  # spread receive blocks apart
         rd = rd + gap * np.arange(R, dtype=np.int64)[None, :]
@@ -286,7 +286,7 @@ def a2av_case(R, W, dtype, counts, gap=0, seed=0, ws=False):
     want = oracle.all_to_all_v(xs, counts, sd, rd, [max(int(v), 1) for v in recv_rows], W,
                                recvs=[a.copy() for a in init])
     dc = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int64).reshape(-1)).cuda()
-    work = cap = None
+    work = None
     if ws:                                   # the descriptor form (when it applies)
         # a capacity bound at the form's 192 MiB threshold (it sizes the
         # launch only), so that these small exchanges take the form too
@@ -313,6 +313,24 @@ def test_a2av_random_counts(R, W, dtype, ws):
     recvs, want, _, _ = a2av_case(R, W, dtype, counts, seed=R + W, ws=ws)
     for d in range(R):
         assert bits_equal(host(recvs[d]), want[d]), f"dest {d}"
+
+
+@pytest.mark.parametrize("R,W,dtype", [(2, 8, "bf16"), (8, 8, "bf16"), (8, 7168, "bf16"),
+                                     (3, 4, "fp32"), (16, 8, "bf16")])
+def test_a2av_one_pass_grid_ragged_total(R, W, dtype):
+    """The plain form's one-pass grid (chosen above 256 MiB of receive
+    capacity; the capacity only sizes the launch) on small random exchanges:
+    whole tiles, then the tile that reaches the total, then surplus
+    workgroups with nothing to move."""
+    say("a2av one-pass ragged", R, W, dtype)
+    g = np.random.default_rng(7000 + R * 10 + W)
+    hi = 6 if W > 1000 else 3000
+    counts = g.integers(0, hi, size=(R, R)).astype(np.int64)
+    row_bytes = W * (2 if dtype == "bf16" else 4)
+    cap = (256 << 20) // row_bytes + 4096
+    recvs, want, _, _ = a2av_case(R, W, dtype, counts, seed=R + W, cap=cap)
+    for d in range(R):
+        assert bits_equal(host(recvs[d]), want[d]), f"rank {d}"
 
 
 def test_a2av_gapped_receive_layout_keeps_poison():
