@@ -380,6 +380,56 @@ __global__ __launch_bounds__(kBlock) void a2av_res_kernel8(RankPtrs p, RowLimits
   a2av_body<B, NT, kA2aResU, kBlock, true, false>(p, lim, R, counts, sdispls, rdispls, ct, row_units);
 }
 
+// One tile of the chunk kernel's all-aligned path on the one-pass grid: UN
+// 16-byte chunks per lane, located, loaded, then stored.  FULL: every chunk
+// lies inside the total, so no load or store sits in a branch (a2av_tile).
+template <bool NT, int UN, bool FULL>
+__device__ __forceinline__ void chunk_vec_tile(uint64_t wbase, int lane, uint64_t total, int nb,
+                                               int top, bool wl, uint64_t my_end,
+                                               uint64_t my_src, uint64_t my_dst,
+                                               const uint64_t *s_end, const uint64_t *s_src,
+                                               const uint64_t *s_dst, uint64_t &blo,
+                                               uint64_t &bhi, uint64_t &sbase, uint64_t &dbase) {
+  const uint64_t base = wbase + lane;
+  u32x4 v[UN];
+  uint64_t da[UN];
+#pragma unroll
+  for (int u = 0; u < UN; u++) {
+    const uint64_t x = base + (uint64_t)u * kBlock;
+    int wlo;
+    if (wl && wave_block(my_end, wbase + (uint64_t)u * kBlock, wlo)) {
+      blo = wlo > 0 ? readlane64(my_end, wlo - 1) : 0;
+      bhi = readlane64(my_end, wlo);
+      sbase = readlane64(my_src, wlo) - blo * 16;
+      dbase = readlane64(my_dst, wlo) - blo * 16;
+    }
+    if (FULL || x < total) {
+      if (x < blo || x >= bhi) {
+        int lo = 0;
+        for (int step = top; step > 0; step >>= 1) {
+          const int c = lo + step;
+          if (c <= nb && s_end[c - 1] <= x) lo = c;
+        }
+        blo = lo > 0 ? s_end[lo - 1] : 0;
+        bhi = s_end[lo];
+        sbase = s_src[lo] - blo * 16;
+        dbase = s_dst[lo] - blo * 16;
+      }
+      da[u] = dbase + x * 16;
+      if constexpr (NT) v[u] = __builtin_nontemporal_load(gconst<u32x4>(sbase + x * 16));
+      else v[u] = *gconst<u32x4>(sbase + x * 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UN; u++) {
+    const uint64_t x = base + (uint64_t)u * kBlock;
+    if (FULL || x < total) {
+      if constexpr (NT) __builtin_nontemporal_store(v[u], gmut<u32x4>(da[u]));
+      else *gmut<u32x4>(da[u]) = v[u];
+    }
+  }
+}
+
 // Rows whose size or buffers do not allow 16-byte units on every row (the
 // host only knows the row size): the index space is 16-byte chunks of each
 // block, every block padded to whole chunks, so a chunk never spans two
@@ -473,11 +523,43 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimit
   }
   __syncthreads();
 
+  if constexpr (!FAST) {
+    if (s_allvec) {
+      // The one-pass grid with every block aligned whole chunks: whole tiles
+      // without bound checks, then the tile that reaches the total (as in
+      // a2av_body's one-pass form).  The resident grid's loop below, with
+      // its checks, measured 5% slower than the general loop here.
+      const uint64_t total = s_end[nb - 1];
+      int top = 1;
+      while (top * 2 <= nb) top *= 2;
+      const uint64_t tile = (uint64_t)kBlock * UN;
+      const int lane = threadIdx.x & 63;
+      const bool wl = COLL_A2A_WAVE_LOCATE && nb <= 64;
+      uint64_t my_end = ~0ull, my_src = 0, my_dst = 0;
+      if (wl && lane < nb) {
+        my_end = s_end[lane];
+        my_src = s_src[lane];
+        my_dst = s_dst[lane];
+      }
+      uint64_t blo = 1, bhi = 0, sbase = 0, dbase = 0;
+      for (uint64_t wbase = (uint64_t)blockIdx.x * tile + (threadIdx.x - lane); wbase < total;
+           wbase += (uint64_t)gridDim.x * tile) {
+        if (wbase + 63 + (uint64_t)(UN - 1) * kBlock < total) {
+          chunk_vec_tile<NT, UN, true>(wbase, lane, total, nb, top, wl, my_end, my_src, my_dst,
+                                       s_end, s_src, s_dst, blo, bhi, sbase, dbase);
+        } else {
+          chunk_vec_tile<NT, UN, false>(wbase, lane, total, nb, top, wl, my_end, my_src,
+                                        my_dst, s_end, s_src, s_dst, blo, bhi, sbase, dbase);
+          break;
+        }
+      }
+      return;
+    }
+  }
   if (FAST && s_allvec) {
     // Every block is 16-byte aligned at both ends and a whole number of
-    // chunks (e.g. rows of one bf16 with equal counts): plain vector copies.
-    // (Used on the resident grid only: on the one-pass grid this loop
-    // measured 5% slower than the general one at 64 MiB per rank.)
+    // chunks (e.g. rows of one bf16 with equal counts): plain vector copies
+    // (the resident grid; the one-pass grid takes the form above).
     const uint64_t total = s_end[nb - 1];
     int top = 1;
     while (top * 2 <= nb) top *= 2;
