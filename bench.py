@@ -494,6 +494,21 @@ def copy_ceiling(torch, coll, W):
             "runtime_copy_frac": round(gbr / HBM_PEAK_GBS, 4)}
 
 
+def expert_table_search(torch, coll, W):
+    """The test expert's other path, the table search (a workspace of the
+    row-prefix tables alone: no per-row descriptors), on the step's receive
+    buffers in place, graph-timed beside the step's row-descriptor path."""
+    E, T, K, H = W["moe"]
+    R_ = len(W["recv"])
+    ws = torch.empty(coll.moe_expert_workspace_bytes(R_, E), dtype=torch.uint8, device="cuda")
+    fn = coll.prepare(coll.moe_expert_scale, W["recv"], W["ec"], W["rd"], E, H, ws)
+    t = _graph_time(torch, lambda i: fn(), 1, n=8, reps=3)
+    nb = 2 * W["moe_rows"] * H * 2
+    del ws, fn
+    return {"us": round(t * 1e6, 2), "bytes": nb, "GBps": round(nb / t / 1e9, 1),
+            "frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def fanout_ceiling(torch, coll):
     """The 1 -> 8 fan-out pattern alone, at the MoE permute's volume: the
     library's Broadcast from one 448 MiB buffer to 8 others (4096 tokens x
@@ -896,6 +911,10 @@ def report(path):
         f = d["fanout_ceiling_1to8"]
         ex.append(f"| 1 → 8 fan-out at the permute's volume (Broadcast, 448 MiB to 8 buffers, graph) | "
                   f"{f['us']} µs, {f['GBps']} GB/s = {_as_pct(f['frac'])} |")
+    if d.get("moe_expert_table_search"):
+        e = d["moe_expert_table_search"]
+        ex.append(f"| test expert by table search (no row descriptors), the MoE shape (graph) | "
+                  f"{e['us']} µs, {e['GBps']} GB/s = {_as_pct(e['frac'])} |")
     if d.get("allreduce_16mib_layout_ab"):
         a = d["allreduce_16mib_layout_ab"]
         ex.append(f"| AllReduce 16 MiB × 8, torch allocations vs rank arena | "
@@ -1037,7 +1056,7 @@ def main():
                       "frac": round(step_bytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del g
 
-    fused = lat = ceil_ = fan = None
+    fused = lat = ceil_ = fan = ets = None
     if not args.only:
         print("[bench] fused MoE path", file=sys.stderr, flush=True)
         fused = moe_fused(torch, coll, W, {n: rows_out[n]["us"] for n in names})
@@ -1046,6 +1065,7 @@ def main():
             lat = latency_rows_graph(torch, coll, W, {n: rows_out[n]["us"] for n in names})
             ceil_ = copy_ceiling(torch, coll, W)
             fan = fanout_ceiling(torch, coll)
+            ets = expert_table_search(torch, coll, W)
 
     ab = extra = None
     if not args.no_sweep and not args.only:
@@ -1086,6 +1106,7 @@ def main():
         "latency_rows_graph": lat,
         "copy_ceiling_1gib": ceil_,
         "fanout_ceiling_1to8": fan,
+        "moe_expert_table_search": ets,
     }
     print(json.dumps(out))
 
