@@ -293,7 +293,11 @@ __device__ __forceinline__ void a2av_body(const RankPtrs &p, const RowLimits &li
     }
     return;
   }
-  // the current block's bounds and address bases live in registers; LDS is
+  // The resident grid: every tile in the checked form, written out here
+  // rather than through a2av_tile (the same steps), so that its instructions
+  // stay those it was measured with; whole tiles without checks, and the
+  // helper's slightly different code, measured slower on this grid.
+  // The current block's bounds and address bases live in registers; LDS is
   // read only when a unit falls outside them.  The loop runs while the wave's
   // first unit is inside the total, so the wave stays whole for its ballots.
   uint64_t blo = 1, bhi = 0, sbase = 0, dbase = 0;
@@ -559,7 +563,9 @@ __global__ __launch_bounds__(kBlock) void a2av_chunk_kernel(RankPtrs p, RowLimit
   if (FAST && s_allvec) {
     // Every block is 16-byte aligned at both ends and a whole number of
     // chunks (e.g. rows of one bf16 with equal counts): plain vector copies
-    // (the resident grid; the one-pass grid takes the form above).
+    // (the resident grid; the one-pass grid takes the form above).  The same
+    // steps as chunk_vec_tile, written out with their checks: whole tiles
+    // without them measured slower on this grid.
     const uint64_t total = s_end[nb - 1];
     int top = 1;
     while (top * 2 <= nb) top *= 2;
