@@ -45,7 +45,7 @@ constexpr int kA2aResU = COLL_A2A_RES_U;      // ... resident grid
 constexpr int kA2aBlock = COLL_A2A_BLOCK;
 // receive capacity up to which the plain form runs a resident grid
 #ifndef COLL_A2A_RESIDENT_MAX_BYTES
-#define COLL_A2A_RESIDENT_MAX_BYTES (256ull << 20)
+#define COLL_A2A_RESIDENT_MAX_BYTES (64ull << 20)
 #endif
 // 1: R <= 8 uses the one-block-per-lane table (a2av_kernel8 / a2av_res_kernel8)
 #ifndef COLL_A2A_SMALL
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kA2aBlock) void a2av_kernel8(RankPtrs p, RowLimits 
                                                        const int64_t *rdispls, int ct, uint64_t row_units) {
   a2av_body<B, NT, kA2aU, kA2aBlock, true, true>(p, lim, R, counts, sdispls, rdispls, ct, row_units);
 }
-// Resident grid (up to 256 MiB): kA2aResU units per lane per tile.
+// Resident grid (up to 64 MiB of capacity): kA2aResU units per lane per tile.
 template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void a2av_res_kernel(RankPtrs p, RowLimits lim, int R,
                                                           const int64_t *counts,
@@ -918,8 +918,10 @@ int launch_a2av(const Launch &L, int R, const RankPtrs &p, const RowLimits &lim,
   // Large exchanges: one workgroup per tile of the bound (surplus workgroups
   // exit at once).  Up to kResidentMaxBytes, and without a bound: a resident
   // grid of 4 workgroups per CU looping over tiles of kA2aResU units per lane,
-  // which builds the block table once per workgroup (measured on MI355X at
-  // R = 8: +4..8% at 16-32 MiB per rank, -2..4% from 64 MiB per rank up).
+  // which builds the block table once per workgroup.  MI355X, R = 8, graph
+  // replay, since the one-pass grid's whole tiles lost their bound checks:
+  // one-pass 1.5-2 points slower at 4-8 MiB per rank, 0.3-0.7 faster at 16,
+  // 2-3 faster at 32, 1 faster at the MoE exchange of 256 tokens (28 MiB).
   constexpr uint64_t kResidentMaxBytes = COLL_A2A_RESIDENT_MAX_BYTES;
   const uint64_t cap_bytes = (uint64_t)rows_capacity * row_bytes;
   const bool resident = rows_capacity == 0 || cap_bytes <= kResidentMaxBytes;

@@ -204,8 +204,8 @@ int coll_broadcast(int nranks, const void *sendbuf_root, void *const *recvbufs, 
  *   recv_rows_capacity: the rows of all receive buffers together, an upper
  *   bound of the rows moved that the host knows without reading the counts.
  *   It only shapes the launch, never the result or the memory addressed.
- *   Above 256 MiB of capacity there is one workgroup per tile of the bound.
- *   Up to 256 MiB, or with 0 (unknown), a resident grid loops over the tiles
+ *   Above 64 MiB of capacity there is one workgroup per tile of the bound.
+ *   Up to 64 MiB, or with 0 (unknown), a resident grid loops over the tiles
  *   (the faster forms on MI355X at those sizes).
  */
 int coll_all_to_all_v(int nranks, const void *const *sendbufs, const int64_t *sendcounts,

@@ -318,7 +318,7 @@ def test_a2av_random_counts(R, W, dtype, ws):
 @pytest.mark.parametrize("R,W,dtype", [(2, 8, "bf16"), (8, 8, "bf16"), (8, 7168, "bf16"),
                                      (3, 4, "fp32"), (16, 8, "bf16")])
 def test_a2av_one_pass_grid_ragged_total(R, W, dtype):
-    """The plain form's one-pass grid (chosen above 256 MiB of receive
+    """The plain form's one-pass grid (chosen above 64 MiB of receive
     capacity; the capacity only sizes the launch) on small random exchanges:
     whole tiles, then the tile that reaches the total, then surplus
     workgroups with nothing to move."""
